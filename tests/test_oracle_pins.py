@@ -1,0 +1,330 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula: each checks a closed form, an
+invariant, a brute-force construction along a different route, finite
+differences, or a published test vector.
+"""
+
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_theta(rng, k, b, std):
+    return rng.standard_normal((k, b * (b - 1) // 2)) * std
+
+
+# ---------------------------------------------------------------- rounding --
+def test_round_bf16_special_values():
+    r = O.round_bf16
+    assert r(1.0) == 1.0
+    assert r(1.0 + 2.0 ** -8) == 1.0                      # tie, 1.0 is even
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6      # tie, rounds to even
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    assert r(-1.0 - 2.0 ** -8) == -1.0
+    assert r(0.0) == 0.0
+    assert r(2.0 ** -130) == 2.0 ** -130                  # subnormal, exact
+    assert r(3.0 * 2.0 ** -134) == 2.0 ** -132            # subnormal tie -> even
+
+
+def test_round_bf16_is_nearest_representable():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(20000) * 10.0 ** rng.uniform(-6, 6, 20000)
+    y = O.round_bf16(x)
+    bits = y.astype(np.float32).view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)                     # y is a bf16 value
+    assert np.all(y.astype(np.float32).astype(np.float64) == y)
+    up = (bits + 0x10000).view(np.float32).astype(np.float64)
+    dn = (bits - 0x10000).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(x - y) <= np.abs(x - up))
+    assert np.all(np.abs(x - y) <= np.abs(x - dn))
+
+
+def test_round_bf16_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(50000) * 3).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+# ------------------------------------------------------------ permutations --
+def test_mix64_published_vector():
+    lines = [l for l in open(os.path.join(GOLDEN, "splitmix64_seed1234567.txt"))
+             if l.strip() and not l.startswith("#")]
+    seed = int(lines[0].split()[1])
+    expect = [int(l) for l in lines[1:]]
+    got = [O.mix64(seed + O.GOLDEN_GAMMA * (i + 1)) for i in range(len(expect))]
+    assert got == expect
+
+
+def test_permutation_is_bijection_and_deterministic():
+    for n in (1, 2, 7, 256, 5632, 11008):
+        p = O.make_permutation(123, 0, 0, n)
+        assert p.dtype == np.int64
+        assert np.array_equal(np.sort(p), np.arange(n))
+        assert np.array_equal(p, O.make_permutation(123, 0, 0, n))
+
+
+def test_permutation_streams_differ():
+    a = O.make_permutation(5, 0, 0, 512)
+    assert not np.array_equal(a, O.make_permutation(5, 0, 1, 512))
+    assert not np.array_equal(a, O.make_permutation(5, 1, 0, 512))
+    assert not np.array_equal(a, O.make_permutation(6, 0, 0, 512))
+    # consecutive merges are not shifts of one another
+    b = O.make_permutation(5, 1, 0, 512)
+    assert not np.array_equal(a[1:], b[:-1])
+
+
+def test_permutation_uniform_chi2():
+    # all 24 permutations of 4 items, 24000 seeds: chi^2 with 23 dof
+    counts = {p: 0 for p in itertools.permutations(range(4))}
+    trials = 24000
+    for s in range(trials):
+        counts[tuple(O.make_permutation(s, 3, 1, 4))] += 1
+    exp = trials / 24
+    chi2 = sum((c - exp) ** 2 / exp for c in counts.values())
+    assert chi2 < 49.7          # p = 0.001 critical value for 23 dof
+
+
+def test_permutation_sort_order():
+    # the permutation lists indices in ascending key order, ties by index
+    seed, k, side, n = 99, 2, 1, 64
+    base = O.mix64(seed + O.GOLDEN_GAMMA * (2 * k + side + 1))
+    keys = np.array([O.mix64(base + O.GOLDEN_GAMMA * (i + 1)) for i in range(n)], dtype=np.uint64)
+    p = O.make_permutation(seed, k, side, n)
+    assert np.all(keys[p][1:] > keys[p][:-1])
+
+
+# ----------------------------------------------------------- unpack_skew ----
+def test_unpack_skew_positions():
+    b = 6
+    theta = np.arange(1, b * (b - 1) // 2 + 1, dtype=np.float64)
+    S = O.unpack_skew(theta, b)
+    p = 0
+    for i in range(b):                 # row-major walk of the strict upper triangle
+        for j in range(i + 1, b):
+            assert S[i, j] == theta[p] and S[j, i] == -theta[p]
+            assert p == i * b - i * (i + 1) // 2 + (j - i - 1)
+            p += 1
+    assert np.all(np.diag(S) == 0)
+    assert np.array_equal(S, -S.T)
+
+
+# ----------------------------------------------------------------- Cayley ---
+def test_cayley_b2_closed_form():
+    for a in (0.0, 0.3, -1.7, 5.0):
+        Q = O.cayley(O.unpack_skew(np.array([a]), 2))
+        c, s = (1 - a * a) / (1 + a * a), 2 * a / (1 + a * a)
+        assert np.allclose(Q, [[c, s], [-s, c]], atol=1e-15, rtol=0)
+
+
+def test_cayley_zero_is_identity():
+    for b in (2, 32, 256):
+        Q = O.cayley(O.unpack_skew(np.zeros(b * (b - 1) // 2), b))
+        assert np.array_equal(Q, np.eye(b))
+
+
+@pytest.mark.parametrize("b,var", [(32, 1e-2), (64, 1e-3), (256, 1e-3), (512, 1e-3)])
+def test_cayley_orthogonal_det_one(b, var):
+    rng = np.random.default_rng(b)
+    S = O.unpack_skew(rng.standard_normal(b * (b - 1) // 2) * np.sqrt(var), b)
+    Q = O.cayley(S)
+    assert np.linalg.norm(Q.T @ Q - np.eye(b)) <= 1e-10
+    assert abs(np.linalg.det(Q) - 1.0) <= 1e-10
+    # Q(-S) = Q(S)^T and Q = 2 (I - S)^-1 - I
+    assert np.allclose(O.cayley(-S), Q.T, atol=1e-13, rtol=0)
+    assert np.allclose(Q, 2 * np.linalg.inv(np.eye(b) - S) - np.eye(b), atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- forward ---
+def _case(rng, m, n, b, N, wstd=0.1, tstd=0.2):
+    W0 = rng.standard_normal((m, n)) * wstd
+    thR = _rand_theta(rng, m // b, b, tstd)
+    thP = _rand_theta(rng, n // b, b, tstd)
+    sigma = O.make_permutation(int(rng.integers(1 << 62)), 0, 0, m)
+    tau = O.make_permutation(int(rng.integers(1 << 62)), 0, 1, n)
+    X = rng.standard_normal((N, n))
+    gY = rng.standard_normal((N, m))
+    return W0, thR, thP, sigma, tau, X, gY
+
+
+SHAPES = [(256, 256, 32, 64), (40, 24, 8, 5), (37, 50, 6, 9), (16, 16, 16, 3), (10, 7, 4, 2)]
+
+
+@pytest.mark.parametrize("m,n,b,N", SHAPES)
+def test_forward_matches_dense_brute_force(m, n, b, N):
+    rng = np.random.default_rng([m, n, b, N])
+    W0, thR, thP, sigma, tau, X, _ = _case(rng, m, n, b, N)
+    R = O.dense_orthogonal(thR, sigma, b)
+    P = O.dense_orthogonal(thP, tau, b)
+    Y = O.forward(W0, thR, thP, sigma, tau, X, b)
+    assert np.allclose(Y, X @ (R @ W0 @ P).T, atol=1e-12, rtol=0)
+    assert np.allclose(R.T @ R, np.eye(m), atol=1e-12)
+    v = rng.standard_normal(m)
+    assert abs(np.linalg.norm(R @ v) - np.linalg.norm(v)) < 1e-12
+
+
+def test_forward_zero_generators_is_plain_matmul():
+    rng = np.random.default_rng(3)
+    W0, thR, thP, sigma, tau, X, _ = _case(rng, 48, 32, 8, 7)
+    Y = O.forward(W0, 0 * thR, 0 * thP, sigma, tau, X, 8)
+    assert np.allclose(Y, np.matmul(X, W0.T), atol=1e-13, rtol=0)
+
+
+def test_tail_coordinates_untouched_by_R():
+    # coordinates in the identity tail of R pass W0 P x through unchanged
+    rng = np.random.default_rng(4)
+    m, n, b = 21, 16, 4
+    W0, thR, thP, sigma, tau, X, _ = _case(rng, m, n, b, 3)
+    Y = O.forward(W0, thR, thP, sigma, tau, X, b)
+    Y0 = O.forward(W0, 0 * thR, thP, sigma, tau, X, b)
+    tail = sigma[(m // b) * b:]
+    assert np.allclose(Y[:, tail], Y0[:, tail], atol=1e-14, rtol=0)
+
+
+@pytest.mark.parametrize("m,n,b", [(64, 48, 16), (256, 256, 32), (50, 30, 7)])
+def test_spectral_invariance(m, n, b):
+    rng = np.random.default_rng([m, n, b, 1])
+    W0, thR, thP, sigma, tau, _, _ = _case(rng, m, n, b, 1)
+    W = O.dense_orthogonal(thR, sigma, b) @ W0 @ O.dense_orthogonal(thP, tau, b)
+    s0 = np.linalg.svd(W0, compute_uv=False)
+    s1 = np.linalg.svd(W, compute_uv=False)
+    assert np.max(np.abs(s0 - s1)) <= 1e-9 * s0[0]
+    s2 = np.linalg.svd(O.merge(W0, thR, thP, sigma, tau, b), compute_uv=False)
+    assert np.max(np.abs(s0 - s2)) <= 1e-9 * s0[0]
+
+
+# --------------------------------------------------------------- backward ---
+def _loss(W0, thR, thP, sigma, tau, X, gY, b):
+    return float(np.sum(gY * O.forward(W0, thR, thP, sigma, tau, X, b)))
+
+
+@pytest.mark.parametrize("m,n,b,N", [(10, 7, 3, 4), (12, 9, 4, 3), (8, 8, 8, 2)])
+def test_backward_generators_finite_differences(m, n, b, N):
+    rng = np.random.default_rng([m, n, b, N, 9])
+    W0, thR, thP, sigma, tau, X, gY = _case(rng, m, n, b, N, wstd=0.5, tstd=0.4)
+    _, dR, dP = O.backward(W0, thR, thP, sigma, tau, X, gY, b)
+    h = 1e-6
+    for th, d, side in ((thR, dR, 0), (thP, dP, 1)):
+        fd = np.zeros_like(th)
+        for idx in np.ndindex(th.shape):
+            tp, tm = th.copy(), th.copy()
+            tp[idx] += h
+            tm[idx] -= h
+            args_p = (tp, thP) if side == 0 else (thR, tp)
+            args_m = (tm, thP) if side == 0 else (thR, tm)
+            fd[idx] = (_loss(W0, *args_p, sigma, tau, X, gY, b)
+                       - _loss(W0, *args_m, sigma, tau, X, gY, b)) / (2 * h)
+        assert np.allclose(d, fd, atol=1e-7, rtol=1e-6), (side, np.max(np.abs(d - fd)))
+
+
+def test_backward_dx_is_dense_transpose():
+    rng = np.random.default_rng(11)
+    m, n, b = 37, 50, 6
+    W0, thR, thP, sigma, tau, X, gY = _case(rng, m, n, b, 5)
+    dX, _, _ = O.backward(W0, thR, thP, sigma, tau, X, gY, b)
+    W = O.dense_orthogonal(thR, sigma, b) @ W0 @ O.dense_orthogonal(thP, tau, b)
+    assert np.allclose(dX, gY @ W, atol=1e-12, rtol=0)
+
+
+def test_chain_rule_b2_closed_form():
+    # at b=2, Q(a) = [[c, s], [-s, c]] and dQ/da is known in closed form
+    rng = np.random.default_rng(2)
+    for a in (0.0, 0.7, -2.5):
+        G = rng.standard_normal((2, 2))
+        Q = O.cayley(O.unpack_skew(np.array([a]), 2))
+        dQ = np.array([[-4 * a, 2 * (1 - a * a)], [-2 * (1 - a * a), -4 * a]]) / (1 + a * a) ** 2
+        assert np.allclose(O.chain_rule(G, Q), [np.sum(G * dQ)], atol=1e-13, rtol=0)
+
+
+# ------------------------------------------------------------------ merge ---
+@pytest.mark.parametrize("m,n,b", [(64, 48, 16), (37, 50, 6), (256, 256, 32)])
+def test_merge_is_dense_product(m, n, b):
+    rng = np.random.default_rng([m, n, b, 2])
+    W0, thR, thP, sigma, tau, _, _ = _case(rng, m, n, b, 1)
+    W = O.merge(W0, thR, thP, sigma, tau, b)
+    Wd = O.dense_orthogonal(thR, sigma, b) @ W0 @ O.dense_orthogonal(thP, tau, b)
+    assert np.allclose(W, Wd, atol=1e-12, rtol=0)
+
+
+def test_merge_preserves_function():
+    rng = np.random.default_rng(21)
+    m, n, b = 40, 24, 8
+    W0, thR, thP, sigma, tau, X, _ = _case(rng, m, n, b, 6)
+    before = O.forward(W0, thR, thP, sigma, tau, X, b)
+    W1 = O.merge(W0, thR, thP, sigma, tau, b)
+    s1, t1 = O.make_permutation(77, 1, 0, m), O.make_permutation(77, 1, 1, n)
+    after = O.forward(W1, 0 * thR, 0 * thP, s1, t1, X, b)
+    assert np.allclose(before, after, atol=1e-12, rtol=0)
+
+
+def test_zero_merge_is_pure_relayout():
+    rng = np.random.default_rng(22)
+    m, n, b = 40, 24, 8
+    W0, thR, thP, sigma, tau, _, _ = _case(rng, m, n, b, 1)
+    for contract in (False, True):
+        W = O.round_bf16(W0) if contract else W0
+        assert np.array_equal(O.merge(W, 0 * thR, 0 * thP, sigma, tau, b, contract=contract), W)
+    Wp = O.pack(W0, sigma, tau)
+    assert np.array_equal(O.unpack(Wp, sigma, tau), W0)
+    assert Wp[3, 5] == W0[sigma[3], tau[5]]
+
+
+# ------------------------------------------------------ bf16 contract mode ---
+def test_contract_mode_reduces_to_exact_without_rounding(monkeypatch):
+    rng = np.random.default_rng(31)
+    m, n, b = 24, 40, 8
+    W0, thR, thP, sigma, tau, X, gY = _case(rng, m, n, b, 5)
+    ref_f = O.forward(W0, thR, thP, sigma, tau, X, b)
+    ref_b = O.backward(W0, thR, thP, sigma, tau, X, gY, b)
+    ref_m = O.merge(W0, thR, thP, sigma, tau, b)
+    import oracle.poetx as P
+    monkeypatch.setattr(P, "round_bf16", lambda x: np.asarray(x, dtype=np.float64))
+    assert np.array_equal(P.forward(W0, thR, thP, sigma, tau, X, b, contract=True), ref_f)
+    got = P.backward(W0, thR, thP, sigma, tau, X, gY, b, contract=True)
+    for g, r in zip(got, ref_b):
+        assert np.array_equal(g, r)
+    assert np.array_equal(P.merge(W0, thR, thP, sigma, tau, b, contract=True), ref_m)
+
+
+def test_contract_mode_outputs_are_bf16_and_close():
+    rng = np.random.default_rng(32)
+    m, n, b = 64, 48, 16
+    W0, thR, thP, sigma, tau, X, gY = _case(rng, m, n, b, 33)
+    W0 = O.round_bf16(W0)
+    X = O.round_bf16(X)
+    gY = O.round_bf16(gY)
+    Yc = O.forward(W0, thR, thP, sigma, tau, X, b, contract=True)
+    Ye = O.forward(W0, thR, thP, sigma, tau, X, b)
+    assert np.array_equal(O.round_bf16(Yc), Yc)
+    assert np.linalg.norm(Yc - Ye) <= 2e-2 * np.linalg.norm(Ye)
+    dXc, dRc, dPc = O.backward(W0, thR, thP, sigma, tau, X, gY, b, contract=True)
+    dXe, dRe, dPe = O.backward(W0, thR, thP, sigma, tau, X, gY, b)
+    assert np.array_equal(O.round_bf16(dXc), dXc)
+    for c, e in ((dXc, dXe), (dRc, dRe), (dPc, dPe)):
+        assert np.linalg.norm(c - e) <= 3e-2 * np.linalg.norm(e)
+
+
+# ------------------------------------------------------------------- Adam ---
+def test_adam_first_step_closed_form():
+    g = np.array([0.5, -2.0, 1e-3, 0.0])
+    th, m, v = O.adam_step(np.ones(4), g, np.zeros(4), np.zeros(4), 1, lr=0.1)
+    # m_hat = g and v_hat = g^2 at step 1, so the step is lr * g / (|g| + eps)
+    assert np.allclose(th, 1.0 - 0.1 * g / (np.abs(g) + 1e-8), atol=1e-15, rtol=0)
+    assert np.allclose(m, 0.1 * g) and np.allclose(v, 0.001 * g * g)
+
+
+def test_adam_second_step_by_hand():
+    th, m, v = O.adam_step(np.array([0.0]), np.array([1.0]), np.zeros(1), np.zeros(1), 1, lr=1.0)
+    th, m, v = O.adam_step(th, np.array([-1.0]), m, v, 2, lr=1.0)
+    # m2 = 0.9*0.1 - 0.1 = -0.01 ; v2 = 0.999*0.001 + 0.001 = 0.001999
+    mhat = -0.01 / (1 - 0.81)
+    vhat = 0.001999 / (1 - 0.998001)
+    assert np.allclose(th, [-(1 / (1 + 1e-8)) - mhat / (np.sqrt(vhat) + 1e-8)], atol=1e-12, rtol=0)
