@@ -1,0 +1,198 @@
+/*
+ * poetx.h -- C ABI of the POET-X layer hot path on AMD Instinct MI355X (gfx950).
+ *
+ * One linear layer uses the weight W = R * W0 * P.  W0 (m x n, out x in) is
+ * frozen; R (m x m) and P (n x n) are permuted block-diagonal orthogonal
+ * matrices whose b x b blocks are Cayley transforms of trainable
+ * skew-symmetric generators.  The library computes the forward product
+ * y = R (W0 (P x)), the backward onto the generators (and the input) with the
+ * blocks and intermediate activations recomputed instead of stored, and the
+ * periodic merge W0 <- R W0 P with generator reset and re-permutation.
+ *
+ * Sources (cited by page title and section):
+ *  [P3] "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
+ *       Transformation", gist.science summary of arXiv 2603.05500,
+ *       "Technische samenvatting" > "Methodologie" items 1-5.
+ *  [P1] "POET-X：基于正交变换缩放的内存高效LLM训练方法" (ai-stack.site),
+ *       实践 2 (Cayley transform), 实践 4 (recompute), 实践 5 (fp32 accumulation).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *    unless a parameter says "host".  The library never allocates or frees
+ *    device memory; scratch space is the caller's workspace `ws` of at least
+ *    poetx_workspace_bytes(...) bytes, 256-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on `stream` and returns; none synchronizes the host.
+ *  - Tokens are rows: X is N x n, Y and dY are N x m, so Y = X W^T.
+ *  - Block structure: k_R = m / b blocks on the R side, k_P = n / b on the P
+ *    side (integer division).  The m - k_R*b (resp. n - k_P*b) leftover
+ *    coordinates form an identity tail with no generator.
+ *  - Generators ("theta"): fp32, [k][b(b-1)/2], the strict upper triangle of
+ *    each skew block S in row-major order: S[i][j] = theta[p], S[j][i] = -theta[p]
+ *    for i < j, p = i*b - i*(i+1)/2 + (j-i-1).  Only this triangle is stored
+ *    [P3 item 4].  Block l of R is Q_l = (I - S_l)^-1 (I + S_l) [P1 实践 2].
+ *  - Permutations: int32 index maps, never matrices [P3 item 2].  sigma (length
+ *    m) and tau (length n): block l of R acts on the true coordinates
+ *    sigma[l*b .. l*b+b-1], the tail on sigma[k_R*b ..]; likewise tau for P.
+ *  - Working weight layout: the two permutations next to W0 are folded into
+ *    the stored weight [P3 item 2, second bullet]: the buffer W0p holds
+ *    W0p[i][j] = W0[sigma[i]][tau[j]].  poetx_merge with zero generators is a
+ *    pure relayout, which is how a caller packs a true-coordinate W0 (start
+ *    from identity sigma, tau) and unpacks it again.
+ *  - dtype (poetx_layer.dtype) applies to W0p, X, Y, dY and dX: POETX_F32 or
+ *    POETX_BF16.  With bf16 every product runs on bf16 MFMA with fp32
+ *    accumulation [P1 实践 5]; intermediate activations are stored in bf16.
+ *    Generators, their gradients and the Cayley solve are fp32.
+ *  - Results are deterministic: identical inputs give bit-identical outputs.
+ *  - Errors: a negative poetx_status; poetx_last_error() then describes it.
+ *    Arguments are validated on the host before anything is enqueued, so an
+ *    error leaves every output untouched.  A failed kernel launch returns
+ *    POETX_EHIP.  No exception crosses the ABI.
+ *  - Sizes: 1 <= m, n <= 32768; 0 <= N < 2^31; b in {32, 64, 128, 256, 512}.
+ *    N == 0 is a valid empty call (nothing is enqueued except the gradient
+ *    reset of poetx_backward when POETX_ACCUMULATE_GRAD is not set).
+ */
+#ifndef POETX_H
+#define POETX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  POETX_OK = 0,
+  POETX_EINVAL = -1,     /* null pointer, bad enum, bad block size          */
+  POETX_ESHAPE = -2,     /* m, n, N or a count out of range                 */
+  POETX_EDTYPE = -3,     /* unsupported dtype                                */
+  POETX_EWORKSPACE = -4, /* workspace too small or misaligned                */
+  POETX_EHIP = -5        /* a HIP runtime call or kernel launch failed       */
+} poetx_status;
+
+typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
+
+/* poetx_layer.flags */
+#define POETX_ACCUMULATE_GRAD 1u /* backward adds into dthR/dthP instead of overwriting */
+
+/* op codes for poetx_workspace_bytes */
+#define POETX_OP_FORWARD 0
+#define POETX_OP_BACKWARD 1
+#define POETX_OP_MERGE 2
+
+typedef struct {
+  int64_t m;      /* rows of W0 = output features                         */
+  int64_t n;      /* columns of W0 = input features                       */
+  int32_t b;      /* block size of R and P                                */
+  int32_t dtype;  /* poetx_dtype of W0p, X, Y, dY, dX                     */
+  uint32_t flags; /* POETX_ACCUMULATE_GRAD                                */
+  uint32_t reserved; /* must be 0                                         */
+} poetx_layer;
+
+/*
+ * Bytes of workspace that op (POETX_OP_*) needs for this layer and N tokens.
+ * Returns 0 and sets the last error if the layer is invalid.  Host only.
+ */
+size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op);
+
+/*
+ * Bytes of workspace poetx_build_blocks needs for nblocks blocks of size b.
+ */
+size_t poetx_build_workspace_bytes(int64_t nblocks, int32_t b);
+
+/*
+ * a1-a2: batched Cayley builder [P1 实践 2; P3 item 4].
+ * For each block l < nblocks: S_l from theta[l] (layout above), then
+ * Q_l = (I - S_l)^-1 (I + S_l), computed as 2 (I - S_l)^-1 - I with an exact
+ * fp32 Gauss-Jordan solve (no pivoting: I - S has symmetric part I).
+ *   theta  [nblocks][b(b-1)/2] fp32, device
+ *   Q32    [nblocks][b][b] fp32 row-major, device, nullable
+ *   Qbf16  [nblocks][b][b] bf16 Q, row-major, device, nullable
+ *   QTbf16 [nblocks][b][b] bf16 Q^T, row-major, device, nullable
+ *   ws     workspace of poetx_build_workspace_bytes(nblocks, b) bytes
+ * nblocks == 0 is a no-op.
+ */
+int poetx_build_blocks(const float* theta, int64_t nblocks, int32_t b, float* Q32,
+                       void* Qbf16, void* QTbf16, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * a3-a5: forward Y = X W^T, W = R W0 P, computed input-centrically as
+ * P, then W0, then R on each token [P3 item 1], with P and R applied as
+ * gathers/scatters and batched block products [P3 items 2-3].
+ *   W0p   [m][n] dtype, working layout
+ *   thR   [k_R][b(b-1)/2] fp32;  thP [k_P][b(b-1)/2] fp32
+ *   sigma [m] int32, tau [n] int32 (must be permutations; not checked)
+ *   X     [N][n] dtype;  Y [N][m] dtype (written)
+ */
+int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR,
+                  const float* thP, const int32_t* sigma, const int32_t* tau,
+                  const void* X, int64_t N, void* Y, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/*
+ * a0, a6-a9: backward of L = <dY, Y> with W0 frozen.  The Cayley blocks and
+ * the intermediate activations are recomputed from X rather than stored
+ * (POET-Xmem gradient checkpointing, [P3 item 5]); the gradient reaches the
+ * stored generators through the Cayley map [P1 实践 2 step 3]:
+ * dL/dS = 1/2 (I + Q^T) G (I + Q^T) with G = dL/dQ, and
+ * dL/dtheta_p = G_S[i][j] - G_S[j][i].
+ *   dY   [N][m] dtype
+ *   dX   [N][n] dtype, written; nullable (then not computed)
+ *   dthR [k_R][b(b-1)/2] fp32, dthP [k_P][b(b-1)/2] fp32: overwritten, or
+ *        accumulated into when layer->flags has POETX_ACCUMULATE_GRAD
+ */
+int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR,
+                   const float* thP, const int32_t* sigma, const int32_t* tau,
+                   const void* X, const void* dY, int64_t N, void* dX, float* dthR,
+                   float* dthP, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * a10-a11: merge W0 <- R W0 P [P3 item 1], then theta_R, theta_P <- 0 and
+ * new permutations sigma' = perm(seed, merge_index, side 0),
+ * tau' = perm(seed, merge_index, side 1) (see poetx_make_permutation), with
+ * W0p rewritten in place into the new working layout:
+ * W0p'[i][j] = (R W0 P)[sigma'[i]][tau'[j]].
+ *   W0p        [m][n] dtype, in/out
+ *   thR, thP   fp32, zeroed on return
+ *   sigma, tau int32, in: current permutations; out: the new ones
+ * The permutations are drawn on the device; nothing is copied to or from the
+ * host.  With zero generators the result is an exact relayout.
+ */
+int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int32_t* sigma,
+                int32_t* tau, uint64_t perm_seed, uint64_t merge_index, void* ws,
+                size_t ws_bytes, void* stream);
+
+/*
+ * a11 on the host: the permutation poetx_merge draws for (seed, merge_index,
+ * side), written to host_out[0..n-1].  The pages only say the permutations are
+ * index maps [P3 item 2]; the generator adopted for "uniform random from a
+ * seed" is: mix64 = SplitMix64's output function (Steele, Lea & Flood 2014),
+ * gamma = 0x9E3779B97F4A7C15,
+ * base = mix64(seed + gamma*(2*merge_index + side + 1)),
+ * key_i = mix64(base + gamma*(i+1)), and the permutation lists 0..n-1 in
+ * ascending (key_i, i) order.  side: 0 = sigma (R), 1 = tau (P).
+ */
+int poetx_make_permutation(uint64_t seed, uint64_t merge_index, int32_t side, int64_t n,
+                           int32_t* host_out);
+
+/*
+ * a12: one Adam step (Kingma & Ba 2015, with bias correction, no weight
+ * decay) on count fp32 generators, in place:
+ *   m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2;
+ *   theta <- theta - lr * (m / (1-b1^step)) / (sqrt(v / (1-b2^step)) + eps).
+ * step >= 1.  Not on the pages (they leave the generator optimizer open).
+ */
+int poetx_adam_step(float* theta, const float* grad, float* m, float* v, int64_t count,
+                    int64_t step, float lr, float beta1, float beta2, float eps,
+                    void* stream);
+
+/* Message of the last error on this thread ("" if none). */
+const char* poetx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POETX_H */

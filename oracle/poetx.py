@@ -287,3 +287,4 @@ def adam_step(theta, grad, m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8
     mhat = m / (1.0 - beta1 ** step)
     vhat = v / (1.0 - beta2 ** step)
     return theta - lr * mhat / (np.sqrt(vhat) + eps), m, v
+

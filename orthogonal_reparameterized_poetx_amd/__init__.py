@@ -1,0 +1,31 @@
+"""POET-X layer hot path on AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libpoetx.so`` (HIP kernels behind the C ABI declared in
+``include/poetx.h``); this package is its thin Python binding, with PyTorch
+tensors supplying device memory and streams.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    OP_BACKWARD,
+    OP_FORWARD,
+    OP_MERGE,
+    POETX_ACCUMULATE_GRAD,
+    POETX_BF16,
+    POETX_F32,
+    Layer,
+    PoetxError,
+    build_workspace_bytes,
+    last_error,
+    lib,
+    make_workspace,
+    poetx_adam_step,
+    poetx_backward,
+    poetx_build_blocks,
+    poetx_forward,
+    poetx_make_permutation,
+    poetx_merge,
+    workspace_bytes,
+)
+from .layer import PoetxLayer  # noqa: F401,E402

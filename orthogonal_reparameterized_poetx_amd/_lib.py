@@ -1,0 +1,162 @@
+"""ctypes binding of libpoetx.so (include/poetx.h).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  Tensors are torch tensors on a ROCm device; their data pointers
+and the current HIP stream are passed through unchanged.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpoetx.so")
+
+POETX_F32 = 0
+POETX_BF16 = 1
+POETX_ACCUMULATE_GRAD = 1
+OP_FORWARD, OP_BACKWARD, OP_MERGE = 0, 1, 2
+
+_STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDTYPE",
+           -4: "POETX_EWORKSPACE", -5: "POETX_EHIP"}
+
+EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
+            "poetx_forward", "poetx_backward", "poetx_merge", "poetx_make_permutation",
+            "poetx_adam_step", "poetx_last_error")
+
+
+class Layer(ctypes.Structure):
+    """poetx_layer: W0 is m x n (out x in), block size b, dtype of W0/X/Y."""
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("b", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+    def __init__(self, m, n, b, dtype=POETX_BF16, flags=0):
+        super().__init__(int(m), int(n), int(b), int(dtype), int(flags), 0)
+
+    @property
+    def kR(self):
+        return self.m // self.b
+
+    @property
+    def kP(self):
+        return self.n // self.b
+
+    @property
+    def ntheta(self):
+        return self.b * (self.b - 1) // 2
+
+
+class PoetxError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__("%s failed: %s (%d): %s" % (fn, _STATUS.get(code, "?"), code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libpoetx.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libpoetx.so not found at %s; build it with __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, u64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+    LP = ctypes.POINTER(Layer)
+    sig = {
+        "poetx_workspace_bytes": (sz, [LP, i64, ctypes.c_int]),
+        "poetx_build_workspace_bytes": (sz, [i64, i32]),
+        "poetx_build_blocks": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
+        "poetx_forward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
+        "poetx_backward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "poetx_merge": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
+        "poetx_make_permutation": (ctypes.c_int, [u64, u64, i32, i64, vp]),
+        "poetx_adam_step": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_float, vp]),
+        "poetx_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def last_error():
+    return lib().poetx_last_error().decode()
+
+
+def _check(fn, code):
+    if code != 0:
+        raise PoetxError(fn, code, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_bytes(layer, N, op):
+    n = lib().poetx_workspace_bytes(ctypes.byref(layer), int(N), int(op))
+    if n == 0:
+        msg = last_error()
+        if msg:
+            raise PoetxError("poetx_workspace_bytes", -1, msg)
+    return n
+
+
+def build_workspace_bytes(nblocks, b):
+    return lib().poetx_build_workspace_bytes(int(nblocks), int(b))
+
+
+def make_workspace(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def poetx_build_blocks(theta, nblocks, b, Q32=None, Qbf16=None, QTbf16=None, ws=None, stream=None):
+    nb = ws.numel() if ws is not None else 0
+    _check("poetx_build_blocks", lib().poetx_build_blocks(_ptr(theta), int(nblocks), int(b), _ptr(Q32), _ptr(Qbf16),
+                                                          _ptr(QTbf16), _ptr(ws), nb, _stream(stream)))
+
+
+def poetx_forward(layer, W0p, thR, thP, sigma, tau, X, N, Y, ws, stream=None):
+    _check("poetx_forward", lib().poetx_forward(ctypes.byref(layer), _ptr(W0p), _ptr(thR), _ptr(thP), _ptr(sigma),
+                                                _ptr(tau), _ptr(X), int(N), _ptr(Y), _ptr(ws),
+                                                ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def poetx_backward(layer, W0p, thR, thP, sigma, tau, X, dY, N, dX, dthR, dthP, ws, stream=None):
+    _check("poetx_backward", lib().poetx_backward(ctypes.byref(layer), _ptr(W0p), _ptr(thR), _ptr(thP), _ptr(sigma),
+                                                  _ptr(tau), _ptr(X), _ptr(dY), int(N), _ptr(dX), _ptr(dthR),
+                                                  _ptr(dthP), _ptr(ws), ws.numel() if ws is not None else 0,
+                                                  _stream(stream)))
+
+
+def poetx_merge(layer, W0p, thR, thP, sigma, tau, perm_seed, merge_index, ws, stream=None):
+    _check("poetx_merge", lib().poetx_merge(ctypes.byref(layer), _ptr(W0p), _ptr(thR), _ptr(thP), _ptr(sigma),
+                                            _ptr(tau), int(perm_seed) & (2 ** 64 - 1), int(merge_index),
+                                            _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def poetx_make_permutation(seed, merge_index, side, n):
+    """Host generator; returns a list of n ints."""
+    buf = (ctypes.c_int32 * max(int(n), 1))()
+    _check("poetx_make_permutation", lib().poetx_make_permutation(int(seed) & (2 ** 64 - 1), int(merge_index),
+                                                                  int(side), int(n), ctypes.cast(buf, ctypes.c_void_p)))
+    return list(buf)[: int(n)]
+
+
+def poetx_adam_step(theta, grad, m, v, count, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, stream=None):
+    _check("poetx_adam_step", lib().poetx_adam_step(_ptr(theta), _ptr(grad), _ptr(m), _ptr(v), int(count), int(step),
+                                                    float(lr), float(beta1), float(beta2), float(eps),
+                                                    _stream(stream)))

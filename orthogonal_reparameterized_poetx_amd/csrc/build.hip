@@ -1,0 +1,485 @@
+// Cayley block builder, batched small fp32 GEMM and chain-rule projection.
+//
+// Q = (I - S)^-1 (I + S) for skew S [P1 "POET-X：基于正交变换缩放的内存高效LLM训练方法",
+// 实践 2], with S unpacked from the stored strict upper triangle
+// [P3 "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
+// Transformation", Methodologie item 4].  The pages' own GPU route fuses a
+// truncated Neumann series; here the inverse is exact: M = (I - S)^-1 by
+// Gauss-Jordan without pivoting (I - S has symmetric part I, so every leading
+// block is invertible and no growth occurs), then Q = 2M - I because
+// (I - S)^-1 (I + S) = (I - S)^-1 (2I - (I - S)).
+#include "common.h"
+#include "kernels.h"
+
+namespace poetx {
+
+// ----------------------------------------------------------------------------
+// Register-resident blocked Gauss-Jordan, one workgroup per B x B matrix.
+// Wave w owns a (32*TT) x (32*TT) tile of the matrix in MFMA accumulator
+// layout; a panel step K = [32p, 32p+32) inverts the diagonal 32x32 block in
+// LDS, forms the new row panel, and updates every other tile with one rank-32
+// MFMA product.
+// ----------------------------------------------------------------------------
+template <int B> struct GJShape {
+  static constexpr int TT = (B >= 256) ? 2 : 1;
+  static constexpr int WT = 32 * TT;
+  static constexpr int WPR = B / WT;
+  static constexpr int NW = WPR * WPR;
+  static constexpr int NT = 64 * NW;
+};
+
+// MODE 0: trailing updates on fp32 MFMA (exact products).
+// MODE 6: operands split three ways into bf16 (x = h + m + l, |x - h - m - l|
+//         <= 2^-27 |x|) and the six products of order <= 2 accumulated on bf16
+//         MFMA: fp32-level accuracy at bf16 MFMA rate.
+template <int B, int MODE>
+__global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
+  using S = GJShape<B>;
+  constexpr int TT = S::TT, NT = S::NT, WPR = S::WPR;
+  constexpr bool X6 = MODE == 6;
+  constexpr int PC = 33;       // fp32 column-panel pitch (32 + 1)
+  constexpr int PR = B + 1;    // fp32 row-panel pitch
+  constexpr int HP = 40;       // bf16 operand pitch (32 + 8): conflict-free b128 reads
+  __shared__ float Pcol[X6 ? 1 : B * PC];     // old column panel A[:, K] (fp32 mode)
+  __shared__ float Prow[32 * PR];             // old row panel A[K, :], then the new one
+  __shared__ float Dm[32 * PC];               // diagonal block -> its inverse
+  __shared__ bf16 OpA[X6 ? 3 * B * HP : 2];   // -A[:, K] split h|m|l, [i][kk]
+  __shared__ bf16 OpB[X6 ? 3 * B * HP : 2];   // new A[K, :]^T split h|m|l, [j][kk]
+
+  const int blk = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int tr = (wave / WPR) * S::WT;
+  const int tc = (wave % WPR) * S::WT;
+  const int lc = lane & 31;
+
+  // value of the old column panel A[i][K0 + t]
+  auto pcol = [&](int i, int t) -> float {
+    if constexpr (X6)
+      return -((float)OpA[i * HP + t] + (float)OpA[B * HP + i * HP + t] + (float)OpA[2 * B * HP + i * HP + t]);
+    else
+      return Pcol[i * PC + t];
+  };
+
+  f32x16 acc[TT][TT];
+  // ---- load A = I - S (theta mode) or A from a strided matrix
+#pragma unroll
+  for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < TT; ++tj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = tr + 32 * ti + c32_row(lane, r);
+        const int j = tc + 32 * tj + lc;
+        float v;
+        if (g.theta) {
+          const float* th = g.theta + (int64_t)blk * (B * (B - 1) / 2);
+          if (i == j) v = 1.0f;
+          else if (i < j) v = -th[i * B - i * (i + 1) / 2 + (j - i - 1)];
+          else v = th[j * B - j * (j + 1) / 2 + (i - j - 1)];
+        } else {
+          v = g.in[(int64_t)blk * g.in_stride + (int64_t)i * g.in_ld + j];
+        }
+        acc[ti][tj][r] = v;
+      }
+
+  for (int p = 0; p < B / 32; ++p) {
+    const int K0 = 32 * p;
+    // ---- (a) publish the old column and row panels
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < TT; ++tj) {
+        const int I0 = tr + 32 * ti, J0 = tc + 32 * tj;
+        if (J0 == K0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = I0 + c32_row(lane, r);
+            const float v = acc[ti][tj][r];
+            if constexpr (X6) {
+              const float x = -v;
+              const bf16 h = (bf16)x;
+              const float r1 = x - (float)h;
+              const bf16 m = (bf16)r1;
+              const bf16 l = (bf16)(r1 - (float)m);
+              OpA[i * HP + lc] = h;
+              OpA[B * HP + i * HP + lc] = m;
+              OpA[2 * B * HP + i * HP + lc] = l;
+            } else {
+              Pcol[i * PC + lc] = v;
+            }
+          }
+        }
+        if (I0 == K0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Prow[c32_row(lane, r) * PR + J0 + lc] = acc[ti][tj][r];
+        }
+      }
+    __syncthreads();
+    // ---- (b) invert the diagonal 32x32 block in place (all threads)
+    for (int e = tid; e < 1024; e += NT) Dm[(e >> 5) * PC + (e & 31)] = Prow[(e >> 5) * PR + K0 + (e & 31)];
+    __syncthreads();
+    for (int k = 0; k < 32; ++k) {
+      const float pinv = 1.0f / Dm[k * PC + k];
+      float nv[(1024 + NT - 1) / NT];
+#pragma unroll
+      for (int q = 0; q < (1024 + NT - 1) / NT; ++q) {
+        const int e = tid + q * NT;
+        if (e < 1024) {
+          const int i = e >> 5, j = e & 31;
+          if (i == k) nv[q] = (j == k) ? pinv : Dm[k * PC + j] * pinv;
+          else {
+            const float f = Dm[i * PC + k];
+            nv[q] = (j == k) ? -f * pinv : Dm[i * PC + j] - f * (Dm[k * PC + j] * pinv);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < (1024 + NT - 1) / NT; ++q) {
+        const int e = tid + q * NT;
+        if (e < 1024) Dm[(e >> 5) * PC + (e & 31)] = nv[q];
+      }
+      __syncthreads();
+    }
+    // ---- (c) new row panel: A[K, j] <- Dinv A[K, j] (j outside K), A[K, K] <- Dinv
+    {
+      constexpr int PER = (32 * B + NT - 1) / NT;
+      float nv[PER];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int e = tid + q * NT;
+        if (e < 32 * B) {
+          const int kk = e / B, j = e % B;
+          float s;
+          if (j >= K0 && j < K0 + 32) s = Dm[kk * PC + (j - K0)];
+          else {
+            s = 0.f;
+#pragma unroll 8
+            for (int t = 0; t < 32; ++t) s += Dm[kk * PC + t] * Prow[t * PR + j];
+          }
+          nv[q] = s;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int e = tid + q * NT;
+        if (e < 32 * B) {
+          const int kk = e / B, j = e % B;
+          Prow[kk * PR + j] = nv[q];
+          if constexpr (X6) {
+            const float x = nv[q];
+            const bf16 h = (bf16)x;
+            const float r1 = x - (float)h;
+            const bf16 m = (bf16)r1;
+            const bf16 l = (bf16)(r1 - (float)m);
+            OpB[j * HP + kk] = h;
+            OpB[B * HP + j * HP + kk] = m;
+            OpB[2 * B * HP + j * HP + kk] = l;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // ---- (d) update every tile
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < TT; ++tj) {
+        const int I0 = tr + 32 * ti, J0 = tc + 32 * tj;
+        if (J0 == K0) {
+          // column panel: A[K, K] <- Dinv, A[i, K] <- -A[i, K] Dinv
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = I0 + c32_row(lane, r);
+            float v;
+            if (I0 == K0) v = Dm[(i - K0) * PC + lc];
+            else {
+              float s = 0.f;
+#pragma unroll 8
+              for (int t = 0; t < 32; ++t) s += pcol(i, t) * Dm[t * PC + lc];
+              v = -s;
+            }
+            acc[ti][tj][r] = v;
+          }
+        } else if (I0 == K0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[ti][tj][r] = Prow[c32_row(lane, r) * PR + J0 + lc];
+        } else {
+          if constexpr (X6) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              const int ko = 16 * s + 8 * (lane >> 5);
+              bf16x8 a[3], b[3];
+#pragma unroll
+              for (int q = 0; q < 3; ++q) {
+                a[q] = *reinterpret_cast<const bf16x8*>(&OpA[q * B * HP + (I0 + lc) * HP + ko]);
+                b[q] = *reinterpret_cast<const bf16x8*>(&OpB[q * B * HP + (J0 + lc) * HP + ko]);
+              }
+              // order-2 terms first, then order 1, then the leading product
+              acc[ti][tj] = mfma32(a[0], b[2], acc[ti][tj]);
+              acc[ti][tj] = mfma32(a[1], b[1], acc[ti][tj]);
+              acc[ti][tj] = mfma32(a[2], b[0], acc[ti][tj]);
+              acc[ti][tj] = mfma32(a[0], b[1], acc[ti][tj]);
+              acc[ti][tj] = mfma32(a[1], b[0], acc[ti][tj]);
+              acc[ti][tj] = mfma32(a[0], b[0], acc[ti][tj]);
+            }
+          } else {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+              const int kk = 2 * s + (lane >> 5);
+              const float a = -Pcol[(I0 + lc) * PC + kk];
+              const float bb = Prow[kk * PR + J0 + lc];
+              acc[ti][tj] = mfma32f(a, bb, acc[ti][tj]);
+            }
+          }
+        }
+      }
+    __syncthreads();
+  }
+
+  // ---- outputs: M to a strided matrix, or Q = 2M - I in the requested layouts
+#pragma unroll
+  for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < TT; ++tj) {
+      const int I0 = tr + 32 * ti, J0 = tc + 32 * tj;
+      const int j = J0 + lc;
+      if (g.out) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = I0 + c32_row(lane, r);
+          g.out[(int64_t)blk * g.out_stride + (int64_t)i * g.out_ld + j] = acc[ti][tj][r];
+        }
+      }
+      const int64_t base = (int64_t)blk * B * B;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint16_t qb[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 4 * r4 + rr;
+          const int i = I0 + c32_row(lane, r);
+          const float q = 2.0f * acc[ti][tj][r] - (i == j ? 1.0f : 0.0f);
+          if (g.q32) g.q32[base + (int64_t)i * B + j] = q;
+          qb[rr] = f32_to_bits(q);
+          if (g.qbf) g.qbf[base + (int64_t)i * B + j] = qb[rr];
+        }
+        if (g.qtbf) {
+          const int i0 = I0 + c32_row(lane, 4 * r4);
+          uint2 v;
+          v.x = pack2(qb[0], qb[1]);
+          v.y = pack2(qb[2], qb[3]);
+          *reinterpret_cast<uint2*>(&g.qtbf[base + (int64_t)j * B + i0]) = v;
+        }
+      }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Batched small fp32 GEMM: C = alpha * opA * opB + beta * C per batch item,
+// opA = A or A^T (+ I), opB = B or B^T (+ I).  64x64 tiles, 4 waves of 32x32,
+// K in chunks of 32.  MODE 0: fp32 MFMA; MODE 3 / 6: operands split into 2 / 3
+// bf16 pieces and the 3 / 6 leading cross products accumulated on bf16 MFMA
+// (relative error about 2^-17 / 2^-26 per product).
+// M, N, K are multiples of 32.
+// ----------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
+  constexpr int HP = 40;
+  constexpr int FP = 33;
+  constexpr int NS = MODE == 0 ? 0 : (MODE == 3 ? 2 : 3);   // bf16 pieces per operand
+  __shared__ bf16 Ah[NS ? NS * 64 * HP : 2];
+  __shared__ bf16 Bh[NS ? NS * 64 * HP : 2];
+  __shared__ float Af[NS ? 1 : 64 * FP];
+  __shared__ float Bf[NS ? 1 : 64 * FP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
+  const int64_t bz = blockIdx.z;
+  const float* A = a.A + bz * a.sA;
+  const float* Bm = a.B + bz * a.sB;
+  float* C = a.C + bz * a.sC;
+  const bool active = (row0 + 32 * wi < a.M) && (col0 + 32 * wj < a.N);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  auto put = [&](bf16* dst, int idx, float v) {
+    const bf16 h = (bf16)v;
+    dst[idx] = h;
+    if constexpr (NS >= 2) {
+      const float r1 = v - (float)h;
+      const bf16 m = (bf16)r1;
+      dst[64 * HP + idx] = m;
+      if constexpr (NS == 3) dst[2 * 64 * HP + idx] = (bf16)(r1 - (float)m);
+    }
+  };
+  for (int k0 = 0; k0 < a.K; k0 += 32) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = tid + 256 * q;
+      // element of opA: consecutive threads walk the contiguous dimension
+      const int ia = a.transA ? (e & 63) : (e >> 5);
+      const int ka = a.transA ? (e >> 6) : (e & 31);
+      const int gi = row0 + ia, gka = k0 + ka;
+      float va = 0.f;
+      if (gi < a.M) {
+        va = a.transA ? A[(int64_t)gka * a.lda + gi] : A[(int64_t)gi * a.lda + gka];
+        if (a.addIA && gi == gka) va += 1.0f;
+      }
+      // element of opB
+      const int jb = a.transB ? (e >> 5) : (e & 63);
+      const int kb = a.transB ? (e & 31) : (e >> 6);
+      const int gj = col0 + jb, gkb = k0 + kb;
+      float vb = 0.f;
+      if (gj < a.N) {
+        vb = a.transB ? Bm[(int64_t)gj * a.ldb + gkb] : Bm[(int64_t)gkb * a.ldb + gj];
+        if (a.addIB && gkb == gj) vb += 1.0f;
+      }
+      if constexpr (NS) {
+        put(Ah, ia * HP + ka, va);
+        put(Bh, jb * HP + kb, vb);
+      } else {
+        Af[ia * FP + ka] = va;
+        Bf[jb * FP + kb] = vb;
+      }
+    }
+    __syncthreads();
+    if (active) {
+      const int lc = lane & 31;
+      if constexpr (NS) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int ko = 16 * s + 8 * (lane >> 5);
+          bf16x8 x[NS], y[NS];
+#pragma unroll
+          for (int q = 0; q < NS; ++q) {
+            x[q] = *reinterpret_cast<const bf16x8*>(&Ah[q * 64 * HP + (32 * wi + lc) * HP + ko]);
+            y[q] = *reinterpret_cast<const bf16x8*>(&Bh[q * 64 * HP + (32 * wj + lc) * HP + ko]);
+          }
+          if constexpr (NS == 3) {
+            acc = mfma32(x[0], y[2], acc);
+            acc = mfma32(x[1], y[1], acc);
+            acc = mfma32(x[2], y[0], acc);
+          }
+          acc = mfma32(x[0], y[1], acc);
+          acc = mfma32(x[1], y[0], acc);
+          acc = mfma32(x[0], y[0], acc);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          const int kk = 2 * s + (lane >> 5);
+          acc = mfma32f(Af[(32 * wi + lc) * FP + kk], Bf[(32 * wj + lc) * FP + kk], acc);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (active) {
+    const int j = col0 + 32 * wj + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = row0 + 32 * wi + c32_row(lane, r);
+      float* cp = C + (int64_t)i * a.ldc + j;
+      const float old = (a.beta != 0.f) ? *cp : 0.f;
+      *cp = a.alpha * acc[r] + a.beta * old;
+    }
+  }
+}
+
+// I - S for a batch of b x b blocks (b = 512 route), fp32 [blk][b][b]
+__global__ void unpack_eye_minus_s_kernel(const float* __restrict__ theta, int b, float* __restrict__ A) {
+  const int blk = blockIdx.y;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)b * b) return;
+  const int i = (int)(e / b), j = (int)(e % b);
+  const float* th = theta + (int64_t)blk * (b * (b - 1) / 2);
+  float v;
+  if (i == j) v = 1.f;
+  else if (i < j) v = -th[i * b - i * (i + 1) / 2 + (j - i - 1)];
+  else v = th[j * b - j * (j + 1) / 2 + (i - j - 1)];
+  A[(int64_t)blk * b * b + e] = v;
+}
+
+// Q = 2M - I from M [blk][b][b] into Q32 / Qbf16 / QTbf16 (32x32 LDS transpose)
+__global__ __launch_bounds__(256) void finalize_q_kernel(const float* __restrict__ M, int b, float* q32,
+                                                         uint16_t* qbf, uint16_t* qtbf) {
+  __shared__ uint16_t t[32][33];
+  const int blk = blockIdx.z;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 8 rows per pass
+  const int64_t base = (int64_t)blk * b * b;
+  for (int r = ty; r < 32; r += 8) {
+    const int i = i0 + r, j = j0 + tx;
+    const float q = 2.f * M[base + (int64_t)i * b + j] - (i == j ? 1.f : 0.f);
+    if (q32) q32[base + (int64_t)i * b + j] = q;
+    const uint16_t h = f32_to_bits(q);
+    if (qbf) qbf[base + (int64_t)i * b + j] = h;
+    t[r][tx] = h;
+  }
+  __syncthreads();
+  if (qtbf)
+    for (int r = ty; r < 32; r += 8) qtbf[base + (int64_t)(j0 + r) * b + i0 + tx] = t[tx][r];
+}
+
+// dtheta[blk][p(i,j)] (+)= GS[i][j] - GS[j][i], i < j.  grid (ceil(b/256), b-1, nblk)
+__global__ void skew_project_kernel(const float* __restrict__ GS, int b, float* __restrict__ dth, int accumulate) {
+  const int blk = blockIdx.z, i = blockIdx.y;
+  const int j = i + 1 + blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= b) return;
+  const float* g = GS + (int64_t)blk * b * b;
+  const float v = g[(int64_t)i * b + j] - g[(int64_t)j * b + i];
+  float* d = dth + (int64_t)blk * (b * (b - 1) / 2) + (i * b - i * (i + 1) / 2 + (j - i - 1));
+  *d = accumulate ? (*d + v) : v;
+}
+
+// ----------------------------------------------------------------------------
+// host launchers
+// ----------------------------------------------------------------------------
+template <int B, int MODE>
+static void launch_gj_t(int nblk, const GJArgs& g, hipStream_t s) {
+  hipLaunchKernelGGL((gj_kernel<B, MODE>), dim3(nblk), dim3(GJShape<B>::NT), 0, s, g);
+}
+
+void launch_gj(int B, int mode, int nblk, const GJArgs& g, hipStream_t s) {
+  if (nblk <= 0) return;
+  const bool x6 = mode == 6;
+  switch (B) {
+    case 32: x6 ? launch_gj_t<32, 6>(nblk, g, s) : launch_gj_t<32, 0>(nblk, g, s); break;
+    case 64: x6 ? launch_gj_t<64, 6>(nblk, g, s) : launch_gj_t<64, 0>(nblk, g, s); break;
+    case 128: x6 ? launch_gj_t<128, 6>(nblk, g, s) : launch_gj_t<128, 0>(nblk, g, s); break;
+    case 256: x6 ? launch_gj_t<256, 6>(nblk, g, s) : launch_gj_t<256, 0>(nblk, g, s); break;
+    default: break;
+  }
+}
+
+void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s) {
+  if (batch <= 0) return;
+  dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, batch);
+  if (mode == 6) hipLaunchKernelGGL(bgemm_kernel<6>, grid, dim3(256), 0, s, a);
+  else if (mode == 3) hipLaunchKernelGGL(bgemm_kernel<3>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(bgemm_kernel<0>, grid, dim3(256), 0, s, a);
+}
+
+void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s) {
+  if (nblk <= 0) return;
+  dim3 grid((unsigned)(((int64_t)b * b + 255) / 256), nblk);
+  hipLaunchKernelGGL(unpack_eye_minus_s_kernel, grid, dim3(256), 0, s, theta, b, A);
+}
+
+void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qbf, uint16_t* qtbf, hipStream_t s) {
+  if (nblk <= 0) return;
+  dim3 grid(b / 32, b / 32, nblk);
+  hipLaunchKernelGGL(finalize_q_kernel, grid, dim3(256), 0, s, M, b, q32, qbf, qtbf);
+}
+
+void launch_skew_project(const float* GS, int b, int nblk, float* dth, int accumulate, hipStream_t s) {
+  if (nblk <= 0) return;
+  dim3 grid((b + 255) / 256, b - 1, nblk);
+  hipLaunchKernelGGL(skew_project_kernel, grid, dim3(256), 0, s, GS, b, dth, accumulate);
+}
+
+}  // namespace poetx

@@ -1,0 +1,86 @@
+// Kernel argument structs and host-side launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace poetx {
+
+// ---- Cayley builder (build.hip)
+struct GJArgs {
+  const float* theta;   // theta mode: [blk][b(b-1)/2]; nullptr selects matrix mode
+  const float* in;      // matrix mode input
+  int64_t in_stride;
+  int in_ld;
+  float* out;           // optional M output (strided)
+  int64_t out_stride;
+  int out_ld;
+  float* q32;           // optional Q = 2M - I outputs, [blk][B][B]
+  uint16_t* qbf;
+  uint16_t* qtbf;
+};
+// mode 0: fp32 MFMA trailing updates; mode 6: split bf16 x6 (fp32-level accuracy)
+void launch_gj(int B, int mode, int nblk, const GJArgs& g, hipStream_t s);
+
+struct BGemmArgs {
+  int M, N, K;
+  const float* A; int64_t sA; int lda; int transA; int addIA;
+  const float* B; int64_t sB; int ldb; int transB; int addIB;
+  float* C; int64_t sC; int ldc;
+  float alpha, beta;
+};
+// mode 0: fp32 MFMA; 3 / 6: split bf16 x3 / x6
+void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s);
+void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s);
+void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qbf, uint16_t* qtbf, hipStream_t s);
+void launch_skew_project(const float* GS, int b, int nblk, float* dth, int accumulate, hipStream_t s);
+
+// ---- block transforms (transform.hip)
+// gather-in : out[t][l*B+i] = sum_kk in[t][perm[l*B+kk]] * Mq(kk, i); tail copies in[t][perm[j]]
+// scatter-out: out[t][perm[l*B+i]] = sum_kk in[t][l*B+kk] * Mq(kk, i); tail copies in[t][j]
+// with Mq(kk, i) = bq[l][i][kk] (bf16 path) or, for fp32, q[l][i][kk] (trans=0) / q[l][kk][i] (trans=1)
+struct XformArgs {
+  const void* in;
+  void* out;
+  void* emit;           // gather-in only: gathered copy of in (nullable)
+  const int32_t* perm;
+  const void* bq;
+  int64_t N;
+  int W, B, k;
+  int trans;            // fp32 only
+};
+// returns false if no kernel configuration fits this shape
+bool launch_gather_in_bf16(const XformArgs& a, hipStream_t s);
+bool launch_scatter_out_bf16(const XformArgs& a, hipStream_t s);
+void launch_gather_in_f32(const XformArgs& a, hipStream_t s);
+void launch_scatter_out_f32(const XformArgs& a, hipStream_t s);
+
+// ---- dense GEMMs (gemm.hip): C[M][N] = A[M][K] * op(B)
+// nt: B is [N][K] (C = A B^T); nn: B is [K][N] (C = A B)
+void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N,
+                      int64_t K, hipStream_t s);
+void launch_gemm_f32(bool nn, const float* A, const float* Bm, float* C, int64_t M, int64_t N, int64_t K,
+                     hipStream_t s);
+
+// ---- block Gram reduction (gram.hip): G[l][i][j] = sum_t A[t][l*B+i] * C[t][l*B+j]
+size_t gram_partials_bytes(int64_t N, int B, int k, bool f32);
+void launch_gram(bool f32, const void* A, const void* C, int64_t N, int W, int B, int k, float* G, void* partials,
+                 hipStream_t s);
+
+// ---- merge (merge.hip)
+// V = D_R W D_P on b x b tiles of the working-layout weight W [m][n]:
+//   bf16: qr = Q_R bf16 row-major [kR][b][b], qpt = Q_P^T bf16 [kP][b][b]
+//   f32 : qr = Q_R fp32, qpt = Q_P fp32 (row-major, not transposed)
+void launch_merge_tiles(bool f32, const void* W, void* V, const void* qr, const void* qpt, int64_t m, int64_t n, int b,
+                        int kR, int kP, hipStream_t s);
+void launch_perm_keys_rank(uint64_t seed, uint64_t merge_index, int side, int64_t n, uint64_t* keys, int32_t* out,
+                           hipStream_t s);
+void launch_invert_perm(const int32_t* p, int64_t n, int32_t* inv, hipStream_t s);
+void launch_relayout(bool f32, const void* V, void* W, const int32_t* sinv_old, const int32_t* snew,
+                     const int32_t* tinv_old, const int32_t* tnew, int64_t m, int64_t n, hipStream_t s);
+void launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
+void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+void launch_adam(float* theta, const float* grad, float* m, float* v, int64_t n, float lr, float b1, float b2,
+                 float eps, float bc1, float bc2, hipStream_t s);
+
+}  // namespace poetx
