@@ -1,0 +1,232 @@
+"""Benchmark: POET-X layer fwd+bwd tokens/s on one MI355X.
+
+Workload (default): the LLaMA-1B-shaped layer set -- q, k, v, o 2048x2048,
+gate, up 5632x2048, down 2048x5632 -- bf16 W0, block size 256, 8192 tokens,
+generators ~N(0, 1e-3).  One step is the hot path over one batch: forward of
+all seven matrices, then backward of all seven (reverse order) with the
+blocks and activations recomputed, generator gradients for every block and
+the input gradient.  Inputs are seeded synthetic tensors already resident in
+HBM before the timed region.
+
+Prints one JSON line.  Besides the throughput it reports, for the kernel class
+with the largest share of the step ("dominant"), the achieved rate from HIP
+events recorded on the launch stream inside the library against the MI355X
+peak (bf16 MFMA 2.5 PFLOP/s dense, HBM 8 TB/s), the HBM traffic measured by
+rocprofv3 counters when a matching record exists under profiles/, and the
+float64 oracle timed on the host cores on a bounded token sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+MFMA_CLASSES = ("gemm_nt", "gemm_nn")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=None, help="override the token count (default 8192)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=512, help="token sample of the oracle baseline")
+    ap.add_argument("--profile-steps", type=int, default=3)
+    return ap.parse_args()
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "orthogonal_reparameterized_poetx_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(cls):
+    """HBM bytes per launch from a committed rocprofv3 counter record, if its
+    kernel source hash still matches the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % cls)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash(rec.get("source_files", [])):
+        return None
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workloads as WL
+    import orthogonal_reparameterized_poetx_amd as P
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = WL.CONFIGS[3]
+    N = args.tokens or cfg["N"]
+
+    def up(pair, dt):
+        a = np.ascontiguousarray(pair[0])
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a.astype(np.float32)).to(dev)
+
+    # ---- resident inputs: seven packed layers, their inputs and upstream grads
+    layers, Xs, gYs, outs = [], {}, [], []
+    for j in range(len(cfg["mats"])):
+        inp = WL.matrix_inputs(3, j, N=N)
+        lay = P.PoetxLayer(inp["m"], inp["n"], inp["b"], "bf16", dev, perm_seed=inp["perm_seed"])
+        lay.pack(up(inp["W0"], "bf16"))
+        lay.thR.copy_(up(inp["thR"], "f32"))
+        lay.thP.copy_(up(inp["thP"], "f32"))
+        owner = WL.input_owner(cfg, j)
+        if owner not in Xs:
+            Xs[owner] = up(inp["X"], "bf16")
+        lay.x_key = owner
+        gYs.append(up(inp["gY"], "bf16"))
+        outs.append(dict(Y=torch.empty(N, inp["m"], dtype=torch.bfloat16, device=dev),
+                         dX=torch.empty(N, inp["n"], dtype=torch.bfloat16, device=dev),
+                         dR=torch.empty_like(lay.thR), dP=torch.empty_like(lay.thP)))
+        layers.append(lay)
+        # allocate workspaces up front (nothing is allocated in the timed region)
+        lay.workspace(P.OP_FORWARD, N)
+        lay.workspace(P.OP_BACKWARD, N)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for lay, o in zip(layers, outs):
+            lay.forward(Xs[lay.x_key], Y=o["Y"])
+        for lay, g, o in zip(reversed(layers), reversed(gYs), reversed(outs)):
+            lay.backward(Xs[lay.x_key], g, dX=o["dX"], dthR=o["dR"], dthP=o["dP"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-kernel breakdown (separate pass: events around every launch)
+    P.timing_enable(True)
+    for _ in range(args.profile_steps):
+        step()
+    torch.cuda.synchronize()
+    kern = P.timing_summary()
+    P.timing_enable(False)
+    per_step = {k: dict(v, ms=v["ms"] / args.profile_steps, launches=v["launches"] / args.profile_steps,
+                        flops=v["flops"] / args.profile_steps, bytes=v["bytes"] / args.profile_steps)
+                for k, v in kern.items()}
+    dom = max(per_step, key=lambda k: per_step[k]["ms"])
+    d = per_step[dom]
+    if dom in MFMA_CLASSES or dom in ("cayley_build", "chain_rule"):
+        achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    else:
+        achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = round(d["ms"] / max(d["launches"], 1), 4)
+    rec = traffic_record(dom)
+    roof["traffic"] = None if rec is None else rec["hbm_bytes_per_launch"]
+    breakdown = {}
+    for k, v in sorted(per_step.items(), key=lambda kv: -kv[1]["ms"]):
+        e = dict(ms=round(v["ms"], 4), launches=round(v["launches"], 2))
+        if v["flops"] > 0:
+            e["tflops"] = round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1)
+        if v["bytes"] > 0:
+            e["gbs"] = round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)
+        breakdown[k] = e
+
+    # ---- merge of the whole layer set (periodic: not part of a step)
+    for lay in layers:
+        lay.workspace(P.OP_MERGE)
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for lay in layers:
+        lay.merge()
+    e3.record(stream)
+    torch.cuda.synchronize()
+    merge_ms = e2.elapsed_time(e3)
+
+    result = {
+        "metric": "POET-X layer fwd+bwd tokens/sec and % of MFMA/HBM roofline, 1 GPU",
+        "value": round(N / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs with the layer set's shapes)",
+        "config": {"workload": cfg["name"], "tokens": N, "matrices": len(cfg["mats"]), "b": cfg["b"],
+                   "shapes": ["%dx%d" % (m, n) for _, m, n in cfg["mats"]]},
+        "roofline": roof,
+        "kernels_per_step": breakdown,
+        "merge_ms_layer_set": round(merge_ms, 3),
+    }
+
+    # ---- float64 oracle on the host cores, bounded token sample
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(ntok):
+    import numpy as np
+
+    import oracle
+    import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = WL.CONFIGS[3]
+    rows = np.arange(ntok)
+    # time only the oracle calls (input generation excluded)
+    tot = 0.0
+    for j in range(len(cfg["mats"])):
+        inp = WL.matrix_inputs(3, j, rows=rows)
+        s = oracle.make_permutation(inp["perm_seed"], 0, 0, inp["m"])
+        t = oracle.make_permutation(inp["perm_seed"], 0, 1, inp["n"])
+        a = (inp["W0"][1], inp["thR"][1], inp["thP"][1], s, t, inp["X"][1])
+        ts = time.perf_counter()
+        oracle.forward(*a, inp["b"], contract=True)
+        oracle.backward(*a, inp["gY"][1], inp["b"], contract=True)
+        tot += time.perf_counter() - ts
+    return {"value": round(ntok / tot, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "float64 oracle (bf16 contract mode), fwd+bwd of all 7 layer-set matrices on the first %d "
+                      "of the 8192 tokens; %.1f s; per-step block builds and chain rule included once" % (ntok, tot)}
+
+
+if __name__ == "__main__":
+    main()

@@ -191,6 +191,20 @@ int poetx_adam_step(float* theta, const float* grad, float* m, float* v, int64_t
 /* Message of the last error on this thread ("" if none). */
 const char* poetx_last_error(void);
 
+/*
+ * Diagnostics (not part of the method): per-kernel timing for measurement.
+ * poetx_timing_enable(1) clears the record and starts recording a HIP event
+ * pair on the caller's stream around every kernel the library launches,
+ * together with the launch's algorithmic flops and HBM bytes; (0) stops.
+ * poetx_timing_summary synchronizes the recorded events and writes one line
+ * per kernel class, "name launches total_ms flops bytes\n", into buf (host,
+ * len bytes, NUL-terminated); returns the number of classes or a negative
+ * status.  Recording adds host work per launch; leave it off when timing
+ * whole steps.  Not thread-safe.
+ */
+int poetx_timing_enable(int on);
+int poetx_timing_summary(char* buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,8 @@ from ._lib import (  # noqa: F401
     poetx_forward,
     poetx_make_permutation,
     poetx_merge,
+    timing_enable,
+    timing_summary,
     workspace_bytes,
 )
 from .layer import PoetxLayer  # noqa: F401,E402

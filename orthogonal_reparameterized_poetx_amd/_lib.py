@@ -22,7 +22,7 @@ _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDT
 
 EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
             "poetx_forward", "poetx_backward", "poetx_merge", "poetx_make_permutation",
-            "poetx_adam_step", "poetx_last_error")
+            "poetx_adam_step", "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
 
 
 class Layer(ctypes.Structure):
@@ -76,6 +76,8 @@ def lib():
         "poetx_adam_step": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_float, vp]),
         "poetx_last_error": (ctypes.c_char_p, []),
+        "poetx_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+        "poetx_timing_summary": (ctypes.c_int, [ctypes.c_char_p, sz]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -160,3 +162,20 @@ def poetx_adam_step(theta, grad, m, v, count, step, lr=1e-3, beta1=0.9, beta2=0.
     _check("poetx_adam_step", lib().poetx_adam_step(_ptr(theta), _ptr(grad), _ptr(m), _ptr(v), int(count), int(step),
                                                     float(lr), float(beta1), float(beta2), float(eps),
                                                     _stream(stream)))
+
+
+def timing_enable(on):
+    _check("poetx_timing_enable", lib().poetx_timing_enable(1 if on else 0))
+
+
+def timing_summary():
+    """{kernel class: dict(launches, ms, flops, bytes)} of the recorded launches."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().poetx_timing_summary(buf, len(buf))
+    if n < 0:
+        raise PoetxError("poetx_timing_summary", n, last_error())
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms, fl, by = line.split()
+        out[name] = dict(launches=int(cnt), ms=float(ms), flops=float(fl), bytes=float(by))
+    return out

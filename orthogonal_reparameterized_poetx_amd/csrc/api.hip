@@ -37,6 +37,41 @@ int check_launch(const char* what) {
   return POETX_OK;
 }
 
+// ---- optional per-launch timing (diagnostics)
+struct TimingRec {
+  const char* name;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+
+void clear_timing() {
+  for (auto& r : g_recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_recs.clear();
+}
+
+// Records an event pair around the launches issued during its lifetime.
+struct Tm {
+  bool on;
+  size_t idx;
+  hipStream_t s;
+  Tm(hipStream_t st, const char* name, double flops, double bytes) : on(g_timing), idx(0), s(st) {
+    if (!on) return;
+    TimingRec r{name, nullptr, nullptr, flops, bytes};
+    if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) { on = false; return; }
+    (void)hipEventRecord(r.a, s);
+    g_recs.push_back(r);
+    idx = g_recs.size() - 1;
+  }
+  ~Tm() {
+    if (on) (void)hipEventRecord(g_recs[idx].b, s);
+  }
+};
+
 constexpr int64_t kMaxDim = 32768;
 constexpr size_t kAlign = 256;
 
@@ -89,6 +124,7 @@ size_t build_ws_bytes(int64_t nblk, int b) {
 int build(const float* theta, int64_t nblk, int b, float* q32, uint16_t* qbf, uint16_t* qtbf, void* ws, int mode,
           hipStream_t s) {
   if (nblk <= 0) return POETX_OK;
+  Tm tm(s, "cayley_build", 2.0 * b * (double)b * b * nblk, 0.0);
   if (b <= 256) {
     GJArgs g{};
     g.theta = theta;
@@ -146,6 +182,7 @@ int build(const float* theta, int64_t nblk, int b, float* q32, uint16_t* qbf, ui
 int chain(float* G, const float* q32, float* tmp, int64_t nblk, int b, float* dth, bool accumulate, int mode,
           hipStream_t s) {
   if (nblk <= 0) return POETX_OK;
+  Tm tm(s, "chain_rule", 4.0 * b * (double)b * b * nblk, 0.0);
   const int64_t sb = (int64_t)b * b;
   BGemmArgs q{};
   q.M = q.N = q.K = b;
@@ -164,6 +201,9 @@ int chain(float* G, const float* q32, float* tmp, int64_t nblk, int b, float* dt
   launch_skew_project(G, b, (int)nblk, dth, accumulate ? 1 : 0, s);
   return check_launch("chain rule");
 }
+
+// block-product flops of one transform: N tokens x k blocks x 2 b^2
+double xf_flops(int64_t N, int k, int b) { return 2.0 * N * k * (double)b * b; }
 
 struct Shape {
   int64_t m, n, N;
@@ -352,18 +392,27 @@ int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR, c
   // z1' = D_P (Pi_tau x): gather by tau, multiply by Q_P^T per block
   XformArgs p{};
   p.in = X; p.out = w.z1; p.emit = nullptr; p.perm = tau; p.N = N; p.W = (int)S.n; p.B = S.b; p.k = S.kP;
-  if (S.f32) { p.bq = w.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
-  else { p.bq = w.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld b=%d", (long long)S.n, S.b); }
+  {
+    Tm tm(s, "xform_gather_in", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
+    if (S.f32) { p.bq = w.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
+    else { p.bq = w.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld b=%d", (long long)S.n, S.b); }
+  }
   if ((rc = check_launch("P-side transform"))) return rc;
   // z2' = z1' W0p^T
-  if (S.f32) launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
-  else launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
+  {
+    Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+    if (S.f32) launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
+    else launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
+  }
   if ((rc = check_launch("forward GEMM"))) return rc;
   // y = Pi_sigma^T (D_R z2'): multiply by Q_R^T per block, scatter by sigma
   XformArgs r{};
   r.in = w.z2; r.out = Y; r.perm = sigma; r.N = N; r.W = (int)S.m; r.B = S.b; r.k = S.kR;
-  if (S.f32) { r.bq = w.q32R; r.trans = 0; launch_scatter_out_f32(r, s); }
-  else { r.bq = w.qbR; if (!launch_scatter_out_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld b=%d", (long long)S.m, S.b); }
+  {
+    Tm tm(s, "xform_scatter_out", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
+    if (S.f32) { r.bq = w.q32R; r.trans = 0; launch_scatter_out_f32(r, s); }
+    else { r.bq = w.qbR; if (!launch_scatter_out_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld b=%d", (long long)S.m, S.b); }
+  }
   return check_launch("R-side transform");
 }
 
@@ -404,27 +453,50 @@ int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, 
   // recompute z1' (and keep the gathered x' for dL/dQ_P), then z2'
   XformArgs p{};
   p.in = X; p.out = w.z1; p.emit = w.xg; p.perm = tau; p.N = N; p.W = (int)S.n; p.B = S.b; p.k = S.kP;
-  if (S.f32) { p.bq = w.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
-  else { p.bq = w.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
-  if (S.f32) launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
-  else launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
+  {
+    // recompute pass: algorithmic bytes are the read of X and the write of z1'
+    Tm tm(s, "xform_gather_in", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
+    if (S.f32) { p.bq = w.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
+    else { p.bq = w.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
+  }
+  {
+    Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+    if (S.f32) launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
+    else launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
+  }
   if ((rc = check_launch("recompute"))) return rc;
   // R side: gY' = Pi_sigma gY (kept), gz2' = D_R^T gY' (blocks Q_R), G_R = gY'^T z2'
   XformArgs r{};
   r.in = dY; r.out = w.gz2; r.emit = w.gyg; r.perm = sigma; r.N = N; r.W = (int)S.m; r.B = S.b; r.k = S.kR;
-  if (S.f32) { r.bq = w.q32R; r.trans = 1; launch_gather_in_f32(r, s); }
-  else { r.bq = w.qtR; if (!launch_gather_in_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld", (long long)S.m); }
-  launch_gram(S.f32, w.gyg, w.z2, N, (int)S.m, S.b, S.kR, w.GR, w.part, s);
+  {
+    // algorithmic bytes: read gY, write gz2' (the gathered copy is implementation traffic)
+    Tm tm(s, "xform_gather_in", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
+    if (S.f32) { r.bq = w.q32R; r.trans = 1; launch_gather_in_f32(r, s); }
+    else { r.bq = w.qtR; if (!launch_gather_in_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld", (long long)S.m); }
+  }
+  {
+    // algorithmic bytes: the read of z2' (gY is counted with the transform)
+    Tm tm(s, "gram", xf_flops(N, S.kR, S.b), 1.0 * N * S.m * S.es);
+    launch_gram(S.f32, w.gyg, w.z2, N, (int)S.m, S.b, S.kR, w.GR, w.part, s);
+  }
   if ((rc = check_launch("R-side backward"))) return rc;
   // gz1' = gz2' W0p (into the z1' buffer)
   void* gz1 = w.z1;
-  if (S.f32) launch_gemm_f32(true, (const float*)w.gz2, (const float*)W0p, (float*)gz1, N, S.n, S.m, s);
-  else launch_gemm_bf16(true, (const uint16_t*)w.gz2, (const uint16_t*)W0p, (uint16_t*)gz1, N, S.n, S.m, s);
+  {
+    Tm tm(s, "gemm_nn", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+    if (S.f32) launch_gemm_f32(true, (const float*)w.gz2, (const float*)W0p, (float*)gz1, N, S.n, S.m, s);
+    else launch_gemm_bf16(true, (const uint16_t*)w.gz2, (const uint16_t*)W0p, (uint16_t*)gz1, N, S.n, S.m, s);
+  }
   // P side: G_P = gz1'^T x', dX = Pi_tau^T D_P^T gz1'
-  launch_gram(S.f32, gz1, w.xg, N, (int)S.n, S.b, S.kP, w.GP, w.part, s);
+  {
+    // algorithmic bytes: the read of x (gz1' is counted with the dX transform)
+    Tm tm(s, "gram", xf_flops(N, S.kP, S.b), 1.0 * N * S.n * S.es);
+    launch_gram(S.f32, gz1, w.xg, N, (int)S.n, S.b, S.kP, w.GP, w.part, s);
+  }
   if (dX) {
     XformArgs q{};
     q.in = gz1; q.out = dX; q.perm = tau; q.N = N; q.W = (int)S.n; q.B = S.b; q.k = S.kP;
+    Tm tm(s, "xform_scatter_out", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
     if (S.f32) { q.bq = w.q32P; q.trans = 1; launch_scatter_out_f32(q, s); }
     else { q.bq = w.qtP; if (!launch_scatter_out_bf16(q, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
   }
@@ -455,6 +527,7 @@ int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int
   } else {
     if ((rc = build(thR, S.kR, S.b, nullptr, w.qbR, nullptr, w.bws, bmode, s))) return rc;
     if ((rc = build(thP, S.kP, S.b, nullptr, nullptr, w.qtP, w.bws, bmode, s))) return rc;
+    Tm tm(s, "merge_tiles", 4.0 * S.m * S.n * S.b, 2.0 * S.m * S.n * S.es);
     launch_merge_tiles(false, W0p, w.V, w.qbR, w.qtP, S.m, S.n, S.b, S.kR, S.kP, s);
   }
   if ((rc = check_launch("merge tiles"))) return rc;
@@ -463,7 +536,10 @@ int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int
   launch_perm_keys_rank(perm_seed, merge_index, 1, S.n, w.keys, w.tnew, s);
   launch_invert_perm(sigma, S.m, w.sinv, s);
   launch_invert_perm(tau, S.n, w.tinv, s);
-  launch_relayout(S.f32, w.V, W0p, w.sinv, w.snew, w.tinv, w.tnew, S.m, S.n, s);
+  {
+    Tm tm(s, "merge_relayout", 0.0, 2.0 * S.m * S.n * S.es);
+    launch_relayout(S.f32, w.V, W0p, w.sinv, w.snew, w.tinv, w.tnew, S.m, S.n, s);
+  }
   launch_copy_i32(w.snew, sigma, S.m, s);
   launch_copy_i32(w.tnew, tau, S.n, s);
   launch_fill_f32(thR, 0.f, (int64_t)S.kR * (S.b * (S.b - 1) / 2), s);
@@ -492,8 +568,41 @@ int poetx_adam_step(float* theta, const float* grad, float* m, float* v, int64_t
   if (!theta || !grad || !m || !v) return fail(POETX_EINVAL, "NULL tensor argument");
   const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
   const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
-  launch_adam(theta, grad, m, v, count, lr, beta1, beta2, eps, (float)bc1, (float)bc2, static_cast<hipStream_t>(stream));
+  {
+    Tm tm(static_cast<hipStream_t>(stream), "adam", 0.0, 7.0 * 4.0 * count);
+    launch_adam(theta, grad, m, v, count, lr, beta1, beta2, eps, (float)bc1, (float)bc2,
+                static_cast<hipStream_t>(stream));
+  }
   return check_launch("adam");
+}
+
+int poetx_timing_enable(int on) {
+  clear_timing();
+  g_timing = on != 0;
+  return POETX_OK;
+}
+
+int poetx_timing_summary(char* buf, size_t len) {
+  if (!buf || len == 0) return fail(POETX_EINVAL, "NULL buffer");
+  struct Agg { std::string name; int n; double ms, flops, bytes; };
+  std::vector<Agg> agg;
+  for (auto& r : g_recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(POETX_EHIP, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(POETX_EHIP, "event elapsed time failed");
+    auto it = std::find_if(agg.begin(), agg.end(), [&](const Agg& a) { return a.name == r.name; });
+    if (it == agg.end()) { agg.push_back({r.name, 0, 0, 0, 0}); it = agg.end() - 1; }
+    it->n += 1; it->ms += ms; it->flops += r.flops; it->bytes += r.bytes;
+  }
+  std::string out;
+  char line[256];
+  for (auto& a : agg) {
+    snprintf(line, sizeof line, "%s %d %.6f %.6e %.6e\n", a.name.c_str(), a.n, a.ms, a.flops, a.bytes);
+    out += line;
+  }
+  if (out.size() + 1 > len) return fail(POETX_EINVAL, "buffer too small (%zu bytes needed)", out.size() + 1);
+  memcpy(buf, out.c_str(), out.size() + 1);
+  return (int)agg.size();
 }
 
 }  // extern "C"
