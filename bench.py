@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=512, help="token sample of the oracle baseline")
     ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--per-layer-builds", action="store_true",
+                    help="let every forward / backward call build its own blocks (one builder launch per call) "
+                         "instead of one batched build per pass")
     return ap.parse_args()
 
 
@@ -106,17 +109,35 @@ def main():
                          dX=torch.empty(N, inp["n"], dtype=torch.bfloat16, device=dev),
                          dR=torch.empty_like(lay.thR), dP=torch.empty_like(lay.thP)))
         layers.append(lay)
-        # allocate workspaces up front (nothing is allocated in the timed region)
-        lay.workspace(P.OP_FORWARD, N)
-        lay.workspace(P.OP_BACKWARD, N)
+        # allocate workspaces and block buffers up front (nothing is allocated in the timed region)
+        if args.per_layer_builds:
+            lay.workspace(P.OP_FORWARD, N)
+            lay.workspace(P.OP_BACKWARD, N)
+        else:
+            lay.workspace(P.OP_FORWARD_BLOCKS, N)
+            lay.workspace(P.OP_BACKWARD_BLOCKS, N)
+            lay.block_buffers("forward")
+            lay.block_buffers("backward")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step_per_layer():
         for lay, o in zip(layers, outs):
             lay.forward(Xs[lay.x_key], Y=o["Y"])
         for lay, g, o in zip(reversed(layers), reversed(gYs), reversed(outs)):
             lay.backward(Xs[lay.x_key], g, dX=o["dX"], dthR=o["dR"], dthP=o["dP"])
+
+    def step_batched():
+        # blocks of all seven matrices in one build per pass; the backward pass
+        # rebuilds them from the generators instead of keeping the forward's
+        P.build_layer_blocks(layers, "forward")
+        for lay, o in zip(layers, outs):
+            lay.forward_blocks(Xs[lay.x_key], Y=o["Y"])
+        P.build_layer_blocks(layers, "backward")
+        for lay, g, o in zip(reversed(layers), reversed(gYs), reversed(outs)):
+            lay.backward_blocks(Xs[lay.x_key], g, dX=o["dX"], dthR=o["dR"], dthP=o["dP"])
+
+    step = step_per_layer if args.per_layer_builds else step_batched
 
     for _ in range(args.warmup):
         step()
@@ -188,7 +209,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian inputs with the layer set's shapes)",
         "config": {"workload": cfg["name"], "tokens": N, "matrices": len(cfg["mats"]), "b": cfg["b"],
-                   "shapes": ["%dx%d" % (m, n) for _, m, n in cfg["mats"]]},
+                   "shapes": ["%dx%d" % (m, n) for _, m, n in cfg["mats"]],
+                   "block_builds": "per layer call" if args.per_layer_builds else "batched per pass"},
         "roofline": roof,
         "kernels_per_step": breakdown,
         "merge_ms_layer_set": round(merge_ms, 3),

@@ -81,6 +81,8 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
 #define POETX_OP_FORWARD 0
 #define POETX_OP_BACKWARD 1
 #define POETX_OP_MERGE 2
+#define POETX_OP_FORWARD_BLOCKS 3  /* poetx_forward_blocks  */
+#define POETX_OP_BACKWARD_BLOCKS 4 /* poetx_backward_blocks */
 
 typedef struct {
   int64_t m;      /* rows of W0 = output features                         */
@@ -98,7 +100,40 @@ typedef struct {
 size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op);
 
 /*
- * Bytes of workspace poetx_build_blocks needs for nblocks blocks of size b.
+ * One batch of Cayley blocks for poetx_build_block_sets: the generators of
+ * nblocks blocks and where their Q goes (layouts as in poetx_build_blocks).
+ */
+typedef struct {
+  const float* theta; /* [nblocks][b(b-1)/2] fp32, device                  */
+  int64_t nblocks;    /* >= 0                                              */
+  float* Q32;         /* [nblocks][b][b] fp32 Q, device, nullable          */
+  void* Qbf16;        /* [nblocks][b][b] bf16 Q, device, nullable          */
+  void* QTbf16;       /* [nblocks][b][b] bf16 Q^T, device, nullable        */
+} poetx_block_set;
+
+/*
+ * Prebuilt Cayley blocks of one layer for poetx_forward_blocks and
+ * poetx_backward_blocks, each [k][b][b] row-major on the device (R side:
+ * k = k_R, P side: k = k_P).  Which are read:
+ *   fp32 layer, forward and backward: Q32R, Q32P;
+ *   bf16 layer, forward:  QR, QP (bf16 Q);
+ *   bf16 layer, backward: Q32R, Q32P (fp32 Q, for the chain rule), QP,
+ *                         QTR, QTP (bf16 Q^T).
+ * The others may be NULL.
+ */
+typedef struct {
+  const float* Q32R;
+  const float* Q32P;
+  const void* QR;
+  const void* QP;
+  const void* QTR;
+  const void* QTP;
+} poetx_blocks;
+
+/*
+ * Bytes of workspace poetx_build_blocks needs for nblocks blocks of size b;
+ * for poetx_build_block_sets, pass the largest nblocks of its sets.  Zero
+ * for b <= 256.
  */
 size_t poetx_build_workspace_bytes(int64_t nblocks, int32_t b);
 
@@ -118,6 +153,20 @@ int poetx_build_blocks(const float* theta, int64_t nblocks, int32_t b, float* Q3
                        void* Qbf16, void* QTbf16, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * a1-a2 over several independent batches at once (e.g. the R and P sides of
+ * every layer of a model): the same blocks poetx_build_blocks gives for each
+ * set, with the sets of one call sharing kernel launches so that the grid
+ * covers the blocks of all of them.  The pages fuse the block builds to cut
+ * launches and data movement [P3 item 4; P1 实践 2].
+ *   sets   host array of count poetx_block_set (count in [0, 4096]); every
+ *          set has the same block size b
+ *   ws     poetx_build_workspace_bytes(max nblocks over the sets, b) bytes
+ * Output buffers must not overlap each other or any theta.
+ */
+int poetx_build_block_sets(const poetx_block_set* sets, int32_t count, int32_t b, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
  * a3-a5: forward Y = X W^T, W = R W0 P, computed input-centrically as
  * P, then W0, then R on each token [P3 item 1], with P and R applied as
  * gathers/scatters and batched block products [P3 items 2-3].
@@ -130,6 +179,17 @@ int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR,
                   const float* thP, const int32_t* sigma, const int32_t* tau,
                   const void* X, int64_t N, void* Y, void* ws, size_t ws_bytes,
                   void* stream);
+
+/*
+ * poetx_forward with the Cayley blocks built beforehand (poetx_build_blocks
+ * or poetx_build_block_sets from the layer's current generators): a3-a5
+ * only.  Same arguments and results as poetx_forward, with the generators
+ * replaced by the blocks (poetx_blocks above).  Workspace:
+ * poetx_workspace_bytes(layer, N, POETX_OP_FORWARD_BLOCKS).
+ */
+int poetx_forward_blocks(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                         const int32_t* sigma, const int32_t* tau, const void* X, int64_t N,
+                         void* Y, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * a0, a6-a9: backward of L = <dY, Y> with W0 frozen.  The Cayley blocks and
@@ -147,6 +207,19 @@ int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR,
                    const float* thP, const int32_t* sigma, const int32_t* tau,
                    const void* X, const void* dY, int64_t N, void* dX, float* dthR,
                    float* dthP, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * poetx_backward with the Cayley blocks built beforehand (the caller
+ * rebuilds them from the generators for the backward pass, which keeps the
+ * blocks recomputed rather than held from the forward pass [P3 item 5]):
+ * a0, a6-a9 with the same arguments and results as poetx_backward, the
+ * generators replaced by the blocks.  Workspace:
+ * poetx_workspace_bytes(layer, N, POETX_OP_BACKWARD_BLOCKS).
+ */
+int poetx_backward_blocks(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                          const int32_t* sigma, const int32_t* tau, const void* X, const void* dY,
+                          int64_t N, void* dX, float* dthR, float* dthP, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /*
  * a10-a11: merge W0 <- R W0 P [P3 item 1], then theta_R, theta_P <- 0 and
@@ -197,7 +270,7 @@ const char* poetx_last_error(void);
  * pair on the caller's stream around every kernel the library launches,
  * together with the launch's algorithmic flops and HBM bytes; (0) stops.
  * poetx_timing_summary synchronizes the recorded events and writes one line
- * per kernel class, "name launches total_ms flops bytes\n", into buf (host,
+ * per kernel class, "name launches total_ms flops bytes" and a newline, into buf (host,
  * len bytes, NUL-terminated); returns the number of classes or a negative
  * status.  Recording adds host work per launch; leave it off when timing
  * whole steps.  Not thread-safe.

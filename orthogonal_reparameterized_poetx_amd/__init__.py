@@ -9,25 +9,33 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     OP_BACKWARD,
+    OP_BACKWARD_BLOCKS,
     OP_FORWARD,
+    OP_FORWARD_BLOCKS,
     OP_MERGE,
     POETX_ACCUMULATE_GRAD,
     POETX_BF16,
     POETX_F32,
+    Blocks,
+    BlockSet,
     Layer,
     PoetxError,
     build_workspace_bytes,
     last_error,
     lib,
+    make_blocks,
     make_workspace,
     poetx_adam_step,
     poetx_backward,
+    poetx_backward_blocks,
+    poetx_build_block_sets,
     poetx_build_blocks,
     poetx_forward,
+    poetx_forward_blocks,
     poetx_make_permutation,
     poetx_merge,
     timing_enable,
     timing_summary,
     workspace_bytes,
 )
-from .layer import PoetxLayer  # noqa: F401,E402
+from .layer import PoetxLayer, build_layer_blocks  # noqa: F401,E402

@@ -15,14 +15,15 @@ LIB_PATH = os.path.join(_HERE, "libpoetx.so")
 POETX_F32 = 0
 POETX_BF16 = 1
 POETX_ACCUMULATE_GRAD = 1
-OP_FORWARD, OP_BACKWARD, OP_MERGE = 0, 1, 2
+OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS = 0, 1, 2, 3, 4
 
 _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDTYPE",
            -4: "POETX_EWORKSPACE", -5: "POETX_EHIP"}
 
 EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
-            "poetx_forward", "poetx_backward", "poetx_merge", "poetx_make_permutation",
-            "poetx_adam_step", "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
+            "poetx_build_block_sets", "poetx_forward", "poetx_forward_blocks", "poetx_backward",
+            "poetx_backward_blocks", "poetx_merge", "poetx_make_permutation", "poetx_adam_step",
+            "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
 
 
 class Layer(ctypes.Structure):
@@ -46,6 +47,26 @@ class Layer(ctypes.Structure):
         return self.b * (self.b - 1) // 2
 
 
+class BlockSet(ctypes.Structure):
+    """poetx_block_set: one batch of generators and where its Q goes."""
+    _fields_ = [("theta", ctypes.c_void_p), ("nblocks", ctypes.c_int64), ("Q32", ctypes.c_void_p),
+                ("Qbf16", ctypes.c_void_p), ("QTbf16", ctypes.c_void_p)]
+
+
+class Blocks(ctypes.Structure):
+    """poetx_blocks: prebuilt Cayley blocks of one layer."""
+    _fields_ = [("Q32R", ctypes.c_void_p), ("Q32P", ctypes.c_void_p), ("QR", ctypes.c_void_p),
+                ("QP", ctypes.c_void_p), ("QTR", ctypes.c_void_p), ("QTP", ctypes.c_void_p)]
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_blocks(Q32R=None, Q32P=None, QR=None, QP=None, QTR=None, QTP=None):
+    return Blocks(_addr(Q32R), _addr(Q32P), _addr(QR), _addr(QP), _addr(QTR), _addr(QTP))
+
+
 class PoetxError(RuntimeError):
     def __init__(self, fn, code, msg):
         super().__init__("%s failed: %s (%d): %s" % (fn, _STATUS.get(code, "?"), code, msg))
@@ -65,12 +86,16 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, u64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
     LP = ctypes.POINTER(Layer)
+    BP = ctypes.POINTER(Blocks)
     sig = {
         "poetx_workspace_bytes": (sz, [LP, i64, ctypes.c_int]),
         "poetx_build_workspace_bytes": (sz, [i64, i32]),
         "poetx_build_blocks": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
+        "poetx_build_block_sets": (ctypes.c_int, [ctypes.POINTER(BlockSet), i32, i32, vp, sz, vp]),
         "poetx_forward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
+        "poetx_forward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, i64, vp, vp, sz, vp]),
         "poetx_backward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "poetx_backward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_merge": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
         "poetx_make_permutation": (ctypes.c_int, [u64, u64, i32, i64, vp]),
         "poetx_adam_step": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float,
@@ -129,6 +154,29 @@ def poetx_build_blocks(theta, nblocks, b, Q32=None, Qbf16=None, QTbf16=None, ws=
     nb = ws.numel() if ws is not None else 0
     _check("poetx_build_blocks", lib().poetx_build_blocks(_ptr(theta), int(nblocks), int(b), _ptr(Q32), _ptr(Qbf16),
                                                           _ptr(QTbf16), _ptr(ws), nb, _stream(stream)))
+
+
+def poetx_build_block_sets(sets, b, ws=None, stream=None):
+    """sets: sequence of (theta, nblocks, Q32, Qbf16, QTbf16) with tensors or None."""
+    arr = (BlockSet * max(len(sets), 1))()
+    for i, (th, nb, q32, qbf, qt) in enumerate(sets):
+        arr[i] = BlockSet(_addr(th), int(nb), _addr(q32), _addr(qbf), _addr(qt))
+    nbytes = ws.numel() if ws is not None else 0
+    _check("poetx_build_block_sets", lib().poetx_build_block_sets(arr, len(sets), int(b), _ptr(ws), nbytes,
+                                                                  _stream(stream)))
+
+
+def poetx_forward_blocks(layer, W0p, blocks, sigma, tau, X, N, Y, ws, stream=None):
+    _check("poetx_forward_blocks", lib().poetx_forward_blocks(
+        ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
+        _ptr(X), int(N), _ptr(Y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def poetx_backward_blocks(layer, W0p, blocks, sigma, tau, X, dY, N, dX, dthR, dthP, ws, stream=None):
+    _check("poetx_backward_blocks", lib().poetx_backward_blocks(
+        ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
+        _ptr(X), _ptr(dY), int(N), _ptr(dX), _ptr(dthR), _ptr(dthP), _ptr(ws), ws.numel() if ws is not None else 0,
+        _stream(stream)))
 
 
 def poetx_forward(layer, W0p, thR, thP, sigma, tau, X, N, Y, ws, stream=None):

@@ -118,23 +118,15 @@ size_t build_ws_bytes(int64_t nblk, int b) {
   return a.off + kAlign;
 }
 
-// Cayley blocks.  mode 6: split-bf16 x6 MFMA products (fp32-level accuracy);
-// mode 0: fp32 MFMA.  Both give Q accurate to fp32 rounding, so rounding Q to
-// bf16 agrees with rounding the exact Q except in rare ties at the boundary.
-int build(const float* theta, int64_t nblk, int b, float* q32, uint16_t* qbf, uint16_t* qtbf, void* ws, int mode,
-          hipStream_t s) {
-  if (nblk <= 0) return POETX_OK;
-  Tm tm(s, "cayley_build", 2.0 * b * (double)b * b * nblk, 0.0);
-  if (b <= 256) {
-    GJArgs g{};
-    g.theta = theta;
-    g.q32 = q32;
-    g.qbf = qbf;
-    g.qtbf = qtbf;
-    launch_gj(b, mode, (int)nblk, g, s);
-    return check_launch("cayley builder");
-  }
-  // b = 512: 2x2 block inverse with 256-wide Schur complement.
+// Output layouts wanted for one batch of Cayley blocks.
+struct QOut {
+  float* q32;
+  uint16_t* qbf;
+  uint16_t* qtbf;
+};
+
+int build_schur512(const float* theta, int64_t nblk, QOut o, void* ws, int mode, hipStream_t s) {
+  // 2x2 block inverse with 256-wide Schur complement:
   //   [A B; C D]^-1 = [Ai + Ai B Si C Ai, -Ai B Si; -Si C Ai, Si], Si = (D - C Ai B)^-1
   Arena a(ws);
   float* Af = a.take<float>((size_t)nblk * 512 * 512);
@@ -143,10 +135,15 @@ int build(const float* theta, int64_t nblk, int b, float* q32, uint16_t* qbf, ui
   float* Vm = a.take<float>((size_t)nblk * 256 * 256);
   const int64_t SB = 512 * 512, SH = 256 * 256;
   launch_unpack_eye_minus_s(theta, 512, (int)nblk, Af, s);
-  GJArgs g{};
-  g.in = Af; g.in_stride = SB; g.in_ld = 512;
-  g.out = Mf; g.out_stride = SB; g.out_ld = 512;      // A^-1 into M11
-  launch_gj(256, mode, (int)nblk, g, s);
+  auto gj = [&](float* in, float* out) {
+    GJArgs g{};
+    g.nseg = 1;
+    g.start[0] = 0;
+    g.start[1] = (int)nblk;
+    g.in = in; g.in_stride = SB; g.in_ld = 512;
+    g.out = out; g.out_stride = SB; g.out_ld = 512;
+    launch_gj(256, mode, (int)nblk, g, s);
+  };
   auto gemm = [&](const float* A, int lda, const float* B, int ldb, float* C, int ldc, float alpha, float beta,
                   int64_t sA, int64_t sB, int64_t sC) {
     BGemmArgs q{};
@@ -164,41 +161,90 @@ int build(const float* theta, int64_t nblk, int b, float* q32, uint16_t* qbf, ui
   float* M12 = Mf + 256;
   float* M21 = Mf + 256 * 512;
   float* M22 = Mf + 256 * 512 + 256;
+  gj(Af, M11);                                                    // Ai = A^-1 into M11
   gemm(M11, 512, A12, 512, Tm, 256, 1.f, 0.f, SB, SB, SH);        // T = Ai B
   gemm(A21, 512, Tm, 256, A22, 512, -1.f, 1.f, SB, SH, SB);       // Sc = D - C T
-  GJArgs g2{};
-  g2.in = A22; g2.in_stride = SB; g2.in_ld = 512;
-  g2.out = M22; g2.out_stride = SB; g2.out_ld = 512;               // Si
-  launch_gj(256, mode, (int)nblk, g2, s);
+  gj(A22, M22);                                                   // Si
   gemm(A21, 512, M11, 512, Vm, 256, 1.f, 0.f, SB, SB, SH);        // V = C Ai
   gemm(Tm, 256, M22, 512, M12, 512, -1.f, 0.f, SH, SB, SB);       // M12 = -T Si
   gemm(M22, 512, Vm, 256, M21, 512, -1.f, 0.f, SB, SH, SB);       // M21 = -Si V
   gemm(M12, 512, Vm, 256, M11, 512, -1.f, 1.f, SB, SH, SB);       // M11 = Ai - M12 V
-  launch_finalize_q(Mf, 512, (int)nblk, q32, qbf, qtbf, s);
+  launch_finalize_q(Mf, 512, (int)nblk, o.q32, o.qbf, o.qtbf, s);
   return check_launch("cayley builder (b=512)");
 }
 
-// dtheta from G = dL/dQ:  G_S = 1/2 (I + Q^T) G (I + Q^T);  dtheta_p = G_S[i][j] - G_S[j][i]
-int chain(float* G, const float* q32, float* tmp, int64_t nblk, int b, float* dth, bool accumulate, int mode,
-          hipStream_t s) {
+// Cayley blocks of several independent batches (layers, sides) with as few
+// launches as possible: up to GJ_MAXSEG batches share one Gauss-Jordan launch,
+// so the grid covers the blocks of all of them.  mode 6: split-bf16 x6 MFMA
+// products (fp32-level accuracy); mode 0: fp32 MFMA.  Both give Q accurate
+// to fp32 rounding.  b = 512 goes batch by batch through the Schur path (ws
+// sized for the largest batch).
+int build_sets(const float* const* theta, const int64_t* nblk, const QOut* out, int nsets, int b, void* ws, int mode,
+               hipStream_t s) {
+  int64_t total = 0;
+  for (int i = 0; i < nsets; ++i) total += nblk[i];
+  if (total <= 0) return POETX_OK;
+  Tm tm(s, "cayley_build", 2.0 * b * (double)b * b * total, 0.0);
+  if (b <= 256) {
+    int i = 0;
+    while (i < nsets) {
+      GJArgs g{};
+      int launched = 0;
+      for (; i < nsets && g.nseg < GJ_MAXSEG; ++i) {
+        if (nblk[i] <= 0) continue;
+        g.seg[g.nseg] = GJSeg{theta[i], out[i].q32, out[i].qbf, out[i].qtbf};
+        g.start[g.nseg] = launched;
+        launched += (int)nblk[i];
+        ++g.nseg;
+      }
+      g.start[g.nseg] = launched;
+      if (launched > 0) launch_gj(b, mode, launched, g, s);
+    }
+    return check_launch("cayley builder");
+  }
+  for (int i = 0; i < nsets; ++i) {
+    if (nblk[i] <= 0) continue;
+    const int rc = build_schur512(theta[i], nblk[i], out[i], ws, mode, s);
+    if (rc) return rc;
+  }
+  return POETX_OK;
+}
+
+// a layer's R and P blocks
+int build2(const float* th0, int64_t n0, QOut o0, const float* th1, int64_t n1, QOut o1, int b, void* ws, int mode,
+           hipStream_t s) {
+  const float* th[2] = {th0, th1};
+  const int64_t nb[2] = {n0, n1};
+  const QOut o[2] = {o0, o1};
+  return build_sets(th, nb, o, 2, b, ws, mode, s);
+}
+
+// dtheta from G = dL/dQ:  G_S = 1/2 (I + Q^T) G (I + Q^T);  dtheta_p = G_S[i][j] - G_S[j][i].
+// G holds the R blocks then the P blocks contiguously; the fp32 blocks of the
+// two sides may live apart (q32R, q32P).  Both sides in one pass.
+int chain(float* G, const float* q32R, const float* q32P, float* tmp, int64_t nR, int64_t nP, int b, float* dthR,
+          float* dthP, bool accumulate, int mode, hipStream_t s) {
+  const int64_t nblk = nR + nP;
   if (nblk <= 0) return POETX_OK;
   Tm tm(s, "chain_rule", 4.0 * b * (double)b * b * nblk, 0.0);
   const int64_t sb = (int64_t)b * b;
   BGemmArgs q{};
   q.M = q.N = q.K = b;
   q.A = G; q.sA = sb; q.lda = b;
-  q.B = q32; q.sB = sb; q.ldb = b; q.transB = 1; q.addIB = 1;
+  q.B = q32R; q.sB = sb; q.ldb = b; q.transB = 1; q.addIB = 1;
+  q.B1 = q32P; q.nb0 = (int)nR;
   q.C = tmp; q.sC = sb; q.ldc = b;
   q.alpha = 1.f; q.beta = 0.f;
   launch_bgemm(mode, (int)nblk, q, s);
   BGemmArgs r{};
   r.M = r.N = r.K = b;
-  r.A = q32; r.sA = sb; r.lda = b; r.transA = 1; r.addIA = 1;
+  r.A = q32R; r.sA = sb; r.lda = b; r.transA = 1; r.addIA = 1;
+  r.A1 = q32P; r.nb0 = (int)nR;
   r.B = tmp; r.sB = sb; r.ldb = b;
   r.C = G; r.sC = sb; r.ldc = b;
   r.alpha = 0.5f; r.beta = 0.f;
   launch_bgemm(mode, (int)nblk, r, s);
-  launch_skew_project(G, b, (int)nblk, dth, accumulate ? 1 : 0, s);
+  launch_skew_project(G, b, (int)nblk, dthR, (int)nR, dthP, accumulate ? 1 : 0, s);
   return check_launch("chain rule");
 }
 
@@ -222,24 +268,36 @@ Shape shape_of(const poetx_layer* L, int64_t N) {
   return S;
 }
 
-// ---- workspace plans (same code sizes and carves)
+// Cayley blocks one forward / backward consumes (built by the call itself,
+// or handed in by the caller).  fp32 layers use q32R / q32P only; bf16
+// forward uses qbR, qbP; bf16 backward uses q32R, q32P (chain rule), qbP,
+// qtR and qtP.
+struct Blk {
+  const float *q32R, *q32P;
+  const uint16_t *qbR, *qbP, *qtR, *qtP;
+};
+
+// ---- workspace plans (same code sizes and carves).  own = the call builds
+// its own blocks into the workspace.
 struct FwdWs {
   float *q32R, *q32P;
   uint16_t *qbR, *qbP;
   void* bws;
   void *z1, *z2;
 };
-FwdWs plan_fwd(const Shape& S, void* base, size_t* bytes) {
+FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes) {
   Arena a(base);
   FwdWs w{};
-  if (S.f32) {
-    w.q32R = a.take<float>((size_t)S.kR * S.b * S.b);
-    w.q32P = a.take<float>((size_t)S.kP * S.b * S.b);
-  } else {
-    w.qbR = a.take<uint16_t>((size_t)S.kR * S.b * S.b);
-    w.qbP = a.take<uint16_t>((size_t)S.kP * S.b * S.b);
+  if (own) {
+    if (S.f32) {
+      w.q32R = a.take<float>((size_t)S.kR * S.b * S.b);
+      w.q32P = a.take<float>((size_t)S.kP * S.b * S.b);
+    } else {
+      w.qbR = a.take<uint16_t>((size_t)S.kR * S.b * S.b);
+      w.qbP = a.take<uint16_t>((size_t)S.kP * S.b * S.b);
+    }
+    w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
   }
-  w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
   w.z1 = a.take<char>((size_t)S.N * S.n * S.es);
   w.z2 = a.take<char>((size_t)S.N * S.m * S.es);
   *bytes = a.off + kAlign;
@@ -254,26 +312,28 @@ struct BwdWs {
   float *GR, *GP, *tmp;
   void* part;
 };
-BwdWs plan_bwd(const Shape& S, void* base, size_t* bytes) {
+BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes) {
   Arena a(base);
   BwdWs w{};
   const size_t bb = (size_t)S.b * S.b;
-  w.q32R = a.take<float>(S.kR * bb);
-  w.q32P = a.take<float>(S.kP * bb);
-  if (!S.f32) {
-    w.qbP = a.take<uint16_t>(S.kP * bb);
-    w.qtR = a.take<uint16_t>(S.kR * bb);
-    w.qtP = a.take<uint16_t>(S.kP * bb);
+  if (own) {
+    w.q32R = a.take<float>((S.kR + S.kP) * bb);   // R blocks, then P blocks
+    w.q32P = w.q32R ? w.q32R + S.kR * bb : nullptr;
+    if (!S.f32) {
+      w.qbP = a.take<uint16_t>(S.kP * bb);
+      w.qtR = a.take<uint16_t>(S.kR * bb);
+      w.qtP = a.take<uint16_t>(S.kP * bb);
+    }
+    w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
   }
-  w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
   w.z1 = a.take<char>((size_t)S.N * S.n * S.es);
   w.xg = a.take<char>((size_t)S.N * S.n * S.es);
   w.z2 = a.take<char>((size_t)S.N * S.m * S.es);
   w.gyg = a.take<char>((size_t)S.N * S.m * S.es);
   w.gz2 = a.take<char>((size_t)S.N * S.m * S.es);
-  w.GR = a.take<float>(S.kR * bb);
-  w.GP = a.take<float>(S.kP * bb);
-  w.tmp = a.take<float>(std::max(S.kR, S.kP) * bb);
+  w.GR = a.take<float>((S.kR + S.kP) * bb);     // R blocks, then P blocks
+  w.GP = w.GR ? w.GR + S.kR * bb : nullptr;
+  w.tmp = a.take<float>((S.kR + S.kP) * bb);
   const size_t pb = std::max(gram_partials_bytes(S.N, S.b, S.kR, S.f32), gram_partials_bytes(S.N, S.b, S.kP, S.f32));
   w.part = a.take<char>(pb);
   *bytes = a.off + kAlign;
@@ -324,78 +384,18 @@ uint64_t mix64(uint64_t z) {
   return z ^ (z >> 31);
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* poetx_last_error(void) { return g_err.c_str(); }
-
-size_t poetx_build_workspace_bytes(int64_t nblocks, int32_t b) {
-  if (!valid_b(b) || nblocks < 0) {
-    fail(POETX_EINVAL, "bad build request nblocks=%lld b=%d", (long long)nblocks, b);
-    return 0;
-  }
-  return build_ws_bytes(nblocks, b);
-}
-
-size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op) {
-  if (validate_layer(layer) != POETX_OK) return 0;
-  if (op != POETX_OP_MERGE && validate_N(N) != POETX_OK) return 0;
-  const Shape S = shape_of(layer, op == POETX_OP_MERGE ? 0 : N);
-  size_t bytes = 0;
-  switch (op) {
-    case POETX_OP_FORWARD: plan_fwd(S, nullptr, &bytes); break;
-    case POETX_OP_BACKWARD: plan_bwd(S, nullptr, &bytes); break;
-    case POETX_OP_MERGE: plan_merge(S, nullptr, &bytes); break;
-    default: fail(POETX_EINVAL, "unknown op %d", op); return 0;
-  }
-  return bytes;
-}
-
-int poetx_build_blocks(const float* theta, int64_t nblocks, int32_t b, float* Q32, void* Qbf16, void* QTbf16,
-                       void* ws, size_t ws_bytes, void* stream) {
-  if (!valid_b(b)) return fail(POETX_EINVAL, "block size b=%d not in {32,64,128,256,512}", b);
-  if (nblocks < 0 || nblocks > (int64_t(1) << 20)) return fail(POETX_ESHAPE, "nblocks=%lld", (long long)nblocks);
-  if (nblocks == 0) return POETX_OK;
-  if (!theta) return fail(POETX_EINVAL, "theta is NULL");
-  if (!Q32 && !Qbf16 && !QTbf16) return fail(POETX_EINVAL, "no output requested");
-  const int rc = check_ws(ws, ws_bytes, build_ws_bytes(nblocks, b));
-  if (rc) return rc;
-  return build(theta, nblocks, b, Q32, static_cast<uint16_t*>(Qbf16), static_cast<uint16_t*>(QTbf16), ws, 6,
-               static_cast<hipStream_t>(stream));
-}
-
-int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR, const float* thP,
-                  const int32_t* sigma, const int32_t* tau, const void* X, int64_t N, void* Y, void* ws,
-                  size_t ws_bytes, void* stream) {
-  int rc = validate_layer(layer);
-  if (rc) return rc;
-  if ((rc = validate_N(N))) return rc;
-  if (N == 0) return POETX_OK;
-  const Shape S = shape_of(layer, N);
-  if (!W0p || !sigma || !tau || !X || !Y) return fail(POETX_EINVAL, "NULL tensor argument");
-  if ((S.kR > 0 && !thR) || (S.kP > 0 && !thP)) return fail(POETX_EINVAL, "NULL generator");
-  size_t need = 0;
-  plan_fwd(S, nullptr, &need);
-  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  FwdWs w = plan_fwd(S, ws, &need);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int bmode = S.f32 ? 0 : 6;
-  // Cayley blocks (recomputed every call; nothing is cached between calls)
-  if (S.f32) {
-    if ((rc = build(thR, S.kR, S.b, w.q32R, nullptr, nullptr, w.bws, bmode, s))) return rc;
-    if ((rc = build(thP, S.kP, S.b, w.q32P, nullptr, nullptr, w.bws, bmode, s))) return rc;
-  } else {
-    if ((rc = build(thR, S.kR, S.b, nullptr, w.qbR, nullptr, w.bws, bmode, s))) return rc;
-    if ((rc = build(thP, S.kP, S.b, nullptr, w.qbP, nullptr, w.bws, bmode, s))) return rc;
-  }
+// forward after the blocks exist: a3, a4, a5
+int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
+             void* Y, const FwdWs& w, hipStream_t s) {
+  const int64_t N = S.N;
+  int rc;
   // z1' = D_P (Pi_tau x): gather by tau, multiply by Q_P^T per block
   XformArgs p{};
   p.in = X; p.out = w.z1; p.emit = nullptr; p.perm = tau; p.N = N; p.W = (int)S.n; p.B = S.b; p.k = S.kP;
   {
     Tm tm(s, "xform_gather_in", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
-    if (S.f32) { p.bq = w.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
-    else { p.bq = w.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld b=%d", (long long)S.n, S.b); }
+    if (S.f32) { p.bq = q.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
+    else { p.bq = q.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld b=%d", (long long)S.n, S.b); }
   }
   if ((rc = check_launch("P-side transform"))) return rc;
   // z2' = z1' W0p^T
@@ -410,54 +410,26 @@ int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR, c
   r.in = w.z2; r.out = Y; r.perm = sigma; r.N = N; r.W = (int)S.m; r.B = S.b; r.k = S.kR;
   {
     Tm tm(s, "xform_scatter_out", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
-    if (S.f32) { r.bq = w.q32R; r.trans = 0; launch_scatter_out_f32(r, s); }
-    else { r.bq = w.qbR; if (!launch_scatter_out_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld b=%d", (long long)S.m, S.b); }
+    if (S.f32) { r.bq = q.q32R; r.trans = 0; launch_scatter_out_f32(r, s); }
+    else { r.bq = q.qbR; if (!launch_scatter_out_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld b=%d", (long long)S.m, S.b); }
   }
   return check_launch("R-side transform");
 }
 
-int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, const float* thP,
-                   const int32_t* sigma, const int32_t* tau, const void* X, const void* dY, int64_t N, void* dX,
-                   float* dthR, float* dthP, void* ws, size_t ws_bytes, void* stream) {
-  int rc = validate_layer(layer);
-  if (rc) return rc;
-  if ((rc = validate_N(N))) return rc;
-  const Shape S = shape_of(layer, N);
-  if (N > 0 && (!W0p || !sigma || !tau || !X || !dY)) return fail(POETX_EINVAL, "NULL tensor argument");
-  if ((S.kR > 0 && (!thR || !dthR)) || (S.kP > 0 && (!thP || !dthP)))
-    return fail(POETX_EINVAL, "NULL generator or generator gradient");
-  const bool accum = (layer->flags & POETX_ACCUMULATE_GRAD) != 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t ntR = (int64_t)S.kR * (S.b * (S.b - 1) / 2), ntP = (int64_t)S.kP * (S.b * (S.b - 1) / 2);
-  if (N == 0) {
-    if (!accum) {
-      launch_fill_f32(dthR, 0.f, ntR, s);
-      launch_fill_f32(dthP, 0.f, ntP, s);
-    }
-    return check_launch("zero gradients");
-  }
-  size_t need = 0;
-  plan_bwd(S, nullptr, &need);
-  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  BwdWs w = plan_bwd(S, ws, &need);
-  const int bmode = S.f32 ? 0 : 6;   // Cayley builder
+// backward after the blocks exist: a0 (recompute), a6, a7, a8, a9
+int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
+             const void* dY, void* dX, float* dthR, float* dthP, bool accum, const BwdWs& w, hipStream_t s) {
+  const int64_t N = S.N;
   const int cmode = S.f32 ? 0 : 3;   // chain-rule products
-  // recompute the blocks (not stored between forward and backward)
-  if (S.f32) {
-    if ((rc = build(thR, S.kR, S.b, w.q32R, nullptr, nullptr, w.bws, bmode, s))) return rc;
-    if ((rc = build(thP, S.kP, S.b, w.q32P, nullptr, nullptr, w.bws, bmode, s))) return rc;
-  } else {
-    if ((rc = build(thR, S.kR, S.b, w.q32R, nullptr, w.qtR, w.bws, bmode, s))) return rc;
-    if ((rc = build(thP, S.kP, S.b, w.q32P, w.qbP, w.qtP, w.bws, bmode, s))) return rc;
-  }
+  int rc;
   // recompute z1' (and keep the gathered x' for dL/dQ_P), then z2'
   XformArgs p{};
   p.in = X; p.out = w.z1; p.emit = w.xg; p.perm = tau; p.N = N; p.W = (int)S.n; p.B = S.b; p.k = S.kP;
   {
     // recompute pass: algorithmic bytes are the read of X and the write of z1'
     Tm tm(s, "xform_gather_in", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
-    if (S.f32) { p.bq = w.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
-    else { p.bq = w.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
+    if (S.f32) { p.bq = q.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
+    else { p.bq = q.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
   }
   {
     Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
@@ -471,8 +443,8 @@ int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, 
   {
     // algorithmic bytes: read gY, write gz2' (the gathered copy is implementation traffic)
     Tm tm(s, "xform_gather_in", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
-    if (S.f32) { r.bq = w.q32R; r.trans = 1; launch_gather_in_f32(r, s); }
-    else { r.bq = w.qtR; if (!launch_gather_in_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld", (long long)S.m); }
+    if (S.f32) { r.bq = q.q32R; r.trans = 1; launch_gather_in_f32(r, s); }
+    else { r.bq = q.qtR; if (!launch_gather_in_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld", (long long)S.m); }
   }
   {
     // algorithmic bytes: the read of z2' (gY is counted with the transform)
@@ -494,17 +466,210 @@ int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, 
     launch_gram(S.f32, gz1, w.xg, N, (int)S.n, S.b, S.kP, w.GP, w.part, s);
   }
   if (dX) {
-    XformArgs q{};
-    q.in = gz1; q.out = dX; q.perm = tau; q.N = N; q.W = (int)S.n; q.B = S.b; q.k = S.kP;
+    XformArgs t{};
+    t.in = gz1; t.out = dX; t.perm = tau; t.N = N; t.W = (int)S.n; t.B = S.b; t.k = S.kP;
     Tm tm(s, "xform_scatter_out", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
-    if (S.f32) { q.bq = w.q32P; q.trans = 1; launch_scatter_out_f32(q, s); }
-    else { q.bq = w.qtP; if (!launch_scatter_out_bf16(q, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
+    if (S.f32) { t.bq = q.q32P; t.trans = 1; launch_scatter_out_f32(t, s); }
+    else { t.bq = q.qtP; if (!launch_scatter_out_bf16(t, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
   }
   if ((rc = check_launch("P-side backward"))) return rc;
   // chain rule through the Cayley map onto the stored upper triangle
-  if ((rc = chain(w.GR, w.q32R, w.tmp, S.kR, S.b, dthR, accum, cmode, s))) return rc;
-  if ((rc = chain(w.GP, w.q32P, w.tmp, S.kP, S.b, dthP, accum, cmode, s))) return rc;
+  return chain(w.GR, q.q32R, q.q32P, w.tmp, S.kR, S.kP, S.b, dthR, dthP, accum, cmode, s);
+}
+
+// shared argument checks of forward / forward_blocks
+int check_fwd_args(const poetx_layer* layer, int64_t N, const void* W0p, const int32_t* sigma, const int32_t* tau,
+                   const void* X, const void* Y) {
+  int rc = validate_layer(layer);
+  if (rc) return rc;
+  if ((rc = validate_N(N))) return rc;
+  if (N > 0 && (!W0p || !sigma || !tau || !X || !Y)) return fail(POETX_EINVAL, "NULL tensor argument");
   return POETX_OK;
+}
+
+int check_bwd_args(const poetx_layer* layer, int64_t N, const void* W0p, const int32_t* sigma, const int32_t* tau,
+                   const void* X, const void* dY, const float* dthR, const float* dthP) {
+  int rc = validate_layer(layer);
+  if (rc) return rc;
+  if ((rc = validate_N(N))) return rc;
+  const Shape S = shape_of(layer, N);
+  if (N > 0 && (!W0p || !sigma || !tau || !X || !dY)) return fail(POETX_EINVAL, "NULL tensor argument");
+  if ((S.kR > 0 && !dthR) || (S.kP > 0 && !dthP)) return fail(POETX_EINVAL, "NULL generator gradient");
+  return POETX_OK;
+}
+
+// gradient reset of an empty backward
+int zero_grads(const Shape& S, bool accum, float* dthR, float* dthP, hipStream_t s) {
+  if (!accum) {
+    launch_fill_f32(dthR, 0.f, (int64_t)S.kR * (S.b * (S.b - 1) / 2), s);
+    launch_fill_f32(dthP, 0.f, (int64_t)S.kP * (S.b * (S.b - 1) / 2), s);
+  }
+  return check_launch("zero gradients");
+}
+
+int check_blocks(const Shape& S, const poetx_blocks* q, bool backward) {
+  if (!q) return fail(POETX_EINVAL, "blocks is NULL");
+  const bool R = S.kR > 0, P = S.kP > 0;
+  if (S.f32 || backward) {
+    if ((R && !q->Q32R) || (P && !q->Q32P)) return fail(POETX_EINVAL, "NULL fp32 blocks (Q32R / Q32P)");
+  }
+  if (!S.f32 && !backward && ((R && !q->QR) || (P && !q->QP)))
+    return fail(POETX_EINVAL, "NULL bf16 blocks (QR / QP)");
+  if (!S.f32 && backward && ((P && !q->QP) || (R && !q->QTR) || (P && !q->QTP)))
+    return fail(POETX_EINVAL, "NULL bf16 blocks (QP / QTR / QTP)");
+  return POETX_OK;
+}
+
+Blk blk_of(const poetx_blocks* q) {
+  return Blk{q->Q32R, q->Q32P, static_cast<const uint16_t*>(q->QR), static_cast<const uint16_t*>(q->QP),
+             static_cast<const uint16_t*>(q->QTR), static_cast<const uint16_t*>(q->QTP)};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* poetx_last_error(void) { return g_err.c_str(); }
+
+size_t poetx_build_workspace_bytes(int64_t nblocks, int32_t b) {
+  if (!valid_b(b) || nblocks < 0) {
+    fail(POETX_EINVAL, "bad build request nblocks=%lld b=%d", (long long)nblocks, b);
+    return 0;
+  }
+  return build_ws_bytes(nblocks, b);
+}
+
+size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op) {
+  if (validate_layer(layer) != POETX_OK) return 0;
+  if (op != POETX_OP_MERGE && validate_N(N) != POETX_OK) return 0;
+  const Shape S = shape_of(layer, op == POETX_OP_MERGE ? 0 : N);
+  size_t bytes = 0;
+  switch (op) {
+    case POETX_OP_FORWARD: plan_fwd(S, true, nullptr, &bytes); break;
+    case POETX_OP_BACKWARD: plan_bwd(S, true, nullptr, &bytes); break;
+    case POETX_OP_FORWARD_BLOCKS: plan_fwd(S, false, nullptr, &bytes); break;
+    case POETX_OP_BACKWARD_BLOCKS: plan_bwd(S, false, nullptr, &bytes); break;
+    case POETX_OP_MERGE: plan_merge(S, nullptr, &bytes); break;
+    default: fail(POETX_EINVAL, "unknown op %d", op); return 0;
+  }
+  return bytes;
+}
+
+int poetx_build_blocks(const float* theta, int64_t nblocks, int32_t b, float* Q32, void* Qbf16, void* QTbf16,
+                       void* ws, size_t ws_bytes, void* stream) {
+  poetx_block_set set{theta, nblocks, Q32, Qbf16, QTbf16};
+  return poetx_build_block_sets(&set, 1, b, ws, ws_bytes, stream);
+}
+
+int poetx_build_block_sets(const poetx_block_set* sets, int32_t count, int32_t b, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!valid_b(b)) return fail(POETX_EINVAL, "block size b=%d not in {32,64,128,256,512}", b);
+  if (count < 0 || count > 4096) return fail(POETX_ESHAPE, "count=%d out of range [0, 4096]", count);
+  if (count > 0 && !sets) return fail(POETX_EINVAL, "sets is NULL");
+  int64_t total = 0, largest = 0;
+  for (int i = 0; i < count; ++i) {
+    const poetx_block_set& t = sets[i];
+    if (t.nblocks < 0 || t.nblocks > (int64_t(1) << 20))
+      return fail(POETX_ESHAPE, "set %d: nblocks=%lld", i, (long long)t.nblocks);
+    if (t.nblocks == 0) continue;
+    if (!t.theta) return fail(POETX_EINVAL, "set %d: theta is NULL", i);
+    if (!t.Q32 && !t.Qbf16 && !t.QTbf16) return fail(POETX_EINVAL, "set %d: no output requested", i);
+    total += t.nblocks;
+    largest = std::max(largest, t.nblocks);
+  }
+  if (total > (int64_t(1) << 24)) return fail(POETX_ESHAPE, "%lld blocks in one call", (long long)total);
+  if (total == 0) return POETX_OK;
+  const int rc = check_ws(ws, ws_bytes, build_ws_bytes(largest, b));
+  if (rc) return rc;
+  std::vector<const float*> th((size_t)count);
+  std::vector<int64_t> nb((size_t)count);
+  std::vector<QOut> out((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    th[(size_t)i] = sets[i].theta;
+    nb[(size_t)i] = sets[i].nblocks;
+    out[(size_t)i] = QOut{sets[i].Q32, static_cast<uint16_t*>(sets[i].Qbf16), static_cast<uint16_t*>(sets[i].QTbf16)};
+  }
+  return build_sets(th.data(), nb.data(), out.data(), count, b, ws, 6, static_cast<hipStream_t>(stream));
+}
+
+int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR, const float* thP,
+                  const int32_t* sigma, const int32_t* tau, const void* X, int64_t N, void* Y, void* ws,
+                  size_t ws_bytes, void* stream) {
+  int rc = check_fwd_args(layer, N, W0p, sigma, tau, X, Y);
+  if (rc) return rc;
+  if (N == 0) return POETX_OK;
+  const Shape S = shape_of(layer, N);
+  if ((S.kR > 0 && !thR) || (S.kP > 0 && !thP)) return fail(POETX_EINVAL, "NULL generator");
+  size_t need = 0;
+  plan_fwd(S, true, nullptr, &need);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const FwdWs w = plan_fwd(S, true, ws, &need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bmode = S.f32 ? 0 : 6;
+  // Cayley blocks (recomputed every call; nothing is cached between calls)
+  if (S.f32) rc = build2(thR, S.kR, QOut{w.q32R, nullptr, nullptr}, thP, S.kP, QOut{w.q32P, nullptr, nullptr}, S.b,
+                       w.bws, bmode, s);
+  else rc = build2(thR, S.kR, QOut{nullptr, w.qbR, nullptr}, thP, S.kP, QOut{nullptr, w.qbP, nullptr}, S.b, w.bws,
+                   bmode, s);
+  if (rc) return rc;
+  return fwd_core(S, W0p, Blk{w.q32R, w.q32P, w.qbR, w.qbP, nullptr, nullptr}, sigma, tau, X, Y, w, s);
+}
+
+int poetx_forward_blocks(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                         const int32_t* sigma, const int32_t* tau, const void* X, int64_t N, void* Y, void* ws,
+                         size_t ws_bytes, void* stream) {
+  int rc = check_fwd_args(layer, N, W0p, sigma, tau, X, Y);
+  if (rc) return rc;
+  const Shape S = shape_of(layer, N);
+  if ((rc = check_blocks(S, blocks, false))) return rc;
+  if (N == 0) return POETX_OK;
+  size_t need = 0;
+  plan_fwd(S, false, nullptr, &need);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const FwdWs w = plan_fwd(S, false, ws, &need);
+  return fwd_core(S, W0p, blk_of(blocks), sigma, tau, X, Y, w, static_cast<hipStream_t>(stream));
+}
+
+int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, const float* thP,
+                   const int32_t* sigma, const int32_t* tau, const void* X, const void* dY, int64_t N, void* dX,
+                   float* dthR, float* dthP, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_bwd_args(layer, N, W0p, sigma, tau, X, dY, dthR, dthP);
+  if (rc) return rc;
+  const Shape S = shape_of(layer, N);
+  if ((S.kR > 0 && !thR) || (S.kP > 0 && !thP)) return fail(POETX_EINVAL, "NULL generator");
+  const bool accum = (layer->flags & POETX_ACCUMULATE_GRAD) != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) return zero_grads(S, accum, dthR, dthP, s);
+  size_t need = 0;
+  plan_bwd(S, true, nullptr, &need);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const BwdWs w = plan_bwd(S, true, ws, &need);
+  const int bmode = S.f32 ? 0 : 6;   // Cayley builder
+  // recompute the blocks (not stored between forward and backward)
+  if (S.f32) rc = build2(thR, S.kR, QOut{w.q32R, nullptr, nullptr}, thP, S.kP, QOut{w.q32P, nullptr, nullptr}, S.b,
+                       w.bws, bmode, s);
+  else rc = build2(thR, S.kR, QOut{w.q32R, nullptr, w.qtR}, thP, S.kP, QOut{w.q32P, w.qbP, w.qtP}, S.b, w.bws,
+                   bmode, s);
+  if (rc) return rc;
+  return bwd_core(S, W0p, Blk{w.q32R, w.q32P, nullptr, w.qbP, w.qtR, w.qtP}, sigma, tau, X, dY, dX, dthR, dthP,
+                  accum, w, s);
+}
+
+int poetx_backward_blocks(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                          const int32_t* sigma, const int32_t* tau, const void* X, const void* dY, int64_t N,
+                          void* dX, float* dthR, float* dthP, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_bwd_args(layer, N, W0p, sigma, tau, X, dY, dthR, dthP);
+  if (rc) return rc;
+  const Shape S = shape_of(layer, N);
+  if ((rc = check_blocks(S, blocks, true))) return rc;
+  const bool accum = (layer->flags & POETX_ACCUMULATE_GRAD) != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) return zero_grads(S, accum, dthR, dthP, s);
+  size_t need = 0;
+  plan_bwd(S, false, nullptr, &need);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const BwdWs w = plan_bwd(S, false, ws, &need);
+  return bwd_core(S, W0p, blk_of(blocks), sigma, tau, X, dY, dX, dthR, dthP, accum, w, s);
 }
 
 int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int32_t* sigma, int32_t* tau,
@@ -521,12 +686,14 @@ int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bmode = S.f32 ? 0 : 6;
   if (S.f32) {
-    if ((rc = build(thR, S.kR, S.b, w.q32R, nullptr, nullptr, w.bws, bmode, s))) return rc;
-    if ((rc = build(thP, S.kP, S.b, w.q32P, nullptr, nullptr, w.bws, bmode, s))) return rc;
+    if ((rc = build2(thR, S.kR, QOut{w.q32R, nullptr, nullptr}, thP, S.kP, QOut{w.q32P, nullptr, nullptr}, S.b,
+                     w.bws, bmode, s)))
+      return rc;
     launch_merge_tiles(true, W0p, w.V, w.q32R, w.q32P, S.m, S.n, S.b, S.kR, S.kP, s);
   } else {
-    if ((rc = build(thR, S.kR, S.b, nullptr, w.qbR, nullptr, w.bws, bmode, s))) return rc;
-    if ((rc = build(thP, S.kP, S.b, nullptr, nullptr, w.qtP, w.bws, bmode, s))) return rc;
+    if ((rc = build2(thR, S.kR, QOut{nullptr, w.qbR, nullptr}, thP, S.kP, QOut{nullptr, nullptr, w.qtP}, S.b, w.bws,
+                     bmode, s)))
+      return rc;
     Tm tm(s, "merge_tiles", 4.0 * S.m * S.n * S.b, 2.0 * S.m * S.n * S.es);
     launch_merge_tiles(false, W0p, w.V, w.qbR, w.qtP, S.m, S.n, S.b, S.kR, S.kP, s);
   }

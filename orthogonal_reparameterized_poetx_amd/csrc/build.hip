@@ -13,18 +13,24 @@
 
 namespace poetx {
 
+// orders this wave's LDS accesses (and the compiler's view of them)
+__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // ----------------------------------------------------------------------------
 // Register-resident blocked Gauss-Jordan, one workgroup per B x B matrix.
-// Wave w owns a (32*TT) x (32*TT) tile of the matrix in MFMA accumulator
-// layout; a panel step K = [32p, 32p+32) inverts the diagonal 32x32 block in
-// LDS, forms the new row panel, and updates every other tile with one rank-32
-// MFMA product.
+// Wave w owns (32*TR) x (32*TC) of the matrix in MFMA accumulator layout; a
+// panel step K = [32p, 32p+32) inverts the diagonal 32x32 block in LDS, forms
+// the new row panel, and updates every other tile with one rank-32 MFMA
+// product.  One launch serves two independent batches (the R and the P
+// sets of blocks (e.g. the R and P sides of several layers): workgroup w takes
+// the segment s with start[s] <= w < start[s+1].
 // ----------------------------------------------------------------------------
 template <int B> struct GJShape {
-  static constexpr int TT = (B >= 256) ? 2 : 1;
-  static constexpr int WT = 32 * TT;
-  static constexpr int WPR = B / WT;
-  static constexpr int NW = WPR * WPR;
+  static constexpr int TR = (B >= 256) ? 2 : 1;  // MFMA tiles per wave along rows
+  static constexpr int TC = (B >= 256) ? 4 : 1;  // ... along columns
+  static constexpr int WPR = B / (32 * TR);      // waves along rows
+  static constexpr int WPC = B / (32 * TC);      // waves along columns
+  static constexpr int NW = WPR * WPC;
   static constexpr int NT = 64 * NW;
 };
 
@@ -35,7 +41,7 @@ template <int B> struct GJShape {
 template <int B, int MODE>
 __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
   using S = GJShape<B>;
-  constexpr int TT = S::TT, NT = S::NT, WPR = S::WPR;
+  constexpr int TR = S::TR, TC = S::TC, NT = S::NT, WPC = S::WPC;
   constexpr bool X6 = MODE == 6;
   constexpr int PC = 33;       // fp32 column-panel pitch (32 + 1)
   constexpr int PR = B + 1;    // fp32 row-panel pitch
@@ -43,38 +49,41 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
   __shared__ float Pcol[X6 ? 1 : B * PC];     // old column panel A[:, K] (fp32 mode)
   __shared__ float Prow[32 * PR];             // old row panel A[K, :], then the new one
   __shared__ float Dm[32 * PC];               // diagonal block -> its inverse
+  __shared__ float colb[32];                  // column broadcast of the diagonal-block pivots
   __shared__ bf16 OpA[X6 ? 3 * B * HP : 2];   // -A[:, K] split h|m|l, [i][kk]
   __shared__ bf16 OpB[X6 ? 3 * B * HP : 2];   // new A[K, :]^T split h|m|l, [j][kk]
 
-  const int blk = blockIdx.x;
+  int seg = 0;
+  while (seg + 1 < g.nseg && (int)blockIdx.x >= g.start[seg + 1]) ++seg;
+  const int blk = (int)blockIdx.x - g.start[seg];
+  const GJSeg& sg = g.seg[seg];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int tr = (wave / WPR) * S::WT;
-  const int tc = (wave % WPR) * S::WT;
+  const int tr = (wave / WPC) * 32 * TR;
+  const int tc = (wave % WPC) * 32 * TC;
   const int lc = lane & 31;
 
-  // value of the old column panel A[i][K0 + t]
-  auto pcol = [&](int i, int t) -> float {
-    if constexpr (X6)
-      return -((float)OpA[i * HP + t] + (float)OpA[B * HP + i * HP + t] + (float)OpA[2 * B * HP + i * HP + t]);
-    else
-      return Pcol[i * PC + t];
+  auto split3 = [](float x, bf16& h, bf16& m, bf16& l) {
+    h = (bf16)x;
+    const float r1 = x - (float)h;
+    m = (bf16)r1;
+    l = (bf16)(r1 - (float)m);
   };
 
-  f32x16 acc[TT][TT];
+  f32x16 acc[TR][TC];
   // ---- load A = I - S (theta mode) or A from a strided matrix
 #pragma unroll
-  for (int ti = 0; ti < TT; ++ti)
+  for (int ti = 0; ti < TR; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < TT; ++tj)
+    for (int tj = 0; tj < TC; ++tj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = tr + 32 * ti + c32_row(lane, r);
         const int j = tc + 32 * tj + lc;
         float v;
-        if (g.theta) {
-          const float* th = g.theta + (int64_t)blk * (B * (B - 1) / 2);
+        if (sg.theta) {
+          const float* th = sg.theta + (int64_t)blk * (B * (B - 1) / 2);
           if (i == j) v = 1.0f;
           else if (i < j) v = -th[i * B - i * (i + 1) / 2 + (j - i - 1)];
           else v = th[j * B - j * (j + 1) / 2 + (i - j - 1)];
@@ -88,9 +97,9 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
     const int K0 = 32 * p;
     // ---- (a) publish the old column and row panels
 #pragma unroll
-    for (int ti = 0; ti < TT; ++ti)
+    for (int ti = 0; ti < TR; ++ti)
 #pragma unroll
-      for (int tj = 0; tj < TT; ++tj) {
+      for (int tj = 0; tj < TC; ++tj) {
         const int I0 = tr + 32 * ti, J0 = tc + 32 * tj;
         if (J0 == K0) {
 #pragma unroll
@@ -98,11 +107,8 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
             const int i = I0 + c32_row(lane, r);
             const float v = acc[ti][tj][r];
             if constexpr (X6) {
-              const float x = -v;
-              const bf16 h = (bf16)x;
-              const float r1 = x - (float)h;
-              const bf16 m = (bf16)r1;
-              const bf16 l = (bf16)(r1 - (float)m);
+              bf16 h, m, l;
+              split3(-v, h, m, l);
               OpA[i * HP + lc] = h;
               OpA[B * HP + i * HP + lc] = m;
               OpA[2 * B * HP + i * HP + lc] = l;
@@ -117,97 +123,103 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
         }
       }
     __syncthreads();
-    // ---- (b) invert the diagonal 32x32 block in place (all threads)
-    for (int e = tid; e < 1024; e += NT) Dm[(e >> 5) * PC + (e & 31)] = Prow[(e >> 5) * PR + K0 + (e & 31)];
+    // ---- (b) invert the diagonal 32x32 block: wave 0, one column per lane
+    // (lane j + 32h holds rows 16h..16h+15 of column j), column k broadcast
+    // through LDS, row k by a cross-lane read.  No workgroup barrier inside.
+    if (wave == 0) {
+      const int j = lane & 31, h = lane >> 5;
+      float d[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) d[r] = Prow[(16 * h + r) * PR + K0 + j];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        if (j == k) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) colb[16 * h + r] = d[r];
+        }
+        lds_wave_fence();
+        float col[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) col[r] = colb[16 * h + r];
+        const float pinv = 1.0f / colb[k];
+        const float rk = __shfl(d[k & 15], j + 32 * (k >> 4));
+        const float nrow = (j == k) ? pinv : rk * pinv;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = 16 * h + r;
+          d[r] = (i == k) ? nrow : ((j == k) ? -col[r] * pinv : d[r] - col[r] * nrow);
+        }
+        lds_wave_fence();
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Dm[(16 * h + r) * PC + j] = d[r];
+    }
     __syncthreads();
-    for (int k = 0; k < 32; ++k) {
-      const float pinv = 1.0f / Dm[k * PC + k];
-      float nv[(1024 + NT - 1) / NT];
-#pragma unroll
-      for (int q = 0; q < (1024 + NT - 1) / NT; ++q) {
-        const int e = tid + q * NT;
-        if (e < 1024) {
-          const int i = e >> 5, j = e & 31;
-          if (i == k) nv[q] = (j == k) ? pinv : Dm[k * PC + j] * pinv;
-          else {
-            const float f = Dm[i * PC + k];
-            nv[q] = (j == k) ? -f * pinv : Dm[i * PC + j] - f * (Dm[k * PC + j] * pinv);
-          }
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < (1024 + NT - 1) / NT; ++q) {
-        const int e = tid + q * NT;
-        if (e < 1024) Dm[(e >> 5) * PC + (e & 31)] = nv[q];
-      }
-      __syncthreads();
-    }
-    // ---- (c) new row panel: A[K, j] <- Dinv A[K, j] (j outside K), A[K, K] <- Dinv
+    // ---- (c) new row panel: A[K, j] <- Dinv A[K, j] (j outside K), A[K, K] <- Dinv.
+    // Each thread owns RB rows x CB columns of the 32 x B panel.
     {
-      constexpr int PER = (32 * B + NT - 1) / NT;
-      float nv[PER];
+      constexpr int CB = 4;
+      constexpr int RB = 32 * B / (NT * CB);
+      const int cg = tid % (B / CB), rg = tid / (B / CB);
+      float nv[RB][CB];
 #pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int e = tid + q * NT;
-        if (e < 32 * B) {
-          const int kk = e / B, j = e % B;
-          float s;
-          if (j >= K0 && j < K0 + 32) s = Dm[kk * PC + (j - K0)];
-          else {
-            s = 0.f;
-#pragma unroll 8
-            for (int t = 0; t < 32; ++t) s += Dm[kk * PC + t] * Prow[t * PR + j];
-          }
-          nv[q] = s;
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) nv[rb][cb] = 0.f;
+      const bool diag = (cg * CB >= K0) && (cg * CB < K0 + 32);
+      if (!diag) {
+#pragma unroll 4
+        for (int t = 0; t < 32; ++t) {
+          float dv[RB], pv[CB];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) dv[rb] = Dm[(rg * RB + rb) * PC + t];
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) pv[cb] = Prow[t * PR + cg * CB + cb];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) nv[rb][cb] += dv[rb] * pv[cb];
         }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) nv[rb][cb] = Dm[(rg * RB + rb) * PC + cg * CB + cb - K0];
       }
       __syncthreads();
 #pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int e = tid + q * NT;
-        if (e < 32 * B) {
-          const int kk = e / B, j = e % B;
-          Prow[kk * PR + j] = nv[q];
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int kk = rg * RB + rb, jj = cg * CB + cb;
+          Prow[kk * PR + jj] = nv[rb][cb];
           if constexpr (X6) {
-            const float x = nv[q];
-            const bf16 h = (bf16)x;
-            const float r1 = x - (float)h;
-            const bf16 m = (bf16)r1;
-            const bf16 l = (bf16)(r1 - (float)m);
-            OpB[j * HP + kk] = h;
-            OpB[B * HP + j * HP + kk] = m;
-            OpB[2 * B * HP + j * HP + kk] = l;
+            bf16 hh, mm, ll;
+            split3(nv[rb][cb], hh, mm, ll);
+            OpB[jj * HP + kk] = hh;
+            OpB[B * HP + jj * HP + kk] = mm;
+            OpB[2 * B * HP + jj * HP + kk] = ll;
           }
         }
-      }
       __syncthreads();
     }
-    // ---- (d) update every tile
+    // ---- (d) update every tile.  Rows outside K: A[i, j] -= A[i, K] newrow[K, j],
+    // where for j in K the new row panel holds Dinv and the tile starts from
+    // zero, giving A[i, K] <- -A[i, K] Dinv.  Rows in K: the new row panel.
 #pragma unroll
-    for (int ti = 0; ti < TT; ++ti)
+    for (int ti = 0; ti < TR; ++ti) {
+      const int I0 = tr + 32 * ti;
 #pragma unroll
-      for (int tj = 0; tj < TT; ++tj) {
-        const int I0 = tr + 32 * ti, J0 = tc + 32 * tj;
-        if (J0 == K0) {
-          // column panel: A[K, K] <- Dinv, A[i, K] <- -A[i, K] Dinv
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I0 + c32_row(lane, r);
-            float v;
-            if (I0 == K0) v = Dm[(i - K0) * PC + lc];
-            else {
-              float s = 0.f;
-#pragma unroll 8
-              for (int t = 0; t < 32; ++t) s += pcol(i, t) * Dm[t * PC + lc];
-              v = -s;
-            }
-            acc[ti][tj][r] = v;
-          }
-        } else if (I0 == K0) {
+      for (int tj = 0; tj < TC; ++tj) {
+        const int J0 = tc + 32 * tj;
+        if (I0 == K0) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[ti][tj][r] = Prow[c32_row(lane, r) * PR + J0 + lc];
         } else {
+          if (J0 == K0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[ti][tj][r] = 0.f;
+          }
           if constexpr (X6) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -237,14 +249,15 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
           }
         }
       }
+    }
     __syncthreads();
   }
 
   // ---- outputs: M to a strided matrix, or Q = 2M - I in the requested layouts
 #pragma unroll
-  for (int ti = 0; ti < TT; ++ti)
+  for (int ti = 0; ti < TR; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < TT; ++tj) {
+    for (int tj = 0; tj < TC; ++tj) {
       const int I0 = tr + 32 * ti, J0 = tc + 32 * tj;
       const int j = J0 + lc;
       if (g.out) {
@@ -263,16 +276,16 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
           const int r = 4 * r4 + rr;
           const int i = I0 + c32_row(lane, r);
           const float q = 2.0f * acc[ti][tj][r] - (i == j ? 1.0f : 0.0f);
-          if (g.q32) g.q32[base + (int64_t)i * B + j] = q;
+          if (sg.q32) sg.q32[base + (int64_t)i * B + j] = q;
           qb[rr] = f32_to_bits(q);
-          if (g.qbf) g.qbf[base + (int64_t)i * B + j] = qb[rr];
+          if (sg.qbf) sg.qbf[base + (int64_t)i * B + j] = qb[rr];
         }
-        if (g.qtbf) {
+        if (sg.qtbf) {
           const int i0 = I0 + c32_row(lane, 4 * r4);
           uint2 v;
           v.x = pack2(qb[0], qb[1]);
           v.y = pack2(qb[2], qb[3]);
-          *reinterpret_cast<uint2*>(&g.qtbf[base + (int64_t)j * B + i0]) = v;
+          *reinterpret_cast<uint2*>(&sg.qtbf[base + (int64_t)j * B + i0]) = v;
         }
       }
     }
@@ -299,9 +312,11 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
   const int wi = wave >> 1, wj = wave & 1;
   const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
   const int64_t bz = blockIdx.z;
-  const float* A = a.A + bz * a.sA;
-  const float* Bm = a.B + bz * a.sB;
-  float* C = a.C + bz * a.sC;
+  const bool second = bz >= a.nb0;
+  const int64_t z1 = bz - a.nb0;
+  const float* A = (second && a.A1) ? a.A1 + z1 * a.sA : a.A + bz * a.sA;
+  const float* Bm = (second && a.B1) ? a.B1 + z1 * a.sB : a.B + bz * a.sB;
+  float* C = (second && a.C1) ? a.C1 + z1 * a.sC : a.C + bz * a.sC;
   const bool active = (row0 + 32 * wi < a.M) && (col0 + 32 * wj < a.N);
   f32x16 acc;
 #pragma unroll
@@ -316,7 +331,9 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
       if constexpr (NS == 3) dst[2 * 64 * HP + idx] = (bf16)(r1 - (float)m);
     }
   };
-  for (int k0 = 0; k0 < a.K; k0 += 32) {
+  // next K chunk is fetched into registers while the current one is multiplied
+  float va[8], vb[8];
+  auto fetch = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int e = tid + 256 * q;
@@ -324,29 +341,46 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
       const int ia = a.transA ? (e & 63) : (e >> 5);
       const int ka = a.transA ? (e >> 6) : (e & 31);
       const int gi = row0 + ia, gka = k0 + ka;
-      float va = 0.f;
+      float x = 0.f;
       if (gi < a.M) {
-        va = a.transA ? A[(int64_t)gka * a.lda + gi] : A[(int64_t)gi * a.lda + gka];
-        if (a.addIA && gi == gka) va += 1.0f;
+        x = a.transA ? A[(int64_t)gka * a.lda + gi] : A[(int64_t)gi * a.lda + gka];
+        if (a.addIA && gi == gka) x += 1.0f;
       }
+      va[q] = x;
       // element of opB
       const int jb = a.transB ? (e >> 5) : (e & 63);
       const int kb = a.transB ? (e & 31) : (e >> 6);
       const int gj = col0 + jb, gkb = k0 + kb;
-      float vb = 0.f;
+      float y = 0.f;
       if (gj < a.N) {
-        vb = a.transB ? Bm[(int64_t)gj * a.ldb + gkb] : Bm[(int64_t)gkb * a.ldb + gj];
-        if (a.addIB && gkb == gj) vb += 1.0f;
+        y = a.transB ? Bm[(int64_t)gj * a.ldb + gkb] : Bm[(int64_t)gkb * a.ldb + gj];
+        if (a.addIB && gkb == gj) y += 1.0f;
       }
+      vb[q] = y;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = tid + 256 * q;
+      const int ia = a.transA ? (e & 63) : (e >> 5);
+      const int ka = a.transA ? (e >> 6) : (e & 31);
+      const int jb = a.transB ? (e >> 5) : (e & 63);
+      const int kb = a.transB ? (e & 31) : (e >> 6);
       if constexpr (NS) {
-        put(Ah, ia * HP + ka, va);
-        put(Bh, jb * HP + kb, vb);
+        put(Ah, ia * HP + ka, va[q]);
+        put(Bh, jb * HP + kb, vb[q]);
       } else {
-        Af[ia * FP + ka] = va;
-        Bf[jb * FP + kb] = vb;
+        Af[ia * FP + ka] = va[q];
+        Bf[jb * FP + kb] = vb[q];
       }
     }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < a.K; k0 += 32) {
+    stash();
     __syncthreads();
+    if (k0 + 32 < a.K) fetch(k0 + 32);
     if (active) {
       const int lc = lane & 31;
       if constexpr (NS) {
@@ -425,14 +459,17 @@ __global__ __launch_bounds__(256) void finalize_q_kernel(const float* __restrict
     for (int r = ty; r < 32; r += 8) qtbf[base + (int64_t)(j0 + r) * b + i0 + tx] = t[tx][r];
 }
 
-// dtheta[blk][p(i,j)] (+)= GS[i][j] - GS[j][i], i < j.  grid (ceil(b/256), b-1, nblk)
-__global__ void skew_project_kernel(const float* __restrict__ GS, int b, float* __restrict__ dth, int accumulate) {
+// dtheta[blk][p(i,j)] (+)= GS[i][j] - GS[j][i], i < j.  grid (ceil(b/256), b-1, nblk);
+// blocks [0, n0) write dth0, the rest dth1.
+__global__ void skew_project_kernel(const float* __restrict__ GS, int b, float* __restrict__ dth0, int n0,
+                                    float* __restrict__ dth1, int accumulate) {
   const int blk = blockIdx.z, i = blockIdx.y;
   const int j = i + 1 + blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= b) return;
   const float* g = GS + (int64_t)blk * b * b;
   const float v = g[(int64_t)i * b + j] - g[(int64_t)j * b + i];
-  float* d = dth + (int64_t)blk * (b * (b - 1) / 2) + (i * b - i * (i + 1) / 2 + (j - i - 1));
+  float* dth = blk < n0 ? dth0 + (int64_t)blk * (b * (b - 1) / 2) : dth1 + (int64_t)(blk - n0) * (b * (b - 1) / 2);
+  float* d = dth + (i * b - i * (i + 1) / 2 + (j - i - 1));
   *d = accumulate ? (*d + v) : v;
 }
 
@@ -476,10 +513,11 @@ void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qb
   hipLaunchKernelGGL(finalize_q_kernel, grid, dim3(256), 0, s, M, b, q32, qbf, qtbf);
 }
 
-void launch_skew_project(const float* GS, int b, int nblk, float* dth, int accumulate, hipStream_t s) {
+void launch_skew_project(const float* GS, int b, int nblk, float* dth0, int n0, float* dth1, int accumulate,
+                         hipStream_t s) {
   if (nblk <= 0) return;
   dim3 grid((b + 255) / 256, b - 1, nblk);
-  hipLaunchKernelGGL(skew_project_kernel, grid, dim3(256), 0, s, GS, b, dth, accumulate);
+  hipLaunchKernelGGL(skew_project_kernel, grid, dim3(256), 0, s, GS, b, dth0, n0, dth1, accumulate);
 }
 
 }  // namespace poetx

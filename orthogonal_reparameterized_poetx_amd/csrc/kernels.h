@@ -7,17 +7,23 @@
 namespace poetx {
 
 // ---- Cayley builder (build.hip)
-struct GJArgs {
+struct GJSeg {
   const float* theta;   // theta mode: [blk][b(b-1)/2]; nullptr selects matrix mode
-  const float* in;      // matrix mode input
+  float* q32;           // optional Q = 2M - I outputs, [blk][B][B]
+  uint16_t* qbf;
+  uint16_t* qtbf;
+};
+constexpr int GJ_MAXSEG = 16;
+struct GJArgs {
+  GJSeg seg[GJ_MAXSEG]; // workgroup w uses the segment s with start[s] <= w < start[s+1]
+  int start[GJ_MAXSEG + 1];
+  int nseg;
+  const float* in;      // matrix mode input (one segment)
   int64_t in_stride;
   int in_ld;
   float* out;           // optional M output (strided)
   int64_t out_stride;
   int out_ld;
-  float* q32;           // optional Q = 2M - I outputs, [blk][B][B]
-  uint16_t* qbf;
-  uint16_t* qtbf;
 };
 // mode 0: fp32 MFMA trailing updates; mode 6: split bf16 x6 (fp32-level accuracy)
 void launch_gj(int B, int mode, int nblk, const GJArgs& g, hipStream_t s);
@@ -28,12 +34,17 @@ struct BGemmArgs {
   const float* B; int64_t sB; int ldb; int transB; int addIB;
   float* C; int64_t sC; int ldc;
   float alpha, beta;
+  // optional second segment: batch items z >= nb0 use A1 / B1 / C1 (when set)
+  // at index z - nb0 instead of A / B / C at index z
+  const float* A1; const float* B1; float* C1; int nb0;
 };
 // mode 0: fp32 MFMA; 3 / 6: split bf16 x3 / x6
 void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s);
 void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s);
 void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qbf, uint16_t* qtbf, hipStream_t s);
-void launch_skew_project(const float* GS, int b, int nblk, float* dth, int accumulate, hipStream_t s);
+// blocks [0, n0) project into dth0, the rest into dth1
+void launch_skew_project(const float* GS, int b, int nblk, float* dth0, int n0, float* dth1, int accumulate,
+                         hipStream_t s);
 
 // ---- block transforms (transform.hip)
 // gather-in : out[t][l*B+i] = sum_kk in[t][perm[l*B+kk]] * Mq(kk, i); tail copies in[t][perm[j]]

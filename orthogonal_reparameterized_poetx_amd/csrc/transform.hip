@@ -253,7 +253,9 @@ __global__ __launch_bounds__(MAXT) void scatter_out_kernel(XformArgs a) {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) acc[c2][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (l < k) {
-#pragma unroll
+        // two k chunks in flight: fully unrolled, the loads of every chunk
+        // would be issued up front and not fit beside the held results
+#pragma unroll 2
         for (int kc = 0; kc < KC; ++kc) {
           bf16x8 af[TT];
 #pragma unroll
@@ -287,6 +289,8 @@ __global__ __launch_bounds__(MAXT) void scatter_out_kernel(XformArgs a) {
         for (int tt = 0; tt < TT; ++tt) {
           res[s][2 * cp + c2][tt][0] = pack2(f32_to_bits(acc[c2][tt][0]), f32_to_bits(acc[c2][tt][1]));
           res[s][2 * cp + c2][tt][1] = pack2(f32_to_bits(acc[c2][tt][2]), f32_to_bits(acc[c2][tt][3]));
+          // materialise the packed bf16 pair here (not as fp32 until the scatter)
+          asm volatile("" : "+v"(res[s][2 * cp + c2][tt][0]), "+v"(res[s][2 * cp + c2][tt][1]));
         }
     }
   }

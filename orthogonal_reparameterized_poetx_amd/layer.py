@@ -27,6 +27,7 @@ class PoetxLayer:
         self.perm_seed = int(perm_seed)
         self.merges = 0
         self._ws = {}
+        self._blk = {}
 
     # -- workspaces (grown on demand, reused across calls)
     def workspace(self, op, N=0):
@@ -67,9 +68,65 @@ class PoetxLayer:
             dthP = torch.empty_like(self.thP)
         self.layer.flags = L.POETX_ACCUMULATE_GRAD if accumulate else 0
         ws = self.workspace(L.OP_BACKWARD, N)
-        L.poetx_backward(self.layer, self.W0p, self.thR, self.thP, self.sigma, self.tau, X, dY, N,
-                         dX if want_dx else None, dthR, dthP, ws, stream)
-        self.layer.flags = 0
+        try:
+            L.poetx_backward(self.layer, self.W0p, self.thR, self.thP, self.sigma, self.tau, X, dY, N,
+                             dX if want_dx else None, dthR, dthP, ws, stream)
+        finally:
+            self.layer.flags = 0
+        return dX, dthR, dthP
+
+    # -- prebuilt blocks: built for many layers at once (build_layer_blocks),
+    #    then consumed by forward_blocks / backward_blocks
+    def block_buffers(self, kind):
+        """Device buffers of this layer's Cayley blocks for kind "forward" or
+        "backward" (the outputs each pass reads; see poetx_blocks)."""
+        if kind in self._blk:
+            return self._blk[kind]
+        kR, kP, b, dev = self.m // self.b, self.n // self.b, self.b, self.device
+
+        def t(k, dt):
+            return torch.empty(k, b, b, dtype=dt, device=dev)
+        f32, bf = torch.float32, torch.bfloat16
+        if self.dt == L.POETX_F32:
+            q = dict(Q32R=t(kR, f32), Q32P=t(kP, f32))
+        elif kind == "forward":
+            q = dict(QR=t(kR, bf), QP=t(kP, bf))
+        else:
+            q = dict(Q32R=t(kR, f32), Q32P=t(kP, f32), QP=t(kP, bf), QTR=t(kR, bf), QTP=t(kP, bf))
+        self._blk[kind] = (q, L.make_blocks(**q))
+        return self._blk[kind]
+
+    def block_sets(self, kind):
+        """poetx_block_set entries (R side, P side) filling block_buffers(kind)."""
+        q, _ = self.block_buffers(kind)
+        kR, kP = self.m // self.b, self.n // self.b
+        return [(self.thR, kR, q.get("Q32R"), q.get("QR"), q.get("QTR")),
+                (self.thP, kP, q.get("Q32P"), q.get("QP"), q.get("QTP"))]
+
+    def forward_blocks(self, X, Y=None, stream=None):
+        N = X.shape[0]
+        if Y is None:
+            Y = torch.empty(N, self.m, dtype=self.tdtype, device=self.device)
+        ws = self.workspace(L.OP_FORWARD_BLOCKS, N)
+        L.poetx_forward_blocks(self.layer, self.W0p, self.block_buffers("forward")[1], self.sigma, self.tau, X, N,
+                               Y, ws, stream)
+        return Y
+
+    def backward_blocks(self, X, dY, dX=None, dthR=None, dthP=None, want_dx=True, accumulate=False, stream=None):
+        N = X.shape[0]
+        if dX is None and want_dx:
+            dX = torch.empty(N, self.n, dtype=self.tdtype, device=self.device)
+        if dthR is None:
+            dthR = torch.empty_like(self.thR)
+        if dthP is None:
+            dthP = torch.empty_like(self.thP)
+        self.layer.flags = L.POETX_ACCUMULATE_GRAD if accumulate else 0
+        ws = self.workspace(L.OP_BACKWARD_BLOCKS, N)
+        try:
+            L.poetx_backward_blocks(self.layer, self.W0p, self.block_buffers("backward")[1], self.sigma, self.tau,
+                                    X, dY, N, dX if want_dx else None, dthR, dthP, ws, stream)
+        finally:
+            self.layer.flags = 0
         return dX, dthR, dthP
 
     def merge(self, stream=None):
@@ -77,3 +134,23 @@ class PoetxLayer:
         L.poetx_merge(self.layer, self.W0p, self.thR, self.thP, self.sigma, self.tau, self.perm_seed,
                       self.merges, ws, stream)
         self.merges += 1
+
+
+_build_ws = {}
+
+
+def build_layer_blocks(layers, kind, stream=None):
+    """Build the Cayley blocks of every layer for kind ("forward" or
+    "backward") with one poetx_build_block_sets call per block size, so the
+    builder's grid spans the blocks of all the layers."""
+    by_b = {}
+    for lay in layers:
+        by_b.setdefault(lay.b, []).extend(lay.block_sets(kind))
+    for b, sets in by_b.items():
+        dev = layers[0].device
+        need = L.build_workspace_bytes(max(s[1] for s in sets), b)
+        ws = _build_ws.get((dev, b))
+        if need and (ws is None or ws.numel() < need):
+            ws = L.make_workspace(need, dev)
+            _build_ws[(dev, b)] = ws
+        L.poetx_build_block_sets(sets, b, ws if need else None, stream)

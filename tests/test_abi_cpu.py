@@ -101,3 +101,52 @@ def test_workspace_sizes_grow_with_tokens():
     assert P.workspace_bytes(lay, 0, P.OP_MERGE) >= 2048 * 5632 * 2
     assert P.build_workspace_bytes(29, 512) > 29 * 2 * 512 * 512 * 4
     assert P.build_workspace_bytes(29, 256) == 0
+
+
+def test_prebuilt_block_entry_points_validate_on_host():
+    P = _P()
+    L = P.lib()
+    fake = ctypes.c_void_p(0x1000)
+    lay = P.Layer(512, 256, 64, P.POETX_BF16)
+    fneed = P.workspace_bytes(lay, 64, P.OP_FORWARD_BLOCKS)
+    bneed = P.workspace_bytes(lay, 64, P.OP_BACKWARD_BLOCKS)
+    # the prebuilt-block calls need no block storage of their own
+    assert 0 < fneed < P.workspace_bytes(lay, 64, P.OP_FORWARD)
+    assert 0 < bneed < P.workspace_bytes(lay, 64, P.OP_BACKWARD)
+    f = 0x2000
+    fwd_ok = P.Blocks(None, None, f, f, None, None)          # bf16 forward reads QR, QP
+    bwd_ok = P.Blocks(f, f, None, f, f, f)                   # bf16 backward: Q32R/P, QP, QTR, QTP
+    # NULL blocks struct, or a block array the pass reads left NULL
+    assert L.poetx_forward_blocks(ctypes.byref(lay), fake, None, fake, fake, fake, 64, fake, fake, fneed, None) == -1
+    for blk in [P.Blocks(None, None, None, f, None, None), P.Blocks(f, f, f, None, f, f)]:
+        assert L.poetx_forward_blocks(ctypes.byref(lay), fake, ctypes.byref(blk), fake, fake, fake, 64, fake, fake,
+                                      fneed, None) == -1, P.last_error()
+    for blk in [fwd_ok, P.Blocks(None, f, f, f, f, f), P.Blocks(f, f, f, f, None, f), P.Blocks(f, f, f, None, f, f)]:
+        assert L.poetx_backward_blocks(ctypes.byref(lay), fake, ctypes.byref(blk), fake, fake, fake, fake, 64, fake,
+                                       fake, fake, fake, bneed, None) == -1, P.last_error()
+    # workspace checks apply with valid blocks
+    assert L.poetx_forward_blocks(ctypes.byref(lay), fake, ctypes.byref(fwd_ok), fake, fake, fake, 64, fake, fake,
+                                  fneed - 1, None) == -4
+    assert L.poetx_backward_blocks(ctypes.byref(lay), fake, ctypes.byref(bwd_ok), fake, fake, fake, fake, 64, fake,
+                                   fake, fake, fake, bneed - 1, None) == -4
+    # fp32 layers read Q32R / Q32P in both passes
+    l32 = P.Layer(512, 256, 64, P.POETX_F32)
+    assert L.poetx_forward_blocks(ctypes.byref(l32), fake, ctypes.byref(fwd_ok), fake, fake, fake, 64, fake, fake,
+                                  1 << 30, None) == -1
+    # batched builder: count range, NULL sets, bad set, b=512 workspace
+    S = P.BlockSet
+    one = (S * 2)(S(0x1000, 4, 0x2000, None, None), S(0x3000, 3, None, 0x4000, None))
+    assert L.poetx_build_block_sets(one, -1, 64, None, 0, None) == -2
+    assert L.poetx_build_block_sets(None, 2, 64, None, 0, None) == -1
+    assert L.poetx_build_block_sets(one, 2, 48, None, 0, None) == -1
+    assert L.poetx_build_block_sets(one, 0, 64, None, 0, None) == 0
+    bad = (S * 2)(S(0x1000, 4, 0x2000, None, None), S(0x3000, 3, None, None, None))
+    assert L.poetx_build_block_sets(bad, 2, 64, None, 0, None) == -1
+    bad = (S * 2)(S(0x1000, 4, 0x2000, None, None), S(None, 3, 0x2000, None, None))
+    assert L.poetx_build_block_sets(bad, 2, 64, None, 0, None) == -1
+    bad = (S * 2)(S(0x1000, -4, 0x2000, None, None), S(0x3000, 3, 0x2000, None, None))
+    assert L.poetx_build_block_sets(bad, 2, 64, None, 0, None) == -2
+    assert L.poetx_build_block_sets(one, 2, 512, None, 0, None) == -4
+    # empty sets are skipped without a look at their pointers
+    empty = (S * 1)(S(None, 0, None, None, None))
+    assert L.poetx_build_block_sets(empty, 1, 64, None, 0, None) == 0

@@ -1,0 +1,121 @@
+"""GPU parity of the batched builder and the prebuilt-block entry points.
+
+poetx_build_block_sets must give, for every set, the blocks poetx_build_blocks
+gives for that set alone, bit for bit (one block never depends on another, and
+both run the same kernels).  poetx_forward_blocks / poetx_backward_blocks with
+blocks rebuilt from the generators must reproduce poetx_forward /
+poetx_backward bit for bit, and so meet the oracle bound of those calls.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as WL
+from gpu_util import compare, from_dev, make_layer, oracle_perms, to_dev, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("b,counts", [
+    (32, [3, 0, 5, 1, 2, 7, 1, 4, 0, 2, 6, 1, 3, 2, 5, 1, 1, 2, 3, 4]),   # 20 sets: two launches of <= 16
+    (64, [4, 9]),
+    (128, [2, 1, 3]),
+    (256, [5, 3, 1, 2]),
+    (512, [2, 1]),
+])
+def test_block_sets_match_single_builds(b, counts):
+    torch = torch_mod()
+    import orthogonal_reparameterized_poetx_amd as P
+    _log("block sets b=%d counts=%s" % (b, counts))
+    rng = np.random.default_rng(1000 + b)
+    dev = "cuda:0"
+    nt = b * (b - 1) // 2
+    sets, single = [], []
+    for i, nb in enumerate(counts):
+        th = to_dev((rng.standard_normal((max(nb, 1), nt)) * np.sqrt(1e-3)).astype(np.float32)[:nb], "f32")
+        # vary which outputs a set asks for
+        want = [(True, True, True), (True, False, False), (False, True, True), (False, False, True)][i % 4]
+        q32 = torch.full((nb, b, b), np.nan, dtype=torch.float32, device=dev) if want[0] else None
+        qb = torch.zeros(nb, b, b, dtype=torch.bfloat16, device=dev) if want[1] else None
+        qt = torch.zeros(nb, b, b, dtype=torch.bfloat16, device=dev) if want[2] else None
+        sets.append((th, nb, q32, qb, qt))
+        single.append(tuple(torch.empty(nb, b, b, dtype=t, device=dev)
+                            for t in (torch.float32, torch.bfloat16, torch.bfloat16)))
+    ws = P.make_workspace(P.build_workspace_bytes(max(counts), b), dev)
+    P.poetx_build_block_sets(sets, b, ws)
+    for (th, nb, _, _, _), (q32, qb, qt) in zip(sets, single):
+        ws1 = P.make_workspace(P.build_workspace_bytes(nb, b), dev)
+        P.poetx_build_blocks(th, nb, b, q32, qb, qt, ws1)
+    torch.cuda.synchronize()
+    for (th, nb, q32, qb, qt), ref in zip(sets, single):
+        for got, want in zip((q32, qb, qt), ref):
+            if got is not None:
+                assert torch.equal(got, want)
+    # one spot check against the oracle
+    th, nb, q32, _, _ = next(s for s in sets if s[1] > 0 and s[2] is not None)
+    ref = oracle.cayley(oracle.unpack_skew(from_dev(th)[0], b))
+    compare(from_dev(q32)[0], ref, "f32", "Q32[0]")
+
+
+LAYER_GROUPS = [
+    # (dtype, [(m, n)], b, N): several layers sharing one batched build
+    ("bf16", [(600, 520), (256, 768), (512, 512)], 256, 70),
+    ("bf16", [(300, 200), (130, 64), (64, 300)], 64, 45),
+    ("f32", [(96, 80), (200, 96)], 32, 37),
+    ("bf16", [(1100, 700), (512, 1024)], 512, 24),
+]
+
+
+@pytest.mark.parametrize("dtype,shapes,b,N", LAYER_GROUPS)
+def test_prebuilt_blocks_match_self_building_calls(dtype, shapes, b, N):
+    torch = torch_mod()
+    from orthogonal_reparameterized_poetx_amd import build_layer_blocks
+    layers, inps, ds = [], [], []
+    for i, (m, n) in enumerate(shapes):
+        inp = WL.small_case(40 + i, m, n, b, N, dtype=dtype)
+        lay, d = make_layer(inp)
+        layers.append(lay), inps.append(inp), ds.append(d)
+    _log("prebuilt %s b=%d N=%d shapes=%s" % (dtype, b, N, shapes))
+    build_layer_blocks(layers, "forward")
+    build_layer_blocks(layers, "backward")
+    for lay, inp, d in zip(layers, inps, ds):
+        Y = lay.forward(d["X"])
+        dX, dR, dP = lay.backward(d["X"], d["gY"])
+        Yb = lay.forward_blocks(d["X"])
+        dXb, dRb, dPb = lay.backward_blocks(d["X"], d["gY"])
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Yb)
+        assert torch.equal(dX, dXb) and torch.equal(dR, dRb) and torch.equal(dP, dPb)
+        sigma, tau = oracle_perms(inp, 0)
+        args = (inp["W0"][1], inp["thR"][1], inp["thP"][1], sigma, tau, inp["X"][1])
+        contract = dtype == "bf16"
+        compare(from_dev(Yb), oracle.forward(*args, b, contract=contract), dtype, "Y")
+        dXr, dRr, dPr = oracle.backward(*args, inp["gY"][1], b, contract=contract)
+        compare(from_dev(dXb), dXr, dtype, "dX")
+        if dRr.size:
+            compare(from_dev(dRb), dRr, dtype, "dthR")
+        if dPr.size:
+            compare(from_dev(dPb), dPr, dtype, "dthP")
+
+
+def test_prebuilt_backward_accumulate_and_empty():
+    torch = torch_mod()
+    from orthogonal_reparameterized_poetx_amd import build_layer_blocks
+    inp = WL.small_case(3, 256, 256, 64, 40, dtype="bf16")
+    lay, d = make_layer(inp)
+    build_layer_blocks([lay], "backward")
+    _, dR, dP = lay.backward_blocks(d["X"], d["gY"])
+    dR2, dP2 = dR.clone(), dP.clone()
+    lay.backward_blocks(d["X"], d["gY"], dthR=dR2, dthP=dP2, want_dx=False, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dR2, dR + dR) and torch.equal(dP2, dP + dP)
+    build_layer_blocks([lay], "forward")
+    lay.forward_blocks(d["X"][:0])
+    _, z1, z2 = lay.backward_blocks(d["X"][:0], d["gY"][:0], dthR=dR2, dthP=dP2, want_dx=False)
+    torch.cuda.synchronize()
+    assert not z1.any().item() and not z2.any().item()
