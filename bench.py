@@ -30,6 +30,28 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 MFMA_CLASSES = ("gemm_nt", "gemm_nn")
 
+# kernel name (demangled, as rocprofv3 prints it) -> timing class of the library,
+# and the dispatches one timed launch of the class makes
+KERNEL_CLASSES = [
+    ("gather_in_kernel", "xform_gather_in", 1),
+    ("scatter_out_kernel", "xform_scatter_out", 1),
+    ("gemm_bf16_kernel<false>", "gemm_nt", 1),
+    ("gemm_bf16_kernel<true>", "gemm_nn", 1),
+    ("gj_kernel", "cayley_build", 1),
+    ("gram_bf16_kernel", "gram", 2),
+    ("gram_reduce_kernel", "gram", 2),
+    ("bgemm_kernel", "chain_rule", 3),
+    ("skew_project_kernel", "chain_rule", 3),
+]
+CALIBRATION_BYTES = 256 << 20   # the copy kernel reads and writes this many bytes each
+
+
+def kernel_class(name):
+    for key, cls, per in KERNEL_CLASSES:
+        if key in name:
+            return cls, per
+    return None, 1
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -38,8 +60,16 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (default 8192)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=512, help="token sample of the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=3072, help="token sample of the oracle baseline")
     ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with one plain copy kernel of %d MiB (read and write) for counter calibration"
+                         % (CALIBRATION_BYTES >> 20))
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                         "'bench.py --calibrate-copy' into profiles/traffic_<class>.json")
+    ap.add_argument("--kernel-stats", metavar="CSV",
+                    help="no GPU: summarize a rocprofv3 --stats kernel_stats.csv by kernel class")
     ap.add_argument("--per-layer-builds", action="store_true",
                     help="let every forward / backward call build its own blocks (one builder launch per call) "
                          "instead of one batched build per pass")
@@ -66,8 +96,102 @@ def traffic_record(cls):
     return rec
 
 
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise SystemExit("no *%s under %s" % (suffix, d))
+
+
+def _pmc_per_dispatch(d, counter):
+    """{dispatch id: (kernel name, counter value)} from a rocprofv3 counter_collection.csv."""
+    import csv
+    out = {}
+    with open(_find_csv(d, "counter_collection.csv")) as fh:
+        for row in csv.DictReader(fh):
+            if row.get("Counter_Name") != counter:
+                continue
+            did = int(row["Dispatch_Id"])
+            name, val = out.get(did, (row["Kernel_Name"], 0.0))
+            out[did] = (name, val + float(row["Counter_Value"]))
+    return out
+
+
+def traffic_from(fetch_dir, write_dir):
+    """HBM bytes per launch of every kernel class, from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) scaled by what they read for the calibration copy."""
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+
+    def calib(tab):
+        cand = [v for n, v in tab.values() if "neg" in n.lower()]
+        if not cand:
+            raise SystemExit("calibration copy kernel not found")
+        return CALIBRATION_BYTES / (cand[-1] * 1024.0)
+    kf, kw = calib(fetch), calib(write)
+    agg = {}
+    for tab, k, key in ((fetch, kf, "fetch"), (write, kw, "write")):
+        for name, v in tab.values():
+            cls, per = kernel_class(name)
+            if cls is None:
+                continue
+            a = agg.setdefault(cls, dict(fetch=0.0, write=0.0, dispatches_fetch=0, dispatches_write=0, per=per,
+                                         kernels=set()))
+            a[key] += v * 1024.0 * k
+            a["dispatches_" + key] += 1
+            a["kernels"].add(name.split("(")[0])
+    src_files = ["api.hip", "build.hip", "transform.hip", "gemm.hip", "gram.hip", "common.h", "kernels.h"]
+    h = kernel_source_hash(src_files)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for cls, a in agg.items():
+        launches_f = a["dispatches_fetch"] / a["per"]
+        launches_w = a["dispatches_write"] / a["per"]
+        rec = dict(kernel_class=cls, source_hash=h, source_files=src_files,
+                   hbm_bytes_per_launch=round(a["fetch"] / launches_f + a["write"] / launches_w),
+                   fetch_bytes_per_launch=round(a["fetch"] / launches_f),
+                   write_bytes_per_launch=round(a["write"] / launches_w),
+                   launches=launches_f, calibration=dict(fetch_scale=round(kf, 4), write_scale=round(kw, 4),
+                                                         copy_bytes=CALIBRATION_BYTES),
+                   kernels=sorted(a["kernels"]))
+        with open(os.path.join(ROOT, "profiles", "traffic_%s.json" % cls), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        print("%-18s %12.0f B/launch (fetch %.0f, write %.0f) over %d launches"
+              % (cls, rec["hbm_bytes_per_launch"], rec["fetch_bytes_per_launch"], rec["write_bytes_per_launch"],
+                 launches_f))
+
+
+def kernel_stats(path):
+    """Per-class totals of a rocprofv3 kernel_stats.csv (durations in ns)."""
+    import csv
+    agg = {}
+    rows = list(csv.DictReader(open(path)))
+    for row in rows:
+        cls, per = kernel_class(row["Name"])
+        cls = cls or "other"
+        a = agg.setdefault(cls, [0, 0.0, per])
+        a[0] += int(row["Calls"])
+        a[1] += float(row["TotalDurationNs"])
+    print("%-18s %8s %14s %14s" % ("class", "launches", "total_ms", "avg_ms/launch"))
+    for cls, (calls, tot, per) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        n = calls / per
+        print("%-18s %8.0f %14.3f %14.4f" % (cls, n, tot * 1e-6, tot * 1e-6 / max(n, 1)))
+    print()
+    print("%-60s %7s %12s %12s" % ("kernel", "calls", "total_ms", "avg_ms"))
+    for row in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print("%-60s %7s %12.3f %12.4f" % (row["Name"].split("(")[0][:60], row["Calls"],
+                                           float(row["TotalDurationNs"]) * 1e-6, float(row["AverageNs"]) * 1e-6))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
+    if args.kernel_stats:
+        kernel_stats(args.kernel_stats)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU). "
               "Run with --gpus 1.", file=sys.stderr)
@@ -215,6 +339,14 @@ def main():
         "kernels_per_step": breakdown,
         "merge_ms_layer_set": round(merge_ms, 3),
     }
+
+    if args.calibrate_copy:
+        # one plain copy kernel of known size: reads and writes CALIBRATION_BYTES
+        src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
 
     # ---- float64 oracle on the host cores, bounded token sample
     if not args.no_cpu:
