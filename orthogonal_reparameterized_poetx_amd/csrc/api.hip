@@ -283,7 +283,7 @@ struct FwdWs {
   float *q32R, *q32P;
   uint16_t *qbR, *qbP;
   void* bws;
-  void *z1, *z2;
+  void *z1, *z2, *sc;
 };
 FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes) {
   Arena a(base);
@@ -300,6 +300,7 @@ FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes) {
   }
   w.z1 = a.take<char>((size_t)S.N * S.n * S.es);
   w.z2 = a.take<char>((size_t)S.N * S.m * S.es);
+  if (!S.f32) w.sc = a.take<char>((size_t)S.N * std::max(S.n, S.m) * S.es);   // permuted rows / block products
   *bytes = a.off + kAlign;
   return w;
 }
@@ -384,93 +385,151 @@ uint64_t mix64(uint64_t z) {
   return z ^ (z >> 31);
 }
 
+// bf16 row permutation of an [N][W] token matrix (see PermArgs)
+int permute(bool gather, const void* in, const void* tail_in, void* out, void* tail_out, const int32_t* perm,
+            int64_t N, int W, int tail0, size_t es, hipStream_t s) {
+  PermArgs p{};
+  p.in = static_cast<const uint16_t*>(in);
+  p.tail_in = static_cast<const uint16_t*>(tail_in);
+  p.out = static_cast<uint16_t*>(out);
+  p.tail_out = static_cast<uint16_t*>(tail_out);
+  p.perm = perm;
+  p.N = N; p.W = W; p.tail0 = tail0;
+  Tm tm(s, "xform_permute", 0.0, 2.0 * N * W * es);
+  launch_permute_bf16(gather, p, s);
+  return check_launch(gather ? "row gather" : "row scatter");
+}
+
+// block products over contiguous columns: out[t][l*b+i] = sum_kk in[t][l*b+kk] * q[l][i][kk]
+// for l < k (bf16, fp32 accumulation); columns from k*b on are not touched
+int blockmul(const void* in, const uint16_t* q, void* out, int64_t N, int W, int b, int k, hipStream_t s) {
+  if (k <= 0 || N <= 0) return POETX_OK;
+  GemmArgs g{};
+  g.A = static_cast<const uint16_t*>(in);
+  g.B = q;
+  g.C = static_cast<uint16_t*>(out);
+  g.M = (int)N; g.N = b; g.K = b;
+  g.lda = W; g.ldb = b; g.ldc = W;
+  g.sA = b; g.sB = (int64_t)b * b; g.sC = b;
+  g.batch = k;
+  Tm tm(s, "xform_blockmul", xf_flops(N, k, b), 2.0 * N * (double)k * b * 2);
+  launch_gemm_bf16(false, g, s);
+  return check_launch("block product");
+}
+
 // forward after the blocks exist: a3, a4, a5
 int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
              void* Y, const FwdWs& w, hipStream_t s) {
   const int64_t N = S.N;
+  const int n = (int)S.n, m = (int)S.m;
   int rc;
-  // z1' = D_P (Pi_tau x): gather by tau, multiply by Q_P^T per block
-  XformArgs p{};
-  p.in = X; p.out = w.z1; p.emit = nullptr; p.perm = tau; p.N = N; p.W = (int)S.n; p.B = S.b; p.k = S.kP;
-  {
-    Tm tm(s, "xform_gather_in", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
-    if (S.f32) { p.bq = q.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
-    else { p.bq = q.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld b=%d", (long long)S.n, S.b); }
+  if (S.f32) {
+    // z1' = D_P (Pi_tau x), z2' = z1' W0p^T, y = Pi_sigma^T (D_R z2'), each in one pass
+    XformArgs p{};
+    p.in = X; p.out = w.z1; p.perm = tau; p.N = N; p.W = n; p.B = S.b; p.k = S.kP; p.bq = q.q32P; p.trans = 0;
+    {
+      Tm tm(s, "xform_fp32", xf_flops(N, S.kP, S.b), 2.0 * N * n * S.es);
+      launch_gather_in_f32(p, s);
+    }
+    {
+      Tm tm(s, "gemm_fp32", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+      launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
+    }
+    XformArgs r{};
+    r.in = w.z2; r.out = Y; r.perm = sigma; r.N = N; r.W = m; r.B = S.b; r.k = S.kR; r.bq = q.q32R; r.trans = 0;
+    {
+      Tm tm(s, "xform_fp32", xf_flops(N, S.kR, S.b), 2.0 * N * m * S.es);
+      launch_scatter_out_f32(r, s);
+    }
+    return check_launch("fp32 forward");
   }
-  if ((rc = check_launch("P-side transform"))) return rc;
+  // z1' = D_P x' with x' = Pi_tau x (the identity tail of x' goes straight to z1')
+  if ((rc = permute(true, X, nullptr, w.sc, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
+  if ((rc = blockmul(w.sc, q.qbP, w.z1, N, n, S.b, S.kP, s))) return rc;
   // z2' = z1' W0p^T
   {
     Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-    if (S.f32) launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
-    else launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
+    launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
   }
   if ((rc = check_launch("forward GEMM"))) return rc;
-  // y = Pi_sigma^T (D_R z2'): multiply by Q_R^T per block, scatter by sigma
-  XformArgs r{};
-  r.in = w.z2; r.out = Y; r.perm = sigma; r.N = N; r.W = (int)S.m; r.B = S.b; r.k = S.kR;
-  {
-    Tm tm(s, "xform_scatter_out", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
-    if (S.f32) { r.bq = q.q32R; r.trans = 0; launch_scatter_out_f32(r, s); }
-    else { r.bq = q.qbR; if (!launch_scatter_out_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld b=%d", (long long)S.m, S.b); }
-  }
-  return check_launch("R-side transform");
+  // y = Pi_sigma^T r with r = D_R z2' (the tail of r is the tail of z2')
+  if ((rc = blockmul(w.z2, q.qbR, w.sc, N, m, S.b, S.kR, s))) return rc;
+  return permute(false, w.sc, w.z2, Y, nullptr, sigma, N, m, S.kR * S.b, S.es, s);
 }
 
 // backward after the blocks exist: a0 (recompute), a6, a7, a8, a9
 int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
              const void* dY, void* dX, float* dthR, float* dthP, bool accum, const BwdWs& w, hipStream_t s) {
   const int64_t N = S.N;
+  const int n = (int)S.n, m = (int)S.m;
   const int cmode = S.f32 ? 0 : 3;   // chain-rule products
   int rc;
-  // recompute z1' (and keep the gathered x' for dL/dQ_P), then z2'
-  XformArgs p{};
-  p.in = X; p.out = w.z1; p.emit = w.xg; p.perm = tau; p.N = N; p.W = (int)S.n; p.B = S.b; p.k = S.kP;
-  {
-    // recompute pass: algorithmic bytes are the read of X and the write of z1'
-    Tm tm(s, "xform_gather_in", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
-    if (S.f32) { p.bq = q.q32P; p.trans = 0; launch_gather_in_f32(p, s); }
-    else { p.bq = q.qbP; if (!launch_gather_in_bf16(p, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
+  if (S.f32) {
+    // recompute z1' (keeping x' = Pi_tau x for dL/dQ_P) and z2'
+    XformArgs p{};
+    p.in = X; p.out = w.z1; p.emit = w.xg; p.perm = tau; p.N = N; p.W = n; p.B = S.b; p.k = S.kP; p.bq = q.q32P;
+    p.trans = 0;
+    {
+      Tm tm(s, "xform_fp32", xf_flops(N, S.kP, S.b), 2.0 * N * n * S.es);
+      launch_gather_in_f32(p, s);
+    }
+    {
+      Tm tm(s, "gemm_fp32", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+      launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
+    }
+    // R side: gY' = Pi_sigma gY (kept), gz2' = D_R^T gY'
+    XformArgs r{};
+    r.in = dY; r.out = w.gz2; r.emit = w.gyg; r.perm = sigma; r.N = N; r.W = m; r.B = S.b; r.k = S.kR;
+    r.bq = q.q32R; r.trans = 1;
+    {
+      Tm tm(s, "xform_fp32", xf_flops(N, S.kR, S.b), 2.0 * N * m * S.es);
+      launch_gather_in_f32(r, s);
+    }
+  } else {
+    // recompute x' = Pi_tau x (kept for dL/dQ_P), z1' = D_P x', z2' = z1' W0p^T
+    if ((rc = permute(true, X, nullptr, w.xg, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
+    if ((rc = blockmul(w.xg, q.qbP, w.z1, N, n, S.b, S.kP, s))) return rc;
+    {
+      Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+      launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
+    }
+    if ((rc = check_launch("recompute"))) return rc;
+    // R side: gY' = Pi_sigma gY (kept), gz2' = D_R^T gY' (blocks Q_R^T)
+    if ((rc = permute(true, dY, nullptr, w.gyg, w.gz2, sigma, N, m, S.kR * S.b, S.es, s))) return rc;
+    if ((rc = blockmul(w.gyg, q.qtR, w.gz2, N, m, S.b, S.kR, s))) return rc;
   }
+  // G_R = gY'^T z2' per block
   {
-    Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-    if (S.f32) launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
-    else launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
-  }
-  if ((rc = check_launch("recompute"))) return rc;
-  // R side: gY' = Pi_sigma gY (kept), gz2' = D_R^T gY' (blocks Q_R), G_R = gY'^T z2'
-  XformArgs r{};
-  r.in = dY; r.out = w.gz2; r.emit = w.gyg; r.perm = sigma; r.N = N; r.W = (int)S.m; r.B = S.b; r.k = S.kR;
-  {
-    // algorithmic bytes: read gY, write gz2' (the gathered copy is implementation traffic)
-    Tm tm(s, "xform_gather_in", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
-    if (S.f32) { r.bq = q.q32R; r.trans = 1; launch_gather_in_f32(r, s); }
-    else { r.bq = q.qtR; if (!launch_gather_in_bf16(r, s)) return fail(POETX_ESHAPE, "no transform config for m=%lld", (long long)S.m); }
-  }
-  {
-    // algorithmic bytes: the read of z2' (gY is counted with the transform)
-    Tm tm(s, "gram", xf_flops(N, S.kR, S.b), 1.0 * N * S.m * S.es);
-    launch_gram(S.f32, w.gyg, w.z2, N, (int)S.m, S.b, S.kR, w.GR, w.part, s);
+    // algorithmic bytes: the reads of gY' and z2'
+    Tm tm(s, "gram", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
+    launch_gram(S.f32, w.gyg, w.z2, N, m, S.b, S.kR, w.GR, w.part, s);
   }
   if ((rc = check_launch("R-side backward"))) return rc;
   // gz1' = gz2' W0p (into the z1' buffer)
   void* gz1 = w.z1;
   {
-    Tm tm(s, "gemm_nn", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+    Tm tm(s, S.f32 ? "gemm_fp32" : "gemm_nn", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
     if (S.f32) launch_gemm_f32(true, (const float*)w.gz2, (const float*)W0p, (float*)gz1, N, S.n, S.m, s);
     else launch_gemm_bf16(true, (const uint16_t*)w.gz2, (const uint16_t*)W0p, (uint16_t*)gz1, N, S.n, S.m, s);
   }
-  // P side: G_P = gz1'^T x', dX = Pi_tau^T D_P^T gz1'
+  // G_P = gz1'^T x' per block
   {
-    // algorithmic bytes: the read of x (gz1' is counted with the dX transform)
-    Tm tm(s, "gram", xf_flops(N, S.kP, S.b), 1.0 * N * S.n * S.es);
-    launch_gram(S.f32, gz1, w.xg, N, (int)S.n, S.b, S.kP, w.GP, w.part, s);
+    Tm tm(s, "gram", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
+    launch_gram(S.f32, gz1, w.xg, N, n, S.b, S.kP, w.GP, w.part, s);
   }
+  if ((rc = check_launch("P-side gradient"))) return rc;
+  // dX = Pi_tau^T D_P^T gz1'
   if (dX) {
-    XformArgs t{};
-    t.in = gz1; t.out = dX; t.perm = tau; t.N = N; t.W = (int)S.n; t.B = S.b; t.k = S.kP;
-    Tm tm(s, "xform_scatter_out", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
-    if (S.f32) { t.bq = q.q32P; t.trans = 1; launch_scatter_out_f32(t, s); }
-    else { t.bq = q.qtP; if (!launch_scatter_out_bf16(t, s)) return fail(POETX_ESHAPE, "no transform config for n=%lld", (long long)S.n); }
+    if (S.f32) {
+      XformArgs t{};
+      t.in = gz1; t.out = dX; t.perm = tau; t.N = N; t.W = n; t.B = S.b; t.k = S.kP; t.bq = q.q32P; t.trans = 1;
+      Tm tm(s, "xform_fp32", xf_flops(N, S.kP, S.b), 2.0 * N * n * S.es);
+      launch_scatter_out_f32(t, s);
+    } else {
+      // x' is no longer needed: its buffer takes the block products
+      if ((rc = blockmul(gz1, q.qtP, w.xg, N, n, S.b, S.kP, s))) return rc;
+      if ((rc = permute(false, w.xg, gz1, dX, nullptr, tau, N, n, S.kP * S.b, S.es, s))) return rc;
+    }
   }
   if ((rc = check_launch("P-side backward"))) return rc;
   // chain rule through the Cayley map onto the stored upper triangle

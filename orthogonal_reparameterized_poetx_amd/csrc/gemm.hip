@@ -23,22 +23,56 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, const_cast<uint16_t*>(p)));
 }
 
-template <bool NN>
-__global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
-                                                        uint16_t* __restrict__ C, int M, int N, int K, int tiles_n,
-                                                        int ntiles) {
-  __shared__ __align__(16) uint16_t As[2][GBM * GBK];
-  __shared__ __align__(16) uint16_t Bs[2][GBN * GBK];
+// 16-byte global -> LDS copy that bypasses the VGPRs: lane i of the wave
+// writes lds_base + 16 i (lds_base must be wave-uniform).  Streaming tiles this
+// way, one contiguous KiB per instruction, reaches several times the L2
+// bandwidth of register loads in MFMA-fragment order.
+__device__ __forceinline__ void g2l16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Buffer resource over [base, base + bytes): loads past the end read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nrec = (int)(bytes < 0x7fffffff ? (bytes > 0 ? bytes : 0) : 0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+// 16-byte buffer load straight into LDS: lane i writes lds_base + 16 i
+__device__ __forceinline__ void b2l16(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+}
+
+// LDS tile layouts (bf16, 16-byte chunks XOR-swizzled by row):
+//   A (and NT B): [256 rows][64 k], chunk c of row r stored at chunk c ^ (r & 7)
+//   NN B:         [64 k rows][256 n], chunk c of row r stored at chunk c ^ (r & 7)
+// The direct loads pick each lane's source chunk so that the fixed lane ->
+// LDS slot placement produces exactly this layout.
+// BATCHED only names the instantiation used for batched block products, so
+// that profiles tell it apart from the weight products.
+template <bool NN, bool BATCHED>
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
+  // two buffers as separate LDS objects, each named at compile time below, so
+  // the compiler can tell reads of one from the asynchronous fill of the other
+  __shared__ __align__(16) uint16_t As0[GBM * GBK], As1[GBM * GBK];
+  __shared__ __align__(16) uint16_t Bs0[GBN * GBK], Bs1[GBN * GBK];
   // XCD-aware tile order: dispatch id d runs on XCD d % 8; give each XCD a
-  // contiguous run of tiles (row-major over the tile grid).
+  // contiguous run of tiles (batch-major, then row-major over the tile grid).
   const int d = blockIdx.x;
   const int per = (ntiles + 7) / 8;
   const int tile = (d % 8) * per + d / 8;
   if (tile >= ntiles) return;
-  const int bm = tile / tiles_n, bn = tile % tiles_n;
+  const int tpb = tiles_m * tiles_n;
+  const int bz = tile / tpb, rem = tile - bz * tpb;
+  const int bm = rem / tiles_n, bn = rem - bm * tiles_n;
   const int m0 = bm * GBM, n0 = bn * GBN;
+  const int M = g.M, N = g.N, K = g.K;
+  const uint16_t* __restrict__ A = g.A + bz * g.sA;
+  const uint16_t* __restrict__ Bm = g.B + bz * g.sB;
+  uint16_t* __restrict__ C = g.C + bz * g.sC;
+  const int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
   const int wm = wave >> 2, wn = wave & 3;
 
   f32x16 acc[4][2];
@@ -49,48 +83,59 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
+  // full K step: asynchronous buffer loads into LDS.  Per lane, one 32-bit
+  // byte offset per instruction is loop-invariant; the K position is a
+  // scalar offset.  Rows past M (or N) lie outside the tile's buffer range
+  // and read zero.
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * lda, (int64_t)min(M - m0, GBM) * lda * 2);
+  const __amdgpu_buffer_rsrc_t rb = NN ? make_rsrc(Bm + n0, ((int64_t)K * ldb - n0) * 2)
+                                       : make_rsrc(Bm + (int64_t)n0 * ldb, (int64_t)min(N - n0, GBN) * ldb * 2);
+  int voa[4], vob[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = wave * 32 + q * 8 + (lane >> 3);
+    const int cs = (lane & 7) ^ (lane >> 3);
+    voa[q] = (int)(((int64_t)r * lda + cs * 8) * 2);
+    if constexpr (!NN) {
+      vob[q] = (int)(((int64_t)r * ldb + cs * 8) * 2);
+    } else {
+      const int kr = wave * 8 + q * 2 + (lane >> 5);
+      const int cn = (lane & 31) ^ (kr & 7);
+      vob[q] = (int)(((int64_t)kr * ldb + cn * 8) * 2);
+    }
+  }
+  auto dload = [&](int k0, uint16_t* as_, uint16_t* bs_) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      b2l16(ra, voa[q], k0 * 2, as_ + (wave * 32 + q * 8) * GBK);
+      if constexpr (!NN) b2l16(rb, vob[q], k0 * 2, bs_ + (wave * 32 + q * 8) * GBK);
+      else b2l16(rb, vob[q], (int)((int64_t)k0 * ldb * 2), bs_ + (wave * 8 + q * 2) * GBN);
+    }
+  };
+  // partial last K step: the loads above also fetch columns (A, NT B) or
+  // rows (NN B) past K; zero them in LDS once the loads have landed
+  auto zero_tail = [&](int k0, uint16_t* as_, uint16_t* bs_) {
+    const int kv = K - k0;                  // valid k in this step (multiple of 8)
+    if (kv >= GBK) return;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + 512 * q;
       const int row = e >> 3, c = e & 7;
-      const int gm = m0 + row, gk = k0 + c * 8;
-      ra[q] = (gm < M && gk < K) ? ldg16(A + (int64_t)gm * K + gk) : make_uint4(0, 0, 0, 0);
-      if constexpr (!NN) {
-        const int gn = n0 + row;
-        rb[q] = (gn < N && gk < K) ? ldg16(Bm + (int64_t)gn * K + gk) : make_uint4(0, 0, 0, 0);
-      } else {
+      if (c * 8 >= kv) {
+        *reinterpret_cast<uint4*>(as_ + row * GBK + ((c ^ (row & 7)) << 3)) = make_uint4(0, 0, 0, 0);
+        if constexpr (!NN) *reinterpret_cast<uint4*>(bs_ + row * GBK + ((c ^ (row & 7)) << 3)) = make_uint4(0, 0, 0, 0);
+      }
+      if constexpr (NN) {
         const int kr = e >> 5, cn = e & 31;
-        const int gkr = k0 + kr, gn = n0 + cn * 8;
-        rb[q] = (gkr < K && gn < N) ? ldg16(Bm + (int64_t)gkr * N + gn) : make_uint4(0, 0, 0, 0);
+        if (kr >= kv) *reinterpret_cast<uint4*>(bs_ + kr * GBN + ((cn ^ (kr & 7)) << 3)) = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid + 512 * q;
-      const int row = e >> 3, c = e & 7;
-      *reinterpret_cast<uint4*>(&As[buf][row * GBK + ((c ^ (row & 7)) << 3)]) = ra[q];
-      if constexpr (!NN) {
-        *reinterpret_cast<uint4*>(&Bs[buf][row * GBK + ((c ^ (row & 7)) << 3)]) = rb[q];
-      } else {
-        const int kr = e >> 5, cn = e & 31;
-        *reinterpret_cast<uint4*>(&Bs[buf][kr * GBN + ((cn ^ (kr & 7)) << 3)]) = rb[q];
-      }
-    }
-  };
-
-  const int nk = (K + GBK - 1) / GBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GBK);
-    const uint16_t* as = As[buf];
-    const uint16_t* bs = Bs[buf];
+  auto compute = [&](const uint16_t* as, const uint16_t* bs) {
+    // recompute the fragment addresses here rather than keep two hoisted sets
+    // (one per buffer) alive across the loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 af[4], bfr[2];
@@ -107,13 +152,13 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
           const int ch = 2 * s + (lane >> 5);
           bfr[j] = *reinterpret_cast<const bf16x8*>(&bs[row * GBK + ((ch ^ (row & 7)) << 3)]);
         } else {
-          const int g = lane >> 4, q = lane & 15;
-          const int ncol = wn * 64 + j * 32 + 16 * (g & 1) + 4 * (q & 3);
+          const int gq = lane >> 4, q = lane & 15;
+          const int ncol = wn * 64 + j * 32 + 16 * (gq & 1) + 4 * (q & 3);
           const int chn = ncol >> 3, within = ncol & 7;
           i16x4 h[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int kr = 16 * s + 8 * (g >> 1) + 4 * hh + (q >> 2);
+            const int kr = 16 * s + 8 * (gq >> 1) + 4 * hh + (q >> 2);
             h[hh] = ds_read_tr16(&bs[kr * GBN + ((chn ^ (kr & 7)) << 3) + within]);
           }
           typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -126,9 +171,30 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+  };
+
+  // double buffer, unrolled by two so each step names its buffers
+  // statically; pairs of steps in the loop (one back edge, no early exit),
+  // an odd last step after it
+  const int nk = (K + GBK - 1) / GBK;
+  dload(0, As0, Bs0);
+  vm_wait();
+  zero_tail(0, As0, Bs0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    dload((kt + 1) * GBK, As1, Bs1);
+    compute(As0, Bs0);
+    vm_wait();
+    zero_tail((kt + 1) * GBK, As1, Bs1);
+    __syncthreads();
+    if (kt + 2 < nk) dload((kt + 2) * GBK, As0, Bs0);
+    compute(As1, Bs1);
+    vm_wait();
+    if (kt + 2 < nk) zero_tail((kt + 2) * GBK, As0, Bs0);
     __syncthreads();
   }
+  if (kt < nk) compute(As0, Bs0);
 
   // epilogue: bf16 stores
 #pragma unroll
@@ -140,50 +206,68 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int gm = m0 + wm * 128 + i * 32 + c32_row(lane, r);
-          if (gm < M) C[(int64_t)gm * N + gn] = f32_to_bits(acc[i][j][r]);
+          if (gm < M) C[(int64_t)gm * ldc + gn] = f32_to_bits(acc[i][j][r]);
         }
       }
     }
 }
 
-// Generic bf16 GEMM for shapes the tiled kernel cannot take (K or N not a
-// multiple of 8): 16x16 outputs per workgroup, LDS tiles, fp32 sums.
+// Generic bf16 GEMM for shapes the tiled kernel cannot take (a dimension,
+// stride or offset not a multiple of 8): 16x16 outputs per workgroup, LDS
+// tiles, fp32 sums.
 template <bool NN>
-__global__ __launch_bounds__(256) void gemm_bf16_generic_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
-                                                                uint16_t* __restrict__ C, int M, int N, int K) {
+__global__ __launch_bounds__(256) void gemm_bf16_generic_kernel(GemmArgs g) {
   __shared__ float as[16][17], bs[16][17];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int M = g.M, N = g.N, K = g.K;
+  const uint16_t* __restrict__ A = g.A + blockIdx.z * g.sA;
+  const uint16_t* __restrict__ Bm = g.B + blockIdx.z * g.sB;
+  uint16_t* __restrict__ C = g.C + blockIdx.z * g.sC;
   const int gm = blockIdx.y * 16 + ty, gn = blockIdx.x * 16 + tx;
   float s = 0.f;
   for (int k0 = 0; k0 < K; k0 += 16) {
     const int ar = blockIdx.y * 16 + ty, ak = k0 + tx;
-    as[ty][tx] = (ar < M && ak < K) ? bits_to_f32(A[(int64_t)ar * K + ak]) : 0.f;
+    as[ty][tx] = (ar < M && ak < K) ? bits_to_f32(A[(int64_t)ar * g.lda + ak]) : 0.f;
     const int bk = k0 + ty, bn = blockIdx.x * 16 + tx;
     float bv = 0.f;
-    if (bk < K && bn < N) bv = NN ? bits_to_f32(Bm[(int64_t)bk * N + bn]) : bits_to_f32(Bm[(int64_t)bn * K + bk]);
+    if (bk < K && bn < N) bv = NN ? bits_to_f32(Bm[(int64_t)bk * g.ldb + bn]) : bits_to_f32(Bm[(int64_t)bn * g.ldb + bk]);
     bs[ty][tx] = bv;
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) s = fmaf(as[ty][kk], bs[kk][tx], s);
     __syncthreads();
   }
-  if (gm < M && gn < N) C[(int64_t)gm * N + gn] = f32_to_bits(s);
+  if (gm < M && gn < N) C[(int64_t)gm * g.ldc + gn] = f32_to_bits(s);
+}
+
+static bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return;
+  const bool tiled = g.K > 0 && g.K % 8 == 0 && g.N % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+                     g.sA % 8 == 0 && g.sB % 8 == 0 && aligned8(g.A) && aligned8(g.B);
+  if (tiled) {
+    const int tn = (g.N + GBN - 1) / GBN, tm = (g.M + GBM - 1) / GBM;
+    const int nt = tn * tm * g.batch;
+    const int grid = ((nt + 7) / 8) * 8;
+    if (nn) hipLaunchKernelGGL((gemm_bf16_kernel<true, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    else if (g.batch > 1) hipLaunchKernelGGL((gemm_bf16_kernel<false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    else hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+  } else {
+    dim3 grid((unsigned)((g.N + 15) / 16), (unsigned)((g.M + 15) / 16), (unsigned)g.batch);
+    if (nn) hipLaunchKernelGGL(gemm_bf16_generic_kernel<true>, grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL(gemm_bf16_generic_kernel<false>, grid, dim3(256), 0, s, g);
+  }
 }
 
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N, int64_t K,
                       hipStream_t s) {
-  if (M <= 0 || N <= 0) return;
-  if ((K % 8) == 0 && (N % 8) == 0 && K > 0) {
-    const int tn = (int)((N + GBN - 1) / GBN), tm = (int)((M + GBM - 1) / GBM);
-    const int nt = tn * tm;
-    const int grid = ((nt + 7) / 8) * 8;
-    if (nn) hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3(grid), dim3(512), 0, s, A, Bm, C, (int)M, (int)N, (int)K, tn, nt);
-    else hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3(grid), dim3(512), 0, s, A, Bm, C, (int)M, (int)N, (int)K, tn, nt);
-  } else {
-    dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16));
-    if (nn) hipLaunchKernelGGL(gemm_bf16_generic_kernel<true>, grid, dim3(256), 0, s, A, Bm, C, (int)M, (int)N, (int)K);
-    else hipLaunchKernelGGL(gemm_bf16_generic_kernel<false>, grid, dim3(256), 0, s, A, Bm, C, (int)M, (int)N, (int)K);
-  }
+  GemmArgs g{};
+  g.A = A; g.B = Bm; g.C = C;
+  g.M = (int)M; g.N = (int)N; g.K = (int)K;
+  g.lda = K; g.ldb = nn ? N : K; g.ldc = N;
+  g.batch = 1;
+  launch_gemm_bf16(nn, g, s);
 }
 
 // fp32 GEMM: 64x64 tile, 256 threads x (4x4), K chunks of 16, fp32 FMA

@@ -47,9 +47,23 @@ void launch_skew_project(const float* GS, int b, int nblk, float* dth0, int n0, 
                          hipStream_t s);
 
 // ---- block transforms (transform.hip)
+// bf16 row permutations of a token-major [N][W] matrix:
+//   gather : out[t][j] = in[t][perm[j]]; if tail_out, also tail_out[t][j] for j >= tail0
+//   scatter: out[t][perm[j]] = src[t][j], src = in (j < tail0) or tail_in (j >= tail0; NULL = in)
+struct PermArgs {
+  const uint16_t* in;
+  const uint16_t* tail_in;
+  uint16_t* out;
+  uint16_t* tail_out;
+  const int32_t* perm;
+  int64_t N;
+  int W, tail0;
+};
+void launch_permute_bf16(bool gather, const PermArgs& a, hipStream_t s);
+// fp32 transforms, permutation and block product in one pass:
 // gather-in : out[t][l*B+i] = sum_kk in[t][perm[l*B+kk]] * Mq(kk, i); tail copies in[t][perm[j]]
 // scatter-out: out[t][perm[l*B+i]] = sum_kk in[t][l*B+kk] * Mq(kk, i); tail copies in[t][j]
-// with Mq(kk, i) = bq[l][i][kk] (bf16 path) or, for fp32, q[l][i][kk] (trans=0) / q[l][kk][i] (trans=1)
+// with Mq(kk, i) = q[l][i][kk] (trans=0) / q[l][kk][i] (trans=1)
 struct XformArgs {
   const void* in;
   void* out;
@@ -58,16 +72,26 @@ struct XformArgs {
   const void* bq;
   int64_t N;
   int W, B, k;
-  int trans;            // fp32 only
+  int trans;
 };
-// returns false if no kernel configuration fits this shape
-bool launch_gather_in_bf16(const XformArgs& a, hipStream_t s);
-bool launch_scatter_out_bf16(const XformArgs& a, hipStream_t s);
 void launch_gather_in_f32(const XformArgs& a, hipStream_t s);
 void launch_scatter_out_f32(const XformArgs& a, hipStream_t s);
 
 // ---- dense GEMMs (gemm.hip): C[M][N] = A[M][K] * op(B)
 // nt: B is [N][K] (C = A B^T); nn: B is [K][N] (C = A B)
+// Batched bf16 GEMM with strides (elements): for z < batch,
+//   NT: C_z[M][N] = A_z[M][K] * B_z[N][K]^T,  NN: C_z[M][N] = A_z[M][K] * B_z[K][N]
+// with X_z = X + z * sX and row strides lda, ldb, ldc.
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  int64_t sA, sB, sC;
+  int batch;
+};
+void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s);
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N,
                       int64_t K, hipStream_t s);
 void launch_gemm_f32(bool nn, const float* A, const float* Bm, float* C, int64_t M, int64_t N, int64_t K,
