@@ -75,6 +75,9 @@ def parse():
                          "'bench.py --calibrate-copy' into profiles/traffic_<class>.json")
     ap.add_argument("--kernel-stats", metavar="CSV",
                     help="no GPU: summarize a rocprofv3 --stats kernel_stats.csv by kernel class")
+    ap.add_argument("--workload", choices=("layerset", "stack24"), default="layerset",
+                    help="layerset: fwd+bwd of the LLaMA-1B layer set (default); stack24: one training step of the "
+                         "24-layer stack with Adam and the global merge")
     ap.add_argument("--per-layer-builds", action="store_true",
                     help="let every forward / backward call build its own blocks (one builder launch per call) "
                          "instead of one batched build per pass")
@@ -189,8 +192,168 @@ def kernel_stats(path):
                                            float(row["TotalDurationNs"]) * 1e-6, float(row["AverageNs"]) * 1e-6))
 
 
+# ---------------------------------------------------------------------------
+# 24-layer stack of layer-set shapes: one training step over 168 matrices
+# ---------------------------------------------------------------------------
+class Stack:
+    """The 24-layer stack resident in HBM: bf16 W0p per matrix in its working
+    layout, all generators (and their gradients and Adam moments) in single
+    fp32 buffers so the optimizer step is one launch, and per-matrix inputs,
+    upstream gradients and outputs.
+
+    Matrices listed in ``exact`` (and every matrix sharing their input) take
+    their values from the shared numpy recipe of ``workloads`` so the oracle
+    can check them; the rest draw the same distributions on the device from a
+    torch generator seeded by (config, matrix, stream)."""
+
+    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=()):
+        import math
+        import numpy as np
+        self.P, self.torch, self.N = P, torch, N
+        cfg = WL.CONFIGS[5]
+        b = cfg["b"]
+        nt = b * (b - 1) // 2
+        mats = [(l, idx, m, n) for l in range(nlayers) for idx, (_, m, n) in enumerate(cfg["mats"])]
+        total = sum(m // b + n // b for _, _, m, n in mats) * nt
+        f32 = torch.float32
+        self.theta = torch.zeros(total, dtype=f32, device=dev)
+        self.grad = torch.zeros_like(self.theta)
+        self.m1 = torch.zeros_like(self.theta)
+        self.v1 = torch.zeros_like(self.theta)
+        gen = torch.Generator(device=dev)
+
+        def drawn(c, j, s, shape, var, dt):
+            gen.manual_seed((c << 40) | (j << 8) | s)
+            return (torch.randn(shape, generator=gen, device=dev, dtype=f32) * math.sqrt(var)).to(dt)
+
+        def up(pair, dt):
+            a = np.ascontiguousarray(pair[0])
+            if dt == torch.bfloat16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a.astype(np.float32)).to(dev)
+
+        exact_owners = {WL.input_owner(cfg, j) for j in exact}
+        pool = {}
+        self.layers, self.X, self.gY, self.out = [], {}, [], []
+        off = 0
+        bf = torch.bfloat16
+        for l, idx, m, n in mats:
+            j = 7 * l + idx
+            lay = P.PoetxLayer(m, n, b, "bf16", dev, perm_seed=WL.perm_seed(5, j), ws_pool=pool)
+            kR, kP = m // b, n // b
+            lay.thR = self.theta[off:off + kR * nt].view(kR, nt)
+            lay.dR = self.grad[off:off + kR * nt].view(kR, nt)
+            off += kR * nt
+            lay.thP = self.theta[off:off + kP * nt].view(kP, nt)
+            lay.dP = self.grad[off:off + kP * nt].view(kP, nt)
+            off += kP * nt
+            owner = WL.input_owner(cfg, j)
+            if j in exact:
+                inp = WL.matrix_inputs(5, j, N=N)
+                lay.pack(up(inp["W0"], bf))
+                lay.thR.copy_(up(inp["thR"], f32))
+                lay.thP.copy_(up(inp["thP"], f32))
+                gy = up(inp["gY"], bf)
+            else:
+                lay.pack(drawn(5, j, 1, (m, n), cfg["w_var"], bf))
+                lay.thR.copy_(drawn(5, j, 2, (kR, nt), cfg["theta_var"], f32))
+                lay.thP.copy_(drawn(5, j, 3, (kP, nt), cfg["theta_var"], f32))
+                gy = drawn(5, j, 5, (N, m), 1.0, bf)
+            if owner not in self.X:
+                if owner in exact_owners:
+                    self.X[owner] = up(WL.stored(WL.gaussian(5, owner, 4, (N, n), 1.0), "bf16"), bf)
+                else:
+                    self.X[owner] = drawn(5, owner, 4, (N, n), 1.0, bf)
+            lay.x_key = owner
+            lay.j = j
+            self.layers.append(lay)
+            self.gY.append(gy)
+            self.out.append(dict(Y=torch.empty(N, m, dtype=bf, device=dev), dX=torch.empty(N, n, dtype=bf, device=dev)))
+        for lay in self.layers:
+            for kind in ("forward", "backward", "merge"):
+                lay.block_buffers(kind)
+            lay.workspace(P.OP_FORWARD_BLOCKS, N)
+            lay.workspace(P.OP_BACKWARD_BLOCKS, N)
+            lay.workspace(P.OP_MERGE_BLOCKS)
+        self.adam_steps = 0
+
+    def forward_backward(self):
+        P = self.P
+        P.build_layer_blocks(self.layers, "forward")
+        for lay, o in zip(self.layers, self.out):
+            lay.forward_blocks(self.X[lay.x_key], Y=o["Y"])
+        P.build_layer_blocks(self.layers, "backward")
+        for lay, g, o in zip(reversed(self.layers), reversed(self.gY), reversed(self.out)):
+            lay.backward_blocks(self.X[lay.x_key], g, dX=o["dX"], dthR=lay.dR, dthP=lay.dP)
+
+    def adam(self):
+        self.adam_steps += 1
+        self.P.poetx_adam_step(self.theta, self.grad, self.m1, self.v1, self.theta.numel(), self.adam_steps)
+
+    def merge(self):
+        self.P.build_layer_blocks(self.layers, "merge")
+        for lay in self.layers:
+            lay.merge_blocks()
+
+    def step(self):
+        self.forward_backward()
+        self.adam()
+        self.merge()
+
+
+def bench_stack(args):
+    import torch
+
+    import workloads as WL
+    import orthogonal_reparameterized_poetx_amd as P
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    N = args.tokens or WL.CONFIGS[5]["N"]
+    st = Stack(P, WL, torch, dev, N)
+    torch.cuda.synchronize()
+    resident = torch.cuda.memory_allocated()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    fb = mg = ad = 0.0
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        st.forward_backward()
+        ev[1].record(stream)
+        st.adam()
+        ev[2].record(stream)
+        st.merge()
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        fb += ev[0].elapsed_time(ev[1])
+        ad += ev[1].elapsed_time(ev[2])
+        mg += ev[2].elapsed_time(ev[3])
+    k = args.steps
+    ms = (fb + ad + mg) / k
+    print(json.dumps({
+        "metric": "POET-X 24-layer stack training step (fwd+bwd, Adam, global merge), 1 GPU",
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": k, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Gaussian inputs with the stack's shapes)",
+        "config": {"workload": WL.CONFIGS[5]["name"], "tokens": N, "matrices": len(st.layers), "b": WL.CONFIGS[5]["b"]},
+        "phases_ms": {"fwd_bwd": round(fb / k, 3), "adam": round(ad / k, 3), "merge": round(mg / k, 3)},
+        "generators": st.theta.numel(),
+        "resident_gb": round(resident / 1e9, 3),
+        "peak_hbm_gb": round(torch.cuda.max_memory_allocated() / 1e9, 3),
+    }), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload == "stack24":
+        if args.gpus != 1:
+            print("bench.py measures one GPU. Run with --gpus 1.", file=sys.stderr)
+            sys.exit(2)
+        bench_stack(args)
+        return
     if args.traffic_from:
         traffic_from(*args.traffic_from)
         return

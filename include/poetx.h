@@ -83,6 +83,7 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
 #define POETX_OP_MERGE 2
 #define POETX_OP_FORWARD_BLOCKS 3  /* poetx_forward_blocks  */
 #define POETX_OP_BACKWARD_BLOCKS 4 /* poetx_backward_blocks */
+#define POETX_OP_MERGE_BLOCKS 5    /* poetx_merge_blocks    */
 
 typedef struct {
   int64_t m;      /* rows of W0 = output features                         */
@@ -118,7 +119,8 @@ typedef struct {
  *   fp32 layer, forward and backward: Q32R, Q32P;
  *   bf16 layer, forward:  QR, QP (bf16 Q);
  *   bf16 layer, backward: Q32R, Q32P (fp32 Q, for the chain rule), QP,
- *                         QTR, QTP (bf16 Q^T).
+ *                         QTR, QTP (bf16 Q^T);
+ *   merge: Q32R, Q32P (fp32 layer) or QR, QTP (bf16 layer).
  * The others may be NULL.
  */
 typedef struct {
@@ -236,6 +238,17 @@ int poetx_backward_blocks(const poetx_layer* layer, const void* W0p, const poetx
 int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int32_t* sigma,
                 int32_t* tau, uint64_t perm_seed, uint64_t merge_index, void* ws,
                 size_t ws_bytes, void* stream);
+
+/*
+ * poetx_merge with the Cayley blocks built beforehand from the layer's
+ * current generators (poetx_build_block_sets lets a merge of many layers
+ * share builder launches).  Same arguments and results as poetx_merge, the
+ * blocks (poetx_blocks above) added.  Workspace:
+ * poetx_workspace_bytes(layer, 0, POETX_OP_MERGE_BLOCKS).
+ */
+int poetx_merge_blocks(const poetx_layer* layer, void* W0p, const poetx_blocks* blocks, float* thR,
+                       float* thP, int32_t* sigma, int32_t* tau, uint64_t perm_seed,
+                       uint64_t merge_index, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * a11 on the host: the permutation poetx_merge draws for (seed, merge_index,

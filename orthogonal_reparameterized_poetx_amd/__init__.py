@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     OP_FORWARD,
     OP_FORWARD_BLOCKS,
     OP_MERGE,
+    OP_MERGE_BLOCKS,
     POETX_ACCUMULATE_GRAD,
     POETX_BF16,
     POETX_F32,
@@ -34,6 +35,7 @@ from ._lib import (  # noqa: F401
     poetx_forward_blocks,
     poetx_make_permutation,
     poetx_merge,
+    poetx_merge_blocks,
     timing_enable,
     timing_summary,
     workspace_bytes,

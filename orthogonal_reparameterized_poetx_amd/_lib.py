@@ -15,14 +15,15 @@ LIB_PATH = os.path.join(_HERE, "libpoetx.so")
 POETX_F32 = 0
 POETX_BF16 = 1
 POETX_ACCUMULATE_GRAD = 1
-OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS = 0, 1, 2, 3, 4
+OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS, OP_MERGE_BLOCKS = 0, 1, 2, 3, 4, 5
 
 _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDTYPE",
            -4: "POETX_EWORKSPACE", -5: "POETX_EHIP"}
 
 EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
             "poetx_build_block_sets", "poetx_forward", "poetx_forward_blocks", "poetx_backward",
-            "poetx_backward_blocks", "poetx_merge", "poetx_make_permutation", "poetx_adam_step",
+            "poetx_backward_blocks", "poetx_merge", "poetx_merge_blocks", "poetx_make_permutation",
+            "poetx_adam_step",
             "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
 
 
@@ -97,6 +98,7 @@ def lib():
         "poetx_backward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_backward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_merge": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
+        "poetx_merge_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
         "poetx_make_permutation": (ctypes.c_int, [u64, u64, i32, i64, vp]),
         "poetx_adam_step": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_float, vp]),
@@ -196,6 +198,13 @@ def poetx_merge(layer, W0p, thR, thP, sigma, tau, perm_seed, merge_index, ws, st
     _check("poetx_merge", lib().poetx_merge(ctypes.byref(layer), _ptr(W0p), _ptr(thR), _ptr(thP), _ptr(sigma),
                                             _ptr(tau), int(perm_seed) & (2 ** 64 - 1), int(merge_index),
                                             _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def poetx_merge_blocks(layer, W0p, blocks, thR, thP, sigma, tau, perm_seed, merge_index, ws, stream=None):
+    _check("poetx_merge_blocks", lib().poetx_merge_blocks(
+        ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(thR), _ptr(thP),
+        _ptr(sigma), _ptr(tau), int(perm_seed) & (2 ** 64 - 1), int(merge_index), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def poetx_make_permutation(seed, merge_index, side, n):

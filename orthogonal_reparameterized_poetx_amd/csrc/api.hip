@@ -349,18 +349,20 @@ struct MrgWs {
   uint64_t* keys;
   int32_t *snew, *tnew, *sinv, *tinv;
 };
-MrgWs plan_merge(const Shape& S, void* base, size_t* bytes) {
+MrgWs plan_merge(const Shape& S, bool own, void* base, size_t* bytes) {
   Arena a(base);
   MrgWs w{};
   const size_t bb = (size_t)S.b * S.b;
-  if (S.f32) {
-    w.q32R = a.take<float>(S.kR * bb);
-    w.q32P = a.take<float>(S.kP * bb);
-  } else {
-    w.qbR = a.take<uint16_t>(S.kR * bb);
-    w.qtP = a.take<uint16_t>(S.kP * bb);
+  if (own) {
+    if (S.f32) {
+      w.q32R = a.take<float>(S.kR * bb);
+      w.q32P = a.take<float>(S.kP * bb);
+    } else {
+      w.qbR = a.take<uint16_t>(S.kR * bb);
+      w.qtP = a.take<uint16_t>(S.kP * bb);
+    }
+    w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
   }
-  w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
   w.V = a.take<char>((size_t)S.m * S.n * S.es * (S.f32 ? 2 : 1));
   w.keys = a.take<uint64_t>(std::max(S.m, S.n));
   w.snew = a.take<int32_t>(S.m);
@@ -566,6 +568,14 @@ int zero_grads(const Shape& S, bool accum, float* dthR, float* dthP, hipStream_t
   return check_launch("zero gradients");
 }
 
+int check_merge_blocks(const Shape& S, const poetx_blocks* q) {
+  if (!q) return fail(POETX_EINVAL, "blocks is NULL");
+  const bool R = S.kR > 0, P = S.kP > 0;
+  if (S.f32 && ((R && !q->Q32R) || (P && !q->Q32P))) return fail(POETX_EINVAL, "NULL fp32 blocks (Q32R / Q32P)");
+  if (!S.f32 && ((R && !q->QR) || (P && !q->QTP))) return fail(POETX_EINVAL, "NULL bf16 blocks (QR / QTP)");
+  return POETX_OK;
+}
+
 int check_blocks(const Shape& S, const poetx_blocks* q, bool backward) {
   if (!q) return fail(POETX_EINVAL, "blocks is NULL");
   const bool R = S.kR > 0, P = S.kP > 0;
@@ -577,6 +587,36 @@ int check_blocks(const Shape& S, const poetx_blocks* q, bool backward) {
   if (!S.f32 && backward && ((P && !q->QP) || (R && !q->QTR) || (P && !q->QTP)))
     return fail(POETX_EINVAL, "NULL bf16 blocks (QP / QTR / QTP)");
   return POETX_OK;
+}
+
+// merge after the blocks exist: tile products, new permutations, relayout,
+// generator reset (a10, a11)
+int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
+               uint64_t perm_seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
+  int rc;
+  {
+    Tm tm(s, "merge_tiles", 4.0 * S.m * S.n * S.b, 2.0 * S.m * S.n * S.es);
+    if (S.f32) launch_merge_tiles(true, W0p, w.V, q.q32R, q.q32P, S.m, S.n, S.b, S.kR, S.kP, s);
+    else launch_merge_tiles(false, W0p, w.V, q.qbR, q.qtP, S.m, S.n, S.b, S.kR, S.kP, s);
+  }
+  if ((rc = check_launch("merge tiles"))) return rc;
+  // new permutations, old inverses, relayout into the caller's buffer
+  {
+    Tm tm(s, "merge_permutations", 0.0, 0.0);
+    launch_perm_keys_rank(perm_seed, merge_index, 0, S.m, w.keys, w.snew, s);
+    launch_perm_keys_rank(perm_seed, merge_index, 1, S.n, w.keys, w.tnew, s);
+    launch_invert_perm(sigma, S.m, w.sinv, s);
+    launch_invert_perm(tau, S.n, w.tinv, s);
+  }
+  {
+    Tm tm(s, "merge_relayout", 0.0, 2.0 * S.m * S.n * S.es);
+    launch_relayout(S.f32, w.V, W0p, w.sinv, w.snew, w.tinv, w.tnew, S.m, S.n, s);
+  }
+  launch_copy_i32(w.snew, sigma, S.m, s);
+  launch_copy_i32(w.tnew, tau, S.n, s);
+  launch_fill_f32(thR, 0.f, (int64_t)S.kR * (S.b * (S.b - 1) / 2), s);
+  launch_fill_f32(thP, 0.f, (int64_t)S.kP * (S.b * (S.b - 1) / 2), s);
+  return check_launch("merge relayout");
 }
 
 Blk blk_of(const poetx_blocks* q) {
@@ -600,15 +640,17 @@ size_t poetx_build_workspace_bytes(int64_t nblocks, int32_t b) {
 
 size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op) {
   if (validate_layer(layer) != POETX_OK) return 0;
-  if (op != POETX_OP_MERGE && validate_N(N) != POETX_OK) return 0;
-  const Shape S = shape_of(layer, op == POETX_OP_MERGE ? 0 : N);
+  const bool merge_op = op == POETX_OP_MERGE || op == POETX_OP_MERGE_BLOCKS;
+  if (!merge_op && validate_N(N) != POETX_OK) return 0;
+  const Shape S = shape_of(layer, merge_op ? 0 : N);
   size_t bytes = 0;
   switch (op) {
     case POETX_OP_FORWARD: plan_fwd(S, true, nullptr, &bytes); break;
     case POETX_OP_BACKWARD: plan_bwd(S, true, nullptr, &bytes); break;
     case POETX_OP_FORWARD_BLOCKS: plan_fwd(S, false, nullptr, &bytes); break;
     case POETX_OP_BACKWARD_BLOCKS: plan_bwd(S, false, nullptr, &bytes); break;
-    case POETX_OP_MERGE: plan_merge(S, nullptr, &bytes); break;
+    case POETX_OP_MERGE: plan_merge(S, true, nullptr, &bytes); break;
+    case POETX_OP_MERGE_BLOCKS: plan_merge(S, false, nullptr, &bytes); break;
     default: fail(POETX_EINVAL, "unknown op %d", op); return 0;
   }
   return bytes;
@@ -739,38 +781,35 @@ int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int
   if (!W0p || !sigma || !tau) return fail(POETX_EINVAL, "NULL tensor argument");
   if ((S.kR > 0 && !thR) || (S.kP > 0 && !thP)) return fail(POETX_EINVAL, "NULL generator");
   size_t need = 0;
-  plan_merge(S, nullptr, &need);
+  plan_merge(S, true, nullptr, &need);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  MrgWs w = plan_merge(S, ws, &need);
+  const MrgWs w = plan_merge(S, true, ws, &need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bmode = S.f32 ? 0 : 6;
-  if (S.f32) {
-    if ((rc = build2(thR, S.kR, QOut{w.q32R, nullptr, nullptr}, thP, S.kP, QOut{w.q32P, nullptr, nullptr}, S.b,
-                     w.bws, bmode, s)))
-      return rc;
-    launch_merge_tiles(true, W0p, w.V, w.q32R, w.q32P, S.m, S.n, S.b, S.kR, S.kP, s);
-  } else {
-    if ((rc = build2(thR, S.kR, QOut{nullptr, w.qbR, nullptr}, thP, S.kP, QOut{nullptr, nullptr, w.qtP}, S.b, w.bws,
-                     bmode, s)))
-      return rc;
-    Tm tm(s, "merge_tiles", 4.0 * S.m * S.n * S.b, 2.0 * S.m * S.n * S.es);
-    launch_merge_tiles(false, W0p, w.V, w.qbR, w.qtP, S.m, S.n, S.b, S.kR, S.kP, s);
-  }
-  if ((rc = check_launch("merge tiles"))) return rc;
-  // new permutations, old inverses, relayout into the caller's buffer
-  launch_perm_keys_rank(perm_seed, merge_index, 0, S.m, w.keys, w.snew, s);
-  launch_perm_keys_rank(perm_seed, merge_index, 1, S.n, w.keys, w.tnew, s);
-  launch_invert_perm(sigma, S.m, w.sinv, s);
-  launch_invert_perm(tau, S.n, w.tinv, s);
-  {
-    Tm tm(s, "merge_relayout", 0.0, 2.0 * S.m * S.n * S.es);
-    launch_relayout(S.f32, w.V, W0p, w.sinv, w.snew, w.tinv, w.tnew, S.m, S.n, s);
-  }
-  launch_copy_i32(w.snew, sigma, S.m, s);
-  launch_copy_i32(w.tnew, tau, S.n, s);
-  launch_fill_f32(thR, 0.f, (int64_t)S.kR * (S.b * (S.b - 1) / 2), s);
-  launch_fill_f32(thP, 0.f, (int64_t)S.kP * (S.b * (S.b - 1) / 2), s);
-  return check_launch("merge relayout");
+  if (S.f32) rc = build2(thR, S.kR, QOut{w.q32R, nullptr, nullptr}, thP, S.kP, QOut{w.q32P, nullptr, nullptr}, S.b,
+                       w.bws, bmode, s);
+  else rc = build2(thR, S.kR, QOut{nullptr, w.qbR, nullptr}, thP, S.kP, QOut{nullptr, nullptr, w.qtP}, S.b, w.bws,
+                   bmode, s);
+  if (rc) return rc;
+  return merge_core(S, W0p, Blk{w.q32R, w.q32P, w.qbR, nullptr, nullptr, w.qtP}, thR, thP, sigma, tau, perm_seed,
+                    merge_index, w, s);
+}
+
+int poetx_merge_blocks(const poetx_layer* layer, void* W0p, const poetx_blocks* blocks, float* thR, float* thP,
+                       int32_t* sigma, int32_t* tau, uint64_t perm_seed, uint64_t merge_index, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc = validate_layer(layer);
+  if (rc) return rc;
+  const Shape S = shape_of(layer, 0);
+  if (!W0p || !sigma || !tau) return fail(POETX_EINVAL, "NULL tensor argument");
+  if ((S.kR > 0 && !thR) || (S.kP > 0 && !thP)) return fail(POETX_EINVAL, "NULL generator");
+  if ((rc = check_merge_blocks(S, blocks))) return rc;
+  size_t need = 0;
+  plan_merge(S, false, nullptr, &need);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const MrgWs w = plan_merge(S, false, ws, &need);
+  return merge_core(S, W0p, blk_of(blocks), thR, thP, sigma, tau, perm_seed, merge_index, w,
+                    static_cast<hipStream_t>(stream));
 }
 
 int poetx_make_permutation(uint64_t seed, uint64_t merge_index, int32_t side, int64_t n, int32_t* host_out) {

@@ -13,7 +13,7 @@ struct GJSeg {
   uint16_t* qbf;
   uint16_t* qtbf;
 };
-constexpr int GJ_MAXSEG = 16;
+constexpr int GJ_MAXSEG = 64;
 struct GJArgs {
   GJSeg seg[GJ_MAXSEG]; // workgroup w uses the segment s with start[s] <= w < start[s+1]
   int start[GJ_MAXSEG + 1];

@@ -173,26 +173,31 @@ __global__ void perm_keys_kernel(uint64_t seed, uint64_t merge_index, int side, 
   keys[i] = mix64_dev(base + g * (uint64_t)(i + 1));
 }
 
-// out[rank(i)] = i with rank(i) = #{j : (key_j, j) < (key_i, i)}
-__global__ __launch_bounds__(256) void perm_rank_kernel(const uint64_t* __restrict__ keys, int64_t n, int32_t* out) {
-  __shared__ uint64_t tile[2048];
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// out[rank(i)] = i with rank(i) = #{j : (key_j, j) < (key_i, i)}.  Each of
+// the 16 indices of a workgroup is ranked by 16 lanes that split the scan
+// over j and sum their counts with cross-lane shuffles.
+constexpr int RANK_I = 16, RANK_J = 16, RANK_TILE = 2048;
+__global__ __launch_bounds__(RANK_I * RANK_J) void perm_rank_kernel(const uint64_t* __restrict__ keys, int64_t n,
+                                                                    int32_t* out) {
+  __shared__ uint64_t tile[RANK_TILE];
+  const int li = threadIdx.x / RANK_J, lj = threadIdx.x % RANK_J;
+  const int64_t i = (int64_t)blockIdx.x * RANK_I + li;
   const uint64_t ki = i < n ? keys[i] : 0;
-  int64_t rank = 0;
-  for (int64_t j0 = 0; j0 < n; j0 += 2048) {
-    const int cnt = (int)min((int64_t)2048, n - j0);
+  int rank = 0;
+  for (int64_t j0 = 0; j0 < n; j0 += RANK_TILE) {
+    const int cnt = (int)min((int64_t)RANK_TILE, n - j0);
     __syncthreads();
-    for (int e = threadIdx.x; e < cnt; e += blockDim.x) tile[e] = keys[j0 + e];
+    for (int e = threadIdx.x; e < cnt; e += RANK_I * RANK_J) tile[e] = keys[j0 + e];
     __syncthreads();
-    if (i < n) {
-      for (int e = 0; e < cnt; ++e) {
-        const uint64_t kj = tile[e];
-        const int64_t j = j0 + e;
-        rank += (kj < ki) || (kj == ki && j < i);
-      }
+    for (int e = lj; e < cnt; e += RANK_J) {
+      const uint64_t kj = tile[e];
+      const int64_t j = j0 + e;
+      rank += (kj < ki) || (kj == ki && j < i);
     }
   }
-  if (i < n) out[rank] = (int32_t)i;
+#pragma unroll
+  for (int off = RANK_J / 2; off > 0; off >>= 1) rank += __shfl_xor(rank, off, RANK_J);
+  if (i < n && lj == 0) out[rank] = (int32_t)i;
 }
 
 void launch_perm_keys_rank(uint64_t seed, uint64_t merge_index, int side, int64_t n, uint64_t* keys, int32_t* out,
@@ -200,7 +205,8 @@ void launch_perm_keys_rank(uint64_t seed, uint64_t merge_index, int side, int64_
   if (n <= 0) return;
   const unsigned g = (unsigned)((n + 255) / 256);
   hipLaunchKernelGGL(perm_keys_kernel, dim3(g), dim3(256), 0, s, seed, merge_index, side, n, keys);
-  hipLaunchKernelGGL(perm_rank_kernel, dim3(g), dim3(256), 0, s, keys, n, out);
+  hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)((n + RANK_I - 1) / RANK_I)), dim3(RANK_I * RANK_J), 0, s, keys,
+                     n, out);
 }
 
 __global__ void invert_perm_kernel(const int32_t* __restrict__ p, int64_t n, int32_t* __restrict__ inv) {

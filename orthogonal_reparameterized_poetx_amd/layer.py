@@ -12,7 +12,7 @@ from . import _lib as L
 
 
 class PoetxLayer:
-    def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0):
+    def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0, ws_pool=None):
         self.device = torch.device(device)
         self.dt = L.POETX_BF16 if dtype == "bf16" else L.POETX_F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -26,7 +26,9 @@ class PoetxLayer:
         self.tau = torch.arange(n, dtype=torch.int32, device=self.device)
         self.perm_seed = int(perm_seed)
         self.merges = 0
-        self._ws = {}
+        # workspaces by op; layers that run one after another on one stream
+        # may share a pool (each op's buffer grows to the largest request)
+        self._ws = {} if ws_pool is None else ws_pool
         self._blk = {}
 
     # -- workspaces (grown on demand, reused across calls)
@@ -78,8 +80,8 @@ class PoetxLayer:
     # -- prebuilt blocks: built for many layers at once (build_layer_blocks),
     #    then consumed by forward_blocks / backward_blocks
     def block_buffers(self, kind):
-        """Device buffers of this layer's Cayley blocks for kind "forward" or
-        "backward" (the outputs each pass reads; see poetx_blocks)."""
+        """Device buffers of this layer's Cayley blocks for kind "forward",
+        "backward" or "merge" (the arrays each call reads; see poetx_blocks)."""
         if kind in self._blk:
             return self._blk[kind]
         kR, kP, b, dev = self.m // self.b, self.n // self.b, self.b, self.device
@@ -91,6 +93,8 @@ class PoetxLayer:
             q = dict(Q32R=t(kR, f32), Q32P=t(kP, f32))
         elif kind == "forward":
             q = dict(QR=t(kR, bf), QP=t(kP, bf))
+        elif kind == "merge":
+            q = dict(QR=t(kR, bf), QTP=t(kP, bf))
         else:
             q = dict(Q32R=t(kR, f32), Q32P=t(kP, f32), QP=t(kP, bf), QTR=t(kR, bf), QTP=t(kP, bf))
         self._blk[kind] = (q, L.make_blocks(**q))
@@ -129,6 +133,13 @@ class PoetxLayer:
             self.layer.flags = 0
         return dX, dthR, dthP
 
+    def merge_blocks(self, stream=None):
+        """Merge with blocks from build_layer_blocks(..., "merge")."""
+        ws = self.workspace(L.OP_MERGE_BLOCKS)
+        L.poetx_merge_blocks(self.layer, self.W0p, self.block_buffers("merge")[1], self.thR, self.thP, self.sigma,
+                             self.tau, self.perm_seed, self.merges, ws, stream)
+        self.merges += 1
+
     def merge(self, stream=None):
         ws = self.workspace(L.OP_MERGE)
         L.poetx_merge(self.layer, self.W0p, self.thR, self.thP, self.sigma, self.tau, self.perm_seed,
@@ -140,9 +151,9 @@ _build_ws = {}
 
 
 def build_layer_blocks(layers, kind, stream=None):
-    """Build the Cayley blocks of every layer for kind ("forward" or
-    "backward") with one poetx_build_block_sets call per block size, so the
-    builder's grid spans the blocks of all the layers."""
+    """Build the Cayley blocks of every layer for kind ("forward",
+    "backward" or "merge") with one poetx_build_block_sets call per block
+    size, so the builder's grid spans the blocks of all the layers."""
     by_b = {}
     for lay in layers:
         by_b.setdefault(lay.b, []).extend(lay.block_sets(kind))

@@ -66,7 +66,8 @@ def compare(got, ref, dtype, name, rms_floor=True, max_fail_frac=0.0):
     strict = d > ab + rel * np.abs(ref)
     stats = dict(name=name, n=int(ref.size), fail=int(bad.sum()), strict=float(strict.mean()) if d.size else 0.0,
                  max_abs=float(d.max()) if d.size else 0.0,
-                 max_ratio=float((d / tol).max()) if d.size else 0.0,
+                 max_ratio=float(np.max(np.where(tol > 0, d / np.where(tol > 0, tol, 1.0),
+                                                 np.where(d > 0, np.inf, 0.0)))) if d.size else 0.0,
                  rel_norm=float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)))
     assert stats["fail"] <= max_fail_frac * max(ref.size, 1), stats
     if dtype == "bf16":

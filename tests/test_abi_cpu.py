@@ -150,3 +150,21 @@ def test_prebuilt_block_entry_points_validate_on_host():
     # empty sets are skipped without a look at their pointers
     empty = (S * 1)(S(None, 0, None, None, None))
     assert L.poetx_build_block_sets(empty, 1, 64, None, 0, None) == 0
+
+
+def test_merge_blocks_validates_on_host():
+    P = _P()
+    L = P.lib()
+    fake = ctypes.c_void_p(0x1000)
+    f = 0x2000
+    lay = P.Layer(512, 256, 64, P.POETX_BF16)
+    need = P.workspace_bytes(lay, 0, P.OP_MERGE_BLOCKS)
+    assert 0 < need < P.workspace_bytes(lay, 0, P.OP_MERGE)
+    ok = P.Blocks(None, None, f, None, None, f)          # bf16 merge reads QR and QTP
+    args = lambda blk, nb: (ctypes.byref(lay), fake, blk, fake, fake, fake, fake, 1, 1, fake, nb, None)
+    assert L.poetx_merge_blocks(*args(None, need)) == -1
+    assert L.poetx_merge_blocks(*args(ctypes.byref(P.Blocks(None, None, f, f, f, None)), need)) == -1
+    assert L.poetx_merge_blocks(*args(ctypes.byref(ok), need - 1)) == -4
+    l32 = P.Layer(512, 256, 64, P.POETX_F32)
+    assert L.poetx_merge_blocks(ctypes.byref(l32), fake, ctypes.byref(ok), fake, fake, fake, fake, 1, 1, fake,
+                                1 << 30, None) == -1

@@ -22,7 +22,7 @@ def _log(msg):
 
 
 @pytest.mark.parametrize("b,counts", [
-    (32, [3, 0, 5, 1, 2, 7, 1, 4, 0, 2, 6, 1, 3, 2, 5, 1, 1, 2, 3, 4]),   # 20 sets: two launches of <= 16
+    (32, [3, 0, 5, 1, 2, 7, 1, 4, 0, 2, 6, 1, 3, 2, 5, 1, 1, 2, 3, 4] * 3 + [2] * 10),   # 70 sets: two launches
     (64, [4, 9]),
     (128, [2, 1, 3]),
     (256, [5, 3, 1, 2]),
@@ -119,3 +119,21 @@ def test_prebuilt_backward_accumulate_and_empty():
     _, z1, z2 = lay.backward_blocks(d["X"][:0], d["gY"][:0], dthR=dR2, dthP=dP2, want_dx=False)
     torch.cuda.synchronize()
     assert not z1.any().item() and not z2.any().item()
+
+
+@pytest.mark.parametrize("dtype,m,n,b", [("bf16", 600, 520, 256), ("bf16", 1100, 700, 512), ("f32", 96, 80, 32),
+                                         ("bf16", 300, 200, 64)])
+def test_merge_blocks_matches_merge(dtype, m, n, b):
+    torch = torch_mod()
+    from orthogonal_reparameterized_poetx_amd import build_layer_blocks
+    inp = WL.small_case(51, m, n, b, 4, dtype=dtype)
+    a, _ = make_layer(inp)
+    c, _ = make_layer(inp)
+    _log("merge_blocks %s m=%d n=%d b=%d" % (dtype, m, n, b))
+    a.merge()
+    build_layer_blocks([c], "merge")
+    c.merge_blocks()
+    torch.cuda.synchronize()
+    assert torch.equal(a.W0p, c.W0p)
+    assert torch.equal(a.sigma, c.sigma) and torch.equal(a.tau, c.tau)
+    assert not c.thR.any().item() and not c.thP.any().item()
