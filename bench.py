@@ -39,14 +39,15 @@ MFMA_CLASSES = {"gemm_nt": 2500.0, "gemm_nn": 2500.0, "cayley_build": 157.3, "ch
 KERNEL_CLASSES = [
     ("permute_gather_kernel", "xform_permute", 1),
     ("permute_scatter_kernel", "xform_permute", 1),
-    ("gemm_bf16_kernel<false, true>", "xform_blockmul", 1),
-    ("gemm_bf16_kernel<false, false>", "gemm_nt", 1),
-    ("gemm_bf16_kernel<true, false>", "gemm_nn", 1),
+    ("gemm_bf16_kernel<false, true, false>", "xform_blockmul", 1),
+    ("gemm_bf16_kernel<false, false, false>", "gemm_nt", 1),
+    ("gemm_bf16_kernel<true, false, false>", "gemm_nn", 1),
+    ("gemm_bf16_kernel<true, true, true>", "chain_rule", 5),
+    ("chain_prep", "chain_rule", 5),
+    ("skew_project_kernel", "chain_rule", 5),
     ("gj_kernel", "cayley_build", 1),
     ("gram_bf16_kernel", "gram", 2),
     ("gram_reduce_kernel", "gram", 2),
-    ("bgemm_kernel", "chain_rule", 3),
-    ("skew_project_kernel", "chain_rule", 3),
 ]
 CALIBRATION_BYTES = 256 << 20   # the copy kernel reads and writes this many bytes each
 

@@ -222,28 +222,45 @@ int build2(const float* th0, int64_t n0, QOut o0, const float* th1, int64_t n1, 
 // dtheta from G = dL/dQ:  G_S = 1/2 (I + Q^T) G (I + Q^T);  dtheta_p = G_S[i][j] - G_S[j][i].
 // G holds the R blocks then the P blocks contiguously; the fp32 blocks of the
 // two sides may live apart (q32R, q32P).  Both sides in one pass.
-int chain(float* G, const float* q32R, const float* q32P, float* tmp, int64_t nR, int64_t nP, int b, float* dthR,
-          float* dthP, bool accumulate, int mode, hipStream_t s) {
+// bf16 layers: each product is one bf16 GEMM over a tripled K on split
+// operands (fp32-level accuracy), fp32 accumulation and output; cat holds
+// the four split operands.  fp32 layers: fp32 MFMA products.
+int chain(float* G, const float* q32R, const float* q32P, float* tmp, uint16_t* const* cat, int64_t nR, int64_t nP,
+          int b, float* dthR, float* dthP, bool accumulate, bool f32, hipStream_t s) {
   const int64_t nblk = nR + nP;
   if (nblk <= 0) return POETX_OK;
   Tm tm(s, "chain_rule", 4.0 * b * (double)b * b * nblk, 0.0);
   const int64_t sb = (int64_t)b * b;
-  BGemmArgs q{};
-  q.M = q.N = q.K = b;
-  q.A = G; q.sA = sb; q.lda = b;
-  q.B = q32R; q.sB = sb; q.ldb = b; q.transB = 1; q.addIB = 1;
-  q.B1 = q32P; q.nb0 = (int)nR;
-  q.C = tmp; q.sC = sb; q.ldc = b;
-  q.alpha = 1.f; q.beta = 0.f;
-  launch_bgemm(mode, (int)nblk, q, s);
-  BGemmArgs r{};
-  r.M = r.N = r.K = b;
-  r.A = q32R; r.sA = sb; r.lda = b; r.transA = 1; r.addIA = 1;
-  r.A1 = q32P; r.nb0 = (int)nR;
-  r.B = tmp; r.sB = sb; r.ldb = b;
-  r.C = G; r.sC = sb; r.ldc = b;
-  r.alpha = 0.5f; r.beta = 0.f;
-  launch_bgemm(mode, (int)nblk, r, s);
+  if (!f32) {
+    launch_chain_prep1(G, q32R, q32P, (int)nR, (int)nblk, b, cat[0], cat[1], cat[2], s);
+    GemmArgs g{};
+    g.M = g.N = b; g.K = 3 * b;
+    g.lda = 3 * b; g.ldb = b; g.ldc = b;
+    g.sA = 3 * sb; g.sB = 3 * sb; g.sC = sb;
+    g.batch = (int)nblk;
+    g.A = cat[0]; g.B = cat[1]; g.Cf = tmp;                 // T = G (I + Q^T)
+    launch_gemm_bf16_f32out(g, s);
+    launch_chain_prep2(tmp, (int)nblk, b, cat[3], s);
+    g.A = cat[2]; g.B = cat[3]; g.Cf = G;                   // G_S = (I + Q^T) T / 2
+    launch_gemm_bf16_f32out(g, s);
+  } else {
+    BGemmArgs q{};
+    q.M = q.N = q.K = b;
+    q.A = G; q.sA = sb; q.lda = b;
+    q.B = q32R; q.sB = sb; q.ldb = b; q.transB = 1; q.addIB = 1;
+    q.B1 = q32P; q.nb0 = (int)nR;
+    q.C = tmp; q.sC = sb; q.ldc = b;
+    q.alpha = 1.f; q.beta = 0.f;
+    launch_bgemm(0, (int)nblk, q, s);
+    BGemmArgs r{};
+    r.M = r.N = r.K = b;
+    r.A = q32R; r.sA = sb; r.lda = b; r.transA = 1; r.addIA = 1;
+    r.A1 = q32P; r.nb0 = (int)nR;
+    r.B = tmp; r.sB = sb; r.ldb = b;
+    r.C = G; r.sC = sb; r.ldc = b;
+    r.alpha = 0.5f; r.beta = 0.f;
+    launch_bgemm(0, (int)nblk, r, s);
+  }
   launch_skew_project(G, b, (int)nblk, dthR, (int)nR, dthP, accumulate ? 1 : 0, s);
   return check_launch("chain rule");
 }
@@ -311,6 +328,7 @@ struct BwdWs {
   void* bws;
   void *z1, *xg, *z2, *gyg, *gz2;
   float *GR, *GP, *tmp;
+  uint16_t *cat[4];   // chain-rule split operands (bf16 layers)
   void* part;
 };
 BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes) {
@@ -335,6 +353,8 @@ BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes) {
   w.GR = a.take<float>((S.kR + S.kP) * bb);     // R blocks, then P blocks
   w.GP = w.GR ? w.GR + S.kR * bb : nullptr;
   w.tmp = a.take<float>((S.kR + S.kP) * bb);
+  if (!S.f32)
+    for (auto& c : w.cat) c = a.take<uint16_t>((S.kR + S.kP) * 3 * bb);
   const size_t pb = std::max(gram_partials_bytes(S.N, S.b, S.kR, S.f32), gram_partials_bytes(S.N, S.b, S.kP, S.f32));
   w.part = a.take<char>(pb);
   *bytes = a.off + kAlign;
@@ -464,7 +484,6 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
              const void* dY, void* dX, float* dthR, float* dthP, bool accum, const BwdWs& w, hipStream_t s) {
   const int64_t N = S.N;
   const int n = (int)S.n, m = (int)S.m;
-  const int cmode = S.f32 ? 0 : 3;   // chain-rule products
   int rc;
   if (S.f32) {
     // recompute z1' (keeping x' = Pi_tau x for dL/dQ_P) and z2'
@@ -535,7 +554,7 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   }
   if ((rc = check_launch("P-side backward"))) return rc;
   // chain rule through the Cayley map onto the stored upper triangle
-  return chain(w.GR, q.q32R, q.q32P, w.tmp, S.kR, S.kP, S.b, dthR, dthP, accum, cmode, s);
+  return chain(w.GR, q.q32R, q.q32P, w.tmp, w.cat, S.kR, S.kP, S.b, dthR, dthP, accum, S.f32, s);
 }
 
 // shared argument checks of forward / forward_blocks

@@ -501,6 +501,76 @@ void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL(bgemm_kernel<0>, grid, dim3(256), 0, s, a);
 }
 
+// ---------------------------------------------------------------------------
+// chain-rule operand preparation (see kernels.h): one thread per (row, col)
+// of a block; bf16 hi / lo split of fp32 values
+// ---------------------------------------------------------------------------
+// 32 x 32 tile per workgroup (256 threads, 4 elements each); Q is read
+// coalesced and transposed through LDS
+__global__ __launch_bounds__(256) void chain_prep1_kernel(const float* __restrict__ G, const float* __restrict__ qR,
+                                                          const float* __restrict__ qP, int nR, int b,
+                                                          uint16_t* __restrict__ Acat, uint16_t* __restrict__ Bcat,
+                                                          uint16_t* __restrict__ A2cat) {
+  __shared__ float qt[32][33];
+  const int z = blockIdx.z;
+  const int64_t bb = (int64_t)b * b;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // ty 0..7
+  const float* q = z < nR ? qR + (int64_t)z * bb : qP + (int64_t)(z - nR) * bb;
+  // qt[jj][ii] = Q[j0 + jj][i0 + ii]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int jj = ty + 8 * r;
+    qt[jj][tx] = q[(int64_t)(j0 + jj) * b + i0 + tx];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ii = ty + 8 * r;
+    const int i = i0 + ii, j = j0 + tx;
+    // B'[i][j] = (I + Q^T)[i][j] = delta_ij + Q[j][i]
+    const float bp = qt[tx][ii] + (i == j ? 1.f : 0.f);
+    const float g = G[z * bb + (int64_t)i * b + j];
+    bf16 gh, gl, bh, bl;
+    split_bf16(g, gh, gl);
+    split_bf16(bp, bh, bl);
+    const uint16_t GH = __builtin_bit_cast(uint16_t, gh), GL = __builtin_bit_cast(uint16_t, gl);
+    const uint16_t BH = __builtin_bit_cast(uint16_t, bh), BL = __builtin_bit_cast(uint16_t, bl);
+    uint16_t* a = Acat + z * 3 * bb + (int64_t)i * 3 * b;      // row i of [b][3b]
+    a[j] = GH; a[b + j] = GH; a[2 * b + j] = GL;
+    uint16_t* c = Bcat + z * 3 * bb;                            // rows i, b+i, 2b+i of [3b][b]
+    c[(int64_t)i * b + j] = BH; c[(int64_t)(b + i) * b + j] = BL; c[(int64_t)(2 * b + i) * b + j] = BH;
+    uint16_t* a2 = A2cat + z * 3 * bb + (int64_t)i * 3 * b;
+    a2[j] = BH; a2[b + j] = BH; a2[2 * b + j] = BL;
+  }
+}
+
+__global__ void chain_prep2_kernel(const float* __restrict__ T, int b, uint16_t* __restrict__ Tcat) {
+  const int z = blockIdx.y;
+  const int64_t bb = (int64_t)b * b;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= bb) return;
+  const int i = e / b, j = e - i * b;
+  bf16 h, l;
+  split_bf16(0.5f * T[z * bb + e], h, l);   // the 1/2 of G_S, exact in fp32
+  const uint16_t H = __builtin_bit_cast(uint16_t, h), L = __builtin_bit_cast(uint16_t, l);
+  uint16_t* c = Tcat + z * 3 * bb;
+  c[(int64_t)i * b + j] = H; c[(int64_t)(b + i) * b + j] = L; c[(int64_t)(2 * b + i) * b + j] = H;
+}
+
+void launch_chain_prep1(const float* G, const float* qR, const float* qP, int nR, int nblk, int b, uint16_t* Acat,
+                        uint16_t* Bcat, uint16_t* A2cat, hipStream_t s) {
+  if (nblk <= 0) return;
+  dim3 grid((unsigned)(b / 32), (unsigned)(b / 32), (unsigned)nblk);   // b is a multiple of 32
+  hipLaunchKernelGGL(chain_prep1_kernel, grid, dim3(256), 0, s, G, qR, qP, nR, b, Acat, Bcat, A2cat);
+}
+
+void launch_chain_prep2(const float* T, int nblk, int b, uint16_t* Tcat, hipStream_t s) {
+  if (nblk <= 0) return;
+  dim3 grid((unsigned)(((int64_t)b * b + 255) / 256), (unsigned)nblk);
+  hipLaunchKernelGGL(chain_prep2_kernel, grid, dim3(256), 0, s, T, b, Tcat);
+}
+
 void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s) {
   if (nblk <= 0) return;
   dim3 grid((unsigned)(((int64_t)b * b + 255) / 256), nblk);

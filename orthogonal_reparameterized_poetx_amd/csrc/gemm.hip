@@ -43,13 +43,17 @@ __device__ __forceinline__ void b2l16(__amdgpu_buffer_rsrc_t r, int voff, int so
 }
 
 // LDS tile layouts (bf16, 16-byte chunks XOR-swizzled by row):
-//   A (and NT B): [256 rows][64 k], chunk c of row r stored at chunk c ^ (r & 7)
+//   A (and NT B): [256 rows][64 k], chunk c of row r stored at chunk c ^ ((r >> 1) & 7):
+//     a 16-lane phase of a fragment read (16 consecutive rows, one chunk)
+//     then touches every bank once (rows r, r+1 differ in the bank half,
+//     the key spreads the 8 row pairs over the 8 chunk positions)
 //   NN B:         [64 k rows][256 n], chunk c of row r stored at chunk c ^ (r & 7)
 // The direct loads pick each lane's source chunk so that the fixed lane ->
 // LDS slot placement produces exactly this layout.
 // BATCHED only names the instantiation used for batched block products, so
-// that profiles tell it apart from the weight products.
-template <bool NN, bool BATCHED>
+// that profiles tell it apart from the weight products.  OUTF32 writes the
+// fp32 accumulators to g.Cf instead of bf16 to g.C.
+template <bool NN, bool BATCHED, bool OUTF32 = false>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
   // two buffers as separate LDS objects, each named at compile time below, so
   // the compiler can tell reads of one from the asynchronous fill of the other
@@ -68,7 +72,8 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
   const int M = g.M, N = g.N, K = g.K;
   const uint16_t* __restrict__ A = g.A + bz * g.sA;
   const uint16_t* __restrict__ Bm = g.B + bz * g.sB;
-  uint16_t* __restrict__ C = g.C + bz * g.sC;
+  uint16_t* __restrict__ C = OUTF32 ? nullptr : g.C + bz * g.sC;
+  float* __restrict__ Cf = OUTF32 ? g.Cf + bz * g.sC : nullptr;
   const int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = wave * 32 + q * 8 + (lane >> 3);
-    const int cs = (lane & 7) ^ (lane >> 3);
+    const int cs = (lane & 7) ^ ((r >> 1) & 7);
     voa[q] = (int)(((int64_t)r * lda + cs * 8) * 2);
     if constexpr (!NN) {
       vob[q] = (int)(((int64_t)r * ldb + cs * 8) * 2);
@@ -122,8 +127,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
       const int e = tid + 512 * q;
       const int row = e >> 3, c = e & 7;
       if (c * 8 >= kv) {
-        *reinterpret_cast<uint4*>(as_ + row * GBK + ((c ^ (row & 7)) << 3)) = make_uint4(0, 0, 0, 0);
-        if constexpr (!NN) *reinterpret_cast<uint4*>(bs_ + row * GBK + ((c ^ (row & 7)) << 3)) = make_uint4(0, 0, 0, 0);
+        const int cz = c ^ ((row >> 1) & 7);
+        *reinterpret_cast<uint4*>(as_ + row * GBK + (cz << 3)) = make_uint4(0, 0, 0, 0);
+        if constexpr (!NN) *reinterpret_cast<uint4*>(bs_ + row * GBK + (cz << 3)) = make_uint4(0, 0, 0, 0);
       }
       if constexpr (NN) {
         const int kr = e >> 5, cn = e & 31;
@@ -136,21 +142,20 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
     // (one per buffer) alive across the loop
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 af[4], bfr[2];
+    // fragments of k sub-step s (16 wide) for this wave's 128 x 64 output
+    auto frag = [&](int s, bf16x8* af, bf16x8* bfr) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wm * 128 + i * 32 + (lane & 31);
         const int ch = 2 * s + (lane >> 5);
-        af[i] = *reinterpret_cast<const bf16x8*>(&as[row * GBK + ((ch ^ (row & 7)) << 3)]);
+        af[i] = *reinterpret_cast<const bf16x8*>(&as[row * GBK + ((ch ^ ((row >> 1) & 7)) << 3)]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if constexpr (!NN) {
           const int row = wn * 64 + j * 32 + (lane & 31);
           const int ch = 2 * s + (lane >> 5);
-          bfr[j] = *reinterpret_cast<const bf16x8*>(&bs[row * GBK + ((ch ^ (row & 7)) << 3)]);
+          bfr[j] = *reinterpret_cast<const bf16x8*>(&bs[row * GBK + ((ch ^ ((row >> 1) & 7)) << 3)]);
         } else {
           const int gq = lane >> 4, q = lane & 15;
           const int ncol = wn * 64 + j * 32 + 16 * (gq & 1) + 4 * (q & 3);
@@ -166,10 +171,17 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
           bfr[j] = __builtin_bit_cast(bf16x8, v);
         }
       }
+    };
+    // fragments of sub-step s + 1 load while the products of sub-step s run
+    bf16x8 af[2][4], bfr[2][2];
+    frag(0, af[0], bfr[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) frag(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(bfr[s & 1][j], af[s & 1][i], acc[i][j]);
     }
   };
 
@@ -196,20 +208,98 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
   }
   if (kt < nk) compute(As0, Bs0);
 
-  // epilogue: bf16 stores
+  // epilogue.  The products run with the operands swapped, so acc[i][j]
+  // holds the transposed 32 x 32 sub-tile: register r of lane l is
+  // C[row l % 32][col 8 (r / 4) + 4 (l / 32) + r % 4], i.e. four
+  // consecutive columns of one row per register quad.
+  if constexpr (OUTF32) {
+    // fp32: the same staging in two rounds of 64 rows (16 KiB per wave and
+    // round): 16-byte writes into 256-byte rows, chunk c at c ^ (row & 15),
+    // then 16-byte row-order stores (4 rows of 256 bytes per instruction)
+    uint32_t* st = reinterpret_cast<uint32_t*>((wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? Bs0 : Bs1) +
+                                               (wave & 1) * (128 * 64));
+    const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(Cf) & 15) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int gn = n0 + wn * 64 + j * 32 + (lane & 31);
-      if (gn < N) {
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * h + ii;
+        const int row = ii * 32 + (lane & 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gm = m0 + wm * 128 + i * 32 + c32_row(lane, r);
-          if (gm < M) C[(int64_t)gm * ldc + gn] = f32_to_bits(acc[i][j][r]);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[i][j];
+            const int chunk = j * 8 + 2 * q + (lane >> 5);
+            *reinterpret_cast<float4*>(st + row * 64 + ((chunk ^ (row & 15)) << 2)) =
+                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int e = it * 64 + lane;
+        const int row = e >> 4, chunk = e & 15;
+        const float4 v = *reinterpret_cast<const float4*>(st + row * 64 + ((chunk ^ (row & 15)) << 2));
+        const int gm = m0 + wm * 128 + h * 64 + row, gn = n0 + wn * 64 + chunk * 4;
+        if (gm < M && gn < N) {
+          float* cp = Cf + (int64_t)gm * ldc + gn;
+          if (vec && gn + 3 < N) *reinterpret_cast<float4*>(cp) = v;
+          else {
+            const float w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2)
+              if (gn + e2 < N) cp[e2] = w[e2];
+          }
         }
       }
     }
+  } else {
+    // bf16: each wave stages its 128 x 64 tile (16 KiB) in the now idle LDS
+    // buffers, 8-byte writes into 128-byte rows, chunk c at c ^ ((row >> 1) & 7)
+    // and the two halves of a chunk swapped on rows with bit 4 set (32 rows of
+    // one write touch each bank pair once); then whole rows leave as 16-byte
+    // stores, 8 rows of 128 bytes per wave instruction.
+    __syncthreads();
+    uint16_t* st = (wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? Bs0 : Bs1) + (wave & 1) * (128 * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[i][j];
+          const int chunk = j * 4 + q, half = lane >> 5;
+          const int off = row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3) + ((half ^ ((row >> 4) & 1)) << 2);
+          uint2 v;
+          v.x = pack2(f32_to_bits(a[4 * q]), f32_to_bits(a[4 * q + 1]));
+          v.y = pack2(f32_to_bits(a[4 * q + 2]), f32_to_bits(a[4 * q + 3]));
+          *reinterpret_cast<uint2*>(st + off) = v;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's staging writes are done
+    const bool vec = (ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int e = it * 64 + lane;
+      const int row = e >> 3, chunk = e & 7;
+      uint4 v = *reinterpret_cast<const uint4*>(st + row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3));
+      if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      const int gm = m0 + wm * 128 + row, gn = n0 + wn * 64 + chunk * 8;
+      if (gm < M && gn < N) {
+        uint16_t* cp = C + (int64_t)gm * ldc + gn;
+        if (vec) *reinterpret_cast<uint4*>(cp) = v;
+        else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2)
+            if (gn + e2 < N) cp[e2] = (uint16_t)(w[e2 >> 1] >> (16 * (e2 & 1)));
+        }
+      }
+    }
+  }
 }
 
 // Generic bf16 GEMM for shapes the tiled kernel cannot take (a dimension,
@@ -258,6 +348,14 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     if (nn) hipLaunchKernelGGL(gemm_bf16_generic_kernel<true>, grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL(gemm_bf16_generic_kernel<false>, grid, dim3(256), 0, s, g);
   }
+}
+
+void launch_gemm_bf16_f32out(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return;
+  const int tn = (g.N + GBN - 1) / GBN, tm = (g.M + GBM - 1) / GBM;
+  const int nt = tn * tm * g.batch;
+  const int grid = ((nt + 7) / 8) * 8;
+  hipLaunchKernelGGL((gemm_bf16_kernel<true, true, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
 }
 
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N, int64_t K,

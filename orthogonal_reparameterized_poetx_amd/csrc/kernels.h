@@ -42,6 +42,15 @@ struct BGemmArgs {
 void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s);
 void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s);
 void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qbf, uint16_t* qtbf, hipStream_t s);
+// chain-rule operands for fp32-accurate products as single bf16 GEMMs over a
+// tripled K (x = hi + lo, x*y ~ hi*hi + hi*lo + lo*hi).  Block z < nR uses
+// qR[z], else qP[z - nR].  With B' = I + Q^T:
+//   prep1: Acat[z] = [G_hi | G_hi | G_lo] ([b][3b]), Bcat[z] = [B'_hi; B'_lo; B'_hi]
+//          ([3b][b]), A2cat[z] = [B'_hi | B'_hi | B'_lo] ([b][3b])
+//   prep2: Tcat[z] = split of (T / 2) as [hi; lo; hi] ([3b][b])
+void launch_chain_prep1(const float* G, const float* qR, const float* qP, int nR, int nblk, int b, uint16_t* Acat,
+                        uint16_t* Bcat, uint16_t* A2cat, hipStream_t s);
+void launch_chain_prep2(const float* T, int nblk, int b, uint16_t* Tcat, hipStream_t s);
 // blocks [0, n0) project into dth0, the rest into dth1
 void launch_skew_project(const float* GS, int b, int nblk, float* dth0, int n0, float* dth1, int accumulate,
                          hipStream_t s);
@@ -86,12 +95,17 @@ struct GemmArgs {
   const uint16_t* A;
   const uint16_t* B;
   uint16_t* C;
+  float* Cf;           // fp32 output of launch_gemm_bf16_f32out
+
   int M, N, K;
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC;
   int batch;
 };
 void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s);
+// NN with fp32 output to g.Cf (tiled path only: K, N, lda, ldb, sA, sB multiples
+// of 8 and 16-byte aligned operands; the caller guarantees it)
+void launch_gemm_bf16_f32out(const GemmArgs& g, hipStream_t s);
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N,
                       int64_t K, hipStream_t s);
 void launch_gemm_f32(bool nn, const float* A, const float* Bm, float* C, int64_t M, int64_t N, int64_t K,
