@@ -21,10 +21,14 @@ __device__ __forceinline__ i16x4 ds_read_tr16g(const uint16_t* p) {
 
 static int gram_tile(int B) { return B < 128 ? B : 128; }
 
+// token chunks per launch: about 512 workgroups in all.  More chunks fill
+// the chip faster but every chunk writes a full fp32 partial of the blocks,
+// which the reduction reads back (at 32 chunks the partials outweigh the
+// bf16 operands); measured on the 2048- and 5632-wide layer-set shapes.
 static int gram_chunks(int64_t N, int B, int k) {
   const int ti = gram_tile(B);
   const int64_t tiles = (int64_t)k * (B / ti) * (B / ti);
-  int64_t s = (1024 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  int64_t s = (512 + tiles - 1) / (tiles > 0 ? tiles : 1);
   const int64_t maxs = (N + 255) / 256;
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;

@@ -62,19 +62,23 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_gather_kernel(PermArgs a
   uint16_t* __restrict__ out = a.out + t0 * W;
   uint16_t* __restrict__ tout = a.tail_out ? a.tail_out + t0 * W : nullptr;
   if (VEC) {
+    // each thread owns 8-column chunks and reads their indices once for all
+    // rows of the workgroup
     const int nch = W >> 3;
-    for (int e = tid; e < nr * nch; e += PERM_THREADS) {
-      const int r = e / nch, c = e - r * nch;
+    for (int c = tid; c < nch; c += PERM_THREADS) {
       const int4 pa = *reinterpret_cast<const int4*>(a.perm + c * 8);
       const int4 pb = *reinterpret_cast<const int4*>(a.perm + c * 8 + 4);
-      const uint16_t* row = rows + r * W;
-      uint4 v;
-      v.x = pack2(row[pa.x], row[pa.y]);
-      v.y = pack2(row[pa.z], row[pa.w]);
-      v.z = pack2(row[pb.x], row[pb.y]);
-      v.w = pack2(row[pb.z], row[pb.w]);
-      stg16(out + (int64_t)r * W + c * 8, v);
-      if (tout && c * 8 >= a.tail0) stg16(tout + (int64_t)r * W + c * 8, v);
+      const bool tl = tout && c * 8 >= a.tail0;
+      for (int r = 0; r < nr; ++r) {
+        const uint16_t* row = rows + r * W;
+        uint4 v;
+        v.x = pack2(row[pa.x], row[pa.y]);
+        v.y = pack2(row[pa.z], row[pa.w]);
+        v.z = pack2(row[pb.x], row[pb.y]);
+        v.w = pack2(row[pb.z], row[pb.w]);
+        stg16(out + (int64_t)r * W + c * 8, v);
+        if (tl) stg16(tout + (int64_t)r * W + c * 8, v);
+      }
     }
   } else {
     for (int e = tid; e < nr * W; e += PERM_THREADS) {
@@ -98,16 +102,18 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(PermArgs 
   const uint16_t* __restrict__ tin = (a.tail_in ? a.tail_in : a.in) + t0 * W;
   if (VEC) {
     const int nch = W >> 3;
-    for (int e = tid; e < nr * nch; e += PERM_THREADS) {
-      const int r = e / nch, c = e - r * nch;
-      const uint4 v = ldg16((c * 8 < a.tail0 ? in : tin) + (int64_t)r * W + c * 8);
+    for (int c = tid; c < nch; c += PERM_THREADS) {
       const int4 pa = *reinterpret_cast<const int4*>(a.perm + c * 8);
       const int4 pb = *reinterpret_cast<const int4*>(a.perm + c * 8 + 4);
-      uint16_t* row = rows + r * W;
-      row[pa.x] = (uint16_t)(v.x & 0xffff); row[pa.y] = (uint16_t)(v.x >> 16);
-      row[pa.z] = (uint16_t)(v.y & 0xffff); row[pa.w] = (uint16_t)(v.y >> 16);
-      row[pb.x] = (uint16_t)(v.z & 0xffff); row[pb.y] = (uint16_t)(v.z >> 16);
-      row[pb.z] = (uint16_t)(v.w & 0xffff); row[pb.w] = (uint16_t)(v.w >> 16);
+      const uint16_t* src = (c * 8 < a.tail0 ? in : tin) + c * 8;
+      for (int r = 0; r < nr; ++r) {
+        const uint4 v = ldg16(src + (int64_t)r * W);
+        uint16_t* row = rows + r * W;
+        row[pa.x] = (uint16_t)(v.x & 0xffff); row[pa.y] = (uint16_t)(v.x >> 16);
+        row[pa.z] = (uint16_t)(v.y & 0xffff); row[pa.w] = (uint16_t)(v.y >> 16);
+        row[pb.x] = (uint16_t)(v.z & 0xffff); row[pb.y] = (uint16_t)(v.z >> 16);
+        row[pb.z] = (uint16_t)(v.w & 0xffff); row[pb.w] = (uint16_t)(v.w >> 16);
+      }
     }
   } else {
     for (int e = tid; e < nr * W; e += PERM_THREADS) {
