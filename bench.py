@@ -274,8 +274,9 @@ class Stack:
             for kind in ("forward", "backward", "merge"):
                 lay.block_buffers(kind)
             lay.workspace(P.OP_FORWARD_BLOCKS, N)
-            lay.workspace(P.OP_BACKWARD_BLOCKS, N)
+            lay.workspace(P.OP_BACKWARD_DQ, N)
             lay.workspace(P.OP_MERGE_BLOCKS)
+            lay.dq_buffers()
         self.adam_steps = 0
 
     def forward_backward(self):
@@ -285,7 +286,8 @@ class Stack:
             lay.forward_blocks(self.X[lay.x_key], Y=o["Y"])
         P.build_layer_blocks(self.layers, "backward")
         for lay, g, o in zip(reversed(self.layers), reversed(self.gY), reversed(self.out)):
-            lay.backward_blocks(self.X[lay.x_key], g, dX=o["dX"], dthR=lay.dR, dthP=lay.dP)
+            lay.backward_blocks_dq(self.X[lay.x_key], g, dX=o["dX"])
+        P.chain_rule_layers(self.layers, [(lay.dR, lay.dP) for lay in self.layers])
 
     def adam(self):
         self.adam_steps += 1
@@ -408,9 +410,10 @@ def main():
             lay.workspace(P.OP_BACKWARD, N)
         else:
             lay.workspace(P.OP_FORWARD_BLOCKS, N)
-            lay.workspace(P.OP_BACKWARD_BLOCKS, N)
+            lay.workspace(P.OP_BACKWARD_DQ, N)
             lay.block_buffers("forward")
             lay.block_buffers("backward")
+            lay.dq_buffers()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -422,13 +425,15 @@ def main():
 
     def step_batched():
         # blocks of all seven matrices in one build per pass; the backward pass
-        # rebuilds them from the generators instead of keeping the forward's
+        # rebuilds them from the generators instead of keeping the forward's,
+        # and runs the chain rule once for all seven after their dL/dQ
         P.build_layer_blocks(layers, "forward")
         for lay, o in zip(layers, outs):
             lay.forward_blocks(Xs[lay.x_key], Y=o["Y"])
         P.build_layer_blocks(layers, "backward")
         for lay, g, o in zip(reversed(layers), reversed(gYs), reversed(outs)):
-            lay.backward_blocks(Xs[lay.x_key], g, dX=o["dX"], dthR=o["dR"], dthP=o["dP"])
+            lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"])
+        P.chain_rule_layers(layers, [(o["dR"], o["dP"]) for o in outs])
 
     step = step_per_layer if args.per_layer_builds else step_batched
 
@@ -504,7 +509,8 @@ def main():
         "data": "synthetic (seeded Gaussian inputs with the layer set's shapes)",
         "config": {"workload": cfg["name"], "tokens": N, "matrices": len(cfg["mats"]), "b": cfg["b"],
                    "shapes": ["%dx%d" % (m, n) for _, m, n in cfg["mats"]],
-                   "block_builds": "per layer call" if args.per_layer_builds else "batched per pass"},
+                   "block_builds": "per layer call" if args.per_layer_builds else
+                   "batched per pass (Cayley builds and chain rule over all seven matrices)"},
         "roofline": roof,
         "kernels_per_step": breakdown,
         "merge_ms_layer_set": round(merge_ms, 3),

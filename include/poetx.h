@@ -84,6 +84,7 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
 #define POETX_OP_FORWARD_BLOCKS 3  /* poetx_forward_blocks  */
 #define POETX_OP_BACKWARD_BLOCKS 4 /* poetx_backward_blocks */
 #define POETX_OP_MERGE_BLOCKS 5    /* poetx_merge_blocks    */
+#define POETX_OP_BACKWARD_DQ 6     /* poetx_backward_blocks_dq */
 
 typedef struct {
   int64_t m;      /* rows of W0 = output features                         */
@@ -222,6 +223,49 @@ int poetx_backward_blocks(const poetx_layer* layer, const void* W0p, const poetx
                           const int32_t* sigma, const int32_t* tau, const void* X, const void* dY,
                           int64_t N, void* dX, float* dthR, float* dthP, void* ws, size_t ws_bytes,
                           void* stream);
+
+/*
+ * a0, a6-a8 without the chain rule: poetx_backward_blocks up to the gradient
+ * with respect to the orthogonal blocks, G_l = dL/dQ_l, which it writes
+ * instead of the generator gradients.  The chain rule through the Cayley
+ * map [P1 实践 2 step 3] then runs for many layers at once in
+ * poetx_chain_rule_sets, so its small per-block products fill the GPU.
+ *   GR [k_R][b][b], GP [k_P][b][b] fp32, device, overwritten
+ * bf16 layers only; layer->flags must not carry POETX_ACCUMULATE_GRAD (it
+ * belongs to poetx_chain_rule_sets).  N == 0 writes zeros.  Workspace:
+ * poetx_workspace_bytes(layer, N, POETX_OP_BACKWARD_DQ).
+ */
+int poetx_backward_blocks_dq(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                             const int32_t* sigma, const int32_t* tau, const void* X, const void* dY,
+                             int64_t N, void* dX, float* GR, float* GP, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* One batch of blocks for poetx_chain_rule_sets. */
+typedef struct {
+  const float* Q32; /* [nblocks][b][b] fp32 Cayley blocks Q, device           */
+  const float* G;   /* [nblocks][b][b] fp32 dL/dQ, device                      */
+  int64_t nblocks;  /* >= 0                                                    */
+  float* dtheta;    /* [nblocks][b(b-1)/2] fp32 generator gradient, device     */
+} poetx_chain_set;
+
+/*
+ * a9 over many batches at once: for every block,
+ * G_S = 1/2 (I + Q^T) G (I + Q^T) and dtheta_p = G_S[i][j] - G_S[j][i] on the
+ * stored upper triangle [P1 实践 2 step 3; P3 item 4].  The products are
+ * fp32-accurate (bf16 MFMA on a hi/lo split of each fp32 operand, fp32
+ * accumulation), as in poetx_backward for bf16 layers, and bit-identical to
+ * it block for block.
+ *   sets   host array of count poetx_chain_set (count in [0, 65536]), one
+ *          block size b for all
+ *   flags  POETX_ACCUMULATE_GRAD: add into dtheta instead of overwriting
+ *   ws     poetx_chain_workspace_bytes(total blocks over the sets, b) bytes
+ * G and Q are only read.
+ */
+int poetx_chain_rule_sets(const poetx_chain_set* sets, int32_t count, int32_t b, uint32_t flags,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of poetx_chain_rule_sets for total_blocks blocks of size b. */
+size_t poetx_chain_workspace_bytes(int64_t total_blocks, int32_t b);
 
 /*
  * a10-a11: merge W0 <- R W0 P [P3 item 1], then theta_R, theta_P <- 0 and

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     OP_BACKWARD,
+    OP_BACKWARD_DQ,
     OP_BACKWARD_BLOCKS,
     OP_FORWARD,
     OP_FORWARD_BLOCKS,
@@ -19,9 +20,11 @@ from ._lib import (  # noqa: F401
     POETX_F32,
     Blocks,
     BlockSet,
+    ChainSet,
     Layer,
     PoetxError,
     build_workspace_bytes,
+    chain_workspace_bytes,
     last_error,
     lib,
     make_blocks,
@@ -29,8 +32,10 @@ from ._lib import (  # noqa: F401
     poetx_adam_step,
     poetx_backward,
     poetx_backward_blocks,
+    poetx_backward_blocks_dq,
     poetx_build_block_sets,
     poetx_build_blocks,
+    poetx_chain_rule_sets,
     poetx_forward,
     poetx_forward_blocks,
     poetx_make_permutation,
@@ -40,4 +45,4 @@ from ._lib import (  # noqa: F401
     timing_summary,
     workspace_bytes,
 )
-from .layer import PoetxLayer, build_layer_blocks  # noqa: F401,E402
+from .layer import PoetxLayer, build_layer_blocks, chain_rule_layers  # noqa: F401,E402

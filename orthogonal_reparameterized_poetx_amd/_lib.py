@@ -15,14 +15,15 @@ LIB_PATH = os.path.join(_HERE, "libpoetx.so")
 POETX_F32 = 0
 POETX_BF16 = 1
 POETX_ACCUMULATE_GRAD = 1
-OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS, OP_MERGE_BLOCKS = 0, 1, 2, 3, 4, 5
+OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS, OP_MERGE_BLOCKS, OP_BACKWARD_DQ = range(7)
 
 _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDTYPE",
            -4: "POETX_EWORKSPACE", -5: "POETX_EHIP"}
 
 EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
             "poetx_build_block_sets", "poetx_forward", "poetx_forward_blocks", "poetx_backward",
-            "poetx_backward_blocks", "poetx_merge", "poetx_merge_blocks", "poetx_make_permutation",
+            "poetx_backward_blocks", "poetx_backward_blocks_dq", "poetx_chain_rule_sets",
+            "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_make_permutation",
             "poetx_adam_step",
             "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
 
@@ -68,6 +69,12 @@ def make_blocks(Q32R=None, Q32P=None, QR=None, QP=None, QTR=None, QTP=None):
     return Blocks(_addr(Q32R), _addr(Q32P), _addr(QR), _addr(QP), _addr(QTR), _addr(QTP))
 
 
+class ChainSet(ctypes.Structure):
+    """poetx_chain_set: blocks, their dL/dQ and the generator gradient."""
+    _fields_ = [("Q32", ctypes.c_void_p), ("G", ctypes.c_void_p), ("nblocks", ctypes.c_int64),
+                ("dtheta", ctypes.c_void_p)]
+
+
 class PoetxError(RuntimeError):
     def __init__(self, fn, code, msg):
         super().__init__("%s failed: %s (%d): %s" % (fn, _STATUS.get(code, "?"), code, msg))
@@ -97,6 +104,9 @@ def lib():
         "poetx_forward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, i64, vp, vp, sz, vp]),
         "poetx_backward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_backward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "poetx_backward_blocks_dq": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "poetx_chain_rule_sets": (ctypes.c_int, [ctypes.POINTER(ChainSet), i32, i32, ctypes.c_uint32, vp, sz, vp]),
+        "poetx_chain_workspace_bytes": (sz, [i64, i32]),
         "poetx_merge": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
         "poetx_merge_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
         "poetx_make_permutation": (ctypes.c_int, [u64, u64, i32, i64, vp]),
@@ -179,6 +189,28 @@ def poetx_backward_blocks(layer, W0p, blocks, sigma, tau, X, dY, N, dX, dthR, dt
         ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
         _ptr(X), _ptr(dY), int(N), _ptr(dX), _ptr(dthR), _ptr(dthP), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream)))
+
+
+def poetx_backward_blocks_dq(layer, W0p, blocks, sigma, tau, X, dY, N, dX, GR, GP, ws, stream=None):
+    _check("poetx_backward_blocks_dq", lib().poetx_backward_blocks_dq(
+        ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
+        _ptr(X), _ptr(dY), int(N), _ptr(dX), _ptr(GR), _ptr(GP), _ptr(ws), ws.numel() if ws is not None else 0,
+        _stream(stream)))
+
+
+def chain_workspace_bytes(total_blocks, b):
+    return lib().poetx_chain_workspace_bytes(int(total_blocks), int(b))
+
+
+def poetx_chain_rule_sets(sets, b, accumulate=False, ws=None, stream=None):
+    """sets: sequence of (Q32, G, nblocks, dtheta) tensors."""
+    arr = (ChainSet * max(len(sets), 1))()
+    for i, (q, g, nb, d) in enumerate(sets):
+        arr[i] = ChainSet(_addr(q), _addr(g), int(nb), _addr(d))
+    nbytes = ws.numel() if ws is not None else 0
+    _check("poetx_chain_rule_sets", lib().poetx_chain_rule_sets(arr, len(sets), int(b),
+                                                                POETX_ACCUMULATE_GRAD if accumulate else 0,
+                                                                _ptr(ws), nbytes, _stream(stream)))
 
 
 def poetx_forward(layer, W0p, thR, thP, sigma, tau, X, N, Y, ws, stream=None):

@@ -225,24 +225,39 @@ int build2(const float* th0, int64_t n0, QOut o0, const float* th1, int64_t n1, 
 // bf16 layers: each product is one bf16 GEMM over a tripled K on split
 // operands (fp32-level accuracy), fp32 accumulation and output; cat holds
 // the four split operands.  fp32 layers: fp32 MFMA products.
+// split-operand chain rule over nblk blocks described by cs; GS (fp32
+// [nblk][b][b], contiguous) receives G_S and may alias the g arrays only when
+// a single segment covers them contiguously in block order.
+void chain_bf16(const ChainSegs& cs, int nblk, int b, float* T, uint16_t* const* cat, float* GS, int accumulate,
+                hipStream_t s) {
+  const int64_t sb = (int64_t)b * b;
+  launch_chain_prep1(cs, nblk, b, cat[0], cat[1], cat[2], s);
+  GemmArgs g{};
+  g.M = g.N = b; g.K = 3 * b;
+  g.lda = 3 * b; g.ldb = b; g.ldc = b;
+  g.sA = 3 * sb; g.sB = 3 * sb; g.sC = sb;
+  g.batch = nblk;
+  g.A = cat[0]; g.B = cat[1]; g.Cf = T;                   // T = G (I + Q^T)
+  launch_gemm_bf16_f32out(g, s);
+  launch_chain_prep2(T, nblk, b, cat[3], s);
+  g.A = cat[2]; g.B = cat[3]; g.Cf = GS;                  // G_S = (I + Q^T) T / 2
+  launch_gemm_bf16_f32out(g, s);
+  launch_skew_project(GS, b, nblk, cs, accumulate, s);
+}
+
 int chain(float* G, const float* q32R, const float* q32P, float* tmp, uint16_t* const* cat, int64_t nR, int64_t nP,
           int b, float* dthR, float* dthP, bool accumulate, bool f32, hipStream_t s) {
   const int64_t nblk = nR + nP;
   if (nblk <= 0) return POETX_OK;
   Tm tm(s, "chain_rule", 4.0 * b * (double)b * b * nblk, 0.0);
   const int64_t sb = (int64_t)b * b;
+  ChainSegs cs{};
+  cs.nseg = 0;
+  if (nR > 0) { cs.seg[cs.nseg] = ChainSeg{q32R, G, dthR}; cs.start[cs.nseg] = 0; ++cs.nseg; }
+  if (nP > 0) { cs.seg[cs.nseg] = ChainSeg{q32P, G + nR * sb, dthP}; cs.start[cs.nseg] = (int)nR; ++cs.nseg; }
+  cs.start[cs.nseg] = (int)nblk;
   if (!f32) {
-    launch_chain_prep1(G, q32R, q32P, (int)nR, (int)nblk, b, cat[0], cat[1], cat[2], s);
-    GemmArgs g{};
-    g.M = g.N = b; g.K = 3 * b;
-    g.lda = 3 * b; g.ldb = b; g.ldc = b;
-    g.sA = 3 * sb; g.sB = 3 * sb; g.sC = sb;
-    g.batch = (int)nblk;
-    g.A = cat[0]; g.B = cat[1]; g.Cf = tmp;                 // T = G (I + Q^T)
-    launch_gemm_bf16_f32out(g, s);
-    launch_chain_prep2(tmp, (int)nblk, b, cat[3], s);
-    g.A = cat[2]; g.B = cat[3]; g.Cf = G;                   // G_S = (I + Q^T) T / 2
-    launch_gemm_bf16_f32out(g, s);
+    chain_bf16(cs, (int)nblk, b, tmp, cat, G, accumulate ? 1 : 0, s);
   } else {
     BGemmArgs q{};
     q.M = q.N = q.K = b;
@@ -260,9 +275,22 @@ int chain(float* G, const float* q32R, const float* q32P, float* tmp, uint16_t* 
     r.C = G; r.sC = sb; r.ldc = b;
     r.alpha = 0.5f; r.beta = 0.f;
     launch_bgemm(0, (int)nblk, r, s);
+    launch_skew_project(G, b, (int)nblk, cs, accumulate ? 1 : 0, s);
   }
-  launch_skew_project(G, b, (int)nblk, dthR, (int)nR, dthP, accumulate ? 1 : 0, s);
   return check_launch("chain rule");
+}
+
+// blocks per chunk of poetx_chain_rule_sets and its workspace
+constexpr int64_t kChainChunk = 512;
+size_t chain_ws_bytes(int64_t total, int b) {
+  const int64_t c = std::min<int64_t>(total, kChainChunk);
+  if (c <= 0) return 0;
+  Arena a(nullptr);
+  const size_t bb = (size_t)b * b;
+  for (int i = 0; i < 4; ++i) a.take<uint16_t>(c * 3 * bb);
+  a.take<float>(c * bb);   // T
+  a.take<float>(c * bb);   // G_S
+  return a.off + kAlign;
 }
 
 // block-product flops of one transform: N tokens x k blocks x 2 b^2
@@ -331,7 +359,7 @@ struct BwdWs {
   uint16_t *cat[4];   // chain-rule split operands (bf16 layers)
   void* part;
 };
-BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes) {
+BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes, bool dq = false) {
   Arena a(base);
   BwdWs w{};
   const size_t bb = (size_t)S.b * S.b;
@@ -350,11 +378,13 @@ BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes) {
   w.z2 = a.take<char>((size_t)S.N * S.m * S.es);
   w.gyg = a.take<char>((size_t)S.N * S.m * S.es);
   w.gz2 = a.take<char>((size_t)S.N * S.m * S.es);
-  w.GR = a.take<float>((S.kR + S.kP) * bb);     // R blocks, then P blocks
-  w.GP = w.GR ? w.GR + S.kR * bb : nullptr;
-  w.tmp = a.take<float>((S.kR + S.kP) * bb);
-  if (!S.f32)
-    for (auto& c : w.cat) c = a.take<uint16_t>((S.kR + S.kP) * 3 * bb);
+  if (!dq) {   // dL/dQ and the chain rule stay inside the call
+    w.GR = a.take<float>((S.kR + S.kP) * bb);     // R blocks, then P blocks
+    w.GP = w.GR ? w.GR + S.kR * bb : nullptr;
+    w.tmp = a.take<float>((S.kR + S.kP) * bb);
+    if (!S.f32)
+      for (auto& c : w.cat) c = a.take<uint16_t>((S.kR + S.kP) * 3 * bb);
+  }
   const size_t pb = std::max(gram_partials_bytes(S.N, S.b, S.kR, S.f32), gram_partials_bytes(S.N, S.b, S.kP, S.f32));
   w.part = a.take<char>(pb);
   *bytes = a.off + kAlign;
@@ -480,8 +510,12 @@ int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
 }
 
 // backward after the blocks exist: a0 (recompute), a6, a7, a8, a9
+// gR / gP non-null: write dL/dQ there and stop before the chain rule
 int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
-             const void* dY, void* dX, float* dthR, float* dthP, bool accum, const BwdWs& w, hipStream_t s) {
+             const void* dY, void* dX, float* dthR, float* dthP, bool accum, const BwdWs& w, hipStream_t s,
+             float* gR = nullptr, float* gP = nullptr) {
+  float* const GR = gR ? gR : w.GR;
+  float* const GP = gR ? gP : w.GP;
   const int64_t N = S.N;
   const int n = (int)S.n, m = (int)S.m;
   int rc;
@@ -523,7 +557,7 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   {
     // algorithmic bytes: the reads of gY' and z2'
     Tm tm(s, "gram", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
-    launch_gram(S.f32, w.gyg, w.z2, N, m, S.b, S.kR, w.GR, w.part, s);
+    launch_gram(S.f32, w.gyg, w.z2, N, m, S.b, S.kR, GR, w.part, s);
   }
   if ((rc = check_launch("R-side backward"))) return rc;
   // gz1' = gz2' W0p (into the z1' buffer)
@@ -536,7 +570,7 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   // G_P = gz1'^T x' per block
   {
     Tm tm(s, "gram", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
-    launch_gram(S.f32, gz1, w.xg, N, n, S.b, S.kP, w.GP, w.part, s);
+    launch_gram(S.f32, gz1, w.xg, N, n, S.b, S.kP, GP, w.part, s);
   }
   if ((rc = check_launch("P-side gradient"))) return rc;
   // dX = Pi_tau^T D_P^T gz1'
@@ -553,6 +587,7 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
     }
   }
   if ((rc = check_launch("P-side backward"))) return rc;
+  if (gR) return POETX_OK;
   // chain rule through the Cayley map onto the stored upper triangle
   return chain(w.GR, q.q32R, q.q32P, w.tmp, w.cat, S.kR, S.kP, S.b, dthR, dthP, accum, S.f32, s);
 }
@@ -668,6 +703,7 @@ size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op) {
     case POETX_OP_BACKWARD: plan_bwd(S, true, nullptr, &bytes); break;
     case POETX_OP_FORWARD_BLOCKS: plan_fwd(S, false, nullptr, &bytes); break;
     case POETX_OP_BACKWARD_BLOCKS: plan_bwd(S, false, nullptr, &bytes); break;
+    case POETX_OP_BACKWARD_DQ: plan_bwd(S, false, nullptr, &bytes, true); break;
     case POETX_OP_MERGE: plan_merge(S, true, nullptr, &bytes); break;
     case POETX_OP_MERGE_BLOCKS: plan_merge(S, false, nullptr, &bytes); break;
     default: fail(POETX_EINVAL, "unknown op %d", op); return 0;
@@ -790,6 +826,89 @@ int poetx_backward_blocks(const poetx_layer* layer, const void* W0p, const poetx
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const BwdWs w = plan_bwd(S, false, ws, &need);
   return bwd_core(S, W0p, blk_of(blocks), sigma, tau, X, dY, dX, dthR, dthP, accum, w, s);
+}
+
+int poetx_backward_blocks_dq(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                             const int32_t* sigma, const int32_t* tau, const void* X, const void* dY, int64_t N,
+                             void* dX, float* GR, float* GP, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_bwd_args(layer, N, W0p, sigma, tau, X, dY, GR, GP);
+  if (rc) return rc;
+  if (layer->flags & POETX_ACCUMULATE_GRAD)
+    return fail(POETX_EINVAL, "POETX_ACCUMULATE_GRAD applies to poetx_chain_rule_sets, not to dL/dQ");
+  const Shape S = shape_of(layer, N);
+  if (S.f32) return fail(POETX_EDTYPE, "poetx_backward_blocks_dq takes bf16 layers");
+  if ((rc = check_blocks(S, blocks, true))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    launch_fill_f32(GR, 0.f, (int64_t)S.kR * S.b * S.b, s);
+    launch_fill_f32(GP, 0.f, (int64_t)S.kP * S.b * S.b, s);
+    return check_launch("zero dL/dQ");
+  }
+  size_t need = 0;
+  plan_bwd(S, false, nullptr, &need, true);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const BwdWs w = plan_bwd(S, false, ws, &need, true);
+  return bwd_core(S, W0p, blk_of(blocks), sigma, tau, X, dY, dX, nullptr, nullptr, false, w, s, GR, GP);
+}
+
+size_t poetx_chain_workspace_bytes(int64_t total_blocks, int32_t b) {
+  if (!valid_b(b) || total_blocks < 0) {
+    fail(POETX_EINVAL, "bad chain request total_blocks=%lld b=%d", (long long)total_blocks, b);
+    return 0;
+  }
+  return chain_ws_bytes(total_blocks, b);
+}
+
+int poetx_chain_rule_sets(const poetx_chain_set* sets, int32_t count, int32_t b, uint32_t flags, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!valid_b(b)) return fail(POETX_EINVAL, "block size b=%d not in {32,64,128,256,512}", b);
+  if (count < 0 || count > 65536) return fail(POETX_ESHAPE, "count=%d out of range [0, 65536]", count);
+  if (count > 0 && !sets) return fail(POETX_EINVAL, "sets is NULL");
+  if (flags & ~POETX_ACCUMULATE_GRAD) return fail(POETX_EINVAL, "unknown flags 0x%x", flags);
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const poetx_chain_set& t = sets[i];
+    if (t.nblocks < 0 || t.nblocks > (int64_t(1) << 20))
+      return fail(POETX_ESHAPE, "set %d: nblocks=%lld", i, (long long)t.nblocks);
+    if (t.nblocks > 0 && (!t.Q32 || !t.G || !t.dtheta)) return fail(POETX_EINVAL, "set %d: NULL array", i);
+    total += t.nblocks;
+  }
+  if (total > (int64_t(1) << 24)) return fail(POETX_ESHAPE, "%lld blocks in one call", (long long)total);
+  if (total == 0) return POETX_OK;
+  const int rc = check_ws(ws, ws_bytes, chain_ws_bytes(total, b));
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t chunk = std::min<int64_t>(total, kChainChunk);
+  const size_t bb = (size_t)b * b;
+  Arena a(ws);
+  uint16_t* cat[4];
+  for (auto& c : cat) c = a.take<uint16_t>(chunk * 3 * bb);
+  float* T = a.take<float>(chunk * bb);
+  float* GS = a.take<float>(chunk * bb);
+  Tm tm(s, "chain_rule", 4.0 * b * (double)b * b * total, 0.0);
+  // walk the sets in chunks of at most kChainChunk blocks and CH_MAXSEG pieces
+  int si = 0;
+  int64_t off = 0;   // blocks of set si already done
+  while (si < count) {
+    ChainSegs cs{};
+    int n = 0;
+    while (si < count && cs.nseg < CH_MAXSEG && n < chunk) {
+      const poetx_chain_set& t = sets[si];
+      const int64_t left = t.nblocks - off;
+      if (left <= 0) { ++si; off = 0; continue; }
+      const int take = (int)std::min<int64_t>(left, chunk - n);
+      cs.seg[cs.nseg] = ChainSeg{t.Q32 + off * (int64_t)bb, t.G + off * (int64_t)bb,
+                                 t.dtheta + off * (int64_t)(b * (b - 1) / 2)};
+      cs.start[cs.nseg] = n;
+      ++cs.nseg;
+      n += take;
+      off += take;
+      if (off >= t.nblocks) { ++si; off = 0; }
+    }
+    cs.start[cs.nseg] = n;
+    if (n > 0) chain_bf16(cs, n, b, T, cat, GS, (flags & POETX_ACCUMULATE_GRAD) ? 1 : 0, s);
+  }
+  return check_launch("chain rule");
 }
 
 int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int32_t* sigma, int32_t* tau,

@@ -461,14 +461,20 @@ __global__ __launch_bounds__(256) void finalize_q_kernel(const float* __restrict
 
 // dtheta[blk][p(i,j)] (+)= GS[i][j] - GS[j][i], i < j.  grid (ceil(b/256), b-1, nblk);
 // blocks [0, n0) write dth0, the rest dth1.
-__global__ void skew_project_kernel(const float* __restrict__ GS, int b, float* __restrict__ dth0, int n0,
-                                    float* __restrict__ dth1, int accumulate) {
+__device__ __forceinline__ int chain_seg(const ChainSegs& cs, int z) {
+  int sg = 0;
+  while (sg + 1 < cs.nseg && z >= cs.start[sg + 1]) ++sg;
+  return sg;
+}
+
+__global__ void skew_project_kernel(const float* __restrict__ GS, int b, ChainSegs cs, int accumulate) {
   const int blk = blockIdx.z, i = blockIdx.y;
   const int j = i + 1 + blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= b) return;
+  const int sg = chain_seg(cs, blk);
   const float* g = GS + (int64_t)blk * b * b;
   const float v = g[(int64_t)i * b + j] - g[(int64_t)j * b + i];
-  float* dth = blk < n0 ? dth0 + (int64_t)blk * (b * (b - 1) / 2) : dth1 + (int64_t)(blk - n0) * (b * (b - 1) / 2);
+  float* dth = cs.seg[sg].dth + (int64_t)(blk - cs.start[sg]) * (b * (b - 1) / 2);
   float* d = dth + (i * b - i * (i + 1) / 2 + (j - i - 1));
   *d = accumulate ? (*d + v) : v;
 }
@@ -507,16 +513,17 @@ void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // 32 x 32 tile per workgroup (256 threads, 4 elements each); Q is read
 // coalesced and transposed through LDS
-__global__ __launch_bounds__(256) void chain_prep1_kernel(const float* __restrict__ G, const float* __restrict__ qR,
-                                                          const float* __restrict__ qP, int nR, int b,
-                                                          uint16_t* __restrict__ Acat, uint16_t* __restrict__ Bcat,
-                                                          uint16_t* __restrict__ A2cat) {
+__global__ __launch_bounds__(256) void chain_prep1_kernel(ChainSegs cs, int b, uint16_t* __restrict__ Acat,
+                                                          uint16_t* __restrict__ Bcat, uint16_t* __restrict__ A2cat) {
   __shared__ float qt[32][33];
   const int z = blockIdx.z;
+  const int sg = chain_seg(cs, z);
   const int64_t bb = (int64_t)b * b;
+  const int64_t zl = z - cs.start[sg];
+  const float* __restrict__ q = cs.seg[sg].q + zl * bb;
+  const float* __restrict__ G = cs.seg[sg].g + zl * bb;
   const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // ty 0..7
-  const float* q = z < nR ? qR + (int64_t)z * bb : qP + (int64_t)(z - nR) * bb;
   // qt[jj][ii] = Q[j0 + jj][i0 + ii]
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -530,7 +537,7 @@ __global__ __launch_bounds__(256) void chain_prep1_kernel(const float* __restric
     const int i = i0 + ii, j = j0 + tx;
     // B'[i][j] = (I + Q^T)[i][j] = delta_ij + Q[j][i]
     const float bp = qt[tx][ii] + (i == j ? 1.f : 0.f);
-    const float g = G[z * bb + (int64_t)i * b + j];
+    const float g = G[(int64_t)i * b + j];
     bf16 gh, gl, bh, bl;
     split_bf16(g, gh, gl);
     split_bf16(bp, bh, bl);
@@ -558,11 +565,11 @@ __global__ void chain_prep2_kernel(const float* __restrict__ T, int b, uint16_t*
   c[(int64_t)i * b + j] = H; c[(int64_t)(b + i) * b + j] = L; c[(int64_t)(2 * b + i) * b + j] = H;
 }
 
-void launch_chain_prep1(const float* G, const float* qR, const float* qP, int nR, int nblk, int b, uint16_t* Acat,
-                        uint16_t* Bcat, uint16_t* A2cat, hipStream_t s) {
+void launch_chain_prep1(const ChainSegs& cs, int nblk, int b, uint16_t* Acat, uint16_t* Bcat, uint16_t* A2cat,
+                        hipStream_t s) {
   if (nblk <= 0) return;
   dim3 grid((unsigned)(b / 32), (unsigned)(b / 32), (unsigned)nblk);   // b is a multiple of 32
-  hipLaunchKernelGGL(chain_prep1_kernel, grid, dim3(256), 0, s, G, qR, qP, nR, b, Acat, Bcat, A2cat);
+  hipLaunchKernelGGL(chain_prep1_kernel, grid, dim3(256), 0, s, cs, b, Acat, Bcat, A2cat);
 }
 
 void launch_chain_prep2(const float* T, int nblk, int b, uint16_t* Tcat, hipStream_t s) {
@@ -583,11 +590,10 @@ void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qb
   hipLaunchKernelGGL(finalize_q_kernel, grid, dim3(256), 0, s, M, b, q32, qbf, qtbf);
 }
 
-void launch_skew_project(const float* GS, int b, int nblk, float* dth0, int n0, float* dth1, int accumulate,
-                         hipStream_t s) {
+void launch_skew_project(const float* GS, int b, int nblk, const ChainSegs& cs, int accumulate, hipStream_t s) {
   if (nblk <= 0) return;
   dim3 grid((b + 255) / 256, b - 1, nblk);
-  hipLaunchKernelGGL(skew_project_kernel, grid, dim3(256), 0, s, GS, b, dth0, n0, dth1, accumulate);
+  hipLaunchKernelGGL(skew_project_kernel, grid, dim3(256), 0, s, GS, b, cs, accumulate);
 }
 
 }  // namespace poetx

@@ -118,22 +118,24 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
     }
   };
   // partial last K step: the loads above also fetch columns (A, NT B) or
-  // rows (NN B) past K; zero them in LDS once the loads have landed
+  // rows (NN B) past K.  Each lane zeroes the LDS slots its own loads filled,
+  // after its wave's loads have landed (slots of other waves' loads may
+  // still be in flight).
   auto zero_tail = [&](int k0, uint16_t* as_, uint16_t* bs_) {
     const int kv = K - k0;                  // valid k in this step (multiple of 8)
     if (kv >= GBK) return;
+    const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = tid + 512 * q;
-      const int row = e >> 3, c = e & 7;
-      if (c * 8 >= kv) {
-        const int cz = c ^ ((row >> 1) & 7);
-        *reinterpret_cast<uint4*>(as_ + row * GBK + (cz << 3)) = make_uint4(0, 0, 0, 0);
-        if constexpr (!NN) *reinterpret_cast<uint4*>(bs_ + row * GBK + (cz << 3)) = make_uint4(0, 0, 0, 0);
+      const int r = wave * 32 + q * 8 + (lane >> 3);
+      const int cs = (lane & 7) ^ ((r >> 1) & 7);     // the source chunk this lane loaded
+      if (cs * 8 >= kv) {
+        *reinterpret_cast<uint4*>(as_ + (wave * 32 + q * 8) * GBK + lane * 8) = z;
+        if constexpr (!NN) *reinterpret_cast<uint4*>(bs_ + (wave * 32 + q * 8) * GBK + lane * 8) = z;
       }
       if constexpr (NN) {
-        const int kr = e >> 5, cn = e & 31;
-        if (kr >= kv) *reinterpret_cast<uint4*>(bs_ + kr * GBN + ((cn ^ (kr & 7)) << 3)) = make_uint4(0, 0, 0, 0);
+        const int kr = wave * 8 + q * 2 + (lane >> 5);
+        if (kr >= kv) *reinterpret_cast<uint4*>(bs_ + (wave * 8 + q * 2) * GBN + lane * 8) = z;
       }
     }
   };

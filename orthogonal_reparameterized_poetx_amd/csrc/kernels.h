@@ -42,19 +42,30 @@ struct BGemmArgs {
 void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s);
 void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s);
 void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qbf, uint16_t* qtbf, hipStream_t s);
-// chain-rule operands for fp32-accurate products as single bf16 GEMMs over a
-// tripled K (x = hi + lo, x*y ~ hi*hi + hi*lo + lo*hi).  Block z < nR uses
-// qR[z], else qP[z - nR].  With B' = I + Q^T:
+// chain rule over blocks from up to CH_MAXSEG sources: block z of a launch
+// belongs to the segment s with start[s] <= z < start[s+1] and is block
+// z - start[s] of that segment's arrays (q: fp32 Q, g: dL/dQ, dth: output).
+constexpr int CH_MAXSEG = 64;
+struct ChainSeg {
+  const float* q;
+  const float* g;
+  float* dth;
+};
+struct ChainSegs {
+  ChainSeg seg[CH_MAXSEG];
+  int start[CH_MAXSEG + 1];
+  int nseg;
+};
+// operands for fp32-accurate products as single bf16 GEMMs over a tripled K
+// (x = hi + lo, x*y ~ hi*hi + hi*lo + lo*hi).  With B' = I + Q^T:
 //   prep1: Acat[z] = [G_hi | G_hi | G_lo] ([b][3b]), Bcat[z] = [B'_hi; B'_lo; B'_hi]
 //          ([3b][b]), A2cat[z] = [B'_hi | B'_hi | B'_lo] ([b][3b])
 //   prep2: Tcat[z] = split of (T / 2) as [hi; lo; hi] ([3b][b])
-void launch_chain_prep1(const float* G, const float* qR, const float* qP, int nR, int nblk, int b, uint16_t* Acat,
-                        uint16_t* Bcat, uint16_t* A2cat, hipStream_t s);
+void launch_chain_prep1(const ChainSegs& cs, int nblk, int b, uint16_t* Acat, uint16_t* Bcat, uint16_t* A2cat,
+                        hipStream_t s);
 void launch_chain_prep2(const float* T, int nblk, int b, uint16_t* Tcat, hipStream_t s);
-// blocks [0, n0) project into dth0, the rest into dth1
-void launch_skew_project(const float* GS, int b, int nblk, float* dth0, int n0, float* dth1, int accumulate,
-                         hipStream_t s);
-
+// dth of block z = (GS[z] - GS[z]^T) on the strict upper triangle (GS contiguous)
+void launch_skew_project(const float* GS, int b, int nblk, const ChainSegs& cs, int accumulate, hipStream_t s);
 // ---- block transforms (transform.hip)
 // bf16 row permutations of a token-major [N][W] matrix:
 //   gather : out[t][j] = in[t][perm[j]]; if tail_out, also tail_out[t][j] for j >= tail0

@@ -133,6 +133,25 @@ class PoetxLayer:
             self.layer.flags = 0
         return dX, dthR, dthP
 
+    def dq_buffers(self):
+        """fp32 dL/dQ of this layer's R and P blocks ([k][b][b] each)."""
+        if "dq" not in self._blk:
+            kR, kP, b = self.m // self.b, self.n // self.b, self.b
+            self._blk["dq"] = (torch.empty(kR, b, b, dtype=torch.float32, device=self.device),
+                               torch.empty(kP, b, b, dtype=torch.float32, device=self.device))
+        return self._blk["dq"]
+
+    def backward_blocks_dq(self, X, dY, dX=None, want_dx=True, stream=None):
+        """Backward up to dL/dQ (see chain_rule_layers); returns (dX, GR, GP)."""
+        N = X.shape[0]
+        if dX is None and want_dx:
+            dX = torch.empty(N, self.n, dtype=self.tdtype, device=self.device)
+        GR, GP = self.dq_buffers()
+        ws = self.workspace(L.OP_BACKWARD_DQ, N)
+        L.poetx_backward_blocks_dq(self.layer, self.W0p, self.block_buffers("backward")[1], self.sigma, self.tau,
+                                   X, dY, N, dX if want_dx else None, GR, GP, ws, stream)
+        return dX, GR, GP
+
     def merge_blocks(self, stream=None):
         """Merge with blocks from build_layer_blocks(..., "merge")."""
         ws = self.workspace(L.OP_MERGE_BLOCKS)
@@ -165,3 +184,26 @@ def build_layer_blocks(layers, kind, stream=None):
             ws = L.make_workspace(need, dev)
             _build_ws[(dev, b)] = ws
         L.poetx_build_block_sets(sets, b, ws if need else None, stream)
+
+
+_chain_ws = {}
+
+
+def chain_rule_layers(layers, grads, accumulate=False, stream=None):
+    """Generator gradients of many layers from their dL/dQ (backward_blocks_dq)
+    and backward blocks, in one poetx_chain_rule_sets call per block size.
+    grads: one (dthR, dthP) pair per layer."""
+    by_b = {}
+    for lay, (dR, dP) in zip(layers, grads):
+        q, _ = lay.block_buffers("backward")
+        GR, GP = lay.dq_buffers()
+        kR, kP = lay.m // lay.b, lay.n // lay.b
+        by_b.setdefault(lay.b, []).extend([(q["Q32R"], GR, kR, dR), (q["Q32P"], GP, kP, dP)])
+    for b, sets in by_b.items():
+        dev = layers[0].device
+        need = L.chain_workspace_bytes(sum(s[2] for s in sets), b)
+        ws = _chain_ws.get((dev, b))
+        if need and (ws is None or ws.numel() < need):
+            ws = L.make_workspace(need, dev)
+            _chain_ws[(dev, b)] = ws
+        L.poetx_chain_rule_sets(sets, b, accumulate, ws if need else None, stream)

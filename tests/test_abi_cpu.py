@@ -168,3 +168,35 @@ def test_merge_blocks_validates_on_host():
     l32 = P.Layer(512, 256, 64, P.POETX_F32)
     assert L.poetx_merge_blocks(ctypes.byref(l32), fake, ctypes.byref(ok), fake, fake, fake, fake, 1, 1, fake,
                                 1 << 30, None) == -1
+
+
+def test_deferred_chain_entry_points_validate_on_host():
+    P = _P()
+    L = P.lib()
+    fake = ctypes.c_void_p(0x1000)
+    f = 0x2000
+    lay = P.Layer(512, 256, 64, P.POETX_BF16)
+    need = P.workspace_bytes(lay, 64, P.OP_BACKWARD_DQ)
+    assert 0 < need < P.workspace_bytes(lay, 64, P.OP_BACKWARD_BLOCKS)
+    blk = P.Blocks(f, f, None, f, f, f)
+    args = lambda l, GR, GP, nb: (ctypes.byref(l), fake, ctypes.byref(blk), fake, fake, fake, fake, 64, fake, GR, GP,
+                                  fake, nb, None)
+    assert L.poetx_backward_blocks_dq(*args(lay, None, fake, need)) == -1
+    assert L.poetx_backward_blocks_dq(*args(lay, fake, fake, need - 1)) == -4
+    acc = P.Layer(512, 256, 64, P.POETX_BF16, P.POETX_ACCUMULATE_GRAD)
+    assert L.poetx_backward_blocks_dq(*args(acc, fake, fake, need)) == -1
+    l32 = P.Layer(512, 256, 64, P.POETX_F32)
+    assert L.poetx_backward_blocks_dq(*args(l32, fake, fake, 1 << 30)) == -3
+    S = P.ChainSet
+    two = (S * 2)(S(0x1000, 0x2000, 3, 0x3000), S(0x1000, 0x2000, 5, 0x3000))
+    wneed = P.chain_workspace_bytes(8, 64)
+    assert wneed > 8 * 64 * 64 * 8
+    assert L.poetx_chain_rule_sets(two, -1, 64, 0, None, 0, None) == -2
+    assert L.poetx_chain_rule_sets(None, 2, 64, 0, None, 0, None) == -1
+    assert L.poetx_chain_rule_sets(two, 2, 48, 0, None, 0, None) == -1
+    assert L.poetx_chain_rule_sets(two, 2, 64, 4, fake, wneed, None) == -1
+    assert L.poetx_chain_rule_sets(two, 2, 64, 0, fake, wneed - 1, None) == -4
+    bad = (S * 1)(S(0x1000, None, 3, 0x3000))
+    assert L.poetx_chain_rule_sets(bad, 1, 64, 0, fake, wneed, None) == -1
+    assert L.poetx_chain_rule_sets((S * 1)(S(None, None, 0, None)), 1, 64, 0, None, 0, None) == 0
+    assert L.poetx_chain_rule_sets(two, 0, 64, 0, None, 0, None) == 0

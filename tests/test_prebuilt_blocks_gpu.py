@@ -137,3 +137,37 @@ def test_merge_blocks_matches_merge(dtype, m, n, b):
     assert torch.equal(a.W0p, c.W0p)
     assert torch.equal(a.sigma, c.sigma) and torch.equal(a.tau, c.tau)
     assert not c.thR.any().item() and not c.thP.any().item()
+
+
+@pytest.mark.parametrize("shapes,b,N", [
+    ([(600, 520), (256, 768), (512, 512)], 256, 70),
+    ([(512, 1024)] * 40, 32, 20),                 # 80 sets, 1920 blocks: several chunks of the batched chain
+    ([(1100, 700), (512, 1024)], 512, 24),
+])
+def test_deferred_chain_matches_backward_blocks(shapes, b, N):
+    torch = torch_mod()
+    from orthogonal_reparameterized_poetx_amd import build_layer_blocks, chain_rule_layers
+    layers, ds = [], []
+    for i, (m, n) in enumerate(shapes):
+        inp = WL.small_case(60 + i, m, n, b, N, dtype="bf16")
+        lay, d = make_layer(inp)
+        layers.append(lay), ds.append(d)
+    _log("deferred chain b=%d layers=%d" % (b, len(layers)))
+    build_layer_blocks(layers, "backward")
+    ref, grads, dxs = [], [], []
+    for lay, d in zip(layers, ds):
+        ref.append(lay.backward_blocks(d["X"], d["gY"]))
+        dX, _, _ = lay.backward_blocks_dq(d["X"], d["gY"])
+        dxs.append(dX)
+        grads.append((torch.empty_like(lay.thR), torch.empty_like(lay.thP)))
+    chain_rule_layers(layers, grads)
+    torch.cuda.synchronize()
+    for (dX0, dR0, dP0), dX, (dR, dP) in zip(ref, dxs, grads):
+        assert torch.equal(dX0, dX)
+        assert torch.equal(dR0, dR) and torch.equal(dP0, dP)
+    # accumulation into existing gradients
+    acc = [(dR.clone(), dP.clone()) for dR, dP in grads]
+    chain_rule_layers(layers, acc, accumulate=True)
+    torch.cuda.synchronize()
+    for (dR, dP), (aR, aP) in zip(grads, acc):
+        assert torch.equal(aR, dR + dR) and torch.equal(aP, dP + dP)
