@@ -280,11 +280,21 @@ class Stack:
         self.adam_steps = 0
 
     def forward_backward(self):
-        P = self.P
+        P, torch = self.P, self.torch
+        main = torch.cuda.current_stream()
+        if not hasattr(self, "side"):
+            self.side = torch.cuda.Stream()      # default priority
+            self.bwd_ready = torch.cuda.Event()
+        # the backward blocks depend only on the generators: build them on a
+        # second stream while the forward pass runs
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            P.build_layer_blocks(self.layers, "backward")
+            self.bwd_ready.record(self.side)
         P.build_layer_blocks(self.layers, "forward")
         for lay, o in zip(self.layers, self.out):
             lay.forward_blocks(self.X[lay.x_key], Y=o["Y"])
-        P.build_layer_blocks(self.layers, "backward")
+        main.wait_event(self.bwd_ready)
         for lay, g, o in zip(reversed(self.layers), reversed(self.gY), reversed(self.out)):
             lay.backward_blocks_dq(self.X[lay.x_key], g, dX=o["dX"])
         P.chain_rule_layers(self.layers, [(lay.dR, lay.dP) for lay in self.layers])
@@ -423,14 +433,23 @@ def main():
         for lay, g, o in zip(reversed(layers), reversed(gYs), reversed(outs)):
             lay.backward(Xs[lay.x_key], g, dX=o["dX"], dthR=o["dR"], dthP=o["dP"])
 
+    side = torch.cuda.Stream()          # default priority
+    bwd_blocks_ready = torch.cuda.Event()
+
     def step_batched():
         # blocks of all seven matrices in one build per pass; the backward pass
-        # rebuilds them from the generators instead of keeping the forward's,
-        # and runs the chain rule once for all seven after their dL/dQ
+        # rebuilds them from the generators instead of keeping the forward's
+        # (on a second stream, concurrently with the forward pass: the build
+        # needs only the generators), and runs the chain rule once for all
+        # seven after their dL/dQ
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            P.build_layer_blocks(layers, "backward")
+            bwd_blocks_ready.record(side)
         P.build_layer_blocks(layers, "forward")
         for lay, o in zip(layers, outs):
             lay.forward_blocks(Xs[lay.x_key], Y=o["Y"])
-        P.build_layer_blocks(layers, "backward")
+        stream.wait_event(bwd_blocks_ready)
         for lay, g, o in zip(reversed(layers), reversed(gYs), reversed(outs)):
             lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"])
         P.chain_rule_layers(layers, [(o["dR"], o["dP"]) for o in outs])

@@ -179,10 +179,12 @@ def build_layer_blocks(layers, kind, stream=None):
     for b, sets in by_b.items():
         dev = layers[0].device
         need = L.build_workspace_bytes(max(s[1] for s in sets), b)
-        ws = _build_ws.get((dev, b))
+        # one workspace per kind: builds of different kinds may run
+        # concurrently on different streams
+        ws = _build_ws.get((dev, b, kind))
         if need and (ws is None or ws.numel() < need):
             ws = L.make_workspace(need, dev)
-            _build_ws[(dev, b)] = ws
+            _build_ws[(dev, b, kind)] = ws
         L.poetx_build_block_sets(sets, b, ws if need else None, stream)
 
 
