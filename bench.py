@@ -75,10 +75,13 @@ def parse():
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
                          "'bench.py --calibrate-copy' into profiles/traffic_<class>.json")
     ap.add_argument("--kernel-stats", metavar="CSV",
-                    help="no GPU: summarize a rocprofv3 --stats kernel_stats.csv by kernel class")
+                    help="no GPU: summarize by kernel class a rocprofv3 kernel_stats.csv (whole run) or a "
+                         "kernel_trace.csv (only the marked, serialized per-kernel timing pass)")
     ap.add_argument("--workload", choices=("layerset", "stack24"), default="layerset",
                     help="layerset: fwd+bwd of the LLaMA-1B layer set (default); stack24: one training step of the "
                          "24-layer stack with Adam and the global merge")
+    ap.add_argument("--streams", type=int, default=3,
+                    help="HIP streams the seven independent matrices are spread over (batched mode)")
     ap.add_argument("--per-layer-builds", action="store_true",
                     help="let every forward / backward call build its own blocks (one builder launch per call) "
                          "instead of one batched build per pass")
@@ -171,11 +174,33 @@ def traffic_from(fetch_dir, write_dir):
                  launches_f))
 
 
-def kernel_stats(path):
-    """Per-class totals of a rocprofv3 kernel_stats.csv (durations in ns)."""
+def _trace_window(path, steps):
+    """kernel_stats-like rows from a rocprofv3 kernel_trace.csv, restricted to
+    the launches between the two marker kernels (sigmoid) that bracket the
+    serialized per-kernel timing pass; durations divided into per-step
+    figures by ``steps``."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    marks = [r for r in rows if "sigmoid" in r["Kernel_Name"]]
+    if len(marks) < 2:
+        raise SystemExit("marker kernels not found in %s" % path)
+    t0, t1 = int(marks[-2]["End_Timestamp"]), int(marks[-1]["Start_Timestamp"])
+    agg = {}
+    for r in rows:
+        if int(r["Start_Timestamp"]) >= t0 and int(r["End_Timestamp"]) <= t1:
+            a = agg.setdefault(r["Kernel_Name"], [0, 0.0])
+            a[0] += 1
+            a[1] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return [dict(Name=k, Calls=str(v[0]), TotalDurationNs=str(v[1]), AverageNs=str(v[1] / v[0]))
+            for k, v in agg.items()]
+
+
+def kernel_stats(path, steps=None):
+    """Per-class totals of a rocprofv3 kernel_stats.csv, or of the marked
+    per-kernel timing window of a kernel_trace.csv (durations in ns)."""
     import csv
     agg = {}
-    rows = list(csv.DictReader(open(path)))
+    rows = _trace_window(path, steps) if path.endswith("kernel_trace.csv") else list(csv.DictReader(open(path)))
     for row in rows:
         cls, per = kernel_class(row["Name"])
         cls = cls or "other"
@@ -207,7 +232,7 @@ class Stack:
     can check them; the rest draw the same distributions on the device from a
     torch generator seeded by (config, matrix, stream)."""
 
-    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=()):
+    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=(), streams=3):
         import math
         import numpy as np
         self.P, self.torch, self.N = P, torch, N
@@ -234,13 +259,19 @@ class Stack:
             return torch.from_numpy(a.astype(np.float32)).to(dev)
 
         exact_owners = {WL.input_owner(cfg, j) for j in exact}
-        pool = {}
+        # matrices run on `streams` streams (matrix i on stream i % streams);
+        # each stream has its own workspace pool
+        self.nstreams = max(int(streams), 1)
+        pools = [{} for _ in range(self.nstreams)]
         self.layers, self.X, self.gY, self.out = [], {}, [], []
+        mats_done = []
         off = 0
         bf = torch.bfloat16
         for l, idx, m, n in mats:
             j = 7 * l + idx
-            lay = P.PoetxLayer(m, n, b, "bf16", dev, perm_seed=WL.perm_seed(5, j), ws_pool=pool)
+            lay = P.PoetxLayer(m, n, b, "bf16", dev, perm_seed=WL.perm_seed(5, j),
+                               ws_pool=pools[len(mats_done) % self.nstreams])
+            mats_done.append(j)
             kR, kP = m // b, n // b
             lay.thR = self.theta[off:off + kR * nt].view(kR, nt)
             lay.dR = self.grad[off:off + kR * nt].view(kR, nt)
@@ -279,12 +310,22 @@ class Stack:
             lay.dq_buffers()
         self.adam_steps = 0
 
+    def _fan_out(self, main, idx_items, fn):
+        for w in self.workers[1:]:
+            w.wait_stream(main)
+        for i, item in idx_items:
+            with self.torch.cuda.stream(self.workers[i % self.nstreams]):
+                fn(*item)
+        for w in self.workers[1:]:
+            main.wait_stream(w)
+
     def forward_backward(self):
         P, torch = self.P, self.torch
         main = torch.cuda.current_stream()
         if not hasattr(self, "side"):
-            self.side = torch.cuda.Stream()      # default priority
+            self.side = torch.cuda.Stream()      # all streams at the default priority
             self.bwd_ready = torch.cuda.Event()
+            self.workers = [main] + [torch.cuda.Stream() for _ in range(self.nstreams - 1)]
         # the backward blocks depend only on the generators: build them on a
         # second stream while the forward pass runs
         self.side.wait_stream(main)
@@ -292,11 +333,12 @@ class Stack:
             P.build_layer_blocks(self.layers, "backward")
             self.bwd_ready.record(self.side)
         P.build_layer_blocks(self.layers, "forward")
-        for lay, o in zip(self.layers, self.out):
-            lay.forward_blocks(self.X[lay.x_key], Y=o["Y"])
+        n = len(self.layers)
+        self._fan_out(main, [(i, (self.layers[i], self.out[i])) for i in range(n)],
+                      lambda lay, o: lay.forward_blocks(self.X[lay.x_key], Y=o["Y"]))
         main.wait_event(self.bwd_ready)
-        for lay, g, o in zip(reversed(self.layers), reversed(self.gY), reversed(self.out)):
-            lay.backward_blocks_dq(self.X[lay.x_key], g, dX=o["dX"])
+        self._fan_out(main, [(i, (self.layers[i], self.gY[i], self.out[i])) for i in reversed(range(n))],
+                      lambda lay, g, o: lay.backward_blocks_dq(self.X[lay.x_key], g, dX=o["dX"]))
         P.chain_rule_layers(self.layers, [(lay.dR, lay.dP) for lay in self.layers])
 
     def adam(self):
@@ -305,8 +347,10 @@ class Stack:
 
     def merge(self):
         self.P.build_layer_blocks(self.layers, "merge")
-        for lay in self.layers:
-            lay.merge_blocks()
+        main = self.torch.cuda.current_stream()
+        if not hasattr(self, "workers"):
+            self.workers = [main] + [self.torch.cuda.Stream() for _ in range(self.nstreams - 1)]
+        self._fan_out(main, list(enumerate((lay,) for lay in self.layers)), lambda lay: lay.merge_blocks())
 
     def step(self):
         self.forward_backward()
@@ -322,7 +366,7 @@ def bench_stack(args):
     dev = "cuda:0"
     torch.cuda.set_device(0)
     N = args.tokens or WL.CONFIGS[5]["N"]
-    st = Stack(P, WL, torch, dev, N)
+    st = Stack(P, WL, torch, dev, N, streams=args.streams)
     torch.cuda.synchronize()
     resident = torch.cuda.memory_allocated()
     stream = torch.cuda.current_stream()
@@ -435,6 +479,22 @@ def main():
 
     side = torch.cuda.Stream()          # default priority
     bwd_blocks_ready = torch.cuda.Event()
+    # the seven matrices are independent given their inputs: spread them over
+    # streams (all at the default priority) so one matrix's kernel tails and
+    # small launches overlap another's work
+    workers = [stream] + [torch.cuda.Stream() for _ in range(max(args.streams, 1) - 1)]
+
+    active = {"workers": workers, "side": side}
+
+    def fan_out(items, fn):
+        ws = active["workers"]
+        for w in ws[1:]:
+            w.wait_stream(stream)
+        for i, item in enumerate(items):
+            with torch.cuda.stream(ws[i % len(ws)]):
+                fn(*item)
+        for w in ws[1:]:
+            stream.wait_stream(w)
 
     def step_batched():
         # blocks of all seven matrices in one build per pass; the backward pass
@@ -442,16 +502,16 @@ def main():
         # (on a second stream, concurrently with the forward pass: the build
         # needs only the generators), and runs the chain rule once for all
         # seven after their dL/dQ
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
+        bs = active["side"]
+        bs.wait_stream(stream)
+        with torch.cuda.stream(bs):
             P.build_layer_blocks(layers, "backward")
-            bwd_blocks_ready.record(side)
+            bwd_blocks_ready.record(bs)
         P.build_layer_blocks(layers, "forward")
-        for lay, o in zip(layers, outs):
-            lay.forward_blocks(Xs[lay.x_key], Y=o["Y"])
+        fan_out(list(zip(layers, outs)), lambda lay, o: lay.forward_blocks(Xs[lay.x_key], Y=o["Y"]))
         stream.wait_event(bwd_blocks_ready)
-        for lay, g, o in zip(reversed(layers), reversed(gYs), reversed(outs)):
-            lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"])
+        fan_out(list(zip(reversed(layers), reversed(gYs), reversed(outs))),
+                lambda lay, g, o: lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"]))
         P.chain_rule_layers(layers, [(o["dR"], o["dP"]) for o in outs])
 
     step = step_per_layer if args.per_layer_builds else step_batched
@@ -467,13 +527,25 @@ def main():
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- per-kernel breakdown (separate pass: events around every launch)
+    # ---- per-kernel breakdown: a separate pass with events around every
+    # launch, with the matrices serialized on one stream so that every launch
+    # has the GPU to itself (its duration then measures the kernel, not its
+    # neighbours).  Two marker kernels (sigmoid on a 1-element tensor)
+    # bracket the pass so that a profiler trace can pick out its launches.
+    marker = torch.zeros(1, device=dev)
+    torch.cuda.synchronize()
+    torch.sigmoid_(marker)
+    torch.cuda.synchronize()
+    active["workers"], active["side"] = [stream], stream
     P.timing_enable(True)
     for _ in range(args.profile_steps):
         step()
     torch.cuda.synchronize()
     kern = P.timing_summary()
     P.timing_enable(False)
+    active["workers"], active["side"] = workers, side
+    torch.sigmoid_(marker)
+    torch.cuda.synchronize()
     per_step = {k: dict(v, ms=v["ms"] / args.profile_steps, launches=v["launches"] / args.profile_steps,
                         flops=v["flops"] / args.profile_steps, bytes=v["bytes"] / args.profile_steps)
                 for k, v in kern.items()}
@@ -529,7 +601,8 @@ def main():
         "config": {"workload": cfg["name"], "tokens": N, "matrices": len(cfg["mats"]), "b": cfg["b"],
                    "shapes": ["%dx%d" % (m, n) for _, m, n in cfg["mats"]],
                    "block_builds": "per layer call" if args.per_layer_builds else
-                   "batched per pass (Cayley builds and chain rule over all seven matrices)"},
+                   "batched per pass (Cayley builds and chain rule over all seven matrices)",
+                   "streams": 1 if args.per_layer_builds else max(args.streams, 1)},
         "roofline": roof,
         "kernels_per_step": breakdown,
         "merge_ms_layer_set": round(merge_ms, 3),
