@@ -465,7 +465,7 @@ int blockmul(const void* in, const uint16_t* q, void* out, int64_t N, int W, int
   g.sA = b; g.sB = (int64_t)b * b; g.sC = b;
   g.batch = k;
   Tm tm(s, "xform_blockmul", xf_flops(N, k, b), 2.0 * N * (double)k * b * 2);
-  launch_gemm_bf16(false, g, s);
+  if (!launch_blockdiag_bf16(g.A, q, g.C, N, W, W, b, k, s)) launch_gemm_bf16(false, g, s);
   return check_launch("block product");
 }
 

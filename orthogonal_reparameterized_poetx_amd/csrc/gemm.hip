@@ -109,12 +109,29 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
       vob[q] = (int)(((int64_t)kr * ldb + cn * 8) * 2);
     }
   }
+  // On a partial last K step the A (and NT B) lanes whose chunk lies at or
+  // past K load nothing: with a strided operand those columns can run past
+  // the end of the allocation on its last row (the buffer range covers whole
+  // rows).  zero_tail fills their slots.
   auto dload = [&](int k0, uint16_t* as_, uint16_t* bs_) {
+    const int kv = K - k0;
+    if (kv >= GBK) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      b2l16(ra, voa[q], k0 * 2, as_ + (wave * 32 + q * 8) * GBK);
-      if constexpr (!NN) b2l16(rb, vob[q], k0 * 2, bs_ + (wave * 32 + q * 8) * GBK);
-      else b2l16(rb, vob[q], (int)((int64_t)k0 * ldb * 2), bs_ + (wave * 8 + q * 2) * GBN);
+      for (int q = 0; q < 4; ++q) {
+        b2l16(ra, voa[q], k0 * 2, as_ + (wave * 32 + q * 8) * GBK);
+        if constexpr (!NN) b2l16(rb, vob[q], k0 * 2, bs_ + (wave * 32 + q * 8) * GBK);
+        else b2l16(rb, vob[q], (int)((int64_t)k0 * ldb * 2), bs_ + (wave * 8 + q * 2) * GBN);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wave * 32 + q * 8 + (lane >> 3);
+        if (((lane & 7) ^ ((r >> 1) & 7)) * 8 < kv) {
+          b2l16(ra, voa[q], k0 * 2, as_ + (wave * 32 + q * 8) * GBK);
+          if constexpr (!NN) b2l16(rb, vob[q], k0 * 2, bs_ + (wave * 32 + q * 8) * GBK);
+        }
+        if constexpr (NN) b2l16(rb, vob[q], (int)((int64_t)k0 * ldb * 2), bs_ + (wave * 8 + q * 2) * GBN);
+      }
     }
   };
   // partial last K step: the loads above also fetch columns (A, NT B) or

@@ -97,6 +97,15 @@ struct XformArgs {
 void launch_gather_in_f32(const XformArgs& a, hipStream_t s);
 void launch_scatter_out_f32(const XformArgs& a, hipStream_t s);
 
+// ---- block-diagonal products (blockdiag.hip)
+// out[t][l*b + i] = sum_kk in[t][l*b + kk] * q[l][i][kk] for l < k, t < N (bf16,
+// fp32 accumulation; row strides lda, ldc; columns from k*b on untouched).
+// Returns false, launching nothing, where the streaming kernel does not apply
+// (b not in {32, 64, 128, 256}, rows or pointers not 16-byte aligned, or
+// offsets beyond 32 bits); the caller then uses the batched GEMM.
+bool launch_blockdiag_bf16(const uint16_t* in, const uint16_t* q, uint16_t* out, int64_t N, int64_t lda,
+                           int64_t ldc, int b, int k, hipStream_t s);
+
 // ---- dense GEMMs (gemm.hip): C[M][N] = A[M][K] * op(B)
 // nt: B is [N][K] (C = A B^T); nn: B is [K][N] (C = A B)
 // Batched bf16 GEMM with strides (elements): for z < batch,
