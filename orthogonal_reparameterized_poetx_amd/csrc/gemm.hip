@@ -7,58 +7,66 @@
 //   NT: C[M][N] = A[M][K] * B[N][K]^T   (z2 = z1 W0p^T; both K-contiguous)
 //   NN: C[M][N] = A[M][K] * B[K][N]     (gz1 = gz2 W0p; B is N-contiguous)
 //
-// bf16 operands, fp32 accumulation on 32x32x16 MFMA, bf16 output.  256x256x64
-// tiles, 8 waves of 128x64, double-buffered LDS with 16-byte XOR swizzle; the
-// NN B operand is read K-major straight from the N-contiguous tile with the
-// gfx950 transposing LDS load.  Tiles are assigned so that the workgroups on
-// one XCD (blockIdx mod 8) work on neighbouring output tiles and share L2.
+// bf16 operands, fp32 accumulation on 32x32x16 MFMA, bf16 output.  256x256
+// output tiles, 8 waves of 128x64, k in steps of 32 through a 4-stage LDS
+// ring with 16-byte XOR swizzles; the NN B operand is read K-major straight
+// from the N-contiguous tile with the gfx950 transposing LDS load.  Tiles are
+// assigned so that the workgroups on one XCD (blockIdx mod 8) work on
+// neighbouring output tiles and share L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace poetx {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GBM = 256, GBN = 256;
 
 __device__ __forceinline__ i16x4 ds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, const_cast<uint16_t*>(p)));
 }
-
-// 16-byte global -> LDS copy that bypasses the VGPRs: lane i of the wave
-// writes lds_base + 16 i (lds_base must be wave-uniform).  Streaming tiles this
-// way, one contiguous KiB per instruction, reaches several times the L2
-// bandwidth of register loads in MFMA-fragment order.
-__device__ __forceinline__ void g2l16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Buffer resource over [base, base + bytes): loads past the end read zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int nrec = (int)(bytes < 0x7fffffff ? (bytes > 0 ? bytes : 0) : 0x7fffffff);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
 }
-// 16-byte buffer load straight into LDS: lane i writes lds_base + 16 i
+// 16-byte buffer load straight into LDS, bypassing the VGPRs: lane i of the
+// wave writes lds_base + 16 i (lds_base must be wave-uniform).  Streaming tiles
+// this way, one contiguous KiB per instruction, reaches several times the L2
+// bandwidth of register loads in MFMA-fragment order.
 __device__ __forceinline__ void b2l16(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
 }
 
-// LDS tile layouts (bf16, 16-byte chunks XOR-swizzled by row):
-//   A (and NT B): [256 rows][64 k], chunk c of row r stored at chunk c ^ ((r >> 1) & 7):
+// Ring of GST LDS stages, each a 32-deep k step of both operands (A tile
+// [256 rows][32 k], then B), filled by buffer-to-LDS loads GST - 1 steps
+// ahead of the step being computed.  16-byte chunks are XOR-swizzled by row
+// (the loads pick each lane's source chunk so that the fixed lane -> LDS slot
+// placement produces the swizzle):
+//   A, NT B: [256 rows][32 k], 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3):
 //     a 16-lane phase of a fragment read (16 consecutive rows, one chunk)
-//     then touches every bank once (rows r, r+1 differ in the bank half,
-//     the key spreads the 8 row pairs over the 8 chunk positions)
-//   NN B:         [64 k rows][256 n], chunk c of row r stored at chunk c ^ (r & 7)
-// The direct loads pick each lane's source chunk so that the fixed lane ->
-// LDS slot placement produces exactly this layout.
+//     touches every bank once
+//   NN B:    [32 k rows][256 n], 512-byte rows, chunk c of row r at
+//     c ^ ((r & 3) << 2): a 32-lane phase of the transposing read (4 rows,
+//     4 chunks, two halves each) touches every bank pair once
 // BATCHED only names the instantiation used for batched block products, so
 // that profiles tell it apart from the weight products.  OUTF32 writes the
-// fp32 accumulators to g.Cf instead of bf16 to g.C.
-template <bool NN, bool BATCHED, bool OUTF32 = false>
+// fp32 accumulators to g.Cf instead of bf16 to g.C.  SMALL takes K below
+// 32 (GST - 2) + 1, where the ring is never full.
+constexpr int GST = 4;                 // ring stages
+constexpr int GSE = 2 * 256 * 32;      // elements per stage (A and B)
+// s_waitcnt immediate waiting for vmcnt <= vm only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  The builtin, unlike inline
+// asm, is seen by the compiler's wait insertion, which then knows which
+// asynchronous LDS fills have completed.
+constexpr unsigned vm_imm(unsigned vm) { return (vm & 15u) | ((vm >> 4) << 14) | (7u << 4) | (15u << 8); }
+
+template <bool NN, bool BATCHED, bool OUTF32, bool SMALL>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
-  // two buffers as separate LDS objects, each named at compile time below, so
-  // the compiler can tell reads of one from the asynchronous fill of the other
-  __shared__ __align__(16) uint16_t As0[GBM * GBK], As1[GBM * GBK];
-  __shared__ __align__(16) uint16_t Bs0[GBN * GBK], Bs1[GBN * GBK];
+  // the four ring stages as separate LDS objects, each named at compile time
+  // below, so that the compiler can tell reads of one from the asynchronous
+  // fills of the others; a stage holds the A tile, then the B tile
+  constexpr int S = GST;
+  __shared__ __align__(16) uint16_t S0[GSE], S1[GSE], S2[GSE], S3[GSE];
   // XCD-aware tile order: dispatch id d runs on XCD d % 8; give each XCD a
   // contiguous run of tiles (batch-major, then row-major over the tile grid).
   const int d = blockIdx.x;
@@ -88,93 +96,87 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // full K step: asynchronous buffer loads into LDS.  Per lane, one 32-bit
-  // byte offset per instruction is loop-invariant; the K position is a
-  // scalar offset.  Rows past M (or N) lie outside the tile's buffer range
-  // and read zero.
+  // asynchronous buffer loads into LDS.  Per lane, one 32-bit byte offset per
+  // instruction is loop-invariant; the K position is a scalar offset for A
+  // and NT B.  Rows past M (or N) lie outside the tile's buffer range and
+  // read zero.  The NN B operand adds its K position to the per-lane offset
+  // instead: the range check covers only that offset, and the last row of a
+  // partial N tile would otherwise read past the end of B.
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * lda, (int64_t)min(M - m0, GBM) * lda * 2);
   const __amdgpu_buffer_rsrc_t rb = NN ? make_rsrc(Bm + n0, ((int64_t)K * ldb - n0) * 2)
                                        : make_rsrc(Bm + (int64_t)n0 * ldb, (int64_t)min(N - n0, GBN) * ldb * 2);
-  int voa[4], vob[4];
+  // per-lane source offsets: instruction q (0, 1) of wave w fills KiB
+  // (2 w + q) of a 16 KiB operand tile
+  //   A, NT B: [256 rows][32 k], 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3)
+  //   NN B:    [32 k rows][256 n], 512-byte rows, chunk c of row r at c ^ ((r & 3) << 2)
+  int voa[2], vob[2], csa[2], krb[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = wave * 32 + q * 8 + (lane >> 3);
-    const int cs = (lane & 7) ^ ((r >> 1) & 7);
+  for (int q = 0; q < 2; ++q) {
+    const int r = (wave * 2 + q) * 16 + (lane >> 2);
+    const int cs = (lane & 3) ^ ((r >> 2) & 3);
+    csa[q] = cs;
     voa[q] = (int)(((int64_t)r * lda + cs * 8) * 2);
     if constexpr (!NN) {
       vob[q] = (int)(((int64_t)r * ldb + cs * 8) * 2);
     } else {
-      const int kr = wave * 8 + q * 2 + (lane >> 5);
-      const int cn = (lane & 31) ^ (kr & 7);
+      const int kr = (wave * 2 + q) * 2 + (lane >> 5);
+      const int cn = (lane & 31) ^ ((kr & 3) << 2);
+      krb[q] = kr;
       vob[q] = (int)(((int64_t)kr * ldb + cn * 8) * 2);
     }
   }
-  // On a partial last K step the A (and NT B) lanes whose chunk lies at or
-  // past K load nothing: with a strided operand those columns can run past
-  // the end of the allocation on its last row (the buffer range covers whole
-  // rows).  zero_tail fills their slots.
-  auto dload = [&](int k0, uint16_t* as_, uint16_t* bs_) {
-    const int kv = K - k0;
-    if (kv >= GBK) {
+  // k ranges of the stages: stage 0 takes the first r0 = K - 32 (nk - 1)
+  // values of k (1..32), stage i >= 1 the 32 from r0 + 32 (i - 1); so only
+  // stage 0 can be partial, and it is loaded before the loop.  Its lanes whose
+  // source lies at or past r0 load nothing (a strided operand could run past
+  // the end of its allocation there) and zero their slot instead.
+  const int nk = (K + 31) / 32;
+  const int r0 = K - 32 * (nk - 1);
+  auto dload = [&](int k0, uint16_t* st) {
+    uint16_t* as_ = st;
+    uint16_t* bs_ = st + 256 * 32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        b2l16(ra, voa[q], k0 * 2, as_ + (wave * 32 + q * 8) * GBK);
-        if constexpr (!NN) b2l16(rb, vob[q], k0 * 2, bs_ + (wave * 32 + q * 8) * GBK);
-        else b2l16(rb, vob[q], (int)((int64_t)k0 * ldb * 2), bs_ + (wave * 8 + q * 2) * GBN);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = wave * 32 + q * 8 + (lane >> 3);
-        if (((lane & 7) ^ ((r >> 1) & 7)) * 8 < kv) {
-          b2l16(ra, voa[q], k0 * 2, as_ + (wave * 32 + q * 8) * GBK);
-          if constexpr (!NN) b2l16(rb, vob[q], k0 * 2, bs_ + (wave * 32 + q * 8) * GBK);
-        }
-        if constexpr (NN) b2l16(rb, vob[q], (int)((int64_t)k0 * ldb * 2), bs_ + (wave * 8 + q * 2) * GBN);
-      }
+    for (int q = 0; q < 2; ++q) {
+      b2l16(ra, voa[q], k0 * 2, as_ + (wave * 2 + q) * 512);
+      if constexpr (!NN) b2l16(rb, vob[q], k0 * 2, bs_ + (wave * 2 + q) * 512);
+      else b2l16(rb, vob[q] + (int)((int64_t)k0 * ldb * 2), 0, bs_ + (wave * 2 + q) * 512);
     }
   };
-  // partial last K step: the loads above also fetch columns (A, NT B) or
-  // rows (NN B) past K.  Each lane zeroes the LDS slots its own loads filled,
-  // after its wave's loads have landed (slots of other waves' loads may
-  // still be in flight).
-  auto zero_tail = [&](int k0, uint16_t* as_, uint16_t* bs_) {
-    const int kv = K - k0;                  // valid k in this step (multiple of 8)
-    if (kv >= GBK) return;
+  auto dload_first = [&](uint16_t* st) {
+    uint16_t* as_ = st;
+    uint16_t* bs_ = st + 256 * 32;
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = wave * 32 + q * 8 + (lane >> 3);
-      const int cs = (lane & 7) ^ ((r >> 1) & 7);     // the source chunk this lane loaded
-      if (cs * 8 >= kv) {
-        *reinterpret_cast<uint4*>(as_ + (wave * 32 + q * 8) * GBK + lane * 8) = z;
-        if constexpr (!NN) *reinterpret_cast<uint4*>(bs_ + (wave * 32 + q * 8) * GBK + lane * 8) = z;
-      }
-      if constexpr (NN) {
-        const int kr = wave * 8 + q * 2 + (lane >> 5);
-        if (kr >= kv) *reinterpret_cast<uint4*>(bs_ + (wave * 8 + q * 2) * GBN + lane * 8) = z;
+    for (int q = 0; q < 2; ++q) {
+      if (csa[q] * 8 < r0) b2l16(ra, voa[q], 0, as_ + (wave * 2 + q) * 512);
+      else *reinterpret_cast<uint4*>(as_ + (wave * 2 + q) * 512 + lane * 8) = z;
+      if constexpr (!NN) {
+        if (csa[q] * 8 < r0) b2l16(rb, vob[q], 0, bs_ + (wave * 2 + q) * 512);
+        else *reinterpret_cast<uint4*>(bs_ + (wave * 2 + q) * 512 + lane * 8) = z;
+      } else {
+        if (krb[q] < r0) b2l16(rb, vob[q], 0, bs_ + (wave * 2 + q) * 512);
+        else *reinterpret_cast<uint4*>(bs_ + (wave * 2 + q) * 512 + lane * 8) = z;
       }
     }
   };
-  auto compute = [&](const uint16_t* as, const uint16_t* bs) {
-    // recompute the fragment addresses here rather than keep two hoisted sets
-    // (one per buffer) alive across the loop
+  auto compute = [&](const uint16_t* st) {
+    const uint16_t* as = st;
+    const uint16_t* bs = st + 256 * 32;
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
-    // fragments of k sub-step s (16 wide) for this wave's 128 x 64 output
     auto frag = [&](int s, bf16x8* af, bf16x8* bfr) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wm * 128 + i * 32 + (lane & 31);
         const int ch = 2 * s + (lane >> 5);
-        af[i] = *reinterpret_cast<const bf16x8*>(&as[row * GBK + ((ch ^ ((row >> 1) & 7)) << 3)]);
+        af[i] = *reinterpret_cast<const bf16x8*>(&as[row * 32 + ((ch ^ ((row >> 2) & 3)) << 3)]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if constexpr (!NN) {
           const int row = wn * 64 + j * 32 + (lane & 31);
           const int ch = 2 * s + (lane >> 5);
-          bfr[j] = *reinterpret_cast<const bf16x8*>(&bs[row * GBK + ((ch ^ ((row >> 1) & 7)) << 3)]);
+          bfr[j] = *reinterpret_cast<const bf16x8*>(&bs[row * 32 + ((ch ^ ((row >> 2) & 3)) << 3)]);
         } else {
           const int gq = lane >> 4, q = lane & 15;
           const int ncol = wn * 64 + j * 32 + 16 * (gq & 1) + 4 * (q & 3);
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int kr = 16 * s + 8 * (gq >> 1) + 4 * hh + (q >> 2);
-            h[hh] = ds_read_tr16(&bs[kr * GBN + ((chn ^ (kr & 7)) << 3) + within]);
+            h[hh] = ds_read_tr16(&bs[kr * 256 + ((chn ^ ((kr & 3) << 2)) << 3) + within]);
           }
           typedef short i16x8 __attribute__((ext_vector_type(8)));
           i16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
@@ -191,41 +193,72 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
         }
       }
     };
-    // fragments of sub-step s + 1 load while the products of sub-step s run
     bf16x8 af[2][4], bfr[2][2];
     frag(0, af[0], bfr[0]);
+    frag(1, af[1], bfr[1]);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) frag(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(bfr[s & 1][j], af[s & 1][i], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(bfr[s][j], af[s][i], acc[i][j]);
     }
   };
 
-  // double buffer, unrolled by two so each step names its buffers
-  // statically; pairs of steps in the loop (one back edge, no early exit),
-  // an odd last step after it
-  const int nk = (K + GBK - 1) / GBK;
-  dload(0, As0, Bs0);
-  vm_wait();
-  zero_tail(0, As0, Bs0);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    dload((kt + 1) * GBK, As1, Bs1);
-    compute(As0, Bs0);
-    vm_wait();
-    zero_tail((kt + 1) * GBK, As1, Bs1);
-    __syncthreads();
-    if (kt + 2 < nk) dload((kt + 2) * GBK, As0, Bs0);
-    compute(As1, Bs1);
-    vm_wait();
-    if (kt + 2 < nk) zero_tail((kt + 2) * GBK, As0, Bs0);
-    __syncthreads();
+  // The ring, unrolled by S so that each step names its stages statically.
+  // Per lane a full step issues 4 loads, so before step i the loads of steps
+  // i+1 .. i+S-2 (issued earlier) may stay in flight.  With nk >= S - 1 (the
+  // launcher picks SMALL otherwise) the prologue fills stages 0 .. S-2
+  // unconditionally, so every wait in the steady loop below is one constant.
+  dload_first(S0);
+  asm volatile("" ::: "memory");
+  if (!SMALL || 1 < nk) dload(r0, S1);
+  asm volatile("" ::: "memory");
+  if (!SMALL || 2 < nk) dload(r0 + 32, S2);
+  asm volatile("" ::: "memory");
+  // steady step: wait for this lane's loads of step I (the 4 (S - 2) loads
+  // issued after them may stay in flight), barrier, refill the stage that
+  // step I - 1 read, compute
+#define G4STEADY(I, CUR, NEXT)                                                       \
+  {                                                                                  \
+    asm volatile("" ::: "memory");                                                   \
+    __builtin_amdgcn_s_waitcnt(vm_imm(4 * (S - 2)));                                   \
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                               \
+    __builtin_amdgcn_s_barrier();                                                    \
+    asm volatile("" ::: "memory");                                                   \
+    dload(r0 + ((I) + S - 2) * 32, NEXT);                                            \
+    compute(CUR);                                                                    \
   }
-  if (kt < nk) compute(As0, Bs0);
+  // drain step: as above while loads remain, else wait for all
+#define G4STEP(I, CUR, NEXT)                                                         \
+  {                                                                                  \
+    const int i_ = (I);                                                              \
+    asm volatile("" ::: "memory");                                                   \
+    if (i_ + S - 1 < nk) __builtin_amdgcn_s_waitcnt(vm_imm(4 * (S - 2)));             \
+    else __builtin_amdgcn_s_waitcnt(vm_imm(0));                                        \
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                               \
+    __builtin_amdgcn_s_barrier();                                                    \
+    asm volatile("" ::: "memory");                                                   \
+    if (i_ + S - 1 < nk) dload(r0 + (i_ + S - 2) * 32, NEXT);                        \
+    compute(CUR);                                                                    \
+  }
+  // whole rounds in which every step refills a stage (one back edge, no early
+  // exit: an exit in the middle makes the compiler copy the accumulators),
+  // then the remaining S - 1 .. 2 S - 2 steps
+  int kt = 0;
+  if constexpr (!SMALL) {
+    for (; kt + 2 * S - 2 < nk; kt += S) {
+      G4STEADY(kt, S0, S3) G4STEADY(kt + 1, S1, S0) G4STEADY(kt + 2, S2, S1) G4STEADY(kt + 3, S3, S2)
+    }
+  }
+  if (kt < nk) G4STEP(kt, S0, S3)
+  if (kt + 1 < nk) G4STEP(kt + 1, S1, S0)
+  if (kt + 2 < nk) G4STEP(kt + 2, S2, S1)
+  if (kt + 3 < nk) G4STEP(kt + 3, S3, S2)
+  if (kt + 4 < nk) G4STEP(kt + 4, S0, S3)
+  if (kt + 5 < nk) G4STEP(kt + 5, S1, S0)
+#undef G4STEADY
+#undef G4STEP
 
   // epilogue.  The products run with the operands swapped, so acc[i][j]
   // holds the transposed 32 x 32 sub-tile: register r of lane l is
@@ -235,7 +268,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
     // fp32: the same staging in two rounds of 64 rows (16 KiB per wave and
     // round): 16-byte writes into 256-byte rows, chunk c at c ^ (row & 15),
     // then 16-byte row-order stores (4 rows of 256 bytes per instruction)
-    uint32_t* st = reinterpret_cast<uint32_t*>((wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? Bs0 : Bs1) +
+    uint32_t* st = reinterpret_cast<uint32_t*>((wave < 2 ? S0 : wave < 4 ? S1 : wave < 6 ? S2 : S3) +
                                                (wave & 1) * (128 * 64));
     const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(Cf) & 15) == 0;
 #pragma unroll
@@ -281,7 +314,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
     // one write touch each bank pair once); then whole rows leave as 16-byte
     // stores, 8 rows of 128 bytes per wave instruction.
     __syncthreads();
-    uint16_t* st = (wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? Bs0 : Bs1) + (wave & 1) * (128 * 64);
+    uint16_t* st = (wave < 2 ? S0 : wave < 4 ? S1 : wave < 6 ? S2 : S3) + (wave & 1) * (128 * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = i * 32 + (lane & 31);
@@ -321,6 +354,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
   }
 }
 
+
 // Generic bf16 GEMM for shapes the tiled kernel cannot take (a dimension,
 // stride or offset not a multiple of 8): 16x16 outputs per workgroup, LDS
 // tiles, fp32 sums.
@@ -359,9 +393,16 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     const int tn = (g.N + GBN - 1) / GBN, tm = (g.M + GBM - 1) / GBM;
     const int nt = tn * tm * g.batch;
     const int grid = ((nt + 7) / 8) * 8;
-    if (nn) hipLaunchKernelGGL((gemm_bf16_kernel<true, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
-    else if (g.batch > 1) hipLaunchKernelGGL((gemm_bf16_kernel<false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
-    else hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    const bool small = (g.K + 31) / 32 < GST - 1;
+#define GEMM_LAUNCH(NN_, BT_)                                                                                  \
+  {                                                                                                           \
+    if (small) hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
+    else hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, false, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
+  }
+    if (nn) GEMM_LAUNCH(true, false)
+    else if (g.batch > 1) GEMM_LAUNCH(false, true)
+    else GEMM_LAUNCH(false, false)
+#undef GEMM_LAUNCH
   } else {
     dim3 grid((unsigned)((g.N + 15) / 16), (unsigned)((g.M + 15) / 16), (unsigned)g.batch);
     if (nn) hipLaunchKernelGGL(gemm_bf16_generic_kernel<true>, grid, dim3(256), 0, s, g);
@@ -374,7 +415,8 @@ void launch_gemm_bf16_f32out(const GemmArgs& g, hipStream_t s) {
   const int tn = (g.N + GBN - 1) / GBN, tm = (g.M + GBM - 1) / GBM;
   const int nt = tn * tm * g.batch;
   const int grid = ((nt + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_bf16_kernel<true, true, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+  if ((g.K + 31) / 32 < GST - 1) hipLaunchKernelGGL((gemm_bf16_kernel<true, true, true, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+  else hipLaunchKernelGGL((gemm_bf16_kernel<true, true, true, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
 }
 
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N, int64_t K,
