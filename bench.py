@@ -48,6 +48,7 @@ KERNEL_CLASSES = [
     ("skew_project_kernel", "chain_rule", 5),
     ("gj_kernel", "cayley_build", 1),
     ("gram_bf16_kernel", "gram", 2),
+    ("gram_stream_kernel", "gram", 2),
     ("gram_reduce_kernel", "gram", 2),
 ]
 CALIBRATION_BYTES = 256 << 20   # the copy kernel reads and writes this many bytes each
