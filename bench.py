@@ -39,6 +39,7 @@ MFMA_CLASSES = {"gemm_nt": 2500.0, "gemm_nn": 2500.0, "cayley_build": 157.3, "ch
 KERNEL_CLASSES = [
     ("permute_gather_kernel", "xform_permute", 1),
     ("permute_scatter_kernel", "xform_permute", 1),
+    ("permute_stream_kernel", "xform_permute", 1),
     ("blockdiag_kernel", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, true, false,", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, false, false,", "gemm_nt", 1),

@@ -136,8 +136,193 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(PermArgs 
 
 static bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// ---------------------------------------------------------------------------
+// Streaming permutation.  One workgroup owns a run of token rows; groups of
+// PS_R = 8192 / W rows stream through a ring of PS_S LDS stages with
+// buffer-to-LDS loads (PS_S - 1 groups in flight), and every output chunk of 8
+// columns is gathered from the staged rows through a uint16 index table in
+// LDS (the permutation for a gather, its inverse for a scatter) and leaves as
+// one 16-byte buffer store.  Reads of one group overlap the writes of the
+// previous ones, which the load-everything-then-store kernel above cannot
+// do.  Per lane every iteration issues exactly two loads and NS stores (idle
+// slots use offsets past the buffer range: the loads read nothing and the
+// stores write nothing), in an order that compiler barriers fix, so the wait
+// for a group is one constant from the PS_S-th iteration on and a smaller one
+// before.
+// ---------------------------------------------------------------------------
+constexpr int PS_S = 6;          // ring stages
+constexpr int PS_E = 8192;       // elements per stage (16 KiB)
+constexpr int PS_THREADS = 512;
+constexpr int PS_OOB = 0x7ffffff0;   // a buffer offset past every range
+
+typedef unsigned ps_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ps_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void ps_b2l16(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
+}
+constexpr unsigned ps_vm_imm(unsigned vm) { return (vm & 15u) | ((vm >> 4) << 14) | (7u << 4) | (15u << 8); }
+__device__ __forceinline__ uint32_t ps_lds_addr(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+
+// LDS reads of the loop as inline asm: the compiler's wait insertion cannot
+// tell which ring stage an asynchronous fill targets and would wait for
+// nearly all of them before every read; the explicit vmcnt wait and the
+// barriers order these instead.  Each block waits for its own results, and
+// its outputs are early-clobber (no in-flight read can land in a register a
+// later address of the block still needs).
+__device__ __forceinline__ void ps_read_idx(uint4& v, uint32_t a) {
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+}
+__device__ __forceinline__ void ps_read8(uint32_t (&x)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_u16 %0, %8\n\tds_read_u16 %1, %9\n\tds_read_u16 %2, %10\n\tds_read_u16 %3, %11\n\t"
+      "ds_read_u16 %4, %12\n\tds_read_u16 %5, %13\n\tds_read_u16 %6, %14\n\tds_read_u16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+// SCATTER: out[t][perm[j]] = in[t][j] (no separate tail source);
+// else out[t][j] = in[t][perm[j]], and TAILOUT also writes tail_out[t][j] for j >= tail0
+template <bool SCATTER, bool TAILOUT>
+__global__ __launch_bounds__(PS_THREADS) void permute_stream_kernel(PermArgs a, int spr) {
+  __shared__ __align__(16) uint16_t P0[PS_E], P1[PS_E], P2[PS_E], P3[PS_E], P4[PS_E], P5[PS_E];
+  __shared__ __align__(16) uint16_t IDX[PS_E];
+  static_assert(PS_S == 6, "the ring is spelled out for six stages");
+  constexpr int NS = TAILOUT ? 4 : 2;                       // stores per lane and iteration
+  const int W = a.W, R = PS_E / W, cpr = W >> 3;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = (int64_t)blockIdx.x * spr * R;
+  if (t0 >= a.N) return;
+  const int rows = (int)min((int64_t)spr * R, a.N - t0);
+  const int nt = (rows + R - 1) / R;                         // row groups of this run
+  const uint32_t gbytes = (uint32_t)R * W * 2;               // bytes of one group
+
+  // loads: slot h * 512 + tid of a stage = element 8 (h * 512 + tid), row / column of the
+  // group; instruction h of wave w fills the KiB at element h * 4096 + w * 512
+  const __amdgpu_buffer_rsrc_t rin = ps_rsrc(a.in + t0 * W, (uint32_t)rows * W * 2);
+  int lo[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = (h * PS_THREADS + tid) * 8;
+    lo[h] = e < R * W ? e * 2 : -1;
+  }
+  auto load_group = [&](int i, uint16_t* st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ps_b2l16(rin, lo[h] >= 0 ? lo[h] + (int)((uint32_t)i * gbytes) : PS_OOB, st + h * PS_THREADS * 8 + wave * 512);
+  };
+  // the first S - 1 groups, in issue order, while the index table is built
+  load_group(0, P0);
+  asm volatile("" ::: "memory");
+  load_group(1, P1);
+  asm volatile("" ::: "memory");
+  load_group(2, P2);
+  asm volatile("" ::: "memory");
+  load_group(3, P3);
+  asm volatile("" ::: "memory");
+  load_group(4, P4);
+  asm volatile("" ::: "memory");
+  for (int j = tid; j < W; j += PS_THREADS) {
+    const int p = a.perm[j];
+    if (SCATTER) IDX[p] = (uint16_t)j;
+    else IDX[j] = (uint16_t)p;
+  }
+
+  // stores: items m * 512 + tid of a group = (row, 8-column chunk)
+  const __amdgpu_buffer_rsrc_t rout = ps_rsrc(a.out + t0 * W, (uint32_t)rows * W * 2);
+  const __amdgpu_buffer_rsrc_t rtail = ps_rsrc(TAILOUT ? a.tail_out + t0 * W : a.out, TAILOUT ? (uint32_t)rows * W * 2 : 0u);
+  int so[2], ro[2], io[2];
+  bool tl[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int item = m * PS_THREADS + tid;
+    const int r = item / cpr, c = item - r * cpr;
+    const bool ok = r < R;
+    so[m] = ok ? (r * W + c * 8) * 2 : -1;
+    ro[m] = r * W * 2;                        // byte offset of the item's row in a stage
+    io[m] = c * 16;                           // byte offset of its 8 indices
+    tl[m] = ok && c * 8 >= a.tail0;
+  }
+  const uint32_t ibase = ps_lds_addr(IDX);
+
+  auto step = [&](int i, const uint16_t* st, uint16_t* next) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();   // all parts of group i landed; the stage of group i - 1 is free
+    asm volatile("" ::: "memory");
+    load_group(i + PS_S - 1, next);
+    const uint32_t sb = ps_lds_addr(st);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      ps_u32x4 v = {0u, 0u, 0u, 0u};
+      if (so[m] >= 0) {
+        uint4 ix;
+        ps_read_idx(ix, ibase + (uint32_t)io[m]);
+        const uint32_t rb = sb + (uint32_t)ro[m];
+        const uint32_t ad[8] = {rb + 2 * (ix.x & 0xffff), rb + 2 * (ix.x >> 16), rb + 2 * (ix.y & 0xffff), rb + 2 * (ix.y >> 16),
+                                rb + 2 * (ix.z & 0xffff), rb + 2 * (ix.z >> 16), rb + 2 * (ix.w & 0xffff), rb + 2 * (ix.w >> 16)};
+        uint32_t x[8];
+        ps_read8(x, ad);
+        v = ps_u32x4{x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16), x[6] | (x[7] << 16)};
+      }
+      const int off = so[m] >= 0 ? so[m] + (int)((uint32_t)i * gbytes) : PS_OOB;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rout, off, 0, 0);
+      if constexpr (TAILOUT) __builtin_amdgcn_raw_buffer_store_b128(v, rtail, tl[m] ? off : PS_OOB, 0, 0);
+    }
+  };
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // index table written
+
+#define PS_WAIT(s)                                                                           \
+  asm volatile("" ::: "memory");                                                             \
+  if (i == 0) __builtin_amdgcn_s_waitcnt(ps_vm_imm(2 * (PS_S - 2) + (s) * NS));              \
+  else __builtin_amdgcn_s_waitcnt(ps_vm_imm(2 * (PS_S - 2) + (PS_S - 1) * NS));
+  for (int i = 0; i < nt; i += PS_S) {
+    PS_WAIT(0) step(i, P0, P5);
+    if (i + 1 >= nt) break;
+    PS_WAIT(1) step(i + 1, P1, P0);
+    if (i + 2 >= nt) break;
+    PS_WAIT(2) step(i + 2, P2, P1);
+    if (i + 3 >= nt) break;
+    PS_WAIT(3) step(i + 3, P3, P2);
+    if (i + 4 >= nt) break;
+    PS_WAIT(4) step(i + 4, P4, P3);
+    if (i + 5 >= nt) break;
+    PS_WAIT(5) step(i + 5, P5, P4);
+  }
+#undef PS_WAIT
+  // fills past the end of the run may still be writing this workgroup's LDS
+  __builtin_amdgcn_s_waitcnt(ps_vm_imm(0));
+}
+
+// true if the streaming kernel took the permutation.  It takes rows of 4096
+// to 8192 columns: measured on 8192 x 2048 and 8192 x 5632 bf16 matrices, it
+// beats the staging kernel at 5632 (5.7 vs 5.3 TB/s) and loses at 2048
+// (4.9 vs 5.4-5.8 TB/s), where a run of 32 rows is only 8 ring iterations.
+static bool launch_permute_stream(bool gather, const PermArgs& a, hipStream_t s) {
+  const int W = a.W;
+  if (W < 4096 || W > PS_E || (W & 7)) return false;
+  if (!a16(a.in) || !a16(a.out) || (a.tail_out && !a16(a.tail_out))) return false;
+  const bool tail = a.tail0 < W;
+  if (!gather && tail && a.tail_in && a.tail_in != a.in) return false;   // separate tail source: not streamed
+  const int R = PS_E / W;
+  const int64_t groups = (a.N + R - 1) / R;
+  int64_t runs = groups < 256 ? groups : 256;
+  int64_t spr = (groups + runs - 1) / runs;
+  if ((spr + PS_S) * (int64_t)R * W * 2 >= 0x7fffffffLL) return false;
+  runs = (groups + spr - 1) / spr;
+  const dim3 grid((unsigned)runs);
+  if (!gather) hipLaunchKernelGGL((permute_stream_kernel<true, false>), grid, dim3(PS_THREADS), 0, s, a, (int)spr);
+  else if (tail && a.tail_out) hipLaunchKernelGGL((permute_stream_kernel<false, true>), grid, dim3(PS_THREADS), 0, s, a, (int)spr);
+  else hipLaunchKernelGGL((permute_stream_kernel<false, false>), grid, dim3(PS_THREADS), 0, s, a, (int)spr);
+  return true;
+}
+
 void launch_permute_bf16(bool gather, const PermArgs& a, hipStream_t s) {
   if (a.N <= 0 || a.W <= 0) return;
+  if (launch_permute_stream(gather, a, s)) return;
   const int R = perm_rows(a.W);
   const dim3 grid((unsigned)((a.N + R - 1) / R));
   const size_t lds = (size_t)R * a.W * sizeof(uint16_t);

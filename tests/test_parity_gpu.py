@@ -77,6 +77,7 @@ SMALL = [
     (70, 90, 32, 1),
     (20, 40, 32, 5),       # m < b: R is the identity
     (512, 256, 256, 129),
+    (4360, 4104, 256, 45),  # rows of 4096+ columns with identity tails (streaming permutation)
 ]
 
 
