@@ -85,6 +85,9 @@ def parse():
                          "24-layer stack with Adam and the global merge")
     ap.add_argument("--streams", type=int, default=3,
                     help="HIP streams the seven independent matrices are spread over (batched mode)")
+    ap.add_argument("--chain", choices=["batched", "per-matrix"], default="batched",
+                    help="layer set: one chain-rule call for all matrices after the backward pass, or one per "
+                         "matrix on its stream")
     ap.add_argument("--per-layer-builds", action="store_true",
                     help="let every forward / backward call build its own blocks (one builder launch per call) "
                          "instead of one batched build per pass")
@@ -503,8 +506,9 @@ def main():
         # blocks of all seven matrices in one build per pass; the backward pass
         # rebuilds them from the generators instead of keeping the forward's
         # (on a second stream, concurrently with the forward pass: the build
-        # needs only the generators), and runs the chain rule once for all
-        # seven after their dL/dQ
+        # needs only the generators); the chain rule runs once for all seven
+        # after their dL/dQ (--chain batched) or per matrix on its stream
+        # right after its dL/dQ (--chain per-matrix)
         bs = active["side"]
         bs.wait_stream(stream)
         with torch.cuda.stream(bs):
@@ -513,9 +517,13 @@ def main():
         P.build_layer_blocks(layers, "forward")
         fan_out(list(zip(layers, outs)), lambda lay, o: lay.forward_blocks(Xs[lay.x_key], Y=o["Y"]))
         stream.wait_event(bwd_blocks_ready)
-        fan_out(list(zip(reversed(layers), reversed(gYs), reversed(outs))),
-                lambda lay, g, o: lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"]))
-        P.chain_rule_layers(layers, [(o["dR"], o["dP"]) for o in outs])
+        def bwd(lay, g, o):
+            lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"])
+            if args.chain == "per-matrix":
+                P.chain_rule_layers([lay], [(o["dR"], o["dP"])])
+        fan_out(list(zip(reversed(layers), reversed(gYs), reversed(outs))), bwd)
+        if args.chain == "batched":
+            P.chain_rule_layers(layers, [(o["dR"], o["dP"]) for o in outs])
 
     step = step_per_layer if args.per_layer_builds else step_batched
 

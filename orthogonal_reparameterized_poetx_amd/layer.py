@@ -204,8 +204,11 @@ def chain_rule_layers(layers, grads, accumulate=False, stream=None):
     for b, sets in by_b.items():
         dev = layers[0].device
         need = L.chain_workspace_bytes(sum(s[2] for s in sets), b)
-        ws = _chain_ws.get((dev, b))
+        # one workspace per stream: chain rules of different layers may run
+        # concurrently on different streams
+        sid = stream.cuda_stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        ws = _chain_ws.get((dev, b, sid))
         if need and (ws is None or ws.numel() < need):
             ws = L.make_workspace(need, dev)
-            _chain_ws[(dev, b)] = ws
+            _chain_ws[(dev, b, sid)] = ws
         L.poetx_chain_rule_sets(sets, b, accumulate, ws if need else None, stream)
