@@ -44,14 +44,16 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
   constexpr int TR = S::TR, TC = S::TC, NT = S::NT, WPC = S::WPC;
   constexpr bool X6 = MODE == 6;
   constexpr int PC = 33;       // fp32 column-panel pitch (32 + 1)
-  constexpr int PR = B + 1;    // fp32 row-panel pitch
+  constexpr int PR = B + 4;    // fp32 row-panel pitch (16-byte rows for vector reads)
+  constexpr int PT = 36;       // pitch of the transposed diagonal inverse
   constexpr int HP = 40;       // bf16 operand pitch (32 + 8): conflict-free b128 reads
   __shared__ float Pcol[X6 ? 1 : B * PC];     // old column panel A[:, K] (fp32 mode)
-  __shared__ float Prow[32 * PR];             // old row panel A[K, :], then the new one
-  __shared__ float Dm[32 * PC];               // diagonal block -> its inverse
-  __shared__ float colb[32];                  // column broadcast of the diagonal-block pivots
-  __shared__ bf16 OpA[X6 ? 3 * B * HP : 2];   // -A[:, K] split h|m|l, [i][kk]
+  __shared__ __align__(16) float Prow[32 * PR];   // old row panel A[K, :], then the new one
+  __shared__ __align__(16) float DmT[32 * PT];    // inverse of the diagonal block, transposed
+  __shared__ __align__(16) bf16 OpA[X6 ? 3 * B * HP : 2];   // -A[:, K] split h|m|l, [i][kk]
   __shared__ bf16 OpB[X6 ? 3 * B * HP : 2];   // new A[K, :]^T split h|m|l, [j][kk]
+  static_assert(!(X6 && B == 256) || 3 * B * HP * sizeof(bf16) >= S::NW * 32 * 33 * sizeof(float),
+                "the transposition scratch fits in OpA");
 
   int seg = 0;
   while (seg + 1 < g.nseg && (int)blockIdx.x >= g.start[seg + 1]) ++seg;
@@ -72,26 +74,65 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
   };
 
   f32x16 acc[TR][TC];
-  // ---- load A = I - S (theta mode) or A from a strided matrix
+  if (sg.theta && X6 && B == 256) {
+    // ---- A = I - S from the stored strict upper triangle with row-contiguous
+    // reads: tiles on or above the diagonal read their rows of the triangle
+    // (A = -theta above the diagonal); a tile below it reads its mirror tile
+    // (rows J0.., columns I0..) the same way and transposes it through this
+    // wave's LDS scratch (A[i][j] = theta(j, i)).  The diagonal tiles read
+    // their lower halves directly.
+    const float* th = sg.theta + (int64_t)blk * (B * (B - 1) / 2);
+    auto tri = [&](int i, int j) { return th[i * B - i * (i + 1) / 2 + (j - i - 1)]; };   // theta(i, j), i < j
+    float* scr = reinterpret_cast<float*>(OpA) + wave * (32 * 33);
 #pragma unroll
-  for (int ti = 0; ti < TR; ++ti)
+    for (int ti = 0; ti < TR; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < TC; ++tj)
+      for (int tj = 0; tj < TC; ++tj) {
+        const int I0 = tr + 32 * ti, J0 = tc + 32 * tj;
+        if (J0 > I0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = tr + 32 * ti + c32_row(lane, r);
-        const int j = tc + 32 * tj + lc;
-        float v;
-        if (sg.theta) {
-          const float* th = sg.theta + (int64_t)blk * (B * (B - 1) / 2);
-          if (i == j) v = 1.0f;
-          else if (i < j) v = -th[i * B - i * (i + 1) / 2 + (j - i - 1)];
-          else v = th[j * B - j * (j + 1) / 2 + (i - j - 1)];
+          for (int r = 0; r < 16; ++r) acc[ti][tj][r] = -tri(I0 + c32_row(lane, r), J0 + lc);
+        } else if (J0 == I0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = I0 + c32_row(lane, r), j = J0 + lc;
+            acc[ti][tj][r] = i == j ? 1.0f : (i < j ? -tri(i, j) : tri(j, i));
+          }
         } else {
-          v = g.in[(int64_t)blk * g.in_stride + (int64_t)i * g.in_ld + j];
+          float m[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m[r] = tri(J0 + c32_row(lane, r), I0 + lc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) scr[c32_row(lane, r) * 33 + lc] = m[r];
+          lds_wave_fence();
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[ti][tj][r] = scr[lc * 33 + c32_row(lane, r)];
+          lds_wave_fence();
         }
-        acc[ti][tj][r] = v;
       }
+    __syncthreads();
+  } else {
+    // ---- A = I - S (theta mode) or A from a strided matrix, element by element
+#pragma unroll
+    for (int ti = 0; ti < TR; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < TC; ++tj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = tr + 32 * ti + c32_row(lane, r);
+          const int j = tc + 32 * tj + lc;
+          float v;
+          if (sg.theta) {
+            const float* th = sg.theta + (int64_t)blk * (B * (B - 1) / 2);
+            if (i == j) v = 1.0f;
+            else if (i < j) v = -th[i * B - i * (i + 1) / 2 + (j - i - 1)];
+            else v = th[j * B - j * (j + 1) / 2 + (i - j - 1)];
+          } else {
+            v = g.in[(int64_t)blk * g.in_stride + (int64_t)i * g.in_ld + j];
+          }
+          acc[ti][tj][r] = v;
+        }
+  }
 
   for (int p = 0; p < B / 32; ++p) {
     const int K0 = 32 * p;
@@ -123,36 +164,31 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
         }
       }
     __syncthreads();
-    // ---- (b) invert the diagonal 32x32 block: wave 0, one column per lane
-    // (lane j + 32h holds rows 16h..16h+15 of column j), column k broadcast
-    // through LDS, row k by a cross-lane read.  No workgroup barrier inside.
+    // ---- (b) invert the diagonal 32x32 block: wave 0, lane j (and j + 32,
+    // which repeats it) holds column j in registers; pivot column k is
+    // broadcast with scalar lane reads, the pivot row is each lane's own
+    // element.  No LDS traffic and no barrier inside.
     if (wave == 0) {
-      const int j = lane & 31, h = lane >> 5;
-      float d[16];
+      const int j = lane & 31;
+      float d[32];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) d[r] = Prow[(16 * h + r) * PR + K0 + j];
+      for (int r = 0; r < 32; ++r) d[r] = Prow[r * PR + K0 + j];
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
-        if (j == k) {
+        float col[32];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) colb[16 * h + r] = d[r];
-        }
-        lds_wave_fence();
-        float col[16];
+        for (int r = 0; r < 32; ++r)
+          col[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d[r]), k));
+        const float pinv = 1.0f / col[k];
+        const float nrow = (j == k) ? pinv : d[k] * pinv;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) col[r] = colb[16 * h + r];
-        const float pinv = 1.0f / colb[k];
-        const float rk = __shfl(d[k & 15], j + 32 * (k >> 4));
-        const float nrow = (j == k) ? pinv : rk * pinv;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 16 * h + r;
-          d[r] = (i == k) ? nrow : ((j == k) ? -col[r] * pinv : d[r] - col[r] * nrow);
-        }
-        lds_wave_fence();
+        for (int r = 0; r < 32; ++r) d[r] = (r == k) ? nrow : ((j == k) ? -col[r] * pinv : d[r] - col[r] * nrow);
       }
+      if (lane < 32) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Dm[(16 * h + r) * PC + j] = d[r];
+        for (int r = 0; r < 32; r += 4)
+          *reinterpret_cast<float4*>(&DmT[j * PT + r]) = make_float4(d[r], d[r + 1], d[r + 2], d[r + 3]);
+      }
     }
     __syncthreads();
     // ---- (c) new row panel: A[K, j] <- Dinv A[K, j] (j outside K), A[K, K] <- Dinv.
@@ -171,10 +207,17 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
 #pragma unroll 4
         for (int t = 0; t < 32; ++t) {
           float dv[RB], pv[CB];
+          if constexpr (RB == 4) {
+            const float4 v = *reinterpret_cast<const float4*>(&DmT[t * PT + rg * RB]);
+            dv[0] = v.x; dv[1] = v.y; dv[2] = v.z; dv[3] = v.w;
+          } else {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) dv[rb] = Dm[(rg * RB + rb) * PC + t];
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) pv[cb] = Prow[t * PR + cg * CB + cb];
+            for (int rb = 0; rb < RB; ++rb) dv[rb] = DmT[t * PT + rg * RB + rb];
+          }
+          {
+            const float4 v = *reinterpret_cast<const float4*>(&Prow[t * PR + cg * CB]);
+            pv[0] = v.x; pv[1] = v.y; pv[2] = v.z; pv[3] = v.w;
+          }
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -184,7 +227,7 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) nv[rb][cb] = Dm[(rg * RB + rb) * PC + cg * CB + cb - K0];
+          for (int cb = 0; cb < CB; ++cb) nv[rb][cb] = DmT[(cg * CB + cb - K0) * PT + rg * RB + rb];
       }
       __syncthreads();
 #pragma unroll
