@@ -645,9 +645,61 @@ int check_blocks(const Shape& S, const poetx_blocks* q, bool backward) {
 
 // merge after the blocks exist: tile products, new permutations, relayout,
 // generator reset (a10, a11)
+// bf16 merge on the streaming kernels, where they apply (b <= 256, rows of a
+// multiple of 8 columns up to 32768, 16-byte aligned operands):
+//   W0p <- W0p D_P        block product in place (columns from kP b on: identity)
+//   V[I] <- Q_R,I W0p[I]  batched NN GEMM over the kR row blocks; tail rows copied
+//   W0p[i][j] <- V[sinv(snew(i))][tinv(tnew(j))]   staged row gather
+// One bf16 rounding after each product, as in the tile kernel.
+bool merge_fast_bf16(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
+                     uint64_t perm_seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
+  const int64_t m = S.m, n = S.n;
+  const int b = S.b;
+  if (S.f32 || (n & 7) || n > 32768 || !q.qbR || !q.qtP) return false;
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (!al(W0p) || !al(w.V) || !al(q.qbR) || !al(q.qtP) || !al(w.tnew)) return false;
+  uint16_t* W = static_cast<uint16_t*>(W0p);
+  uint16_t* V = static_cast<uint16_t*>(w.V);
+  {
+    Tm tm(s, "merge_tiles", 4.0 * m * n * b, 2.0 * m * n * S.es);
+    if (S.kP > 0 && !launch_blockdiag_bf16(W, q.qtP, W, m, n, n, b, S.kP, s)) return false;
+    if (S.kR > 0) {
+      GemmArgs g{};
+      g.A = q.qbR; g.B = W; g.C = V;
+      g.M = b; g.N = (int)n; g.K = b;
+      g.lda = b; g.ldb = n; g.ldc = n;
+      g.sA = (int64_t)b * b; g.sB = (int64_t)b * n; g.sC = (int64_t)b * n;
+      g.batch = S.kR;
+      launch_gemm_bf16(true, g, s);
+    }
+    launch_copy_rows_bf16(W + (int64_t)S.kR * b * n, V + (int64_t)S.kR * b * n, m - (int64_t)S.kR * b, n, s);
+  }
+  {
+    // new permutations, old inverses; then the composed maps in place of the new ones
+    Tm tm(s, "merge_permutations", 0.0, 0.0);
+    launch_perm_keys_rank(perm_seed, merge_index, 0, m, w.keys, w.snew, s);
+    launch_perm_keys_rank(perm_seed, merge_index, 1, n, w.keys, w.tnew, s);
+    launch_invert_perm(sigma, m, w.sinv, s);
+    launch_invert_perm(tau, n, w.tinv, s);
+    launch_copy_i32(w.snew, sigma, m, s);
+    launch_copy_i32(w.tnew, tau, n, s);
+    launch_compose_perm(w.sinv, w.snew, w.snew, m, s);
+    launch_compose_perm(w.tinv, w.tnew, w.tnew, n, s);
+  }
+  {
+    Tm tm(s, "merge_relayout", 0.0, 2.0 * m * n * S.es);
+    launch_relayout_rows_bf16(V, W, w.snew, w.tnew, m, n, s);
+  }
+  launch_fill_f32(thR, 0.f, (int64_t)S.kR * (S.b * (S.b - 1) / 2), s);
+  launch_fill_f32(thP, 0.f, (int64_t)S.kP * (S.b * (S.b - 1) / 2), s);
+  return true;
+}
+
 int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
                uint64_t perm_seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
   int rc;
+  if (S.b <= 256 && merge_fast_bf16(S, W0p, q, thR, thP, sigma, tau, perm_seed, merge_index, w, s))
+    return check_launch("merge");
   {
     Tm tm(s, "merge_tiles", 4.0 * S.m * S.n * S.b, 2.0 * S.m * S.n * S.es);
     if (S.f32) launch_merge_tiles(true, W0p, w.V, q.q32R, q.q32P, S.m, S.n, S.b, S.kR, S.kP, s);

@@ -129,10 +129,12 @@ __device__ __forceinline__ void lds_barrier() {
 }  // namespace
 
 template <int B>
-__global__ __launch_bounds__(Bd<B>::NT) void blockdiag_kernel(const uint16_t* __restrict__ in,
-                                                             const uint16_t* __restrict__ q,
-                                                             uint16_t* __restrict__ out, int64_t N, int64_t lda,
-                                                             int64_t ldc, int k, int tpc) {
+// in and out may be the same matrix (the merge's in-place block product): a
+// workgroup reads every element of its tiles before it writes them, and no
+// two workgroups touch the same elements
+__global__ __launch_bounds__(Bd<B>::NT) void blockdiag_kernel(const uint16_t* in, const uint16_t* __restrict__ q,
+                                                             uint16_t* out, int64_t N, int64_t lda, int64_t ldc, int k,
+                                                             int tpc) {
   using C = Bd<B>;
   // the ring and the staging tile as separate LDS objects, each named at
   // compile time, so that the compiler tells reads of one stage from the

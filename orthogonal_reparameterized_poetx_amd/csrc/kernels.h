@@ -148,6 +148,15 @@ void launch_invert_perm(const int32_t* p, int64_t n, int32_t* inv, hipStream_t s
 void launch_relayout(bool f32, const void* V, void* W, const int32_t* sinv_old, const int32_t* snew,
                      const int32_t* tinv_old, const int32_t* tnew, int64_t m, int64_t n, hipStream_t s);
 void launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
+// out[i] = a[b[i]]
+void launch_compose_perm(const int32_t* a, const int32_t* b, int32_t* out, int64_t n, hipStream_t s);
+// rows [0, rows) of a bf16 [.][n] matrix, n a multiple of 8, 16-byte aligned
+void launch_copy_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t n, hipStream_t s);
+// W[i][j] = V[rmap[i]][cmap[j]] (bf16; V and W distinct).  Returns false,
+// launching nothing, unless n is a multiple of 8 up to 32768 and V, W, cmap are
+// 16-byte aligned.
+bool launch_relayout_rows_bf16(const uint16_t* V, uint16_t* W, const int32_t* rmap, const int32_t* cmap, int64_t m,
+                               int64_t n, hipStream_t s);
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
 void launch_adam(float* theta, const float* grad, float* m, float* v, int64_t n, float lr, float b1, float b2,
                  float eps, float bc1, float bc2, hipStream_t s);

@@ -11,6 +11,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace poetx {
 
 // ---------------------------------------------------------------------------
@@ -254,6 +256,85 @@ void launch_relayout(bool f32, const void* V, void* W, const int32_t* sinv_old, 
   else
     hipLaunchKernelGGL(relayout_bf16_kernel, dim3((unsigned)m), dim3(256), 0, s, static_cast<const uint16_t*>(V),
                        static_cast<uint16_t*>(W), sinv_old, snew, tinv_old, tnew, (int)n);
+}
+
+// out[i] = a[b[i]]
+// (out may be b: each element is read and then written by one thread)
+__global__ void compose_perm_kernel(const int32_t* __restrict__ a, const int32_t* b, int32_t* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = a[b[i]];
+}
+void launch_compose_perm(const int32_t* a, const int32_t* b, int32_t* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(compose_perm_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, b, out, n);
+}
+
+// dst[r][:] = src[r][:] for r < rows (16-byte chunks; n multiple of 8)
+__global__ void copy_rows_bf16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t chunks) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < chunks; e += (int64_t)gridDim.x * blockDim.x)
+    dst[e] = src[e];
+}
+void launch_copy_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t n, hipStream_t s) {
+  const int64_t chunks = rows * n / 8;
+  if (chunks <= 0) return;
+  const int64_t g = std::min<int64_t>((chunks + 255) / 256, 4096);
+  hipLaunchKernelGGL(copy_rows_bf16_kernel, dim3((unsigned)g), dim3(256), 0, s, reinterpret_cast<const uint4*>(src),
+                     reinterpret_cast<uint4*>(dst), chunks);
+}
+
+// W[i][j] = V[rmap[i]][cmap[j]] for bf16 rows of n columns (n multiple of 8,
+// 16-byte aligned rows): R source rows per workgroup are staged in LDS with
+// asynchronous 16-byte loads (one contiguous KiB per wave instruction), then
+// every thread gathers 8-column chunks through LDS, reading each chunk's 8
+// column indices once for all R rows, and writes them as 16-byte stores.
+constexpr int RL_THREADS = 256;
+__global__ __launch_bounds__(RL_THREADS) void relayout_rows_bf16_kernel(const uint16_t* __restrict__ V,
+                                                                        uint16_t* __restrict__ W,
+                                                                        const int32_t* __restrict__ rmap,
+                                                                        const int32_t* __restrict__ cmap, int64_t m,
+                                                                        int n, int R) {
+  extern __shared__ __align__(16) uint16_t rows[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = (int64_t)blockIdx.x * R;
+  const int nr = (int)min((int64_t)R, m - t0);
+  const int cpr = (n + 511) >> 9;   // 1 KiB chunks per row
+  for (int c = wave; c < nr * cpr; c += RL_THREADS / 64) {
+    const int r = c / cpr, j = c - r * cpr;
+    const int e0 = (j << 9) + lane * 8;
+    if (e0 < n)
+      __builtin_amdgcn_global_load_lds(V + (int64_t)rmap[t0 + r] * n + e0,
+                                       (__attribute__((address_space(3))) void*)(rows + r * n + (j << 9)), 16, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint16_t* __restrict__ out = W + t0 * n;
+  for (int c = tid; c < (n >> 3); c += RL_THREADS) {
+    const int4 pa = *reinterpret_cast<const int4*>(cmap + c * 8);
+    const int4 pb = *reinterpret_cast<const int4*>(cmap + c * 8 + 4);
+    for (int r = 0; r < nr; ++r) {
+      const uint16_t* row = rows + r * n;
+      uint4 v;
+      v.x = pack2(row[pa.x], row[pa.y]);
+      v.y = pack2(row[pa.z], row[pa.w]);
+      v.z = pack2(row[pb.x], row[pb.y]);
+      v.w = pack2(row[pb.z], row[pb.w]);
+      stg16(out + (int64_t)r * n + c * 8, v);
+    }
+  }
+}
+bool launch_relayout_rows_bf16(const uint16_t* V, uint16_t* W, const int32_t* rmap, const int32_t* cmap, int64_t m,
+                               int64_t n, hipStream_t s) {
+  if (m <= 0 || n <= 0) return true;
+  if ((n & 7) || n > 32768 || (reinterpret_cast<uintptr_t>(V) & 15) || (reinterpret_cast<uintptr_t>(W) & 15) ||
+      (reinterpret_cast<uintptr_t>(cmap) & 15))
+    return false;
+  int R = (int)(32768 / n);
+  R = R < 1 ? 1 : (R > 16 ? 16 : R);
+  const size_t lds = (size_t)R * n * sizeof(uint16_t);
+  hipLaunchKernelGGL(relayout_rows_bf16_kernel, dim3((unsigned)((m + R - 1) / R)), dim3(RL_THREADS), lds, s, V, W,
+                     rmap, cmap, m, (int)n, R);
+  return true;
 }
 
 __global__ void copy_i32_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int64_t n) {
