@@ -677,14 +677,7 @@ bool merge_fast_bf16(const Shape& S, void* W0p, const Blk& q, float* thR, float*
   {
     // new permutations, old inverses; then the composed maps in place of the new ones
     Tm tm(s, "merge_permutations", 0.0, 0.0);
-    launch_perm_keys_rank(perm_seed, merge_index, 0, m, w.keys, w.snew, s);
-    launch_perm_keys_rank(perm_seed, merge_index, 1, n, w.keys, w.tnew, s);
-    launch_invert_perm(sigma, m, w.sinv, s);
-    launch_invert_perm(tau, n, w.tinv, s);
-    launch_copy_i32(w.snew, sigma, m, s);
-    launch_copy_i32(w.tnew, tau, n, s);
-    launch_compose_perm(w.sinv, w.snew, w.snew, m, s);
-    launch_compose_perm(w.tinv, w.tnew, w.tnew, n, s);
+    launch_merge_permutations(perm_seed, merge_index, sigma, tau, m, n, w.snew, w.tnew, w.sinv, w.tinv, s);
   }
   {
     Tm tm(s, "merge_relayout", 0.0, 2.0 * m * n * S.es);

@@ -148,8 +148,11 @@ void launch_invert_perm(const int32_t* p, int64_t n, int32_t* inv, hipStream_t s
 void launch_relayout(bool f32, const void* V, void* W, const int32_t* sinv_old, const int32_t* snew,
                      const int32_t* tinv_old, const int32_t* tnew, int64_t m, int64_t n, hipStream_t s);
 void launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
-// out[i] = a[b[i]]
-void launch_compose_perm(const int32_t* a, const int32_t* b, int32_t* out, int64_t n, hipStream_t s);
+// The permutation step of a merge, both sides: snew / tnew <- new draws,
+// sinv / tinv <- inverses of the old sigma / tau, sigma / tau <- the new draws,
+// and snew / tnew <- sinv(snew), tinv(tnew) (the relayout's source maps).
+void launch_merge_permutations(uint64_t seed, uint64_t merge_index, int32_t* sigma, int32_t* tau, int64_t m, int64_t n,
+                               int32_t* snew, int32_t* tnew, int32_t* sinv, int32_t* tinv, hipStream_t s);
 // rows [0, rows) of a bf16 [.][n] matrix, n a multiple of 8, 16-byte aligned
 void launch_copy_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t n, hipStream_t s);
 // W[i][j] = V[rmap[i]][cmap[j]] (bf16; V and W distinct).  Returns false,

@@ -211,6 +211,74 @@ void launch_perm_keys_rank(uint64_t seed, uint64_t merge_index, int side, int64_
                      n, out);
 }
 
+// Both sides of a merge in one launch each (workgroups [0, blocks0) take the
+// row side, the rest the column side): the counting rank computes the keys as
+// it goes instead of reading them from memory.
+__device__ __forceinline__ uint64_t perm_key(uint64_t base, int64_t j) {
+  return mix64_dev(base + 0x9E3779B97F4A7C15ull * (uint64_t)(j + 1));
+}
+__global__ __launch_bounds__(RANK_I * RANK_J) void perm_rank2_kernel(uint64_t seed, uint64_t merge_index, int64_t n0,
+                                                                     int64_t n1, int32_t* out0, int32_t* out1,
+                                                                     int blocks0) {
+  __shared__ uint64_t tile[RANK_TILE];
+  const int side = (int)blockIdx.x < blocks0 ? 0 : 1;
+  const int64_t n = side ? n1 : n0;
+  int32_t* out = side ? out1 : out0;
+  const int64_t blk = side ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
+  const uint64_t base = mix64_dev(seed + 0x9E3779B97F4A7C15ull * (2 * merge_index + (uint64_t)side + 1));
+  const int li = threadIdx.x / RANK_J, lj = threadIdx.x % RANK_J;
+  const int64_t i = blk * RANK_I + li;
+  const uint64_t ki = i < n ? perm_key(base, i) : 0;
+  int rank = 0;
+  for (int64_t j0 = 0; j0 < n; j0 += RANK_TILE) {
+    const int cnt = (int)min((int64_t)RANK_TILE, n - j0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < cnt; e += RANK_I * RANK_J) tile[e] = perm_key(base, j0 + e);
+    __syncthreads();
+    for (int e = lj; e < cnt; e += RANK_J) {
+      const uint64_t kj = tile[e];
+      const int64_t j = j0 + e;
+      rank += (kj < ki) || (kj == ki && j < i);
+    }
+  }
+#pragma unroll
+  for (int off = RANK_J / 2; off > 0; off >>= 1) rank += __shfl_xor(rank, off, RANK_J);
+  if (i < n && lj == 0) out[rank] = (int32_t)i;
+}
+// inv0 = p0^-1 (first n0 threads), inv1 = p1^-1
+__global__ void invert_perm2_kernel(const int32_t* __restrict__ p0, int64_t n0, int32_t* __restrict__ inv0,
+                                    const int32_t* __restrict__ p1, int64_t n1, int32_t* __restrict__ inv1) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n0) inv0[p0[e]] = (int32_t)e;
+  else if (e < n0 + n1) inv1[p1[e - n0]] = (int32_t)(e - n0);
+}
+// commit the new permutations and turn them into the relayout's maps:
+// cur[i] <- nw[i], nw[i] <- inv[nw[i]] (per side)
+__global__ void commit_perm2_kernel(int32_t* nw0, int32_t* cur0, const int32_t* __restrict__ inv0, int64_t n0,
+                                    int32_t* nw1, int32_t* cur1, const int32_t* __restrict__ inv1, int64_t n1) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n0) {
+    const int32_t v = nw0[e];
+    cur0[e] = v;
+    nw0[e] = inv0[v];
+  } else if (e < n0 + n1) {
+    const int64_t i = e - n0;
+    const int32_t v = nw1[i];
+    cur1[i] = v;
+    nw1[i] = inv1[v];
+  }
+}
+void launch_merge_permutations(uint64_t seed, uint64_t merge_index, int32_t* sigma, int32_t* tau, int64_t m, int64_t n,
+                               int32_t* snew, int32_t* tnew, int32_t* sinv, int32_t* tinv, hipStream_t s) {
+  if (m <= 0 && n <= 0) return;
+  const int b0 = (int)((m + RANK_I - 1) / RANK_I), b1 = (int)((n + RANK_I - 1) / RANK_I);
+  hipLaunchKernelGGL(perm_rank2_kernel, dim3((unsigned)(b0 + b1)), dim3(RANK_I * RANK_J), 0, s, seed, merge_index, m, n,
+                     snew, tnew, b0);
+  const unsigned g = (unsigned)((m + n + 255) / 256);
+  hipLaunchKernelGGL(invert_perm2_kernel, dim3(g), dim3(256), 0, s, sigma, m, sinv, tau, n, tinv);
+  hipLaunchKernelGGL(commit_perm2_kernel, dim3(g), dim3(256), 0, s, snew, sigma, sinv, m, tnew, tau, tinv, n);
+}
+
 __global__ void invert_perm_kernel(const int32_t* __restrict__ p, int64_t n, int32_t* __restrict__ inv) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) inv[p[i]] = (int32_t)i;
@@ -256,17 +324,6 @@ void launch_relayout(bool f32, const void* V, void* W, const int32_t* sinv_old, 
   else
     hipLaunchKernelGGL(relayout_bf16_kernel, dim3((unsigned)m), dim3(256), 0, s, static_cast<const uint16_t*>(V),
                        static_cast<uint16_t*>(W), sinv_old, snew, tinv_old, tnew, (int)n);
-}
-
-// out[i] = a[b[i]]
-// (out may be b: each element is read and then written by one thread)
-__global__ void compose_perm_kernel(const int32_t* __restrict__ a, const int32_t* b, int32_t* out, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = a[b[i]];
-}
-void launch_compose_perm(const int32_t* a, const int32_t* b, int32_t* out, int64_t n, hipStream_t s) {
-  if (n <= 0) return;
-  hipLaunchKernelGGL(compose_perm_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, b, out, n);
 }
 
 // dst[r][:] = src[r][:] for r < rows (16-byte chunks; n multiple of 8)
