@@ -41,12 +41,11 @@ KERNEL_CLASSES = [
     ("permute_scatter_kernel", "xform_permute", 1),
     ("permute_stream_kernel", "xform_permute", 1),
     ("blockdiag_kernel", "xform_blockmul", 1),
-    ("gemm_bf16_kernel<false, true, false,", "xform_blockmul", 1),
-    ("gemm_bf16_kernel<false, false, false,", "gemm_nt", 1),
-    ("gemm_bf16_kernel<true, false, false,", "gemm_nn", 1),
-    ("gemm_bf16_kernel<true, true, true,", "chain_rule", 5),
-    ("chain_prep", "chain_rule", 5),
-    ("skew_project_kernel", "chain_rule", 5),
+    ("gemm_bf16_kernel<false, true,", "xform_blockmul", 1),
+    ("gemm_bf16_kernel<false, false,", "gemm_nt", 1),
+    ("gemm_bf16_kernel<true, false,", "gemm_nn", 1),
+    ("chain_product_kernel", "chain_rule", 3),
+    ("skew_project_kernel", "chain_rule", 3),
     ("gj_kernel", "cayley_build", 1),
     ("gram_bf16_kernel", "gram", 2),
     ("gram_stream_kernel", "gram", 2),

@@ -222,30 +222,17 @@ int build2(const float* th0, int64_t n0, QOut o0, const float* th1, int64_t n1, 
 // dtheta from G = dL/dQ:  G_S = 1/2 (I + Q^T) G (I + Q^T);  dtheta_p = G_S[i][j] - G_S[j][i].
 // G holds the R blocks then the P blocks contiguously; the fp32 blocks of the
 // two sides may live apart (q32R, q32P).  Both sides in one pass.
-// bf16 layers: each product is one bf16 GEMM over a tripled K on split
-// operands (fp32-level accuracy), fp32 accumulation and output; cat holds
-// the four split operands.  fp32 layers: fp32 MFMA products.
-// split-operand chain rule over nblk blocks described by cs; GS (fp32
-// [nblk][b][b], contiguous) receives G_S and may alias the g arrays only when
-// a single segment covers them contiguously in block order.
-void chain_bf16(const ChainSegs& cs, int nblk, int b, float* T, uint16_t* const* cat, float* GS, int accumulate,
-                hipStream_t s) {
-  const int64_t sb = (int64_t)b * b;
-  launch_chain_prep1(cs, nblk, b, cat[0], cat[1], cat[2], s);
-  GemmArgs g{};
-  g.M = g.N = b; g.K = 3 * b;
-  g.lda = 3 * b; g.ldb = b; g.ldc = b;
-  g.sA = 3 * sb; g.sB = 3 * sb; g.sC = sb;
-  g.batch = nblk;
-  g.A = cat[0]; g.B = cat[1]; g.Cf = T;                   // T = G (I + Q^T)
-  launch_gemm_bf16_f32out(g, s);
-  launch_chain_prep2(T, nblk, b, cat[3], s);
-  g.A = cat[2]; g.B = cat[3]; g.Cf = GS;                  // G_S = (I + Q^T) T / 2
-  launch_gemm_bf16_f32out(g, s);
+// bf16 layers: fp32-accurate products on split bf16 operands (chain.hip);
+// fp32 layers: fp32 MFMA products.
+// split-operand chain rule over nblk blocks described by cs; T ([nblk][b][b]
+// fp32) is scratch; GS (fp32 [nblk][b][b], contiguous) receives G_S and may
+// alias the g arrays only when they are contiguous in block order.
+void chain_bf16(const ChainSegs& cs, int nblk, int b, float* T, float* GS, int accumulate, hipStream_t s) {
+  launch_chain_products(cs, nblk, b, T, GS, s);
   launch_skew_project(GS, b, nblk, cs, accumulate, s);
 }
 
-int chain(float* G, const float* q32R, const float* q32P, float* tmp, uint16_t* const* cat, int64_t nR, int64_t nP,
+int chain(float* G, const float* q32R, const float* q32P, float* tmp, int64_t nR, int64_t nP,
           int b, float* dthR, float* dthP, bool accumulate, bool f32, hipStream_t s) {
   const int64_t nblk = nR + nP;
   if (nblk <= 0) return POETX_OK;
@@ -257,7 +244,7 @@ int chain(float* G, const float* q32R, const float* q32P, float* tmp, uint16_t* 
   if (nP > 0) { cs.seg[cs.nseg] = ChainSeg{q32P, G + nR * sb, dthP}; cs.start[cs.nseg] = (int)nR; ++cs.nseg; }
   cs.start[cs.nseg] = (int)nblk;
   if (!f32) {
-    chain_bf16(cs, (int)nblk, b, tmp, cat, G, accumulate ? 1 : 0, s);
+    chain_bf16(cs, (int)nblk, b, tmp, G, accumulate ? 1 : 0, s);
   } else {
     BGemmArgs q{};
     q.M = q.N = q.K = b;
@@ -287,7 +274,6 @@ size_t chain_ws_bytes(int64_t total, int b) {
   if (c <= 0) return 0;
   Arena a(nullptr);
   const size_t bb = (size_t)b * b;
-  for (int i = 0; i < 4; ++i) a.take<uint16_t>(c * 3 * bb);
   a.take<float>(c * bb);   // T
   a.take<float>(c * bb);   // G_S
   return a.off + kAlign;
@@ -356,7 +342,6 @@ struct BwdWs {
   void* bws;
   void *z1, *xg, *z2, *gyg, *gz2;
   float *GR, *GP, *tmp;
-  uint16_t *cat[4];   // chain-rule split operands (bf16 layers)
   void* part;
 };
 BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes, bool dq = false) {
@@ -382,8 +367,6 @@ BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes, bool dq = fa
     w.GR = a.take<float>((S.kR + S.kP) * bb);     // R blocks, then P blocks
     w.GP = w.GR ? w.GR + S.kR * bb : nullptr;
     w.tmp = a.take<float>((S.kR + S.kP) * bb);
-    if (!S.f32)
-      for (auto& c : w.cat) c = a.take<uint16_t>((S.kR + S.kP) * 3 * bb);
   }
   const size_t pb = std::max(gram_partials_bytes(S.N, S.b, S.kR, S.f32), gram_partials_bytes(S.N, S.b, S.kP, S.f32));
   w.part = a.take<char>(pb);
@@ -589,7 +572,7 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   if ((rc = check_launch("P-side backward"))) return rc;
   if (gR) return POETX_OK;
   // chain rule through the Cayley map onto the stored upper triangle
-  return chain(w.GR, q.q32R, q.q32P, w.tmp, w.cat, S.kR, S.kP, S.b, dthR, dthP, accum, S.f32, s);
+  return chain(w.GR, q.q32R, q.q32P, w.tmp, S.kR, S.kP, S.b, dthR, dthP, accum, S.f32, s);
 }
 
 // shared argument checks of forward / forward_blocks
@@ -926,8 +909,6 @@ int poetx_chain_rule_sets(const poetx_chain_set* sets, int32_t count, int32_t b,
   const int64_t chunk = std::min<int64_t>(total, kChainChunk);
   const size_t bb = (size_t)b * b;
   Arena a(ws);
-  uint16_t* cat[4];
-  for (auto& c : cat) c = a.take<uint16_t>(chunk * 3 * bb);
   float* T = a.take<float>(chunk * bb);
   float* GS = a.take<float>(chunk * bb);
   Tm tm(s, "chain_rule", 4.0 * b * (double)b * b * total, 0.0);
@@ -951,7 +932,7 @@ int poetx_chain_rule_sets(const poetx_chain_set* sets, int32_t count, int32_t b,
       if (off >= t.nblocks) { ++si; off = 0; }
     }
     cs.start[cs.nseg] = n;
-    if (n > 0) chain_bf16(cs, n, b, T, cat, GS, (flags & POETX_ACCUMULATE_GRAD) ? 1 : 0, s);
+    if (n > 0) chain_bf16(cs, n, b, T, GS, (flags & POETX_ACCUMULATE_GRAD) ? 1 : 0, s);
   }
   return check_launch("chain rule");
 }

@@ -1,4 +1,4 @@
-// Cayley block builder, batched small fp32 GEMM and chain-rule projection.
+// Cayley block builder and batched small fp32 GEMM.
 //
 // Q = (I - S)^-1 (I + S) for skew S [P1 "POET-X：基于正交变换缩放的内存高效LLM训练方法",
 // 实践 2], with S unpacked from the stored strict upper triangle
@@ -502,26 +502,6 @@ __global__ __launch_bounds__(256) void finalize_q_kernel(const float* __restrict
     for (int r = ty; r < 32; r += 8) qtbf[base + (int64_t)(j0 + r) * b + i0 + tx] = t[tx][r];
 }
 
-// dtheta[blk][p(i,j)] (+)= GS[i][j] - GS[j][i], i < j.  grid (ceil(b/256), b-1, nblk);
-// blocks [0, n0) write dth0, the rest dth1.
-__device__ __forceinline__ int chain_seg(const ChainSegs& cs, int z) {
-  int sg = 0;
-  while (sg + 1 < cs.nseg && z >= cs.start[sg + 1]) ++sg;
-  return sg;
-}
-
-__global__ void skew_project_kernel(const float* __restrict__ GS, int b, ChainSegs cs, int accumulate) {
-  const int blk = blockIdx.z, i = blockIdx.y;
-  const int j = i + 1 + blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= b) return;
-  const int sg = chain_seg(cs, blk);
-  const float* g = GS + (int64_t)blk * b * b;
-  const float v = g[(int64_t)i * b + j] - g[(int64_t)j * b + i];
-  float* dth = cs.seg[sg].dth + (int64_t)(blk - cs.start[sg]) * (b * (b - 1) / 2);
-  float* d = dth + (i * b - i * (i + 1) / 2 + (j - i - 1));
-  *d = accumulate ? (*d + v) : v;
-}
-
 // ----------------------------------------------------------------------------
 // host launchers
 // ----------------------------------------------------------------------------
@@ -550,77 +530,6 @@ void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL(bgemm_kernel<0>, grid, dim3(256), 0, s, a);
 }
 
-// ---------------------------------------------------------------------------
-// chain-rule operand preparation (see kernels.h): one thread per (row, col)
-// of a block; bf16 hi / lo split of fp32 values
-// ---------------------------------------------------------------------------
-// 32 x 32 tile per workgroup (256 threads, 4 elements each); Q is read
-// coalesced and transposed through LDS
-__global__ __launch_bounds__(256) void chain_prep1_kernel(ChainSegs cs, int b, uint16_t* __restrict__ Acat,
-                                                          uint16_t* __restrict__ Bcat, uint16_t* __restrict__ A2cat) {
-  __shared__ float qt[32][33];
-  const int z = blockIdx.z;
-  const int sg = chain_seg(cs, z);
-  const int64_t bb = (int64_t)b * b;
-  const int64_t zl = z - cs.start[sg];
-  const float* __restrict__ q = cs.seg[sg].q + zl * bb;
-  const float* __restrict__ G = cs.seg[sg].g + zl * bb;
-  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // ty 0..7
-  // qt[jj][ii] = Q[j0 + jj][i0 + ii]
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int jj = ty + 8 * r;
-    qt[jj][tx] = q[(int64_t)(j0 + jj) * b + i0 + tx];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ii = ty + 8 * r;
-    const int i = i0 + ii, j = j0 + tx;
-    // B'[i][j] = (I + Q^T)[i][j] = delta_ij + Q[j][i]
-    const float bp = qt[tx][ii] + (i == j ? 1.f : 0.f);
-    const float g = G[(int64_t)i * b + j];
-    bf16 gh, gl, bh, bl;
-    split_bf16(g, gh, gl);
-    split_bf16(bp, bh, bl);
-    const uint16_t GH = __builtin_bit_cast(uint16_t, gh), GL = __builtin_bit_cast(uint16_t, gl);
-    const uint16_t BH = __builtin_bit_cast(uint16_t, bh), BL = __builtin_bit_cast(uint16_t, bl);
-    uint16_t* a = Acat + z * 3 * bb + (int64_t)i * 3 * b;      // row i of [b][3b]
-    a[j] = GH; a[b + j] = GH; a[2 * b + j] = GL;
-    uint16_t* c = Bcat + z * 3 * bb;                            // rows i, b+i, 2b+i of [3b][b]
-    c[(int64_t)i * b + j] = BH; c[(int64_t)(b + i) * b + j] = BL; c[(int64_t)(2 * b + i) * b + j] = BH;
-    uint16_t* a2 = A2cat + z * 3 * bb + (int64_t)i * 3 * b;
-    a2[j] = BH; a2[b + j] = BH; a2[2 * b + j] = BL;
-  }
-}
-
-__global__ void chain_prep2_kernel(const float* __restrict__ T, int b, uint16_t* __restrict__ Tcat) {
-  const int z = blockIdx.y;
-  const int64_t bb = (int64_t)b * b;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= bb) return;
-  const int i = e / b, j = e - i * b;
-  bf16 h, l;
-  split_bf16(0.5f * T[z * bb + e], h, l);   // the 1/2 of G_S, exact in fp32
-  const uint16_t H = __builtin_bit_cast(uint16_t, h), L = __builtin_bit_cast(uint16_t, l);
-  uint16_t* c = Tcat + z * 3 * bb;
-  c[(int64_t)i * b + j] = H; c[(int64_t)(b + i) * b + j] = L; c[(int64_t)(2 * b + i) * b + j] = H;
-}
-
-void launch_chain_prep1(const ChainSegs& cs, int nblk, int b, uint16_t* Acat, uint16_t* Bcat, uint16_t* A2cat,
-                        hipStream_t s) {
-  if (nblk <= 0) return;
-  dim3 grid((unsigned)(b / 32), (unsigned)(b / 32), (unsigned)nblk);   // b is a multiple of 32
-  hipLaunchKernelGGL(chain_prep1_kernel, grid, dim3(256), 0, s, cs, b, Acat, Bcat, A2cat);
-}
-
-void launch_chain_prep2(const float* T, int nblk, int b, uint16_t* Tcat, hipStream_t s) {
-  if (nblk <= 0) return;
-  dim3 grid((unsigned)(((int64_t)b * b + 255) / 256), (unsigned)nblk);
-  hipLaunchKernelGGL(chain_prep2_kernel, grid, dim3(256), 0, s, T, b, Tcat);
-}
-
 void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s) {
   if (nblk <= 0) return;
   dim3 grid((unsigned)(((int64_t)b * b + 255) / 256), nblk);
@@ -633,10 +542,5 @@ void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qb
   hipLaunchKernelGGL(finalize_q_kernel, grid, dim3(256), 0, s, M, b, q32, qbf, qtbf);
 }
 
-void launch_skew_project(const float* GS, int b, int nblk, const ChainSegs& cs, int accumulate, hipStream_t s) {
-  if (nblk <= 0) return;
-  dim3 grid((b + 255) / 256, b - 1, nblk);
-  hipLaunchKernelGGL(skew_project_kernel, grid, dim3(256), 0, s, GS, b, cs, accumulate);
-}
 
 }  // namespace poetx

@@ -49,8 +49,7 @@ __device__ __forceinline__ void b2l16(__amdgpu_buffer_rsrc_t r, int voff, int so
 //     c ^ ((r & 3) << 2): a 32-lane phase of the transposing read (4 rows,
 //     4 chunks, two halves each) touches every bank pair once
 // BATCHED only names the instantiation used for batched block products, so
-// that profiles tell it apart from the weight products.  OUTF32 writes the
-// fp32 accumulators to g.Cf instead of bf16 to g.C.  SMALL takes K below
+// that profiles tell it apart from the weight products.  SMALL takes K below
 // 32 (GST - 2) + 1, where the ring is never full.
 constexpr int GST = 4;                 // ring stages
 constexpr int GSE = 2 * 256 * 32;      // elements per stage (A and B)
@@ -60,7 +59,7 @@ constexpr int GSE = 2 * 256 * 32;      // elements per stage (A and B)
 // asynchronous LDS fills have completed.
 constexpr unsigned vm_imm(unsigned vm) { return (vm & 15u) | ((vm >> 4) << 14) | (7u << 4) | (15u << 8); }
 
-template <bool NN, bool BATCHED, bool OUTF32, bool SMALL>
+template <bool NN, bool BATCHED, bool SMALL>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
   // the four ring stages as separate LDS objects, each named at compile time
   // below, so that the compiler can tell reads of one from the asynchronous
@@ -80,8 +79,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
   const int M = g.M, N = g.N, K = g.K;
   const uint16_t* __restrict__ A = g.A + bz * g.sA;
   const uint16_t* __restrict__ Bm = g.B + bz * g.sB;
-  uint16_t* __restrict__ C = OUTF32 ? nullptr : g.C + bz * g.sC;
-  float* __restrict__ Cf = OUTF32 ? g.Cf + bz * g.sC : nullptr;
+  uint16_t* __restrict__ C = g.C + bz * g.sC;
   const int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -264,50 +262,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
   // holds the transposed 32 x 32 sub-tile: register r of lane l is
   // C[row l % 32][col 8 (r / 4) + 4 (l / 32) + r % 4], i.e. four
   // consecutive columns of one row per register quad.
-  if constexpr (OUTF32) {
-    // fp32: the same staging in two rounds of 64 rows (16 KiB per wave and
-    // round): 16-byte writes into 256-byte rows, chunk c at c ^ (row & 15),
-    // then 16-byte row-order stores (4 rows of 256 bytes per instruction)
-    uint32_t* st = reinterpret_cast<uint32_t*>((wave < 2 ? S0 : wave < 4 ? S1 : wave < 6 ? S2 : S3) +
-                                               (wave & 1) * (128 * 64));
-    const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(Cf) & 15) == 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      __syncthreads();
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * h + ii;
-        const int row = ii * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x16& a = acc[i][j];
-            const int chunk = j * 8 + 2 * q + (lane >> 5);
-            *reinterpret_cast<float4*>(st + row * 64 + ((chunk ^ (row & 15)) << 2)) =
-                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-          }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int e = it * 64 + lane;
-        const int row = e >> 4, chunk = e & 15;
-        const float4 v = *reinterpret_cast<const float4*>(st + row * 64 + ((chunk ^ (row & 15)) << 2));
-        const int gm = m0 + wm * 128 + h * 64 + row, gn = n0 + wn * 64 + chunk * 4;
-        if (gm < M && gn < N) {
-          float* cp = Cf + (int64_t)gm * ldc + gn;
-          if (vec && gn + 3 < N) *reinterpret_cast<float4*>(cp) = v;
-          else {
-            const float w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2)
-              if (gn + e2 < N) cp[e2] = w[e2];
-          }
-        }
-      }
-    }
-  } else {
+  {
     // bf16: each wave stages its 128 x 64 tile (16 KiB) in the now idle LDS
     // buffers, 8-byte writes into 128-byte rows, chunk c at c ^ ((row >> 1) & 7)
     // and the two halves of a chunk swapped on rows with bit 4 set (32 rows of
@@ -396,8 +351,8 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     const bool small = (g.K + 31) / 32 < GST - 1;
 #define GEMM_LAUNCH(NN_, BT_)                                                                                  \
   {                                                                                                           \
-    if (small) hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
-    else hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, false, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
+    if (small) hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
+    else hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
   }
     if (nn) GEMM_LAUNCH(true, false)
     else if (g.batch > 1) GEMM_LAUNCH(false, true)
@@ -408,15 +363,6 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     if (nn) hipLaunchKernelGGL(gemm_bf16_generic_kernel<true>, grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL(gemm_bf16_generic_kernel<false>, grid, dim3(256), 0, s, g);
   }
-}
-
-void launch_gemm_bf16_f32out(const GemmArgs& g, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return;
-  const int tn = (g.N + GBN - 1) / GBN, tm = (g.M + GBM - 1) / GBM;
-  const int nt = tn * tm * g.batch;
-  const int grid = ((nt + 7) / 8) * 8;
-  if ((g.K + 31) / 32 < GST - 1) hipLaunchKernelGGL((gemm_bf16_kernel<true, true, true, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
-  else hipLaunchKernelGGL((gemm_bf16_kernel<true, true, true, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
 }
 
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N, int64_t K,

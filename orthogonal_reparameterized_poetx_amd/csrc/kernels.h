@@ -56,14 +56,11 @@ struct ChainSegs {
   int start[CH_MAXSEG + 1];
   int nseg;
 };
-// operands for fp32-accurate products as single bf16 GEMMs over a tripled K
-// (x = hi + lo, x*y ~ hi*hi + hi*lo + lo*hi).  With B' = I + Q^T:
-//   prep1: Acat[z] = [G_hi | G_hi | G_lo] ([b][3b]), Bcat[z] = [B'_hi; B'_lo; B'_hi]
-//          ([3b][b]), A2cat[z] = [B'_hi | B'_hi | B'_lo] ([b][3b])
-//   prep2: Tcat[z] = split of (T / 2) as [hi; lo; hi] ([3b][b])
-void launch_chain_prep1(const ChainSegs& cs, int nblk, int b, uint16_t* Acat, uint16_t* Bcat, uint16_t* A2cat,
-                        hipStream_t s);
-void launch_chain_prep2(const float* T, int nblk, int b, uint16_t* Tcat, hipStream_t s);
+// fp32-accurate chain-rule products on split bf16 operands (chain.hip):
+// C1[z] = (I + Q) G^T / 2 and GS[z] = (I + Q^T) C1[z]^T; C1 and GS are
+// contiguous [nblk][b][b] fp32 and GS may alias the segments' g arrays when
+// those are contiguous in block order (G is dead once C1 is formed).
+void launch_chain_products(const ChainSegs& cs, int nblk, int b, float* C1, float* GS, hipStream_t s);
 // dth of block z = (GS[z] - GS[z]^T) on the strict upper triangle (GS contiguous)
 void launch_skew_project(const float* GS, int b, int nblk, const ChainSegs& cs, int accumulate, hipStream_t s);
 // ---- block transforms (transform.hip)
@@ -115,7 +112,6 @@ struct GemmArgs {
   const uint16_t* A;
   const uint16_t* B;
   uint16_t* C;
-  float* Cf;           // fp32 output of launch_gemm_bf16_f32out
 
   int M, N, K;
   int64_t lda, ldb, ldc;
@@ -123,9 +119,6 @@ struct GemmArgs {
   int batch;
 };
 void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s);
-// NN with fp32 output to g.Cf (tiled path only: K, N, lda, ldb, sA, sB multiples
-// of 8 and 16-byte aligned operands; the caller guarantees it)
-void launch_gemm_bf16_f32out(const GemmArgs& g, hipStream_t s);
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N,
                       int64_t K, hipStream_t s);
 void launch_gemm_f32(bool nn, const float* A, const float* Bm, float* C, int64_t M, int64_t N, int64_t K,
