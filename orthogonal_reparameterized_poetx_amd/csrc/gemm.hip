@@ -10,9 +10,11 @@
 // bf16 operands, fp32 accumulation on 32x32x16 MFMA, bf16 output.  256x256
 // output tiles, 8 waves of 128x64, k in steps of 32 through a 4-stage LDS
 // ring with 16-byte XOR swizzles; the NN B operand is read K-major straight
-// from the N-contiguous tile with the gfx950 transposing LDS load.  Tiles are
-// assigned so that the workgroups on one XCD (blockIdx mod 8) work on
-// neighbouring output tiles and share L2.
+// from the N-contiguous tile with the gfx950 transposing LDS load.  The two
+// waves of each SIMD alternate ("ping-pong"): while one issues its step's
+// MFMAs from registers, the other refills the ring and reads its next
+// fragments.  Tiles are assigned so that the workgroups on one XCD
+// (blockIdx mod 8) work on neighbouring output tiles and share L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -157,106 +159,162 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
       }
     }
   };
-  auto compute = [&](const uint16_t* st) {
-    const uint16_t* as = st;
-    const uint16_t* bs = st + 256 * 32;
-    int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));
-    auto frag = [&](int s, bf16x8* af, bf16x8* bfr) {
+  bf16x8 AF[2][4], BF[2][2];
+  // loop-invariant byte offsets of this lane's fragment reads within a stage
+  // (A tile at 0, B tile at 16 KiB; the swizzles as described above).  The
+  // reads are inline asm that waits for its own results: the compiler cannot
+  // tell which ring stage an asynchronous fill targets and would otherwise
+  // wait for every fill in flight before them.
+  uint32_t fa[2], fb[2];
+  {
+    const int l32 = lane & 31, h = lane >> 5, sw = (l32 >> 2) & 3;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + (lane & 31);
-        const int ch = 2 * s + (lane >> 5);
-        af[i] = *reinterpret_cast<const bf16x8*>(&as[row * 32 + ((ch ^ ((row >> 2) & 3)) << 3)]);
-      }
+    for (int s = 0; s < 2; ++s) fa[s] = (uint32_t)((wm * 128 + l32) * 64 + (((2 * s + h) ^ sw) << 4));
+    if constexpr (!NN) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) fb[s] = (uint32_t)(16384 + (wn * 64 + l32) * 64 + (((2 * s + h) ^ sw) << 4));
+    } else {
+      const int gq = lane >> 4, q = lane & 15;
+      const int kr0 = 8 * (gq >> 1) + (q >> 2);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        if constexpr (!NN) {
-          const int row = wn * 64 + j * 32 + (lane & 31);
-          const int ch = 2 * s + (lane >> 5);
-          bfr[j] = *reinterpret_cast<const bf16x8*>(&bs[row * 32 + ((ch ^ ((row >> 2) & 3)) << 3)]);
-        } else {
-          const int gq = lane >> 4, q = lane & 15;
-          const int ncol = wn * 64 + j * 32 + 16 * (gq & 1) + 4 * (q & 3);
-          const int chn = ncol >> 3, within = ncol & 7;
-          i16x4 h[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int kr = 16 * s + 8 * (gq >> 1) + 4 * hh + (q >> 2);
-            h[hh] = ds_read_tr16(&bs[kr * 256 + ((chn ^ ((kr & 3) << 2)) << 3) + within]);
-          }
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          i16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-          bfr[j] = __builtin_bit_cast(bf16x8, v);
-        }
+        const int ncol = wn * 64 + j * 32 + 16 * (gq & 1) + 4 * (q & 3);
+        const int chn = ncol >> 3, within = ncol & 7;
+        fb[j] = (uint32_t)(16384 + 2 * (kr0 * 256 + ((chn ^ ((kr0 & 3) << 2)) << 3) + within));
       }
-    };
-    bf16x8 af[2][4], bfr[2][2];
-    frag(0, af[0], bfr[0]);
-    frag(1, af[1], bfr[1]);
+    }
+  }
+  auto frags = [&](const uint16_t* st) {
+    typedef int pi32x4 __attribute__((ext_vector_type(4)));
+    typedef int pi32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t sb = (uint32_t)reinterpret_cast<uintptr_t>(st);
+    const uint32_t a0 = sb + fa[0], a1 = sb + fa[1], b0 = sb + fb[0], b1 = sb + fb[1];
+    pi32x4 x[8];
+    if constexpr (!NN) {
+      pi32x4 y[4];
+      asm volatile(
+          "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
+          "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %12 offset:6144\n\t"
+          "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:2048\n\t"
+          "ds_read_b128 %6, %13 offset:4096\n\tds_read_b128 %7, %13 offset:6144\n\t"
+          "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:2048\n\t"
+          "ds_read_b128 %10, %15\n\tds_read_b128 %11, %15 offset:2048\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+            "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
+          : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
+          : "memory");
+      BF[0][0] = __builtin_bit_cast(bf16x8, y[0]);
+      BF[0][1] = __builtin_bit_cast(bf16x8, y[1]);
+      BF[1][0] = __builtin_bit_cast(bf16x8, y[2]);
+      BF[1][1] = __builtin_bit_cast(bf16x8, y[3]);
+    } else {
+      // B: j = 0 from b0, j = 1 from b1; k sub-step s at +8192, half hh at +2048
+      pi32x2 y[8];
+      asm volatile(
+          "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:2048\n\t"
+          "ds_read_b128 %2, %16 offset:4096\n\tds_read_b128 %3, %16 offset:6144\n\t"
+          "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:2048\n\t"
+          "ds_read_b128 %6, %17 offset:4096\n\tds_read_b128 %7, %17 offset:6144\n\t"
+          "ds_read_b64_tr_b16 %8, %18\n\tds_read_b64_tr_b16 %9, %18 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %10, %18 offset:8192\n\tds_read_b64_tr_b16 %11, %18 offset:10240\n\t"
+          "ds_read_b64_tr_b16 %12, %19\n\tds_read_b64_tr_b16 %13, %19 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %14, %19 offset:8192\n\tds_read_b64_tr_b16 %15, %19 offset:10240\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+            "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]), "=&v"(y[6]), "=&v"(y[7])
+          : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
+          : "memory");
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const pi32x2 lo = y[4 * j + 2 * s], hi = y[4 * j + 2 * s + 1];
+          const pi32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+          BF[s][j] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      AF[0][i] = __builtin_bit_cast(bf16x8, x[i]);
+      AF[1][i] = __builtin_bit_cast(bf16x8, x[4 + i]);
+    }
+  };
+  auto mma = [&]() {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(bfr[s][j], af[s][i], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(BF[s][j], AF[s][i], acc[i][j]);
     }
   };
 
-  // The ring, unrolled by S so that each step names its stages statically.
-  // Per lane a full step issues 4 loads, so before step i the loads of steps
-  // i+1 .. i+S-2 (issued earlier) may stay in flight.  With nk >= S - 1 (the
-  // launcher picks SMALL otherwise) the prologue fills stages 0 .. S-2
-  // unconditionally, so every wait in the steady loop below is one constant.
+  // Ping-pong ring.  Each wave alternates a memory phase (refill one stage
+  // with buffer-to-LDS loads, read this step's fragments) and a compute phase
+  // (the step's 16 MFMAs from registers), with a workgroup barrier between
+  // phases.  Waves 4..7 run one phase behind waves 0..3; wave w and wave
+  // w + 4 of a workgroup land on the same SIMD (the dispatcher's placement;
+  // correctness does not depend on it), so each SIMD always has one wave
+  // issuing MFMAs while its partner does memory work.  Stage data for step k is complete before the barrier
+  // that opens the first memory phase reading it (every wave waits for its
+  // own loads of step k before that barrier); a stage is refilled only in a
+  // phase after both halves have read it.
   dload_first(S0);
   asm volatile("" ::: "memory");
   if (!SMALL || 1 < nk) dload(r0, S1);
   asm volatile("" ::: "memory");
   if (!SMALL || 2 < nk) dload(r0 + 32, S2);
   asm volatile("" ::: "memory");
-  // steady step: wait for this lane's loads of step I (the 4 (S - 2) loads
-  // issued after them may stay in flight), barrier, refill the stage that
-  // step I - 1 read, compute
-#define G4STEADY(I, CUR, NEXT)                                                       \
+  const bool lag = wave >= 4;
+#define PPBAR(VM)                                                                    \
   {                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                               \
     asm volatile("" ::: "memory");                                                   \
-    __builtin_amdgcn_s_waitcnt(vm_imm(4 * (S - 2)));                                   \
+    __builtin_amdgcn_s_waitcnt(vm_imm(VM));                                          \
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                               \
     __builtin_amdgcn_s_barrier();                                                    \
     asm volatile("" ::: "memory");                                                   \
-    dload(r0 + ((I) + S - 2) * 32, NEXT);                                            \
-    compute(CUR);                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                               \
   }
-  // drain step: as above while loads remain, else wait for all
-#define G4STEP(I, CUR, NEXT)                                                         \
+  if (SMALL) PPBAR(0) else PPBAR(4 * (S - 2))
+  if (lag) __builtin_amdgcn_s_barrier();
+#define PPSTEADY(I, CUR, NEXT)                                                       \
+  {                                                                                  \
+    dload(r0 + ((I) + S - 2) * 32, NEXT);                                            \
+    asm volatile("" ::: "memory");                                                   \
+    frags(CUR);                                                                      \
+    PPBAR(4 * (S - 2))                                                               \
+    mma();                                                                           \
+    PPBAR(4 * (S - 2))                                                               \
+  }
+#define PPSTEP(I, CUR, NEXT)                                                         \
   {                                                                                  \
     const int i_ = (I);                                                              \
+    const bool more = i_ + S - 1 < nk;                                               \
+    if (more) dload(r0 + (i_ + S - 2) * 32, NEXT);                                   \
     asm volatile("" ::: "memory");                                                   \
-    if (i_ + S - 1 < nk) __builtin_amdgcn_s_waitcnt(vm_imm(4 * (S - 2)));             \
-    else __builtin_amdgcn_s_waitcnt(vm_imm(0));                                        \
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                               \
-    __builtin_amdgcn_s_barrier();                                                    \
-    asm volatile("" ::: "memory");                                                   \
-    if (i_ + S - 1 < nk) dload(r0 + (i_ + S - 2) * 32, NEXT);                        \
-    compute(CUR);                                                                    \
+    frags(CUR);                                                                      \
+    if (more) PPBAR(4 * (S - 2)) else PPBAR(0)                                       \
+    mma();                                                                           \
+    if (more) PPBAR(4 * (S - 2)) else PPBAR(0)                                       \
   }
-  // whole rounds in which every step refills a stage (one back edge, no early
-  // exit: an exit in the middle makes the compiler copy the accumulators),
-  // then the remaining S - 1 .. 2 S - 2 steps
   int kt = 0;
   if constexpr (!SMALL) {
     for (; kt + 2 * S - 2 < nk; kt += S) {
-      G4STEADY(kt, S0, S3) G4STEADY(kt + 1, S1, S0) G4STEADY(kt + 2, S2, S1) G4STEADY(kt + 3, S3, S2)
+      PPSTEADY(kt, S0, S3) PPSTEADY(kt + 1, S1, S0) PPSTEADY(kt + 2, S2, S1) PPSTEADY(kt + 3, S3, S2)
     }
   }
-  if (kt < nk) G4STEP(kt, S0, S3)
-  if (kt + 1 < nk) G4STEP(kt + 1, S1, S0)
-  if (kt + 2 < nk) G4STEP(kt + 2, S2, S1)
-  if (kt + 3 < nk) G4STEP(kt + 3, S3, S2)
-  if (kt + 4 < nk) G4STEP(kt + 4, S0, S3)
-  if (kt + 5 < nk) G4STEP(kt + 5, S1, S0)
-#undef G4STEADY
-#undef G4STEP
+  if (kt < nk) PPSTEP(kt, S0, S3)
+  if (kt + 1 < nk) PPSTEP(kt + 1, S1, S0)
+  if (kt + 2 < nk) PPSTEP(kt + 2, S2, S1)
+  if (kt + 3 < nk) PPSTEP(kt + 3, S3, S2)
+  if (kt + 4 < nk) PPSTEP(kt + 4, S0, S3)
+  if (kt + 5 < nk) PPSTEP(kt + 5, S1, S0)
+  if (!lag) __builtin_amdgcn_s_barrier();
+#undef PPSTEADY
+#undef PPSTEP
+#undef PPBAR
 
   // epilogue.  The products run with the operands swapped, so acc[i][j]
   // holds the transposed 32 x 32 sub-tile: register r of lane l is
