@@ -164,31 +164,57 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
         }
       }
     __syncthreads();
-    // ---- (b) invert the diagonal 32x32 block: wave 0, lane j (and j + 32,
-    // which repeats it) holds column j in registers; pivot column k is
-    // broadcast with scalar lane reads, the pivot row is each lane's own
-    // element.  No LDS traffic and no barrier inside.
+    // ---- (b) invert the diagonal 32x32 block D in place (Gauss-Jordan, no
+    // pivoting) on wave 0: lane (cb, rb) = (lane & 7, lane >> 3) holds the
+    // 4x4 sub-block rows 4rb.., columns 4cb.. in registers.  Step k needs the
+    // pivot column on this lane's rows and the pivot row on its columns, four
+    // values each, fetched from their owners with lane permutes.  With the
+    // pivot column cleared (its diagonal entry set to 1) and multipliers
+    // c_r = D[r][k] (r != k), c_k = p - 1, the step is one uniform rank-1
+    // update D -= c n^T with n_j = D[k][j] / p (j != k), n_k = 1 / p:
+    // rows r != k get D[r][j] - D[r][k] D[k][j] / p and -D[r][k] / p in column
+    // k; row k gets D[k][j] / p and 1 / p.
     if (wave == 0) {
-      const int j = lane & 31;
-      float d[32];
+      const int cb = lane & 7, rb = lane >> 3;
+      float d[4][4];
 #pragma unroll
-      for (int r = 0; r < 32; ++r) d[r] = Prow[r * PR + K0 + j];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        float col[32];
-#pragma unroll
-        for (int r = 0; r < 32; ++r)
-          col[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d[r]), k));
-        const float pinv = 1.0f / col[k];
-        const float nrow = (j == k) ? pinv : d[k] * pinv;
-#pragma unroll
-        for (int r = 0; r < 32; ++r) d[r] = (r == k) ? nrow : ((j == k) ? -col[r] * pinv : d[r] - col[r] * nrow);
+      for (int a = 0; a < 4; ++a) {
+        const float4 v = *reinterpret_cast<const float4*>(&Prow[(4 * rb + a) * PR + K0 + 4 * cb]);
+        d[a][0] = v.x; d[a][1] = v.y; d[a][2] = v.z; d[a][3] = v.w;
       }
-      if (lane < 32) {
+#pragma unroll 1
+      for (int kb = 0; kb < 8; ++kb) {
+        const int srcc = (rb * 8 + kb) * 4, srcr = (kb * 8 + cb) * 4;   // byte lane addresses
 #pragma unroll
-        for (int r = 0; r < 32; r += 4)
-          *reinterpret_cast<float4*>(&DmT[j * PT + r]) = make_float4(d[r], d[r + 1], d[r + 2], d[r + 3]);
+        for (int kc = 0; kc < 4; ++kc) {
+          float col[4], row[4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            col[a] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(srcc, __builtin_bit_cast(int, d[a][kc])));
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            row[c] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(srcr, __builtin_bit_cast(int, d[kc][c])));
+          const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d[kc][kc]), kb * 9));
+          const float pinv = 1.0f / p;
+          float n[4], cm[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) n[c] = (cb == kb && c == kc) ? pinv : row[c] * pinv;
+#pragma unroll
+          for (int a = 0; a < 4; ++a) cm[a] = (rb == kb && a == kc) ? p - 1.0f : col[a];
+          if (cb == kb) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) d[a][kc] = (rb == kb && a == kc) ? 1.0f : 0.0f;
+          }
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) d[a][c] = fmaf(-cm[a], n[c], d[a][c]);
+        }
       }
+      // DmT[j][r] = D^-1[r][j]
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<float4*>(&DmT[(4 * cb + c) * PT + 4 * rb]) = make_float4(d[0][c], d[1][c], d[2][c], d[3][c]);
     }
     __syncthreads();
     // ---- (c) new row panel: A[K, j] <- Dinv A[K, j] (j outside K), A[K, K] <- Dinv.
