@@ -158,7 +158,8 @@ def traffic_from(fetch_dir, write_dir):
             a[key] += v * 1024.0 * k
             a["dispatches_" + key] += 1
             a["kernels"].add(name.split("(")[0])
-    src_files = ["api.hip", "build.hip", "transform.hip", "gemm.hip", "gram.hip", "common.h", "kernels.h"]
+    src_files = ["api.hip", "build.hip", "chain.hip", "transform.hip", "blockdiag.hip", "gemm.hip", "gram.hip",
+                 "merge.hip", "common.h", "kernels.h"]
     h = kernel_source_hash(src_files)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for cls, a in agg.items():
