@@ -13,9 +13,6 @@
 
 namespace poetx {
 
-// orders this wave's LDS accesses (and the compiler's view of them)
-__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 // ----------------------------------------------------------------------------
 // Register-resident blocked Gauss-Jordan, one workgroup per B x B matrix.
 // Wave w owns (32*TR) x (32*TC) of the matrix in MFMA accumulator layout; a
@@ -47,13 +44,24 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
   constexpr int PR = B + 4;    // fp32 row-panel pitch (16-byte rows for vector reads)
   constexpr int PT = 36;       // pitch of the transposed diagonal inverse
   constexpr int HP = 40;       // bf16 operand pitch (32 + 8): conflict-free b128 reads
-  __shared__ float Pcol[X6 ? 1 : B * PC];     // old column panel A[:, K] (fp32 mode)
-  __shared__ __align__(16) float Prow[32 * PR];   // old row panel A[K, :], then the new one
-  __shared__ __align__(16) float DmT[32 * PT];    // inverse of the diagonal block, transposed
-  __shared__ __align__(16) bf16 OpA[X6 ? 3 * B * HP : 2];   // -A[:, K] split h|m|l, [i][kk]
-  __shared__ bf16 OpB[X6 ? 3 * B * HP : 2];   // new A[K, :]^T split h|m|l, [j][kk]
-  static_assert(!(X6 && B == 256) || 3 * B * HP * sizeof(bf16) >= S::NW * 32 * 33 * sizeof(float),
-                "the transposition scratch fits in OpA");
+  // one LDS block, carved below; while A is first formed, its start holds the
+  // generator's packed triangle (the panels are not live yet)
+  constexpr int SZ_OP = X6 ? 3 * B * HP * 2 : 16;
+  constexpr int OFF_OPA = 0, OFF_OPB = SZ_OP, OFF_PROW = 2 * SZ_OP;
+  constexpr int OFF_DMT = OFF_PROW + 32 * PR * 4, OFF_PCOL = OFF_DMT + 32 * PT * 4;
+  constexpr int LDS_BYTES = OFF_PCOL + (X6 ? 16 : B * PC * 4);
+  // X6: the fp32 column panel lives in OpB's space, which is dead from the end
+  // of one panel's update until the new row panel is written
+  static_assert(!X6 || B * PC * 4 <= SZ_OP, "the column panel fits in OpB");
+  constexpr int TRI = B * (B - 1) / 2;                         // generator values per block
+  constexpr bool STAGE_TRI = X6 && TRI * 4 <= OFF_DMT;
+  __shared__ __align__(16) char gj_lds[LDS_BYTES];
+  float* Pcol = reinterpret_cast<float*>(gj_lds + (X6 ? OFF_OPB : OFF_PCOL));   // old column panel A[:, K]
+  float* Prow = reinterpret_cast<float*>(gj_lds + OFF_PROW);  // old row panel A[K, :], then the new one
+  float* DmT = reinterpret_cast<float*>(gj_lds + OFF_DMT);    // inverse of the diagonal block, transposed
+  bf16* OpA = reinterpret_cast<bf16*>(gj_lds + OFF_OPA);      // -A[:, K] split h|m|l, [i][kk]
+  bf16* OpB = reinterpret_cast<bf16*>(gj_lds + OFF_OPB);      // new A[K, :]^T split h|m|l, [j][kk]
+  static_assert(!X6 || B < 256 || STAGE_TRI, "the packed triangle fits in the panel buffers");
 
   int seg = 0;
   while (seg + 1 < g.nseg && (int)blockIdx.x >= g.start[seg + 1]) ++seg;
@@ -74,42 +82,32 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
   };
 
   f32x16 acc[TR][TC];
-  if (sg.theta && X6 && B == 256) {
-    // ---- A = I - S from the stored strict upper triangle with row-contiguous
-    // reads: tiles on or above the diagonal read their rows of the triangle
-    // (A = -theta above the diagonal); a tile below it reads its mirror tile
-    // (rows J0.., columns I0..) the same way and transposes it through this
-    // wave's LDS scratch (A[i][j] = theta(j, i)).  The diagonal tiles read
-    // their lower halves directly.
-    const float* th = sg.theta + (int64_t)blk * (B * (B - 1) / 2);
-    auto tri = [&](int i, int j) { return th[i * B - i * (i + 1) / 2 + (j - i - 1)]; };   // theta(i, j), i < j
-    float* scr = reinterpret_cast<float*>(OpA) + wave * (32 * 33);
+  if (sg.theta && STAGE_TRI) {
+    // ---- A = I - S: the packed strict upper triangle (row-major, theta(i, j)
+    // at i B - i (i + 1) / 2 + j - i - 1) is copied to LDS with coalesced
+    // loads, then every wave reads its tiles' entries from there:
+    // A[i][j] = -theta(i, j) above the diagonal, theta(j, i) below it.
+    const float* th = sg.theta + (int64_t)blk * TRI;
+    float* T = reinterpret_cast<float*>(gj_lds);
+    if ((reinterpret_cast<uintptr_t>(th) & 15) == 0) {
+      for (int e = tid; e < TRI / 4; e += NT)
+        reinterpret_cast<float4*>(T)[e] = reinterpret_cast<const float4*>(th)[e];
+      for (int e = (TRI / 4) * 4 + tid; e < TRI; e += NT) T[e] = th[e];
+    } else {
+      for (int e = tid; e < TRI; e += NT) T[e] = th[e];
+    }
+    __syncthreads();
 #pragma unroll
     for (int ti = 0; ti < TR; ++ti)
 #pragma unroll
-      for (int tj = 0; tj < TC; ++tj) {
-        const int I0 = tr + 32 * ti, J0 = tc + 32 * tj;
-        if (J0 > I0) {
+      for (int tj = 0; tj < TC; ++tj)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[ti][tj][r] = -tri(I0 + c32_row(lane, r), J0 + lc);
-        } else if (J0 == I0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I0 + c32_row(lane, r), j = J0 + lc;
-            acc[ti][tj][r] = i == j ? 1.0f : (i < j ? -tri(i, j) : tri(j, i));
-          }
-        } else {
-          float m[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) m[r] = tri(J0 + c32_row(lane, r), I0 + lc);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) scr[c32_row(lane, r) * 33 + lc] = m[r];
-          lds_wave_fence();
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[ti][tj][r] = scr[lc * 33 + c32_row(lane, r)];
-          lds_wave_fence();
+        for (int r = 0; r < 16; ++r) {
+          const int i = tr + 32 * ti + c32_row(lane, r), j = tc + 32 * tj + lc;
+          const int lo = min(i, j), hi = max(i, j);
+          const float v = T[lo * B - lo * (lo + 1) / 2 + (hi - lo - 1)];
+          acc[ti][tj][r] = i == j ? 1.0f : (i < j ? -v : v);
         }
-      }
     __syncthreads();
   } else {
     // ---- A = I - S (theta mode) or A from a strided matrix, element by element
@@ -146,16 +144,7 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = I0 + c32_row(lane, r);
-            const float v = acc[ti][tj][r];
-            if constexpr (X6) {
-              bf16 h, m, l;
-              split3(-v, h, m, l);
-              OpA[i * HP + lc] = h;
-              OpA[B * HP + i * HP + lc] = m;
-              OpA[2 * B * HP + i * HP + lc] = l;
-            } else {
-              Pcol[i * PC + lc] = v;
-            }
+            Pcol[i * PC + lc] = acc[ti][tj][r];
           }
         }
         if (I0 == K0) {
@@ -216,6 +205,29 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<float4*>(&DmT[(4 * cb + c) * PT + 4 * rb]) = make_float4(d[0][c], d[1][c], d[2][c], d[3][c]);
     }
+    // meanwhile the other waves (wave 0 too when it is the only one) split the
+    // column panel: OpA[q][i][kk] = piece q of -A[i, K0 + kk], eight k per
+    // 16-byte write
+    if constexpr (X6) {
+      const int nh = NT > 64 ? NT - 64 : NT, h0 = NT > 64 ? tid - 64 : tid;
+      for (int e = h0; e >= 0 && e < B * 4; e += nh) {
+        const int i = e >> 2, k8 = (e & 3) * 8;
+        uint16_t pc[3][8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          bf16 hh, mm, ll;
+          split3(-Pcol[i * PC + k8 + t], hh, mm, ll);
+          pc[0][t] = __builtin_bit_cast(uint16_t, hh);
+          pc[1][t] = __builtin_bit_cast(uint16_t, mm);
+          pc[2][t] = __builtin_bit_cast(uint16_t, ll);
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          *reinterpret_cast<uint4*>(&OpA[q * B * HP + i * HP + k8]) =
+              make_uint4(pack2(pc[q][0], pc[q][1]), pack2(pc[q][2], pc[q][3]), pack2(pc[q][4], pc[q][5]),
+                         pack2(pc[q][6], pc[q][7]));
+      }
+    }
     __syncthreads();
     // ---- (c) new row panel: A[K, j] <- Dinv A[K, j] (j outside K), A[K, K] <- Dinv.
     // Each thread owns RB rows x CB columns of the 32 x B panel.
@@ -256,20 +268,36 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
           for (int cb = 0; cb < CB; ++cb) nv[rb][cb] = DmT[(cg * CB + cb - K0) * PT + rg * RB + rb];
       }
       __syncthreads();
+      // Prow rows as 16-byte writes; OpB as RB consecutive k of one column
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
+        *reinterpret_cast<float4*>(&Prow[(rg * RB + rb) * PR + cg * CB]) =
+            make_float4(nv[rb][0], nv[rb][1], nv[rb][2], nv[rb][3]);
+      if constexpr (X6) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const int kk = rg * RB + rb, jj = cg * CB + cb;
-          Prow[kk * PR + jj] = nv[rb][cb];
-          if constexpr (X6) {
+          uint16_t hm[3][RB];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
             bf16 hh, mm, ll;
             split3(nv[rb][cb], hh, mm, ll);
-            OpB[jj * HP + kk] = hh;
-            OpB[B * HP + jj * HP + kk] = mm;
-            OpB[2 * B * HP + jj * HP + kk] = ll;
+            hm[0][rb] = __builtin_bit_cast(uint16_t, hh);
+            hm[1][rb] = __builtin_bit_cast(uint16_t, mm);
+            hm[2][rb] = __builtin_bit_cast(uint16_t, ll);
+          }
+          const int o = (cg * CB + cb) * HP + rg * RB;
+#pragma unroll
+          for (int q = 0; q < 3; ++q) {
+            bf16* dst = &OpB[q * B * HP + o];
+            if constexpr (RB == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(hm[q][0], hm[q][1]), pack2(hm[q][2], hm[q][3]));
+            else if constexpr (RB == 2) *reinterpret_cast<uint32_t*>(dst) = pack2(hm[q][0], hm[q][1]);
+            else {
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb) reinterpret_cast<uint16_t*>(dst)[rb] = hm[q][rb];
+            }
           }
         }
+      }
       __syncthreads();
     }
     // ---- (d) update every tile.  Rows outside K: A[i, j] -= A[i, K] newrow[K, j],
