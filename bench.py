@@ -333,12 +333,13 @@ class Stack:
             self.bwd_ready = torch.cuda.Event()
             self.workers = [main] + [torch.cuda.Stream() for _ in range(self.nstreams - 1)]
         # the backward blocks depend only on the generators: build them on a
-        # second stream while the forward pass runs
+        # second stream while the forward pass runs (enqueued after the forward
+        # build, so that build gets the CUs first)
         self.side.wait_stream(main)
+        P.build_layer_blocks(self.layers, "forward")
         with torch.cuda.stream(self.side):
             P.build_layer_blocks(self.layers, "backward")
             self.bwd_ready.record(self.side)
-        P.build_layer_blocks(self.layers, "forward")
         n = len(self.layers)
         self._fan_out(main, [(i, (self.layers[i], self.out[i])) for i in range(n)],
                       lambda lay, o: lay.forward_blocks(self.X[lay.x_key], Y=o["Y"]))
@@ -511,10 +512,12 @@ def main():
         # right after its dL/dQ (--chain per-matrix)
         bs = active["side"]
         bs.wait_stream(stream)
+        # the forward build is enqueued first, so its workgroups take the CUs
+        # before the backward build's
+        P.build_layer_blocks(layers, "forward")
         with torch.cuda.stream(bs):
             P.build_layer_blocks(layers, "backward")
             bwd_blocks_ready.record(bs)
-        P.build_layer_blocks(layers, "forward")
         fan_out(list(zip(layers, outs)), lambda lay, o: lay.forward_blocks(Xs[lay.x_key], Y=o["Y"]))
         stream.wait_event(bwd_blocks_ready)
         def bwd(lay, g, o):

@@ -31,9 +31,9 @@ __device__ __forceinline__ void g2l16(const void* g, void* lds_base) {
 
 constexpr int PERM_THREADS = 256;
 
-// rows per workgroup: as many as fit in 64 KiB of LDS, at most 16
+// rows per workgroup: as many as fit in 32 KiB of LDS, at most 16
 static int perm_rows(int W) {
-  int r = 32768 / (W > 0 ? W : 1);
+  int r = 16384 / (W > 0 ? W : 1);
   return r < 1 ? 1 : (r > 16 ? 16 : r);
 }
 
