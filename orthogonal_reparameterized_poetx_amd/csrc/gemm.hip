@@ -396,6 +396,254 @@ __global__ __launch_bounds__(256) void gemm_bf16_generic_kernel(GemmArgs g) {
   if (gm < M && gn < N) C[(int64_t)gm * g.ldc + gn] = f32_to_bits(s);
 }
 
+// NT for long K (a multiple of 64): the same ping-pong schedule with A
+// through the 4-stage ring of 32-deep steps and B through a 3-stage ring of
+// 64-deep stages ([256 rows][64 k], 128-byte rows, chunk c of row r at
+// c ^ ((r >> 1) & 7)), so that each B load instruction covers 8 whole
+// 128-byte row segments instead of 16 half ones (half the L2 requests for B).
+// The two rings fill 160 KiB of LDS.  Step t reads A stage t % 4 and half
+// t % 2 of B stage (t / 2) % 3; every step refills one A stage (chunk t + 3),
+// every even step one B stage (stage t / 2 + 2).  k is summed in the same
+// order as in the kernel above, so the results are identical.
+__global__ __launch_bounds__(512) void gemm_ntw_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
+  __shared__ __align__(16) uint16_t A0[8192], A1[8192], A2[8192], A3[8192];
+  __shared__ __align__(16) uint16_t B0[16384], B1[16384], B2[16384];
+  const int d = blockIdx.x;
+  const int per = (ntiles + 7) / 8;
+  const int tile = (d % 8) * per + d / 8;
+  if (tile >= ntiles) return;
+  const int tpb = tiles_m * tiles_n;
+  const int bz = tile / tpb, rem = tile - bz * tpb;
+  const int bm = rem / tiles_n, bn = rem - bm * tiles_n;
+  const int m0 = bm * GBM, n0 = bn * GBN;
+  const int M = g.M, N = g.N, K = g.K;
+  const uint16_t* __restrict__ A = g.A + bz * g.sA;
+  const uint16_t* __restrict__ Bm = g.B + bz * g.sB;
+  uint16_t* __restrict__ C = g.C + bz * g.sC;
+  const int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * lda, (int64_t)min(M - m0, GBM) * lda * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + (int64_t)n0 * ldb, (int64_t)min(N - n0, GBN) * ldb * 2);
+  int voa[2], vob[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = (wave * 2 + q) * 16 + (lane >> 2);
+    const int cs = (lane & 3) ^ ((r >> 2) & 3);
+    voa[q] = (int)(((int64_t)r * lda + cs * 8) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (wave * 4 + q) * 8 + (lane >> 3);
+    const int cs = (lane & 7) ^ ((r >> 1) & 7);
+    vob[q] = (int)(((int64_t)r * ldb + cs * 8) * 2);
+  }
+  const int nk = K / 32, np = K / 64;
+  auto dloadA = [&](int c, uint16_t* st) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) b2l16(ra, voa[q], c * 64, st + (wave * 2 + q) * 512);
+  };
+  auto dloadB = [&](int p, uint16_t* st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b2l16(rb, vob[q], p * 128, st + (wave * 4 + q) * 512);
+  };
+  bf16x8 AF[2][4], BF[2][2];
+  uint32_t fa[2], fb[2][2];
+  {
+    const int l32 = lane & 31, h = lane >> 5, sw = (l32 >> 2) & 3, swb = (l32 >> 1) & 7;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) fa[s] = (uint32_t)((wm * 128 + l32) * 64 + (((2 * s + h) ^ sw) << 4));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        fb[hf][s] = (uint32_t)((wn * 64 + l32) * 128 + ((((hf << 2) | (s << 1) | h) ^ swb) << 4));
+  }
+  auto frags = [&](const uint16_t* sta, const uint16_t* stb, int hf) {
+    typedef int pi32x4 __attribute__((ext_vector_type(4)));
+    const uint32_t sa = (uint32_t)reinterpret_cast<uintptr_t>(sta);
+    const uint32_t sb = (uint32_t)reinterpret_cast<uintptr_t>(stb);
+    const uint32_t a0 = sa + fa[0], a1 = sa + fa[1], b0 = sb + fb[hf][0], b1 = sb + fb[hf][1];
+    pi32x4 x[8], y[4];
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
+        "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %12 offset:6144\n\t"
+        "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:2048\n\t"
+        "ds_read_b128 %6, %13 offset:4096\n\tds_read_b128 %7, %13 offset:6144\n\t"
+        "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:4096\n\t"
+        "ds_read_b128 %10, %15\n\tds_read_b128 %11, %15 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+          "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
+        : "memory");
+    BF[0][0] = __builtin_bit_cast(bf16x8, y[0]);
+    BF[0][1] = __builtin_bit_cast(bf16x8, y[1]);
+    BF[1][0] = __builtin_bit_cast(bf16x8, y[2]);
+    BF[1][1] = __builtin_bit_cast(bf16x8, y[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      AF[0][i] = __builtin_bit_cast(bf16x8, x[i]);
+      AF[1][i] = __builtin_bit_cast(bf16x8, x[4 + i]);
+    }
+  };
+  auto mma = [&]() {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(BF[s][j], AF[s][i], acc[i][j]);
+    }
+  };
+  // loads issued by this wave after A chunk t + 1, at the barriers of step t
+  // (B stage (t + 1) / 2 is issued before that chunk): the refills of steps
+  // t - 1 and t, and for t = 0 the prologue's B stage 1 and A chunk 2
+  auto issued_after = [&](int t) {
+    if (t + 1 >= nk) return 0;
+    int n = t == 0 ? 6 : 0;
+#pragma unroll
+    for (int s = t - 1; s <= t; ++s)
+      if (s >= 0) n += 2 * (s + 3 < nk) + 4 * ((s & 1) == 0 && s / 2 + 2 < np);
+    return n;
+  };
+  // prologue: A chunk 0, B stage 0, A chunk 1, B stage 1, A chunk 2
+  dloadA(0, A0);
+  asm volatile("" ::: "memory");
+  dloadB(0, B0);
+  asm volatile("" ::: "memory");
+  dloadA(1, A1);
+  asm volatile("" ::: "memory");
+  dloadB(1, B1);
+  asm volatile("" ::: "memory");
+  if (2 < nk) dloadA(2, A2);
+  asm volatile("" ::: "memory");
+  const bool lag = wave >= 4;
+#define PPBAR(VM)                                                                    \
+  {                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                               \
+    asm volatile("" ::: "memory");                                                   \
+    __builtin_amdgcn_s_waitcnt(vm_imm(VM));                                          \
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                               \
+    __builtin_amdgcn_s_barrier();                                                    \
+    asm volatile("" ::: "memory");                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                               \
+  }
+#define PPBARN(N_)                                                                   \
+  {                                                                                  \
+    const int n_ = (N_);                                                             \
+    if (n_ >= 12) PPBAR(12) else if (n_ >= 10) PPBAR(10) else if (n_ >= 8) PPBAR(8)  \
+    else if (n_ >= 6) PPBAR(6) else if (n_ >= 4) PPBAR(4) else if (n_ >= 2) PPBAR(2) \
+    else PPBAR(0)                                                                    \
+  }
+  // chunk 0 and B stage 0: issued after them, A chunk 1, B stage 1, A chunk 2
+  PPBARN(2 + 4 + 2 * (2 < nk))
+  if (lag) __builtin_amdgcn_s_barrier();
+  // step T (static stage names): A stage AC, refill AN with chunk T + 3; B
+  // stage BC half HF; on even steps refill BN with B stage T / 2 + 2
+#define PPSTEADY(T, AC, AN, BC, HF, BN)                                              \
+  {                                                                                  \
+    if ((HF) == 0) dloadB((T) / 2 + 2, BN);                                          \
+    asm volatile("" ::: "memory");                                                   \
+    dloadA((T) + 3, AN);                                                             \
+    asm volatile("" ::: "memory");                                                   \
+    frags(AC, BC, HF);                                                               \
+    PPBAR(8)                                                                         \
+    mma();                                                                           \
+    PPBAR(8)                                                                         \
+  }
+#define PPSTEP(T, AC, AN, BC, HF, BN)                                                \
+  {                                                                                  \
+    const int t_ = (T);                                                              \
+    if ((HF) == 0 && t_ / 2 + 2 < np) dloadB(t_ / 2 + 2, BN);                        \
+    asm volatile("" ::: "memory");                                                   \
+    if (t_ + 3 < nk) dloadA(t_ + 3, AN);                                             \
+    asm volatile("" ::: "memory");                                                   \
+    frags(AC, BC, HF);                                                               \
+    const int w_ = issued_after(t_);                                                 \
+    PPBARN(w_)                                                                       \
+    mma();                                                                           \
+    PPBARN(w_)                                                                       \
+  }
+#define PPGROUP(M, O)                                                                \
+  M((O) + 0, A0, A3, B0, 0, B2) M((O) + 1, A1, A0, B0, 1, B2)                        \
+  M((O) + 2, A2, A1, B1, 0, B0) M((O) + 3, A3, A2, B1, 1, B0)                        \
+  M((O) + 4, A0, A3, B2, 0, B1) M((O) + 5, A1, A0, B2, 1, B1)                        \
+  M((O) + 6, A2, A1, B0, 0, B2) M((O) + 7, A3, A2, B0, 1, B2)                        \
+  M((O) + 8, A0, A3, B1, 0, B0) M((O) + 9, A1, A0, B1, 1, B0)                        \
+  M((O) + 10, A2, A1, B2, 0, B1) M((O) + 11, A3, A2, B2, 1, B1)
+#define GSTEP(T, AC, AN, BC, HF, BN) if ((T) < nk) PPSTEP(T, AC, AN, BC, HF, BN)
+  // steps 0..11 (guarded), whole groups of 12 whose every refill happens,
+  // then the last 12..14 steps (guarded)
+  PPGROUP(GSTEP, 0)
+  int t0 = 12;
+  for (; t0 + 14 < nk; t0 += 12) { PPGROUP(PPSTEADY, t0) }
+  PPGROUP(GSTEP, t0)
+  GSTEP(t0 + 12, A0, A3, B0, 0, B2)
+  GSTEP(t0 + 13, A1, A0, B0, 1, B2)
+  if (!lag) __builtin_amdgcn_s_barrier();
+#undef PPSTEADY
+#undef PPSTEP
+#undef PPBAR
+#undef PPBARN
+#undef PPGROUP
+#undef GSTEP
+  // epilogue as in the kernel above; each wave stages its 128 x 64 tile
+  // (16 KiB) in one A stage or in half of a B stage
+  {
+    __syncthreads();
+    uint16_t* st = wave == 0 ? A0 : wave == 1 ? A1 : wave == 2 ? A2 : wave == 3 ? A3
+                 : (wave < 6 ? B0 : B1) + (wave & 1) * (128 * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[i][j];
+          const int chunk = j * 4 + q, half = lane >> 5;
+          const int off = row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3) + ((half ^ ((row >> 4) & 1)) << 2);
+          uint2 v;
+          v.x = pack2(f32_to_bits(a[4 * q]), f32_to_bits(a[4 * q + 1]));
+          v.y = pack2(f32_to_bits(a[4 * q + 2]), f32_to_bits(a[4 * q + 3]));
+          *reinterpret_cast<uint2*>(st + off) = v;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const bool vec = (ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int e = it * 64 + lane;
+      const int row = e >> 3, chunk = e & 7;
+      uint4 v = *reinterpret_cast<const uint4*>(st + row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3));
+      if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      const int gm = m0 + wm * 128 + row, gn = n0 + wn * 64 + chunk * 8;
+      if (gm < M && gn < N) {
+        uint16_t* cp = C + (int64_t)gm * ldc + gn;
+        if (vec) *reinterpret_cast<uint4*>(cp) = v;
+        else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2)
+            if (gn + e2 < N) cp[e2] = (uint16_t)(w[e2 >> 1] >> (16 * (e2 & 1)));
+        }
+      }
+    }
+  }
+}
+
 static bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
@@ -412,7 +660,11 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     if (small) hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
     else hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
   }
+    // measured: 8192 x 2048 x 5632 in 145-150 instead of 159-165 us; no gain
+    // for K = 2048
+    const bool wide = !nn && g.batch == 1 && g.K % 64 == 0 && g.K >= 4096;
     if (nn) GEMM_LAUNCH(true, false)
+    else if (wide) hipLaunchKernelGGL(gemm_ntw_kernel, dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
     else if (g.batch > 1) GEMM_LAUNCH(false, true)
     else GEMM_LAUNCH(false, false)
 #undef GEMM_LAUNCH
