@@ -43,7 +43,8 @@ KERNEL_CLASSES = [
     ("blockdiag_kernel", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, true,", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, false,", "gemm_nt", 1),
-    ("gemm_ntw_kernel", "gemm_nt", 1),
+    ("gemm_wide_kernel<false>", "gemm_nt", 1),
+    ("gemm_wide_kernel<true>", "gemm_nn", 1),
     ("gemm_bf16_kernel<true, false,", "gemm_nn", 1),
     ("chain_product_kernel", "chain_rule", 3),
     ("skew_project_kernel", "chain_rule", 3),

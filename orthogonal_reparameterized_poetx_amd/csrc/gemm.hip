@@ -396,18 +396,23 @@ __global__ __launch_bounds__(256) void gemm_bf16_generic_kernel(GemmArgs g) {
   if (gm < M && gn < N) C[(int64_t)gm * g.ldc + gn] = f32_to_bits(s);
 }
 
-// NT for long K (a multiple of 64): the same ping-pong schedule with A
-// through the 4-stage ring of 32-deep steps and B through a 3-stage ring of
-// 64-deep stages ([256 rows][64 k], 128-byte rows, chunk c of row r at
-// c ^ ((r >> 1) & 7)), so that each B load instruction covers 8 whole
-// 128-byte row segments instead of 16 half ones (half the L2 requests for B).
-// The two rings fill 160 KiB of LDS.  Step t reads A stage t % 4 and half
-// t % 2 of B stage (t / 2) % 3; every step refills one A stage (chunk t + 3),
-// every even step one B stage (stage t / 2 + 2).  k is summed in the same
+// K >= 2048 (a multiple of 64): the same ping-pong schedule with the operand
+// whose tile rows are 64-byte segments in the 32-deep ring (A of NT) moved
+// to a 3-stage ring of 64-deep stages ([256 rows][64 k], 128-byte rows, chunk
+// c of row r at c ^ ((r >> 1) & 7)), so that each of its load instructions
+// covers 8 whole 128-byte row segments instead of 16 half ones (half the L2
+// requests for that operand).  NT: B takes the 64-deep ring, A keeps a 4-stage
+// ring of 32-deep steps; NN: A takes the 64-deep ring, B (512-byte rows
+// already) keeps the 32-deep ring.  The rings fill 160 KiB of LDS.  Step t
+// reads stage t % 4 of the 32-deep ring and half t % 2 of stage (t / 2) % 3 of
+// the 64-deep ring; every step refills one 32-deep stage (chunk t + 3), every
+// even step one 64-deep stage (stage t / 2 + 2).  k is summed in the same
 // order as in the kernel above, so the results are identical.
-__global__ __launch_bounds__(512) void gemm_ntw_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
-  __shared__ __align__(16) uint16_t A0[8192], A1[8192], A2[8192], A3[8192];
-  __shared__ __align__(16) uint16_t B0[16384], B1[16384], B2[16384];
+template <bool NN>
+__global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
+  // R0..R3: the 32-deep ring (16 KiB stages); W0..W2: the 64-deep ring
+  __shared__ __align__(16) uint16_t R0[8192], R1[8192], R2[8192], R3[8192];
+  __shared__ __align__(16) uint16_t W0[16384], W1[16384], W2[16384];
   const int d = blockIdx.x;
   const int per = (ntiles + 7) / 8;
   const int tile = (d % 8) * per + d / 8;
@@ -435,63 +440,129 @@ __global__ __launch_bounds__(512) void gemm_ntw_kernel(GemmArgs g, int tiles_m, 
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * lda, (int64_t)min(M - m0, GBM) * lda * 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + (int64_t)n0 * ldb, (int64_t)min(N - n0, GBN) * ldb * 2);
-  int voa[2], vob[4];
+  const __amdgpu_buffer_rsrc_t rb = NN ? make_rsrc(Bm + n0, ((int64_t)K * ldb - n0) * 2)
+                                       : make_rsrc(Bm + (int64_t)n0 * ldb, (int64_t)min(N - n0, GBN) * ldb * 2);
+  // per-lane source offsets.  32-deep ring, instruction q (0, 1) of wave w
+  // fills KiB 2 w + q of a stage: NT A [256 rows][32 k] (chunk c of row r at
+  // c ^ ((r >> 2) & 3)), NN B [32 k rows][256 n] (chunk c of row r at
+  // c ^ ((r & 3) << 2)).  64-deep ring, instruction q (0..3) fills KiB 4 w + q.
+  int von[2], vow[4];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int r = (wave * 2 + q) * 16 + (lane >> 2);
-    const int cs = (lane & 3) ^ ((r >> 2) & 3);
-    voa[q] = (int)(((int64_t)r * lda + cs * 8) * 2);
+    if constexpr (!NN) {
+      const int r = (wave * 2 + q) * 16 + (lane >> 2);
+      const int cs = (lane & 3) ^ ((r >> 2) & 3);
+      von[q] = (int)(((int64_t)r * lda + cs * 8) * 2);
+    } else {
+      const int kr = (wave * 2 + q) * 2 + (lane >> 5);
+      const int cn = (lane & 31) ^ ((kr & 3) << 2);
+      von[q] = (int)(((int64_t)kr * ldb + cn * 8) * 2);
+    }
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = (wave * 4 + q) * 8 + (lane >> 3);
     const int cs = (lane & 7) ^ ((r >> 1) & 7);
-    vob[q] = (int)(((int64_t)r * ldb + cs * 8) * 2);
+    vow[q] = (int)(((int64_t)r * (NN ? lda : ldb) + cs * 8) * 2);
   }
   const int nk = K / 32, np = K / 64;
-  auto dloadA = [&](int c, uint16_t* st) {
+  // chunk c (k in [32 c, 32 c + 32)) into a 32-deep stage; the NN B operand
+  // adds its k position to the range-checked per-lane offset
+  auto dloadN = [&](int c, uint16_t* st) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) b2l16(ra, voa[q], c * 64, st + (wave * 2 + q) * 512);
+    for (int q = 0; q < 2; ++q) {
+      if constexpr (!NN) b2l16(ra, von[q], c * 64, st + (wave * 2 + q) * 512);
+      else b2l16(rb, von[q] + (int)((int64_t)c * 32 * ldb * 2), 0, st + (wave * 2 + q) * 512);
+    }
   };
-  auto dloadB = [&](int p, uint16_t* st) {
+  // stage p (k in [64 p, 64 p + 64)) into a 64-deep stage
+  auto dloadW = [&](int p, uint16_t* st) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) b2l16(rb, vob[q], p * 128, st + (wave * 4 + q) * 512);
+    for (int q = 0; q < 4; ++q) b2l16(NN ? ra : rb, vow[q], p * 128, st + (wave * 4 + q) * 512);
   };
   bf16x8 AF[2][4], BF[2][2];
-  uint32_t fa[2], fb[2][2];
+  // loop-invariant byte offsets of this lane's fragment reads: fn[s] in a
+  // 32-deep stage (NT A, or NN B for tile j = s), fw[hf][s] in half hf of a
+  // 64-deep stage
+  uint32_t fn[2], fw[2][2];
   {
-    const int l32 = lane & 31, h = lane >> 5, sw = (l32 >> 2) & 3, swb = (l32 >> 1) & 7;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) fa[s] = (uint32_t)((wm * 128 + l32) * 64 + (((2 * s + h) ^ sw) << 4));
+    const int l32 = lane & 31, h = lane >> 5, swb = (l32 >> 1) & 7;
+    const int wrow = NN ? wm * 128 : wn * 64;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        fb[hf][s] = (uint32_t)((wn * 64 + l32) * 128 + ((((hf << 2) | (s << 1) | h) ^ swb) << 4));
+        fw[hf][s] = (uint32_t)((wrow + l32) * 128 + ((((hf << 2) | (s << 1) | h) ^ swb) << 4));
+    if constexpr (!NN) {
+      const int sw = (l32 >> 2) & 3;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) fn[s] = (uint32_t)((wm * 128 + l32) * 64 + (((2 * s + h) ^ sw) << 4));
+    } else {
+      const int gq = lane >> 4, q = lane & 15;
+      const int kr0 = 8 * (gq >> 1) + (q >> 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ncol = wn * 64 + j * 32 + 16 * (gq & 1) + 4 * (q & 3);
+        const int chn = ncol >> 3, within = ncol & 7;
+        fn[j] = (uint32_t)(2 * (kr0 * 256 + ((chn ^ ((kr0 & 3) << 2)) << 3) + within));
+      }
+    }
   }
-  auto frags = [&](const uint16_t* sta, const uint16_t* stb, int hf) {
+  // fragments of step t from 32-deep stage stn and half hf of 64-deep stage
+  // stw, one asm block that waits for its own reads
+  auto frags = [&](const uint16_t* stn, const uint16_t* stw, int hf) {
     typedef int pi32x4 __attribute__((ext_vector_type(4)));
-    const uint32_t sa = (uint32_t)reinterpret_cast<uintptr_t>(sta);
-    const uint32_t sb = (uint32_t)reinterpret_cast<uintptr_t>(stb);
-    const uint32_t a0 = sa + fa[0], a1 = sa + fa[1], b0 = sb + fb[hf][0], b1 = sb + fb[hf][1];
-    pi32x4 x[8], y[4];
-    asm volatile(
-        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
-        "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %12 offset:6144\n\t"
-        "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:2048\n\t"
-        "ds_read_b128 %6, %13 offset:4096\n\tds_read_b128 %7, %13 offset:6144\n\t"
-        "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:4096\n\t"
-        "ds_read_b128 %10, %15\n\tds_read_b128 %11, %15 offset:4096\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
-          "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
-        : "memory");
-    BF[0][0] = __builtin_bit_cast(bf16x8, y[0]);
-    BF[0][1] = __builtin_bit_cast(bf16x8, y[1]);
-    BF[1][0] = __builtin_bit_cast(bf16x8, y[2]);
-    BF[1][1] = __builtin_bit_cast(bf16x8, y[3]);
+    typedef int pi32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t sn = (uint32_t)reinterpret_cast<uintptr_t>(stn);
+    const uint32_t sw = (uint32_t)reinterpret_cast<uintptr_t>(stw);
+    pi32x4 x[8];
+    if constexpr (!NN) {
+      const uint32_t a0 = sn + fn[0], a1 = sn + fn[1], b0 = sw + fw[hf][0], b1 = sw + fw[hf][1];
+      pi32x4 y[4];
+      asm volatile(
+          "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
+          "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %12 offset:6144\n\t"
+          "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:2048\n\t"
+          "ds_read_b128 %6, %13 offset:4096\n\tds_read_b128 %7, %13 offset:6144\n\t"
+          "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:4096\n\t"
+          "ds_read_b128 %10, %15\n\tds_read_b128 %11, %15 offset:4096\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+            "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
+          : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
+          : "memory");
+      BF[0][0] = __builtin_bit_cast(bf16x8, y[0]);
+      BF[0][1] = __builtin_bit_cast(bf16x8, y[1]);
+      BF[1][0] = __builtin_bit_cast(bf16x8, y[2]);
+      BF[1][1] = __builtin_bit_cast(bf16x8, y[3]);
+    } else {
+      // A: 32-row tiles 4096 bytes apart; B: j = 0 from b0, j = 1 from b1, k
+      // sub-step s at +8192, half hh at +2048
+      const uint32_t a0 = sw + fw[hf][0], a1 = sw + fw[hf][1], b0 = sn + fn[0], b1 = sn + fn[1];
+      pi32x2 y[8];
+      asm volatile(
+          "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:4096\n\t"
+          "ds_read_b128 %2, %16 offset:8192\n\tds_read_b128 %3, %16 offset:12288\n\t"
+          "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:4096\n\t"
+          "ds_read_b128 %6, %17 offset:8192\n\tds_read_b128 %7, %17 offset:12288\n\t"
+          "ds_read_b64_tr_b16 %8, %18\n\tds_read_b64_tr_b16 %9, %18 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %10, %18 offset:8192\n\tds_read_b64_tr_b16 %11, %18 offset:10240\n\t"
+          "ds_read_b64_tr_b16 %12, %19\n\tds_read_b64_tr_b16 %13, %19 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %14, %19 offset:8192\n\tds_read_b64_tr_b16 %15, %19 offset:10240\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+            "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]), "=&v"(y[6]), "=&v"(y[7])
+          : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
+          : "memory");
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const pi32x2 lo = y[4 * j + 2 * s], hi = y[4 * j + 2 * s + 1];
+          const pi32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+          BF[s][j] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       AF[0][i] = __builtin_bit_cast(bf16x8, x[i]);
@@ -507,9 +578,10 @@ __global__ __launch_bounds__(512) void gemm_ntw_kernel(GemmArgs g, int tiles_m, 
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(BF[s][j], AF[s][i], acc[i][j]);
     }
   };
-  // loads issued by this wave after A chunk t + 1, at the barriers of step t
-  // (B stage (t + 1) / 2 is issued before that chunk): the refills of steps
-  // t - 1 and t, and for t = 0 the prologue's B stage 1 and A chunk 2
+  // loads issued by this wave after chunk t + 1 of the 32-deep ring, at the
+  // barriers of step t (64-deep stage (t + 1) / 2 is issued before that
+  // chunk): the refills of steps t - 1 and t, and for t = 0 the prologue's
+  // 64-deep stage 1 and chunk 2
   auto issued_after = [&](int t) {
     if (t + 1 >= nk) return 0;
     int n = t == 0 ? 6 : 0;
@@ -518,16 +590,16 @@ __global__ __launch_bounds__(512) void gemm_ntw_kernel(GemmArgs g, int tiles_m, 
       if (s >= 0) n += 2 * (s + 3 < nk) + 4 * ((s & 1) == 0 && s / 2 + 2 < np);
     return n;
   };
-  // prologue: A chunk 0, B stage 0, A chunk 1, B stage 1, A chunk 2
-  dloadA(0, A0);
+  // prologue: chunk 0, 64-deep stage 0, chunk 1, 64-deep stage 1, chunk 2
+  dloadN(0, R0);
   asm volatile("" ::: "memory");
-  dloadB(0, B0);
+  dloadW(0, W0);
   asm volatile("" ::: "memory");
-  dloadA(1, A1);
+  dloadN(1, R1);
   asm volatile("" ::: "memory");
-  dloadB(1, B1);
+  dloadW(1, W1);
   asm volatile("" ::: "memory");
-  if (2 < nk) dloadA(2, A2);
+  dloadN(2, R2);
   asm volatile("" ::: "memory");
   const bool lag = wave >= 4;
 #define PPBAR(VM)                                                                    \
@@ -547,51 +619,52 @@ __global__ __launch_bounds__(512) void gemm_ntw_kernel(GemmArgs g, int tiles_m, 
     else if (n_ >= 6) PPBAR(6) else if (n_ >= 4) PPBAR(4) else if (n_ >= 2) PPBAR(2) \
     else PPBAR(0)                                                                    \
   }
-  // chunk 0 and B stage 0: issued after them, A chunk 1, B stage 1, A chunk 2
-  PPBARN(2 + 4 + 2 * (2 < nk))
+  // chunk 0 and 64-deep stage 0; issued after them: chunk 1, stage 1, chunk 2
+  PPBAR(8)
   if (lag) __builtin_amdgcn_s_barrier();
-  // step T (static stage names): A stage AC, refill AN with chunk T + 3; B
-  // stage BC half HF; on even steps refill BN with B stage T / 2 + 2
-#define PPSTEADY(T, AC, AN, BC, HF, BN)                                              \
+  // step T (static stage names): 32-deep stage NC, refill NR with chunk
+  // T + 3; half HF of 64-deep stage WC; on even steps refill WR with 64-deep
+  // stage T / 2 + 2
+#define PPSTEADY(T, NC, NR, WC, HF, WR)                                              \
   {                                                                                  \
-    if ((HF) == 0) dloadB((T) / 2 + 2, BN);                                          \
+    if ((HF) == 0) dloadW((T) / 2 + 2, WR);                                          \
     asm volatile("" ::: "memory");                                                   \
-    dloadA((T) + 3, AN);                                                             \
+    dloadN((T) + 3, NR);                                                             \
     asm volatile("" ::: "memory");                                                   \
-    frags(AC, BC, HF);                                                               \
+    frags(NC, WC, HF);                                                               \
     PPBAR(8)                                                                         \
     mma();                                                                           \
     PPBAR(8)                                                                         \
   }
-#define PPSTEP(T, AC, AN, BC, HF, BN)                                                \
+#define PPSTEP(T, NC, NR, WC, HF, WR)                                                \
   {                                                                                  \
     const int t_ = (T);                                                              \
-    if ((HF) == 0 && t_ / 2 + 2 < np) dloadB(t_ / 2 + 2, BN);                        \
+    if ((HF) == 0 && t_ / 2 + 2 < np) dloadW(t_ / 2 + 2, WR);                        \
     asm volatile("" ::: "memory");                                                   \
-    if (t_ + 3 < nk) dloadA(t_ + 3, AN);                                             \
+    if (t_ + 3 < nk) dloadN(t_ + 3, NR);                                             \
     asm volatile("" ::: "memory");                                                   \
-    frags(AC, BC, HF);                                                               \
+    frags(NC, WC, HF);                                                               \
     const int w_ = issued_after(t_);                                                 \
     PPBARN(w_)                                                                       \
     mma();                                                                           \
     PPBARN(w_)                                                                       \
   }
 #define PPGROUP(M, O)                                                                \
-  M((O) + 0, A0, A3, B0, 0, B2) M((O) + 1, A1, A0, B0, 1, B2)                        \
-  M((O) + 2, A2, A1, B1, 0, B0) M((O) + 3, A3, A2, B1, 1, B0)                        \
-  M((O) + 4, A0, A3, B2, 0, B1) M((O) + 5, A1, A0, B2, 1, B1)                        \
-  M((O) + 6, A2, A1, B0, 0, B2) M((O) + 7, A3, A2, B0, 1, B2)                        \
-  M((O) + 8, A0, A3, B1, 0, B0) M((O) + 9, A1, A0, B1, 1, B0)                        \
-  M((O) + 10, A2, A1, B2, 0, B1) M((O) + 11, A3, A2, B2, 1, B1)
-#define GSTEP(T, AC, AN, BC, HF, BN) if ((T) < nk) PPSTEP(T, AC, AN, BC, HF, BN)
+  M((O) + 0, R0, R3, W0, 0, W2) M((O) + 1, R1, R0, W0, 1, W2)                        \
+  M((O) + 2, R2, R1, W1, 0, W0) M((O) + 3, R3, R2, W1, 1, W0)                        \
+  M((O) + 4, R0, R3, W2, 0, W1) M((O) + 5, R1, R0, W2, 1, W1)                        \
+  M((O) + 6, R2, R1, W0, 0, W2) M((O) + 7, R3, R2, W0, 1, W2)                        \
+  M((O) + 8, R0, R3, W1, 0, W0) M((O) + 9, R1, R0, W1, 1, W0)                        \
+  M((O) + 10, R2, R1, W2, 0, W1) M((O) + 11, R3, R2, W2, 1, W1)
+#define GSTEP(T, NC, NR, WC, HF, WR) if ((T) < nk) PPSTEP(T, NC, NR, WC, HF, WR)
   // steps 0..11 (guarded), whole groups of 12 whose every refill happens,
   // then the last 12..14 steps (guarded)
   PPGROUP(GSTEP, 0)
   int t0 = 12;
   for (; t0 + 14 < nk; t0 += 12) { PPGROUP(PPSTEADY, t0) }
   PPGROUP(GSTEP, t0)
-  GSTEP(t0 + 12, A0, A3, B0, 0, B2)
-  GSTEP(t0 + 13, A1, A0, B0, 1, B2)
+  GSTEP(t0 + 12, R0, R3, W0, 0, W2)
+  GSTEP(t0 + 13, R1, R0, W0, 1, W2)
   if (!lag) __builtin_amdgcn_s_barrier();
 #undef PPSTEADY
 #undef PPSTEP
@@ -600,11 +673,11 @@ __global__ __launch_bounds__(512) void gemm_ntw_kernel(GemmArgs g, int tiles_m, 
 #undef PPGROUP
 #undef GSTEP
   // epilogue as in the kernel above; each wave stages its 128 x 64 tile
-  // (16 KiB) in one A stage or in half of a B stage
+  // (16 KiB) in one 32-deep stage or in half of a 64-deep stage
   {
     __syncthreads();
-    uint16_t* st = wave == 0 ? A0 : wave == 1 ? A1 : wave == 2 ? A2 : wave == 3 ? A3
-                 : (wave < 6 ? B0 : B1) + (wave & 1) * (128 * 64);
+    uint16_t* st = wave == 0 ? R0 : wave == 1 ? R1 : wave == 2 ? R2 : wave == 3 ? R3
+                 : (wave < 6 ? W0 : W1) + (wave & 1) * (128 * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = i * 32 + (lane & 31);
@@ -660,11 +733,14 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     if (small) hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
     else hipLaunchKernelGGL((gemm_bf16_kernel<NN_, BT_, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt); \
   }
-    // measured: 8192 x 2048 x 5632 in 145-150 instead of 159-165 us; no gain
-    // for K = 2048
-    const bool wide = !nn && g.batch == 1 && g.K % 64 == 0 && g.K >= 4096;
-    if (nn) GEMM_LAUNCH(true, false)
-    else if (wide) hipLaunchKernelGGL(gemm_ntw_kernel, dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    // measured on the layer set's products (K = 2048 and 5632): NT
+    // 8192 x 2048 x 5632 in 142-147 instead of 159-165 us, and 0.08 ms less
+    // per training step for NT and NN together.  Short K keeps the 4-stage
+    // ring (shorter prologue).
+    const bool wide = g.batch == 1 && g.K % 64 == 0 && g.K >= 2048;
+    if (wide && nn) hipLaunchKernelGGL(gemm_wide_kernel<true>, dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    else if (wide) hipLaunchKernelGGL(gemm_wide_kernel<false>, dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    else if (nn) GEMM_LAUNCH(true, false)
     else if (g.batch > 1) GEMM_LAUNCH(false, true)
     else GEMM_LAUNCH(false, false)
 #undef GEMM_LAUNCH
