@@ -78,6 +78,8 @@ SMALL = [
     (20, 40, 32, 5),       # m < b: R is the identity
     (512, 256, 256, 129),
     (4360, 4104, 256, 45),  # rows of 4096+ columns with identity tails (streaming permutation)
+    (2048, 2048, 256, 45),  # K >= 2048, a multiple of 64: the 64-deep GEMM ring, few tokens
+    (2112, 2240, 64, 70),   # the same with a partial last tile in n and m
 ]
 
 
