@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--chain", choices=["batched", "per-matrix"], default="batched",
                     help="layer set: one chain-rule call for all matrices after the backward pass, or one per "
                          "matrix on its stream")
+    ap.add_argument("--keep-z2", action="store_true",
+                    help="layer set: the variant without activation recompute (the forward keeps z2' for the "
+                         "backward, N*m*2 bytes per matrix); the default recomputes it (POET-Xmem)")
     ap.add_argument("--per-layer-builds", action="store_true",
                     help="let every forward / backward call build its own blocks (one builder launch per call) "
                          "instead of one batched build per pass")
@@ -439,6 +442,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(2)
+    if args.keep_z2 and args.per_layer_builds:
+        print("--keep-z2 uses the prebuilt-block calls; drop --per-layer-builds", file=sys.stderr)
+        sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     cfg = WL.CONFIGS[3]
@@ -465,7 +471,8 @@ def main():
         gYs.append(up(inp["gY"], "bf16"))
         outs.append(dict(Y=torch.empty(N, inp["m"], dtype=torch.bfloat16, device=dev),
                          dX=torch.empty(N, inp["n"], dtype=torch.bfloat16, device=dev),
-                         dR=torch.empty_like(lay.thR), dP=torch.empty_like(lay.thP)))
+                         dR=torch.empty_like(lay.thR), dP=torch.empty_like(lay.thP),
+                         Z2=torch.empty(N, inp["m"], dtype=torch.bfloat16, device=dev) if args.keep_z2 else None))
         layers.append(lay)
         # allocate workspaces and block buffers up front (nothing is allocated in the timed region)
         if args.per_layer_builds:
@@ -520,10 +527,17 @@ def main():
         with torch.cuda.stream(bs):
             P.build_layer_blocks(layers, "backward")
             bwd_blocks_ready.record(bs)
-        fan_out(list(zip(layers, outs)), lambda lay, o: lay.forward_blocks(Xs[lay.x_key], Y=o["Y"]))
+        if args.keep_z2:
+            fan_out(list(zip(layers, outs)),
+                    lambda lay, o: lay.forward_blocks_z2(Xs[lay.x_key], Y=o["Y"], Z2=o["Z2"]))
+        else:
+            fan_out(list(zip(layers, outs)), lambda lay, o: lay.forward_blocks(Xs[lay.x_key], Y=o["Y"]))
         stream.wait_event(bwd_blocks_ready)
         def bwd(lay, g, o):
-            lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"])
+            if args.keep_z2:
+                lay.backward_blocks_dq_z2(Xs[lay.x_key], g, o["Z2"], dX=o["dX"])
+            else:
+                lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"])
             if args.chain == "per-matrix":
                 P.chain_rule_layers([lay], [(o["dR"], o["dP"])])
         fan_out(list(zip(reversed(layers), reversed(gYs), reversed(outs))), bwd)
@@ -618,7 +632,9 @@ def main():
                    "shapes": ["%dx%d" % (m, n) for _, m, n in cfg["mats"]],
                    "block_builds": "per layer call" if args.per_layer_builds else
                    "batched per pass (Cayley builds and chain rule over all seven matrices)",
-                   "streams": 1 if args.per_layer_builds else max(args.streams, 1)},
+                   "streams": 1 if args.per_layer_builds else max(args.streams, 1),
+                   "activations": "z2' kept from the forward pass (no recompute)" if args.keep_z2 else
+                   "recomputed in the backward pass (POET-Xmem)"},
         "roofline": roof,
         "kernels_per_step": breakdown,
         "merge_ms_layer_set": round(merge_ms, 3),

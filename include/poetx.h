@@ -240,6 +240,36 @@ int poetx_backward_blocks_dq(const poetx_layer* layer, const void* W0p, const po
                              int64_t N, void* dX, float* GR, float* GP, void* ws, size_t ws_bytes,
                              void* stream);
 
+/*
+ * The variant without activation recompute: POET-Xmem recomputes the
+ * intermediate activations in the backward pass to save memory [P3 item 5];
+ * keeping the weight product's output z2' = z1' W0p^T from the forward pass
+ * instead saves the backward pass the P-side block product and the forward
+ * GEMM, for N * m * 2 bytes per layer.
+ *
+ * poetx_forward_blocks that also writes z2' to Z2:
+ *   Z2  [N][m] bf16, the working (sigma-permuted) layout, device, written;
+ *       must not overlap any other argument
+ * bf16 layers only (POETX_EDTYPE otherwise); N == 0 writes nothing.
+ * Workspace: poetx_workspace_bytes(layer, N, POETX_OP_FORWARD_BLOCKS).
+ */
+int poetx_forward_blocks_z2(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                            const int32_t* sigma, const int32_t* tau, const void* X, int64_t N,
+                            void* Y, void* Z2, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * poetx_backward_blocks_dq with z2' read from Z2 instead of recomputed:
+ *   Z2  [N][m] bf16, as poetx_forward_blocks_z2 wrote it for the same X,
+ *       W0p and generators (the blocks are rebuilt from the same generators,
+ *       so the results are identical to poetx_backward_blocks_dq's)
+ * x' = Pi_tau x is still gathered again for dL/dQ_P.  bf16 layers only.
+ * Workspace: poetx_workspace_bytes(layer, N, POETX_OP_BACKWARD_DQ).
+ */
+int poetx_backward_blocks_dq_z2(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                                const int32_t* sigma, const int32_t* tau, const void* X, const void* dY,
+                                const void* Z2, int64_t N, void* dX, float* GR, float* GP, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* One batch of blocks for poetx_chain_rule_sets. */
 typedef struct {
   const float* Q32; /* [nblocks][b][b] fp32 Cayley blocks Q, device           */

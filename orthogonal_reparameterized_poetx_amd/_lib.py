@@ -22,7 +22,8 @@ _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDT
 
 EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
             "poetx_build_block_sets", "poetx_forward", "poetx_forward_blocks", "poetx_backward",
-            "poetx_backward_blocks", "poetx_backward_blocks_dq", "poetx_chain_rule_sets",
+            "poetx_backward_blocks", "poetx_backward_blocks_dq", "poetx_forward_blocks_z2",
+            "poetx_backward_blocks_dq_z2", "poetx_chain_rule_sets",
             "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_make_permutation",
             "poetx_adam_step",
             "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
@@ -105,6 +106,9 @@ def lib():
         "poetx_backward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_backward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_backward_blocks_dq": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "poetx_forward_blocks_z2": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, i64, vp, vp, vp, sz, vp]),
+        "poetx_backward_blocks_dq_z2": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz,
+                                                        vp]),
         "poetx_chain_rule_sets": (ctypes.c_int, [ctypes.POINTER(ChainSet), i32, i32, ctypes.c_uint32, vp, sz, vp]),
         "poetx_chain_workspace_bytes": (sz, [i64, i32]),
         "poetx_merge": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
@@ -196,6 +200,19 @@ def poetx_backward_blocks_dq(layer, W0p, blocks, sigma, tau, X, dY, N, dX, GR, G
         ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
         _ptr(X), _ptr(dY), int(N), _ptr(dX), _ptr(GR), _ptr(GP), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream)))
+
+
+def poetx_forward_blocks_z2(layer, W0p, blocks, sigma, tau, X, N, Y, Z2, ws, stream=None):
+    _check("poetx_forward_blocks_z2", lib().poetx_forward_blocks_z2(
+        ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
+        _ptr(X), int(N), _ptr(Y), _ptr(Z2), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def poetx_backward_blocks_dq_z2(layer, W0p, blocks, sigma, tau, X, dY, Z2, N, dX, GR, GP, ws, stream=None):
+    _check("poetx_backward_blocks_dq_z2", lib().poetx_backward_blocks_dq_z2(
+        ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
+        _ptr(X), _ptr(dY), _ptr(Z2), int(N), _ptr(dX), _ptr(GR), _ptr(GP), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def chain_workspace_bytes(total_blocks, b):

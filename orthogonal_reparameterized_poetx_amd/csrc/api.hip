@@ -453,8 +453,10 @@ int blockmul(const void* in, const uint16_t* q, void* out, int64_t N, int W, int
 }
 
 // forward after the blocks exist: a3, a4, a5
+// z2out non-null (bf16): z2' goes there instead of the workspace (kept for
+// the backward pass)
 int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
-             void* Y, const FwdWs& w, hipStream_t s) {
+             void* Y, const FwdWs& w, hipStream_t s, void* z2out = nullptr) {
   const int64_t N = S.N;
   const int n = (int)S.n, m = (int)S.m;
   int rc;
@@ -482,21 +484,24 @@ int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   if ((rc = permute(true, X, nullptr, w.sc, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
   if ((rc = blockmul(w.sc, q.qbP, w.z1, N, n, S.b, S.kP, s))) return rc;
   // z2' = z1' W0p^T
+  void* const z2 = z2out ? z2out : w.z2;
   {
     Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-    launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
+    launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)z2, N, S.m, S.n, s);
   }
   if ((rc = check_launch("forward GEMM"))) return rc;
   // y = Pi_sigma^T r with r = D_R z2' (the tail of r is the tail of z2')
-  if ((rc = blockmul(w.z2, q.qbR, w.sc, N, m, S.b, S.kR, s))) return rc;
-  return permute(false, w.sc, w.z2, Y, nullptr, sigma, N, m, S.kR * S.b, S.es, s);
+  if ((rc = blockmul(z2, q.qbR, w.sc, N, m, S.b, S.kR, s))) return rc;
+  return permute(false, w.sc, z2, Y, nullptr, sigma, N, m, S.kR * S.b, S.es, s);
 }
 
 // backward after the blocks exist: a0 (recompute), a6, a7, a8, a9
 // gR / gP non-null: write dL/dQ there and stop before the chain rule
+// z2in non-null (bf16): z2' kept from the forward pass, so a0 reduces to
+// gathering x' again (no P-side block product, no forward GEMM)
 int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
              const void* dY, void* dX, float* dthR, float* dthP, bool accum, const BwdWs& w, hipStream_t s,
-             float* gR = nullptr, float* gP = nullptr) {
+             float* gR = nullptr, float* gP = nullptr, const void* z2in = nullptr) {
   float* const GR = gR ? gR : w.GR;
   float* const GP = gR ? gP : w.GP;
   const int64_t N = S.N;
@@ -526,8 +531,8 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   } else {
     // recompute x' = Pi_tau x (kept for dL/dQ_P), z1' = D_P x', z2' = z1' W0p^T
     if ((rc = permute(true, X, nullptr, w.xg, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
-    if ((rc = blockmul(w.xg, q.qbP, w.z1, N, n, S.b, S.kP, s))) return rc;
-    {
+    if (!z2in) {
+      if ((rc = blockmul(w.xg, q.qbP, w.z1, N, n, S.b, S.kP, s))) return rc;
       Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
       launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
     }
@@ -540,7 +545,7 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   {
     // algorithmic bytes: the reads of gY' and z2'
     Tm tm(s, "gram", xf_flops(N, S.kR, S.b), 2.0 * N * S.m * S.es);
-    launch_gram(S.f32, w.gyg, w.z2, N, m, S.b, S.kR, GR, w.part, s);
+    launch_gram(S.f32, w.gyg, z2in ? z2in : w.z2, N, m, S.b, S.kR, GR, w.part, s);
   }
   if ((rc = check_launch("R-side backward"))) return rc;
   // gz1' = gz2' W0p (into the z1' buffer)
@@ -706,6 +711,46 @@ Blk blk_of(const poetx_blocks* q) {
              static_cast<const uint16_t*>(q->QTR), static_cast<const uint16_t*>(q->QTP)};
 }
 
+// poetx_forward_blocks(_z2): Z2 non-null keeps z2' for the backward pass
+int forward_blocks_impl(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks, const int32_t* sigma,
+                        const int32_t* tau, const void* X, int64_t N, void* Y, void* Z2, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc = check_fwd_args(layer, N, W0p, sigma, tau, X, Y);
+  if (rc) return rc;
+  const Shape S = shape_of(layer, N);
+  if ((rc = check_blocks(S, blocks, false))) return rc;
+  if (N == 0) return POETX_OK;
+  size_t need = 0;
+  plan_fwd(S, false, nullptr, &need);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const FwdWs w = plan_fwd(S, false, ws, &need);
+  return fwd_core(S, W0p, blk_of(blocks), sigma, tau, X, Y, w, static_cast<hipStream_t>(stream), Z2);
+}
+
+// poetx_backward_blocks_dq(_z2): Z2 non-null is z2' kept from the forward pass
+int backward_dq_impl(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks, const int32_t* sigma,
+                     const int32_t* tau, const void* X, const void* dY, const void* Z2, int64_t N, void* dX,
+                     float* GR, float* GP, void* ws, size_t ws_bytes, void* stream, const char* fn) {
+  int rc = check_bwd_args(layer, N, W0p, sigma, tau, X, dY, GR, GP);
+  if (rc) return rc;
+  if (layer->flags & POETX_ACCUMULATE_GRAD)
+    return fail(POETX_EINVAL, "POETX_ACCUMULATE_GRAD applies to poetx_chain_rule_sets, not to dL/dQ");
+  const Shape S = shape_of(layer, N);
+  if (S.f32) return fail(POETX_EDTYPE, "%s takes bf16 layers", fn);
+  if ((rc = check_blocks(S, blocks, true))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    launch_fill_f32(GR, 0.f, (int64_t)S.kR * S.b * S.b, s);
+    launch_fill_f32(GP, 0.f, (int64_t)S.kP * S.b * S.b, s);
+    return check_launch("zero dL/dQ");
+  }
+  size_t need = 0;
+  plan_bwd(S, false, nullptr, &need, true);
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const BwdWs w = plan_bwd(S, false, ws, &need, true);
+  return bwd_core(S, W0p, blk_of(blocks), sigma, tau, X, dY, dX, nullptr, nullptr, false, w, s, GR, GP, Z2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -802,16 +847,15 @@ int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR, c
 int poetx_forward_blocks(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
                          const int32_t* sigma, const int32_t* tau, const void* X, int64_t N, void* Y, void* ws,
                          size_t ws_bytes, void* stream) {
-  int rc = check_fwd_args(layer, N, W0p, sigma, tau, X, Y);
-  if (rc) return rc;
-  const Shape S = shape_of(layer, N);
-  if ((rc = check_blocks(S, blocks, false))) return rc;
-  if (N == 0) return POETX_OK;
-  size_t need = 0;
-  plan_fwd(S, false, nullptr, &need);
-  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  const FwdWs w = plan_fwd(S, false, ws, &need);
-  return fwd_core(S, W0p, blk_of(blocks), sigma, tau, X, Y, w, static_cast<hipStream_t>(stream));
+  return forward_blocks_impl(layer, W0p, blocks, sigma, tau, X, N, Y, nullptr, ws, ws_bytes, stream);
+}
+
+int poetx_forward_blocks_z2(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                            const int32_t* sigma, const int32_t* tau, const void* X, int64_t N, void* Y, void* Z2,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (layer && layer->dtype == POETX_F32) return fail(POETX_EDTYPE, "poetx_forward_blocks_z2 takes bf16 layers");
+  if (N > 0 && !Z2) return fail(POETX_EINVAL, "Z2 is NULL");
+  return forward_blocks_impl(layer, W0p, blocks, sigma, tau, X, N, Y, Z2, ws, ws_bytes, stream);
 }
 
 int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, const float* thP,
@@ -859,24 +903,17 @@ int poetx_backward_blocks(const poetx_layer* layer, const void* W0p, const poetx
 int poetx_backward_blocks_dq(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
                              const int32_t* sigma, const int32_t* tau, const void* X, const void* dY, int64_t N,
                              void* dX, float* GR, float* GP, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_bwd_args(layer, N, W0p, sigma, tau, X, dY, GR, GP);
-  if (rc) return rc;
-  if (layer->flags & POETX_ACCUMULATE_GRAD)
-    return fail(POETX_EINVAL, "POETX_ACCUMULATE_GRAD applies to poetx_chain_rule_sets, not to dL/dQ");
-  const Shape S = shape_of(layer, N);
-  if (S.f32) return fail(POETX_EDTYPE, "poetx_backward_blocks_dq takes bf16 layers");
-  if ((rc = check_blocks(S, blocks, true))) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (N == 0) {
-    launch_fill_f32(GR, 0.f, (int64_t)S.kR * S.b * S.b, s);
-    launch_fill_f32(GP, 0.f, (int64_t)S.kP * S.b * S.b, s);
-    return check_launch("zero dL/dQ");
-  }
-  size_t need = 0;
-  plan_bwd(S, false, nullptr, &need, true);
-  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  const BwdWs w = plan_bwd(S, false, ws, &need, true);
-  return bwd_core(S, W0p, blk_of(blocks), sigma, tau, X, dY, dX, nullptr, nullptr, false, w, s, GR, GP);
+  return backward_dq_impl(layer, W0p, blocks, sigma, tau, X, dY, nullptr, N, dX, GR, GP, ws, ws_bytes, stream,
+                          "poetx_backward_blocks_dq");
+}
+
+int poetx_backward_blocks_dq_z2(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                                const int32_t* sigma, const int32_t* tau, const void* X, const void* dY,
+                                const void* Z2, int64_t N, void* dX, float* GR, float* GP, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (N > 0 && !Z2) return fail(POETX_EINVAL, "Z2 is NULL");
+  return backward_dq_impl(layer, W0p, blocks, sigma, tau, X, dY, Z2, N, dX, GR, GP, ws, ws_bytes, stream,
+                          "poetx_backward_blocks_dq_z2");
 }
 
 size_t poetx_chain_workspace_bytes(int64_t total_blocks, int32_t b) {

@@ -116,6 +116,18 @@ class PoetxLayer:
                                Y, ws, stream)
         return Y
 
+    def forward_blocks_z2(self, X, Y=None, Z2=None, stream=None):
+        """forward_blocks that also returns z2' (working layout) for backward_blocks_dq_z2."""
+        N = X.shape[0]
+        if Y is None:
+            Y = torch.empty(N, self.m, dtype=self.tdtype, device=self.device)
+        if Z2 is None:
+            Z2 = torch.empty(N, self.m, dtype=self.tdtype, device=self.device)
+        ws = self.workspace(L.OP_FORWARD_BLOCKS, N)
+        L.poetx_forward_blocks_z2(self.layer, self.W0p, self.block_buffers("forward")[1], self.sigma, self.tau, X,
+                                  N, Y, Z2, ws, stream)
+        return Y, Z2
+
     def backward_blocks(self, X, dY, dX=None, dthR=None, dthP=None, want_dx=True, accumulate=False, stream=None):
         N = X.shape[0]
         if dX is None and want_dx:
@@ -150,6 +162,17 @@ class PoetxLayer:
         ws = self.workspace(L.OP_BACKWARD_DQ, N)
         L.poetx_backward_blocks_dq(self.layer, self.W0p, self.block_buffers("backward")[1], self.sigma, self.tau,
                                    X, dY, N, dX if want_dx else None, GR, GP, ws, stream)
+        return dX, GR, GP
+
+    def backward_blocks_dq_z2(self, X, dY, Z2, dX=None, want_dx=True, stream=None):
+        """backward_blocks_dq with z2' from forward_blocks_z2 instead of recomputed; returns (dX, GR, GP)."""
+        N = X.shape[0]
+        if dX is None and want_dx:
+            dX = torch.empty(N, self.n, dtype=self.tdtype, device=self.device)
+        GR, GP = self.dq_buffers()
+        ws = self.workspace(L.OP_BACKWARD_DQ, N)
+        L.poetx_backward_blocks_dq_z2(self.layer, self.W0p, self.block_buffers("backward")[1], self.sigma,
+                                      self.tau, X, dY, Z2, N, dX if want_dx else None, GR, GP, ws, stream)
         return dX, GR, GP
 
     def merge_blocks(self, stream=None):

@@ -200,3 +200,33 @@ def test_deferred_chain_entry_points_validate_on_host():
     assert L.poetx_chain_rule_sets(bad, 1, 64, 0, fake, wneed, None) == -1
     assert L.poetx_chain_rule_sets((S * 1)(S(None, None, 0, None)), 1, 64, 0, None, 0, None) == 0
     assert L.poetx_chain_rule_sets(two, 0, 64, 0, None, 0, None) == 0
+
+
+def test_stored_z2_entry_points_validate_on_host():
+    P = _P()
+    L = P.lib()
+    fake = ctypes.c_void_p(0x1000)
+    f = 0x2000
+    lay = P.Layer(512, 256, 64, P.POETX_BF16)
+    l32 = P.Layer(512, 256, 64, P.POETX_F32)
+    fneed = P.workspace_bytes(lay, 64, P.OP_FORWARD_BLOCKS)
+    bneed = P.workspace_bytes(lay, 64, P.OP_BACKWARD_DQ)
+    fwd = P.Blocks(None, None, f, f, None, None)
+    bwd = P.Blocks(f, f, None, f, f, f)
+    fargs = lambda l, blk, z2, nb: (ctypes.byref(l), fake, blk, fake, fake, fake, 64, fake, z2, fake, nb, None)
+    # NULL Z2, fp32 layer, NULL or incomplete blocks, short workspace
+    assert L.poetx_forward_blocks_z2(*fargs(lay, ctypes.byref(fwd), None, fneed)) == -1
+    assert L.poetx_forward_blocks_z2(*fargs(l32, ctypes.byref(fwd), fake, 1 << 30)) == -3
+    assert L.poetx_forward_blocks_z2(*fargs(lay, None, fake, fneed)) == -1
+    assert L.poetx_forward_blocks_z2(*fargs(lay, ctypes.byref(P.Blocks(None, None, None, f, None, None)), fake,
+                                            fneed)) == -1
+    assert L.poetx_forward_blocks_z2(*fargs(lay, ctypes.byref(fwd), fake, fneed - 1)) == -4
+    bargs = lambda l, blk, z2, GR, nb: (ctypes.byref(l), fake, blk, fake, fake, fake, fake, z2, 64, fake, GR, fake,
+                                        fake, nb, None)
+    assert L.poetx_backward_blocks_dq_z2(*bargs(lay, ctypes.byref(bwd), None, fake, bneed)) == -1
+    assert L.poetx_backward_blocks_dq_z2(*bargs(lay, ctypes.byref(bwd), fake, None, bneed)) == -1
+    assert L.poetx_backward_blocks_dq_z2(*bargs(l32, ctypes.byref(bwd), fake, fake, 1 << 30)) == -3
+    assert L.poetx_backward_blocks_dq_z2(*bargs(lay, ctypes.byref(fwd), fake, fake, bneed)) == -1
+    assert L.poetx_backward_blocks_dq_z2(*bargs(lay, ctypes.byref(bwd), fake, fake, bneed - 1)) == -4
+    acc = P.Layer(512, 256, 64, P.POETX_BF16, P.POETX_ACCUMULATE_GRAD)
+    assert L.poetx_backward_blocks_dq_z2(*bargs(acc, ctypes.byref(bwd), fake, fake, bneed)) == -1

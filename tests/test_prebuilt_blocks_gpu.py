@@ -171,3 +171,40 @@ def test_deferred_chain_matches_backward_blocks(shapes, b, N):
     torch.cuda.synchronize()
     for (dR, dP), (aR, aP) in zip(grads, acc):
         assert torch.equal(aR, dR + dR) and torch.equal(aP, dP + dP)
+
+
+@pytest.mark.parametrize("m,n,b,N", [
+    (600, 520, 256, 70),     # identity tails on both sides
+    (2048, 2048, 256, 45),   # the 64-deep GEMM ring (K >= 2048)
+    (1100, 700, 512, 24),
+])
+def test_stored_z2_matches_recompute(m, n, b, N):
+    """The variant that keeps z2' from the forward pass gives the results of
+    the recomputing one bit for bit, and its z2' is the oracle's Z2 in the
+    working (sigma-gathered) layout."""
+    torch = torch_mod()
+    from orthogonal_reparameterized_poetx_amd import build_layer_blocks
+    inp = WL.small_case(80, m, n, b, N, dtype="bf16")
+    lay, d = make_layer(inp)
+    _log("stored z2 m=%d n=%d b=%d N=%d" % (m, n, b, N))
+    build_layer_blocks([lay], "forward")
+    build_layer_blocks([lay], "backward")
+    Y0 = lay.forward_blocks(d["X"])
+    dX0, GR0, GP0 = (t.clone() for t in lay.backward_blocks_dq(d["X"], d["gY"]))
+    Z2 = torch.full((N, m), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    Y1, _ = lay.forward_blocks_z2(d["X"], Z2=Z2)
+    dX1, GR1, GP1 = lay.backward_blocks_dq_z2(d["X"], d["gY"], Z2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0, Y1) and torch.equal(dX0, dX1)
+    assert torch.equal(GR0, GR1) and torch.equal(GP0, GP1)
+    sigma, tau = oracle_perms(inp, 0)
+    _, mid = oracle.forward(inp["W0"][1], inp["thR"][1], inp["thP"][1], sigma, tau, inp["X"][1], b, contract=True,
+                            intermediates=True)
+    st = compare(from_dev(Z2), mid["Z2"][:, sigma], "bf16", "Z2")
+    _log("  Z2 fail=%d/%d max_tol_ratio=%.3g rel_norm=%.3g" % (st["fail"], st["n"], st["max_ratio"], st["rel_norm"]))
+    assert st["fail"] == 0
+    # N = 0: nothing is written, dL/dQ is zero
+    lay.forward_blocks_z2(d["X"][:0], Z2=Z2[:0])
+    _, GR, GP = lay.backward_blocks_dq_z2(d["X"][:0], d["gY"][:0], Z2[:0], want_dx=False)
+    torch.cuda.synchronize()
+    assert not GR.any().item() and not GP.any().item()
