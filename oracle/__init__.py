@@ -10,7 +10,9 @@ The oracle is written from these pages (cited by title and section):
 * [P3] "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
   Transformation" (gist.science summary of arXiv 2603.05500), section
   "Technische samenvatting" > "Methodologie", items 1-5.  The authority on
-  what POET-X computes.
+  what POET-X computes; item 5 also names POET-XQ (base weights stored
+  quantized, e.g. INT8, and dequantized on the fly): ``quantize_rows`` /
+  ``dequantize_rows``.
 * [P1] "POET-X：基于正交变换缩放的内存高效LLM训练方法" (ai-stack.site review),
   最佳实践 实践 2 (Cayley transform, autodiff to the generator),
   实践 4 (recompute, det = 1), 实践 5 (fp32 accumulation).
@@ -30,11 +32,13 @@ from .poetx import (  # noqa: F401
     cayley,
     chain_rule,
     dense_orthogonal,
+    dequantize_rows,
     forward,
     make_permutation,
     merge,
     mix64,
     pack,
+    quantize_rows,
     round_bf16,
     triu_pairs,
     unpack,

@@ -288,3 +288,31 @@ def adam_step(theta, grad, m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8
     vhat = v / (1.0 - beta2 ** step)
     return theta - lr * mhat / (np.sqrt(vhat) + eps), m, v
 
+
+
+# --------------------------------------------------------------------------
+# POET-XQ: base weights stored as INT8 codes and dequantized for each use
+# [P3 "Methodologie" item 5].  The pages give no granularity; the plainest
+# reading is symmetric per-row codes (one scale per output feature).  The
+# codes are decided in fp32, the precision a GPU decides them in.
+# --------------------------------------------------------------------------
+def quantize_rows(W):
+    """INT8 codes and fp32 scales of a weight [m][n] (bf16 values):
+    s_i = a_i / 127 with a_i = max_j |w_ij|, q_ij = clamp(rne(w_ij / s_i),
+    -127, 127), both divisions in fp32 with round-to-nearest-even; a row of
+    zeros gets s_i = 0 and q_i = 0.  Returns (q int8 [m][n], s float32 [m])."""
+    W32 = np.asarray(W, dtype=np.float32)
+    s = np.max(np.abs(W32), axis=1) / np.float32(127.0)
+    s = s.astype(np.float32)
+    q = np.zeros(W32.shape, dtype=np.int8)
+    nz = s > 0
+    r = W32[nz] / s[nz][:, None]
+    q[nz] = np.clip(np.rint(r), -127, 127).astype(np.int8)
+    return q, s
+
+
+def dequantize_rows(q, s):
+    """bf16 weight values s_i * q_ij: the product rounded to fp32, then to
+    bf16 (both round-to-nearest-even).  Returned as float64."""
+    p = np.asarray(s, dtype=np.float32)[:, None] * np.asarray(q, dtype=np.float32)
+    return round_bf16(p.astype(np.float32).astype(np.float64))

@@ -328,3 +328,56 @@ def test_adam_second_step_by_hand():
     mhat = -0.01 / (1 - 0.81)
     vhat = 0.001999 / (1 - 0.998001)
     assert np.allclose(th, [-(1 / (1 + 1e-8)) - mhat / (np.sqrt(vhat) + 1e-8)], atol=1e-12, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# POET-XQ weight codes [P3 "Methodologie" item 5]: symmetric per-row INT8
+# --------------------------------------------------------------------------
+def test_quantize_rows_worked_examples():
+    u = 2.0 ** -7
+    W = np.array([[127 * u, -64 * u, 3 * u, 0.0],          # absmax 127 u: scale u exactly, codes = integers
+                  [127 * u, 2.5 * u, -2.5 * u, 1.5 * u],   # ties round to even: 2, -2, 2
+                  [0.0, 0.0, 0.0, 0.0],                    # zero row: scale 0, codes 0
+                  [-3.0, 1.0, 0.0, 0.5]])                  # negative maximum
+    q, s = O.quantize_rows(W)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert s[0] == u and s[1] == u and s[2] == 0.0
+    assert s[3] == np.float32(3.0) / np.float32(127.0)
+    assert q[0].tolist() == [127, -64, 3, 0]
+    assert q[1].tolist() == [127, 2, -2, 2]
+    assert q[2].tolist() == [0, 0, 0, 0]
+    assert q[3].tolist() == [-127, 42, 0, 21]            # 127/3 = 42.33, 127/6 = 21.17
+    D = O.dequantize_rows(q, s)
+    assert np.array_equal(D[:3], np.array([[127 * u, -64 * u, 3 * u, 0], [127 * u, 2 * u, -2 * u, 2 * u], [0] * 4]))
+    assert D[3, 0] == -3.0                               # 127 * fp32(3/127) rounds back to 3 in bf16
+
+
+def test_quantize_rows_bounds_and_symmetries():
+    rng = np.random.default_rng(17)
+    W = O.round_bf16(rng.standard_normal((64, 300)) * np.exp(rng.uniform(-6, 2, (64, 1))))
+    q, s = O.quantize_rows(W)
+    sq = s.astype(np.float64)[:, None] * q
+    # rounding to the nearest code: within half a step, plus the fp32
+    # rounding of the quotient w / s (at most 127 * 2^-24 steps), which can
+    # move a value a hair below a half-way point onto it
+    assert np.all(np.abs(sq - W) <= s[:, None] * (0.5 + 127 * 2.0 ** -24) * (1 + 1e-9))
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    # the bf16 dequantized value adds at most half a bf16 ulp of the product
+    # (8 significant bits: 2^-8 relative), and the fp32 product 2^-24 more
+    D = O.dequantize_rows(q, s)
+    assert np.all(np.abs(D - sq) <= (2.0 ** -8 + 2.0 ** -23) * np.abs(sq))
+    # odd symmetry and equivariance under row and column permutations
+    qn, sn = O.quantize_rows(-W)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    pr, pc = rng.permutation(64), rng.permutation(300)
+    qp, sp = O.quantize_rows(W[pr][:, pc])
+    assert np.array_equal(qp, q[pr][:, pc]) and np.array_equal(sp, s[pr])
+
+
+def test_dequantize_rows_matches_torch_rounding():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    q = rng.integers(-127, 128, (40, 77)).astype(np.int8)
+    s = (np.abs(rng.standard_normal(40)) * 1e-2).astype(np.float32)
+    ref = (torch.from_numpy(s)[:, None] * torch.from_numpy(q).to(torch.float32)).to(torch.bfloat16).to(torch.float64)
+    assert np.array_equal(O.dequantize_rows(q, s), ref.numpy())
