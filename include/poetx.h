@@ -76,6 +76,7 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
 
 /* poetx_layer.flags */
 #define POETX_ACCUMULATE_GRAD 1u /* backward adds into dthR/dthP instead of overwriting */
+#define POETX_W0_INT8 2u         /* W0p in the INT8 weight format (bf16 layers), below */
 
 /* op codes for poetx_workspace_bytes */
 #define POETX_OP_FORWARD 0
@@ -91,7 +92,7 @@ typedef struct {
   int64_t n;      /* columns of W0 = input features                       */
   int32_t b;      /* block size of R and P                                */
   int32_t dtype;  /* poetx_dtype of W0p, X, Y, dY, dX                     */
-  uint32_t flags; /* POETX_ACCUMULATE_GRAD                                */
+  uint32_t flags; /* POETX_ACCUMULATE_GRAD, POETX_W0_INT8                 */
   uint32_t reserved; /* must be 0                                         */
 } poetx_layer;
 
@@ -100,6 +101,32 @@ typedef struct {
  * Returns 0 and sets the last error if the layer is invalid.  Host only.
  */
 size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op);
+
+/*
+ * POET-XQ weight storage [P3 item 5: base weights stored quantized, e.g.
+ * INT8, and dequantized on the fly].  With POETX_W0_INT8 in layer->flags
+ * (bf16 layers only) every W0p argument of this library points to the INT8
+ * weight format instead of bf16 [m][n]:
+ *   bytes [0, m*n)            int8 codes q[i][j], row-major, working layout
+ *   bytes [off, off + 4m)     fp32 scales s[i], off = m*n rounded up to 256
+ * The weight a pass uses is w[i][j] = bf16(s[i] * q[i][j]) (fp32 product,
+ * both roundings to nearest even); every pass dequantizes it into its
+ * workspace (the workspace sizes include that buffer), so its results equal
+ * those of the bf16 layer whose W0p holds those values, bit for bit.  A
+ * merge merges the dequantized weight and stores it again as codes:
+ *   s[i] = max_j |w[i][j]| / 127, q[i][j] = clamp(rne(w[i][j] / s[i]), -127, 127)
+ * in fp32 (s[i] = 0, q[i] = 0 for a row of zeros).
+ *
+ * poetx_w0_bytes: bytes of the W0p buffer of this layer (either format);
+ *   0 and the last error set if the layer is invalid.  Host only.
+ * poetx_quantize_w0: W0q (INT8 format) from a bf16 [m][n] weight W0bf16 in
+ *   the same layout, by the rule above.  Device pointers; no workspace.
+ * poetx_dequantize_w0: the bf16 [m][n] weight a pass would use.
+ * Both return POETX_EINVAL when layer->flags lacks POETX_W0_INT8.
+ */
+size_t poetx_w0_bytes(const poetx_layer* layer);
+int poetx_quantize_w0(const poetx_layer* layer, const void* W0bf16, void* W0q, void* stream);
+int poetx_dequantize_w0(const poetx_layer* layer, const void* W0q, void* W0bf16, void* stream);
 
 /*
  * One batch of Cayley blocks for poetx_build_block_sets: the generators of

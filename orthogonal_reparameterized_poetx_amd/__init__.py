@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     OP_MERGE,
     OP_MERGE_BLOCKS,
     POETX_ACCUMULATE_GRAD,
+    POETX_W0_INT8,
     POETX_BF16,
     POETX_F32,
     Blocks,
@@ -33,16 +34,21 @@ from ._lib import (  # noqa: F401
     poetx_backward,
     poetx_backward_blocks,
     poetx_backward_blocks_dq,
+    poetx_backward_blocks_dq_z2,
+    poetx_dequantize_w0,
     poetx_build_block_sets,
     poetx_build_blocks,
     poetx_chain_rule_sets,
     poetx_forward,
     poetx_forward_blocks,
+    poetx_forward_blocks_z2,
     poetx_make_permutation,
     poetx_merge,
     poetx_merge_blocks,
+    poetx_quantize_w0,
     timing_enable,
     timing_summary,
+    w0_bytes,
     workspace_bytes,
 )
 from .layer import PoetxLayer, build_layer_blocks, chain_rule_layers  # noqa: F401,E402

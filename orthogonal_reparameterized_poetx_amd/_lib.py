@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libpoetx.so")
 POETX_F32 = 0
 POETX_BF16 = 1
 POETX_ACCUMULATE_GRAD = 1
+POETX_W0_INT8 = 2
 OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS, OP_MERGE_BLOCKS, OP_BACKWARD_DQ = range(7)
 
 _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDTYPE",
@@ -25,7 +26,7 @@ EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build
             "poetx_backward_blocks", "poetx_backward_blocks_dq", "poetx_forward_blocks_z2",
             "poetx_backward_blocks_dq_z2", "poetx_chain_rule_sets",
             "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_make_permutation",
-            "poetx_adam_step",
+            "poetx_adam_step", "poetx_w0_bytes", "poetx_quantize_w0", "poetx_dequantize_w0",
             "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
 
 
@@ -116,6 +117,9 @@ def lib():
         "poetx_make_permutation": (ctypes.c_int, [u64, u64, i32, i64, vp]),
         "poetx_adam_step": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_float, vp]),
+        "poetx_w0_bytes": (sz, [LP]),
+        "poetx_quantize_w0": (ctypes.c_int, [LP, vp, vp, vp]),
+        "poetx_dequantize_w0": (ctypes.c_int, [LP, vp, vp, vp]),
         "poetx_last_error": (ctypes.c_char_p, []),
         "poetx_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "poetx_timing_summary": (ctypes.c_int, [ctypes.c_char_p, sz]),
@@ -159,6 +163,23 @@ def workspace_bytes(layer, N, op):
 
 def build_workspace_bytes(nblocks, b):
     return lib().poetx_build_workspace_bytes(int(nblocks), int(b))
+
+
+def w0_bytes(layer):
+    n = lib().poetx_w0_bytes(ctypes.byref(layer))
+    if n == 0:
+        raise PoetxError("poetx_w0_bytes", -1, last_error())
+    return n
+
+
+def poetx_quantize_w0(layer, W0bf16, W0q, stream=None):
+    _check("poetx_quantize_w0", lib().poetx_quantize_w0(ctypes.byref(layer), _ptr(W0bf16), _ptr(W0q),
+                                                        _stream(stream)))
+
+
+def poetx_dequantize_w0(layer, W0q, W0bf16, stream=None):
+    _check("poetx_dequantize_w0", lib().poetx_dequantize_w0(ctypes.byref(layer), _ptr(W0q), _ptr(W0bf16),
+                                                            _stream(stream)))
 
 
 def make_workspace(nbytes, device):

@@ -85,7 +85,9 @@ int validate_layer(const poetx_layer* L) {
   if (L->m < 1 || L->m > kMaxDim || L->n < 1 || L->n > kMaxDim)
     return fail(POETX_ESHAPE, "m=%lld n=%lld out of range [1, %lld]", (long long)L->m, (long long)L->n,
                 (long long)kMaxDim);
-  if (L->flags & ~POETX_ACCUMULATE_GRAD) return fail(POETX_EINVAL, "unknown flags 0x%x", L->flags);
+  if (L->flags & ~(POETX_ACCUMULATE_GRAD | POETX_W0_INT8)) return fail(POETX_EINVAL, "unknown flags 0x%x", L->flags);
+  if ((L->flags & POETX_W0_INT8) && L->dtype != POETX_BF16)
+    return fail(POETX_EDTYPE, "POETX_W0_INT8 applies to bf16 layers");
   return POETX_OK;
 }
 
@@ -286,6 +288,7 @@ struct Shape {
   int64_t m, n, N;
   int b, kR, kP;
   bool f32;
+  bool q8;    // W0p holds INT8 codes and per-row scales (POETX_W0_INT8)
   size_t es;  // element size of activations / weight
 };
 
@@ -295,8 +298,23 @@ Shape shape_of(const poetx_layer* L, int64_t N) {
   S.kR = (int)(L->m / L->b);
   S.kP = (int)(L->n / L->b);
   S.f32 = L->dtype == POETX_F32;
+  S.q8 = (L->flags & POETX_W0_INT8) != 0;
   S.es = S.f32 ? 4 : 2;
   return S;
+}
+
+// INT8 weight format: codes [m][n], then fp32 scales [m] at this byte offset
+size_t w0_scale_offset(int64_t m, int64_t n) { return ((size_t)m * n + kAlign - 1) / kAlign * kAlign; }
+
+// the bf16 weight a pass reads: W0p itself, or (INT8 layers) its codes
+// dequantized into the pass's workspace buffer w0
+const void* weight_for_pass(const Shape& S, const void* W0p, void* w0, hipStream_t s) {
+  if (!S.q8) return W0p;
+  const int8_t* q = static_cast<const int8_t*>(W0p);
+  const float* sc = reinterpret_cast<const float*>(static_cast<const char*>(W0p) + w0_scale_offset(S.m, S.n));
+  Tm tm(s, "dequant", 0.0, (double)S.m * S.n * 3);
+  launch_dequant_rows(q, sc, static_cast<uint16_t*>(w0), S.m, S.n, s);
+  return w0;
 }
 
 // Cayley blocks one forward / backward consumes (built by the call itself,
@@ -315,6 +333,7 @@ struct FwdWs {
   uint16_t *qbR, *qbP;
   void* bws;
   void *z1, *z2, *sc;
+  void* w0;
 };
 FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes) {
   Arena a(base);
@@ -332,6 +351,7 @@ FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes) {
   w.z1 = a.take<char>((size_t)S.N * S.n * S.es);
   w.z2 = a.take<char>((size_t)S.N * S.m * S.es);
   if (!S.f32) w.sc = a.take<char>((size_t)S.N * std::max(S.n, S.m) * S.es);   // permuted rows / block products
+  if (S.q8) w.w0 = a.take<char>((size_t)S.m * S.n * 2);                       // dequantized weight
   *bytes = a.off + kAlign;
   return w;
 }
@@ -343,6 +363,7 @@ struct BwdWs {
   void *z1, *xg, *z2, *gyg, *gz2;
   float *GR, *GP, *tmp;
   void* part;
+  void* w0;
 };
 BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes, bool dq = false) {
   Arena a(base);
@@ -370,6 +391,7 @@ BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes, bool dq = fa
   }
   const size_t pb = std::max(gram_partials_bytes(S.N, S.b, S.kR, S.f32), gram_partials_bytes(S.N, S.b, S.kP, S.f32));
   w.part = a.take<char>(pb);
+  if (S.q8) w.w0 = a.take<char>((size_t)S.m * S.n * 2);   // dequantized weight
   *bytes = a.off + kAlign;
   return w;
 }
@@ -381,6 +403,7 @@ struct MrgWs {
   void* V;
   uint64_t* keys;
   int32_t *snew, *tnew, *sinv, *tinv;
+  void* w0;
 };
 MrgWs plan_merge(const Shape& S, bool own, void* base, size_t* bytes) {
   Arena a(base);
@@ -402,6 +425,7 @@ MrgWs plan_merge(const Shape& S, bool own, void* base, size_t* bytes) {
   w.tnew = a.take<int32_t>(S.n);
   w.sinv = a.take<int32_t>(S.m);
   w.tinv = a.take<int32_t>(S.n);
+  if (S.q8) w.w0 = a.take<char>((size_t)S.m * S.n * 2);   // dequantized weight, merged in place
   *bytes = a.off + kAlign;
   return w;
 }
@@ -706,6 +730,23 @@ int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, 
   return check_launch("merge relayout");
 }
 
+// merge of the layer's stored weight: INT8 layers merge their dequantized
+// weight in the workspace and store its new codes and scales
+int merge_w0(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
+             uint64_t seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
+  if (!S.q8) return merge_core(S, W0p, q, thR, thP, sigma, tau, seed, merge_index, w, s);
+  weight_for_pass(S, W0p, w.w0, s);
+  int rc = merge_core(S, w.w0, q, thR, thP, sigma, tau, seed, merge_index, w, s);
+  if (rc) return rc;
+  int8_t* codes = static_cast<int8_t*>(W0p);
+  float* sc = reinterpret_cast<float*>(static_cast<char*>(W0p) + w0_scale_offset(S.m, S.n));
+  {
+    Tm tm(s, "quantize", 0.0, (double)S.m * S.n * 3);
+    launch_quantize_rows(static_cast<const uint16_t*>(w.w0), codes, sc, S.m, S.n, s);
+  }
+  return check_launch("weight quantization");
+}
+
 Blk blk_of(const poetx_blocks* q) {
   return Blk{q->Q32R, q->Q32P, static_cast<const uint16_t*>(q->QR), static_cast<const uint16_t*>(q->QP),
              static_cast<const uint16_t*>(q->QTR), static_cast<const uint16_t*>(q->QTP)};
@@ -724,7 +765,8 @@ int forward_blocks_impl(const poetx_layer* layer, const void* W0p, const poetx_b
   plan_fwd(S, false, nullptr, &need);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const FwdWs w = plan_fwd(S, false, ws, &need);
-  return fwd_core(S, W0p, blk_of(blocks), sigma, tau, X, Y, w, static_cast<hipStream_t>(stream), Z2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return fwd_core(S, weight_for_pass(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, Y, w, s, Z2);
 }
 
 // poetx_backward_blocks_dq(_z2): Z2 non-null is z2' kept from the forward pass
@@ -748,7 +790,8 @@ int backward_dq_impl(const poetx_layer* layer, const void* W0p, const poetx_bloc
   plan_bwd(S, false, nullptr, &need, true);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const BwdWs w = plan_bwd(S, false, ws, &need, true);
-  return bwd_core(S, W0p, blk_of(blocks), sigma, tau, X, dY, dX, nullptr, nullptr, false, w, s, GR, GP, Z2);
+  return bwd_core(S, weight_for_pass(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, dY, dX, nullptr, nullptr,
+                  false, w, s, GR, GP, Z2);
 }
 
 }  // namespace
@@ -841,7 +884,8 @@ int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR, c
   else rc = build2(thR, S.kR, QOut{nullptr, w.qbR, nullptr}, thP, S.kP, QOut{nullptr, w.qbP, nullptr}, S.b, w.bws,
                    bmode, s);
   if (rc) return rc;
-  return fwd_core(S, W0p, Blk{w.q32R, w.q32P, w.qbR, w.qbP, nullptr, nullptr}, sigma, tau, X, Y, w, s);
+  return fwd_core(S, weight_for_pass(S, W0p, w.w0, s), Blk{w.q32R, w.q32P, w.qbR, w.qbP, nullptr, nullptr}, sigma,
+                  tau, X, Y, w, s);
 }
 
 int poetx_forward_blocks(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
@@ -879,7 +923,8 @@ int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, 
   else rc = build2(thR, S.kR, QOut{w.q32R, nullptr, w.qtR}, thP, S.kP, QOut{w.q32P, w.qbP, w.qtP}, S.b, w.bws,
                    bmode, s);
   if (rc) return rc;
-  return bwd_core(S, W0p, Blk{w.q32R, w.q32P, nullptr, w.qbP, w.qtR, w.qtP}, sigma, tau, X, dY, dX, dthR, dthP,
+  return bwd_core(S, weight_for_pass(S, W0p, w.w0, s), Blk{w.q32R, w.q32P, nullptr, w.qbP, w.qtR, w.qtP}, sigma,
+                  tau, X, dY, dX, dthR, dthP,
                   accum, w, s);
 }
 
@@ -897,7 +942,8 @@ int poetx_backward_blocks(const poetx_layer* layer, const void* W0p, const poetx
   plan_bwd(S, false, nullptr, &need);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const BwdWs w = plan_bwd(S, false, ws, &need);
-  return bwd_core(S, W0p, blk_of(blocks), sigma, tau, X, dY, dX, dthR, dthP, accum, w, s);
+  return bwd_core(S, weight_for_pass(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, dY, dX, dthR, dthP, accum,
+                  w, s);
 }
 
 int poetx_backward_blocks_dq(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
@@ -992,7 +1038,7 @@ int poetx_merge(const poetx_layer* layer, void* W0p, float* thR, float* thP, int
   else rc = build2(thR, S.kR, QOut{nullptr, w.qbR, nullptr}, thP, S.kP, QOut{nullptr, nullptr, w.qtP}, S.b, w.bws,
                    bmode, s);
   if (rc) return rc;
-  return merge_core(S, W0p, Blk{w.q32R, w.q32P, w.qbR, nullptr, nullptr, w.qtP}, thR, thP, sigma, tau, perm_seed,
+  return merge_w0(S, W0p, Blk{w.q32R, w.q32P, w.qbR, nullptr, nullptr, w.qtP}, thR, thP, sigma, tau, perm_seed,
                     merge_index, w, s);
 }
 
@@ -1009,8 +1055,37 @@ int poetx_merge_blocks(const poetx_layer* layer, void* W0p, const poetx_blocks* 
   plan_merge(S, false, nullptr, &need);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const MrgWs w = plan_merge(S, false, ws, &need);
-  return merge_core(S, W0p, blk_of(blocks), thR, thP, sigma, tau, perm_seed, merge_index, w,
+  return merge_w0(S, W0p, blk_of(blocks), thR, thP, sigma, tau, perm_seed, merge_index, w,
                     static_cast<hipStream_t>(stream));
+}
+
+size_t poetx_w0_bytes(const poetx_layer* layer) {
+  if (validate_layer(layer) != POETX_OK) return 0;
+  const Shape S = shape_of(layer, 0);
+  if (S.q8) return w0_scale_offset(S.m, S.n) + (size_t)S.m * sizeof(float);
+  return (size_t)S.m * S.n * S.es;
+}
+
+int poetx_quantize_w0(const poetx_layer* layer, const void* W0bf16, void* W0q, void* stream) {
+  int rc = validate_layer(layer);
+  if (rc) return rc;
+  const Shape S = shape_of(layer, 0);
+  if (!S.q8) return fail(POETX_EINVAL, "layer.flags lacks POETX_W0_INT8");
+  if (!W0bf16 || !W0q) return fail(POETX_EINVAL, "NULL tensor argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_quantize_rows(static_cast<const uint16_t*>(W0bf16), static_cast<int8_t*>(W0q),
+                       reinterpret_cast<float*>(static_cast<char*>(W0q) + w0_scale_offset(S.m, S.n)), S.m, S.n, s);
+  return check_launch("weight quantization");
+}
+
+int poetx_dequantize_w0(const poetx_layer* layer, const void* W0q, void* W0bf16, void* stream) {
+  int rc = validate_layer(layer);
+  if (rc) return rc;
+  const Shape S = shape_of(layer, 0);
+  if (!S.q8) return fail(POETX_EINVAL, "layer.flags lacks POETX_W0_INT8");
+  if (!W0bf16 || !W0q) return fail(POETX_EINVAL, "NULL tensor argument");
+  weight_for_pass(S, W0q, W0bf16, static_cast<hipStream_t>(stream));
+  return check_launch("weight dequantization");
 }
 
 int poetx_make_permutation(uint64_t seed, uint64_t merge_index, int32_t side, int64_t n, int32_t* host_out) {

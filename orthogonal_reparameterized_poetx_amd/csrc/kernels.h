@@ -154,6 +154,9 @@ void launch_copy_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int
 bool launch_relayout_rows_bf16(const uint16_t* V, uint16_t* W, const int32_t* rmap, const int32_t* cmap, int64_t m,
                                int64_t n, hipStream_t s);
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+// INT8 weight codes with per-row fp32 scales (quant.hip)
+void launch_dequant_rows(const int8_t* q, const float* sc, uint16_t* w, int64_t m, int64_t n, hipStream_t s);
+void launch_quantize_rows(const uint16_t* w, int8_t* q, float* sc, int64_t m, int64_t n, hipStream_t s);
 void launch_adam(float* theta, const float* grad, float* m, float* v, int64_t n, float lr, float b1, float b2,
                  float eps, float bc1, float bc2, hipStream_t s);
 

@@ -12,14 +12,20 @@ from . import _lib as L
 
 
 class PoetxLayer:
-    def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0, ws_pool=None):
+    def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0, ws_pool=None, w0_int8=False):
+        """w0_int8: keep W0p in the INT8 weight format (per-row codes and
+        scales, POETX_W0_INT8; bf16 layers), dequantized by every pass."""
         self.device = torch.device(device)
         self.dt = L.POETX_BF16 if dtype == "bf16" else L.POETX_F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.layer = L.Layer(m, n, b, self.dt)
+        self.flags = L.POETX_W0_INT8 if w0_int8 else 0
+        self.layer = L.Layer(m, n, b, self.dt, self.flags)
         self.m, self.n, self.b = m, n, b
         nt = b * (b - 1) // 2
-        self.W0p = torch.zeros(m, n, dtype=self.tdtype, device=self.device)
+        if w0_int8:
+            self.W0p = torch.zeros(L.w0_bytes(self.layer), dtype=torch.uint8, device=self.device)
+        else:
+            self.W0p = torch.zeros(m, n, dtype=self.tdtype, device=self.device)
         self.thR = torch.zeros(m // b, nt, dtype=torch.float32, device=self.device)
         self.thP = torch.zeros(n // b, nt, dtype=torch.float32, device=self.device)
         self.sigma = torch.arange(m, dtype=torch.int32, device=self.device)
@@ -43,8 +49,11 @@ class PoetxLayer:
     def pack(self, W0):
         """Load a true-coordinate weight: identity permutations, zero
         generators, then a merge (an exact relayout) into the first random
-        layout (merge index 0)."""
-        self.W0p.copy_(W0.to(self.tdtype))
+        layout (merge index 0).  INT8 layers quantize W0 first."""
+        if self.flags & L.POETX_W0_INT8:
+            L.poetx_quantize_w0(self.layer, W0.to(self.tdtype).contiguous(), self.W0p)
+        else:
+            self.W0p.copy_(W0.to(self.tdtype))
         self.thR.zero_()
         self.thP.zero_()
         self.sigma.copy_(torch.arange(self.m, dtype=torch.int32, device=self.device))
@@ -68,13 +77,13 @@ class PoetxLayer:
             dthR = torch.empty_like(self.thR)
         if dthP is None:
             dthP = torch.empty_like(self.thP)
-        self.layer.flags = L.POETX_ACCUMULATE_GRAD if accumulate else 0
+        self.layer.flags = self.flags | (L.POETX_ACCUMULATE_GRAD if accumulate else 0)
         ws = self.workspace(L.OP_BACKWARD, N)
         try:
             L.poetx_backward(self.layer, self.W0p, self.thR, self.thP, self.sigma, self.tau, X, dY, N,
                              dX if want_dx else None, dthR, dthP, ws, stream)
         finally:
-            self.layer.flags = 0
+            self.layer.flags = self.flags
         return dX, dthR, dthP
 
     # -- prebuilt blocks: built for many layers at once (build_layer_blocks),
@@ -136,13 +145,13 @@ class PoetxLayer:
             dthR = torch.empty_like(self.thR)
         if dthP is None:
             dthP = torch.empty_like(self.thP)
-        self.layer.flags = L.POETX_ACCUMULATE_GRAD if accumulate else 0
+        self.layer.flags = self.flags | (L.POETX_ACCUMULATE_GRAD if accumulate else 0)
         ws = self.workspace(L.OP_BACKWARD_BLOCKS, N)
         try:
             L.poetx_backward_blocks(self.layer, self.W0p, self.block_buffers("backward")[1], self.sigma, self.tau,
                                     X, dY, N, dX if want_dx else None, dthR, dthP, ws, stream)
         finally:
-            self.layer.flags = 0
+            self.layer.flags = self.flags
         return dX, dthR, dthP
 
     def dq_buffers(self):
@@ -174,6 +183,14 @@ class PoetxLayer:
         L.poetx_backward_blocks_dq_z2(self.layer, self.W0p, self.block_buffers("backward")[1], self.sigma,
                                       self.tau, X, dY, Z2, N, dX if want_dx else None, GR, GP, ws, stream)
         return dX, GR, GP
+
+    def weight(self):
+        """The bf16 working-layout weight the passes use ([m][n])."""
+        if not self.flags & L.POETX_W0_INT8:
+            return self.W0p
+        W = torch.empty(self.m, self.n, dtype=torch.bfloat16, device=self.device)
+        L.poetx_dequantize_w0(self.layer, self.W0p, W)
+        return W
 
     def merge_blocks(self, stream=None):
         """Merge with blocks from build_layer_blocks(..., "merge")."""

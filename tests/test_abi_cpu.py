@@ -230,3 +230,25 @@ def test_stored_z2_entry_points_validate_on_host():
     assert L.poetx_backward_blocks_dq_z2(*bargs(lay, ctypes.byref(bwd), fake, fake, bneed - 1)) == -4
     acc = P.Layer(512, 256, 64, P.POETX_BF16, P.POETX_ACCUMULATE_GRAD)
     assert L.poetx_backward_blocks_dq_z2(*bargs(acc, ctypes.byref(bwd), fake, fake, bneed)) == -1
+
+
+def test_int8_weight_format_validates_on_host():
+    P = _P()
+    L = P.lib()
+    fake = ctypes.c_void_p(0x1000)
+    lay = P.Layer(600, 520, 64, P.POETX_BF16, P.POETX_W0_INT8)
+    # codes, then the scales at the next multiple of 256 bytes
+    assert P.w0_bytes(lay) == (600 * 520 + 255) // 256 * 256 + 4 * 600
+    assert P.w0_bytes(P.Layer(600, 520, 64, P.POETX_BF16)) == 600 * 520 * 2
+    # the dequantized copy is part of every pass's workspace
+    plain = P.Layer(600, 520, 64, P.POETX_BF16)
+    for op in (P.OP_FORWARD, P.OP_BACKWARD, P.OP_FORWARD_BLOCKS, P.OP_BACKWARD_DQ, P.OP_MERGE):
+        assert P.workspace_bytes(lay, 64, op) >= P.workspace_bytes(plain, 64, op) + 600 * 520 * 2
+    # fp32 layers cannot carry the flag; the conversions need it
+    l32 = P.Layer(600, 520, 64, P.POETX_F32, P.POETX_W0_INT8)
+    assert L.poetx_w0_bytes(ctypes.byref(l32)) == 0
+    assert L.poetx_quantize_w0(ctypes.byref(l32), fake, fake, None) == -3
+    assert L.poetx_quantize_w0(ctypes.byref(plain), fake, fake, None) == -1
+    assert L.poetx_dequantize_w0(ctypes.byref(plain), fake, fake, None) == -1
+    assert L.poetx_quantize_w0(ctypes.byref(lay), None, fake, None) == -1
+    assert L.poetx_dequantize_w0(ctypes.byref(lay), fake, None, None) == -1
