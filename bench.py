@@ -52,6 +52,8 @@ KERNEL_CLASSES = [
     ("gram_bf16_kernel", "gram", 2),
     ("gram_stream_kernel", "gram", 2),
     ("gram_reduce_kernel", "gram", 2),
+    ("dequant_rows_kernel", "dequant", 1),
+    ("quantize_rows_kernel", "quantize", 1),
 ]
 CALIBRATION_BYTES = 256 << 20   # the copy kernel reads and writes this many bytes each
 
@@ -89,6 +91,9 @@ def parse():
     ap.add_argument("--chain", choices=["batched", "per-matrix"], default="batched",
                     help="layer set: one chain-rule call for all matrices after the backward pass, or one per "
                          "matrix on its stream")
+    ap.add_argument("--w0-int8", action="store_true",
+                    help="layer set: base weights stored as per-row INT8 codes and scales (POET-XQ), dequantized "
+                         "by every pass")
     ap.add_argument("--keep-z2", action="store_true",
                     help="layer set: the variant without activation recompute (the forward keeps z2' for the "
                          "backward, N*m*2 bytes per matrix); the default recomputes it (POET-Xmem)")
@@ -233,7 +238,7 @@ def kernel_stats(path, steps=None):
 # 24-layer stack of layer-set shapes: one training step over 168 matrices
 # ---------------------------------------------------------------------------
 class Stack:
-    """The 24-layer stack resident in HBM: bf16 W0p per matrix in its working
+    """The 24-layer stack resident in HBM: bf16 (or INT8, w0_int8) W0p per matrix in its working
     layout, all generators (and their gradients and Adam moments) in single
     fp32 buffers so the optimizer step is one launch, and per-matrix inputs,
     upstream gradients and outputs.
@@ -243,7 +248,7 @@ class Stack:
     can check them; the rest draw the same distributions on the device from a
     torch generator seeded by (config, matrix, stream)."""
 
-    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=(), streams=3):
+    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=(), streams=3, w0_int8=False):
         import math
         import numpy as np
         self.P, self.torch, self.N = P, torch, N
@@ -281,7 +286,7 @@ class Stack:
         for l, idx, m, n in mats:
             j = 7 * l + idx
             lay = P.PoetxLayer(m, n, b, "bf16", dev, perm_seed=WL.perm_seed(5, j),
-                               ws_pool=pools[len(mats_done) % self.nstreams])
+                               ws_pool=pools[len(mats_done) % self.nstreams], w0_int8=w0_int8)
             mats_done.append(j)
             kR, kP = m // b, n // b
             lay.thR = self.theta[off:off + kR * nt].view(kR, nt)
@@ -378,7 +383,7 @@ def bench_stack(args):
     dev = "cuda:0"
     torch.cuda.set_device(0)
     N = args.tokens or WL.CONFIGS[5]["N"]
-    st = Stack(P, WL, torch, dev, N, streams=args.streams)
+    st = Stack(P, WL, torch, dev, N, streams=args.streams, w0_int8=args.w0_int8)
     torch.cuda.synchronize()
     resident = torch.cuda.memory_allocated()
     stream = torch.cuda.current_stream()
@@ -407,7 +412,8 @@ def bench_stack(args):
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": k, "warmup": args.warmup,
         "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded Gaussian inputs with the stack's shapes)",
-        "config": {"workload": WL.CONFIGS[5]["name"], "tokens": N, "matrices": len(st.layers), "b": WL.CONFIGS[5]["b"]},
+        "config": {"workload": WL.CONFIGS[5]["name"], "tokens": N, "matrices": len(st.layers), "b": WL.CONFIGS[5]["b"],
+                   "base_weights": "INT8 codes with per-row fp32 scales (POET-XQ)" if args.w0_int8 else "bf16"},
         "phases_ms": {"fwd_bwd": round(fb / k, 3), "adam": round(ad / k, 3), "merge": round(mg / k, 3)},
         "generators": st.theta.numel(),
         "resident_gb": round(resident / 1e9, 3),
@@ -460,7 +466,8 @@ def main():
     layers, Xs, gYs, outs = [], {}, [], []
     for j in range(len(cfg["mats"])):
         inp = WL.matrix_inputs(3, j, N=N)
-        lay = P.PoetxLayer(inp["m"], inp["n"], inp["b"], "bf16", dev, perm_seed=inp["perm_seed"])
+        lay = P.PoetxLayer(inp["m"], inp["n"], inp["b"], "bf16", dev, perm_seed=inp["perm_seed"],
+                           w0_int8=args.w0_int8)
         lay.pack(up(inp["W0"], "bf16"))
         lay.thR.copy_(up(inp["thR"], "f32"))
         lay.thP.copy_(up(inp["thP"], "f32"))
@@ -634,7 +641,9 @@ def main():
                    "batched per pass (Cayley builds and chain rule over all seven matrices)",
                    "streams": 1 if args.per_layer_builds else max(args.streams, 1),
                    "activations": "z2' kept from the forward pass (no recompute)" if args.keep_z2 else
-                   "recomputed in the backward pass (POET-Xmem)"},
+                   "recomputed in the backward pass (POET-Xmem)",
+                   "base_weights": "INT8 codes with per-row fp32 scales, dequantized per pass (POET-XQ)"
+                   if args.w0_int8 else "bf16"},
         "roofline": roof,
         "kernels_per_step": breakdown,
         "merge_ms_layer_set": round(merge_ms, 3),
