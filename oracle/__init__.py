@@ -30,7 +30,9 @@ from .poetx import (  # noqa: F401
     backward,
     block_count,
     cayley,
+    cayley_neumann,
     chain_rule,
+    cnp_error_bound,
     dense_orthogonal,
     dequantize_rows,
     forward,

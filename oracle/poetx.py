@@ -86,11 +86,34 @@ def cayley(S):
 
     For skew S this Q is orthogonal with det +1 [P1 实践 4, step 3].  The
     pages' GPU route replaces the inverse by a truncated Neumann series
-    [P3 "Methodologie" item 4]; the oracle keeps the exact definition.
+    [P3 "Methodologie" item 4]: ``cayley_neumann`` below.
     """
     b = S.shape[0]
     eye = np.eye(b)
     return np.linalg.solve(eye - S, eye + S)
+
+
+def cayley_neumann(S, k):
+    """The truncated Neumann form of the Cayley map [P3 "Methodologie" item 4,
+    CNP]: (I - S)^-1 is the series I + S + S^2 + ... for ||S|| < 1, so
+    Q = (I - S)^-1 (I + S) = I + 2 (S + S^2 + ...); keep the first k powers.
+    Plain powers, float64."""
+    S = np.asarray(S, dtype=np.float64)
+    b = S.shape[0]
+    P = np.eye(b)
+    acc = np.zeros((b, b))
+    for _ in range(k):
+        P = P @ S
+        acc = acc + P
+    return np.eye(b) + 2.0 * acc
+
+
+def cnp_error_bound(S, k):
+    """Bound on ||cayley(S) - cayley_neumann(S, k)||_2: the dropped tail
+    2 (S^{k+1} + S^{k+2} + ...) has norm at most 2 f^{k+1} / (1 - f) with
+    f = ||S||_F >= ||S||_2; infinite when f >= 1 (no convergence bound)."""
+    f = float(np.linalg.norm(np.asarray(S, dtype=np.float64)))
+    return 2.0 * f ** (k + 1) / (1.0 - f) if f < 1.0 else np.inf
 
 
 def block_count(dim, b):

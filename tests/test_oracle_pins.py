@@ -381,3 +381,35 @@ def test_dequantize_rows_matches_torch_rounding():
     s = (np.abs(rng.standard_normal(40)) * 1e-2).astype(np.float32)
     ref = (torch.from_numpy(s)[:, None] * torch.from_numpy(q).to(torch.float32)).to(torch.bfloat16).to(torch.float64)
     assert np.array_equal(O.dequantize_rows(q, s), ref.numpy())
+
+
+# --------------------------------------------------------------------------
+# CNP: truncated Neumann form of the Cayley map [P3 "Methodologie" item 4]
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("k", range(1, 7))
+def test_cayley_neumann_closed_form_b2(k):
+    # S = [[0, a], [-a, 0]] has S^2 = -a^2 I: the odd powers are S (-a^2)^m,
+    # the even ones (-a^2)^m I, so the truncated sums are geometric
+    a = 0.3
+    S = np.array([[0.0, a], [-a, 0.0]])
+    odd = sum((-a * a) ** m for m in range((k - 1) // 2 + 1))          # j = 2m + 1 <= k
+    even = sum((-a * a) ** m for m in range(1, k // 2 + 1))           # j = 2m <= k, m >= 1
+    want = np.eye(2) + 2.0 * (odd * S + even * np.eye(2))
+    assert np.allclose(O.cayley_neumann(S, k), want, rtol=0, atol=1e-15)
+
+
+def test_cayley_neumann_limits_and_bound():
+    assert np.array_equal(O.cayley_neumann(np.zeros((8, 8)), 5), np.eye(8))
+    rng = np.random.default_rng(21)
+    for b, scale in [(8, 0.05), (32, 0.004), (64, 0.001)]:
+        S = O.unpack_skew(rng.standard_normal(b * (b - 1) // 2) * scale, b)
+        assert np.array_equal(O.cayley_neumann(S, 1), np.eye(b) + 2.0 * S)
+        exact = O.cayley(S)
+        prev = np.inf
+        for k in range(1, 9):
+            err = np.linalg.norm(O.cayley_neumann(S, k) - exact, 2)
+            assert err <= O.cnp_error_bound(S, k) * (1 + 1e-9) + 1e-14
+            assert err <= prev + 1e-15          # more terms never hurt while ||S|| < 1
+            prev = err
+    big = O.unpack_skew(rng.standard_normal(64 * 63 // 2) * 0.1, 64)
+    assert O.cnp_error_bound(big, 6) == np.inf
