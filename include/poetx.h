@@ -197,6 +197,24 @@ int poetx_build_block_sets(const poetx_block_set* sets, int32_t count, int32_t b
                            size_t ws_bytes, void* stream);
 
 /*
+ * poetx_build_block_sets with the truncated Neumann (CNP) form of the Cayley
+ * map where it is accurate enough [P3 item 4]: (I - S)^-1 = I + S + S^2 + ...
+ * for ||S|| < 1, so Q = I + 2 (S + S^2 + ... + S^terms) with `terms` powers
+ * kept.  A block takes this form only when the dropped tail is provably
+ * small: f = ||S||_F < 1 and 2 f^(terms+1) / (1 - f) <= 2^-22 (a bound on
+ * its spectral norm); every other block gets the exact solve, bit for bit as
+ * poetx_build_block_sets builds it.  The powers are fp32-accurate products.
+ * With the generators at zero (right after a merge) every block takes the
+ * series.
+ *   terms  1..16
+ *   b      32, 64, 128 or 256; at most 65535 blocks per set and per call
+ *   ws     poetx_build_cnp_workspace_bytes(total blocks of the call, b)
+ */
+size_t poetx_build_cnp_workspace_bytes(int64_t total_blocks, int32_t b);
+int poetx_build_block_sets_cnp(const poetx_block_set* sets, int32_t count, int32_t b, int32_t terms,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
  * a3-a5: forward Y = X W^T, W = R W0 P, computed input-centrically as
  * P, then W0, then R on each token [P3 item 1], with P and R applied as
  * gathers/scatters and batched block products [P3 items 2-3].

@@ -22,7 +22,8 @@ _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDT
            -4: "POETX_EWORKSPACE", -5: "POETX_EHIP"}
 
 EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
-            "poetx_build_block_sets", "poetx_forward", "poetx_forward_blocks", "poetx_backward",
+            "poetx_build_block_sets", "poetx_build_cnp_workspace_bytes", "poetx_build_block_sets_cnp",
+            "poetx_forward", "poetx_forward_blocks", "poetx_backward",
             "poetx_backward_blocks", "poetx_backward_blocks_dq", "poetx_forward_blocks_z2",
             "poetx_backward_blocks_dq_z2", "poetx_chain_rule_sets",
             "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_make_permutation",
@@ -102,6 +103,8 @@ def lib():
         "poetx_build_workspace_bytes": (sz, [i64, i32]),
         "poetx_build_blocks": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
         "poetx_build_block_sets": (ctypes.c_int, [ctypes.POINTER(BlockSet), i32, i32, vp, sz, vp]),
+        "poetx_build_cnp_workspace_bytes": (sz, [i64, i32]),
+        "poetx_build_block_sets_cnp": (ctypes.c_int, [ctypes.POINTER(BlockSet), i32, i32, i32, vp, sz, vp]),
         "poetx_forward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "poetx_forward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, i64, vp, vp, sz, vp]),
         "poetx_backward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
@@ -201,6 +204,23 @@ def poetx_build_block_sets(sets, b, ws=None, stream=None):
     nbytes = ws.numel() if ws is not None else 0
     _check("poetx_build_block_sets", lib().poetx_build_block_sets(arr, len(sets), int(b), _ptr(ws), nbytes,
                                                                   _stream(stream)))
+
+
+def build_cnp_workspace_bytes(total_blocks, b):
+    n = lib().poetx_build_cnp_workspace_bytes(int(total_blocks), int(b))
+    if n == 0:
+        raise PoetxError("poetx_build_cnp_workspace_bytes", -1, last_error())
+    return n
+
+
+def poetx_build_block_sets_cnp(sets, b, terms, ws=None, stream=None):
+    """poetx_build_block_sets with the truncated Cayley series where its bound allows."""
+    arr = (BlockSet * max(len(sets), 1))()
+    for i, (th, nb, q32, qbf, qt) in enumerate(sets):
+        arr[i] = BlockSet(_addr(th), int(nb), _addr(q32), _addr(qbf), _addr(qt))
+    nbytes = ws.numel() if ws is not None else 0
+    _check("poetx_build_block_sets_cnp", lib().poetx_build_block_sets_cnp(arr, len(sets), int(b), int(terms),
+                                                                          _ptr(ws), nbytes, _stream(stream)))
 
 
 def poetx_forward_blocks(layer, W0p, blocks, sigma, tau, X, N, Y, ws, stream=None):

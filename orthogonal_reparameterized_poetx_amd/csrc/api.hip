@@ -74,6 +74,10 @@ struct Tm {
 
 constexpr int64_t kMaxDim = 32768;
 constexpr size_t kAlign = 256;
+// tolerance of the truncated Cayley series: bound on the spectral norm of its
+// dropped tail, two fp32 ulps of 1, so that even summed over a 256-wide block
+// (sqrt(256) times) it stays below the 1e-5 fp32 tolerance of the outputs
+constexpr float kCnpTol = 1.0f / (1 << 22);
 
 bool valid_b(int32_t b) { return b == 32 || b == 64 || b == 128 || b == 256 || b == 512; }
 
@@ -181,16 +185,20 @@ int build_schur512(const float* theta, int64_t nblk, QOut o, void* ws, int mode,
 // products (fp32-level accuracy); mode 0: fp32 MFMA.  Both give Q accurate
 // to fp32 rounding.  b = 512 goes batch by batch through the Schur path (ws
 // sized for the largest batch).
+// skip (b <= 256): blocks in the order of the sets (empty sets left out)
+// whose flag is set are not built here
 int build_sets(const float* const* theta, const int64_t* nblk, const QOut* out, int nsets, int b, void* ws, int mode,
-               hipStream_t s) {
+               hipStream_t s, const int* skip = nullptr) {
   int64_t total = 0;
   for (int i = 0; i < nsets; ++i) total += nblk[i];
   if (total <= 0) return POETX_OK;
   Tm tm(s, "cayley_build", 2.0 * b * (double)b * b * total, 0.0);
   if (b <= 256) {
     int i = 0;
+    int64_t first = 0;   // index of this launch's first block among all
     while (i < nsets) {
       GJArgs g{};
+      g.skip = skip ? skip + first : nullptr;
       int launched = 0;
       for (; i < nsets && g.nseg < GJ_MAXSEG; ++i) {
         if (nblk[i] <= 0) continue;
@@ -201,6 +209,7 @@ int build_sets(const float* const* theta, const int64_t* nblk, const QOut* out, 
       }
       g.start[g.nseg] = launched;
       if (launched > 0) launch_gj(b, mode, launched, g, s);
+      first += launched;
     }
     return check_launch("cayley builder");
   }
@@ -862,6 +871,89 @@ int poetx_build_block_sets(const poetx_block_set* sets, int32_t count, int32_t b
     out[(size_t)i] = QOut{sets[i].Q32, static_cast<uint16_t*>(sets[i].Qbf16), static_cast<uint16_t*>(sets[i].QTbf16)};
   }
   return build_sets(th.data(), nb.data(), out.data(), count, b, ws, 6, static_cast<hipStream_t>(stream));
+}
+
+size_t poetx_build_cnp_workspace_bytes(int64_t total_blocks, int32_t b) {
+  if (!valid_b(b) || b > 256 || total_blocks < 0) {
+    fail(POETX_EINVAL, "bad CNP request total_blocks=%lld b=%d", (long long)total_blocks, b);
+    return 0;
+  }
+  const size_t bb = (size_t)b * b;
+  Arena a(nullptr);
+  a.take<float>((size_t)total_blocks * bb);   // S
+  a.take<float>((size_t)total_blocks * bb);   // Horner buffers
+  a.take<float>((size_t)total_blocks * bb);
+  a.take<int>((size_t)total_blocks);          // per-block choice
+  return a.off + kAlign;
+}
+
+int poetx_build_block_sets_cnp(const poetx_block_set* sets, int32_t count, int32_t b, int32_t terms, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!valid_b(b) || b > 256) return fail(POETX_EINVAL, "block size b=%d not in {32,64,128,256}", b);
+  if (terms < 1 || terms > 16) return fail(POETX_EINVAL, "terms=%d out of range [1, 16]", terms);
+  if (count < 0 || count > 4096) return fail(POETX_ESHAPE, "count=%d out of range [0, 4096]", count);
+  if (count > 0 && !sets) return fail(POETX_EINVAL, "sets is NULL");
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const poetx_block_set& t = sets[i];
+    if (t.nblocks < 0 || t.nblocks > 65535) return fail(POETX_ESHAPE, "set %d: nblocks=%lld", i, (long long)t.nblocks);
+    if (t.nblocks == 0) continue;
+    if (!t.theta) return fail(POETX_EINVAL, "set %d: theta is NULL", i);
+    if (!t.Q32 && !t.Qbf16 && !t.QTbf16) return fail(POETX_EINVAL, "set %d: no output requested", i);
+    total += t.nblocks;
+  }
+  if (total > 65535) return fail(POETX_ESHAPE, "%lld blocks in one call (at most 65535)", (long long)total);
+  if (total == 0) return POETX_OK;
+  int rc = check_ws(ws, ws_bytes, poetx_build_cnp_workspace_bytes(total, b));
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t bb = (size_t)b * b;
+  Arena a(ws);
+  float* S = a.take<float>((size_t)total * bb);
+  float* T[2] = {a.take<float>((size_t)total * bb), a.take<float>((size_t)total * bb)};
+  int* use = a.take<int>((size_t)total);
+  std::vector<const float*> th;
+  std::vector<int64_t> nb;
+  std::vector<QOut> out;
+  for (int i = 0; i < count; ++i) {
+    if (sets[i].nblocks == 0) continue;
+    th.push_back(sets[i].theta);
+    nb.push_back(sets[i].nblocks);
+    out.push_back(QOut{sets[i].Q32, static_cast<uint16_t*>(sets[i].Qbf16), static_cast<uint16_t*>(sets[i].QTbf16)});
+  }
+  {
+    Tm tm(s, "cayley_cnp", 4.0 * (terms - 1) * (double)b * bb * total, 0.0);
+    int64_t off = 0;
+    for (size_t i = 0; i < th.size(); ++i) {
+      launch_cnp_unpack_s(th[i], b, (int)nb[i], S + off * bb, s);
+      off += nb[i];
+    }
+    launch_cnp_guard(S, b, (int)total, terms, kCnpTol, use, s);
+    // Horner: T_1 = S, T_j = S (I + T_{j-1}), fp32-accurate split products,
+    // only for the blocks that take the series
+    const float* cur = S;
+    for (int j = 2; j <= terms; ++j) {
+      BGemmArgs q{};
+      q.M = q.N = q.K = b;
+      q.A = S; q.sA = (int64_t)bb; q.lda = b;
+      q.B = cur; q.sB = (int64_t)bb; q.ldb = b; q.addIB = 1;
+      q.C = T[j & 1]; q.sC = (int64_t)bb; q.ldc = b;
+      q.alpha = 1.f; q.beta = 0.f;
+      q.nb0 = (int)total;
+      q.run = use;
+      launch_bgemm(6, (int)total, q, s);
+      cur = q.C;
+    }
+    off = 0;
+    for (size_t i = 0; i < th.size(); ++i) {
+      launch_cnp_finalize(cur + off * bb, use + off, b, (int)nb[i], out[i].q32, out[i].qbf, out[i].qtbf, s);
+      off += nb[i];
+    }
+    if ((rc = check_launch("truncated-series builder"))) return rc;
+  }
+  // every other block: the exact solve (nothing else in the workspace is
+  // needed for b <= 256)
+  return build_sets(th.data(), nb.data(), out.data(), (int)th.size(), b, nullptr, 6, s, use);
 }
 
 int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR, const float* thP,

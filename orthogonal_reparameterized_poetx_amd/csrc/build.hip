@@ -63,6 +63,7 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
   bf16* OpB = reinterpret_cast<bf16*>(gj_lds + OFF_OPB);      // new A[K, :]^T split h|m|l, [j][kk]
   static_assert(!X6 || B < 256 || STAGE_TRI, "the packed triangle fits in the panel buffers");
 
+  if (g.skip && g.skip[blockIdx.x]) return;   // built another way (truncated series)
   int seg = 0;
   while (seg + 1 < g.nseg && (int)blockIdx.x >= g.start[seg + 1]) ++seg;
   const int blk = (int)blockIdx.x - g.start[seg];
@@ -409,6 +410,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
   const int wi = wave >> 1, wj = wave & 1;
   const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
   const int64_t bz = blockIdx.z;
+  if (a.run && !a.run[bz]) return;
   const bool second = bz >= a.nb0;
   const int64_t z1 = bz - a.nb0;
   const float* A = (second && a.A1) ? a.A1 + z1 * a.sA : a.A + bz * a.sA;

@@ -24,6 +24,7 @@ struct GJArgs {
   float* out;           // optional M output (strided)
   int64_t out_stride;
   int out_ld;
+  const int* skip;      // optional: workgroup w does nothing when skip[w] != 0
 };
 // mode 0: fp32 MFMA trailing updates; mode 6: split bf16 x6 (fp32-level accuracy)
 void launch_gj(int B, int mode, int nblk, const GJArgs& g, hipStream_t s);
@@ -37,11 +38,18 @@ struct BGemmArgs {
   // optional second segment: batch items z >= nb0 use A1 / B1 / C1 (when set)
   // at index z - nb0 instead of A / B / C at index z
   const float* A1; const float* B1; float* C1; int nb0;
+  // optional: batch item z is computed only when run[z] != 0
+  const int* run;
 };
 // mode 0: fp32 MFMA; 3 / 6: split bf16 x3 / x6
 void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s);
 void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s);
 void launch_finalize_q(const float* M, int b, int nblk, float* q32, uint16_t* qbf, uint16_t* qtbf, hipStream_t s);
+// truncated Neumann (CNP) builder pieces (cnp.hip)
+void launch_cnp_unpack_s(const float* theta, int b, int nblk, float* S, hipStream_t s);
+void launch_cnp_guard(const float* S, int b, int nblk, int terms, float tol, int* use, hipStream_t s);
+void launch_cnp_finalize(const float* T, const int* use, int b, int nblk, float* q32, uint16_t* qbf, uint16_t* qtbf,
+                         hipStream_t s);
 // chain rule over blocks from up to CH_MAXSEG sources: block z of a launch
 // belongs to the segment s with start[s] <= z < start[s+1] and is block
 // z - start[s] of that segment's arrays (q: fp32 Q, g: dL/dQ, dth: output).

@@ -252,3 +252,26 @@ def test_int8_weight_format_validates_on_host():
     assert L.poetx_dequantize_w0(ctypes.byref(plain), fake, fake, None) == -1
     assert L.poetx_quantize_w0(ctypes.byref(lay), None, fake, None) == -1
     assert L.poetx_dequantize_w0(ctypes.byref(lay), fake, None, None) == -1
+
+
+def test_cnp_builder_validates_on_host():
+    P = _P()
+    L = P.lib()
+    S = P.BlockSet
+    one = (S * 1)(S(0x1000, 4, 0x2000, None, None))
+    need = P.build_cnp_workspace_bytes(4, 64)
+    assert need > 3 * 4 * 64 * 64 * 4
+    fake = ctypes.c_void_p(0x100000)
+    assert L.poetx_build_cnp_workspace_bytes(4, 512) == 0          # b = 512 has no series path
+    assert L.poetx_build_block_sets_cnp(one, 1, 512, 4, fake, 1 << 30, None) == -1
+    assert L.poetx_build_block_sets_cnp(one, 1, 64, 0, fake, need, None) == -1
+    assert L.poetx_build_block_sets_cnp(one, 1, 64, 17, fake, need, None) == -1
+    assert L.poetx_build_block_sets_cnp(one, -1, 64, 4, fake, need, None) == -2
+    assert L.poetx_build_block_sets_cnp(None, 1, 64, 4, fake, need, None) == -1
+    assert L.poetx_build_block_sets_cnp(one, 1, 64, 4, fake, need - 1, None) == -4
+    assert L.poetx_build_block_sets_cnp(one, 1, 64, 4, None, 0, None) == -4
+    big = (S * 2)(S(0x1000, 40000, 0x2000, None, None), S(0x1000, 40000, 0x2000, None, None))
+    assert L.poetx_build_block_sets_cnp(big, 2, 64, 4, fake, 1 << 40, None) == -2
+    assert L.poetx_build_block_sets_cnp((S * 1)(S(0x1000, 70000, 0x2000, None, None)), 1, 64, 4, fake, 1 << 40,
+                                        None) == -2
+    assert L.poetx_build_block_sets_cnp((S * 1)(S(None, 0, None, None, None)), 1, 64, 4, None, 0, None) == 0
