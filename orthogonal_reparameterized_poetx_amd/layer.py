@@ -209,15 +209,25 @@ class PoetxLayer:
 _build_ws = {}
 
 
-def build_layer_blocks(layers, kind, stream=None):
+def build_layer_blocks(layers, kind, stream=None, cnp_terms=0):
     """Build the Cayley blocks of every layer for kind ("forward",
     "backward" or "merge") with one poetx_build_block_sets call per block
-    size, so the builder's grid spans the blocks of all the layers."""
+    size, so the builder's grid spans the blocks of all the layers.
+    cnp_terms > 0 (b <= 256): poetx_build_block_sets_cnp with that many
+    series terms (the truncated series where its bound allows)."""
     by_b = {}
     for lay in layers:
         by_b.setdefault(lay.b, []).extend(lay.block_sets(kind))
     for b, sets in by_b.items():
         dev = layers[0].device
+        if cnp_terms and b <= 256:
+            need = L.build_cnp_workspace_bytes(sum(s[1] for s in sets), b)
+            ws = _build_ws.get((dev, b, kind, "cnp"))
+            if ws is None or ws.numel() < need:
+                ws = L.make_workspace(need, dev)
+                _build_ws[(dev, b, kind, "cnp")] = ws
+            L.poetx_build_block_sets_cnp(sets, b, cnp_terms, ws, stream)
+            continue
         need = L.build_workspace_bytes(max(s[1] for s in sets), b)
         # one workspace per kind: builds of different kinds may run
         # concurrently on different streams
