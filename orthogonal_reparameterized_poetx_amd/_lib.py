@@ -148,11 +148,19 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def stream_handle(stream):
+    """The raw hipStream_t (an int) of a torch.cuda.Stream, a raw handle
+    given as an int, or None (torch's current stream)."""
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return int(stream.cuda_stream)
+    return int(stream)
+
+
 def _stream(stream):
-    if stream is not None:
-        return ctypes.c_void_p(int(stream))
-    import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream_handle(stream))
 
 
 def workspace_bytes(layer, N, op):

@@ -256,7 +256,7 @@ def chain_rule_layers(layers, grads, accumulate=False, stream=None):
         need = L.chain_workspace_bytes(sum(s[2] for s in sets), b)
         # one workspace per stream: chain rules of different layers may run
         # concurrently on different streams
-        sid = stream.cuda_stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        sid = L.stream_handle(stream)
         ws = _chain_ws.get((dev, b, sid))
         if need and (ws is None or ws.numel() < need):
             ws = L.make_workspace(need, dev)

@@ -275,3 +275,17 @@ def test_cnp_builder_validates_on_host():
     assert L.poetx_build_block_sets_cnp((S * 1)(S(0x1000, 70000, 0x2000, None, None)), 1, 64, 4, fake, 1 << 40,
                                         None) == -2
     assert L.poetx_build_block_sets_cnp((S * 1)(S(None, 0, None, None, None)), 1, 64, 4, None, 0, None) == 0
+
+
+def test_stream_handle_normalization():
+    """Every wrapper takes a torch.cuda.Stream-like object (its cuda_stream
+    handle), a raw handle as an int, or None (torch's current stream)."""
+    P = _P()
+    from orthogonal_reparameterized_poetx_amd import _lib
+
+    class FakeStream:
+        cuda_stream = 0x1234
+
+    assert _lib.stream_handle(FakeStream()) == 0x1234
+    assert _lib.stream_handle(0x5678) == 0x5678
+    assert _lib._stream(FakeStream()).value == 0x1234

@@ -312,6 +312,106 @@ def test_contract_mode_outputs_are_bf16_and_close():
         assert np.linalg.norm(c - e) <= 3e-2 * np.linalg.norm(e)
 
 
+# Exact rational arithmetic for the rounding-point pin below: products of
+# bf16 values are formed without error and rounded to bf16 once, by integer
+# arithmetic on the fraction (no float64 step).
+def _bf16_exact(x):
+    from fractions import Fraction
+    x = Fraction(x)
+    if x == 0:
+        return x
+    sgn, a = (1, x) if x > 0 else (-1, -x)
+    # e with 2^(e-1) <= a < 2^e, then the spacing of 8 significant bits
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** (e - 1) > a:
+        e -= 1
+    while Fraction(2) ** e <= a:
+        e += 1
+    q = Fraction(2) ** (e - 8)
+    r = a / q
+    fl = r.numerator // r.denominator
+    rem = r - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * q
+
+
+def _frac_mat(a):
+    from fractions import Fraction
+    return [[Fraction(float(v)) for v in row] for row in np.atleast_2d(a)]
+
+
+def _fmatmul(A, B):
+    return [[sum(A[i][k] * B[k][j] for k in range(len(B))) for j in range(len(B[0]))] for i in range(len(A))]
+
+
+def _ftrans(A):
+    return [list(r) for r in zip(*A)]
+
+
+def _fround(A):
+    return [[_bf16_exact(v) for v in row] for row in A]
+
+
+def _dense_from_b2(theta, perm, dim):
+    """Pi^T diag(Q_0.., I) Pi for b = 2, each Q_l in closed form as exact
+    rationals, rounded to bf16: Q = [[c, s], [-s, c]], c = (1-a^2)/(1+a^2),
+    s = 2a/(1+a^2) for the generator a; gather convention (Pi v)_i = v[perm[i]]."""
+    from fractions import Fraction
+    D = [[Fraction(int(i == j)) for j in range(dim)] for i in range(dim)]
+    for l, a in enumerate(np.asarray(theta)[:, 0]):
+        a = Fraction(float(a))
+        c, s = (1 - a * a) / (1 + a * a), 2 * a / (1 + a * a)
+        q = [[c, s], [-s, c]]
+        for i in range(2):
+            for j in range(2):
+                D[2 * l + i][2 * l + j] = _bf16_exact(q[i][j])
+    Pi = [[Fraction(int(perm[i] == j)) for j in range(dim)] for i in range(dim)]
+    return _fmatmul(_ftrans(Pi), _fmatmul(D, Pi))
+
+
+def test_contract_mode_rounding_points_exact():
+    """Every stored bf16 intermediate of the contract mode (z1, z2, Y, gZ2,
+    gZ1, dX) equals the exactly computed product of its rounded inputs,
+    rounded to bf16 once, and the fp32-kept reductions G_R, G_P are the plain
+    sums of products of those rounded values [P1 实践 5: low-precision storage,
+    high-precision accumulation].  The route is independent of the oracle's:
+    dense permuted block matrices with b = 2 blocks in closed form, exact
+    rational arithmetic, and rounding by integer arithmetic.  Identity tails on
+    both sides (m, n odd)."""
+    rng = np.random.default_rng(77)
+    m, n, b, N = 9, 7, 2, 5
+    W0 = O.round_bf16(rng.standard_normal((m, n)) * 0.4)
+    X = O.round_bf16(rng.standard_normal((N, n)))
+    gY = O.round_bf16(rng.standard_normal((N, m)))
+    thR = _rand_theta(rng, m // b, b, 0.7)
+    thP = _rand_theta(rng, n // b, b, 0.7)
+    sigma = O.make_permutation(91, 0, 0, m)
+    tau = O.make_permutation(91, 0, 1, n)
+    dXo, dRo, dPo, it = O.backward(W0, thR, thP, sigma, tau, X, gY, b, contract=True, intermediates=True)
+    Yo = O.forward(W0, thR, thP, sigma, tau, X, b, contract=True)
+
+    Rm = _dense_from_b2(thR, sigma, m)
+    Pm = _dense_from_b2(thP, tau, n)
+    Wf, Xf, gf = _frac_mat(W0), _frac_mat(X), _frac_mat(gY)
+    Z1 = _fround(_fmatmul(Xf, _ftrans(Pm)))
+    Z2 = _fround(_fmatmul(Z1, _ftrans(Wf)))
+    Y = _fround(_fmatmul(Z2, _ftrans(Rm)))
+    gZ2 = _fround(_fmatmul(gf, Rm))
+    gZ1 = _fround(_fmatmul(gZ2, Wf))
+    dX = _fround(_fmatmul(gZ1, Pm))
+    as64 = lambda A: np.array([[float(v) for v in r] for r in A])
+    for name, want, got in (("Z1", Z1, it["Z1"]), ("Z2", Z2, it["Z2"]), ("Y", Y, Yo), ("gZ2", gZ2, it["gZ2"]),
+                            ("gZ1", gZ1, it["gZ1"]), ("dX", dX, dXo)):
+        assert np.array_equal(as64(want), got), name
+    # G_l = (upstream rows)^T (kept activation rows) over the group's columns
+    for G, up, act, perm in ((it["GR"], gf, Z2, sigma), (it["GP"], gZ1, Xf, tau)):
+        for l, Gl in enumerate(G):
+            cols = perm[2 * l:2 * l + 2]
+            want = [[sum(up[t][cols[i]] * act[t][cols[j]] for t in range(N)) for j in range(2)] for i in range(2)]
+            assert np.allclose(as64(want), Gl, rtol=1e-14, atol=1e-14)
+
+
 # ------------------------------------------------------------------- Adam ---
 def test_adam_first_step_closed_form():
     g = np.array([0.5, -2.0, 1e-3, 0.0])
@@ -396,6 +496,30 @@ def test_cayley_neumann_closed_form_b2(k):
     even = sum((-a * a) ** m for m in range(1, k // 2 + 1))           # j = 2m <= k, m >= 1
     want = np.eye(2) + 2.0 * (odd * S + even * np.eye(2))
     assert np.allclose(O.cayley_neumann(S, k), want, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("k", range(1, 7))
+def test_cnp_error_bound_two_sided_b2(k):
+    """At b = 2, S = [[0, a], [-a, 0]]: the dropped tail 2 S^(k+1) (I - S)^-1
+    is a scaled rotation, so its 2-norm is 2|a|^(k+1) / sqrt(1 + a^2) exactly
+    ((I - S)^-1 = (I + S)/(1 + a^2)).  The bound uses f = ||S||_F = sqrt(2)|a|,
+    so bound / tail = 2^((k+1)/2) sqrt(1 + a^2) / (1 - f): never below 1, and
+    for small a it tends to 2^((k+1)/2), the Frobenius-to-spectral slack of S
+    to the power k+1.  A bound one power too loose (f^k) would exceed that
+    limit by 1/f."""
+    for a in (1e-4, 0.05, 0.3, -0.2):
+        S = np.array([[0.0, a], [-a, 0.0]])
+        tail = np.linalg.norm(O.cayley(S) - O.cayley_neumann(S, k), 2)
+        want_tail = 2.0 * abs(a) ** (k + 1) / np.sqrt(1.0 + a * a)
+        # the difference of two O(1) float64 matrices: absolute error ~1e-16
+        assert abs(tail - want_tail) <= 1e-14
+        bound = O.cnp_error_bound(S, k)
+        assert bound >= want_tail * (1 - 1e-12)
+        lo = 2.0 ** ((k + 1) / 2)
+        hi = lo * np.sqrt(1 + a * a) / (1 - np.sqrt(2) * abs(a))
+        assert lo * (1 - 1e-12) <= bound / want_tail <= hi * (1 + 1e-12)
+        if abs(a) <= 1e-4:
+            assert bound / want_tail <= lo * (1 + 2e-4)
 
 
 def test_cayley_neumann_limits_and_bound():
