@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import workloads as WL
-from gpu_util import compare, from_dev, make_layer, oracle_perms, to_dev, torch_mod
+from gpu_util import compare, from_dev, layer_floors, make_layer, oracle_perms, to_dev, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -35,9 +35,11 @@ def test_block_sets_match_single_builds(b, counts):
     rng = np.random.default_rng(1000 + b)
     dev = "cuda:0"
     nt = b * (b - 1) // 2
-    sets, single = [], []
+    sets, single, host = [], [], []
     for i, nb in enumerate(counts):
-        th = to_dev((rng.standard_normal((max(nb, 1), nt)) * np.sqrt(1e-3)).astype(np.float32)[:nb], "f32")
+        th_h = (rng.standard_normal((max(nb, 1), nt)) * np.sqrt(1e-3)).astype(np.float32)[:nb]
+        host.append(th_h)
+        th = to_dev(th_h, "f32")
         # vary which outputs a set asks for
         want = [(True, True, True), (True, False, False), (False, True, True), (False, False, True)][i % 4]
         q32 = torch.full((nb, b, b), np.nan, dtype=torch.float32, device=dev) if want[0] else None
@@ -57,9 +59,10 @@ def test_block_sets_match_single_builds(b, counts):
             if got is not None:
                 assert torch.equal(got, want)
     # one spot check against the oracle
-    th, nb, q32, _, _ = next(s for s in sets if s[1] > 0 and s[2] is not None)
-    ref = oracle.cayley(oracle.unpack_skew(from_dev(th)[0], b))
-    compare(from_dev(q32)[0], ref, "f32", "Q32[0]")
+    i = next(i for i, s in enumerate(sets) if s[1] > 0 and s[2] is not None)
+    ref = oracle.cayley(oracle.unpack_skew(host[i][0].astype(np.float64), b))
+    # the solve's accuracy is absolute: see test_build_blocks
+    compare(from_dev(sets[i][2])[0], ref, "f32", "Q32[0]", max_strict=1.0)
 
 
 LAYER_GROUPS = [
@@ -94,13 +97,15 @@ def test_prebuilt_blocks_match_self_building_calls(dtype, shapes, b, N):
         sigma, tau = oracle_perms(inp, 0)
         args = (inp["W0"][1], inp["thR"][1], inp["thP"][1], sigma, tau, inp["X"][1])
         contract = dtype == "bf16"
-        compare(from_dev(Yb), oracle.forward(*args, b, contract=contract), dtype, "Y")
-        dXr, dRr, dPr = oracle.backward(*args, inp["gY"][1], b, contract=contract)
-        compare(from_dev(dXb), dXr, dtype, "dX")
+        dXr, dRr, dPr, it = oracle.backward(*args, inp["gY"][1], b, contract=contract, intermediates=True)
+        fl = layer_floors(inp["W0"][1], it)
+        bk, sk = ("bf16", "sum") if contract else ("f32", "f32")
+        compare(from_dev(Yb), oracle.forward(*args, b, contract=contract), bk, "Y", floor=fl["Y"] if contract else None)
+        compare(from_dev(dXb), dXr, bk, "dX", floor=fl["dX"] if contract else None)
         if dRr.size:
-            compare(from_dev(dRb), dRr, dtype, "dthR")
+            compare(from_dev(dRb), dRr, sk, "dthR", terms=N)
         if dPr.size:
-            compare(from_dev(dPb), dPr, dtype, "dthP")
+            compare(from_dev(dPb), dPr, sk, "dthP", terms=N)
 
 
 def test_prebuilt_backward_accumulate_and_empty():
@@ -177,14 +182,18 @@ def test_deferred_chain_matches_backward_blocks(shapes, b, N):
     (600, 520, 256, 70),     # identity tails on both sides
     (2048, 2048, 256, 45),   # the 64-deep GEMM ring (K >= 2048)
     (1100, 700, 512, 24),
+    (2048, 2048, 256, 4096),  # the square layer's shape and token count
 ])
 def test_stored_z2_matches_recompute(m, n, b, N):
     """The variant that keeps z2' from the forward pass gives the results of
-    the recomputing one bit for bit, and its z2' is the oracle's Z2 in the
-    working (sigma-gathered) layout."""
+    the recomputing one bit for bit; its z2' is the oracle's Z2 in the working
+    (sigma-gathered) layout, with a relative rms deviation below ETA (the
+    bound the token-sum floors rest on); and its Y, dX, dL/dQ and (through
+    the batched chain rule) dtheta meet the oracle bounds directly."""
     torch = torch_mod()
-    from orthogonal_reparameterized_poetx_amd import build_layer_blocks
-    inp = WL.small_case(80, m, n, b, N, dtype="bf16")
+    from gpu_util import ETA_BF16
+    from orthogonal_reparameterized_poetx_amd import build_layer_blocks, chain_rule_layers
+    inp = WL.small_case(80, m, n, b, N, dtype="bf16") if N < 1000 else WL.matrix_inputs(2, 0)
     lay, d = make_layer(inp)
     _log("stored z2 m=%d n=%d b=%d N=%d" % (m, n, b, N))
     build_layer_blocks([lay], "forward")
@@ -194,15 +203,28 @@ def test_stored_z2_matches_recompute(m, n, b, N):
     Z2 = torch.full((N, m), float("nan"), dtype=torch.bfloat16, device="cuda:0")
     Y1, _ = lay.forward_blocks_z2(d["X"], Z2=Z2)
     dX1, GR1, GP1 = lay.backward_blocks_dq_z2(d["X"], d["gY"], Z2)
+    dR, dP = torch.empty_like(lay.thR), torch.empty_like(lay.thP)
+    chain_rule_layers([lay], [(dR, dP)])
     torch.cuda.synchronize()
     assert torch.equal(Y0, Y1) and torch.equal(dX0, dX1)
     assert torch.equal(GR0, GR1) and torch.equal(GP0, GP1)
     sigma, tau = oracle_perms(inp, 0)
-    _, mid = oracle.forward(inp["W0"][1], inp["thR"][1], inp["thP"][1], sigma, tau, inp["X"][1], b, contract=True,
-                            intermediates=True)
-    st = compare(from_dev(Z2), mid["Z2"][:, sigma], "bf16", "Z2")
-    _log("  Z2 fail=%d/%d max_tol_ratio=%.3g rel_norm=%.3g" % (st["fail"], st["n"], st["max_ratio"], st["rel_norm"]))
-    assert st["fail"] == 0
+    W0, thR, thP, X, gY = inp["W0"][1], inp["thR"][1], inp["thP"][1], inp["X"][1], inp["gY"][1]
+    dXr, dRr, dPr, it = oracle.backward(W0, thR, thP, sigma, tau, X, gY, b, contract=True, intermediates=True)
+    fl = layer_floors(W0, it)
+    # z2' = rnd(z1' W0p^T): one-ulp flips of z1' reach it through a sum over
+    # n terms (Gaussian, relative rms deviation that of z1'), hence the
+    # token-sum floor; nearly every element meets the stated bound
+    st = compare(from_dev(Z2), it["Z2"][:, sigma], "sum", "Z2", max_strict=1e-3, terms=n)
+    assert st["rel_norm"] <= ETA_BF16
+    compare(from_dev(Y1), oracle.forward(W0, thR, thP, sigma, tau, X, b, contract=True), "bf16", "Y", floor=fl["Y"])
+    compare(from_dev(dX1), dXr, "bf16", "dX", floor=fl["dX"])
+    if it["GR"]:
+        compare(from_dev(GR1), np.array(it["GR"]), "sum", "dL/dQ_R", terms=N)
+        compare(from_dev(dR), dRr, "sum", "dthR", terms=N)
+    if it["GP"]:
+        compare(from_dev(GP1), np.array(it["GP"]), "sum", "dL/dQ_P", terms=N)
+        compare(from_dev(dP), dPr, "sum", "dthP", terms=N)
     # N = 0: nothing is written, dL/dQ is zero
     lay.forward_blocks_z2(d["X"][:0], Z2=Z2[:0])
     _, GR, GP = lay.backward_blocks_dq_z2(d["X"][:0], d["gY"][:0], Z2[:0], want_dx=False)

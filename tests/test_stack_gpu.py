@@ -11,7 +11,7 @@ import pytest
 import bench
 import oracle
 import workloads as WL
-from gpu_util import compare, from_dev, oracle_perms, torch_mod
+from gpu_util import compare, from_dev, layer_floors, oracle_perms, sum_floor, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -49,20 +49,35 @@ def test_stack_training_step():
         b = inp["b"]
         sigma, tau = oracle_perms(inp, 0)
         W0, th0R, th0P, X, gY = inp["W0"][1], inp["thR"][1], inp["thP"][1], inp["X"][1], inp["gY"][1]
-        compare(s["Y"], oracle.forward(W0, th0R, th0P, sigma, tau, X, b, contract=True), "bf16", "Y")
-        dXr, dRr, dPr = oracle.backward(W0, th0R, th0P, sigma, tau, X, gY, b, contract=True)
-        compare(s["dX"], dXr, "bf16", "dX")
-        compare(s["dR"], dRr, "bf16", "dthR")
-        compare(s["dP"], dPr, "bf16", "dthP")
-        # Adam from zero moments on the GPU's own gradients (the gradients are checked above)
+        dXr, dRr, dPr, it = oracle.backward(W0, th0R, th0P, sigma, tau, X, gY, b, contract=True,
+                                            intermediates=True)
+        fl = layer_floors(W0, it)
+        compare(s["Y"], oracle.forward(W0, th0R, th0P, sigma, tau, X, b, contract=True), "bf16", "Y", floor=fl["Y"])
+        compare(s["dX"], dXr, "bf16", "dX", floor=fl["dX"])
+        compare(s["dR"], dRr, "sum", "dthR", terms=X.shape[0])
+        compare(s["dP"], dPr, "sum", "dthP", terms=X.shape[0])
+        # Adam from zero moments on the oracle's gradients.  At the first step
+        # the update is lr g / (|g| + eps), i.e. lr sign(g): where the oracle's
+        # gradient lies within the gradient bound of zero its sign is not
+        # determined by the comparison above, and the two updates may differ
+        # by up to 2 lr; elsewhere they agree to fp32 precision
         hp = {k: float(np.float32(v)) for k, v in dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8).items()}
-        tR = oracle.adam_step(th0R, s["dR"], 0.0, 0.0, 1, **hp)[0]
-        tP = oracle.adam_step(th0P, s["dP"], 0.0, 0.0, 1, **hp)[0]
-        compare(s["tR"], tR, "f32", "theta_R after Adam")
-        compare(s["tP"], tP, "f32", "theta_P after Adam")
-        # merge with the post-Adam generators, relaid to the merge-1 permutations
+        tR = oracle.adam_step(th0R, dRr, 0.0, 0.0, 1, **hp)[0]
+        tP = oracle.adam_step(th0P, dPr, 0.0, 0.0, 1, **hp)[0]
+        for got, ref, g, name in ((s["tR"], tR, dRr, "theta_R after Adam"), (s["tP"], tP, dPr, "theta_P after Adam")):
+            gtol = 1e-3 + 2e-2 * np.abs(g) + sum_floor(g, X.shape[0])
+            sure = np.abs(g) > gtol
+            print("  %s: %d of %d gradient signs undetermined" % (name, int((~sure).sum()), g.size), flush=True)
+            assert (~sure).mean() <= 0.01
+            compare(got[sure], ref[sure], "f32", name)
+            assert np.all(np.abs(got[~sure] - ref[~sure]) <= 2 * hp["lr"] * (1 + 1e-6) + 1e-5 * np.abs(ref[~sure]))
+        # merge with the oracle's post-Adam generators, relaid to the merge-1
+        # permutations; the generators the GPU merged differ from these only in
+        # the undetermined entries (by <= 2 lr), whose first-order effect on the
+        # weight (|dQ| <= 2|M| |dS| |M|, times |W0| ~ 0.02) stays far inside the
+        # 1e-3 absolute part of the bound
         s1, t1 = oracle_perms(inp, 1)
         assert np.array_equal(from_dev(lay.sigma), s1) and np.array_equal(from_dev(lay.tau), t1)
-        Wn = oracle.merge(W0, s["tR"], s["tP"], sigma, tau, b, contract=True)
-        compare(from_dev(lay.W0p), oracle.pack(Wn, s1, t1), "bf16", "W0p merged")
+        Wn = oracle.merge(W0, tR, tP, sigma, tau, b, contract=True)
+        compare(from_dev(lay.W0p), oracle.pack(Wn, s1, t1), "bf16", "W0p merged", floor=fl["W"])
     assert torch.isfinite(m1).all().item() and torch.isfinite(v1).all().item()
