@@ -240,6 +240,31 @@ int poetx_forward_blocks(const poetx_layer* layer, const void* W0p, const poetx_
                          void* Y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * poetx_forward_blocks for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace and allocates nothing: its intermediates
+ * live in a static device array of POETX_NOALLOC_SCRATCH_BYTES (64 MiB) that
+ * every GPU the library runs on holds until the process ends (its device
+ * address is looked up once per device, on the first call with that device
+ * current; the stream must belong to the current device).  Tokens go
+ * through in chunks of the largest multiple of 128 whose forward
+ * intermediates fit the array (N * (n + m + max(m, n)) * 2 bytes for bf16,
+ * N * (n + m) * 4 for fp32); the results are bit-identical to
+ * poetx_forward_blocks.  Calls on one GPU share the array, which keeps the
+ * last call's contents: calls that overlap on one GPU (concurrent streams,
+ * threads) race and must be serialized by the caller.  Errors: those of
+ * poetx_forward_blocks; POETX_EINVAL for POETX_W0_INT8 layers (their
+ * dequantized weight does not fit beside the chunk); POETX_ESHAPE if 128
+ * tokens of the layer exceed the array; POETX_EHIP if the array's address
+ * cannot be obtained.
+ */
+#define POETX_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int poetx_forward_blocks_noalloc(const poetx_layer* layer, const void* W0p,
+                                 const poetx_blocks* blocks, const int32_t* sigma,
+                                 const int32_t* tau, const void* X, int64_t N, void* Y,
+                                 void* stream);
+
+/*
  * a0, a6-a9: backward of L = <dY, Y> with W0 frozen.  The Cayley blocks and
  * the intermediate activations are recomputed from X rather than stored
  * (POET-Xmem gradient checkpointing, [P3 item 5]); the gradient reaches the

@@ -23,7 +23,7 @@ _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDT
 
 EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
             "poetx_build_block_sets", "poetx_build_cnp_workspace_bytes", "poetx_build_block_sets_cnp",
-            "poetx_forward", "poetx_forward_blocks", "poetx_backward",
+            "poetx_forward", "poetx_forward_blocks", "poetx_forward_blocks_noalloc", "poetx_backward",
             "poetx_backward_blocks", "poetx_backward_blocks_dq", "poetx_forward_blocks_z2",
             "poetx_backward_blocks_dq_z2", "poetx_chain_rule_sets",
             "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_make_permutation",
@@ -107,6 +107,7 @@ def lib():
         "poetx_build_block_sets_cnp": (ctypes.c_int, [ctypes.POINTER(BlockSet), i32, i32, i32, vp, sz, vp]),
         "poetx_forward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "poetx_forward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, i64, vp, vp, sz, vp]),
+        "poetx_forward_blocks_noalloc": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, i64, vp, vp]),
         "poetx_backward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_backward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_backward_blocks_dq": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
@@ -235,6 +236,12 @@ def poetx_forward_blocks(layer, W0p, blocks, sigma, tau, X, N, Y, ws, stream=Non
     _check("poetx_forward_blocks", lib().poetx_forward_blocks(
         ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
         _ptr(X), int(N), _ptr(Y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def poetx_forward_blocks_noalloc(layer, W0p, blocks, sigma, tau, X, N, Y, stream=None):
+    _check("poetx_forward_blocks_noalloc", lib().poetx_forward_blocks_noalloc(
+        ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
+        _ptr(X), int(N), _ptr(Y), _stream(stream)))
 
 
 def poetx_backward_blocks(layer, W0p, blocks, sigma, tau, X, dY, N, dX, dthR, dthP, ws, stream=None):

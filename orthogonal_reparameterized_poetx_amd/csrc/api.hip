@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -803,6 +804,51 @@ int backward_dq_impl(const poetx_layer* layer, const void* W0p, const poetx_bloc
                   false, w, s, GR, GP, Z2);
 }
 
+// ---- allocation-free forward: intermediates in a file-scope device array
+// (one per GPU, held until the process ends) instead of a caller workspace.
+// Host code never passes the array's name to a kernel: its device address is
+// taken once per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device
+int scratch_on_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(POETX_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(POETX_EHIP, "device %d out of range [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(POETX_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return POETX_OK;
+}
+
+// tokens per chunk of the allocation-free forward: the largest multiple of
+// 128 whose forward workspace fits the scratch (128 rows keep every chunk's
+// row starts at the alignment of the first, so chunks take the same kernels
+// as one call over all tokens); 0 if not even 128 tokens fit
+int64_t noalloc_chunk(const poetx_layer* layer) {
+  const Shape S1 = shape_of(layer, 1);
+  const int64_t per_token = (S1.n + S1.m + (S1.f32 ? 0 : std::max(S1.n, S1.m))) * (int64_t)S1.es;
+  int64_t c = ((int64_t)kScratchBytes - 8 * (int64_t)kAlign) / per_token / 128 * 128;
+  for (; c >= 128; c -= 128) {
+    size_t need = 0;
+    plan_fwd(shape_of(layer, c), false, nullptr, &need);
+    if (need <= kScratchBytes) return c;
+  }
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -992,6 +1038,37 @@ int poetx_forward_blocks_z2(const poetx_layer* layer, const void* W0p, const poe
   if (layer && layer->dtype == POETX_F32) return fail(POETX_EDTYPE, "poetx_forward_blocks_z2 takes bf16 layers");
   if (N > 0 && !Z2) return fail(POETX_EINVAL, "Z2 is NULL");
   return forward_blocks_impl(layer, W0p, blocks, sigma, tau, X, N, Y, Z2, ws, ws_bytes, stream);
+}
+
+int poetx_forward_blocks_noalloc(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,
+                                 const int32_t* sigma, const int32_t* tau, const void* X, int64_t N, void* Y,
+                                 void* stream) {
+  int rc = check_fwd_args(layer, N, W0p, sigma, tau, X, Y);
+  if (rc) return rc;
+  if (layer->flags & POETX_W0_INT8)
+    return fail(POETX_EINVAL, "poetx_forward_blocks_noalloc: POETX_W0_INT8 layers need a dequantized weight "
+                              "(m*n*2 bytes) beside the scratch; use poetx_forward_blocks");
+  const Shape S0 = shape_of(layer, N);
+  if ((rc = check_blocks(S0, blocks, false))) return rc;
+  if (N == 0) return POETX_OK;
+  const int64_t chunk = noalloc_chunk(layer);
+  if (chunk <= 0)
+    return fail(POETX_ESHAPE, "poetx_forward_blocks_noalloc: 128 tokens of m=%lld n=%lld exceed the %zu-byte scratch",
+                (long long)S0.m, (long long)S0.n, kScratchBytes);
+  void* base = nullptr;
+  if ((rc = scratch_on_device(&base))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Blk q = blk_of(blocks);
+  for (int64_t t0 = 0; t0 < N; t0 += chunk) {
+    const Shape S = shape_of(layer, std::min(chunk, N - t0));
+    size_t need = 0;
+    const FwdWs w = plan_fwd(S, false, base, &need);
+    if (need > kScratchBytes) return fail(POETX_EWORKSPACE, "scratch plan of %zu bytes", need);
+    rc = fwd_core(S, W0p, q, sigma, tau, static_cast<const char*>(X) + t0 * S.n * (int64_t)S.es,
+                  static_cast<char*>(Y) + t0 * S.m * (int64_t)S.es, w, s);
+    if (rc) return rc;
+  }
+  return POETX_OK;
 }
 
 int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, const float* thP,

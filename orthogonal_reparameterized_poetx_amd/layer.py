@@ -125,6 +125,13 @@ class PoetxLayer:
                                Y, ws, stream)
         return Y
 
+    def forward_blocks_noalloc(self, X, Y, stream=None):
+        """forward_blocks without a workspace (poetx_forward_blocks_noalloc):
+        Y must be given, nothing is allocated."""
+        L.poetx_forward_blocks_noalloc(self.layer, self.W0p, self.block_buffers("forward")[1], self.sigma, self.tau,
+                                       X, X.shape[0], Y, stream)
+        return Y
+
     def forward_blocks_z2(self, X, Y=None, Z2=None, stream=None):
         """forward_blocks that also returns z2' (working layout) for backward_blocks_dq_z2."""
         N = X.shape[0]
