@@ -162,8 +162,9 @@ typedef struct {
 
 /*
  * Bytes of workspace poetx_build_blocks needs for nblocks blocks of size b;
- * for poetx_build_block_sets, pass the largest nblocks of its sets.  Zero
- * for b <= 256.
+ * for poetx_build_block_sets, pass the total nblocks of its sets (at b = 512
+ * the blocks of all sets go through one pass of the 2x2 Schur-complement
+ * solve together).  Zero for b <= 256.
  */
 size_t poetx_build_workspace_bytes(int64_t nblocks, int32_t b);
 
@@ -190,7 +191,7 @@ int poetx_build_blocks(const float* theta, int64_t nblocks, int32_t b, float* Q3
  * launches and data movement [P3 item 4; P1 实践 2].
  *   sets   host array of count poetx_block_set (count in [0, 4096]); every
  *          set has the same block size b
- *   ws     poetx_build_workspace_bytes(max nblocks over the sets, b) bytes
+ *   ws     poetx_build_workspace_bytes(total nblocks over the sets, b) bytes
  * Output buffers must not overlap each other or any theta.
  */
 int poetx_build_block_sets(const poetx_block_set* sets, int32_t count, int32_t b, void* ws,

@@ -132,16 +132,28 @@ struct QOut {
   uint16_t* qtbf;
 };
 
-int build_schur512(const float* theta, int64_t nblk, QOut o, void* ws, int mode, hipStream_t s) {
+int build_schur512(const float* const* theta, const int64_t* nblks, const QOut* outs, int nsets, void* ws, int mode,
+                   hipStream_t s) {
   // 2x2 block inverse with 256-wide Schur complement:
   //   [A B; C D]^-1 = [Ai + Ai B Si C Ai, -Ai B Si; -Si C Ai, Si], Si = (D - C Ai B)^-1
+  // over the blocks of every set at once (one pass of launches for all)
+  int64_t nblk = 0;
+  for (int i = 0; i < nsets; ++i) nblk += nblks[i];
+  if (nblk <= 0) return POETX_OK;
   Arena a(ws);
   float* Af = a.take<float>((size_t)nblk * 512 * 512);
   float* Mf = a.take<float>((size_t)nblk * 512 * 512);
   float* Tm = a.take<float>((size_t)nblk * 256 * 256);
   float* Vm = a.take<float>((size_t)nblk * 256 * 256);
   const int64_t SB = 512 * 512, SH = 256 * 256;
-  launch_unpack_eye_minus_s(theta, 512, (int)nblk, Af, s);
+  {
+    int64_t off = 0;
+    for (int i = 0; i < nsets; ++i) {
+      if (nblks[i] <= 0) continue;
+      launch_unpack_eye_minus_s(theta[i], 512, (int)nblks[i], Af + off * SB, s);
+      off += nblks[i];
+    }
+  }
   auto gj = [&](float* in, float* out) {
     GJArgs g{};
     g.nseg = 1;
@@ -176,7 +188,14 @@ int build_schur512(const float* theta, int64_t nblk, QOut o, void* ws, int mode,
   gemm(Tm, 256, M22, 512, M12, 512, -1.f, 0.f, SH, SB, SB);       // M12 = -T Si
   gemm(M22, 512, Vm, 256, M21, 512, -1.f, 0.f, SB, SH, SB);       // M21 = -Si V
   gemm(M12, 512, Vm, 256, M11, 512, -1.f, 1.f, SB, SH, SB);       // M11 = Ai - M12 V
-  launch_finalize_q(Mf, 512, (int)nblk, o.q32, o.qbf, o.qtbf, s);
+  {
+    int64_t off = 0;
+    for (int i = 0; i < nsets; ++i) {
+      if (nblks[i] <= 0) continue;
+      launch_finalize_q(Mf + off * SB, 512, (int)nblks[i], outs[i].q32, outs[i].qbf, outs[i].qtbf, s);
+      off += nblks[i];
+    }
+  }
   return check_launch("cayley builder (b=512)");
 }
 
@@ -184,8 +203,8 @@ int build_schur512(const float* theta, int64_t nblk, QOut o, void* ws, int mode,
 // launches as possible: up to GJ_MAXSEG batches share one Gauss-Jordan launch,
 // so the grid covers the blocks of all of them.  mode 6: split-bf16 x6 MFMA
 // products (fp32-level accuracy); mode 0: fp32 MFMA.  Both give Q accurate
-// to fp32 rounding.  b = 512 goes batch by batch through the Schur path (ws
-// sized for the largest batch).
+// to fp32 rounding.  b = 512 takes the blocks of all batches through one pass
+// of the Schur path (ws sized for all of them together).
 // skip (b <= 256): blocks in the order of the sets (empty sets left out)
 // whose flag is set are not built here
 int build_sets(const float* const* theta, const int64_t* nblk, const QOut* out, int nsets, int b, void* ws, int mode,
@@ -214,12 +233,7 @@ int build_sets(const float* const* theta, const int64_t* nblk, const QOut* out, 
     }
     return check_launch("cayley builder");
   }
-  for (int i = 0; i < nsets; ++i) {
-    if (nblk[i] <= 0) continue;
-    const int rc = build_schur512(theta[i], nblk[i], out[i], ws, mode, s);
-    if (rc) return rc;
-  }
-  return POETX_OK;
+  return build_schur512(theta, nblk, out, nsets, ws, mode, s);
 }
 
 // a layer's R and P blocks
@@ -356,7 +370,7 @@ FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes) {
       w.qbR = a.take<uint16_t>((size_t)S.kR * S.b * S.b);
       w.qbP = a.take<uint16_t>((size_t)S.kP * S.b * S.b);
     }
-    w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
+    w.bws = a.take<char>(build_ws_bytes(S.kR + S.kP, S.b));
   }
   w.z1 = a.take<char>((size_t)S.N * S.n * S.es);
   w.z2 = a.take<char>((size_t)S.N * S.m * S.es);
@@ -387,7 +401,7 @@ BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes, bool dq = fa
       w.qtR = a.take<uint16_t>(S.kR * bb);
       w.qtP = a.take<uint16_t>(S.kP * bb);
     }
-    w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
+    w.bws = a.take<char>(build_ws_bytes(S.kR + S.kP, S.b));
   }
   w.z1 = a.take<char>((size_t)S.N * S.n * S.es);
   w.xg = a.take<char>((size_t)S.N * S.n * S.es);
@@ -406,13 +420,19 @@ BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes, bool dq = fa
   return w;
 }
 
+// rows per segment of the in-place relayout: the rows saved aside number
+// at most 2 ceil(m / L)
+constexpr int kRelayoutL = 16;
+int64_t relayout_max_saved(int64_t m) { return 2 * ((m + kRelayoutL - 1) / kRelayoutL) + 1; }
+
 struct MrgWs {
   float *q32R, *q32P;
   uint16_t *qbR, *qtP;
   void* bws;
-  void* V;
-  uint64_t* keys;
   int32_t *snew, *tnew, *sinv, *tinv;
+  int32_t *dist, *hlist, *slot, *slist, *counts, *nxt;
+  void* saved;
+  int64_t max_saved;
   void* w0;
 };
 MrgWs plan_merge(const Shape& S, bool own, void* base, size_t* bytes) {
@@ -427,15 +447,21 @@ MrgWs plan_merge(const Shape& S, bool own, void* base, size_t* bytes) {
       w.qbR = a.take<uint16_t>(S.kR * bb);
       w.qtP = a.take<uint16_t>(S.kP * bb);
     }
-    w.bws = a.take<char>(build_ws_bytes(std::max(S.kR, S.kP), S.b));
+    w.bws = a.take<char>(build_ws_bytes(S.kR + S.kP, S.b));
   }
-  w.V = a.take<char>((size_t)S.m * S.n * S.es * (S.f32 ? 2 : 1));
-  w.keys = a.take<uint64_t>(std::max(S.m, S.n));
   w.snew = a.take<int32_t>(S.m);
   w.tnew = a.take<int32_t>(S.n);
   w.sinv = a.take<int32_t>(S.m);
   w.tinv = a.take<int32_t>(S.n);
-  if (S.q8) w.w0 = a.take<char>((size_t)S.m * S.n * 2);   // dequantized weight, merged in place
+  w.dist = a.take<int32_t>(S.m);
+  w.hlist = a.take<int32_t>(S.m);
+  w.slot = a.take<int32_t>(S.m);
+  w.nxt = a.take<int32_t>(S.m);
+  w.max_saved = relayout_max_saved(S.m);
+  w.slist = a.take<int32_t>(w.max_saved);
+  w.counts = a.take<int32_t>(2);
+  w.saved = a.take<char>((size_t)w.max_saved * S.n * S.es);   // rows saved aside by the relayout
+  if (S.q8) w.w0 = a.take<char>((size_t)S.m * S.n * 2);       // dequantized weight, merged in place
   *bytes = a.off + kAlign;
   return w;
 }
@@ -666,75 +692,60 @@ int check_blocks(const Shape& S, const poetx_blocks* q, bool backward) {
 }
 
 // merge after the blocks exist: tile products, new permutations, relayout,
-// generator reset (a10, a11)
-// bf16 merge on the streaming kernels, where they apply (b <= 256, rows of a
-// multiple of 8 columns up to 32768, 16-byte aligned operands):
-//   W0p <- W0p D_P        block product in place (columns from kP b on: identity)
-//   V[I] <- Q_R,I W0p[I]  batched NN GEMM over the kR row blocks; tail rows copied
-//   W0p[i][j] <- V[sinv(snew(i))][tinv(tnew(j))]   staged row gather
-// One bf16 rounding after each product, as in the tile kernel.
-bool merge_fast_bf16(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
-                     uint64_t perm_seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
+// generator reset (a10, a11), all on W0p in place.
+// bf16 products on the streaming kernels, where they apply (b <= 256, rows of
+// a multiple of 8 columns up to 32768, 16-byte aligned operands):
+//   W0p <- W0p D_P        block product, row by row
+//   W0p[I] <- Q_R,I W0p[I] batched NN GEMM over the kR row blocks with C = B:
+//                         at b <= 256 one 256-row output tile covers a row
+//                         block, so each workgroup reads exactly the slab
+//                         columns it writes, and no other workgroup touches
+//                         them; tail rows stay
+// otherwise: the staged tile kernels of launch_merge_products_inplace.
+// One bf16 rounding after each product.  Then the new permutations, and
+// W0p[i][j] <- W0p[sinv(snew(i))][tinv(tnew(j))] along the cycles of the
+// row map, with at most relayout_max_saved(m) rows saved aside.
+bool merge_fast_products_bf16(const Shape& S, void* W0p, const Blk& q, hipStream_t s) {
   const int64_t m = S.m, n = S.n;
   const int b = S.b;
-  if (S.f32 || (n & 7) || n > 32768 || !q.qbR || !q.qtP) return false;
+  if (S.f32 || b > 256 || (n & 7) || n > 32768 || !q.qbR || !q.qtP) return false;
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  if (!al(W0p) || !al(w.V) || !al(q.qbR) || !al(q.qtP) || !al(w.tnew)) return false;
+  if (!al(W0p) || !al(q.qbR) || !al(q.qtP)) return false;
   uint16_t* W = static_cast<uint16_t*>(W0p);
-  uint16_t* V = static_cast<uint16_t*>(w.V);
-  {
-    Tm tm(s, "merge_tiles", 4.0 * m * n * b, 2.0 * m * n * S.es);
-    if (S.kP > 0 && !launch_blockdiag_bf16(W, q.qtP, W, m, n, n, b, S.kP, s)) return false;
-    if (S.kR > 0) {
-      GemmArgs g{};
-      g.A = q.qbR; g.B = W; g.C = V;
-      g.M = b; g.N = (int)n; g.K = b;
-      g.lda = b; g.ldb = n; g.ldc = n;
-      g.sA = (int64_t)b * b; g.sB = (int64_t)b * n; g.sC = (int64_t)b * n;
-      g.batch = S.kR;
-      launch_gemm_bf16(true, g, s);
-    }
-    launch_copy_rows_bf16(W + (int64_t)S.kR * b * n, V + (int64_t)S.kR * b * n, m - (int64_t)S.kR * b, n, s);
+  if (S.kP > 0 && !launch_blockdiag_bf16(W, q.qtP, W, m, n, n, b, S.kP, s)) return false;
+  if (S.kR > 0) {
+    GemmArgs g{};
+    g.A = q.qbR; g.B = W; g.C = W;
+    g.M = b; g.N = (int)n; g.K = b;
+    g.lda = b; g.ldb = n; g.ldc = n;
+    g.sA = (int64_t)b * b; g.sB = (int64_t)b * n; g.sC = (int64_t)b * n;
+    g.batch = S.kR;
+    launch_gemm_bf16(true, g, s);
   }
-  {
-    // new permutations, old inverses; then the composed maps in place of the new ones
-    Tm tm(s, "merge_permutations", 0.0, 0.0);
-    launch_merge_permutations(perm_seed, merge_index, sigma, tau, m, n, w.snew, w.tnew, w.sinv, w.tinv, s);
-  }
-  {
-    Tm tm(s, "merge_relayout", 0.0, 2.0 * m * n * S.es);
-    launch_relayout_rows_bf16(V, W, w.snew, w.tnew, m, n, s);
-  }
-  launch_fill_f32(thR, 0.f, (int64_t)S.kR * (S.b * (S.b - 1) / 2), s);
-  launch_fill_f32(thP, 0.f, (int64_t)S.kP * (S.b * (S.b - 1) / 2), s);
   return true;
 }
 
 int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
                uint64_t perm_seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
-  int rc;
-  if (S.b <= 256 && merge_fast_bf16(S, W0p, q, thR, thP, sigma, tau, perm_seed, merge_index, w, s))
-    return check_launch("merge");
   {
     Tm tm(s, "merge_tiles", 4.0 * S.m * S.n * S.b, 2.0 * S.m * S.n * S.es);
-    if (S.f32) launch_merge_tiles(true, W0p, w.V, q.q32R, q.q32P, S.m, S.n, S.b, S.kR, S.kP, s);
-    else launch_merge_tiles(false, W0p, w.V, q.qbR, q.qtP, S.m, S.n, S.b, S.kR, S.kP, s);
+    if (!merge_fast_products_bf16(S, W0p, q, s)) {
+      if (S.f32) launch_merge_products_inplace(true, W0p, q.q32R, q.q32P, S.m, S.n, S.b, S.kR, S.kP, s);
+      else launch_merge_products_inplace(false, W0p, q.qbR, q.qtP, S.m, S.n, S.b, S.kR, S.kP, s);
+    }
   }
-  if ((rc = check_launch("merge tiles"))) return rc;
-  // new permutations, old inverses, relayout into the caller's buffer
+  int rc;
+  if ((rc = check_launch("merge products"))) return rc;
   {
+    // new permutations, old inverses; then the composed maps in place of the new ones
     Tm tm(s, "merge_permutations", 0.0, 0.0);
-    launch_perm_keys_rank(perm_seed, merge_index, 0, S.m, w.keys, w.snew, s);
-    launch_perm_keys_rank(perm_seed, merge_index, 1, S.n, w.keys, w.tnew, s);
-    launch_invert_perm(sigma, S.m, w.sinv, s);
-    launch_invert_perm(tau, S.n, w.tinv, s);
+    launch_merge_permutations(perm_seed, merge_index, sigma, tau, S.m, S.n, w.snew, w.tnew, w.sinv, w.tinv, s);
   }
   {
     Tm tm(s, "merge_relayout", 0.0, 2.0 * S.m * S.n * S.es);
-    launch_relayout(S.f32, w.V, W0p, w.sinv, w.snew, w.tinv, w.tnew, S.m, S.n, s);
+    launch_relayout_inplace(S.f32, W0p, w.saved, w.snew, w.tnew, S.m, S.n, kRelayoutL, w.dist, w.hlist, w.slot,
+                            w.slist, w.counts, w.nxt, w.max_saved, s);
   }
-  launch_copy_i32(w.snew, sigma, S.m, s);
-  launch_copy_i32(w.tnew, tau, S.n, s);
   launch_fill_f32(thR, 0.f, (int64_t)S.kR * (S.b * (S.b - 1) / 2), s);
   launch_fill_f32(thP, 0.f, (int64_t)S.kP * (S.b * (S.b - 1) / 2), s);
   return check_launch("merge relayout");
@@ -893,7 +904,7 @@ int poetx_build_block_sets(const poetx_block_set* sets, int32_t count, int32_t b
   if (!valid_b(b)) return fail(POETX_EINVAL, "block size b=%d not in {32,64,128,256,512}", b);
   if (count < 0 || count > 4096) return fail(POETX_ESHAPE, "count=%d out of range [0, 4096]", count);
   if (count > 0 && !sets) return fail(POETX_EINVAL, "sets is NULL");
-  int64_t total = 0, largest = 0;
+  int64_t total = 0;
   for (int i = 0; i < count; ++i) {
     const poetx_block_set& t = sets[i];
     if (t.nblocks < 0 || t.nblocks > (int64_t(1) << 20))
@@ -902,11 +913,10 @@ int poetx_build_block_sets(const poetx_block_set* sets, int32_t count, int32_t b
     if (!t.theta) return fail(POETX_EINVAL, "set %d: theta is NULL", i);
     if (!t.Q32 && !t.Qbf16 && !t.QTbf16) return fail(POETX_EINVAL, "set %d: no output requested", i);
     total += t.nblocks;
-    largest = std::max(largest, t.nblocks);
   }
   if (total > (int64_t(1) << 24)) return fail(POETX_ESHAPE, "%lld blocks in one call", (long long)total);
   if (total == 0) return POETX_OK;
-  const int rc = check_ws(ws, ws_bytes, build_ws_bytes(largest, b));
+  const int rc = check_ws(ws, ws_bytes, build_ws_bytes(total, b));
   if (rc) return rc;
   std::vector<const float*> th((size_t)count);
   std::vector<int64_t> nb((size_t)count);

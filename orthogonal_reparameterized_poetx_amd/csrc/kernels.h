@@ -162,6 +162,17 @@ void launch_copy_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int
 bool launch_relayout_rows_bf16(const uint16_t* V, uint16_t* W, const int32_t* rmap, const int32_t* cmap, int64_t m,
                                int64_t n, hipStream_t s);
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+// In-place merge products: W <- W D_P (full column groups), then W <- D_R W
+// (full row groups); bf16 through MFMA, fp32 with FMA sums.
+void launch_merge_products_inplace(bool f32, void* W, const void* qr, const void* qpt, int64_t m, int64_t n, int b,
+                                   int kR, int kP, hipStream_t s);
+// In-place relayout W[i][j] <- W[rho(i)][kappa(j)] along the cycles of rho
+// (m <= 32768), cut into segments of at most L <= 64 rows; saved receives up
+// to max_saved rows (max_saved >= 2 ceil(m / L) suffices); dist, hlist,
+// slot, nxt ([m] each), slist ([max_saved]) and counts ([2]) are scratch.
+void launch_relayout_inplace(bool f32, void* W, void* saved, const int32_t* rho, const int32_t* kappa, int64_t m,
+                             int64_t n, int L, int32_t* dist, int32_t* hlist, int32_t* slot, int32_t* slist,
+                             int32_t* counts, int32_t* nxt, int64_t max_saved, hipStream_t s);
 // INT8 weight codes with per-row fp32 scales (quant.hip)
 void launch_dequant_rows(const int8_t* q, const float* sc, uint16_t* w, int64_t m, int64_t n, hipStream_t s);
 void launch_quantize_rows(const uint16_t* w, int8_t* q, float* sc, int64_t m, int64_t n, hipStream_t s);

@@ -394,6 +394,488 @@ bool launch_relayout_rows_bf16(const uint16_t* V, uint16_t* W, const int32_t* rm
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// In-place merge: the products act on W0p where it lies, and the relayout
+// W'[i][j] = W[rho(i)][kappa(j)] moves rows along the cycles of rho.
+// ---------------------------------------------------------------------------
+
+// P side, bf16, any b: W[r][J b + c] <- bf16(sum_k W[r][J b + k] Q_P,J[k][c])
+// for full column groups J < kP.  Workgroup = (32 rows, group J): the rows'
+// segment of group J is staged in LDS before anything is written, and no
+// other workgroup reads or writes it, so the update is in place.  Same
+// operands and MFMA order as merge_tiles_bf16_kernel's first step.
+constexpr int PROW_R = 32;
+__global__ __launch_bounds__(256) void merge_prow_bf16_kernel(uint16_t* W, const uint16_t* __restrict__ qpt, int m,
+                                                              int n, int b, int kP) {
+  __shared__ __align__(16) uint16_t seg[PROW_R * (MRG_MAXB + 8)];
+  const int pitch = b + 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int J = blockIdx.y;
+  const int r0 = blockIdx.x * PROW_R;
+  const int rows = min(PROW_R, m - r0);
+  if (J >= kP || rows <= 0) return;
+  for (int e = tid; e < rows * b; e += 256) {
+    const int r = e / b, k = e - r * b;
+    seg[r * pitch + k] = W[(int64_t)(r0 + r) * n + (int64_t)J * b + k];
+  }
+  __syncthreads();
+  const uint16_t* qpj = qpt + (int64_t)J * b * b;
+  const int lc = lane & 31, hi = lane >> 5;
+  const int ctiles = b / 32;
+  for (int ct = wave; ct < ctiles; ct += 4) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const int cc = ct * 32 + lc;            // A-operand row: output column within the group
+    const bool rok = lc < rows;             // B-operand column: weight row
+    for (int ks = 0; ks < b / 16; ++ks) {
+      const int kk = ks * 16 + 8 * hi;
+      const uint4 av = ldg16(qpj + (int64_t)cc * b + kk);
+      const uint4 bv = rok ? *reinterpret_cast<const uint4*>(&seg[lc * pitch + kk]) : make_uint4(0, 0, 0, 0);
+      acc = mfma32(as_bf16x8(av), as_bf16x8(bv), acc);
+    }
+    if (rok) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int col = ct * 32 + c32_row(lane, r);
+        W[(int64_t)(r0 + lc) * n + (int64_t)J * b + col] = f32_to_bits(acc[r]);
+      }
+    }
+  }
+}
+
+// R side, bf16, any b: W[I b + i][c] <- bf16(sum_k Q_R,I[i][k] W[I b + k][c])
+// for full row groups I < kR.  Workgroup = (group I, slab of 64 columns):
+// the slab of the group's rows is staged in LDS first; same operands and MFMA
+// order as merge_tiles_bf16_kernel's second step.
+constexpr int RCOL_SW = 64;
+__global__ __launch_bounds__(256) void merge_rcol_bf16_kernel(uint16_t* W, const uint16_t* __restrict__ qr, int m, int n,
+                                                              int b, int kR) {
+  __shared__ __align__(16) uint16_t Ut[RCOL_SW * MRG_UP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int I = blockIdx.y;
+  const int c0 = blockIdx.x * RCOL_SW;
+  const int cols = min(RCOL_SW, n - c0);
+  if (I >= kR || cols <= 0) return;
+  const int r0 = I * b;
+  for (int e = tid; e < cols * b; e += 256) {
+    const int r = e / cols, cc = e - r * cols;
+    Ut[cc * MRG_UP + r] = W[(int64_t)(r0 + r) * n + c0 + cc];
+  }
+  __syncthreads();
+  const uint16_t* qri = qr + (int64_t)I * b * b;
+  const int lc = lane & 31, hi = lane >> 5;
+  const int itiles = b / 32, ctiles = (cols + 31) / 32;
+  for (int p = wave; p < itiles * ctiles; p += 4) {
+    const int it = p % itiles, ct = p / itiles;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const int ii = it * 32 + lc;
+    const int cc = ct * 32 + lc;
+    const bool cok = cc < cols;
+    for (int ks = 0; ks < b / 16; ++ks) {
+      const int kk = ks * 16 + 8 * hi;
+      const uint4 av = ldg16(qri + (int64_t)ii * b + kk);
+      const uint4 bv = cok ? *reinterpret_cast<const uint4*>(&Ut[cc * MRG_UP + kk]) : make_uint4(0, 0, 0, 0);
+      acc = mfma32(as_bf16x8(av), as_bf16x8(bv), acc);
+    }
+    if (cok) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = it * 32 + c32_row(lane, r);
+        W[(int64_t)(r0 + i) * n + c0 + cc] = f32_to_bits(acc[r]);
+      }
+    }
+  }
+}
+
+// fp32, in place: P side one row per workgroup (the row staged in LDS), R
+// side one (row group, 32-column slab) per workgroup (the slab staged); the
+// sums run in the order of merge_right_f32_kernel / merge_left_f32_kernel.
+__global__ __launch_bounds__(256) void merge_prow_f32_kernel(float* W, const float* __restrict__ qp, int n, int b,
+                                                             int kP) {
+  __shared__ float row[32768];
+  const int r = blockIdx.x;
+  float* w = W + (int64_t)r * n;
+  for (int c = threadIdx.x; c < kP * b; c += 256) row[c] = w[c];
+  __syncthreads();
+  for (int c = threadIdx.x; c < kP * b; c += 256) {
+    const int J = c / b, cc = c - J * b;
+    const float* q = qp + (int64_t)J * b * b;
+    float s = 0.f;
+    for (int kk = 0; kk < b; ++kk) s = fmaf(row[J * b + kk], q[(int64_t)kk * b + cc], s);
+    w[c] = s;
+  }
+}
+constexpr int RCOL_F32_SW = 32;
+__global__ __launch_bounds__(256) void merge_rcol_f32_kernel(float* W, const float* __restrict__ qr, int n, int b,
+                                                             int kR) {
+  __shared__ float slab[MRG_MAXB * RCOL_F32_SW];
+  const int I = blockIdx.y;
+  const int c0 = blockIdx.x * RCOL_F32_SW;
+  const int cols = min(RCOL_F32_SW, n - c0);
+  if (I >= kR || cols <= 0) return;
+  const int64_t r0 = (int64_t)I * b;
+  for (int e = threadIdx.x; e < b * cols; e += 256) {
+    const int k = e / cols, cc = e - k * cols;
+    slab[k * RCOL_F32_SW + cc] = W[(r0 + k) * n + c0 + cc];
+  }
+  __syncthreads();
+  const float* q = qr + (int64_t)I * b * b;
+  for (int e = threadIdx.x; e < b * cols; e += 256) {
+    const int ii = e / cols, cc = e - ii * cols;
+    float s = 0.f;
+    for (int kk = 0; kk < b; ++kk) s = fmaf(q[(int64_t)ii * b + kk], slab[kk * RCOL_F32_SW + cc], s);
+    W[(r0 + ii) * n + c0 + cc] = s;
+  }
+}
+
+void launch_merge_products_inplace(bool f32, void* W, const void* qr, const void* qpt, int64_t m, int64_t n, int b,
+                                   int kR, int kP, hipStream_t s) {
+  if (m <= 0 || n <= 0) return;
+  if (f32) {
+    if (kP > 0)
+      hipLaunchKernelGGL(merge_prow_f32_kernel, dim3((unsigned)m), dim3(256), 0, s, static_cast<float*>(W),
+                         static_cast<const float*>(qpt), (int)n, b, kP);
+    if (kR > 0)
+      hipLaunchKernelGGL(merge_rcol_f32_kernel, dim3((unsigned)((n + RCOL_F32_SW - 1) / RCOL_F32_SW), (unsigned)kR),
+                         dim3(256), 0, s, static_cast<float*>(W), static_cast<const float*>(qr), (int)n, b, kR);
+    return;
+  }
+  if (kP > 0)
+    hipLaunchKernelGGL(merge_prow_bf16_kernel, dim3((unsigned)((m + PROW_R - 1) / PROW_R), (unsigned)kP), dim3(256), 0,
+                       s, static_cast<uint16_t*>(W), static_cast<const uint16_t*>(qpt), (int)m, (int)n, b, kP);
+  if (kR > 0)
+    hipLaunchKernelGGL(merge_rcol_bf16_kernel, dim3((unsigned)((n + RCOL_SW - 1) / RCOL_SW), (unsigned)kR), dim3(256),
+                       0, s, static_cast<uint16_t*>(W), static_cast<const uint16_t*>(qr), (int)m, (int)n, b, kR);
+}
+
+// ---- relayout along the cycles of rho ----------------------------------
+// Plan (one workgroup, the map in LDS as 16-bit indices, m <= 32768):
+// pointer jumping gives every i its cycle's minimum c (15 doubling rounds),
+// then its distance d(i) along rho to c (list ranking with a self-loop at c).
+// Heads are the i with d(i) % L == 0, so every cycle is cut into segments of
+// at most L positions, each starting at a head and ending just before the
+// next one.  A head whose cycle has another head is "saved": its row is
+// copied aside before any row moves, because the segment ending at it reads
+// it after its own segment has overwritten it.  A cycle with a single head
+// (length <= L) keeps that row in its walker's LDS instead.  Saved heads
+// number at most sum over long cycles of ceil(len / L) < 2 m / L.
+constexpr int CP_THREADS = 1024, CP_MAXM = 32768, CP_PER = CP_MAXM / CP_THREADS;
+__global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* __restrict__ rho, int m, int L,
+                                                                int32_t* __restrict__ dist, int32_t* __restrict__ hlist,
+                                                                int32_t* __restrict__ slot,
+                                                                int32_t* __restrict__ slist,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ nxt) {
+  __shared__ uint16_t A[CP_MAXM], B[CP_MAXM];
+  __shared__ int scanH[CP_THREADS], scanS[CP_THREADS];
+  const int tid = threadIdx.x;
+  int rounds = 0;
+  while ((1 << rounds) < m) ++rounds;
+  for (int i = tid; i < m; i += CP_THREADS) {
+    A[i] = (uint16_t)i;
+    B[i] = (uint16_t)rho[i];
+  }
+  __syncthreads();
+  // A(i) = min over i, rho(i), ..., rho^(2^r - 1)(i); B(i) = rho^(2^r)(i)
+  for (int r = 0; r < rounds; ++r) {
+    uint16_t na[CP_PER], nb[CP_PER];
+#pragma unroll
+    for (int k = 0; k < CP_PER; ++k) {
+      const int i = tid + k * CP_THREADS;
+      if (i < m) {
+        const int j = B[i];
+        na[k] = min(A[i], A[j]);
+        nb[k] = B[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CP_PER; ++k) {
+      const int i = tid + k * CP_THREADS;
+      if (i < m) {
+        A[i] = na[k];
+        B[i] = nb[k];
+      }
+    }
+    __syncthreads();
+  }
+  // list ranking: A(i) <- 0 at the cycle minimum, 1 elsewhere; B(i) <- rho(i),
+  // or i itself at the minimum; then A(i) += A(B(i)), B(i) <- B(B(i))
+  for (int i = tid; i < m; i += CP_THREADS) {
+    const bool c = A[i] == i;
+    A[i] = c ? 0 : 1;
+    B[i] = c ? (uint16_t)i : (uint16_t)rho[i];
+  }
+  __syncthreads();
+  for (int r = 0; r < rounds; ++r) {
+    uint16_t na[CP_PER], nb[CP_PER];
+#pragma unroll
+    for (int k = 0; k < CP_PER; ++k) {
+      const int i = tid + k * CP_THREADS;
+      if (i < m) {
+        const int j = B[i];
+        na[k] = (uint16_t)(A[i] + A[j]);
+        nb[k] = B[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CP_PER; ++k) {
+      const int i = tid + k * CP_THREADS;
+      if (i < m) {
+        A[i] = na[k];
+        B[i] = nb[k];
+      }
+    }
+    __syncthreads();
+  }
+  // heads and saved heads, listed in index order: thread t owns
+  // [t * CP_PER, (t + 1) * CP_PER)
+  int ch = 0, cs = 0;
+  for (int k = 0; k < CP_PER; ++k) {
+    const int i = tid * CP_PER + k;
+    if (i >= m) break;
+    const int d = A[i];
+    dist[i] = d;
+    if (d % L == 0) {
+      ++ch;
+      if (d > 0 || A[rho[i]] >= L) ++cs;
+    }
+  }
+  scanH[tid] = ch;
+  scanS[tid] = cs;
+  __syncthreads();
+  for (int off = 1; off < CP_THREADS; off <<= 1) {
+    const int h = tid >= off ? scanH[tid - off] : 0;
+    const int v = tid >= off ? scanS[tid - off] : 0;
+    __syncthreads();
+    scanH[tid] += h;
+    scanS[tid] += v;
+    __syncthreads();
+  }
+  int oh = scanH[tid] - ch, os = scanS[tid] - cs;   // exclusive prefix
+  for (int k = 0; k < CP_PER; ++k) {
+    const int i = tid * CP_PER + k;
+    if (i >= m) break;
+    const int d = A[i];
+    int sl = -1;
+    if (d % L == 0) {
+      hlist[oh++] = i;
+      if (d > 0 || A[rho[i]] >= L) {
+        sl = os++;
+        slist[sl] = i;
+      }
+    }
+    slot[i] = sl;
+  }
+  if (tid == CP_THREADS - 1) {
+    counts[0] = scanH[tid];
+    counts[1] = scanS[tid];
+  }
+  // nxt(i) = rho(i), with the sign bit set when rho(i) is a head
+  for (int i = tid; i < m; i += CP_THREADS) {
+    const int q = rho[i];
+    nxt[i] = (A[q] % L == 0) ? (int32_t)((uint32_t)q | 0x80000000u) : q;
+  }
+}
+
+// saved[s][:] = W[slist[s]][:] for s < counts[1]; one row per workgroup
+template <typename T>
+__global__ __launch_bounds__(256) void save_heads_kernel(const T* __restrict__ W, T* __restrict__ saved,
+                                                         const int32_t* __restrict__ slist,
+                                                         const int32_t* __restrict__ counts, int n) {
+  const int sidx = blockIdx.x;
+  if (sidx >= counts[1]) return;
+  const T* src = W + (int64_t)slist[sidx] * n;
+  T* dst = saved + (int64_t)sidx * n;
+  for (int c = threadIdx.x; c < n; c += 256) dst[c] = src[c];
+}
+
+// One segment per workgroup: from head h, positions p = h, rho(h), ... while
+// rho(p) is not a head: W[p][j] <- W[rho(p)][kappa(j)] (row rho(p) is still
+// untouched: only this walker writes it, at its next position); at the last
+// position the source is the next head's saved row, or, for a cycle with a
+// single head, the head's own row kept in LDS before the first write.
+// Barriers separate the positions, so a row is read completely before the
+// next position overwrites it.
+template <typename T>
+__global__ __launch_bounds__(256) void walk_rows_kernel(T* W, const T* __restrict__ saved,
+                                                        const int32_t* __restrict__ rho,
+                                                        const int32_t* __restrict__ kappa,
+                                                        const int32_t* __restrict__ dist,
+                                                        const int32_t* __restrict__ hlist,
+                                                        const int32_t* __restrict__ slot,
+                                                        const int32_t* __restrict__ counts, int n, int L) {
+  __shared__ T keep[32768];
+  const int g = blockIdx.x;
+  if (g >= counts[0]) return;
+  const int h = hlist[g];
+  const bool single = slot[h] < 0;
+  if (single) {
+    for (int c = threadIdx.x; c < n; c += 256) keep[c] = W[(int64_t)h * n + c];
+    __syncthreads();
+  }
+  int p = h;
+  // a segment has at most L positions (the bound also ends the walk if rho
+  // were not a permutation)
+  for (int step = 0; step < L; ++step) {
+    const int q = rho[p];
+    const bool last = dist[q] % L == 0;
+    T* dst = W + (int64_t)p * n;
+    if (last && single) {
+      for (int j = threadIdx.x; j < n; j += 256) dst[j] = keep[kappa[j]];
+    } else {
+      const T* src = last ? saved + (int64_t)slot[q] * n : W + (int64_t)q * n;
+      for (int j = threadIdx.x; j < n; j += 256) dst[j] = src[kappa[j]];
+    }
+    __syncthreads();
+    if (last) break;
+    p = q;
+  }
+}
+
+// The segment walk for bf16 rows of a multiple of 8 columns, 16-byte aligned:
+// one thread first chases the segment's positions p_0 = h, p_1, ... (nxt
+// flags the next head), then the rows move in chunks through LDS: a chunk's
+// source rows (p_{t+1}, or for the last position the next head's saved row,
+// or, in a cycle with a single head, the head's own row loaded before any
+// write) are all loaded before any of its destinations is written, and a
+// destination is never a source of a later chunk.  Each 8-column group reads
+// its column indices once for all rows of the chunk.
+constexpr int WK_MAXL = 64;
+constexpr int WK_SLOTS_BYTES = 144 * 1024;
+__global__ __launch_bounds__(256) void walk_rows_staged_bf16_kernel(uint16_t* W, const uint16_t* __restrict__ saved,
+                                                                    const int32_t* __restrict__ nxt,
+                                                                    const int32_t* __restrict__ hlist,
+                                                                    const int32_t* __restrict__ slot,
+                                                                    const int32_t* __restrict__ counts,
+                                                                    const int32_t* __restrict__ kappa, int n, int L) {
+  __shared__ __align__(16) uint16_t rows[WK_SLOTS_BYTES / 2];
+  __shared__ int pos[WK_MAXL + 1];
+  __shared__ int meta[2];
+  const int g = blockIdx.x;
+  if (g >= counts[0]) return;
+  const int tid = threadIdx.x;
+  const int h = hlist[g];
+  if (tid == 0) {
+    int p = h, c = 0, q = h;
+    pos[0] = h;
+    for (int step = 0; step < L; ++step) {
+      const int v = nxt[p];
+      q = v & 0x7fffffff;
+      ++c;
+      if (v < 0) break;
+      pos[c] = q;
+      p = q;
+    }
+    meta[0] = c;   // positions p_0 .. p_{c-1}
+    meta[1] = q;   // the next head
+  }
+  __syncthreads();
+  const int c = meta[0], F = meta[1];
+  const int sF = slot[F];
+  const bool single = sF < 0;     // then F == h: the cycle has this one head
+  const int n8 = n >> 3;
+  const int C = WK_SLOTS_BYTES / (n * 2);   // row slots (>= 4 for n <= 16384, >= 2 up to 32768)
+  auto load_row = [&](const uint16_t* src, int k) {
+    uint4* d = reinterpret_cast<uint4*>(rows + (int64_t)k * n);
+    const uint4* sv = reinterpret_cast<const uint4*>(src);
+    for (int e = tid; e < n8; e += 256) d[e] = sv[e];
+  };
+  // rows of the chunk [t0, t0 + cnt) go from slot sl(k) to p_{t0 + k}
+  auto write_rows = [&](int t0, int cnt, int keep_slot) {
+    for (int e = tid; e < n8; e += 256) {
+      const int4 pa = *reinterpret_cast<const int4*>(kappa + e * 8);
+      const int4 pb = *reinterpret_cast<const int4*>(kappa + e * 8 + 4);
+      for (int k = 0; k < cnt; ++k) {
+        const int t = t0 + k;
+        const int sl = (t == c - 1 && keep_slot >= 0) ? keep_slot : k;
+        const uint16_t* row = rows + (int64_t)sl * n;
+        uint4 v;
+        v.x = pack2(row[pa.x], row[pa.y]);
+        v.y = pack2(row[pa.z], row[pa.w]);
+        v.z = pack2(row[pb.x], row[pb.y]);
+        v.w = pack2(row[pb.z], row[pb.w]);
+        stg16(W + (int64_t)pos[t] * n + e * 8, v);
+      }
+    }
+  };
+  if (single && c <= C) {
+    // the whole cycle fits: slot t holds row p_t, p_t <- p_{(t+1) mod c}
+    for (int k = 0; k < c; ++k) load_row(W + (int64_t)pos[k] * n, k);
+    __syncthreads();
+    for (int e = tid; e < n8; e += 256) {
+      const int4 pa = *reinterpret_cast<const int4*>(kappa + e * 8);
+      const int4 pb = *reinterpret_cast<const int4*>(kappa + e * 8 + 4);
+      for (int t = 0; t < c; ++t) {
+        const uint16_t* row = rows + (int64_t)((t + 1 == c) ? 0 : t + 1) * n;
+        uint4 v;
+        v.x = pack2(row[pa.x], row[pa.y]);
+        v.y = pack2(row[pa.z], row[pa.w]);
+        v.z = pack2(row[pb.x], row[pb.y]);
+        v.w = pack2(row[pb.z], row[pb.w]);
+        stg16(W + (int64_t)pos[t] * n + e * 8, v);
+      }
+    }
+    return;
+  }
+  int keep_slot = -1, cap = C;
+  if (single) {
+    // keep the head's row in the last slot before p_0 is overwritten
+    keep_slot = C - 1;
+    cap = C - 1;
+    load_row(W + (int64_t)h * n, keep_slot);
+  }
+  for (int t0 = 0; t0 < c; t0 += cap) {
+    const int cnt = min(cap, c - t0);
+    for (int k = 0; k < cnt; ++k) {
+      const int t = t0 + k;
+      if (t + 1 < c) load_row(W + (int64_t)pos[t + 1] * n, k);
+      else if (!single) load_row(saved + (int64_t)sF * n, k);
+    }
+    __syncthreads();
+    write_rows(t0, cnt, keep_slot);
+    __syncthreads();
+  }
+}
+
+bool walk_staged_ok(int64_t n, int L, const void* W, const void* saved, const int32_t* kappa) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  return (n & 7) == 0 && n <= 32768 && L <= WK_MAXL && al(W) && al(saved) && al(kappa);
+}
+
+void launch_relayout_inplace(bool f32, void* W, void* saved, const int32_t* rho, const int32_t* kappa, int64_t m,
+                             int64_t n, int L, int32_t* dist, int32_t* hlist, int32_t* slot, int32_t* slist,
+                             int32_t* counts, int32_t* nxt, int64_t max_saved, hipStream_t s) {
+  if (m <= 0 || n <= 0) return;
+  hipLaunchKernelGGL(cycle_plan_kernel, dim3(1), dim3(CP_THREADS), 0, s, rho, (int)m, L, dist, hlist, slot, slist,
+                     counts, nxt);
+  if (!f32 && walk_staged_ok(n, L, W, saved, kappa)) {
+    if (max_saved > 0)
+      hipLaunchKernelGGL(save_heads_kernel<uint16_t>, dim3((unsigned)max_saved), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(W), static_cast<uint16_t*>(saved), slist, counts, (int)n);
+    hipLaunchKernelGGL(walk_rows_staged_bf16_kernel, dim3((unsigned)m), dim3(256), 0, s, static_cast<uint16_t*>(W),
+                       static_cast<const uint16_t*>(saved), nxt, hlist, slot, counts, kappa, (int)n, L);
+    return;
+  }
+  if (f32) {
+    if (max_saved > 0)
+      hipLaunchKernelGGL(save_heads_kernel<float>, dim3((unsigned)max_saved), dim3(256), 0, s,
+                         static_cast<const float*>(W), static_cast<float*>(saved), slist, counts, (int)n);
+    hipLaunchKernelGGL(walk_rows_kernel<float>, dim3((unsigned)m), dim3(256), 0, s, static_cast<float*>(W),
+                       static_cast<const float*>(saved), rho, kappa, dist, hlist, slot, counts, (int)n, L);
+  } else {
+    if (max_saved > 0)
+      hipLaunchKernelGGL(save_heads_kernel<uint16_t>, dim3((unsigned)max_saved), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(W), static_cast<uint16_t*>(saved), slist, counts, (int)n);
+    hipLaunchKernelGGL(walk_rows_kernel<uint16_t>, dim3((unsigned)m), dim3(256), 0, s, static_cast<uint16_t*>(W),
+                       static_cast<const uint16_t*>(saved), rho, kappa, dist, hlist, slot, counts, (int)n, L);
+  }
+}
+
 __global__ void copy_i32_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = src[i];

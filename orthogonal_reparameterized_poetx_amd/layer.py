@@ -235,7 +235,7 @@ def build_layer_blocks(layers, kind, stream=None, cnp_terms=0):
                 _build_ws[(dev, b, kind, "cnp")] = ws
             L.poetx_build_block_sets_cnp(sets, b, cnp_terms, ws, stream)
             continue
-        need = L.build_workspace_bytes(max(s[1] for s in sets), b)
+        need = L.build_workspace_bytes(sum(s[1] for s in sets), b)
         # one workspace per kind: builds of different kinds may run
         # concurrently on different streams
         ws = _build_ws.get((dev, b, kind))

@@ -48,7 +48,7 @@ def test_block_sets_match_single_builds(b, counts):
         sets.append((th, nb, q32, qb, qt))
         single.append(tuple(torch.empty(nb, b, b, dtype=t, device=dev)
                             for t in (torch.float32, torch.bfloat16, torch.bfloat16)))
-    ws = P.make_workspace(P.build_workspace_bytes(max(counts), b), dev)
+    ws = P.make_workspace(P.build_workspace_bytes(sum(counts), b), dev)
     P.poetx_build_block_sets(sets, b, ws)
     for (th, nb, _, _, _), (q32, qb, qt) in zip(sets, single):
         ws1 = P.make_workspace(P.build_workspace_bytes(nb, b), dev)
