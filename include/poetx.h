@@ -110,9 +110,16 @@ size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op);
  *   bytes [0, m*n)            int8 codes q[i][j], row-major, working layout
  *   bytes [off, off + 4m)     fp32 scales s[i], off = m*n rounded up to 256
  * The weight a pass uses is w[i][j] = bf16(s[i] * q[i][j]) (fp32 product,
- * both roundings to nearest even); every pass dequantizes it into its
- * workspace (the workspace sizes include that buffer), so its results equal
- * those of the bf16 layer whose W0p holds those values, bit for bit.  A
+ * both roundings to nearest even), so its results equal those of the bf16
+ * layer whose W0p holds those values, bit for bit.  When n % 16 == 0 and
+ * m % 8 == 0 the passes' GEMMs can read the codes and scales directly and
+ * form w as they stage their tiles, with no bf16 copy of the weight (W0p must
+ * then be 16-byte aligned, else POETX_EINVAL).  They do so by default unless
+ * n or m is a multiple of 64 of at least 2048 (there a dequantized copy in
+ * the workspace feeding the wide bf16 GEMM is faster); those layers, and
+ * other shapes, dequantize w into the pass's workspace first (the workspace
+ * sizes include that buffer).  poetx_forward_blocks_noalloc always reads the
+ * codes directly.  A
  * merge merges the dequantized weight and stores it again as codes:
  *   s[i] = max_j |w[i][j]| / 127, q[i][j] = clamp(rne(w[i][j] / s[i]), -127, 127)
  * in fp32 (s[i] = 0, q[i] = 0 for a row of zeros).
@@ -254,8 +261,9 @@ int poetx_forward_blocks(const poetx_layer* layer, const void* W0p, const poetx_
  * poetx_forward_blocks.  Calls on one GPU share the array, which keeps the
  * last call's contents: calls that overlap on one GPU (concurrent streams,
  * threads) race and must be serialized by the caller.  Errors: those of
- * poetx_forward_blocks; POETX_EINVAL for POETX_W0_INT8 layers (their
- * dequantized weight does not fit beside the chunk); POETX_ESHAPE if 128
+ * poetx_forward_blocks; POETX_EINVAL for POETX_W0_INT8 layers whose GEMMs
+ * cannot read the codes directly (n % 16 or m % 8 nonzero: their dequantized
+ * weight does not fit beside the chunk); POETX_ESHAPE if 128
  * tokens of the layer exceed the array; POETX_EHIP if the array's address
  * cannot be obtained.
  */

@@ -330,6 +330,27 @@ Shape shape_of(const poetx_layer* L, int64_t N) {
 // INT8 weight format: codes [m][n], then fp32 scales [m] at this byte offset
 size_t w0_scale_offset(int64_t m, int64_t n) { return ((size_t)m * n + kAlign - 1) / kAlign * kAlign; }
 
+// INT8 layers whose shapes the fused GEMM takes: the weight products can read
+// the codes and scales directly (bf16(s q) formed inside the GEMM)
+bool q8_direct(const Shape& S) { return S.q8 && S.n % 16 == 0 && S.m % 8 == 0; }
+// K at which the bf16 GEMM takes its wide kernel (gemm.hip)
+bool gemm_wide_k(int64_t K) { return K % 64 == 0 && K >= 2048; }
+// INT8 layers whose passes read the codes directly by default: those whose
+// GEMMs would not take the wide bf16 kernel in either direction.  Where they
+// would, dequantizing into the workspace and running the wide kernel measured
+// faster than the fused GEMM (whose weight tile is fed from registers), so
+// those layers keep the dequantized copy
+bool q8_fused(const Shape& S) { return q8_direct(S) && !gemm_wide_k(S.n) && !gemm_wide_k(S.m); }
+
+// the weight operand of a pass's products: bf16 (W0p itself, or an INT8
+// layer's codes dequantized into the workspace buffer w0) or INT8 codes and
+// scales read by the fused GEMM
+struct Wop {
+  const void* bf;
+  const int8_t* q;
+  const float* sc;
+};
+
 // the bf16 weight a pass reads: W0p itself, or (INT8 layers) its codes
 // dequantized into the pass's workspace buffer w0
 const void* weight_for_pass(const Shape& S, const void* W0p, void* w0, hipStream_t s) {
@@ -339,6 +360,27 @@ const void* weight_for_pass(const Shape& S, const void* W0p, void* w0, hipStream
   Tm tm(s, "dequant", 0.0, (double)S.m * S.n * 3);
   launch_dequant_rows(q, sc, static_cast<uint16_t*>(w0), S.m, S.n, s);
   return w0;
+}
+
+// w0 == nullptr: no room for a dequantized copy (the layer then reads its
+// codes directly; callers check q8_direct first)
+Wop weight_operand(const Shape& S, const void* W0p, void* w0, hipStream_t s) {
+  if (!(q8_fused(S) || (!w0 && q8_direct(S)))) return Wop{weight_for_pass(S, W0p, w0, s), nullptr, nullptr};
+  const int8_t* q = static_cast<const int8_t*>(W0p);
+  const float* sc = reinterpret_cast<const float*>(static_cast<const char*>(W0p) + w0_scale_offset(S.m, S.n));
+  return Wop{nullptr, q, sc};
+}
+
+// C = A W^T (NT: M x N, K) or C = A W (NN) with the pass's weight operand
+int weight_gemm(bool nn, const uint16_t* A, const Wop& W, uint16_t* C, int64_t M, int64_t N, int64_t K,
+                hipStream_t s) {
+  if (!W.q) {
+    launch_gemm_bf16(nn, A, static_cast<const uint16_t*>(W.bf), C, M, N, K, s);
+    return POETX_OK;
+  }
+  if (!launch_gemm_q8(nn, A, W.q, W.sc, C, M, N, K, s))
+    return fail(POETX_EINVAL, "INT8 weight operand not usable by the fused GEMM (alignment)");
+  return POETX_OK;
 }
 
 // Cayley blocks one forward / backward consumes (built by the call itself,
@@ -359,7 +401,9 @@ struct FwdWs {
   void *z1, *z2, *sc;
   void* w0;
 };
-FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes) {
+// w0copy false: no dequantized weight for INT8 layers (their GEMMs read the
+// codes; the no-allocation forward)
+FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes, bool w0copy = true) {
   Arena a(base);
   FwdWs w{};
   if (own) {
@@ -375,7 +419,7 @@ FwdWs plan_fwd(const Shape& S, bool own, void* base, size_t* bytes) {
   w.z1 = a.take<char>((size_t)S.N * S.n * S.es);
   w.z2 = a.take<char>((size_t)S.N * S.m * S.es);
   if (!S.f32) w.sc = a.take<char>((size_t)S.N * std::max(S.n, S.m) * S.es);   // permuted rows / block products
-  if (S.q8) w.w0 = a.take<char>((size_t)S.m * S.n * 2);                       // dequantized weight
+  if (S.q8 && !q8_fused(S) && w0copy) w.w0 = a.take<char>((size_t)S.m * S.n * 2);   // dequantized weight
   *bytes = a.off + kAlign;
   return w;
 }
@@ -415,7 +459,7 @@ BwdWs plan_bwd(const Shape& S, bool own, void* base, size_t* bytes, bool dq = fa
   }
   const size_t pb = std::max(gram_partials_bytes(S.N, S.b, S.kR, S.f32), gram_partials_bytes(S.N, S.b, S.kP, S.f32));
   w.part = a.take<char>(pb);
-  if (S.q8) w.w0 = a.take<char>((size_t)S.m * S.n * 2);   // dequantized weight
+  if (S.q8 && !q8_fused(S)) w.w0 = a.take<char>((size_t)S.m * S.n * 2);   // dequantized weight
   *bytes = a.off + kAlign;
   return w;
 }
@@ -515,7 +559,7 @@ int blockmul(const void* in, const uint16_t* q, void* out, int64_t N, int W, int
 // forward after the blocks exist: a3, a4, a5
 // z2out non-null (bf16): z2' goes there instead of the workspace (kept for
 // the backward pass)
-int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
+int fwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
              void* Y, const FwdWs& w, hipStream_t s, void* z2out = nullptr) {
   const int64_t N = S.N;
   const int n = (int)S.n, m = (int)S.m;
@@ -530,7 +574,7 @@ int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
     }
     {
       Tm tm(s, "gemm_fp32", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-      launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
+      launch_gemm_f32(false, (const float*)w.z1, (const float*)W0.bf, (float*)w.z2, N, S.m, S.n, s);
     }
     XformArgs r{};
     r.in = w.z2; r.out = Y; r.perm = sigma; r.N = N; r.W = m; r.B = S.b; r.k = S.kR; r.bq = q.q32R; r.trans = 0;
@@ -547,7 +591,7 @@ int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   void* const z2 = z2out ? z2out : w.z2;
   {
     Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-    launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)z2, N, S.m, S.n, s);
+    if ((rc = weight_gemm(false, (const uint16_t*)w.z1, W0, (uint16_t*)z2, N, S.m, S.n, s))) return rc;
   }
   if ((rc = check_launch("forward GEMM"))) return rc;
   // y = Pi_sigma^T r with r = D_R z2' (the tail of r is the tail of z2')
@@ -559,7 +603,7 @@ int fwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
 // gR / gP non-null: write dL/dQ there and stop before the chain rule
 // z2in non-null (bf16): z2' kept from the forward pass, so a0 reduces to
 // gathering x' again (no P-side block product, no forward GEMM)
-int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
+int bwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, const int32_t* tau, const void* X,
              const void* dY, void* dX, float* dthR, float* dthP, bool accum, const BwdWs& w, hipStream_t s,
              float* gR = nullptr, float* gP = nullptr, const void* z2in = nullptr) {
   float* const GR = gR ? gR : w.GR;
@@ -578,7 +622,7 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
     }
     {
       Tm tm(s, "gemm_fp32", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-      launch_gemm_f32(false, (const float*)w.z1, (const float*)W0p, (float*)w.z2, N, S.m, S.n, s);
+      launch_gemm_f32(false, (const float*)w.z1, (const float*)W0.bf, (float*)w.z2, N, S.m, S.n, s);
     }
     // R side: gY' = Pi_sigma gY (kept), gz2' = D_R^T gY'
     XformArgs r{};
@@ -594,7 +638,7 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
     if (!z2in) {
       if ((rc = blockmul(w.xg, q.qbP, w.z1, N, n, S.b, S.kP, s))) return rc;
       Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-      launch_gemm_bf16(false, (const uint16_t*)w.z1, (const uint16_t*)W0p, (uint16_t*)w.z2, N, S.m, S.n, s);
+      if ((rc = weight_gemm(false, (const uint16_t*)w.z1, W0, (uint16_t*)w.z2, N, S.m, S.n, s))) return rc;
     }
     if ((rc = check_launch("recompute"))) return rc;
     // R side: gY' = Pi_sigma gY (kept), gz2' = D_R^T gY' (blocks Q_R^T)
@@ -612,8 +656,8 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   void* gz1 = w.z1;
   {
     Tm tm(s, S.f32 ? "gemm_fp32" : "gemm_nn", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-    if (S.f32) launch_gemm_f32(true, (const float*)w.gz2, (const float*)W0p, (float*)gz1, N, S.n, S.m, s);
-    else launch_gemm_bf16(true, (const uint16_t*)w.gz2, (const uint16_t*)W0p, (uint16_t*)gz1, N, S.n, S.m, s);
+    if (S.f32) launch_gemm_f32(true, (const float*)w.gz2, (const float*)W0.bf, (float*)gz1, N, S.n, S.m, s);
+    else if ((rc = weight_gemm(true, (const uint16_t*)w.gz2, W0, (uint16_t*)gz1, N, S.n, S.m, s))) return rc;
   }
   // G_P = gz1'^T x' per block
   {
@@ -640,6 +684,13 @@ int bwd_core(const Shape& S, const void* W0p, const Blk& q, const int32_t* sigma
   return chain(w.GR, q.q32R, q.q32P, w.tmp, S.kR, S.kP, S.b, dthR, dthP, accum, S.f32, s);
 }
 
+// INT8 weights read by the fused GEMM: 16 codes per load
+int check_w0_int8_align(const Shape& S, const void* W0p) {
+  if (S.N > 0 && q8_direct(S) && reinterpret_cast<uintptr_t>(W0p) % 16)
+    return fail(POETX_EINVAL, "INT8 W0p not 16-byte aligned");
+  return POETX_OK;
+}
+
 // shared argument checks of forward / forward_blocks
 int check_fwd_args(const poetx_layer* layer, int64_t N, const void* W0p, const int32_t* sigma, const int32_t* tau,
                    const void* X, const void* Y) {
@@ -647,7 +698,7 @@ int check_fwd_args(const poetx_layer* layer, int64_t N, const void* W0p, const i
   if (rc) return rc;
   if ((rc = validate_N(N))) return rc;
   if (N > 0 && (!W0p || !sigma || !tau || !X || !Y)) return fail(POETX_EINVAL, "NULL tensor argument");
-  return POETX_OK;
+  return check_w0_int8_align(shape_of(layer, N), W0p);
 }
 
 int check_bwd_args(const poetx_layer* layer, int64_t N, const void* W0p, const int32_t* sigma, const int32_t* tau,
@@ -658,7 +709,7 @@ int check_bwd_args(const poetx_layer* layer, int64_t N, const void* W0p, const i
   const Shape S = shape_of(layer, N);
   if (N > 0 && (!W0p || !sigma || !tau || !X || !dY)) return fail(POETX_EINVAL, "NULL tensor argument");
   if ((S.kR > 0 && !dthR) || (S.kP > 0 && !dthP)) return fail(POETX_EINVAL, "NULL generator gradient");
-  return POETX_OK;
+  return check_w0_int8_align(S, W0p);
 }
 
 // gradient reset of an empty backward
@@ -787,7 +838,7 @@ int forward_blocks_impl(const poetx_layer* layer, const void* W0p, const poetx_b
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const FwdWs w = plan_fwd(S, false, ws, &need);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return fwd_core(S, weight_for_pass(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, Y, w, s, Z2);
+  return fwd_core(S, weight_operand(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, Y, w, s, Z2);
 }
 
 // poetx_backward_blocks_dq(_z2): Z2 non-null is z2' kept from the forward pass
@@ -811,7 +862,7 @@ int backward_dq_impl(const poetx_layer* layer, const void* W0p, const poetx_bloc
   plan_bwd(S, false, nullptr, &need, true);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const BwdWs w = plan_bwd(S, false, ws, &need, true);
-  return bwd_core(S, weight_for_pass(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, dY, dX, nullptr, nullptr,
+  return bwd_core(S, weight_operand(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, dY, dX, nullptr, nullptr,
                   false, w, s, GR, GP, Z2);
 }
 
@@ -854,7 +905,7 @@ int64_t noalloc_chunk(const poetx_layer* layer) {
   int64_t c = ((int64_t)kScratchBytes - 8 * (int64_t)kAlign) / per_token / 128 * 128;
   for (; c >= 128; c -= 128) {
     size_t need = 0;
-    plan_fwd(shape_of(layer, c), false, nullptr, &need);
+    plan_fwd(shape_of(layer, c), false, nullptr, &need, false);
     if (need <= kScratchBytes) return c;
   }
   return 0;
@@ -1032,7 +1083,7 @@ int poetx_forward(const poetx_layer* layer, const void* W0p, const float* thR, c
   else rc = build2(thR, S.kR, QOut{nullptr, w.qbR, nullptr}, thP, S.kP, QOut{nullptr, w.qbP, nullptr}, S.b, w.bws,
                    bmode, s);
   if (rc) return rc;
-  return fwd_core(S, weight_for_pass(S, W0p, w.w0, s), Blk{w.q32R, w.q32P, w.qbR, w.qbP, nullptr, nullptr}, sigma,
+  return fwd_core(S, weight_operand(S, W0p, w.w0, s), Blk{w.q32R, w.q32P, w.qbR, w.qbP, nullptr, nullptr}, sigma,
                   tau, X, Y, w, s);
 }
 
@@ -1055,10 +1106,10 @@ int poetx_forward_blocks_noalloc(const poetx_layer* layer, const void* W0p, cons
                                  void* stream) {
   int rc = check_fwd_args(layer, N, W0p, sigma, tau, X, Y);
   if (rc) return rc;
-  if (layer->flags & POETX_W0_INT8)
-    return fail(POETX_EINVAL, "poetx_forward_blocks_noalloc: POETX_W0_INT8 layers need a dequantized weight "
-                              "(m*n*2 bytes) beside the scratch; use poetx_forward_blocks");
   const Shape S0 = shape_of(layer, N);
+  if (S0.q8 && !q8_direct(S0))
+    return fail(POETX_EINVAL, "poetx_forward_blocks_noalloc: POETX_W0_INT8 layers with n %% 16 or m %% 8 nonzero "
+                              "need a dequantized weight (m*n*2 bytes) beside the scratch; use poetx_forward_blocks");
   if ((rc = check_blocks(S0, blocks, false))) return rc;
   if (N == 0) return POETX_OK;
   const int64_t chunk = noalloc_chunk(layer);
@@ -1072,9 +1123,11 @@ int poetx_forward_blocks_noalloc(const poetx_layer* layer, const void* W0p, cons
   for (int64_t t0 = 0; t0 < N; t0 += chunk) {
     const Shape S = shape_of(layer, std::min(chunk, N - t0));
     size_t need = 0;
-    const FwdWs w = plan_fwd(S, false, base, &need);
+    const FwdWs w = plan_fwd(S, false, base, &need, false);
     if (need > kScratchBytes) return fail(POETX_EWORKSPACE, "scratch plan of %zu bytes", need);
-    rc = fwd_core(S, W0p, q, sigma, tau, static_cast<const char*>(X) + t0 * S.n * (int64_t)S.es,
+    // INT8 layers here read their codes in the GEMM (no dequantized copy)
+    const Wop W0 = weight_operand(S, W0p, nullptr, s);
+    rc = fwd_core(S, W0, q, sigma, tau, static_cast<const char*>(X) + t0 * S.n * (int64_t)S.es,
                   static_cast<char*>(Y) + t0 * S.m * (int64_t)S.es, w, s);
     if (rc) return rc;
   }
@@ -1102,7 +1155,7 @@ int poetx_backward(const poetx_layer* layer, const void* W0p, const float* thR, 
   else rc = build2(thR, S.kR, QOut{w.q32R, nullptr, w.qtR}, thP, S.kP, QOut{w.q32P, w.qbP, w.qtP}, S.b, w.bws,
                    bmode, s);
   if (rc) return rc;
-  return bwd_core(S, weight_for_pass(S, W0p, w.w0, s), Blk{w.q32R, w.q32P, nullptr, w.qbP, w.qtR, w.qtP}, sigma,
+  return bwd_core(S, weight_operand(S, W0p, w.w0, s), Blk{w.q32R, w.q32P, nullptr, w.qbP, w.qtR, w.qtP}, sigma,
                   tau, X, dY, dX, dthR, dthP,
                   accum, w, s);
 }
@@ -1121,7 +1174,7 @@ int poetx_backward_blocks(const poetx_layer* layer, const void* W0p, const poetx
   plan_bwd(S, false, nullptr, &need);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const BwdWs w = plan_bwd(S, false, ws, &need);
-  return bwd_core(S, weight_for_pass(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, dY, dX, dthR, dthP, accum,
+  return bwd_core(S, weight_operand(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, dY, dX, dthR, dthP, accum,
                   w, s);
 }
 

@@ -25,6 +25,7 @@
 // count from the eighth iteration on, and a smaller one in the first seven.
 #include "common.h"
 #include "kernels.h"
+#include "ranges.h"
 
 namespace poetx {
 
@@ -183,7 +184,8 @@ __global__ __launch_bounds__(Bd<B>::NT) void blockdiag_kernel(const uint16_t* in
   // ---- per-lane tile addressing
   // loads: instruction h of wave w fills KiB (h NW + w) of a stage; lane i
   // writes slot c = 64 (h NW + w) + i = row c / CPR, chunk c % CPR
-  const __amdgpu_buffer_rsrc_t rin = rsrc(in + t0 * lda + (int64_t)l * B, (uint32_t)(rows - 1) * ldab + 2 * B);
+  const BufRange gin = tile_range(t0, rows, (int64_t)l * B, B, lda, 2);
+  const __amdgpu_buffer_rsrc_t rin = rsrc(in + gin.first, (uint32_t)gin.bytes);
   int voff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -192,7 +194,8 @@ __global__ __launch_bounds__(Bd<B>::NT) void blockdiag_kernel(const uint16_t* in
   }
   const uint32_t tin = (uint32_t)BD_T * ldab, tout = (uint32_t)BD_T * ldcb;
   // stores: thread tid writes chunks idx = h NT + tid = row idx / CPR, chunk idx % CPR
-  const __amdgpu_buffer_rsrc_t rout = rsrc(out + t0 * ldc + (int64_t)l * B, (uint32_t)(rows - 1) * ldcb + 2 * B);
+  const BufRange gout = tile_range(t0, rows, (int64_t)l * B, B, ldc, 2);
+  const __amdgpu_buffer_rsrc_t rout = rsrc(out + gout.first, (uint32_t)gout.bytes);
   int soff[2], sl[2];
   bool sw[2];
 #pragma unroll
@@ -308,20 +311,10 @@ bool launch_blockdiag_bf16(const uint16_t* in, const uint16_t* q, uint16_t* out,
   if ((lda & 7) || (ldc & 7) || (reinterpret_cast<uintptr_t>(in) & 15) || (reinterpret_cast<uintptr_t>(out) & 15) ||
       (reinterpret_cast<uintptr_t>(q) & 15))
     return false;
-  const int lds = (BD_S + 1) * BD_T * b * 2;
-  const int occ_lds = (160 * 1024) / lds, occ_w = 16 / (b / 32 > 0 ? b / 32 : 1);
-  const int occ = occ_lds < occ_w ? occ_lds : occ_w;
-  const int64_t ntiles = (N + BD_T - 1) / BD_T;
-  int64_t runs = (256LL * occ) / k;
-  if (runs < 1) runs = 1;
-  if (runs > ntiles) runs = ntiles;
-  int64_t tpc = (ntiles + runs - 1) / runs;
-  // 32-bit buffer offsets: the loads reach BD_S - 1 tiles past the run
-  const int64_t ld = lda > ldc ? lda : ldc;
-  const int64_t maxt = (0x7fffffffLL / (BD_T * ld * 2)) - BD_S;
-  if (maxt < 1) return false;
-  if (tpc > maxt) tpc = maxt;
-  runs = (ntiles + tpc - 1) / tpc;
+  static_assert(BD_T == BDIAG_T && BD_S == BDIAG_STAGES, "ranges.h mirrors the tiling");
+  const BdiagRuns br = blockdiag_runs(N, lda, ldc, b, k);
+  if (br.runs < 1) return false;
+  const int64_t runs = br.runs, tpc = br.tpc;
   const int64_t grid = runs * k;
   if (grid > 0x7fffffffLL) return false;
   switch (b) {
@@ -332,5 +325,6 @@ bool launch_blockdiag_bf16(const uint16_t* in, const uint16_t* q, uint16_t* out,
   }
   return true;
 }
+
 
 }  // namespace poetx

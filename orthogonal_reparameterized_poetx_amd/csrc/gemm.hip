@@ -17,6 +17,7 @@
 // (blockIdx mod 8) work on neighbouring output tiles and share L2.
 #include "common.h"
 #include "kernels.h"
+#include "ranges.h"
 
 namespace poetx {
 
@@ -26,10 +27,12 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, const_cast<uint16_t*>(p)));
 }
 
-// Buffer resource over [base, base + bytes): loads past the end read zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int nrec = (int)(bytes < 0x7fffffff ? (bytes > 0 ? bytes : 0) : 0x7fffffff);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+// Buffer resource over the exact extent of a tile (ranges.h): loads past it
+// read zero.  The record count is a 32-bit unsigned field; the launcher keeps
+// every operand below 4 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, BufRange r) {
+  const uint32_t nrec = (uint32_t)(r.bytes > 0 ? (r.bytes < 0xffffffffLL ? r.bytes : 0xffffffffLL) : 0);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + r.first), (short)0, (int)nrec, 0x00020000);
 }
 // 16-byte buffer load straight into LDS, bypassing the VGPRs: lane i of the
 // wave writes lds_base + 16 i (lds_base must be wave-uniform).  Streaming tiles
@@ -61,7 +64,7 @@ constexpr int GSE = 2 * 256 * 32;      // elements per stage (A and B)
 // asynchronous LDS fills have completed.
 constexpr unsigned vm_imm(unsigned vm) { return (vm & 15u) | ((vm >> 4) << 14) | (7u << 4) | (15u << 8); }
 
-template <bool NN, bool BATCHED, bool SMALL>
+template <bool NN, bool BATCHED, bool SMALL, bool Q8 = false>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
   // the four ring stages as separate LDS objects, each named at compile time
   // below, so that the compiler can tell reads of one from the asynchronous
@@ -102,9 +105,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
   // read zero.  The NN B operand adds its K position to the per-lane offset
   // instead: the range check covers only that offset, and the last row of a
   // partial N tile would otherwise read past the end of B.
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * lda, (int64_t)min(M - m0, GBM) * lda * 2);
-  const __amdgpu_buffer_rsrc_t rb = NN ? make_rsrc(Bm + n0, ((int64_t)K * ldb - n0) * 2)
-                                       : make_rsrc(Bm + (int64_t)n0 * ldb, (int64_t)min(N - n0, GBN) * ldb * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, gemm_range_a(m0, M, K, lda));
+  const __amdgpu_buffer_rsrc_t rb = NN ? make_rsrc(Bm, gemm_range_b_nn(n0, N, K, ldb))
+                                       : make_rsrc(Bm, gemm_range_b_nt(n0, N, K, ldb));
   // per-lane source offsets: instruction q (0, 1) of wave w fills KiB
   // (2 w + q) of a 16 KiB operand tile
   //   A, NT B: [256 rows][32 k], 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3)
@@ -132,12 +135,93 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
   // the end of its allocation there) and zero their slot instead.
   const int nk = (K + 31) / 32;
   const int r0 = K - 32 * (nk - 1);
+
+  // Q8: the weight operand B as INT8 codes with one fp32 scale per weight row
+  // (g.Bq, g.Bs; ldb counts codes).  Each thread loads 16 codes of one row of
+  // a stage's B tile into registers (a step ahead of their use), forms
+  // bf16(s * q) exactly as the dequantization kernel does, and writes them
+  // into the bf16 tile layout above, so the fragment reads and MFMAs are
+  // those of the bf16 kernel and the products are bit-identical.
+  //   NT: B tile [256 weight rows][32 k]: row qr = tid / 2, codes 16 qh .. 16 qh + 15
+  //   NN: B tile [32 k = weight rows][256 n]: row qk = tid / 16, codes 16 qc .. 16 qc + 15
+  typedef int q8v4 __attribute__((ext_vector_type(4)));
+  const BufRange rqr = !Q8 ? BufRange{0, 0} : NN ? gemm_range_bq_nn(n0, N, K, ldb) : gemm_range_bq_nt(n0, N, K, ldb);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(Q8 ? g.Bq + rqr.first : g.Bq), (short)0,
+      (int)(uint32_t)(rqr.bytes < 0xffffffffLL ? rqr.bytes : 0xffffffffLL), 0x00020000);
+  int qoff = 0, qrow = 0, qk0 = 0;
+  uint32_t qlds0 = 0, qlds1 = 0;
+  float qscale = 0.f;
+  if constexpr (Q8) {
+    if constexpr (!NN) {
+      const int qr = tid >> 1, qh = tid & 1, sw = (qr >> 2) & 3;
+      qrow = qr;
+      qk0 = 16 * qh;
+      qoff = (int)((int64_t)qr * ldb + qh * 16);
+      qlds0 = 16384u + (uint32_t)(qr * 64 + (((2 * qh) ^ sw) << 4));
+      qlds1 = 16384u + (uint32_t)(qr * 64 + (((2 * qh + 1) ^ sw) << 4));
+      qscale = n0 + qr < N ? g.Bs[n0 + qr] : 0.f;
+    } else {
+      const int qk = tid >> 4, qc = tid & 15, sw = (qk & 3) << 2;
+      qrow = qk;
+      qoff = (int)((int64_t)qk * ldb + qc * 16);
+      qlds0 = 16384u + (uint32_t)(qk * 512 + (((2 * qc) ^ sw) << 4));
+      qlds1 = 16384u + (uint32_t)(qk * 512 + (((2 * qc + 1) ^ sw) << 4));
+    }
+  }
+  // codes of the step starting at k0 into registers (NN: with the scale of
+  // this thread's weight row)
+  auto qload = [&](int k0, q8v4& c, float& sc) {
+    if constexpr (Q8) {
+      if constexpr (!NN) {
+        c = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, k0, 0);
+        sc = qscale;
+      } else {
+        c = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (int)((int64_t)k0 * ldb), 0, 0);
+        // one load on every lane (row clamped), so each step issues the same
+        // number of vector-memory operations; rows past K occur only in the
+        // first step, whose conversion zeroes them (kvalid).  The loaded
+        // value is used as is, so nothing waits for it before the conversion
+        sc = g.Bs[min(k0 + qrow, K - 1)];
+      }
+    }
+  };
+  // bf16(s * q) of the 16 codes into the B half of stage st; kvalid (the
+  // first stage only) zeroes the k positions at or past it
+  auto qconv = [&](const q8v4& c, float sc, const uint16_t* st, int kvalid) {
+    if constexpr (Q8) {
+      uint32_t o[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const uint32_t word = (uint32_t)c[h >> 1];
+        const int sh = 16 * (h & 1);
+        float lo = (float)(int8_t)(word >> sh) * sc;
+        float hi = (float)(int8_t)(word >> (sh + 8)) * sc;
+        if (kvalid < 32) {
+          // NT: code 2h (+1) of this thread sits at k = qk0 + 2h (+1); NN: all at k = qrow
+          const int e0 = qk0 + 2 * h;
+          const bool keep_lo = NN ? qrow < kvalid : e0 < kvalid;
+          const bool keep_hi = NN ? qrow < kvalid : e0 + 1 < kvalid;
+          lo = keep_lo ? lo : 0.f;
+          hi = keep_hi ? hi : 0.f;
+        }
+        o[h] = pack2(f32_to_bits(lo), f32_to_bits(hi));
+      }
+      const uint32_t sb = (uint32_t)reinterpret_cast<uintptr_t>(st);
+      const q8v4 v0 = {(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+      const q8v4 v1 = {(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+      asm volatile("ds_write_b128 %0, %2\n\tds_write_b128 %1, %3" ::"v"(sb + qlds0), "v"(sb + qlds1), "v"(v0),
+                   "v"(v1)
+                   : "memory");
+    }
+  };
   auto dload = [&](int k0, uint16_t* st) {
     uint16_t* as_ = st;
     uint16_t* bs_ = st + 256 * 32;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       b2l16(ra, voa[q], k0 * 2, as_ + (wave * 2 + q) * 512);
+      if constexpr (Q8) continue;
       if constexpr (!NN) b2l16(rb, vob[q], k0 * 2, bs_ + (wave * 2 + q) * 512);
       else b2l16(rb, vob[q] + (int)((int64_t)k0 * ldb * 2), 0, bs_ + (wave * 2 + q) * 512);
     }
@@ -150,6 +234,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
     for (int q = 0; q < 2; ++q) {
       if (csa[q] * 8 < r0) b2l16(ra, voa[q], 0, as_ + (wave * 2 + q) * 512);
       else *reinterpret_cast<uint4*>(as_ + (wave * 2 + q) * 512 + lane * 8) = z;
+      if constexpr (Q8) continue;
       if constexpr (!NN) {
         if (csa[q] * 8 < r0) b2l16(rb, vob[q], 0, bs_ + (wave * 2 + q) * 512);
         else *reinterpret_cast<uint4*>(bs_ + (wave * 2 + q) * 512 + lane * 8) = z;
@@ -260,12 +345,32 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
   // that opens the first memory phase reading it (every wave waits for its
   // own loads of step k before that barrier); a stage is refilled only in a
   // phase after both halves have read it.
+  // Q8 code registers: step j's codes live in set j % 2.  Step 0 is
+  // converted here; step j >= 1 in the memory phase of step j - 1, two steps
+  // after its codes were loaded, and the set is then refilled with the codes
+  // of step j + 2
+  q8v4 qcs0{}, qcs1{};
+  float qsc0 = 0.f, qsc1 = 0.f;
   dload_first(S0);
+  if constexpr (Q8) {
+    qload(0, qcs0, qsc0);
+    qconv(qcs0, qsc0, S0, r0);
+  }
   asm volatile("" ::: "memory");
-  if (!SMALL || 1 < nk) dload(r0, S1);
+  if (!SMALL || 1 < nk) {
+    dload(r0, S1);
+    if constexpr (Q8) qload(r0, qcs1, qsc1);
+  }
   asm volatile("" ::: "memory");
-  if (!SMALL || 2 < nk) dload(r0 + 32, S2);
+  if (!SMALL || 2 < nk) {
+    dload(r0 + 32, S2);
+    if constexpr (Q8) qload(r0 + 32, qcs0, qsc0);
+  }
   asm volatile("" ::: "memory");
+  // vector-memory operations one step issues: A and B (bf16), or A, the
+  // codes and (NN) the scales (Q8); two steps' worth may stay in flight
+  constexpr int QOPS = Q8 ? (NN ? 4 : 3) : 4;
+  constexpr int QW = QOPS * (S - 2);
   const bool lag = wave >= 4;
 #define PPBAR(VM)                                                                    \
   {                                                                                  \
@@ -277,40 +382,57 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
     asm volatile("" ::: "memory");                                                   \
     __builtin_amdgcn_sched_barrier(0);                                               \
   }
-  if (SMALL) PPBAR(0) else PPBAR(4 * (S - 2))
+  if (SMALL) PPBAR(0) else PPBAR(QW)
   if (lag) __builtin_amdgcn_s_barrier();
-#define PPSTEADY(I, CUR, NEXT)                                                       \
+  // memory phase of step I: loads of step I + 3 into stage NEXT; Q8: the
+  // codes of step I + 1 (set QS_) converted into stage CONV, then the same set
+  // refilled with the codes of step I + 3; the fragments of stage CUR; then
+  // the compute phase
+#define PPSTEADY(I, CUR, NEXT, CONV, QS_, QC_)                                       \
   {                                                                                  \
     dload(r0 + ((I) + S - 2) * 32, NEXT);                                            \
     asm volatile("" ::: "memory");                                                   \
+    if constexpr (Q8) {                                                              \
+      qconv(QS_, QC_, CONV, 32);                                                     \
+      __builtin_amdgcn_sched_barrier(0);                                             \
+      qload(r0 + ((I) + S - 2) * 32, QS_, QC_);                                      \
+    }                                                                                \
     frags(CUR);                                                                      \
-    PPBAR(4 * (S - 2))                                                               \
+    PPBAR(QW)                                                                        \
     mma();                                                                           \
-    PPBAR(4 * (S - 2))                                                               \
+    PPBAR(QW)                                                                        \
   }
-#define PPSTEP(I, CUR, NEXT)                                                         \
+#define PPSTEP(I, CUR, NEXT, CONV, QS_, QC_)                                         \
   {                                                                                  \
     const int i_ = (I);                                                              \
     const bool more = i_ + S - 1 < nk;                                               \
     if (more) dload(r0 + (i_ + S - 2) * 32, NEXT);                                   \
     asm volatile("" ::: "memory");                                                   \
+    if constexpr (Q8) {                                                              \
+      if (i_ + 1 < nk) qconv(QS_, QC_, CONV, 32);                                    \
+      __builtin_amdgcn_sched_barrier(0);                                             \
+      if (more) qload(r0 + (i_ + S - 2) * 32, QS_, QC_);                             \
+    }                                                                                \
     frags(CUR);                                                                      \
-    if (more) PPBAR(4 * (S - 2)) else PPBAR(0)                                       \
+    if (more) PPBAR(QW) else PPBAR(0)                                                \
     mma();                                                                           \
-    if (more) PPBAR(4 * (S - 2)) else PPBAR(0)                                       \
+    if (more) PPBAR(QW) else PPBAR(0)                                                \
   }
   int kt = 0;
   if constexpr (!SMALL) {
     for (; kt + 2 * S - 2 < nk; kt += S) {
-      PPSTEADY(kt, S0, S3) PPSTEADY(kt + 1, S1, S0) PPSTEADY(kt + 2, S2, S1) PPSTEADY(kt + 3, S3, S2)
+      PPSTEADY(kt, S0, S3, S1, qcs1, qsc1)
+      PPSTEADY(kt + 1, S1, S0, S2, qcs0, qsc0)
+      PPSTEADY(kt + 2, S2, S1, S3, qcs1, qsc1)
+      PPSTEADY(kt + 3, S3, S2, S0, qcs0, qsc0)
     }
   }
-  if (kt < nk) PPSTEP(kt, S0, S3)
-  if (kt + 1 < nk) PPSTEP(kt + 1, S1, S0)
-  if (kt + 2 < nk) PPSTEP(kt + 2, S2, S1)
-  if (kt + 3 < nk) PPSTEP(kt + 3, S3, S2)
-  if (kt + 4 < nk) PPSTEP(kt + 4, S0, S3)
-  if (kt + 5 < nk) PPSTEP(kt + 5, S1, S0)
+  if (kt < nk) PPSTEP(kt, S0, S3, S1, qcs1, qsc1)
+  if (kt + 1 < nk) PPSTEP(kt + 1, S1, S0, S2, qcs0, qsc0)
+  if (kt + 2 < nk) PPSTEP(kt + 2, S2, S1, S3, qcs1, qsc1)
+  if (kt + 3 < nk) PPSTEP(kt + 3, S3, S2, S0, qcs0, qsc0)
+  if (kt + 4 < nk) PPSTEP(kt + 4, S0, S3, S1, qcs1, qsc1)
+  if (kt + 5 < nk) PPSTEP(kt + 5, S1, S0, S2, qcs0, qsc0)
   if (!lag) __builtin_amdgcn_s_barrier();
 #undef PPSTEADY
 #undef PPSTEP
@@ -439,9 +561,9 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)m0 * lda, (int64_t)min(M - m0, GBM) * lda * 2);
-  const __amdgpu_buffer_rsrc_t rb = NN ? make_rsrc(Bm + n0, ((int64_t)K * ldb - n0) * 2)
-                                       : make_rsrc(Bm + (int64_t)n0 * ldb, (int64_t)min(N - n0, GBN) * ldb * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, gemm_range_a(m0, M, K, lda));
+  const __amdgpu_buffer_rsrc_t rb = NN ? make_rsrc(Bm, gemm_range_b_nn(n0, N, K, ldb))
+                                       : make_rsrc(Bm, gemm_range_b_nt(n0, N, K, ldb));
   // per-lane source offsets.  32-deep ring, instruction q (0, 1) of wave w
   // fills KiB 2 w + q of a stage: NT A [256 rows][32 k] (chunk c of row r at
   // c ^ ((r >> 2) & 3)), NN B [32 k rows][256 n] (chunk c of row r at
@@ -721,8 +843,7 @@ static bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1
 
 void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return;
-  const bool tiled = g.K > 0 && g.K % 8 == 0 && g.N % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
-                     g.sA % 8 == 0 && g.sB % 8 == 0 && aligned8(g.A) && aligned8(g.B);
+  const bool tiled = gemm_tiled_shape(g.N, g.K, g.lda, g.ldb, g.sA, g.sB) && aligned8(g.A) && aligned8(g.B);
   if (tiled) {
     const int tn = (g.N + GBN - 1) / GBN, tm = (g.M + GBM - 1) / GBM;
     const int nt = tn * tm * g.batch;
@@ -749,6 +870,33 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     if (nn) hipLaunchKernelGGL(gemm_bf16_generic_kernel<true>, grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL(gemm_bf16_generic_kernel<false>, grid, dim3(256), 0, s, g);
   }
+}
+
+bool launch_gemm_q8(bool nn, const uint16_t* A, const int8_t* codes, const float* scales, uint16_t* C, int64_t M,
+                    int64_t N, int64_t K, hipStream_t s) {
+  if (M <= 0 || N <= 0) return true;
+  GemmArgs g{};
+  g.A = A; g.B = nullptr; g.C = C;
+  g.Bq = codes; g.Bs = scales;
+  g.M = (int)M; g.N = (int)N; g.K = (int)K;
+  g.lda = K; g.ldb = nn ? N : K; g.ldc = N;
+  g.batch = 1;
+  // 16 codes per load: weight rows of a multiple of 16 bytes
+  if (!gemm_tiled_shape(g.N, g.K, g.lda, g.ldb, 0, 0) || g.ldb % 16 != 0 || !aligned8(A) || !aligned8(codes) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3))
+    return false;
+  const int tn = (g.N + GBN - 1) / GBN, tm = (g.M + GBM - 1) / GBM;
+  const int nt = tn * tm;
+  const int grid = ((nt + 7) / 8) * 8;
+  const bool small = (g.K + 31) / 32 < GST - 1;
+  if (nn) {
+    if (small) hipLaunchKernelGGL((gemm_bf16_kernel<true, false, true, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    else hipLaunchKernelGGL((gemm_bf16_kernel<true, false, false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+  } else {
+    if (small) hipLaunchKernelGGL((gemm_bf16_kernel<false, false, true, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    else hipLaunchKernelGGL((gemm_bf16_kernel<false, false, false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+  }
+  return true;
 }
 
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N, int64_t K,

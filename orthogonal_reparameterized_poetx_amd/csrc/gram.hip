@@ -12,6 +12,7 @@
 // second kernel, so the result is deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "ranges.h"
 
 namespace poetx {
 
@@ -49,17 +50,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gr_rsrc(const void* base, uint
 constexpr unsigned gr_vm_imm(unsigned vm) { return (vm & 15u) | ((vm >> 4) << 14) | (7u << 4) | (15u << 8); }
 
 // run plan shared by the launcher and the workspace query
-struct GramRuns { int runs; int tpc; };
-static GramRuns gram_stream_runs(int64_t N, int B, int k) {
-  const int q = (B / GR_TI) * (B / GR_TI);
-  const int64_t ntiles = (N + GR_T - 1) / GR_T;
-  int64_t r = 256 / ((int64_t)k * q);
-  if (r < 1) r = 1;
-  if (r > ntiles) r = ntiles;
-  int64_t tpc = (ntiles + r - 1) / r;
-  r = (ntiles + tpc - 1) / tpc;
-  return GramRuns{(int)r, (int)tpc};
-}
+static_assert(GR_T == GRAM_T && GR_TI == GRAM_TI && GR_S == GRAM_STAGES, "ranges.h mirrors the tiling");
 static bool gram_stream_ok(int64_t N, int W, int B, const void* A, const void* C) {
   if (B != 128 && B != 256) return false;
   if ((W & 7) || (reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(C) & 15)) return false;
@@ -238,8 +229,10 @@ __global__ __launch_bounds__(512) void gram_stream_kernel(const uint16_t* __rest
   // operand tiles [32 tokens][128 columns], 256-byte rows; chunk c of token
   // row t at c ^ ((t & 3) << 2), so that a 32-lane phase of the transposing
   // fragment read (4 rows x 4 chunks x 2 halves) touches every bank pair once
-  const __amdgpu_buffer_rsrc_t ra = gr_rsrc(A + t0 * W + (int64_t)l * B + ti * GR_TI, (uint32_t)(rows - 1) * ldb + 2 * GR_TI);
-  const __amdgpu_buffer_rsrc_t rc = gr_rsrc(C + t0 * W + (int64_t)l * B + tj * GR_TI, (uint32_t)(rows - 1) * ldb + 2 * GR_TI);
+  const BufRange ga = tile_range(t0, rows, (int64_t)l * B + ti * GR_TI, GR_TI, W, 2);
+  const BufRange gc = tile_range(t0, rows, (int64_t)l * B + tj * GR_TI, GR_TI, W, 2);
+  const __amdgpu_buffer_rsrc_t ra = gr_rsrc(A + ga.first, (uint32_t)ga.bytes);
+  const __amdgpu_buffer_rsrc_t rc = gr_rsrc(C + gc.first, (uint32_t)gc.bytes);
   // wave w fills KiB w of both tiles of a stage: token row 4 w + lane / 16, chunk lane % 16
   int voff;
   {

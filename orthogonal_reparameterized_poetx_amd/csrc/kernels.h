@@ -111,6 +111,7 @@ void launch_scatter_out_f32(const XformArgs& a, hipStream_t s);
 bool launch_blockdiag_bf16(const uint16_t* in, const uint16_t* q, uint16_t* out, int64_t N, int64_t lda,
                            int64_t ldc, int b, int k, hipStream_t s);
 
+
 // ---- dense GEMMs (gemm.hip): C[M][N] = A[M][K] * op(B)
 // nt: B is [N][K] (C = A B^T); nn: B is [K][N] (C = A B)
 // Batched bf16 GEMM with strides (elements): for z < batch,
@@ -125,8 +126,19 @@ struct GemmArgs {
   int64_t lda, ldb, ldc;
   int64_t sA, sB, sC;
   int batch;
+  // INT8 weight operand (launch_gemm_q8): codes in place of B, one fp32
+  // scale per weight row
+  const int8_t* Bq;
+  const float* Bs;
 };
 void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s);
+// C = A op(W) with W = bf16(s_i q_ij) formed inside the GEMM from INT8 codes
+// q [rows][cols] and scales s [rows] (NT: W [N][K], rows = N; NN: W [K][N],
+// rows = K).  Returns false (nothing launched) where the tiled kernel does not
+// apply: K % 16 (NT) or N % 16 (NN), K or N not a multiple of 8, or
+// misaligned operands.
+bool launch_gemm_q8(bool nn, const uint16_t* A, const int8_t* codes, const float* scales, uint16_t* C, int64_t M,
+                    int64_t N, int64_t K, hipStream_t s);
 void launch_gemm_bf16(bool nn, const uint16_t* A, const uint16_t* Bm, uint16_t* C, int64_t M, int64_t N,
                       int64_t K, hipStream_t s);
 void launch_gemm_f32(bool nn, const float* A, const float* Bm, float* C, int64_t M, int64_t N, int64_t K,

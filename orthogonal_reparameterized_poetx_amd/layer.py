@@ -14,7 +14,8 @@ from . import _lib as L
 class PoetxLayer:
     def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0, ws_pool=None, w0_int8=False):
         """w0_int8: keep W0p in the INT8 weight format (per-row codes and
-        scales, POETX_W0_INT8; bf16 layers), dequantized by every pass."""
+        scales, POETX_W0_INT8; bf16 layers), turned into bf16 inside the
+        passes' GEMMs or dequantized by each pass (include/poetx.h says which)."""
         self.device = torch.device(device)
         self.dt = L.POETX_BF16 if dtype == "bf16" else L.POETX_F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32

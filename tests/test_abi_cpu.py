@@ -252,6 +252,28 @@ def test_int8_weight_format_validates_on_host():
     plain = P.Layer(600, 520, 64, P.POETX_BF16)
     for op in (P.OP_FORWARD, P.OP_BACKWARD, P.OP_FORWARD_BLOCKS, P.OP_BACKWARD_DQ, P.OP_MERGE):
         assert P.workspace_bytes(lay, 64, op) >= P.workspace_bytes(plain, 64, op) + 600 * 520 * 2
+    # n % 16 == 0 and m % 8 == 0: the GEMMs read the codes, so the passes
+    # need no copy (the merge still merges a dequantized weight)
+    fused = P.Layer(600, 528, 64, P.POETX_BF16, P.POETX_W0_INT8)
+    plain_f = P.Layer(600, 528, 64, P.POETX_BF16)
+    for op in (P.OP_FORWARD, P.OP_BACKWARD, P.OP_FORWARD_BLOCKS, P.OP_BACKWARD_DQ):
+        assert P.workspace_bytes(fused, 64, op) == P.workspace_bytes(plain_f, 64, op)
+    assert P.workspace_bytes(fused, 0, P.OP_MERGE) >= P.workspace_bytes(plain_f, 0, P.OP_MERGE) + 600 * 528 * 2
+    # K >= 2048 (a multiple of 64) in either GEMM: the dequantized copy feeds the wide bf16 kernel
+    big = P.Layer(2048, 2048, 256, P.POETX_BF16, P.POETX_W0_INT8)
+    big_plain = P.Layer(2048, 2048, 256, P.POETX_BF16)
+    for op in (P.OP_FORWARD_BLOCKS, P.OP_BACKWARD_DQ):
+        assert P.workspace_bytes(big, 64, op) == P.workspace_bytes(big_plain, 64, op) + 2048 * 2048 * 2
+    # host-side rejections, before anything is enqueued: codes not 16-byte
+    # aligned (fused shapes), and the no-allocation forward of a layer that
+    # would need a copy
+    blk = P.Blocks()
+    odd = ctypes.c_void_p(0x1008)
+    nb = ctypes.byref(blk)
+    assert L.poetx_forward_blocks_noalloc(ctypes.byref(fused), odd, nb, fake, fake, fake, 64, fake, None) == -1
+    assert "aligned" in P.last_error()
+    assert L.poetx_forward_blocks_noalloc(ctypes.byref(lay), fake, nb, fake, fake, fake, 64, fake, None) == -1
+    assert "INT8" in P.last_error()
     # fp32 layers cannot carry the flag; the conversions need it
     l32 = P.Layer(600, 520, 64, P.POETX_F32, P.POETX_W0_INT8)
     assert L.poetx_w0_bytes(ctypes.byref(l32)) == 0

@@ -59,7 +59,10 @@ def test_quantize_and_dequantize_match_oracle(m, n):
     assert np.array_equal(from_dev(lay.weight()), oracle.dequantize_rows(qr, sr))
 
 
-@pytest.mark.parametrize("m,n,b,N", [(600, 520, 256, 70), (2048, 2048, 256, 45), (512, 256, 64, 33)])
+# n % 16 or m % 8 nonzero: each pass dequantizes into its workspace; the
+# others go through the fused GEMM (ragged tiles, K below and above the ring)
+@pytest.mark.parametrize("m,n,b,N", [(600, 520, 256, 70), (2048, 2048, 256, 45), (512, 256, 64, 33),
+                                     (600, 528, 128, 300), (96, 64, 32, 130)])
 def test_int8_layer_equals_bf16_layer_on_dequantized_weight(m, n, b, N):
     torch = torch_mod()
     import orthogonal_reparameterized_poetx_amd as P

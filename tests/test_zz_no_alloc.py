@@ -2,7 +2,8 @@
 nothing): its output equals poetx_forward_blocks' bit for bit on two calls in
 a row, the second with a smaller input (the scratch array keeps the first
 call's contents), for a bf16 layer whose token count needs several chunks of
-the scratch, a ragged bf16 layer and an fp32 layer; INT8 layers are
+the scratch, a ragged bf16 layer, an fp32 layer and an INT8 layer whose GEMMs
+read the codes directly; INT8 layers that would need a dequantized copy are
 rejected."""
 
 import numpy as np
@@ -18,10 +19,10 @@ def _log(msg):
     print(msg, flush=True)
 
 
-def _check_pair(inp, n_small):
+def _check_pair(inp, n_small, w0_int8=False):
     torch = torch_mod()
     from orthogonal_reparameterized_poetx_amd import build_layer_blocks
-    lay, d = make_layer(inp)
+    lay, d = make_layer(inp, w0_int8=w0_int8)
     build_layer_blocks([lay], "forward")
     X = d["X"]
     N = X.shape[0]
@@ -55,14 +56,25 @@ def test_noalloc_forward_ragged_and_fp32():
     _check_pair(WL.small_case(72, 96, 80, 32, 150, dtype="f32"), 37)
 
 
-def test_noalloc_rejects_int8_layers():
+def test_noalloc_forward_int8_codes():
+    # n % 16 == 0 and m % 8 == 0: the GEMM reads the codes, nothing else is needed
+    _log("noalloc INT8 600x528 b=128")
+    _check_pair(WL.small_case(74, 600, 528, 128, 301, dtype="bf16"), 45, w0_int8=True)
+    # K = 2048 both ways: poetx_forward_blocks dequantizes into its workspace
+    # and runs the wide bf16 kernel, the no-allocation call reads the codes
+    _log("noalloc INT8 2048x2048 b=256")
+    _check_pair(WL.small_case(75, 2048, 2048, 256, 200, dtype="bf16"), 64, w0_int8=True)
+
+
+def test_noalloc_rejects_int8_layers_needing_a_copy():
     torch = torch_mod()
     import orthogonal_reparameterized_poetx_amd as P
     from orthogonal_reparameterized_poetx_amd import build_layer_blocks
-    inp = WL.small_case(73, 256, 256, 64, 8, dtype="bf16")
-    lay = P.PoetxLayer(256, 256, 64, "bf16", "cuda:0", perm_seed=inp["perm_seed"], w0_int8=True)
+    # n = 520: not a multiple of 16, so every pass would dequantize into a workspace
+    inp = WL.small_case(73, 256, 520, 64, 8, dtype="bf16")
+    lay = P.PoetxLayer(256, 520, 64, "bf16", "cuda:0", perm_seed=inp["perm_seed"], w0_int8=True)
     build_layer_blocks([lay], "forward")
-    X = torch.zeros(8, 256, dtype=torch.bfloat16, device="cuda:0")
+    X = torch.zeros(8, 520, dtype=torch.bfloat16, device="cuda:0")
     Y = torch.empty(8, 256, dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(P.PoetxError) as e:
         lay.forward_blocks_noalloc(X, Y)
