@@ -2,7 +2,9 @@
 
 Workload (default): the LLaMA-1B-shaped layer set -- q, k, v, o 2048x2048,
 gate, up 5632x2048, down 2048x5632 -- bf16 W0, block size 256, 8192 tokens,
-generators ~N(0, 1e-3).  One step is the hot path over one batch: forward of
+generators ~N(0, 1e-3).  --workload square: one 2048x2048 layer, b = 256,
+4096 tokens; --workload mlp7b --b B: the 11008x4096 MLP projection at block
+size B, 8192 tokens; --workload stack24: the 24-layer stack's training step.  One step is the hot path over one batch: forward of
 all seven matrices, then backward of all seven (reverse order) with the
 blocks and activations recomputed, generator gradients for every block and
 the input gradient.  Inputs are seeded synthetic tensors already resident in
@@ -28,11 +30,19 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-# MFMA-bound classes and the dense peak of the arithmetic they carry: the
-# weight products run on bf16 MFMA; the Cayley solve and the chain rule are
-# fp32 computations (emulated with split bf16 products), so they take the
-# fp32 peak
-MFMA_CLASSES = {"gemm_nt": 2500.0, "gemm_nn": 2500.0, "cayley_build": 157.3, "chain_rule": 157.3}
+# MFMA-bound classes and the dense peak of the arithmetic they carry (flops
+# counted as the algorithm's own, fp32 for the emulated classes): the weight
+# products run on bf16 MFMA at 2.5 PFLOP/s; the chain rule forms each
+# fp32-accurate product from three bf16 products of split operands (hi hi +
+# hi lo + lo hi), so its fp32 flops peak at 2500/3; the Cayley builder's
+# trailing updates take six (three-way splits), so 2500/6
+MFMA_CLASSES = {"gemm_nt": 2500.0, "gemm_nn": 2500.0, "cayley_build": 2500.0 / 6, "chain_rule": 2500.0 / 3}
+CU_COUNT = 256
+SIMD_COUNT = 1024   # 256 compute units x 4 SIMDs
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")
+# HBM-bound classes of the block transforms (permutations, block products,
+# Gram products)
+HBM_CLASSES = ("xform_permute", "xform_blockmul", "gram")
 
 # kernel name (demangled, as rocprofv3 prints it) -> timing class of the library,
 # and the dispatches one timed launch of the class makes
@@ -56,6 +66,22 @@ KERNEL_CLASSES = [
     ("quantize_rows_kernel", "quantize", 1),
 ]
 CALIBRATION_BYTES = 256 << 20   # the copy kernel reads and writes this many bytes each
+# sources whose hash keys the committed counter records
+SOURCE_FILES = ["api.hip", "build.hip", "chain.hip", "transform.hip", "blockdiag.hip", "gemm.hip", "gram.hip",
+                "merge.hip", "quant.hip", "cnp.hip", "common.h", "kernels.h"]
+
+
+def balance_streams(shapes, N, nstreams):
+    """Stream index per matrix: longest first onto the least loaded stream,
+    by an estimate of each matrix's fwd+bwd time (three GEMMs at 1.1 PF/s;
+    28n + 20m bytes of block transforms per token at 3.5 TB/s)."""
+    cost = [6.0 * N * m * n / 1.1e15 + (28.0 * n + 20.0 * m) * N / 3.5e12 for m, n in shapes]
+    load, where = [0.0] * nstreams, [0] * len(shapes)
+    for i in sorted(range(len(shapes)), key=lambda i: -cost[i]):
+        w = min(range(nstreams), key=lambda w: load[w])
+        where[i] = w
+        load[w] += cost[i]
+    return where
 
 
 def kernel_class(name):
@@ -72,7 +98,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (default 8192)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=3072, help="token sample of the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="token sample of the oracle baseline (default: 3072 for the layer set, all 4096 for the "
+                         "square layer, 2048 for the MLP projection)")
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain copy kernel of %d MiB (read and write) for counter calibration"
@@ -80,20 +108,26 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
                          "'bench.py --calibrate-copy' into profiles/traffic_<class>.json")
+    ap.add_argument("--mfma-from", metavar="PMC_DIR",
+                    help="no GPU: turn a rocprofv3 --pmc run of %s into profiles/mfma_<class>.json"
+                         % " ".join(MFMA_COUNTERS))
     ap.add_argument("--kernel-stats", metavar="CSV",
                     help="no GPU: summarize by kernel class a rocprofv3 kernel_stats.csv (whole run) or a "
                          "kernel_trace.csv (only the marked, serialized per-kernel timing pass)")
-    ap.add_argument("--workload", choices=("layerset", "stack24"), default="layerset",
-                    help="layerset: fwd+bwd of the LLaMA-1B layer set (default); stack24: one training step of the "
-                         "24-layer stack with Adam and the global merge")
+    ap.add_argument("--workload", choices=("layerset", "square", "mlp7b", "stack24"), default="layerset",
+                    help="layerset: fwd+bwd of the LLaMA-1B layer set (default); square: the 2048x2048 layer, b=256, "
+                         "4096 tokens; mlp7b: the LLaMA-7B MLP projection 11008x4096, 8192 tokens, block size --b; "
+                         "stack24: one training step of the 24-layer stack with Adam and the global merge")
+    ap.add_argument("--b", type=int, default=None,
+                    help="block size of --workload mlp7b (64, 128, 256 or 512; default 512)")
     ap.add_argument("--streams", type=int, default=3,
                     help="HIP streams the seven independent matrices are spread over (batched mode)")
     ap.add_argument("--chain", choices=["batched", "per-matrix"], default="batched",
                     help="layer set: one chain-rule call for all matrices after the backward pass, or one per "
                          "matrix on its stream")
     ap.add_argument("--w0-int8", action="store_true",
-                    help="layer set: base weights stored as per-row INT8 codes and scales (POET-XQ), dequantized "
-                         "by every pass")
+                    help="layer set: base weights stored as per-row INT8 codes and scales (POET-XQ), turned "
+                         "into bf16 inside the GEMMs")
     ap.add_argument("--keep-z2", action="store_true",
                     help="layer set: the variant without activation recompute (the forward keeps z2' for the "
                          "backward, N*m*2 bytes per matrix); the default recomputes it (POET-Xmem)")
@@ -109,18 +143,6 @@ def kernel_source_hash(files):
         with open(os.path.join(ROOT, "orthogonal_reparameterized_poetx_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
-
-
-def traffic_record(cls):
-    """HBM bytes per launch from a committed rocprofv3 counter record, if its
-    kernel source hash still matches the current source."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % cls)
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path))
-    if rec.get("source_hash") != kernel_source_hash(rec.get("source_files", [])):
-        return None
-    return rec
 
 
 def _find_csv(d, suffix):
@@ -168,8 +190,7 @@ def traffic_from(fetch_dir, write_dir):
             a[key] += v * 1024.0 * k
             a["dispatches_" + key] += 1
             a["kernels"].add(name.split("(")[0])
-    src_files = ["api.hip", "build.hip", "chain.hip", "transform.hip", "blockdiag.hip", "gemm.hip", "gram.hip",
-                 "merge.hip", "common.h", "kernels.h"]
+    src_files = SOURCE_FILES
     h = kernel_source_hash(src_files)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for cls, a in agg.items():
@@ -188,6 +209,63 @@ def traffic_from(fetch_dir, write_dir):
         print("%-18s %12.0f B/launch (fetch %.0f, write %.0f) over %d launches"
               % (cls, rec["hbm_bytes_per_launch"], rec["fetch_bytes_per_launch"], rec["write_bytes_per_launch"],
                  launches_f))
+
+
+def mfma_from(d):
+    """Per-class MFMA counters from one rocprofv3 --pmc run of MFMA_COUNTERS:
+    bf16 MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of
+    512 flops) and the MFMA pipes' busy fraction over the cycles the compute
+    units ran the kernel: (SQ_VALU_MFMA_BUSY_CYCLES / SIMD_COUNT) /
+    (SQ_BUSY_CU_CYCLES / CU_COUNT).  GRBM_GUI_ACTIVE is recorded but not used:
+    under counter collection it also counts the collection's own time around
+    each dispatch.  Writes profiles/mfma_<class>.json."""
+    import csv
+    per = {}
+    with open(_find_csv(d, "counter_collection.csv")) as fh:
+        for row in csv.DictReader(fh):
+            c = row.get("Counter_Name")
+            if c not in MFMA_COUNTERS:
+                continue
+            did = int(row["Dispatch_Id"])
+            e = per.setdefault(did, dict(name=row["Kernel_Name"]))
+            v = float(row["Counter_Value"])
+            e[c] = max(e.get(c, 0.0), v) if c == "GRBM_GUI_ACTIVE" else e.get(c, 0.0) + v
+    agg = {}
+    for e in per.values():
+        cls, k = kernel_class(e["name"])
+        if cls is None:
+            continue
+        a = agg.setdefault(cls, dict(mops=0.0, busy=0.0, cu=0.0, dispatches=0, per=k, kernels=set()))
+        a["mops"] += e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        a["busy"] += e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        a["cu"] += e.get("SQ_BUSY_CU_CYCLES", 0.0)
+        a["dispatches"] += 1
+        a["kernels"].add(e["name"].split("(")[0])
+    h = kernel_source_hash(SOURCE_FILES)
+    for cls, a in agg.items():
+        launches = a["dispatches"] / a["per"]
+        rec = dict(kernel_class=cls, source_hash=h, source_files=SOURCE_FILES, launches=launches,
+                   mfma_flops_per_launch=round(a["mops"] * 512 / launches),
+                   mfma_busy_frac=round((a["busy"] / SIMD_COUNT) / (a["cu"] / CU_COUNT), 4) if a["cu"] > 0 else None,
+                   cu_busy_cycles_per_launch=round(a["cu"] / CU_COUNT / launches),
+                   counters=list(MFMA_COUNTERS), kernels=sorted(a["kernels"]))
+        with open(os.path.join(ROOT, "profiles", "mfma_%s.json" % cls), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        print("%-18s %14.4g bf16 MFMA flops/launch, MFMA busy %s over %d launches"
+              % (cls, rec["mfma_flops_per_launch"], rec["mfma_busy_frac"], launches))
+
+
+def counter_record(kind, cls):
+    """A committed counter record (traffic or mfma) whose kernel-source hash
+    still matches the sources."""
+    path = os.path.join(ROOT, "profiles", "%s_%s.json" % (kind, cls))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash(rec.get("source_files", [])):
+        return None
+    return rec
 
 
 def _trace_window(path, steps):
@@ -275,9 +353,11 @@ class Stack:
             return torch.from_numpy(a.astype(np.float32)).to(dev)
 
         exact_owners = {WL.input_owner(cfg, j) for j in exact}
-        # matrices run on `streams` streams (matrix i on stream i % streams);
-        # each stream has its own workspace pool
+        # matrices run on `streams` streams (matrix i on stream where[i]);
+        # each stream has its own workspace pool, shared by the matrices that
+        # run on it one after another (never by two streams)
         self.nstreams = max(int(streams), 1)
+        self.where = balance_streams([(m, n) for _, _, m, n in mats], N, self.nstreams)
         pools = [{} for _ in range(self.nstreams)]
         self.layers, self.X, self.gY, self.out = [], {}, [], []
         mats_done = []
@@ -286,7 +366,7 @@ class Stack:
         for l, idx, m, n in mats:
             j = 7 * l + idx
             lay = P.PoetxLayer(m, n, b, "bf16", dev, perm_seed=WL.perm_seed(5, j),
-                               ws_pool=pools[len(mats_done) % self.nstreams], w0_int8=w0_int8)
+                               ws_pool=pools[self.where[len(mats_done)]], w0_int8=w0_int8)
             mats_done.append(j)
             kR, kP = m // b, n // b
             lay.thR = self.theta[off:off + kR * nt].view(kR, nt)
@@ -330,7 +410,7 @@ class Stack:
         for w in self.workers[1:]:
             w.wait_stream(main)
         for i, item in idx_items:
-            with self.torch.cuda.stream(self.workers[i % self.nstreams]):
+            with self.torch.cuda.stream(self.workers[self.where[i]]):
                 fn(*item)
         for w in self.workers[1:]:
             main.wait_stream(w)
@@ -343,10 +423,11 @@ class Stack:
             self.bwd_ready = torch.cuda.Event()
             self.workers = [main] + [torch.cuda.Stream() for _ in range(self.nstreams - 1)]
         # the backward blocks depend only on the generators: build them on a
-        # second stream while the forward pass runs (enqueued after the forward
-        # build, so that build gets the CUs first)
-        self.side.wait_stream(main)
+        # second stream while the forward pass runs.  That build starts once
+        # the forward build is done, so the two do not split the CUs while
+        # nothing else can run
         P.build_layer_blocks(self.layers, "forward")
+        self.side.wait_stream(main)
         with torch.cuda.stream(self.side):
             P.build_layer_blocks(self.layers, "backward")
             self.bwd_ready.record(self.side)
@@ -435,6 +516,9 @@ def main():
     if args.kernel_stats:
         kernel_stats(args.kernel_stats)
         return
+    if args.mfma_from:
+        mfma_from(args.mfma_from)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU). "
               "Run with --gpus 1.", file=sys.stderr)
@@ -453,7 +537,17 @@ def main():
         sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    cfg = WL.CONFIGS[3]
+    # (config number, matrix indices, block size) of the workload
+    if args.workload == "square":
+        c, mats, b_over = 2, [0], None
+    elif args.workload == "mlp7b":
+        c, mats, b_over = 4, [0], args.b or WL.CONFIGS[4]["b"]
+        if b_over not in WL.C4_BLOCK_SIZES:
+            print("--b must be one of %s" % (WL.C4_BLOCK_SIZES,), file=sys.stderr)
+            sys.exit(2)
+    else:
+        c, mats, b_over = 3, list(range(len(WL.CONFIGS[3]["mats"]))), None
+    cfg = WL.CONFIGS[c]
     N = args.tokens or cfg["N"]
 
     def up(pair, dt):
@@ -464,8 +558,8 @@ def main():
 
     # ---- resident inputs: seven packed layers, their inputs and upstream grads
     layers, Xs, gYs, outs = [], {}, [], []
-    for j in range(len(cfg["mats"])):
-        inp = WL.matrix_inputs(3, j, N=N)
+    for j in mats:
+        inp = WL.matrix_inputs(c, j, N=N, b=b_over)
         lay = P.PoetxLayer(inp["m"], inp["n"], inp["b"], "bf16", dev, perm_seed=inp["perm_seed"],
                            w0_int8=args.w0_int8)
         lay.pack(up(inp["W0"], "bf16"))
@@ -503,18 +597,20 @@ def main():
     side = torch.cuda.Stream()          # default priority
     bwd_blocks_ready = torch.cuda.Event()
     # the seven matrices are independent given their inputs: spread them over
-    # streams (all at the default priority) so one matrix's kernel tails and
-    # small launches overlap another's work
+    # streams (all at the default priority), balanced by estimated cost, so one
+    # matrix's kernel tails and small launches overlap another's work
     workers = [stream] + [torch.cuda.Stream() for _ in range(max(args.streams, 1) - 1)]
 
     active = {"workers": workers, "side": side}
+
+    where = {len(workers): balance_streams([(lay.m, lay.n) for lay in layers], N, len(workers)), 1: [0] * len(layers)}
 
     def fan_out(items, fn):
         ws = active["workers"]
         for w in ws[1:]:
             w.wait_stream(stream)
-        for i, item in enumerate(items):
-            with torch.cuda.stream(ws[i % len(ws)]):
+        for item in items:
+            with torch.cuda.stream(ws[where[len(ws)][layers.index(item[0])]]):
                 fn(*item)
         for w in ws[1:]:
             stream.wait_stream(w)
@@ -527,10 +623,11 @@ def main():
         # after their dL/dQ (--chain batched) or per matrix on its stream
         # right after its dL/dQ (--chain per-matrix)
         bs = active["side"]
-        bs.wait_stream(stream)
-        # the forward build is enqueued first, so its workgroups take the CUs
-        # before the backward build's
+        # the backward build waits for the forward build, so the two do not
+        # split the CUs while nothing else can run; it then overlaps the
+        # forward pass
         P.build_layer_blocks(layers, "forward")
+        bs.wait_stream(stream)
         with torch.cuda.stream(bs):
             P.build_layer_blocks(layers, "backward")
             bwd_blocks_ready.record(bs)
@@ -599,8 +696,58 @@ def main():
                     frac=round(achieved / PEAK_HBM_GBS, 4))
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(d["ms"] / max(d["launches"], 1), 4)
-    rec = traffic_record(dom)
+    rec = counter_record("traffic", dom)
     roof["traffic"] = None if rec is None else rec["hbm_bytes_per_launch"]
+    # every class against its own roofline (kernel level: the bytes or flops
+    # each launch must move or compute, over its event-timed duration)
+    classes = {}
+    for k, v in per_step.items():
+        if v["ms"] <= 0:
+            continue
+        if k in MFMA_CLASSES and v["flops"] > 0:
+            a = v["flops"] / (v["ms"] * 1e-3) / 1e12
+            classes[k] = dict(bound="mfma", achieved=round(a, 1), peak=MFMA_CLASSES[k], unit="TFLOP/s",
+                              frac=round(a / MFMA_CLASSES[k], 4))
+        elif k in HBM_CLASSES and v["bytes"] > 0:
+            a = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+            classes[k] = dict(bound="hbm", achieved=round(a, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(a / PEAK_HBM_GBS, 4))
+    # method level: the block transforms' algorithmic bytes per step (per token
+    # and matrix: forward 4(n+m), backward 6(m+n), recompute 4n, bf16) over the
+    # time of every transform kernel (permutations, block products, Gram
+    # products) in the serialized pass
+    shapes = [(cfg["mats"][j % len(cfg["mats"])][1], cfg["mats"][j % len(cfg["mats"])][2]) for j in mats]
+    algo = N * sum(10 * (m + n) + 4 * n for m, n in shapes)
+    xms = sum(per_step[k]["ms"] for k in HBM_CLASSES if k in per_step)
+    transforms = dict(algorithmic_bytes=algo, ms=round(xms, 4),
+                      achieved=round(algo / (xms * 1e-3) / 1e9, 1) if xms > 0 else None, peak=PEAK_HBM_GBS,
+                      unit="GB/s", frac=round(algo / (xms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if xms > 0 else None,
+                      classes=[k for k in HBM_CLASSES if k in per_step])
+    gms = sum(per_step[k]["ms"] for k in ("gemm_nt", "gemm_nn") if k in per_step)
+    gfl = sum(per_step[k]["flops"] for k in ("gemm_nt", "gemm_nn") if k in per_step)
+    gemms = dict(flops=gfl, ms=round(gms, 4), achieved=round(gfl / (gms * 1e-3) / 1e12, 1) if gms > 0 else None,
+                 peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                 frac=round(gfl / (gms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if gms > 0 else None)
+    # the same fractions from rocprofv3 counters (records under profiles/ taken
+    # on the layer set with the current sources): bf16 MFMA flops the
+    # hardware counted, and HBM bytes (FETCH_SIZE + WRITE_SIZE), per launch,
+    # over the event-timed launch duration of this run
+    counters = {}
+    for k, v in per_step.items():
+        if v["launches"] <= 0 or v["ms"] <= 0:
+            continue
+        avg_s = v["ms"] / v["launches"] * 1e-3
+        mf = counter_record("mfma", k) if k in ("gemm_nt", "gemm_nn") else None
+        if mf:
+            a = mf["mfma_flops_per_launch"] / avg_s / 1e12
+            counters[k] = dict(bound="mfma", achieved=round(a, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                               frac=round(a / PEAK_BF16_TFLOPS, 4), mfma_busy=mf["mfma_busy_frac"],
+                               clock_ghz=round(mf["cu_busy_cycles_per_launch"] / avg_s / 1e9, 3))
+        tr = counter_record("traffic", k) if k in HBM_CLASSES else None
+        if tr:
+            a = tr["hbm_bytes_per_launch"] / avg_s / 1e9
+            counters[k] = dict(bound="hbm", achieved=round(a, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                               frac=round(a / PEAK_HBM_GBS, 4))
     breakdown = {}
     for k, v in sorted(per_step.items(), key=lambda kv: -kv[1]["ms"]):
         e = dict(ms=round(v["ms"], 4), launches=round(v["launches"], 2))
@@ -634,19 +781,24 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded Gaussian inputs with the layer set's shapes)",
-        "config": {"workload": cfg["name"], "tokens": N, "matrices": len(cfg["mats"]), "b": cfg["b"],
-                   "shapes": ["%dx%d" % (m, n) for _, m, n in cfg["mats"]],
+        "data": "synthetic (seeded Gaussian inputs with the workload's shapes)",
+        "config": {"workload": cfg["name"] if b_over is None else "%s_b%d" % (cfg["name"], b_over),
+                   "tokens": N, "matrices": len(mats), "b": b_over or cfg["b"],
+                   "shapes": ["%dx%d" % s for s in shapes],
                    "block_builds": "per layer call" if args.per_layer_builds else
-                   "batched per pass (Cayley builds and chain rule over all seven matrices)",
+                   "batched per pass (Cayley builds and chain rule over all matrices)",
                    "streams": 1 if args.per_layer_builds else max(args.streams, 1),
                    "activations": "z2' kept from the forward pass (no recompute)" if args.keep_z2 else
                    "recomputed in the backward pass (POET-Xmem)",
-                   "base_weights": "INT8 codes with per-row fp32 scales, dequantized per pass (POET-XQ)"
-                   if args.w0_int8 else "bf16"},
+                   "base_weights": "INT8 codes with per-row fp32 scales, dequantized inside the GEMMs "
+                   "(POET-XQ)" if args.w0_int8 else "bf16"},
         "roofline": roof,
+        "roofline_classes": classes,
+        "roofline_gemms": gemms,
+        "roofline_transforms": transforms,
+        "roofline_counters": counters if args.workload == "layerset" else None,
         "kernels_per_step": breakdown,
-        "merge_ms_layer_set": round(merge_ms, 3),
+        "merge_ms": round(merge_ms, 3),
     }
 
     if args.calibrate_copy:
@@ -659,11 +811,24 @@ def main():
 
     # ---- float64 oracle on the host cores, bounded token sample
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        ntok = args.cpu_tokens or {"square": 4096, "mlp7b": 2048}.get(args.workload, 3072)
+        result["cpu_baseline"] = cpu_baseline(c, mats, b_over, ntok)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(ntok):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(c, mats, b_over, ntok):
+    """The float64 oracle (bf16 contract mode) on the host cores: forward and
+    backward of the workload's matrices on its first ntok tokens."""
     import numpy as np
 
     import oracle
@@ -672,13 +837,14 @@ def cpu_baseline(ntok):
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
-    cfg = WL.CONFIGS[3]
+        threads = None
+    cfg = WL.CONFIGS[c]
+    ntok = min(ntok, cfg["N"])
     rows = np.arange(ntok)
     # time only the oracle calls (input generation excluded)
     tot = 0.0
-    for j in range(len(cfg["mats"])):
-        inp = WL.matrix_inputs(3, j, rows=rows)
+    for j in mats:
+        inp = WL.matrix_inputs(c, j, rows=rows, b=b_over)
         s = oracle.make_permutation(inp["perm_seed"], 0, 0, inp["m"])
         t = oracle.make_permutation(inp["perm_seed"], 0, 1, inp["n"])
         a = (inp["W0"][1], inp["thR"][1], inp["thP"][1], s, t, inp["X"][1])
@@ -686,9 +852,11 @@ def cpu_baseline(ntok):
         oracle.forward(*a, inp["b"], contract=True)
         oracle.backward(*a, inp["gY"][1], inp["b"], contract=True)
         tot += time.perf_counter() - ts
-    return {"value": round(ntok / tot, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": "float64 oracle (bf16 contract mode), fwd+bwd of all 7 layer-set matrices on the first %d "
-                      "of the 8192 tokens; %.1f s; per-step block builds and chain rule included once" % (ntok, tot)}
+    return {"value": round(ntok / tot, 2), "unit": "tokens/s", "cores": int(threads or os.cpu_count() or 1),
+            "kind": "oracle", "cpu_count": os.cpu_count(), "blas_threads": threads, "cpu_model": cpu_model(),
+            "sample": "float64 oracle (bf16 contract mode), fwd+bwd of the %d matrices of %s on the first %d of the "
+                      "%d tokens; %.1f s; block builds and chain rule included once"
+                      % (len(mats), cfg["name"], ntok, cfg["N"], tot)}
 
 
 if __name__ == "__main__":

@@ -96,3 +96,40 @@ def test_trace_window_keeps_the_marked_pass(tmp_path):
             w.writerow(dict(Kernel_Name=name, Start_Timestamp=t0, End_Timestamp=t1))
     got = {r["Name"]: (int(r["Calls"]), float(r["TotalDurationNs"])) for r in bench._trace_window(path, None)}
     assert got == {"void poetx::gemm_wide_kernel<false>": (2, 200.0), "poetx::gram_reduce_kernel": (1, 10.0)}
+
+
+def test_mfma_summary_from_counters(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda files: "feedbeef")
+    os.makedirs(tmp_path / "profiles")
+    nt = "void poetx::gemm_wide_kernel<false>(poetx::GemmArgs, int, int, int)"
+    rows = []
+    # two launches; MOPS and busy cycles arrive per SE and are summed, GUI_ACTIVE per XCD (max)
+    for did, mops, busy in ((1, 1000.0, 2.0e5), (2, 3000.0, 6.0e5)):
+        rows += [(did, nt, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops / 2), (did, nt, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops / 2),
+                 (did, nt, "SQ_VALU_MFMA_BUSY_CYCLES", busy), (did, nt, "GRBM_GUI_ACTIVE", 1.0e6),
+                 (did, nt, "SQ_BUSY_CU_CYCLES", 256 * 1000.0)]
+    _write_pmc(str(tmp_path / "m"), rows)
+    bench.mfma_from(str(tmp_path / "m"))
+    rec = json.load(open(tmp_path / "profiles" / "mfma_gemm_nt.json"))
+    assert rec["launches"] == 2 and rec["source_hash"] == "feedbeef"
+    assert rec["mfma_flops_per_launch"] == (1000 + 3000) * 512 / 2
+    # busy cycles per SIMD over busy cycles per compute unit
+    assert rec["mfma_busy_frac"] == round(((2.0e5 + 6.0e5) / bench.SIMD_COUNT) / (2 * 1000.0), 4)
+    assert rec["cu_busy_cycles_per_launch"] == 1000
+
+
+def test_balance_streams_places_every_matrix_once():
+    # the layer set: q, k, v, o, gate, up, down at 8192 tokens over 3 streams
+    shapes = [(2048, 2048), (256, 2048), (256, 2048), (2048, 2048), (5632, 2048), (5632, 2048), (2048, 5632)]
+    where = bench.balance_streams(shapes, 8192, 3)
+    assert len(where) == len(shapes) and set(where) <= {0, 1, 2}
+    # the three MLP matrices (largest) each go to a stream of their own
+    assert len({where[4], where[5], where[6]}) == 3
+    assert bench.balance_streams(shapes, 8192, 1) == [0] * len(shapes)
+    # the 24-layer stack: the same shapes 24 times; loads within one matrix of each other
+    stack = shapes * 24
+    w24 = bench.balance_streams(stack, 8192, 3)
+    cost = [6.0 * 8192 * m * n / 1.1e15 + (28.0 * n + 20.0 * m) * 8192 / 3.5e12 for m, n in stack]
+    load = [sum(c for c, w in zip(cost, w24) if w == s) for s in range(3)]
+    assert max(load) - min(load) <= max(cost)
