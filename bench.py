@@ -42,7 +42,7 @@ SIMD_COUNT = 1024   # 256 compute units x 4 SIMDs
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")
 # HBM-bound classes of the block transforms (permutations, block products,
 # Gram products)
-HBM_CLASSES = ("xform_permute", "xform_blockmul", "gram")
+HBM_CLASSES = ("xform_permute", "xform_blockmul", "xform_gather", "gram")
 
 # kernel name (demangled, as rocprofv3 prints it) -> timing class of the library,
 # and the dispatches one timed launch of the class makes
@@ -50,6 +50,7 @@ KERNEL_CLASSES = [
     ("permute_gather_kernel", "xform_permute", 1),
     ("permute_scatter_kernel", "xform_permute", 1),
     ("permute_stream_kernel", "xform_permute", 1),
+    ("gather_blockdiag_kernel", "xform_gather", 1),    # before its substring below
     ("blockdiag_kernel", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, true,", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, false,", "gemm_nt", 1),

@@ -556,6 +556,27 @@ int blockmul(const void* in, const uint16_t* q, void* out, int64_t N, int W, int
   return check_launch("block product");
 }
 
+// gather-in transform z = D (Pi in) over all W = k b columns, with x' = Pi in
+// also written to emit (nullable) for a later Gram product: one fused pass
+// where the kernel applies and measured faster (b = 256, no identity tail, up
+// to 6 blocks per row), else the permutation into sc (emit, if given) and the
+// block product.
+int gather_blockmul(const void* in, const int32_t* perm, const uint16_t* q, void* sc, void* out, void* emit,
+                    int64_t N, int W, int b, int k, size_t es, hipStream_t s) {
+  if (gather_blockdiag_applies(in, perm, q, out, emit, N, W, b, k, W, W, W)) {
+    {
+      Tm tm(s, "xform_gather", xf_flops(N, k, b), (emit ? 6.0 : 4.0) * N * W);
+      launch_gather_blockdiag_bf16(static_cast<const uint16_t*>(in), perm, q, static_cast<uint16_t*>(out),
+                                   static_cast<uint16_t*>(emit), N, W, b, k, W, W, W, s);
+    }
+    return check_launch("gather and block product");
+  }
+  void* xg = emit ? emit : sc;
+  int rc;
+  if ((rc = permute(true, in, nullptr, xg, out, perm, N, W, k * b, es, s))) return rc;
+  return blockmul(xg, q, out, N, W, b, k, s);
+}
+
 // forward after the blocks exist: a3, a4, a5
 // z2out non-null (bf16): z2' goes there instead of the workspace (kept for
 // the backward pass)
@@ -585,8 +606,7 @@ int fwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
     return check_launch("fp32 forward");
   }
   // z1' = D_P x' with x' = Pi_tau x (the identity tail of x' goes straight to z1')
-  if ((rc = permute(true, X, nullptr, w.sc, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
-  if ((rc = blockmul(w.sc, q.qbP, w.z1, N, n, S.b, S.kP, s))) return rc;
+  if ((rc = gather_blockmul(X, tau, q.qbP, w.sc, w.z1, nullptr, N, n, S.b, S.kP, S.es, s))) return rc;
   // z2' = z1' W0p^T
   void* const z2 = z2out ? z2out : w.z2;
   {
@@ -634,16 +654,16 @@ int bwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
     }
   } else {
     // recompute x' = Pi_tau x (kept for dL/dQ_P), z1' = D_P x', z2' = z1' W0p^T
-    if ((rc = permute(true, X, nullptr, w.xg, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
-    if (!z2in) {
-      if ((rc = blockmul(w.xg, q.qbP, w.z1, N, n, S.b, S.kP, s))) return rc;
+    if (z2in) {
+      if ((rc = permute(true, X, nullptr, w.xg, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
+    } else {
+      if ((rc = gather_blockmul(X, tau, q.qbP, nullptr, w.z1, w.xg, N, n, S.b, S.kP, S.es, s))) return rc;
       Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
       if ((rc = weight_gemm(false, (const uint16_t*)w.z1, W0, (uint16_t*)w.z2, N, S.m, S.n, s))) return rc;
     }
     if ((rc = check_launch("recompute"))) return rc;
     // R side: gY' = Pi_sigma gY (kept), gz2' = D_R^T gY' (blocks Q_R^T)
-    if ((rc = permute(true, dY, nullptr, w.gyg, w.gz2, sigma, N, m, S.kR * S.b, S.es, s))) return rc;
-    if ((rc = blockmul(w.gyg, q.qtR, w.gz2, N, m, S.b, S.kR, s))) return rc;
+    if ((rc = gather_blockmul(dY, sigma, q.qtR, nullptr, w.gz2, w.gyg, N, m, S.b, S.kR, S.es, s))) return rc;
   }
   // G_R = gY'^T z2' per block
   {

@@ -327,4 +327,299 @@ bool launch_blockdiag_bf16(const uint16_t* in, const uint16_t* q, uint16_t* out,
 }
 
 
+// ---------------------------------------------------------------------------
+// Row gather and block product in one pass (the gather-in side: P forward,
+// its recompute, R backward), b = 256 and rows of at most 2048 columns:
+//   out[t][l*256 + i] = sum_kk q[l][i][kk] * in[t][perm[l*256 + kk]]   (l < k)
+//   emit[t][l*256 + kk] = in[t][perm[l*256 + kk]]                      (optional)
+// One workgroup per (block l, token run), the block in VGPRs as in
+// blockdiag_kernel.  The gather needs b columns spread over the whole row, so
+// the run's tiles of 16 whole token rows are loaded (contiguous 16-byte loads
+// into registers, three tiles ahead) and written to one of two LDS stages,
+// and the block's columns are picked from there through the permutation into
+// a contiguous 16 x 256 tile that the MFMAs (16x16x32) read.  Every block of a
+// run reads the same rows: the k workgroups of a run sit on one XCD
+// (blockIdx mod 8), so the rows come from HBM once and from L2 for the
+// others, and each workgroup touches the rows of the tile GB_PF beyond its
+// loads with one 4-byte load per 128-byte line, so that they are in L2 when
+// loaded.  Against a permutation pass and a block-product pass, the permuted
+// rows are neither written nor read back (with emit they are written once,
+// for a later Gram product).  Each tile costs about 2 us whatever the width,
+// so with 8 blocks per row the two streaming passes are faster; the kernel is
+// used up to 6 blocks per row.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int GB_T = 16;                 // tokens per tile
+constexpr int GB_B = 256;                // block size
+constexpr int GB_MAXW = 2048;            // widest row the kernel takes (16 rows fill a 64 KiB stage)
+constexpr int GB_MAXK = 6;               // widest row it is used for: 6 blocks (see gather_blockdiag_applies)
+constexpr int GB_PF = 3;                 // tiles of L2 prefetch ahead of staging
+
+__device__ __forceinline__ void b2l4(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void b2l16s(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+}
+// eight 2-byte LDS reads at independent addresses, packed in pairs (the first
+// of a pair in the low half)
+__device__ __forceinline__ u32x4 lds_gather8(const uint32_t (&a)[8]) {
+  uint32_t v[8];
+  asm volatile(
+      "ds_read_u16 %0, %8\n\tds_read_u16 %1, %9\n\tds_read_u16 %2, %10\n\tds_read_u16 %3, %11\n\t"
+      "ds_read_u16 %4, %12\n\tds_read_u16 %5, %13\n\tds_read_u16 %6, %14\n\tds_read_u16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+  return u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+}
+__device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ u32x4 lds_read16(uint32_t a) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+}  // namespace
+
+// NOPS = W / 256: 16-byte row loads per thread per tile
+template <bool EMIT, int NOPS>
+__global__ __launch_bounds__(512) void gather_blockdiag_kernel(GatherBdArgs a) {
+  // the two row stages, each named at compile time (see blockdiag_kernel)
+  __shared__ __align__(16) uint16_t R0[GB_T * GB_MAXW], R1[GB_T * GB_MAXW];
+  __shared__ __align__(16) uint16_t XT[GB_T * GB_B], OT[GB_T * GB_B];
+  __shared__ __align__(16) uint32_t PD[512];   // sink of the prefetch loads (never read)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k = a.k, W = a.W;
+  // workgroup g runs on XCD g % 8; the k blocks of a run share an XCD
+  const int g = blockIdx.x, j = g >> 3;
+  const int l = j % k, run = (g & 7) + 8 * (j / k);
+  if (run >= a.runs) return;
+  const int64_t t0 = (int64_t)run * a.tpr * GB_T;
+  if (t0 >= a.N) return;
+  const int rows = (int)min((int64_t)a.tpr * GB_T, a.N - t0);
+  const int nt = (rows + GB_T - 1) / GB_T;
+
+  // ---- q[l] -> LDS (rows 0..127 in R0, 128..255 in R1; 16-byte chunk c of
+  // row r at c ^ (r & 15)), then wave w takes rows 32 w .. 32 w + 31 as
+  // 16x16x32 A fragments: qf[mt][ks] = rows 32 w + 16 mt + lane % 16,
+  // k = 32 ks + 8 (lane / 16) .. + 7
+  bf16x8 qf[2][8];
+  {
+    const __amdgpu_buffer_rsrc_t rq = rsrc(a.q + (int64_t)l * GB_B * GB_B, 2u * GB_B * GB_B);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int slot = c * 512 + tid, r = slot >> 5, p = slot & 31;
+      uint16_t* dst = (c < 8 ? R0 : R1) + ((c & 7) * 512 + wave * 64) * 8;
+      b2l16s(rq, (r * GB_B + ((p ^ (r & 15)) << 3)) * 2, 0, dst);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+    lds_barrier();
+    const int r0 = 32 * wave + (lane & 15);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int r = r0 + 16 * mt;
+      const uint16_t* base = (r < 128 ? R0 : R1) + (r & 127) * GB_B;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qf[mt][ks] = *reinterpret_cast<const bf16x8*>(base + (((4 * ks + (lane >> 4)) ^ (lane & 15)) << 3));
+    }
+    lds_barrier();   // the stages are free
+  }
+
+  // ---- this thread's gather: token row t = tid / 32 of a tile, block columns
+  // kk = 8 kg .. 8 kg + 7 (kg = tid % 32), from row columns perm[l*256 + kk]
+  const int gt = tid >> 5, kg = tid & 31;
+  uint32_t gof[8];
+  {
+    const int4* pp = reinterpret_cast<const int4*>(a.perm + (int64_t)l * GB_B + 8 * kg);
+    const int4 p0 = pp[0], p1 = pp[1];
+    const int pc[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gof[e] = (uint32_t)(gt * W + pc[e]) * 2u;
+  }
+  const uint32_t xw = lds_addr(XT) + (uint32_t)(gt * 512 + ((kg ^ (gt & 15)) << 4));
+  // fragment reads of the x' tile: token lane % 16, chunk 4 ks + lane / 16
+  uint32_t xra[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    xra[ks] = lds_addr(XT) + (uint32_t)((lane & 15) * 512 + (((4 * ks + (lane >> 4)) ^ (lane & 15)) << 4));
+  // output staging: lane writes out[token lane % 16][32 w + 16 mt + 4 (lane / 16) .. + 3]
+  uint32_t ow[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int c = 4 * wave + 2 * mt + (lane >> 5), h = (lane >> 4) & 1;
+    ow[mt] = lds_addr(OT) + (uint32_t)((lane & 15) * 512 + ((c ^ (lane & 15)) << 4) + (h << 3));
+  }
+  const uint32_t orr = lds_addr(OT) + (uint32_t)(gt * 512 + ((kg ^ (gt & 15)) << 4));
+
+  // ---- global ranges and per-lane offsets
+  const BufRange gin = tile_range(t0, rows, 0, W, a.lda, 2);
+  const __amdgpu_buffer_rsrc_t rin = rsrc(a.in + gin.first, (uint32_t)gin.bytes);
+  const BufRange gout = tile_range(t0, rows, (int64_t)l * GB_B, GB_B, a.ldc, 2);
+  const __amdgpu_buffer_rsrc_t rout = rsrc(a.out + gout.first, (uint32_t)gout.bytes);
+  __amdgpu_buffer_rsrc_t remit = rout;
+  if constexpr (EMIT) {
+    const BufRange ge = tile_range(t0, rows, (int64_t)l * GB_B, GB_B, a.lde, 2);
+    remit = rsrc(a.emit + ge.first, (uint32_t)ge.bytes);
+  }
+  const int cpr = W >> 3;                  // 16-byte chunks per row
+  int voff[NOPS];
+#pragma unroll
+  for (int op = 0; op < NOPS; ++op) {
+    const int c = op * 512 + tid, r = c / cpr, p = c - r * cpr;
+    voff[op] = (int)((uint32_t)r * (uint32_t)a.lda * 2u + (uint32_t)(p << 4));
+  }
+  // prefetch: lane tid touches 128-byte line tid of the tile's rows (lines past
+  // the tile repeat its last one)
+  int pvoff;
+  {
+    const int lpr = W >> 6, lines = GB_T * lpr;
+    const int L = tid < lines ? tid : lines - 1, r = L / lpr;
+    pvoff = (int)((uint32_t)r * (uint32_t)a.lda * 2u + (uint32_t)((L - r * lpr) << 7));
+  }
+  const uint32_t tin = (uint32_t)GB_T * (uint32_t)a.lda * 2u;
+  const int soutv = gt * (int)a.ldc * 2 + kg * 16;
+  const int semit = EMIT ? gt * (int)a.lde * 2 + kg * 16 : 0;
+  const uint32_t tout = (uint32_t)GB_T * (uint32_t)a.ldc * 2u, temit = EMIT ? (uint32_t)GB_T * (uint32_t)a.lde * 2u : 0u;
+
+  // tile rows travel through registers: tile j is loaded into register set
+  // j % 2 three steps ahead, written to LDS stage j % 2 one step ahead, and
+  // gathered in step j, so two tiles are in flight from memory while one is
+  // gathered (the LDS alone holds only two tiles of 2048-column rows)
+  typedef u32x4 RowSet[NOPS];
+  RowSet V0, V1;
+  auto vload = [&](int i, RowSet& v) {
+#pragma unroll
+    for (int op = 0; op < NOPS; ++op)
+      v[op] = __builtin_amdgcn_raw_buffer_load_b128(rin, voff[op], (int)((uint32_t)i * tin), 0);
+  };
+  const uint32_t vsl = (uint32_t)tid * 16u;
+  auto vstore = [&](const RowSet& v, uint16_t* st) {
+    const uint32_t sb = lds_addr(st) + vsl;
+#pragma unroll
+    for (int op = 0; op < NOPS; ++op) lds_write16(sb + (uint32_t)op * 8192u, v[op]);
+  };
+  auto prefetch = [&](int i) { b2l4(rin, pvoff, (int)((uint32_t)i * tin), PD + wave * 64); };
+
+  // prologue: tiles 0..2 into registers (tile 0 on to stage 0), L2 prefetch
+  // of tiles 3 .. 2 + GB_PF
+  vload(0, V0);
+  vload(1, V1);
+#pragma unroll
+  for (int i = 3; i < 3 + GB_PF; ++i) prefetch(i);
+  vstore(V0, R0);
+  vload(2, V0);
+
+  // step i: tile i in stage cur; register set vn holds tile i + 1
+  auto step = [&](int i, const uint16_t* cur, uint16_t* nxt, RowSet& vn) {
+    lds_barrier();                      // tile i staged; x' and output tiles free
+    prefetch(i + 3 + GB_PF);            // past the run: reads nothing
+    uint32_t ad[8];
+    const uint32_t cb = lds_addr(cur);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ad[e] = cb + gof[e];
+    const u32x4 xv = lds_gather8(ad);
+    lds_write16(xw, xv);
+    if constexpr (EMIT)
+      __builtin_amdgcn_raw_buffer_store_b128(xv, remit, semit + (int)((uint32_t)i * temit), 0, 0);
+    vstore(vn, nxt);                    // tile i + 1; stage nxt held tile i - 1, gathered before the barrier
+    vload(i + 3, vn);
+    lds_barrier();                      // x' tile complete
+    // the eight k steps' fragments in one block of reads (one LDS round trip)
+    i32x4 xf[8];
+    lds_read8(xf, xra);
+    f32x4 acc[2] = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      acc[0] = mfma16(qf[0][ks], __builtin_bit_cast(bf16x8, xf[ks]), acc[0]);
+      acc[1] = mfma16(qf[1][ks], __builtin_bit_cast(bf16x8, xf[ks]), acc[1]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      lds_write8b(ow[mt], uint2{pk_bf16(acc[mt][0], acc[mt][1]), pk_bf16(acc[mt][2], acc[mt][3])});
+    lds_barrier();                      // output tile complete
+    const u32x4 ov = lds_read16(orr);
+    bst16(ov, rout, soutv + (int)((uint32_t)i * tout));
+  };
+  int i = 0;
+  for (; i + 2 <= nt; i += 2) {
+    step(i, R0, R1, V1);
+    step(i + 1, R1, R0, V0);
+  }
+  if (i < nt) step(i, R0, R1, V1);
+  // prefetches past the run may still be writing LDS
+  __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+}
+
+// Launch plan: runs of whole 16-token tiles, about 256 workgroups, at least 4
+// tiles per run.  The launch returns false (nothing launched) where the
+// kernel does not apply: b != 256, W = k b above 2048, unaligned rows or
+// operands, offsets past 32 bits.
+namespace {
+struct GbPlan { int64_t runs, tpr; };
+GbPlan gather_blockdiag_plan(int64_t N, int k) {
+  const int64_t ntiles = (N + GB_T - 1) / GB_T;
+  int64_t runs = 256 / k;
+  if (runs > ntiles / 4) runs = ntiles / 4;
+  runs = runs / 8 * 8;
+  if (runs < 8) runs = 8;
+  if (runs > ntiles) runs = ntiles;
+  const int64_t tpr = (ntiles + runs - 1) / runs;
+  return GbPlan{(ntiles + tpr - 1) / tpr, tpr};
+}
+}  // namespace
+
+bool gather_blockdiag_applies(const void* in, const int32_t* perm, const void* q, const void* out, const void* emit,
+                              int64_t N, int W, int b, int k, int64_t lda, int64_t ldc, int64_t lde) {
+  // measured against the permutation + block-product passes (8192 tokens):
+  // 7.1 vs 11.2 us at 256 columns, 15.0 vs 24.8 at 1024, 23.4 vs 26.7 at
+  // 1536, 32.3 vs 30.5 at 2048; so up to 6 blocks per row
+  if (b != GB_B || k <= 0 || k > GB_MAXK || W != k * GB_B || N <= 0) return false;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if ((lda & 7) || (ldc & 7) || (emit && (lde & 7)) || !al16(in) || !al16(out) || !al16(q) || (emit && !al16(emit)) ||
+      !al16(perm))
+    return false;
+  // every per-lane offset, with the row loads and prefetches up to GB_PF + 3
+  // tiles past a run, below 2^31
+  const GbPlan p = gather_blockdiag_plan(N, k);
+  const int64_t ld = std::max(lda, std::max(ldc, emit ? lde : (int64_t)0));
+  return (p.tpr + GB_PF + 4) * GB_T * ld * 2 < 0x7fffffffLL;
+}
+
+bool launch_gather_blockdiag_bf16(const uint16_t* in, const int32_t* perm, const uint16_t* q, uint16_t* out,
+                                  uint16_t* emit, int64_t N, int W, int b, int k, int64_t lda, int64_t ldc,
+                                  int64_t lde, hipStream_t s) {
+  if (!gather_blockdiag_applies(in, perm, q, out, emit, N, W, b, k, lda, ldc, lde)) return false;
+  const GbPlan p = gather_blockdiag_plan(N, k);
+  const int64_t runs = p.runs, tpr = p.tpr;
+  GatherBdArgs a{};
+  a.in = in; a.perm = perm; a.q = q; a.out = out; a.emit = emit;
+  a.N = N; a.W = W; a.k = k; a.runs = (int)runs; a.tpr = (int)tpr;
+  a.lda = lda; a.ldc = ldc; a.lde = lde;
+  const int64_t grid = 8 * (int64_t)k * ((runs + 7) / 8);
+  auto go = [&](auto em, auto nops) {
+    hipLaunchKernelGGL((gather_blockdiag_kernel<decltype(em)::value, decltype(nops)::value>), dim3((unsigned)grid),
+                       dim3(512), 0, s, a);
+  };
+  auto by_k = [&](auto em) {
+    switch (k) {
+      case 1: go(em, std::integral_constant<int, 1>{}); break;
+      case 2: go(em, std::integral_constant<int, 2>{}); break;
+      case 3: go(em, std::integral_constant<int, 3>{}); break;
+      case 4: go(em, std::integral_constant<int, 4>{}); break;
+      case 5: go(em, std::integral_constant<int, 5>{}); break;
+      case 6: go(em, std::integral_constant<int, 6>{}); break;
+      case 7: go(em, std::integral_constant<int, 7>{}); break;
+      default: go(em, std::integral_constant<int, 8>{}); break;
+    }
+  };
+  if (emit) by_k(std::true_type{});
+  else by_k(std::false_type{});
+  return true;
+}
+
 }  // namespace poetx

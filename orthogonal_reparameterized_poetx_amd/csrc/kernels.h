@@ -111,6 +111,25 @@ void launch_scatter_out_f32(const XformArgs& a, hipStream_t s);
 bool launch_blockdiag_bf16(const uint16_t* in, const uint16_t* q, uint16_t* out, int64_t N, int64_t lda,
                            int64_t ldc, int b, int k, hipStream_t s);
 
+// gather and block product in one pass (blockdiag.hip):
+//   out[t][l*b + i] = sum_kk q[l][i][kk] in[t][perm[l*b + kk]], l < k, W = k b
+//   emit (nullable) [t][l*b + kk] = in[t][perm[l*b + kk]]
+// false (nothing launched) where it does not apply (b != 256, W > 2048, ...)
+struct GatherBdArgs {
+  const uint16_t* in;
+  const int32_t* perm;
+  const uint16_t* q;
+  uint16_t* out;
+  uint16_t* emit;
+  int64_t N;
+  int W, k, runs, tpr;
+  int64_t lda, ldc, lde;
+};
+bool gather_blockdiag_applies(const void* in, const int32_t* perm, const void* q, const void* out, const void* emit,
+                              int64_t N, int W, int b, int k, int64_t lda, int64_t ldc, int64_t lde);
+bool launch_gather_blockdiag_bf16(const uint16_t* in, const int32_t* perm, const uint16_t* q, uint16_t* out,
+                                  uint16_t* emit, int64_t N, int W, int b, int k, int64_t lda, int64_t ldc,
+                                  int64_t lde, hipStream_t s);
 
 // ---- dense GEMMs (gemm.hip): C[M][N] = A[M][K] * op(B)
 // nt: B is [N][K] (C = A B^T); nn: B is [K][N] (C = A B)
