@@ -85,6 +85,29 @@ def balance_streams(shapes, N, nstreams):
     return where
 
 
+def dominant_roofline(per_step):
+    """roofline of the class with the most time in a serialized pass: achieved
+    algorithmic flops (MFMA classes) or bytes over its event-timed duration,
+    against the MI355X peak, with the HBM bytes per launch from the committed
+    counter record (null if none for the current sources)."""
+    dom = max(per_step, key=lambda k: per_step[k]["ms"])
+    d = per_step[dom]
+    if dom in MFMA_CLASSES:
+        achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
+        peak = MFMA_CLASSES[dom]
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4))
+    else:
+        achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = round(d["ms"] / max(d["launches"], 1), 4)
+    rec = counter_record("traffic", dom)
+    roof["traffic"] = None if rec is None else rec["hbm_bytes_per_launch"]
+    return roof
+
+
 def kernel_class(name):
     for key, cls, per in KERNEL_CLASSES:
         if key in name:
@@ -489,6 +512,24 @@ def bench_stack(args):
         mg += ev[2].elapsed_time(ev[3])
     k = args.steps
     ms = (fb + ad + mg) / k
+    # per-kernel pass: one step with every matrix on the main stream, HIP
+    # events around each launch
+    saved = (st.workers, st.side)
+    st.workers, st.side = [stream] * st.nstreams, stream
+    P.timing_enable(True)
+    st.step()
+    torch.cuda.synchronize()
+    kern = P.timing_summary()
+    P.timing_enable(False)
+    st.workers, st.side = saved
+    per_step = {c: dict(v) for c, v in kern.items()}
+    roof = dominant_roofline(per_step)
+    cpu = None
+    if not args.no_cpu:
+        # one layer's seven matrices on the oracle; a stack step runs 24 layers
+        cpu = cpu_baseline(5, list(range(7)), None, args.cpu_tokens or 1024)
+        cpu["value"] = round(cpu["value"] / 24, 3)
+        cpu["sample"] += "; the rate is that sample's tokens/s over 24 layers (Adam and merge not included)"
     print(json.dumps({
         "metric": "POET-X 24-layer stack training step (fwd+bwd, Adam, global merge), 1 GPU",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": k, "warmup": args.warmup,
@@ -500,6 +541,10 @@ def bench_stack(args):
         "generators": st.theta.numel(),
         "resident_gb": round(resident / 1e9, 3),
         "peak_hbm_gb": round(torch.cuda.max_memory_allocated() / 1e9, 3),
+        "roofline": roof,
+        "kernels_per_step": {c: dict(ms=round(v["ms"], 4), launches=v["launches"])
+                             for c, v in sorted(per_step.items(), key=lambda kv: -kv[1]["ms"])},
+        "cpu_baseline": cpu,
     }), flush=True)
 
 
@@ -684,21 +729,7 @@ def main():
     per_step = {k: dict(v, ms=v["ms"] / args.profile_steps, launches=v["launches"] / args.profile_steps,
                         flops=v["flops"] / args.profile_steps, bytes=v["bytes"] / args.profile_steps)
                 for k, v in kern.items()}
-    dom = max(per_step, key=lambda k: per_step[k]["ms"])
-    d = per_step[dom]
-    if dom in MFMA_CLASSES:
-        achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
-        peak = MFMA_CLASSES[dom]
-        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4))
-    else:
-        achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4))
-    roof["kernel"] = dom
-    roof["avg_launch_ms"] = round(d["ms"] / max(d["launches"], 1), 4)
-    rec = counter_record("traffic", dom)
-    roof["traffic"] = None if rec is None else rec["hbm_bytes_per_launch"]
+    roof = dominant_roofline(per_step)
     # every class against its own roofline (kernel level: the bytes or flops
     # each launch must move or compute, over its event-timed duration)
     classes = {}

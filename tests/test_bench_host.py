@@ -121,7 +121,7 @@ def test_mfma_summary_from_counters(tmp_path, monkeypatch):
 
 def test_balance_streams_places_every_matrix_once():
     # the layer set: q, k, v, o, gate, up, down at 8192 tokens over 3 streams
-    shapes = [(2048, 2048), (256, 2048), (256, 2048), (2048, 2048), (5632, 2048), (5632, 2048), (2048, 5632)]
+    shapes = [(2048, 2048)] * 4 + [(5632, 2048), (5632, 2048), (2048, 5632)]
     where = bench.balance_streams(shapes, 8192, 3)
     assert len(where) == len(shapes) and set(where) <= {0, 1, 2}
     # the three MLP matrices (largest) each go to a stream of their own
