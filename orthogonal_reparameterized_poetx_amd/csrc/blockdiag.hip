@@ -299,6 +299,189 @@ __global__ __launch_bounds__(Bd<B>::NT) void blockdiag_kernel(const uint16_t* in
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
 }
 
+// b = 256 with the two halves of the workgroup out of phase.  Waves 0-3 own
+// output columns 0-127 of the block, waves 4-7 columns 128-255; every wave
+// alternates a memory phase (refill a ring stage, store its half of the
+// previous tile from its staging half, read the tile's fragments) and a
+// compute phase (16 MFMAs, results to its staging half), with a workgroup
+// barrier between phases, and waves 4-7 run one phase behind waves 0-3, so
+// one half issues MFMAs while the other works on LDS (in blockdiag_kernel
+// every wave does both in the same phase, so the two costs add).  Tile i must
+// have landed before waves 0-3 read it: waves 0-3 wait for their part of it
+// before their memory phase, waves 4-7 before their compute phase of tile
+// i - 1, both at the barrier that opens that read.
+namespace {
+constexpr int PP_S = BDIAG_PP_STAGES;   // ring stages (the staging tile is one more buffer)
+// vector-memory operations a wave has issued after its loads of tile j when
+// it waits for them: the prologue loads tiles 0 .. S-2; memory phase m loads
+// tile m + S - 1 and (m >= 1) stores tile m - 1, two operations each
+constexpr int pp_vm(int j) {
+  return j == 0 ? 2 * (PP_S - 2) : j < PP_S - 1 ? 2 * PP_S - 6 + 2 * j : j == PP_S - 1 ? 4 * (PP_S - 2) : 4 * PP_S - 6;
+}
+static_assert(pp_vm(PP_S) < 64, "vmcnt field");
+}  // namespace
+
+__global__ __launch_bounds__(512) void blockdiag_pp_kernel(const uint16_t* in, const uint16_t* __restrict__ q,
+                                                           uint16_t* out, int64_t N, int64_t lda, int64_t ldc, int k,
+                                                           int tpc) {
+  constexpr int B = 256;
+  using C = Bd<B>;
+  // the seven ring stages, then the staging tile (every access in the loop is
+  // an explicit LDS instruction, so the stages need no names of their own)
+  __shared__ __align__(16) uint16_t RING[(PP_S + 1) * C::TILE];
+  uint16_t* const ST = RING + PP_S * C::TILE;
+  static_assert(C::NW == 8 && (PP_S + 1) * C::TILE * 2 <= 160 * 1024, "eight waves; the LDS holds the ring");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wg = wave & 3;
+  const int l = blockIdx.x % k;
+  const int64_t t0 = (int64_t)(blockIdx.x / k) * tpc * BD_T;
+  if (t0 >= N) return;
+  const int rows = (int)min((int64_t)tpc * BD_T, N - t0);
+  const int nt = (rows + BD_T - 1) / BD_T;
+  const uint32_t ldab = (uint32_t)lda * 2, ldcb = (uint32_t)ldc * 2;
+
+  // ---- q[l] -> VGPR fragments (as in blockdiag_kernel)
+  bf16x8 qf[C::KS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q + (int64_t)l * B * B, 2u * B * B);
+    auto qload = [&](uint16_t* dst, int a) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = (h * C::NW + wave) * 64 + lane, r = c / C::CPR, p = c % C::CPR;
+        b2l16(rq, ((32 * a + r) * B + ((p ^ swz<B>(r)) << 3)) * 2, dst + (h * C::NW + wave) * 512);
+      }
+    };
+#pragma unroll
+    for (int a = 0; a < 8; ++a) qload(RING + a * C::TILE, a);
+    __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+    lds_barrier();
+    const uint16_t* qb = RING + wave * C::TILE;
+    const int r = lane & 31;
+#pragma unroll
+    for (int j = 0; j < C::KS; ++j)
+      qf[j] = *reinterpret_cast<const bf16x8*>(qb + r * B + (((2 * j + (lane >> 5)) ^ swz<B>(r)) << 3));
+  }
+  lds_barrier();
+
+  // ---- tile loads (as in blockdiag_kernel)
+  const BufRange gin = tile_range(t0, rows, (int64_t)l * B, B, lda, 2);
+  const __amdgpu_buffer_rsrc_t rin = rsrc(in + gin.first, (uint32_t)gin.bytes);
+  int voff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = (h * C::NW + wave) * 64 + lane, r = c / C::CPR, p = c % C::CPR;
+    voff[h] = (int)((uint32_t)r * ldab + (uint32_t)((p ^ swz<B>(r)) << 4));
+  }
+  const uint32_t tin = (uint32_t)BD_T * ldab, tout = (uint32_t)BD_T * ldcb;
+  auto load_tile = [&](int i, uint16_t* stage) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      b2l16(rin, voff[h] + (int)((uint32_t)i * tin), stage + (h * C::NW + wave) * 512);
+  };
+  const int r32 = lane & 31, hl = lane >> 5;
+  // fragment j of this lane: row r32, 16-byte chunk 2 j + hl (swizzled)
+  const uint32_t xrow = (uint32_t)(r32 * (2 * B)), xsw = (uint32_t)swz<B>(r32);
+
+  // ---- staging: half grp of ST holds this half's 32 x 128 results, rows of
+  // 256 bytes, 16-byte chunk c of row r at c ^ (r & 15)
+  const uint32_t stb = lds_addr(ST) + (uint32_t)grp * 8192u;
+  uint32_t wst[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) wst[g] = stb + (uint32_t)(r32 * 256 + (((4 * wg + g) ^ (r32 & 15)) << 4) + (hl << 3));
+  // stores: thread t of the half writes row t / 8, chunks t % 8 and 8 + t % 8
+  const BufRange gout = tile_range(t0, rows, (int64_t)l * B, B, ldc, 2);
+  const __amdgpu_buffer_rsrc_t rout = rsrc(out + gout.first, (uint32_t)gout.bytes);
+  const int tg = tid & 255, sr = tg >> 3;
+  uint32_t rst[2];
+  int sof[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cc = 8 * h + (tg & 7);
+    rst[h] = stb + (uint32_t)(sr * 256 + ((cc ^ (sr & 15)) << 4));
+    sof[h] = (int)((uint32_t)sr * ldcb + (uint32_t)((128 * grp + 8 * cc) * 2));
+  }
+  auto store_prev = [&](int i) {   // this half of tile i from staging
+    i32x4 v0, v1;
+    lds_read2(v0, v1, rst[0], rst[1]);
+    bst16(__builtin_bit_cast(u32x4, v0), rout, sof[0] + (int)((uint32_t)i * tout));
+    bst16(__builtin_bit_cast(u32x4, v1), rout, sof[1] + (int)((uint32_t)i * tout));
+  };
+
+  f32x16 acc;
+  i32x4 xf[C::KS];
+  // memory phase of tile i (ring stage `stage`; `next` held tile i - 1)
+  auto mem = [&](int i, const uint16_t* stage, uint16_t* next) {
+    load_tile(i + PP_S - 1, next);
+    if (i > 0) store_prev(i - 1);
+    const uint32_t sb = lds_addr(stage) + xrow;
+    uint32_t a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = sb + ((((uint32_t)(2 * j + hl)) ^ xsw) << 4);
+    lds_read8(*reinterpret_cast<i32x4(*)[8]>(&xf[0]), a);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = sb + ((((uint32_t)(2 * (8 + j) + hl)) ^ xsw) << 4);
+    lds_read8(*reinterpret_cast<i32x4(*)[8]>(&xf[8]), a);
+  };
+  auto mma = [&]() {
+    acc = f32x16{};
+#pragma unroll
+    for (int j = 0; j < C::KS; ++j) acc = mfma32(qf[j], __builtin_bit_cast(bf16x8, xf[j]), acc);
+    // acc register 4 g + e of lane l is out[token l % 32][col 32 w + 8 g + 4 (l / 32) + e]
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      lds_write8b(wst[g], uint2{pk_bf16(acc[4 * g], acc[4 * g + 1]), pk_bf16(acc[4 * g + 2], acc[4 * g + 3])});
+  };
+
+#pragma unroll
+  for (int t = 0; t < PP_S - 1; ++t) {
+    load_tile(t, RING + t * C::TILE);
+    asm volatile("" ::: "memory");
+  }
+  if (grp == 1) {
+    // tile 0 must be complete at the barrier that opens waves 0-3's first read
+    __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(0), 15));
+    lds_barrier();
+  }
+  // wait (immediate count) for this wave's loads of tile j
+  auto wait_tile = [](int j) {
+    switch (j) {
+      case 0: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(0), 15)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(1), 15)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(2), 15)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(3), 15)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(4), 15)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(5), 15)); break;
+      case 6: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(6), 15)); break;
+      case 7: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(7), 15)); break;
+      case 8: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(8), 15)); break;
+      default: __builtin_amdgcn_s_waitcnt(wait_imm(pp_vm(PP_S), 15)); break;
+    }
+  };
+  static_assert(PP_S <= 9, "wait_tile spells out the first pass for up to nine stages");
+  // tile i: the memory phase, then the compute phase, each opened by a barrier
+  int cs = 0, ns = PP_S - 1;   // ring stages of tile i and of tile i - 1
+  for (int i = 0; i < nt; ++i) {
+    asm volatile("" ::: "memory");
+    if (grp == 0) wait_tile(i);
+    lds_barrier();
+    mem(i, RING + cs * C::TILE, RING + ns * C::TILE);
+    asm volatile("" ::: "memory");
+    if (grp == 1) wait_tile(i + 1);
+    lds_barrier();
+    mma();
+    ns = cs;
+    cs = cs == PP_S - 1 ? 0 : cs + 1;
+  }
+  // the last tile: each half stores its staging after a barrier; waves 0-3
+  // take one more barrier so that both halves pass the same number
+  lds_barrier();
+  store_prev(nt - 1);
+  if (grp == 0) lds_barrier();
+  __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+}
+
 // Launch plan: grid = k blocks x C token runs, C sized so that the grid is
 // about one wave of workgroups over the 256 CUs at the occupancy the LDS
 // footprint allows.  Returns false (nothing launched) where the kernel does
@@ -321,7 +504,7 @@ bool launch_blockdiag_bf16(const uint16_t* in, const uint16_t* q, uint16_t* out,
     case 32: hipLaunchKernelGGL(blockdiag_kernel<32>, dim3((unsigned)grid), dim3(64), 0, s, in, q, out, N, lda, ldc, k, (int)tpc); break;
     case 64: hipLaunchKernelGGL(blockdiag_kernel<64>, dim3((unsigned)grid), dim3(128), 0, s, in, q, out, N, lda, ldc, k, (int)tpc); break;
     case 128: hipLaunchKernelGGL(blockdiag_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, in, q, out, N, lda, ldc, k, (int)tpc); break;
-    default: hipLaunchKernelGGL(blockdiag_kernel<256>, dim3((unsigned)grid), dim3(512), 0, s, in, q, out, N, lda, ldc, k, (int)tpc); break;
+    default: hipLaunchKernelGGL(blockdiag_pp_kernel, dim3((unsigned)grid), dim3(512), 0, s, in, q, out, N, lda, ldc, k, (int)tpc); break;
   }
   return true;
 }

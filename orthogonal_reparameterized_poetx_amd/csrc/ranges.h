@@ -73,7 +73,10 @@ POETX_HD inline GramRuns gram_stream_runs(int64_t N, int B, int k) {
 // workgroups per block and tiles per run.  Runs are cut so that every
 // per-lane offset, including the ring's loads of up to 6 tiles past a run's
 // end (which read zero), stays below 2^31.  runs == 0: no such cut exists.
-constexpr int BDIAG_T = 32, BDIAG_STAGES = 7;
+// (Nine stages, the most the LDS holds at b = 256, measured no faster.)
+constexpr int BDIAG_T = 32, BDIAG_STAGES = 7, BDIAG_PP_STAGES = 7;
+// ring loads reach this many tiles past a run (the deeper ring of the two)
+constexpr int BDIAG_REACH = BDIAG_STAGES > BDIAG_PP_STAGES ? BDIAG_STAGES : BDIAG_PP_STAGES;
 struct BdiagRuns { int64_t runs; int64_t tpc; };
 POETX_HD inline BdiagRuns blockdiag_runs(int64_t N, int64_t lda, int64_t ldc, int b, int k) {
   const int lds = (BDIAG_STAGES + 1) * BDIAG_T * b * 2;
@@ -85,7 +88,7 @@ POETX_HD inline BdiagRuns blockdiag_runs(int64_t N, int64_t lda, int64_t ldc, in
   if (runs > ntiles) runs = ntiles;
   int64_t tpc = (ntiles + runs - 1) / runs;
   const int64_t ld = lda > ldc ? lda : ldc;
-  const int64_t maxt = (0x7fffffffLL / (BDIAG_T * ld * 2)) - BDIAG_STAGES;
+  const int64_t maxt = (0x7fffffffLL / (BDIAG_T * ld * 2)) - BDIAG_REACH;
   if (maxt < 1) return BdiagRuns{0, 0};
   if (tpc > maxt) tpc = maxt;
   runs = (ntiles + tpc - 1) / tpc;

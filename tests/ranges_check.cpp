@@ -58,7 +58,7 @@ int main() {
       const BdiagRuns br = blockdiag_runs(N, lda, ldc, b, k);
       if (br.runs < 1) continue;   // the launcher takes the GEMM path instead
       const long long ld = lda > ldc ? lda : ldc;
-      if ((br.tpc + BDIAG_STAGES) * BDIAG_T * ld * 2 >= 0x7fffffffLL) {
+      if ((br.tpc + BDIAG_REACH) * BDIAG_T * ld * 2 >= 0x7fffffffLL) {
         std::printf("FAIL bdiag 32-bit offsets | %s\n", buf);
         return 1;
       }
