@@ -52,6 +52,7 @@ KERNEL_CLASSES = [
     ("permute_stream_kernel", "xform_permute", 1),
     ("gather_blockdiag_kernel", "xform_gather", 1),    # before its substring below
     ("blockdiag_kernel", "xform_blockmul", 1),
+    ("blockdiag_pp_kernel", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, true,", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, false,", "gemm_nt", 1),
     ("gemm_wide_kernel<false>", "gemm_nt", 1),
