@@ -180,13 +180,30 @@ int build_schur512(const float* const* theta, const int64_t* nblks, const QOut* 
   float* M12 = Mf + 256;
   float* M21 = Mf + 256 * 512;
   float* M22 = Mf + 256 * 512 + 256;
+  // two independent products with the same alpha and beta in one launch
+  // (batch items nblk .. 2 nblk - 1 take the second)
+  auto gemm_pair = [&](const float* A, int lda, int64_t sA, const float* B, int ldb, int64_t sB, float* C, int ldc,
+                       int64_t sC, const float* A1, int lda1, int64_t sA1, const float* B1, int ldb1, int64_t sB1,
+                       float* C1, int ldc1, int64_t sC1, float alpha) {
+    BGemmArgs q{};
+    q.M = q.N = q.K = 256;
+    q.A = A; q.sA = sA; q.lda = lda;
+    q.B = B; q.sB = sB; q.ldb = ldb;
+    q.C = C; q.sC = sC; q.ldc = ldc;
+    q.A1 = A1; q.sA1 = sA1; q.lda1 = lda1;
+    q.B1 = B1; q.sB1 = sB1; q.ldb1 = ldb1;
+    q.C1 = C1; q.sC1 = sC1; q.ldc1 = ldc1;
+    q.nb0 = (int)nblk;
+    q.alpha = alpha; q.beta = 0.f;
+    launch_bgemm(mode, 2 * (int)nblk, q, s);
+  };
   gj(Af, M11);                                                    // Ai = A^-1 into M11
-  gemm(M11, 512, A12, 512, Tm, 256, 1.f, 0.f, SB, SB, SH);        // T = Ai B
+  gemm_pair(M11, 512, SB, A12, 512, SB, Tm, 256, SH,              // T = Ai B
+            A21, 512, SB, M11, 512, SB, Vm, 256, SH, 1.f);        // V = C Ai
   gemm(A21, 512, Tm, 256, A22, 512, -1.f, 1.f, SB, SH, SB);       // Sc = D - C T
   gj(A22, M22);                                                   // Si
-  gemm(A21, 512, M11, 512, Vm, 256, 1.f, 0.f, SB, SB, SH);        // V = C Ai
-  gemm(Tm, 256, M22, 512, M12, 512, -1.f, 0.f, SH, SB, SB);       // M12 = -T Si
-  gemm(M22, 512, Vm, 256, M21, 512, -1.f, 0.f, SB, SH, SB);       // M21 = -Si V
+  gemm_pair(Tm, 256, SH, M22, 512, SB, M12, 512, SB,              // M12 = -T Si
+            M22, 512, SB, Vm, 256, SH, M21, 512, SB, -1.f);       // M21 = -Si V
   gemm(M12, 512, Vm, 256, M11, 512, -1.f, 1.f, SB, SH, SB);       // M11 = Ai - M12 V
   {
     int64_t off = 0;

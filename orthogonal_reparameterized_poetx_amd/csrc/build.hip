@@ -389,6 +389,31 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
     }
 }
 
+// one batch item of a BGemmArgs launch: its operands, leading dimensions
+struct BGemmItem {
+  const float* A; const float* B; float* C;
+  int lda, ldb, ldc;
+};
+__device__ __forceinline__ BGemmItem bgemm_item(const BGemmArgs& a, int64_t bz) {
+  BGemmItem t;
+  if (bz >= a.nb0) {
+    const int64_t z = bz - a.nb0;
+    const int64_t sA = a.sA1 ? a.sA1 : a.sA, sB = a.sB1 ? a.sB1 : a.sB, sC = a.sC1 ? a.sC1 : a.sC;
+    t.A = a.A1 ? a.A1 + z * sA : a.A + bz * a.sA;
+    t.B = a.B1 ? a.B1 + z * sB : a.B + bz * a.sB;
+    t.C = a.C1 ? a.C1 + z * sC : a.C + bz * a.sC;
+    t.lda = (a.A1 && a.lda1) ? a.lda1 : a.lda;
+    t.ldb = (a.B1 && a.ldb1) ? a.ldb1 : a.ldb;
+    t.ldc = (a.C1 && a.ldc1) ? a.ldc1 : a.ldc;
+  } else {
+    t.A = a.A + bz * a.sA;
+    t.B = a.B + bz * a.sB;
+    t.C = a.C + bz * a.sC;
+    t.lda = a.lda; t.ldb = a.ldb; t.ldc = a.ldc;
+  }
+  return t;
+}
+
 // ----------------------------------------------------------------------------
 // Batched small fp32 GEMM: C = alpha * opA * opB + beta * C per batch item,
 // opA = A or A^T (+ I), opB = B or B^T (+ I).  64x64 tiles, 4 waves of 32x32,
@@ -411,11 +436,11 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
   const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
   const int64_t bz = blockIdx.z;
   if (a.run && !a.run[bz]) return;
-  const bool second = bz >= a.nb0;
-  const int64_t z1 = bz - a.nb0;
-  const float* A = (second && a.A1) ? a.A1 + z1 * a.sA : a.A + bz * a.sA;
-  const float* Bm = (second && a.B1) ? a.B1 + z1 * a.sB : a.B + bz * a.sB;
-  float* C = (second && a.C1) ? a.C1 + z1 * a.sC : a.C + bz * a.sC;
+  const BGemmItem it = bgemm_item(a, bz);
+  const float* A = it.A;
+  const float* Bm = it.B;
+  float* C = it.C;
+  const int lda = it.lda, ldb = it.ldb, ldc = it.ldc;
   const bool active = (row0 + 32 * wi < a.M) && (col0 + 32 * wj < a.N);
   f32x16 acc;
 #pragma unroll
@@ -442,7 +467,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
       const int gi = row0 + ia, gka = k0 + ka;
       float x = 0.f;
       if (gi < a.M) {
-        x = a.transA ? A[(int64_t)gka * a.lda + gi] : A[(int64_t)gi * a.lda + gka];
+        x = a.transA ? A[(int64_t)gka * lda + gi] : A[(int64_t)gi * lda + gka];
         if (a.addIA && gi == gka) x += 1.0f;
       }
       va[q] = x;
@@ -452,7 +477,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
       const int gj = col0 + jb, gkb = k0 + kb;
       float y = 0.f;
       if (gj < a.N) {
-        y = a.transB ? Bm[(int64_t)gj * a.ldb + gkb] : Bm[(int64_t)gkb * a.ldb + gj];
+        y = a.transB ? Bm[(int64_t)gj * ldb + gkb] : Bm[(int64_t)gkb * ldb + gj];
         if (a.addIB && gkb == gj) y += 1.0f;
       }
       vb[q] = y;
@@ -516,9 +541,164 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = row0 + 32 * wi + c32_row(lane, r);
-      float* cp = C + (int64_t)i * a.ldc + j;
+      float* cp = C + (int64_t)i * ldc + j;
       const float old = (a.beta != 0.f) ? *cp : 0.f;
       *cp = a.alpha * acc[r] + a.beta * old;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// The split-bf16 x6 batched GEMM for sizes in multiples of 128 (the products
+// of the b = 512 Schur solve, and the truncated series at b >= 128):
+// TM x 128 tiles (TM = 128, or 64 where 128-row tiles would leave CUs idle),
+// 8 waves of 32 x (32 TJ) (two waves per SIMD, so one splits and stores while
+// the other multiplies), K = 32 NC in chunks of 32, fully unrolled.  Each
+// chunk is loaded as 16-byte vectors two chunks ahead into registers, split
+// into its three bf16 pieces on the way to one of two LDS buffers, and
+// multiplied from there; one barrier per chunk.  Operands are not
+// transposed; A + I / B + I as in bgemm_kernel.  The products are accumulated
+// in the order of bgemm_kernel<6>, so the results agree with it bit for bit.
+// ----------------------------------------------------------------------------
+namespace {
+constexpr int X6P = 40;                       // LDS pitch in bf16 (32 k + 8)
+}  // namespace
+
+template <int NC, int TM>
+__global__ __launch_bounds__(512) void bgemm_x6_t128_kernel(BGemmArgs a) {
+  constexpr int WR = TM / 32, WC = 8 / WR;    // waves along rows, along columns
+  constexpr int TJ = 128 / WC / 32;           // 32-column MFMA tiles per wave
+  constexpr int NA = TM * 8 / 512;            // A float4 per thread per chunk
+  constexpr int PA = TM * X6P, PB = 128 * X6P;          // one piece of A, of B
+  constexpr int BUF = 3 * PA + 3 * PB;
+  __shared__ __align__(16) bf16 L[2 * BUF];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / WC, wc = wave % WC;
+  const int row0 = blockIdx.y * TM, col0 = blockIdx.x * 128;
+  const int64_t bz = blockIdx.z;
+  if (a.run && !a.run[bz]) return;
+  const BGemmItem it = bgemm_item(a, bz);
+
+  // loads of one chunk: A row row0 + (e >> 3), float4 (e & 7) of the chunk's
+  // 32 k; B rows k0 + 2 (tid & 15) and the next, float4 (tid >> 4) of the 128
+  // columns (k fastest across lanes, so that the transposed LDS writes of a
+  // wave fall on distinct banks)
+  const int kp = tid & 15, jq = tid >> 4;
+  float4 ra[2][NA], rb[2][2];
+  auto load = [&](int c, int set) {
+    const int k0 = 32 * c;
+#pragma unroll
+    for (int o = 0; o < NA; ++o) {
+      const int e = tid + 512 * o, r = e >> 3, q = e & 7;
+      ra[set][o] = *reinterpret_cast<const float4*>(it.A + (int64_t)(row0 + r) * it.lda + k0 + 4 * q);
+    }
+    const float* src = it.B + (int64_t)(k0 + 2 * kp) * it.ldb + col0 + 4 * jq;
+    rb[set][0] = *reinterpret_cast<const float4*>(src);
+    rb[set][1] = *reinterpret_cast<const float4*>(src + it.ldb);
+  };
+  auto split3 = [](float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+    const bf16 hh = (bf16)x;
+    const float r1 = x - (float)hh;
+    const bf16 mm = (bf16)r1;
+    h = __builtin_bit_cast(uint16_t, hh);
+    m = __builtin_bit_cast(uint16_t, mm);
+    l = __builtin_bit_cast(uint16_t, (bf16)(r1 - (float)mm));
+  };
+  // A piece q at [q][row][k]; B piece q at [q][col][k] after the A pieces
+  auto stash = [&](int c, int set, bf16* buf) {
+    const int k0 = 32 * c;
+#pragma unroll
+    for (int o = 0; o < NA; ++o) {
+      const int e = tid + 512 * o, r = e >> 3, q = e & 7;
+      const float v[4] = {ra[set][o].x, ra[set][o].y, ra[set][o].z, ra[set][o].w};
+      uint16_t pc[3][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float x = v[t];
+        if (a.addIA && row0 + r == k0 + 4 * q + t) x += 1.0f;
+        split3(x, pc[0][t], pc[1][t], pc[2][t]);
+      }
+#pragma unroll
+      for (int pq = 0; pq < 3; ++pq)
+        *reinterpret_cast<uint2*>(buf + pq * PA + r * X6P + 4 * q) =
+            make_uint2(pack2(pc[pq][0], pc[pq][1]), pack2(pc[pq][2], pc[pq][3]));
+    }
+    const float v0[4] = {rb[set][0].x, rb[set][0].y, rb[set][0].z, rb[set][0].w};
+    const float v1[4] = {rb[set][1].x, rb[set][1].y, rb[set][1].z, rb[set][1].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = 4 * jq + t, k = 2 * kp;
+      float x0 = v0[t], x1 = v1[t];
+      if (a.addIB) {
+        if (col0 + j == k0 + k) x0 += 1.0f;
+        if (col0 + j == k0 + k + 1) x1 += 1.0f;
+      }
+      uint16_t p0[3], p1[3];
+      split3(x0, p0[0], p0[1], p0[2]);
+      split3(x1, p1[0], p1[1], p1[2]);
+#pragma unroll
+      for (int pq = 0; pq < 3; ++pq)
+        *reinterpret_cast<uint32_t*>(buf + 3 * PA + pq * PB + j * X6P + k) = pack2(p0[pq], p1[pq]);
+    }
+  };
+
+  f32x16 acc[TJ];
+#pragma unroll
+  for (int tj = 0; tj < TJ; ++tj)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tj][r] = 0.f;
+  const int lc = lane & 31;
+  auto compute = [&](const bf16* buf) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int ko = 16 * s + 8 * (lane >> 5);
+      bf16x8 x[3], y[TJ][3];
+#pragma unroll
+      for (int pq = 0; pq < 3; ++pq) {
+        x[pq] = *reinterpret_cast<const bf16x8*>(buf + pq * PA + (32 * wr + lc) * X6P + ko);
+#pragma unroll
+        for (int t = 0; t < TJ; ++t)
+          y[t][pq] = *reinterpret_cast<const bf16x8*>(buf + 3 * PA + pq * PB + (32 * TJ * wc + 32 * t + lc) * X6P + ko);
+      }
+#pragma unroll
+      for (int tj = 0; tj < TJ; ++tj) {
+        f32x16 c = acc[tj];
+        c = mfma32(x[0], y[tj][2], c);
+        c = mfma32(x[1], y[tj][1], c);
+        c = mfma32(x[2], y[tj][0], c);
+        c = mfma32(x[0], y[tj][1], c);
+        c = mfma32(x[1], y[tj][0], c);
+        c = mfma32(x[0], y[tj][0], c);
+        acc[tj] = c;
+      }
+    }
+  };
+
+  // chunk c sits in register set c % 2 from two chunks before its stash
+  load(0, 0);
+  if (NC > 1) load(1, 1);
+  stash(0, 0, L);
+  if (NC > 2) load(2, 0);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    compute(L + (c & 1) * BUF);
+    if (c + 1 < NC) {
+      stash(c + 1, (c + 1) & 1, L + ((c + 1) & 1) * BUF);
+      if (c + 3 < NC) load(c + 3, (c + 1) & 1);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int tj = 0; tj < TJ; ++tj) {
+    const int j = col0 + 32 * TJ * wc + 32 * tj + lc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = row0 + 32 * wr + c32_row(lane, r);
+      float* cp = it.C + (int64_t)i * it.ldc + j;
+      const float old = (a.beta != 0.f) ? *cp : 0.f;
+      *cp = a.alpha * acc[tj][r] + a.beta * old;
     }
   }
 }
@@ -578,8 +758,33 @@ void launch_gj(int B, int mode, int nblk, const GJArgs& g, hipStream_t s) {
   }
 }
 
+// the 128x128-tile kernel applies: split x6, no transposes, M and N multiples
+// of 128, K = 128 or 256, 16-byte aligned rows of A and B in every segment
+static bool bgemm_t128_applies(int mode, const BGemmArgs& a) {
+  if (mode != 6 || a.transA || a.transB || a.M % 128 || a.N % 128 || (a.K != 128 && a.K != 256)) return false;
+  auto al = [](const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  auto al4 = [](int64_t v) { return (v & 3) == 0; };
+  return al(a.A) && al(a.B) && al(a.A1) && al(a.B1) && al4(a.lda) && al4(a.ldb) && al4(a.lda1) && al4(a.ldb1) &&
+         al4(a.sA) && al4(a.sB) && al4(a.sA1) && al4(a.sB1);
+}
+
 void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s) {
   if (batch <= 0) return;
+  if (bgemm_t128_applies(mode, a)) {
+    // 128-row tiles where 64-row ones would need a second round of
+    // workgroups (29 blocks at b = 512: 64-row tiles 14 us, 128-row 19 us;
+    // 58: 27 and 22 us)
+    const bool tall = 2 * (int64_t)batch * (a.M / 128) * (a.N / 128) > 256;
+    dim3 grid(a.N / 128, a.M / (tall ? 128 : 64), batch);
+    if (a.K == 256) {
+      if (tall) hipLaunchKernelGGL((bgemm_x6_t128_kernel<8, 128>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((bgemm_x6_t128_kernel<8, 64>), grid, dim3(512), 0, s, a);
+    } else {
+      if (tall) hipLaunchKernelGGL((bgemm_x6_t128_kernel<4, 128>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((bgemm_x6_t128_kernel<4, 64>), grid, dim3(512), 0, s, a);
+    }
+    return;
+  }
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, batch);
   if (mode == 6) hipLaunchKernelGGL(bgemm_kernel<6>, grid, dim3(256), 0, s, a);
   else if (mode == 3) hipLaunchKernelGGL(bgemm_kernel<3>, grid, dim3(256), 0, s, a);

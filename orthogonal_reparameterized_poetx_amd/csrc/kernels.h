@@ -36,8 +36,10 @@ struct BGemmArgs {
   float* C; int64_t sC; int ldc;
   float alpha, beta;
   // optional second segment: batch items z >= nb0 use A1 / B1 / C1 (when set)
-  // at index z - nb0 instead of A / B / C at index z
+  // at index z - nb0 instead of A / B / C at index z, with the leading
+  // dimensions and batch strides lda1 .. sC1 where those are nonzero
   const float* A1; const float* B1; float* C1; int nb0;
+  int lda1, ldb1, ldc1; int64_t sA1, sB1, sC1;
   // optional: batch item z is computed only when run[z] != 0
   const int* run;
 };
