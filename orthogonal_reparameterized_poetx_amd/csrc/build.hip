@@ -185,7 +185,11 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
           for (int c = 0; c < 4; ++c)
             row[c] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(srcr, __builtin_bit_cast(int, d[kc][c])));
           const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d[kc][kc]), kb * 9));
-          const float pinv = 1.0f / p;
+          // 1/p: the hardware reciprocal and one Newton step (within an ulp
+          // of the quotient; the division's full sequence sat on the pivot
+          // chain, which is sequential over all b pivots)
+          const float r0 = __builtin_amdgcn_rcpf(p);
+          const float pinv = fmaf(fmaf(-p, r0, 1.0f), r0, r0);
           float n[4], cm[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) n[c] = (cb == kb && c == kc) ? pinv : row[c] * pinv;
@@ -231,8 +235,65 @@ __global__ __launch_bounds__(GJShape<B>::NT) void gj_kernel(GJArgs g) {
     }
     __syncthreads();
     // ---- (c) new row panel: A[K, j] <- Dinv A[K, j] (j outside K), A[K, K] <- Dinv.
-    // Each thread owns RB rows x CB columns of the 32 x B panel.
-    {
+    if constexpr (X6) {
+      // on split-bf16 MFMA like the update: wave w < B / 32 forms columns
+      // 32 w .. 32 w + 31 (Dinv times its old columns, or Dinv itself in
+      // the diagonal tile), reading and writing only those columns of Prow
+      if (wave < B / 32) {
+        const int J0 = 32 * wave, hi = lane >> 5;
+        f32x16 c;
+        if (J0 == K0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[r] = DmT[lc * PT + c32_row(lane, r)];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[r] = 0.f;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            bf16x8 a[3], bq[3];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int k = 16 * s + 8 * hi + e;
+              bf16 h, m, l;
+              split3(DmT[k * PT + lc], h, m, l);            // A[i = lc][k] = Dinv[lc][k]
+              a[0][e] = h; a[1][e] = m; a[2][e] = l;
+              split3(Prow[k * PR + J0 + lc], h, m, l);      // B[k][j = lc]
+              bq[0][e] = h; bq[1][e] = m; bq[2][e] = l;
+            }
+            // order-2 terms first, then order 1, then the leading product
+            c = mfma32(a[0], bq[2], c);
+            c = mfma32(a[1], bq[1], c);
+            c = mfma32(a[2], bq[0], c);
+            c = mfma32(a[0], bq[1], c);
+            c = mfma32(a[1], bq[0], c);
+            c = mfma32(a[0], bq[0], c);
+          }
+        }
+        // Prow rows i = c32_row(lane, r), column J0 + lc; OpB[q][J0 + lc][i]
+        // as four consecutive rows per 8-byte write
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Prow[c32_row(lane, r) * PR + J0 + lc] = c[r];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint16_t hm[3][4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            bf16 h, m, l;
+            split3(c[4 * g4 + t], h, m, l);
+            hm[0][t] = __builtin_bit_cast(uint16_t, h);
+            hm[1][t] = __builtin_bit_cast(uint16_t, m);
+            hm[2][t] = __builtin_bit_cast(uint16_t, l);
+          }
+          const int i0 = 8 * g4 + 4 * hi;
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+            *reinterpret_cast<uint2*>(&OpB[q * B * HP + (J0 + lc) * HP + i0]) =
+                make_uint2(pack2(hm[q][0], hm[q][1]), pack2(hm[q][2], hm[q][3]));
+        }
+      }
+      __syncthreads();
+    } else {
+      // fp32: each thread owns RB rows x CB columns of the 32 x B panel.
       constexpr int CB = 4;
       constexpr int RB = 32 * B / (NT * CB);
       const int cg = tid % (B / CB), rg = tid / (B / CB);
@@ -703,18 +764,37 @@ __global__ __launch_bounds__(512) void bgemm_x6_t128_kernel(BGemmArgs a) {
   }
 }
 
-// I - S for a batch of b x b blocks (b = 512 route), fp32 [blk][b][b]
-__global__ void unpack_eye_minus_s_kernel(const float* __restrict__ theta, int b, float* __restrict__ A) {
+// I - S for a batch of b x b blocks (b = 512 route), fp32 [blk][b][b].  One
+// workgroup per pair of 32x32 tiles (I, J) and (J, I), I <= J: the upper
+// tile's entries are rows of the packed triangle (theta(i, j), j > i, is
+// contiguous in j), read once, written negated to (I, J) and, transposed
+// through LDS, to (J, I), so every read and write is along rows.
+__global__ __launch_bounds__(256) void unpack_eye_minus_s_kernel(const float* __restrict__ theta, int b,
+                                                                 float* __restrict__ A) {
+  __shared__ float t[32][33];
   const int blk = blockIdx.y;
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (int64_t)b * b) return;
-  const int i = (int)(e / b), j = (int)(e % b);
+  const int nt = b / 32;
+  // tile pair p -> (I, J), I <= J, row by row of the upper tile triangle
+  int p = blockIdx.x, I = 0;
+  while (p >= nt - I) { p -= nt - I; ++I; }
+  const int J = I + p;
   const float* th = theta + (int64_t)blk * (b * (b - 1) / 2);
-  float v;
-  if (i == j) v = 1.f;
-  else if (i < j) v = -th[i * b - i * (i + 1) / 2 + (j - i - 1)];
-  else v = th[j * b - j * (j + 1) / 2 + (i - j - 1)];
-  A[(int64_t)blk * b * b + e] = v;
+  float* Ab = A + (int64_t)blk * b * b;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 8 rows per pass
+  for (int r = ty; r < 32; r += 8) {
+    const int i = 32 * I + r, j = 32 * J + tx;
+    float v = 0.f;
+    if (j > i) v = th[i * b - i * (i + 1) / 2 + (j - i - 1)];
+    t[r][tx] = v;
+    // upper tile: -theta above the diagonal, 1 on it; in a diagonal tile the
+    // entries below it are the mirror, written in the second pass
+    if (I != J || j >= i) Ab[(int64_t)i * b + j] = (i == j) ? 1.f : -v;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int i = 32 * J + r, j = 32 * I + tx;   // entry (i, j) of the lower tile = theta(j, i)
+    if (I != J || i > j) Ab[(int64_t)i * b + j] = t[tx][r];
+  }
 }
 
 // Q = 2M - I from M [blk][b][b] into Q32 / Qbf16 / QTbf16 (32x32 LDS transpose)
@@ -792,8 +872,9 @@ void launch_bgemm(int mode, int batch, const BGemmArgs& a, hipStream_t s) {
 }
 
 void launch_unpack_eye_minus_s(const float* theta, int b, int nblk, float* A, hipStream_t s) {
-  if (nblk <= 0) return;
-  dim3 grid((unsigned)(((int64_t)b * b + 255) / 256), nblk);
+  if (nblk <= 0 || b % 32) return;
+  const int nt = b / 32;
+  dim3 grid((unsigned)(nt * (nt + 1) / 2), nblk);
   hipLaunchKernelGGL(unpack_eye_minus_s_kernel, grid, dim3(256), 0, s, theta, b, A);
 }
 

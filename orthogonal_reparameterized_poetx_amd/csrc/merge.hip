@@ -562,7 +562,11 @@ void launch_merge_products_inplace(bool f32, void* W, const void* qr, const void
 // it after its own segment has overwritten it.  A cycle with a single head
 // (length <= L) keeps that row in its walker's LDS instead.  Saved heads
 // number at most sum over long cycles of ceil(len / L) < 2 m / L.
-constexpr int CP_THREADS = 1024, CP_MAXM = 32768, CP_PER = CP_MAXM / CP_THREADS;
+// KP = rows per thread (one of a few counts with 1024 KP >= m): the
+// doubling rounds touch only slots that exist (a thread's slots past m are
+// skipped in every loop).
+constexpr int CP_THREADS = 1024, CP_MAXM = 32768, CP_WAVES = CP_THREADS / 64;
+template <int KP>
 __global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* __restrict__ rho, int m, int L,
                                                                 int32_t* __restrict__ dist, int32_t* __restrict__ hlist,
                                                                 int32_t* __restrict__ slot,
@@ -570,7 +574,7 @@ __global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* _
                                                                 int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ nxt) {
   __shared__ uint16_t A[CP_MAXM], B[CP_MAXM];
-  __shared__ int scanH[CP_THREADS], scanS[CP_THREADS];
+  __shared__ int wsH[CP_WAVES], wsS[CP_WAVES];
   const int tid = threadIdx.x;
   int rounds = 0;
   while ((1 << rounds) < m) ++rounds;
@@ -581,9 +585,9 @@ __global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* _
   __syncthreads();
   // A(i) = min over i, rho(i), ..., rho^(2^r - 1)(i); B(i) = rho^(2^r)(i)
   for (int r = 0; r < rounds; ++r) {
-    uint16_t na[CP_PER], nb[CP_PER];
+    uint16_t na[KP], nb[KP];
 #pragma unroll
-    for (int k = 0; k < CP_PER; ++k) {
+    for (int k = 0; k < KP; ++k) {
       const int i = tid + k * CP_THREADS;
       if (i < m) {
         const int j = B[i];
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* _
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < CP_PER; ++k) {
+    for (int k = 0; k < KP; ++k) {
       const int i = tid + k * CP_THREADS;
       if (i < m) {
         A[i] = na[k];
@@ -611,9 +615,9 @@ __global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* _
   }
   __syncthreads();
   for (int r = 0; r < rounds; ++r) {
-    uint16_t na[CP_PER], nb[CP_PER];
+    uint16_t na[KP], nb[KP];
 #pragma unroll
-    for (int k = 0; k < CP_PER; ++k) {
+    for (int k = 0; k < KP; ++k) {
       const int i = tid + k * CP_THREADS;
       if (i < m) {
         const int j = B[i];
@@ -623,7 +627,7 @@ __global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* _
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < CP_PER; ++k) {
+    for (int k = 0; k < KP; ++k) {
       const int i = tid + k * CP_THREADS;
       if (i < m) {
         A[i] = na[k];
@@ -632,53 +636,102 @@ __global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* _
     }
     __syncthreads();
   }
-  // heads and saved heads, listed in index order: thread t owns
-  // [t * CP_PER, (t + 1) * CP_PER)
-  int ch = 0, cs = 0;
-  for (int k = 0; k < CP_PER; ++k) {
-    const int i = tid * CP_PER + k;
-    if (i >= m) break;
+  // distances out (coalesced); then, with rho back in B, per row the flags
+  // head (d % L == 0) and saved head (a head whose cycle has another head:
+  // d > 0, or rho(i)'s distance >= L) into B, and nxt(i) = rho(i), with the
+  // sign bit set when rho(i) is a head
+  __syncthreads();
+  for (int i = tid; i < m; i += CP_THREADS) {
     const int d = A[i];
     dist[i] = d;
-    if (d % L == 0) {
-      ++ch;
-      if (d > 0 || A[rho[i]] >= L) ++cs;
+    B[i] = (uint16_t)rho[i];
+  }
+  __syncthreads();
+  uint16_t fl[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int i = tid + k * CP_THREADS;
+    if (i < m) {
+      const int d = A[i], q = B[i], dq = A[q];
+      const bool h = d % L == 0;
+      fl[k] = (uint16_t)(h ? (d > 0 || dq >= L ? 3 : 1) : 0);
+      nxt[i] = (dq % L == 0) ? (int32_t)((uint32_t)q | 0x80000000u) : q;
     }
   }
-  scanH[tid] = ch;
-  scanS[tid] = cs;
   __syncthreads();
-  for (int off = 1; off < CP_THREADS; off <<= 1) {
-    const int h = tid >= off ? scanH[tid - off] : 0;
-    const int v = tid >= off ? scanS[tid - off] : 0;
-    __syncthreads();
-    scanH[tid] += h;
-    scanS[tid] += v;
-    __syncthreads();
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int i = tid + k * CP_THREADS;
+    if (i < m) B[i] = fl[k];
   }
-  int oh = scanH[tid] - ch, os = scanS[tid] - cs;   // exclusive prefix
-  for (int k = 0; k < CP_PER; ++k) {
-    const int i = tid * CP_PER + k;
+  __syncthreads();
+  // heads and saved heads, listed in index order: thread t owns
+  // [t * KP, (t + 1) * KP); the slots go through A (as 16 bits,
+  // 0xffff for none) so that slot[] is written along rows
+  int ch = 0, cs = 0;
+  for (int k = 0; k < KP; ++k) {
+    const int i = tid * KP + k;
     if (i >= m) break;
-    const int d = A[i];
-    int sl = -1;
-    if (d % L == 0) {
-      hlist[oh++] = i;
-      if (d > 0 || A[rho[i]] >= L) {
-        sl = os++;
-        slist[sl] = i;
+    const int f = B[i];
+    ch += f & 1;
+    cs += f >> 1;
+  }
+  // prefix sums over the threads: within each wave by lane shifts, then
+  // over the wave totals
+  const int lane = tid & 63, wave = tid >> 6;
+  int ih = ch, is = cs;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int h2 = __shfl_up(ih, off), s2 = __shfl_up(is, off);
+    if (lane >= off) {
+      ih += h2;
+      is += s2;
+    }
+  }
+  if (lane == 63) {
+    wsH[wave] = ih;
+    wsS[wave] = is;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int th = lane < CP_WAVES ? wsH[lane] : 0, ts = lane < CP_WAVES ? wsS[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < CP_WAVES; off <<= 1) {
+      const int h2 = __shfl_up(th, off), s2 = __shfl_up(ts, off);
+      if (lane >= off) {
+        th += h2;
+        ts += s2;
       }
     }
-    slot[i] = sl;
+    if (lane < CP_WAVES) {
+      wsH[lane] = th;
+      wsS[lane] = ts;
+    }
+  }
+  __syncthreads();
+  int oh = (wave ? wsH[wave - 1] : 0) + ih - ch, os = (wave ? wsS[wave - 1] : 0) + is - cs;   // exclusive prefix
+  for (int k = 0; k < KP; ++k) {
+    const int i = tid * KP + k;
+    if (i >= m) break;
+    const int f = B[i];
+    uint16_t sl = 0xffff;
+    if (f & 1) {
+      hlist[oh++] = i;
+      if (f & 2) {
+        sl = (uint16_t)os;
+        slist[os++] = i;
+      }
+    }
+    A[i] = sl;
   }
   if (tid == CP_THREADS - 1) {
-    counts[0] = scanH[tid];
-    counts[1] = scanS[tid];
+    counts[0] = wsH[CP_WAVES - 1];
+    counts[1] = wsS[CP_WAVES - 1];
   }
-  // nxt(i) = rho(i), with the sign bit set when rho(i) is a head
+  __syncthreads();
   for (int i = tid; i < m; i += CP_THREADS) {
-    const int q = rho[i];
-    nxt[i] = (A[q] % L == 0) ? (int32_t)((uint32_t)q | 0x80000000u) : q;
+    const int sl = A[i];
+    slot[i] = sl == 0xffff ? -1 : sl;
   }
 }
 
@@ -851,8 +904,23 @@ void launch_relayout_inplace(bool f32, void* W, void* saved, const int32_t* rho,
                              int64_t n, int L, int32_t* dist, int32_t* hlist, int32_t* slot, int32_t* slist,
                              int32_t* counts, int32_t* nxt, int64_t max_saved, hipStream_t s) {
   if (m <= 0 || n <= 0) return;
-  hipLaunchKernelGGL(cycle_plan_kernel, dim3(1), dim3(CP_THREADS), 0, s, rho, (int)m, L, dist, hlist, slot, slist,
-                     counts, nxt);
+  {
+    const int kp = (int)((m + CP_THREADS - 1) / CP_THREADS);
+#define POETX_CP(K)                                                                                          \
+  hipLaunchKernelGGL(cycle_plan_kernel<K>, dim3(1), dim3(CP_THREADS), 0, s, rho, (int)m, L, dist, hlist, slot, \
+                     slist, counts, nxt)
+    if (kp <= 1) POETX_CP(1);
+    else if (kp <= 2) POETX_CP(2);
+    else if (kp <= 3) POETX_CP(3);
+    else if (kp <= 4) POETX_CP(4);
+    else if (kp <= 6) POETX_CP(6);
+    else if (kp <= 8) POETX_CP(8);
+    else if (kp <= 11) POETX_CP(11);
+    else if (kp <= 16) POETX_CP(16);
+    else if (kp <= 22) POETX_CP(22);
+    else POETX_CP(32);
+#undef POETX_CP
+  }
   if (!f32 && walk_staged_ok(n, L, W, saved, kappa)) {
     if (max_saved > 0)
       hipLaunchKernelGGL(save_heads_kernel<uint16_t>, dim3((unsigned)max_saved), dim3(256), 0, s,
