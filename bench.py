@@ -73,11 +73,16 @@ SOURCE_FILES = ["api.hip", "build.hip", "chain.hip", "transform.hip", "blockdiag
                 "merge.hip", "quant.hip", "cnp.hip", "common.h", "kernels.h"]
 
 
-def balance_streams(shapes, N, nstreams):
+def balance_streams(shapes, N, nstreams, kind="step"):
     """Stream index per matrix: longest first onto the least loaded stream,
     by an estimate of each matrix's fwd+bwd time (three GEMMs at 1.1 PF/s;
-    28n + 20m bytes of block transforms per token at 3.5 TB/s)."""
-    cost = [6.0 * N * m * n / 1.1e15 + (28.0 * n + 20.0 * m) * N / 3.5e12 for m, n in shapes]
+    28n + 20m bytes of block transforms per token at 3.5 TB/s), or for
+    kind "merge" of its merge (a chain of about ten short launches, 100 us,
+    and 8mn bytes of products and relayout at 3 TB/s)."""
+    if kind == "merge":
+        cost = [1e-4 + 8.0 * m * n / 3e12 for m, n in shapes]
+    else:
+        cost = [6.0 * N * m * n / 1.1e15 + (28.0 * n + 20.0 * m) * N / 3.5e12 for m, n in shapes]
     load, where = [0.0] * nstreams, [0] * len(shapes)
     for i in sorted(range(len(shapes)), key=lambda i: -cost[i]):
         w = min(range(nstreams), key=lambda w: load[w])
@@ -427,8 +432,17 @@ class Stack:
                 lay.block_buffers(kind)
             lay.workspace(P.OP_FORWARD_BLOCKS, N)
             lay.workspace(P.OP_BACKWARD_DQ, N)
-            lay.workspace(P.OP_MERGE_BLOCKS)
             lay.dq_buffers()
+        # the merges run on the worker streams and the side stream (idle
+        # while they run; the merge is a chain of short launches per matrix,
+        # so a fourth queue adds overlap), balanced by m n, each stream with
+        # its own merge workspace
+        self.nmerge = self.nstreams + 1
+        self.mwhere = balance_streams([(m, n) for _, _, m, n in mats], N, self.nmerge, "merge")
+        need = [1] * self.nmerge
+        for i, lay in enumerate(self.layers):
+            need[self.mwhere[i]] = max(need[self.mwhere[i]], lay.workspace_need(P.OP_MERGE_BLOCKS))
+        self.merge_ws = [P.make_workspace(x, dev) for x in need]
         self.adam_steps = 0
 
     def _fan_out(self, main, idx_items, fn):
@@ -440,13 +454,16 @@ class Stack:
         for w in self.workers[1:]:
             main.wait_stream(w)
 
+    def _streams(self, main):
+        if not hasattr(self, "side"):
+            self.side = self.torch.cuda.Stream()      # all streams at the default priority
+            self.bwd_ready = self.torch.cuda.Event()
+            self.workers = [main] + [self.torch.cuda.Stream() for _ in range(self.nstreams - 1)]
+
     def forward_backward(self):
         P, torch = self.P, self.torch
         main = torch.cuda.current_stream()
-        if not hasattr(self, "side"):
-            self.side = torch.cuda.Stream()      # all streams at the default priority
-            self.bwd_ready = torch.cuda.Event()
-            self.workers = [main] + [torch.cuda.Stream() for _ in range(self.nstreams - 1)]
+        self._streams(main)
         # the backward blocks depend only on the generators: build them on a
         # second stream while the forward pass runs.  That build starts once
         # the forward build is done, so the two do not split the CUs while
@@ -471,9 +488,16 @@ class Stack:
     def merge(self):
         self.P.build_layer_blocks(self.layers, "merge")
         main = self.torch.cuda.current_stream()
-        if not hasattr(self, "workers"):
-            self.workers = [main] + [self.torch.cuda.Stream() for _ in range(self.nstreams - 1)]
-        self._fan_out(main, list(enumerate((lay,) for lay in self.layers)), lambda lay: lay.merge_blocks())
+        self._streams(main)
+        ms = self.workers + [self.side]
+        for w in ms[1:]:
+            w.wait_stream(main)
+        for i, lay in enumerate(self.layers):
+            k = self.mwhere[i]
+            with self.torch.cuda.stream(ms[k]):
+                lay.merge_blocks(ws=self.merge_ws[k])
+        for w in ms[1:]:
+            main.wait_stream(w)
 
     def step(self):
         self.forward_backward()

@@ -834,8 +834,7 @@ int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, 
     launch_relayout_inplace(S.f32, W0p, w.saved, w.snew, w.tnew, S.m, S.n, kRelayoutL, w.dist, w.hlist, w.slot,
                             w.slist, w.counts, w.nxt, w.max_saved, s);
   }
-  launch_fill_f32(thR, 0.f, (int64_t)S.kR * (S.b * (S.b - 1) / 2), s);
-  launch_fill_f32(thP, 0.f, (int64_t)S.kP * (S.b * (S.b - 1) / 2), s);
+  launch_fill2_f32(thR, (int64_t)S.kR * (S.b * (S.b - 1) / 2), thP, (int64_t)S.kP * (S.b * (S.b - 1) / 2), 0.f, s);
   return check_launch("merge relayout");
 }
 

@@ -195,6 +195,7 @@ void launch_copy_rows_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int
 bool launch_relayout_rows_bf16(const uint16_t* V, uint16_t* W, const int32_t* rmap, const int32_t* cmap, int64_t m,
                                int64_t n, hipStream_t s);
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+void launch_fill2_f32(float* p0, int64_t n0, float* p1, int64_t n1, float v, hipStream_t s);
 // In-place merge products: W <- W D_P (full column groups), then W <- D_R W
 // (full row groups); bf16 through MFMA, fp32 with FMA sums.
 void launch_merge_products_inplace(bool f32, void* W, const void* qr, const void* qpt, int64_t m, int64_t n, int b,

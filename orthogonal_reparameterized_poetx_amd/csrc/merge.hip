@@ -217,10 +217,22 @@ void launch_perm_keys_rank(uint64_t seed, uint64_t merge_index, int side, int64_
 __device__ __forceinline__ uint64_t perm_key(uint64_t base, int64_t j) {
   return mix64_dev(base + 0x9E3779B97F4A7C15ull * (uint64_t)(j + 1));
 }
+// Blocks from blocks01 on invert the old permutations instead (inv0 = p0^-1,
+// inv1 = p1^-1), which the same launch can do: they read only p0, p1.
 __global__ __launch_bounds__(RANK_I * RANK_J) void perm_rank2_kernel(uint64_t seed, uint64_t merge_index, int64_t n0,
                                                                      int64_t n1, int32_t* out0, int32_t* out1,
-                                                                     int blocks0) {
+                                                                     int blocks0, int blocks01,
+                                                                     const int32_t* __restrict__ p0,
+                                                                     int32_t* __restrict__ inv0,
+                                                                     const int32_t* __restrict__ p1,
+                                                                     int32_t* __restrict__ inv1) {
   __shared__ uint64_t tile[RANK_TILE];
+  if ((int)blockIdx.x >= blocks01) {
+    const int64_t e = (int64_t)((int)blockIdx.x - blocks01) * (RANK_I * RANK_J) + threadIdx.x;
+    if (e < n0) inv0[p0[e]] = (int32_t)e;
+    else if (e < n0 + n1) inv1[p1[e - n0]] = (int32_t)(e - n0);
+    return;
+  }
   const int side = (int)blockIdx.x < blocks0 ? 0 : 1;
   const int64_t n = side ? n1 : n0;
   int32_t* out = side ? out1 : out0;
@@ -245,13 +257,6 @@ __global__ __launch_bounds__(RANK_I * RANK_J) void perm_rank2_kernel(uint64_t se
   for (int off = RANK_J / 2; off > 0; off >>= 1) rank += __shfl_xor(rank, off, RANK_J);
   if (i < n && lj == 0) out[rank] = (int32_t)i;
 }
-// inv0 = p0^-1 (first n0 threads), inv1 = p1^-1
-__global__ void invert_perm2_kernel(const int32_t* __restrict__ p0, int64_t n0, int32_t* __restrict__ inv0,
-                                    const int32_t* __restrict__ p1, int64_t n1, int32_t* __restrict__ inv1) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < n0) inv0[p0[e]] = (int32_t)e;
-  else if (e < n0 + n1) inv1[p1[e - n0]] = (int32_t)(e - n0);
-}
 // commit the new permutations and turn them into the relayout's maps:
 // cur[i] <- nw[i], nw[i] <- inv[nw[i]] (per side)
 __global__ void commit_perm2_kernel(int32_t* nw0, int32_t* cur0, const int32_t* __restrict__ inv0, int64_t n0,
@@ -272,10 +277,10 @@ void launch_merge_permutations(uint64_t seed, uint64_t merge_index, int32_t* sig
                                int32_t* snew, int32_t* tnew, int32_t* sinv, int32_t* tinv, hipStream_t s) {
   if (m <= 0 && n <= 0) return;
   const int b0 = (int)((m + RANK_I - 1) / RANK_I), b1 = (int)((n + RANK_I - 1) / RANK_I);
-  hipLaunchKernelGGL(perm_rank2_kernel, dim3((unsigned)(b0 + b1)), dim3(RANK_I * RANK_J), 0, s, seed, merge_index, m, n,
-                     snew, tnew, b0);
+  const int binv = (int)((m + n + RANK_I * RANK_J - 1) / (RANK_I * RANK_J));
+  hipLaunchKernelGGL(perm_rank2_kernel, dim3((unsigned)(b0 + b1 + binv)), dim3(RANK_I * RANK_J), 0, s, seed,
+                     merge_index, m, n, snew, tnew, b0, b0 + b1, sigma, sinv, tau, tinv);
   const unsigned g = (unsigned)((m + n + 255) / 256);
-  hipLaunchKernelGGL(invert_perm2_kernel, dim3(g), dim3(256), 0, s, sigma, m, sinv, tau, n, tinv);
   hipLaunchKernelGGL(commit_perm2_kernel, dim3(g), dim3(256), 0, s, snew, sigma, sinv, m, tnew, tau, tinv, n);
 }
 
@@ -960,6 +965,19 @@ __global__ void fill_f32_kernel(float* p, float v, int64_t n) {
 void launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
   if (n <= 0) return;
   hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, v, n);
+}
+
+// two arrays set to v in one launch (the first n0 threads take p0)
+__global__ void fill2_f32_kernel(float* p0, int64_t n0, float* p1, int64_t n1, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n0) p0[i] = v;
+  else if (i - n0 < n1) p1[i - n0] = v;
+}
+void launch_fill2_f32(float* p0, int64_t n0, float* p1, int64_t n1, float v, hipStream_t s) {
+  if (n0 < 0) n0 = 0;
+  if (n1 < 0) n1 = 0;
+  if (n0 + n1 <= 0) return;
+  hipLaunchKernelGGL(fill2_f32_kernel, dim3((unsigned)((n0 + n1 + 255) / 256)), dim3(256), 0, s, p0, n0, p1, n1, v);
 }
 
 // Adam (Kingma & Ba 2015, Algorithm 1), bias corrections passed in

@@ -47,6 +47,10 @@ class PoetxLayer:
             self._ws[op] = ws
         return ws
 
+    def workspace_need(self, op, N=0):
+        """Bytes of workspace that op needs for N tokens."""
+        return L.workspace_bytes(self.layer, N, op)
+
     def pack(self, W0):
         """Load a true-coordinate weight: identity permutations, zero
         generators, then a merge (an exact relayout) into the first random
@@ -200,9 +204,14 @@ class PoetxLayer:
         L.poetx_dequantize_w0(self.layer, self.W0p, W)
         return W
 
-    def merge_blocks(self, stream=None):
-        """Merge with blocks from build_layer_blocks(..., "merge")."""
-        ws = self.workspace(L.OP_MERGE_BLOCKS)
+    def merge_blocks(self, stream=None, ws=None):
+        """Merge with blocks from build_layer_blocks(..., "merge"); ws: a merge
+        workspace of the caller's (at least workspace_bytes(layer, 0,
+        OP_MERGE_BLOCKS) bytes), else this layer's own."""
+        if ws is None:
+            ws = self.workspace(L.OP_MERGE_BLOCKS)
+        elif ws.numel() < L.workspace_bytes(self.layer, 0, L.OP_MERGE_BLOCKS):
+            raise ValueError("merge workspace too small")
         L.poetx_merge_blocks(self.layer, self.W0p, self.block_buffers("merge")[1], self.thR, self.thP, self.sigma,
                              self.tau, self.perm_seed, self.merges, ws, stream)
         self.merges += 1
