@@ -91,7 +91,7 @@ def balance_streams(shapes, N, nstreams, kind="step"):
     return where
 
 
-def dominant_roofline(per_step):
+def dominant_roofline(per_step, tag):
     """roofline of the class with the most time in a serialized pass: achieved
     algorithmic flops (MFMA classes) or bytes over its event-timed duration,
     against the MI355X peak, with the HBM bytes per launch from the committed
@@ -109,7 +109,7 @@ def dominant_roofline(per_step):
                     frac=round(achieved / PEAK_HBM_GBS, 4))
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(d["ms"] / max(d["launches"], 1), 4)
-    rec = counter_record("traffic", dom)
+    rec = counter_record("traffic", dom, tag)
     roof["traffic"] = None if rec is None else rec["hbm_bytes_per_launch"]
     return roof
 
@@ -197,6 +197,17 @@ def _pmc_per_dispatch(d, counter):
     return out
 
 
+def _marked(names):
+    """Dispatch ids strictly between the last two marker kernels (sigmoid)
+    that bracket the serialized per-kernel pass, from {dispatch id: name};
+    every id when the run has no markers."""
+    marks = sorted(d for d, n in names.items() if "sigmoid" in n)
+    if len(marks) < 2:
+        return set(names)
+    lo, hi = marks[-2], marks[-1]
+    return {d for d in names if lo < d < hi}
+
+
 def traffic_from(fetch_dir, write_dir):
     """HBM bytes per launch of every kernel class, from FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch) scaled by what they read for the calibration copy."""
@@ -211,7 +222,10 @@ def traffic_from(fetch_dir, write_dir):
     kf, kw = calib(fetch), calib(write)
     agg = {}
     for tab, k, key in ((fetch, kf, "fetch"), (write, kw, "write")):
-        for name, v in tab.values():
+        keep = _marked({d: nv[0] for d, nv in tab.items()})
+        for did, (name, v) in tab.items():
+            if did not in keep:
+                continue
             cls, per = kernel_class(name)
             if cls is None:
                 continue
@@ -226,7 +240,7 @@ def traffic_from(fetch_dir, write_dir):
     for cls, a in agg.items():
         launches_f = a["dispatches_fetch"] / a["per"]
         launches_w = a["dispatches_write"] / a["per"]
-        rec = dict(kernel_class=cls, source_hash=h, source_files=src_files,
+        rec = dict(kernel_class=cls, workload=profiled_run_tag(), source_hash=h, source_files=src_files,
                    hbm_bytes_per_launch=round(a["fetch"] / launches_f + a["write"] / launches_w),
                    fetch_bytes_per_launch=round(a["fetch"] / launches_f),
                    write_bytes_per_launch=round(a["write"] / launches_w),
@@ -261,7 +275,10 @@ def mfma_from(d):
             v = float(row["Counter_Value"])
             e[c] = max(e.get(c, 0.0), v) if c == "GRBM_GUI_ACTIVE" else e.get(c, 0.0) + v
     agg = {}
-    for e in per.values():
+    keep = _marked({d: e["name"] for d, e in per.items()})
+    for did, e in per.items():
+        if did not in keep:
+            continue
         cls, k = kernel_class(e["name"])
         if cls is None:
             continue
@@ -274,7 +291,8 @@ def mfma_from(d):
     h = kernel_source_hash(SOURCE_FILES)
     for cls, a in agg.items():
         launches = a["dispatches"] / a["per"]
-        rec = dict(kernel_class=cls, source_hash=h, source_files=SOURCE_FILES, launches=launches,
+        rec = dict(kernel_class=cls, workload=profiled_run_tag(), source_hash=h, source_files=SOURCE_FILES,
+                   launches=launches,
                    mfma_flops_per_launch=round(a["mops"] * 512 / launches),
                    mfma_busy_frac=round((a["busy"] / SIMD_COUNT) / (a["cu"] / CU_COUNT), 4) if a["cu"] > 0 else None,
                    cu_busy_cycles_per_launch=round(a["cu"] / CU_COUNT / launches),
@@ -286,14 +304,29 @@ def mfma_from(d):
               % (cls, rec["mfma_flops_per_launch"], rec["mfma_busy_frac"], launches))
 
 
-def counter_record(kind, cls):
-    """A committed counter record (traffic or mfma) whose kernel-source hash
-    still matches the sources."""
+def run_tag(workload, tokens, w0_int8=False, keep_z2=False):
+    """Names the run a counter record was taken on: workload, tokens and variant."""
+    return "%s, %d tokens (%s weights, activations %s)" % (workload, tokens, "INT8" if w0_int8 else "bf16",
+                                                          "kept" if keep_z2 else "recomputed")
+
+
+def profiled_run_tag():
+    """The run the committed counter records come from: bench.py's default
+    (the layer set, bf16 weights, recompute)."""
+    import workloads as WL
+    return run_tag(WL.CONFIGS[3]["name"], WL.CONFIGS[3]["N"])
+
+
+def counter_record(kind, cls, tag):
+    """A committed counter record (traffic or mfma) of class cls taken on the
+    run named tag, whose kernel-source hash still matches the sources."""
     path = os.path.join(ROOT, "profiles", "%s_%s.json" % (kind, cls))
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("source_hash") != kernel_source_hash(rec.get("source_files", [])):
+        return None
+    if rec.get("workload") != tag:
         return None
     return rec
 
@@ -548,7 +581,7 @@ def bench_stack(args):
     P.timing_enable(False)
     st.workers, st.side = saved
     per_step = {c: dict(v) for c, v in kern.items()}
-    roof = dominant_roofline(per_step)
+    roof = dominant_roofline(per_step, run_tag(WL.CONFIGS[5]["name"], N, args.w0_int8))
     cpu = None
     if not args.no_cpu:
         # one layer's seven matrices on the oracle; a stack step runs 24 layers
@@ -754,7 +787,9 @@ def main():
     per_step = {k: dict(v, ms=v["ms"] / args.profile_steps, launches=v["launches"] / args.profile_steps,
                         flops=v["flops"] / args.profile_steps, bytes=v["bytes"] / args.profile_steps)
                 for k, v in kern.items()}
-    roof = dominant_roofline(per_step)
+    tag = run_tag(cfg["name"] if b_over is None else "%s_b%d" % (cfg["name"], b_over), N, args.w0_int8,
+                  args.keep_z2)
+    roof = dominant_roofline(per_step, tag)
     # every class against its own roofline (kernel level: the bytes or flops
     # each launch must move or compute, over its event-timed duration)
     classes = {}
@@ -794,13 +829,13 @@ def main():
         if v["launches"] <= 0 or v["ms"] <= 0:
             continue
         avg_s = v["ms"] / v["launches"] * 1e-3
-        mf = counter_record("mfma", k) if k in ("gemm_nt", "gemm_nn") else None
+        mf = counter_record("mfma", k, tag) if k in ("gemm_nt", "gemm_nn") else None
         if mf:
             a = mf["mfma_flops_per_launch"] / avg_s / 1e12
             counters[k] = dict(bound="mfma", achieved=round(a, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                                frac=round(a / PEAK_BF16_TFLOPS, 4), mfma_busy=mf["mfma_busy_frac"],
                                clock_ghz=round(mf["cu_busy_cycles_per_launch"] / avg_s / 1e9, 3))
-        tr = counter_record("traffic", k) if k in HBM_CLASSES else None
+        tr = counter_record("traffic", k, tag) if k in HBM_CLASSES else None
         if tr:
             a = tr["hbm_bytes_per_launch"] / avg_s / 1e9
             counters[k] = dict(bound="hbm", achieved=round(a, 1), peak=PEAK_HBM_GBS, unit="GB/s",
@@ -853,7 +888,7 @@ def main():
         "roofline_classes": classes,
         "roofline_gemms": gemms,
         "roofline_transforms": transforms,
-        "roofline_counters": counters if args.workload == "layerset" else None,
+        "roofline_counters": counters or None,
         "kernels_per_step": breakdown,
         "merge_ms": round(merge_ms, 3),
     }

@@ -68,6 +68,14 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     # a Gram launch is the streaming kernel plus its reduction (two dispatches)
     g = json.load(open(tmp_path / "profiles" / "traffic_gram.json"))
     assert g["launches"] == 1 and g["hbm_bytes_per_launch"] == round(120.0 * 1024 * 2 + 10.0 * 1024)
+    # the records name the run they were taken on and serve that run only
+    tag = bench.profiled_run_tag()
+    assert rec["workload"] == tag
+    assert bench.counter_record("traffic", "gemm_nt", tag)["hbm_bytes_per_launch"] == rec["hbm_bytes_per_launch"]
+    assert bench.counter_record("traffic", "gemm_nt", bench.run_tag("llama7b_mlp_11008x4096_bf16_b256", 8192)) is None
+    assert bench.counter_record("traffic", "gemm_nt", bench.run_tag("llama1b_layerset_bf16_b256", 4096)) is None
+    assert bench.counter_record("traffic", "gemm_nt", bench.run_tag("llama1b_layerset_bf16_b256", 8192,
+                                                                      w0_int8=True)) is None
 
 
 def test_traffic_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
@@ -117,6 +125,27 @@ def test_mfma_summary_from_counters(tmp_path, monkeypatch):
     # busy cycles per SIMD over busy cycles per compute unit
     assert rec["mfma_busy_frac"] == round(((2.0e5 + 6.0e5) / bench.SIMD_COUNT) / (2 * 1000.0), 4)
     assert rec["cu_busy_cycles_per_launch"] == 1000
+
+
+def test_counter_summaries_keep_the_marked_pass(tmp_path, monkeypatch):
+    # dispatches before the marker pair (warmup, timed steps) and after it
+    # (the merge's small products) stay out of the per-launch figures
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda files: "feedbeef")
+    os.makedirs(tmp_path / "profiles")
+    nn = "void poetx::gemm_wide_kernel<true>(poetx::GemmArgs, int, int, int)"
+    mark = "void at::native::vectorized_elementwise_kernel<4, at::native::sigmoid_kernel_cuda...>"
+    rows = []
+    for did, name, mops in ((1, nn, 10.0), (2, mark, 0.0), (3, nn, 4000.0), (4, nn, 4000.0), (5, mark, 0.0),
+                            (6, nn, 10.0)):
+        rows += [(did, name, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops), (did, name, "SQ_VALU_MFMA_BUSY_CYCLES", 1.0),
+                 (did, name, "GRBM_GUI_ACTIVE", 1.0), (did, name, "SQ_BUSY_CU_CYCLES", 256.0)]
+    _write_pmc(str(tmp_path / "m"), rows)
+    bench.mfma_from(str(tmp_path / "m"))
+    rec = json.load(open(tmp_path / "profiles" / "mfma_gemm_nn.json"))
+    assert rec["launches"] == 2 and rec["mfma_flops_per_launch"] == 4000 * 512
+    assert bench._marked({1: nn, 2: mark, 3: nn, 5: mark, 6: nn}) == {3}
+    assert bench._marked({1: nn, 3: nn}) == {1, 3}
 
 
 def test_balance_streams_places_every_matrix_once():
