@@ -152,6 +152,8 @@ def parse():
                     help="block size of --workload mlp7b (64, 128, 256 or 512; default 512)")
     ap.add_argument("--streams", type=int, default=3,
                     help="HIP streams the seven independent matrices are spread over (batched mode)")
+    ap.add_argument("--merge", choices=["sets", "layers"], default="sets",
+                    help="stack24: each merge stream's matrices in one batched merge call, or one call per matrix")
     ap.add_argument("--chain", choices=["batched", "per-matrix"], default="batched",
                     help="layer set: one chain-rule call for all matrices after the backward pass, or one per "
                          "matrix on its stream")
@@ -389,7 +391,7 @@ class Stack:
     can check them; the rest draw the same distributions on the device from a
     torch generator seeded by (config, matrix, stream)."""
 
-    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=(), streams=3, w0_int8=False):
+    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=(), streams=3, w0_int8=False, merge="sets"):
         import math
         import numpy as np
         self.P, self.torch, self.N = P, torch, N
@@ -475,6 +477,13 @@ class Stack:
         need = [1] * self.nmerge
         for i, lay in enumerate(self.layers):
             need[self.mwhere[i]] = max(need[self.mwhere[i]], lay.workspace_need(P.OP_MERGE_BLOCKS))
+        # merge="sets": each stream merges its matrices with one batched call
+        # (poetx_merge_blocks_sets: the launches after the block products are
+        # shared); "layers": one poetx_merge_blocks call per matrix
+        self.merge_mode = merge
+        self.mgroups = [[lay for i, lay in enumerate(self.layers) if self.mwhere[i] == k] for k in range(self.nmerge)]
+        if merge == "sets":
+            need = [max(P.merge_sets_workspace_need(g), 1) for g in self.mgroups]
         self.merge_ws = [P.make_workspace(x, dev) for x in need]
         self.adam_steps = 0
 
@@ -525,10 +534,16 @@ class Stack:
         ms = self.workers + [self.side]
         for w in ms[1:]:
             w.wait_stream(main)
-        for i, lay in enumerate(self.layers):
-            k = self.mwhere[i]
-            with self.torch.cuda.stream(ms[k]):
-                lay.merge_blocks(ws=self.merge_ws[k])
+        if self.merge_mode == "sets":
+            for k, g in enumerate(self.mgroups):
+                if g:
+                    with self.torch.cuda.stream(ms[k]):
+                        self.P.merge_layers_sets(g, ws=self.merge_ws[k])
+        else:
+            for i, lay in enumerate(self.layers):
+                k = self.mwhere[i]
+                with self.torch.cuda.stream(ms[k]):
+                    lay.merge_blocks(ws=self.merge_ws[k])
         for w in ms[1:]:
             main.wait_stream(w)
 
@@ -546,7 +561,7 @@ def bench_stack(args):
     dev = "cuda:0"
     torch.cuda.set_device(0)
     N = args.tokens or WL.CONFIGS[5]["N"]
-    st = Stack(P, WL, torch, dev, N, streams=args.streams, w0_int8=args.w0_int8)
+    st = Stack(P, WL, torch, dev, N, streams=args.streams, w0_int8=args.w0_int8, merge=args.merge)
     torch.cuda.synchronize()
     resident = torch.cuda.memory_allocated()
     stream = torch.cuda.current_stream()
@@ -594,7 +609,8 @@ def bench_stack(args):
         "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded Gaussian inputs with the stack's shapes)",
         "config": {"workload": WL.CONFIGS[5]["name"], "tokens": N, "matrices": len(st.layers), "b": WL.CONFIGS[5]["b"],
-                   "base_weights": "INT8 codes with per-row fp32 scales (POET-XQ)" if args.w0_int8 else "bf16"},
+                   "base_weights": "INT8 codes with per-row fp32 scales (POET-XQ)" if args.w0_int8 else "bf16",
+                   "merge": "one batched call per stream" if args.merge == "sets" else "one call per matrix"},
         "phases_ms": {"fwd_bwd": round(fb / k, 3), "adam": round(ad / k, 3), "merge": round(mg / k, 3)},
         "generators": st.theta.numel(),
         "resident_gb": round(resident / 1e9, 3),

@@ -403,6 +403,38 @@ int poetx_merge_blocks(const poetx_layer* layer, void* W0p, const poetx_blocks* 
                        float* thP, int32_t* sigma, int32_t* tau, uint64_t perm_seed,
                        uint64_t merge_index, void* ws, size_t ws_bytes, void* stream);
 
+/* One layer's arguments of poetx_merge_blocks, for poetx_merge_blocks_sets. */
+typedef struct {
+  const poetx_layer* layer;
+  void* W0p;
+  const poetx_blocks* blocks;
+  float* thR;
+  float* thP;
+  int32_t* sigma;
+  int32_t* tau;
+  uint64_t perm_seed;
+  uint64_t merge_index;
+} poetx_merge_set;
+
+/*
+ * a10-a11 for several layers at once: the global merge of a model [P3
+ * item 1: every layer merged at the same step].  The results are those of
+ * poetx_merge_blocks on each set in turn, bit for bit; the permutation
+ * draws, the relayout plans, the relayouts and the generator resets of up to
+ * 16 sets share one launch per stage (bf16 layers whose rows are a multiple
+ * of 8 columns and 16-byte aligned; other layers are merged one by one
+ * inside the call).  The sets' buffers must be disjoint.  count == 0 is a
+ * no-op.
+ *   ws  workspace of poetx_merge_sets_workspace_bytes(sets, count) bytes
+ * Errors are detected on the host, before any launch, for every set.
+ */
+int poetx_merge_blocks_sets(const poetx_merge_set* sets, int32_t count, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Workspace bytes of poetx_merge_blocks_sets (0 with the error set for an
+ * invalid layer). */
+size_t poetx_merge_sets_workspace_bytes(const poetx_merge_set* sets, int32_t count);
+
 /*
  * a11 on the host: the permutation poetx_merge draws for (seed, merge_index,
  * side), written to host_out[0..n-1].  The pages only say the permutations are

@@ -54,4 +54,5 @@ from ._lib import (  # noqa: F401
     w0_bytes,
     workspace_bytes,
 )
-from .layer import PoetxLayer, build_layer_blocks, chain_rule_layers  # noqa: F401,E402
+from .layer import (PoetxLayer, build_layer_blocks, chain_rule_layers, merge_layers_sets,  # noqa: F401,E402
+                    merge_sets_workspace_need)

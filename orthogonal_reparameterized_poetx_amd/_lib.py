@@ -26,7 +26,8 @@ EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build
             "poetx_forward", "poetx_forward_blocks", "poetx_forward_blocks_noalloc", "poetx_backward",
             "poetx_backward_blocks", "poetx_backward_blocks_dq", "poetx_forward_blocks_z2",
             "poetx_backward_blocks_dq_z2", "poetx_chain_rule_sets",
-            "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_make_permutation",
+            "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_merge_blocks_sets",
+            "poetx_merge_sets_workspace_bytes", "poetx_make_permutation",
             "poetx_adam_step", "poetx_w0_bytes", "poetx_quantize_w0", "poetx_dequantize_w0",
             "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
 
@@ -78,6 +79,13 @@ class ChainSet(ctypes.Structure):
                 ("dtheta", ctypes.c_void_p)]
 
 
+class MergeSet(ctypes.Structure):
+    """poetx_merge_set: one layer's arguments of poetx_merge_blocks."""
+    _fields_ = [("layer", ctypes.POINTER(Layer)), ("W0p", ctypes.c_void_p), ("blocks", ctypes.POINTER(Blocks)),
+                ("thR", ctypes.c_void_p), ("thP", ctypes.c_void_p), ("sigma", ctypes.c_void_p),
+                ("tau", ctypes.c_void_p), ("perm_seed", ctypes.c_uint64), ("merge_index", ctypes.c_uint64)]
+
+
 class PoetxError(RuntimeError):
     def __init__(self, fn, code, msg):
         super().__init__("%s failed: %s (%d): %s" % (fn, _STATUS.get(code, "?"), code, msg))
@@ -118,6 +126,8 @@ def lib():
         "poetx_chain_workspace_bytes": (sz, [i64, i32]),
         "poetx_merge": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
         "poetx_merge_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, u64, u64, vp, sz, vp]),
+        "poetx_merge_blocks_sets": (ctypes.c_int, [ctypes.POINTER(MergeSet), i32, vp, sz, vp]),
+        "poetx_merge_sets_workspace_bytes": (sz, [ctypes.POINTER(MergeSet), i32]),
         "poetx_make_permutation": (ctypes.c_int, [u64, u64, i32, i64, vp]),
         "poetx_adam_step": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_float, vp]),
@@ -310,6 +320,29 @@ def poetx_merge_blocks(layer, W0p, blocks, thR, thP, sigma, tau, perm_seed, merg
         ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(thR), _ptr(thP),
         _ptr(sigma), _ptr(tau), int(perm_seed) & (2 ** 64 - 1), int(merge_index), _ptr(ws),
         ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def merge_sets(entries):
+    """poetx_merge_set array from (layer, W0p, blocks, thR, thP, sigma, tau,
+    perm_seed, merge_index) tuples; the Layer and Blocks objects must outlive
+    the call (the array points at them)."""
+    arr = (MergeSet * max(len(entries), 1))()
+    for i, (layer, W0p, blocks, thR, thP, sigma, tau, seed, index) in enumerate(entries):
+        arr[i] = MergeSet(ctypes.pointer(layer), _addr(W0p), ctypes.pointer(blocks), _addr(thR), _addr(thP),
+                          _addr(sigma), _addr(tau), int(seed) & (2 ** 64 - 1), int(index))
+    return arr
+
+
+def merge_sets_workspace_bytes(sets, count):
+    n = lib().poetx_merge_sets_workspace_bytes(sets, int(count))
+    if n == 0 and count > 0:
+        raise PoetxError("poetx_merge_sets_workspace_bytes", -1, last_error())
+    return n
+
+
+def poetx_merge_blocks_sets(sets, count, ws, stream=None):
+    _check("poetx_merge_blocks_sets", lib().poetx_merge_blocks_sets(
+        sets, int(count), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def poetx_make_permutation(seed, merge_index, side, n):

@@ -813,8 +813,8 @@ bool merge_fast_products_bf16(const Shape& S, void* W0p, const Blk& q, hipStream
   return true;
 }
 
-int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
-               uint64_t perm_seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
+// W0p <- R W0p P where it lies (the merge's block products)
+int merge_products(const Shape& S, void* W0p, const Blk& q, hipStream_t s) {
   {
     Tm tm(s, "merge_tiles", 4.0 * S.m * S.n * S.b, 2.0 * S.m * S.n * S.es);
     if (!merge_fast_products_bf16(S, W0p, q, s)) {
@@ -822,8 +822,13 @@ int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, 
       else launch_merge_products_inplace(false, W0p, q.qbR, q.qtP, S.m, S.n, S.b, S.kR, S.kP, s);
     }
   }
+  return check_launch("merge products");
+}
+
+int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
+               uint64_t perm_seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
   int rc;
-  if ((rc = check_launch("merge products"))) return rc;
+  if ((rc = merge_products(S, W0p, q, s))) return rc;
   {
     // new permutations, old inverses; then the composed maps in place of the new ones
     Tm tm(s, "merge_permutations", 0.0, 0.0);
@@ -1325,6 +1330,102 @@ int poetx_merge_blocks(const poetx_layer* layer, void* W0p, const poetx_blocks* 
   const MrgWs w = plan_merge(S, false, ws, &need);
   return merge_w0(S, W0p, blk_of(blocks), thR, thP, sigma, tau, perm_seed, merge_index, w,
                     static_cast<hipStream_t>(stream));
+}
+
+namespace {
+// host checks of one merge set (as poetx_merge_blocks makes them) and its
+// workspace bytes
+int check_merge_set(const poetx_merge_set& m, Shape* S, size_t* need) {
+  int rc = validate_layer(m.layer);
+  if (rc) return rc;
+  *S = shape_of(m.layer, 0);
+  if (!m.W0p || !m.sigma || !m.tau) return fail(POETX_EINVAL, "NULL tensor argument");
+  if ((S->kR > 0 && !m.thR) || (S->kP > 0 && !m.thP)) return fail(POETX_EINVAL, "NULL generator");
+  if ((rc = check_merge_blocks(*S, m.blocks))) return rc;
+  plan_merge(*S, false, nullptr, need);
+  *need = (*need + kAlign - 1) / kAlign * kAlign;
+  return POETX_OK;
+}
+}  // namespace
+
+size_t poetx_merge_sets_workspace_bytes(const poetx_merge_set* sets, int32_t count) {
+  if (count < 0 || (count > 0 && !sets)) {
+    fail(POETX_EINVAL, "bad set list");
+    return 0;
+  }
+  size_t tot = kAlign;
+  for (int32_t k = 0; k < count; ++k) {
+    Shape S;
+    size_t need = 0;
+    if (check_merge_set(sets[k], &S, &need)) return 0;
+    tot += need;
+  }
+  return tot;
+}
+
+int poetx_merge_blocks_sets(const poetx_merge_set* sets, int32_t count, void* ws, size_t ws_bytes, void* stream) {
+  if (count < 0 || (count > 0 && !sets)) return fail(POETX_EINVAL, "bad set list");
+  if (count == 0) return POETX_OK;
+  std::vector<Shape> S(count);
+  std::vector<size_t> off(count + 1, 0);
+  int rc;
+  for (int32_t k = 0; k < count; ++k) {
+    size_t need = 0;
+    if ((rc = check_merge_set(sets[k], &S[k], &need))) return rc;
+    off[k + 1] = off[k] + need;
+  }
+  if ((rc = check_ws(ws, ws_bytes, off[count] + kAlign))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  std::vector<MrgWs> w(count);
+  std::vector<int> batched;
+  for (int32_t k = 0; k < count; ++k) {
+    size_t b = 0;
+    w[k] = plan_merge(S[k], false, base + off[k], &b);
+    const poetx_merge_set& m = sets[k];
+    const Blk q = blk_of(m.blocks);
+    if (S[k].q8 || S[k].f32 || !walk_staged_ok(S[k].n, kRelayoutL, m.W0p, w[k].saved, w[k].tnew)) {
+      // merged alone (dequantized copy, fp32 or unaligned rows)
+      if ((rc = merge_w0(S[k], m.W0p, q, m.thR, m.thP, m.sigma, m.tau, m.perm_seed, m.merge_index, w[k], s)))
+        return rc;
+      continue;
+    }
+    if ((rc = merge_products(S[k], m.W0p, q, s))) return rc;
+    batched.push_back(k);
+  }
+  for (size_t c0 = 0; c0 < batched.size(); c0 += MERGE_BATCH) {
+    MergeBatch b{};
+    b.count = (int)std::min(batched.size() - c0, (size_t)MERGE_BATCH);
+    double bytes = 0.0;
+    for (int i = 0; i < b.count; ++i) {
+      const int k = batched[c0 + i];
+      const poetx_merge_set& m = sets[k];
+      const MrgWs& x = w[k];
+      MergeItem& it = b.it[i];
+      it.W = m.W0p; it.saved = x.saved;
+      it.sigma = m.sigma; it.tau = m.tau; it.snew = x.snew; it.tnew = x.tnew; it.sinv = x.sinv; it.tinv = x.tinv;
+      it.dist = x.dist; it.hlist = x.hlist; it.slot = x.slot; it.slist = x.slist; it.counts = x.counts;
+      it.nxt = x.nxt;
+      it.thR = m.thR; it.thP = m.thP;
+      it.nthR = (int64_t)S[k].kR * (S[k].b * (S[k].b - 1) / 2);
+      it.nthP = (int64_t)S[k].kP * (S[k].b * (S[k].b - 1) / 2);
+      it.m = S[k].m; it.n = S[k].n; it.max_saved = x.max_saved;
+      it.seed = m.perm_seed; it.merge_index = m.merge_index;
+      bytes += 2.0 * S[k].m * S[k].n * S[k].es;
+    }
+    {
+      Tm tm(s, "merge_permutations", 0.0, 0.0);
+      launch_merge_permutations_batch(b, s);
+    }
+    {
+      Tm tm(s, "merge_relayout", 0.0, bytes);
+      launch_cycle_plans_batch(b, kRelayoutL, s);
+      launch_relayout_staged_batch(b, kRelayoutL, s);
+    }
+    launch_zero_generators_batch(b, s);
+    if ((rc = check_launch("batched merge"))) return rc;
+  }
+  return POETX_OK;
 }
 
 size_t poetx_w0_bytes(const poetx_layer* layer) {

@@ -207,6 +207,38 @@ void launch_merge_products_inplace(bool f32, void* W, const void* qr, const void
 void launch_relayout_inplace(bool f32, void* W, void* saved, const int32_t* rho, const int32_t* kappa, int64_t m,
                              int64_t n, int L, int32_t* dist, int32_t* hlist, int32_t* slot, int32_t* slist,
                              int32_t* counts, int32_t* nxt, int64_t max_saved, hipStream_t s);
+// The permutation step and the in-place relayout of several merges in one
+// launch per stage.  One item per matrix, its buffers disjoint from the other
+// items': W (bf16 [m][n]), saved (rows set aside), the current permutations
+// sigma / tau, the merge scratch (snew, tnew, sinv, tinv, dist, hlist, slot,
+// nxt: [m] or [n]; slist [max_saved]; counts [2]) and the generators thR / thP
+// (nthR, nthP entries), zeroed by launch_zero_generators_batch.
+struct MergeItem {
+  void* W;
+  void* saved;
+  int32_t *sigma, *tau, *snew, *tnew, *sinv, *tinv;
+  int32_t *dist, *hlist, *slot, *slist, *counts, *nxt;
+  float *thR, *thP;
+  int64_t nthR, nthP, m, n, max_saved;
+  uint64_t seed, merge_index;
+};
+constexpr int MERGE_BATCH = 16;   // items per launch (the batch travels as a kernel argument)
+struct MergeBatch {
+  MergeItem it[MERGE_BATCH];
+  int count;
+  int start[MERGE_BATCH + 1];     // first workgroup of each item (set by the launchers)
+};
+// launch_merge_permutations for every item
+void launch_merge_permutations_batch(const MergeBatch& b, hipStream_t s);
+// the relayout plans (cycle heads and segments) of every item, rho = snew
+void launch_cycle_plans_batch(const MergeBatch& b, int L, hipStream_t s);
+// head rows set aside and the segment walks of every item (bf16 W with rows
+// of a multiple of 8 columns, W, saved and tnew 16-byte aligned:
+// walk_staged_ok), kappa = tnew
+void launch_relayout_staged_batch(const MergeBatch& b, int L, hipStream_t s);
+bool walk_staged_ok(int64_t n, int L, const void* W, const void* saved, const int32_t* kappa);
+// thR, thP <- 0 for every item
+void launch_zero_generators_batch(const MergeBatch& b, hipStream_t s);
 // INT8 weight codes with per-row fp32 scales (quant.hip)
 void launch_dequant_rows(const int8_t* q, const float* sc, uint16_t* w, int64_t m, int64_t n, hipStream_t s);
 void launch_quantize_rows(const uint16_t* w, int8_t* q, float* sc, int64_t m, int64_t n, hipStream_t s);

@@ -217,27 +217,35 @@ void launch_perm_keys_rank(uint64_t seed, uint64_t merge_index, int side, int64_
 __device__ __forceinline__ uint64_t perm_key(uint64_t base, int64_t j) {
   return mix64_dev(base + 0x9E3779B97F4A7C15ull * (uint64_t)(j + 1));
 }
-// Blocks from blocks01 on invert the old permutations instead (inv0 = p0^-1,
-// inv1 = p1^-1), which the same launch can do: they read only p0, p1.
-__global__ __launch_bounds__(RANK_I * RANK_J) void perm_rank2_kernel(uint64_t seed, uint64_t merge_index, int64_t n0,
-                                                                     int64_t n1, int32_t* out0, int32_t* out1,
-                                                                     int blocks0, int blocks01,
-                                                                     const int32_t* __restrict__ p0,
-                                                                     int32_t* __restrict__ inv0,
-                                                                     const int32_t* __restrict__ p1,
-                                                                     int32_t* __restrict__ inv1) {
+// The item of a batched launch that workgroup g belongs to (starts[k] is
+// its first workgroup).
+__device__ __forceinline__ int batch_item(const MergeBatch& b, int g) {
+  int k = 0;
+  while (k + 1 < b.count && g >= b.start[k + 1]) ++k;
+  return k;
+}
+
+// Per item: workgroups [0, b0) rank the row side, [b0, b0 + b1) the column
+// side, and the rest invert the old permutations (sinv = sigma^-1, tinv =
+// tau^-1), which the same launch can do: they read only sigma, tau.
+__global__ __launch_bounds__(RANK_I * RANK_J) void perm_rank2_kernel(MergeBatch bt) {
   __shared__ uint64_t tile[RANK_TILE];
-  if ((int)blockIdx.x >= blocks01) {
-    const int64_t e = (int64_t)((int)blockIdx.x - blocks01) * (RANK_I * RANK_J) + threadIdx.x;
-    if (e < n0) inv0[p0[e]] = (int32_t)e;
-    else if (e < n0 + n1) inv1[p1[e - n0]] = (int32_t)(e - n0);
+  const int kb = batch_item(bt, (int)blockIdx.x);
+  const MergeItem& it = bt.it[kb];
+  const int lb = (int)blockIdx.x - bt.start[kb];
+  const int64_t n0 = it.m, n1 = it.n;
+  const int blocks0 = (int)((n0 + RANK_I - 1) / RANK_I), blocks01 = blocks0 + (int)((n1 + RANK_I - 1) / RANK_I);
+  if (lb >= blocks01) {
+    const int64_t e = (int64_t)(lb - blocks01) * (RANK_I * RANK_J) + threadIdx.x;
+    if (e < n0) it.sinv[it.sigma[e]] = (int32_t)e;
+    else if (e < n0 + n1) it.tinv[it.tau[e - n0]] = (int32_t)(e - n0);
     return;
   }
-  const int side = (int)blockIdx.x < blocks0 ? 0 : 1;
+  const int side = lb < blocks0 ? 0 : 1;
   const int64_t n = side ? n1 : n0;
-  int32_t* out = side ? out1 : out0;
-  const int64_t blk = side ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
-  const uint64_t base = mix64_dev(seed + 0x9E3779B97F4A7C15ull * (2 * merge_index + (uint64_t)side + 1));
+  int32_t* out = side ? it.tnew : it.snew;
+  const int64_t blk = side ? (int64_t)lb - blocks0 : (int64_t)lb;
+  const uint64_t base = mix64_dev(it.seed + 0x9E3779B97F4A7C15ull * (2 * it.merge_index + (uint64_t)side + 1));
   const int li = threadIdx.x / RANK_J, lj = threadIdx.x % RANK_J;
   const int64_t i = blk * RANK_I + li;
   const uint64_t ki = i < n ? perm_key(base, i) : 0;
@@ -259,29 +267,50 @@ __global__ __launch_bounds__(RANK_I * RANK_J) void perm_rank2_kernel(uint64_t se
 }
 // commit the new permutations and turn them into the relayout's maps:
 // cur[i] <- nw[i], nw[i] <- inv[nw[i]] (per side)
-__global__ void commit_perm2_kernel(int32_t* nw0, int32_t* cur0, const int32_t* __restrict__ inv0, int64_t n0,
-                                    int32_t* nw1, int32_t* cur1, const int32_t* __restrict__ inv1, int64_t n1) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < n0) {
-    const int32_t v = nw0[e];
-    cur0[e] = v;
-    nw0[e] = inv0[v];
-  } else if (e < n0 + n1) {
-    const int64_t i = e - n0;
-    const int32_t v = nw1[i];
-    cur1[i] = v;
-    nw1[i] = inv1[v];
+__global__ void commit_perm2_kernel(MergeBatch bt) {
+  const int k = batch_item(bt, (int)blockIdx.x);
+  const MergeItem& it = bt.it[k];
+  const int64_t e = (int64_t)((int)blockIdx.x - bt.start[k]) * blockDim.x + threadIdx.x;
+  if (e < it.m) {
+    const int32_t v = it.snew[e];
+    it.sigma[e] = v;
+    it.snew[e] = it.sinv[v];
+  } else if (e < it.m + it.n) {
+    const int64_t i = e - it.m;
+    const int32_t v = it.tnew[i];
+    it.tau[i] = v;
+    it.tnew[i] = it.tinv[v];
   }
+}
+void launch_merge_permutations_batch(const MergeBatch& b, hipStream_t s) {
+  if (b.count <= 0) return;
+  MergeBatch t = b;
+  int tot = 0;
+  for (int k = 0; k < t.count; ++k) {
+    t.start[k] = tot;
+    const MergeItem& it = t.it[k];
+    tot += (int)((it.m + RANK_I - 1) / RANK_I) + (int)((it.n + RANK_I - 1) / RANK_I) +
+           (int)((it.m + it.n + RANK_I * RANK_J - 1) / (RANK_I * RANK_J));
+  }
+  t.start[t.count] = tot;
+  if (tot > 0) hipLaunchKernelGGL(perm_rank2_kernel, dim3((unsigned)tot), dim3(RANK_I * RANK_J), 0, s, t);
+  tot = 0;
+  for (int k = 0; k < t.count; ++k) {
+    t.start[k] = tot;
+    tot += (int)((t.it[k].m + t.it[k].n + 255) / 256);
+  }
+  t.start[t.count] = tot;
+  if (tot > 0) hipLaunchKernelGGL(commit_perm2_kernel, dim3((unsigned)tot), dim3(256), 0, s, t);
 }
 void launch_merge_permutations(uint64_t seed, uint64_t merge_index, int32_t* sigma, int32_t* tau, int64_t m, int64_t n,
                                int32_t* snew, int32_t* tnew, int32_t* sinv, int32_t* tinv, hipStream_t s) {
   if (m <= 0 && n <= 0) return;
-  const int b0 = (int)((m + RANK_I - 1) / RANK_I), b1 = (int)((n + RANK_I - 1) / RANK_I);
-  const int binv = (int)((m + n + RANK_I * RANK_J - 1) / (RANK_I * RANK_J));
-  hipLaunchKernelGGL(perm_rank2_kernel, dim3((unsigned)(b0 + b1 + binv)), dim3(RANK_I * RANK_J), 0, s, seed,
-                     merge_index, m, n, snew, tnew, b0, b0 + b1, sigma, sinv, tau, tinv);
-  const unsigned g = (unsigned)((m + n + 255) / 256);
-  hipLaunchKernelGGL(commit_perm2_kernel, dim3(g), dim3(256), 0, s, snew, sigma, sinv, m, tnew, tau, tinv, n);
+  MergeBatch b{};
+  b.count = 1;
+  MergeItem& it = b.it[0];
+  it.sigma = sigma; it.tau = tau; it.snew = snew; it.tnew = tnew; it.sinv = sinv; it.tinv = tinv;
+  it.m = m; it.n = n; it.seed = seed; it.merge_index = merge_index;
+  launch_merge_permutations_batch(b, s);
 }
 
 __global__ void invert_perm_kernel(const int32_t* __restrict__ p, int64_t n, int32_t* __restrict__ inv) {
@@ -571,13 +600,18 @@ void launch_merge_products_inplace(bool f32, void* W, const void* qr, const void
 // doubling rounds touch only slots that exist (a thread's slots past m are
 // skipped in every loop).
 constexpr int CP_THREADS = 1024, CP_MAXM = 32768, CP_WAVES = CP_THREADS / 64;
+// One workgroup per item of the batch (rho = its snew).
 template <int KP>
-__global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* __restrict__ rho, int m, int L,
-                                                                int32_t* __restrict__ dist, int32_t* __restrict__ hlist,
-                                                                int32_t* __restrict__ slot,
-                                                                int32_t* __restrict__ slist,
-                                                                int32_t* __restrict__ counts,
-                                                                int32_t* __restrict__ nxt) {
+__global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(MergeBatch bt, int L) {
+  const MergeItem& it = bt.it[blockIdx.x];
+  const int32_t* __restrict__ rho = it.snew;
+  const int m = (int)it.m;
+  int32_t* __restrict__ dist = it.dist;
+  int32_t* __restrict__ hlist = it.hlist;
+  int32_t* __restrict__ slot = it.slot;
+  int32_t* __restrict__ slist = it.slist;
+  int32_t* __restrict__ counts = it.counts;
+  int32_t* __restrict__ nxt = it.nxt;
   __shared__ uint16_t A[CP_MAXM], B[CP_MAXM];
   __shared__ int wsH[CP_WAVES], wsS[CP_WAVES];
   const int tid = threadIdx.x;
@@ -740,15 +774,16 @@ __global__ __launch_bounds__(CP_THREADS) void cycle_plan_kernel(const int32_t* _
   }
 }
 
-// saved[s][:] = W[slist[s]][:] for s < counts[1]; one row per workgroup
+// saved[s][:] = W[slist[s]][:] for s < counts[1]; one row per workgroup,
+// item blockIdx.y of the batch
 template <typename T>
-__global__ __launch_bounds__(256) void save_heads_kernel(const T* __restrict__ W, T* __restrict__ saved,
-                                                         const int32_t* __restrict__ slist,
-                                                         const int32_t* __restrict__ counts, int n) {
+__global__ __launch_bounds__(256) void save_heads_kernel(MergeBatch bt) {
+  const MergeItem& it = bt.it[blockIdx.y];
   const int sidx = blockIdx.x;
-  if (sidx >= counts[1]) return;
-  const T* src = W + (int64_t)slist[sidx] * n;
-  T* dst = saved + (int64_t)sidx * n;
+  if (sidx >= it.counts[1]) return;
+  const int n = (int)it.n;
+  const T* src = static_cast<const T*>(it.W) + (int64_t)it.slist[sidx] * n;
+  T* dst = static_cast<T*>(it.saved) + (int64_t)sidx * n;
   for (int c = threadIdx.x; c < n; c += 256) dst[c] = src[c];
 }
 
@@ -805,15 +840,20 @@ __global__ __launch_bounds__(256) void walk_rows_kernel(T* W, const T* __restric
 // its column indices once for all rows of the chunk.
 constexpr int WK_MAXL = 64;
 constexpr int WK_SLOTS_BYTES = 144 * 1024;
-__global__ __launch_bounds__(256) void walk_rows_staged_bf16_kernel(uint16_t* W, const uint16_t* __restrict__ saved,
-                                                                    const int32_t* __restrict__ nxt,
-                                                                    const int32_t* __restrict__ hlist,
-                                                                    const int32_t* __restrict__ slot,
-                                                                    const int32_t* __restrict__ counts,
-                                                                    const int32_t* __restrict__ kappa, int n, int L) {
+// Item blockIdx.y of the batch (kappa = its tnew), segment blockIdx.x.
+__global__ __launch_bounds__(256) void walk_rows_staged_bf16_kernel(MergeBatch bt, int L) {
   __shared__ __align__(16) uint16_t rows[WK_SLOTS_BYTES / 2];
   __shared__ int pos[WK_MAXL + 1];
   __shared__ int meta[2];
+  const MergeItem& it = bt.it[blockIdx.y];
+  uint16_t* W = static_cast<uint16_t*>(it.W);
+  const uint16_t* __restrict__ saved = static_cast<const uint16_t*>(it.saved);
+  const int32_t* __restrict__ nxt = it.nxt;
+  const int32_t* __restrict__ hlist = it.hlist;
+  const int32_t* __restrict__ slot = it.slot;
+  const int32_t* __restrict__ counts = it.counts;
+  const int32_t* __restrict__ kappa = it.tnew;
+  const int n = (int)it.n;
   const int g = blockIdx.x;
   if (g >= counts[0]) return;
   const int tid = threadIdx.x;
@@ -905,45 +945,61 @@ bool walk_staged_ok(int64_t n, int L, const void* W, const void* saved, const in
   return (n & 7) == 0 && n <= 32768 && L <= WK_MAXL && al(W) && al(saved) && al(kappa);
 }
 
+void launch_cycle_plans_batch(const MergeBatch& b, int L, hipStream_t s) {
+  int64_t mmax = 0;
+  for (int k = 0; k < b.count; ++k) mmax = std::max(mmax, b.it[k].m);
+  if (b.count <= 0 || mmax <= 0) return;
+  const int kp = (int)((mmax + CP_THREADS - 1) / CP_THREADS);
+#define POETX_CP(K) hipLaunchKernelGGL(cycle_plan_kernel<K>, dim3((unsigned)b.count), dim3(CP_THREADS), 0, s, b, L)
+  if (kp <= 1) POETX_CP(1);
+  else if (kp <= 2) POETX_CP(2);
+  else if (kp <= 3) POETX_CP(3);
+  else if (kp <= 4) POETX_CP(4);
+  else if (kp <= 6) POETX_CP(6);
+  else if (kp <= 8) POETX_CP(8);
+  else if (kp <= 11) POETX_CP(11);
+  else if (kp <= 16) POETX_CP(16);
+  else if (kp <= 22) POETX_CP(22);
+  else POETX_CP(32);
+#undef POETX_CP
+}
+
+void launch_relayout_staged_batch(const MergeBatch& b, int L, hipStream_t s) {
+  int64_t smax = 0, mmax = 0;
+  for (int k = 0; k < b.count; ++k) {
+    smax = std::max(smax, b.it[k].max_saved);
+    mmax = std::max(mmax, b.it[k].m);
+  }
+  if (b.count <= 0 || mmax <= 0) return;
+  if (smax > 0)
+    hipLaunchKernelGGL(save_heads_kernel<uint16_t>, dim3((unsigned)smax, (unsigned)b.count), dim3(256), 0, s, b);
+  hipLaunchKernelGGL(walk_rows_staged_bf16_kernel, dim3((unsigned)mmax, (unsigned)b.count), dim3(256), 0, s, b, L);
+}
+
 void launch_relayout_inplace(bool f32, void* W, void* saved, const int32_t* rho, const int32_t* kappa, int64_t m,
                              int64_t n, int L, int32_t* dist, int32_t* hlist, int32_t* slot, int32_t* slist,
                              int32_t* counts, int32_t* nxt, int64_t max_saved, hipStream_t s) {
   if (m <= 0 || n <= 0) return;
-  {
-    const int kp = (int)((m + CP_THREADS - 1) / CP_THREADS);
-#define POETX_CP(K)                                                                                          \
-  hipLaunchKernelGGL(cycle_plan_kernel<K>, dim3(1), dim3(CP_THREADS), 0, s, rho, (int)m, L, dist, hlist, slot, \
-                     slist, counts, nxt)
-    if (kp <= 1) POETX_CP(1);
-    else if (kp <= 2) POETX_CP(2);
-    else if (kp <= 3) POETX_CP(3);
-    else if (kp <= 4) POETX_CP(4);
-    else if (kp <= 6) POETX_CP(6);
-    else if (kp <= 8) POETX_CP(8);
-    else if (kp <= 11) POETX_CP(11);
-    else if (kp <= 16) POETX_CP(16);
-    else if (kp <= 22) POETX_CP(22);
-    else POETX_CP(32);
-#undef POETX_CP
-  }
+  MergeBatch b{};
+  b.count = 1;
+  MergeItem& it = b.it[0];
+  it.W = W; it.saved = saved;
+  it.snew = const_cast<int32_t*>(rho); it.tnew = const_cast<int32_t*>(kappa);
+  it.dist = dist; it.hlist = hlist; it.slot = slot; it.slist = slist; it.counts = counts; it.nxt = nxt;
+  it.m = m; it.n = n; it.max_saved = max_saved;
+  launch_cycle_plans_batch(b, L, s);
   if (!f32 && walk_staged_ok(n, L, W, saved, kappa)) {
-    if (max_saved > 0)
-      hipLaunchKernelGGL(save_heads_kernel<uint16_t>, dim3((unsigned)max_saved), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(W), static_cast<uint16_t*>(saved), slist, counts, (int)n);
-    hipLaunchKernelGGL(walk_rows_staged_bf16_kernel, dim3((unsigned)m), dim3(256), 0, s, static_cast<uint16_t*>(W),
-                       static_cast<const uint16_t*>(saved), nxt, hlist, slot, counts, kappa, (int)n, L);
+    launch_relayout_staged_batch(b, L, s);
     return;
   }
   if (f32) {
     if (max_saved > 0)
-      hipLaunchKernelGGL(save_heads_kernel<float>, dim3((unsigned)max_saved), dim3(256), 0, s,
-                         static_cast<const float*>(W), static_cast<float*>(saved), slist, counts, (int)n);
+      hipLaunchKernelGGL(save_heads_kernel<float>, dim3((unsigned)max_saved, 1), dim3(256), 0, s, b);
     hipLaunchKernelGGL(walk_rows_kernel<float>, dim3((unsigned)m), dim3(256), 0, s, static_cast<float*>(W),
                        static_cast<const float*>(saved), rho, kappa, dist, hlist, slot, counts, (int)n, L);
   } else {
     if (max_saved > 0)
-      hipLaunchKernelGGL(save_heads_kernel<uint16_t>, dim3((unsigned)max_saved), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(W), static_cast<uint16_t*>(saved), slist, counts, (int)n);
+      hipLaunchKernelGGL(save_heads_kernel<uint16_t>, dim3((unsigned)max_saved, 1), dim3(256), 0, s, b);
     hipLaunchKernelGGL(walk_rows_kernel<uint16_t>, dim3((unsigned)m), dim3(256), 0, s, static_cast<uint16_t*>(W),
                        static_cast<const uint16_t*>(saved), rho, kappa, dist, hlist, slot, counts, (int)n, L);
   }
@@ -972,6 +1028,20 @@ __global__ void fill2_f32_kernel(float* p0, int64_t n0, float* p1, int64_t n1, f
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n0) p0[i] = v;
   else if (i - n0 < n1) p1[i - n0] = v;
+}
+// thR, thP <- 0 of item blockIdx.y
+__global__ void zero_generators_kernel(MergeBatch bt) {
+  const MergeItem& it = bt.it[blockIdx.y];
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < it.nthR) it.thR[i] = 0.f;
+  else if (i - it.nthR < it.nthP) it.thP[i - it.nthR] = 0.f;
+}
+void launch_zero_generators_batch(const MergeBatch& b, hipStream_t s) {
+  int64_t tmax = 0;
+  for (int k = 0; k < b.count; ++k) tmax = std::max(tmax, b.it[k].nthR + b.it[k].nthP);
+  if (b.count <= 0 || tmax <= 0) return;
+  hipLaunchKernelGGL(zero_generators_kernel, dim3((unsigned)((tmax + 255) / 256), (unsigned)b.count), dim3(256), 0, s,
+                     b);
 }
 void launch_fill2_f32(float* p0, int64_t n0, float* p1, int64_t n1, float v, hipStream_t s) {
   if (n0 < 0) n0 = 0;

@@ -226,6 +226,35 @@ class PoetxLayer:
 _build_ws = {}
 
 
+def merge_layers_sets(layers, ws=None, stream=None):
+    """poetx_merge_blocks_sets over the layers (blocks from
+    build_layer_blocks(layers, "merge")): the same results as each layer's
+    merge_blocks, with the launches after the block products shared.  ws: a
+    workspace of at least merge_sets_workspace_need(layers) bytes, else one is
+    allocated."""
+    if not layers:
+        return
+    sets = L.merge_sets([(lay.layer, lay.W0p, lay.block_buffers("merge")[1], lay.thR, lay.thP, lay.sigma, lay.tau,
+                          lay.perm_seed, lay.merges) for lay in layers])
+    need = L.merge_sets_workspace_bytes(sets, len(layers))
+    if ws is None:
+        ws = L.make_workspace(need, layers[0].device)
+    elif ws.numel() < need:
+        raise ValueError("merge workspace too small")
+    L.poetx_merge_blocks_sets(sets, len(layers), ws, stream)
+    for lay in layers:
+        lay.merges += 1
+
+
+def merge_sets_workspace_need(layers):
+    """Bytes of workspace merge_layers_sets needs for these layers."""
+    if not layers:
+        return 0
+    sets = L.merge_sets([(lay.layer, lay.W0p, lay.block_buffers("merge")[1], lay.thR, lay.thP, lay.sigma, lay.tau,
+                          lay.perm_seed, lay.merges) for lay in layers])
+    return L.merge_sets_workspace_bytes(sets, len(layers))
+
+
 def build_layer_blocks(layers, kind, stream=None, cnp_terms=0):
     """Build the Cayley blocks of every layer for kind ("forward",
     "backward" or "merge") with one poetx_build_block_sets call per block

@@ -178,6 +178,33 @@ def test_merge_blocks_validates_on_host():
                                 1 << 30, None) == -1
 
 
+def test_merge_sets_validate_on_host():
+    P = _P()
+    L = P.lib()
+    from orthogonal_reparameterized_poetx_amd import _lib
+    f = 0x2000
+    a = P.Layer(512, 256, 64, P.POETX_BF16)
+    c = P.Layer(600, 520, 256, P.POETX_BF16)
+    ok = P.Blocks(None, None, f, None, None, f)
+    sets = _lib.MergeSet * 2
+    good = sets(_lib.MergeSet(ctypes.pointer(a), f, ctypes.pointer(ok), f, f, f, f, 1, 0),
+                _lib.MergeSet(ctypes.pointer(c), f, ctypes.pointer(ok), f, f, f, f, 2, 0))
+    need = L.poetx_merge_sets_workspace_bytes(good, 2)
+    single = P.workspace_bytes(a, 0, P.OP_MERGE_BLOCKS) + P.workspace_bytes(c, 0, P.OP_MERGE_BLOCKS)
+    assert need >= single
+    assert L.poetx_merge_blocks_sets(good, 0, None, 0, None) == 0
+    assert L.poetx_merge_blocks_sets(good, -1, None, 0, None) == -1
+    assert L.poetx_merge_blocks_sets(None, 2, None, 0, None) == -1
+    assert L.poetx_merge_blocks_sets(good, 2, ctypes.c_void_p(0x100000), need - 1, None) == -4
+    # a set without its blocks, or with a bad block size, fails before any launch
+    bad = sets(good[0], _lib.MergeSet(ctypes.pointer(c), f, None, f, f, f, f, 2, 0))
+    assert L.poetx_merge_blocks_sets(bad, 2, ctypes.c_void_p(0x100000), need, None) == -1
+    assert L.poetx_merge_sets_workspace_bytes(bad, 2) == 0
+    wrong = P.Layer(512, 256, 48, P.POETX_BF16)
+    bad2 = sets(good[0], _lib.MergeSet(ctypes.pointer(wrong), f, ctypes.pointer(ok), f, f, f, f, 2, 0))
+    assert L.poetx_merge_blocks_sets(bad2, 2, ctypes.c_void_p(0x100000), need, None) == -1
+
+
 def test_deferred_chain_entry_points_validate_on_host():
     P = _P()
     L = P.lib()

@@ -144,6 +144,42 @@ def test_merge_blocks_matches_merge(dtype, m, n, b):
     assert not c.thR.any().item() and not c.thP.any().item()
 
 
+def test_merge_sets_match_merge_blocks():
+    # batched stages (bf16, rows of a multiple of 8 columns; 21 such sets, so
+    # two launches per stage) beside sets merged one by one inside the call
+    # (fp32, 90-column rows); two merges in a row
+    torch = torch_mod()
+    from orthogonal_reparameterized_poetx_amd import build_layer_blocks, merge_layers_sets
+    cases = [("bf16", 600, 520, 256), ("bf16", 300, 200, 64), ("f32", 96, 80, 32), ("bf16", 70, 90, 32),
+             ("bf16", 256, 768, 128)] + [("bf16", 128, 64, 32)] * 18
+    a, c = [], []
+    for i, (dt, m, n, b) in enumerate(cases):
+        inp = WL.small_case(60 + i, m, n, b, 4, dtype=dt)
+        a.append(make_layer(inp)[0])
+        c.append(make_layer(inp)[0])
+    _log("merge sets: %d layers" % len(cases))
+    m0 = [lay.merges for lay in a]     # the packing merge made by make_layer
+    for rnd in range(2):
+        build_layer_blocks(a, "merge")
+        for lay in a:
+            lay.merge_blocks()
+        build_layer_blocks(c, "merge")
+        merge_layers_sets(c)
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(a, c)):
+            assert torch.equal(x.W0p, y.W0p), (rnd, i, cases[i])
+            assert torch.equal(x.sigma, y.sigma) and torch.equal(x.tau, y.tau), (rnd, i)
+            assert not y.thR.any().item() and not y.thP.any().item(), (rnd, i)
+            assert x.merges == y.merges == m0[i] + rnd + 1
+        # new generators for the next round, the same on both sides
+        for i, (x, y) in enumerate(zip(a, c)):
+            g = torch.Generator(device="cuda").manual_seed(1000 * rnd + i)
+            for tx, ty in ((x.thR, y.thR), (x.thP, y.thP)):
+                v = torch.randn(tx.shape, generator=g, device="cuda") * 0.03
+                tx.copy_(v)
+                ty.copy_(v)
+
+
 @pytest.mark.parametrize("shapes,b,N", [
     ([(600, 520), (256, 768), (512, 512)], 256, 70),
     ([(512, 1024)] * 40, 32, 20),                 # 80 sets, 1920 blocks: several chunks of the batched chain
