@@ -147,16 +147,16 @@ def test_merge_blocks_matches_merge(dtype, m, n, b):
 def test_merge_sets_match_merge_blocks():
     # batched stages (bf16, rows of a multiple of 8 columns; 21 such sets, so
     # two launches per stage) beside sets merged one by one inside the call
-    # (fp32, 90-column rows); two merges in a row
+    # (fp32, 90-column rows and INT8 weights); two merges in a row
     torch = torch_mod()
     from orthogonal_reparameterized_poetx_amd import build_layer_blocks, merge_layers_sets
     cases = [("bf16", 600, 520, 256), ("bf16", 300, 200, 64), ("f32", 96, 80, 32), ("bf16", 70, 90, 32),
-             ("bf16", 256, 768, 128)] + [("bf16", 128, 64, 32)] * 18
+             ("int8", 512, 256, 64), ("bf16", 256, 768, 128)] + [("bf16", 128, 64, 32)] * 18
     a, c = [], []
     for i, (dt, m, n, b) in enumerate(cases):
-        inp = WL.small_case(60 + i, m, n, b, 4, dtype=dt)
-        a.append(make_layer(inp)[0])
-        c.append(make_layer(inp)[0])
+        inp = WL.small_case(60 + i, m, n, b, 4, dtype="bf16" if dt == "int8" else dt)
+        a.append(make_layer(inp, w0_int8=dt == "int8")[0])
+        c.append(make_layer(inp, w0_int8=dt == "int8")[0])
     _log("merge sets: %d layers" % len(cases))
     m0 = [lay.merges for lay in a]     # the packing merge made by make_layer
     for rnd in range(2):
