@@ -1335,7 +1335,7 @@ int poetx_merge_blocks(const poetx_layer* layer, void* W0p, const poetx_blocks* 
 namespace {
 // host checks of one merge set (as poetx_merge_blocks makes them) and its
 // workspace bytes
-int check_merge_set(const poetx_merge_set& m, Shape* S, size_t* need) {
+int check_merge_set_(const poetx_merge_set& m, Shape* S, size_t* need) {
   int rc = validate_layer(m.layer);
   if (rc) return rc;
   *S = shape_of(m.layer, 0);
@@ -1345,6 +1345,15 @@ int check_merge_set(const poetx_merge_set& m, Shape* S, size_t* need) {
   plan_merge(*S, false, nullptr, need);
   *need = (*need + kAlign - 1) / kAlign * kAlign;
   return POETX_OK;
+}
+// the same, the error message naming the set
+int check_merge_set(const poetx_merge_set& m, int32_t k, Shape* S, size_t* need) {
+  const int rc = check_merge_set_(m, S, need);
+  if (rc) {
+    const std::string msg = g_err;
+    fail(rc, "merge set %d: %s", (int)k, msg.c_str());
+  }
+  return rc;
 }
 }  // namespace
 
@@ -1357,7 +1366,7 @@ size_t poetx_merge_sets_workspace_bytes(const poetx_merge_set* sets, int32_t cou
   for (int32_t k = 0; k < count; ++k) {
     Shape S;
     size_t need = 0;
-    if (check_merge_set(sets[k], &S, &need)) return 0;
+    if (check_merge_set(sets[k], k, &S, &need)) return 0;
     tot += need;
   }
   return tot;
@@ -1371,7 +1380,7 @@ int poetx_merge_blocks_sets(const poetx_merge_set* sets, int32_t count, void* ws
   int rc;
   for (int32_t k = 0; k < count; ++k) {
     size_t need = 0;
-    if ((rc = check_merge_set(sets[k], &S[k], &need))) return rc;
+    if ((rc = check_merge_set(sets[k], k, &S[k], &need))) return rc;
     off[k + 1] = off[k] + need;
   }
   if ((rc = check_ws(ws, ws_bytes, off[count] + kAlign))) return rc;

@@ -199,6 +199,7 @@ def test_merge_sets_validate_on_host():
     # a set without its blocks, or with a bad block size, fails before any launch
     bad = sets(good[0], _lib.MergeSet(ctypes.pointer(c), f, None, f, f, f, f, 2, 0))
     assert L.poetx_merge_blocks_sets(bad, 2, ctypes.c_void_p(0x100000), need, None) == -1
+    assert "merge set 1" in P.last_error()
     assert L.poetx_merge_sets_workspace_bytes(bad, 2) == 0
     wrong = P.Layer(512, 256, 48, P.POETX_BF16)
     bad2 = sets(good[0], _lib.MergeSet(ctypes.pointer(wrong), f, ctypes.pointer(ok), f, f, f, f, 2, 0))
