@@ -36,7 +36,11 @@ PEAK_HBM_GBS = 8000.0
 # fp32-accurate product from three bf16 products of split operands (hi hi +
 # hi lo + lo hi), so its fp32 flops peak at 2500/3; the Cayley builder's
 # trailing updates take six (three-way splits), so 2500/6
-MFMA_CLASSES = {"gemm_nt": 2500.0, "gemm_nn": 2500.0, "cayley_build": 2500.0 / 6, "chain_rule": 2500.0 / 3}
+MFMA_CLASSES = {"gemm_nt": 2500.0, "gemm_nt_rside": 2500.0, "gemm_nn": 2500.0, "cayley_build": 2500.0 / 6,
+                "chain_rule": 2500.0 / 3}
+# the weight products (gemm_nt_rside: the forward's, with the R-side block
+# product of b = 256 in its epilogue; its flops include that product's)
+GEMM_CLASSES = ("gemm_nt", "gemm_nt_rside", "gemm_nn")
 CU_COUNT = 256
 SIMD_COUNT = 1024   # 256 compute units x 4 SIMDs
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")
@@ -55,8 +59,9 @@ KERNEL_CLASSES = [
     ("blockdiag_pp_kernel", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, true,", "xform_blockmul", 1),
     ("gemm_bf16_kernel<false, false,", "gemm_nt", 1),
-    ("gemm_wide_kernel<false>", "gemm_nt", 1),
-    ("gemm_wide_kernel<true>", "gemm_nn", 1),
+    ("gemm_wide_kernel<false, false>", "gemm_nt", 1),
+    ("gemm_wide_kernel<false, true>", "gemm_nt_rside", 1),
+    ("gemm_wide_kernel<true, false>", "gemm_nn", 1),
     ("gemm_bf16_kernel<true, false,", "gemm_nn", 1),
     ("chain_product_kernel", "chain_rule", 3),
     ("skew_project_kernel", "chain_rule", 3),
@@ -831,8 +836,8 @@ def main():
                       achieved=round(algo / (xms * 1e-3) / 1e9, 1) if xms > 0 else None, peak=PEAK_HBM_GBS,
                       unit="GB/s", frac=round(algo / (xms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if xms > 0 else None,
                       classes=[k for k in HBM_CLASSES if k in per_step])
-    gms = sum(per_step[k]["ms"] for k in ("gemm_nt", "gemm_nn") if k in per_step)
-    gfl = sum(per_step[k]["flops"] for k in ("gemm_nt", "gemm_nn") if k in per_step)
+    gms = sum(per_step[k]["ms"] for k in GEMM_CLASSES if k in per_step)
+    gfl = sum(per_step[k]["flops"] for k in GEMM_CLASSES if k in per_step)
     gemms = dict(flops=gfl, ms=round(gms, 4), achieved=round(gfl / (gms * 1e-3) / 1e12, 1) if gms > 0 else None,
                  peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                  frac=round(gfl / (gms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if gms > 0 else None)
@@ -845,7 +850,7 @@ def main():
         if v["launches"] <= 0 or v["ms"] <= 0:
             continue
         avg_s = v["ms"] / v["launches"] * 1e-3
-        mf = counter_record("mfma", k, tag) if k in ("gemm_nt", "gemm_nn") else None
+        mf = counter_record("mfma", k, tag) if k in GEMM_CLASSES else None
         if mf:
             a = mf["mfma_flops_per_launch"] / avg_s / 1e12
             counters[k] = dict(bound="mfma", achieved=round(a, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",

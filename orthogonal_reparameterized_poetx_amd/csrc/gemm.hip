@@ -530,7 +530,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_generic_kernel(GemmArgs g) {
 // the 64-deep ring; every step refills one 32-deep stage (chunk t + 3), every
 // even step one 64-deep stage (stage t / 2 + 2).  k is summed in the same
 // order as in the kernel above, so the results are identical.
-template <bool NN>
+//
+// RS (NT only): the forward's R-side block product at b = 256 in the
+// epilogue.  A 256-column output tile is exactly one R block, so the tile,
+// rounded to bf16 as z2' is, goes into the LDS as the A operand of a
+// K = 256 NT product with the block (B operand: rows = output features),
+// k in 32-deep chunks through two stages, and that product is what the
+// epilogue writes.  Summed over k in ascending 16-deep steps on the same
+// MFMA with the same operand roles as the block product kernel, so the
+// result is bit-identical to the two passes; it saves their z2' write and
+// read [P3 "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
+// Transformation", Methodologie item 3: the block-parallel transform].
+template <bool NN, bool RS = false>
 __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
   // R0..R3: the 32-deep ring (16 KiB stages); W0..W2: the 64-deep ring
   __shared__ __align__(16) uint16_t R0[8192], R1[8192], R2[8192], R3[8192];
@@ -788,6 +799,115 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m,
   GSTEP(t0 + 12, R0, R3, W0, 0, W2)
   GSTEP(t0 + 13, R1, R0, W0, 1, W2)
   if (!lag) __builtin_amdgcn_s_barrier();
+  if constexpr (RS) {
+    // r = bf16(z2') Q^T for this tile (the ring is drained: every step's
+    // loads were waited for).  Q chunks c (k in [32 c, 32 c + 32)) go to the
+    // two halves of W2 in the 32-deep layout; the z2' tile fills the other
+    // eight 16 KiB stages, stage c holding columns [32 c, 32 c + 32).
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(g.Qr, gemm_range_q(bn));
+    int vq[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = (wave * 2 + q) * 16 + (lane >> 2);
+      const int cs = (lane & 3) ^ ((r >> 2) & 3);
+      vq[q] = (r * GBN + cs * 8) * 2;
+    }
+    auto qload = [&](int c, uint16_t* st) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) b2l16(rq, vq[q], c * 64, st + (wave * 2 + q) * 512);
+    };
+    uint16_t* const Q0 = W2;
+    uint16_t* const Q1 = W2 + 8192;
+    qload(0, Q0);
+    asm volatile("" ::: "memory");
+    qload(1, Q1);
+    asm volatile("" ::: "memory");
+    // this wave's 128 x 64 part: column group j is stage 2 wn + j, rows
+    // 128 wm ..; lane holds columns 8 q + 4 (lane / 32) + e of row
+    // lane % 32 of row group i, i.e. half lane / 32 of 16-byte chunk q,
+    // stored at chunk q ^ ((row >> 2) & 3) (the layout of the ring's A
+    // stages).  Each stage is named statically, so that the compiler sees
+    // that these writes do not touch the stages the Q chunks are filling.
+    auto zwrite = [&](uint16_t* zs, int j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + (lane & 31);
+        const f32x16& a = acc[i][j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int off = row * 32 + ((q ^ ((row >> 2) & 3)) << 3) + (lane >> 5) * 4;
+          uint2 v;
+          v.x = pack2(f32_to_bits(a[4 * q]), f32_to_bits(a[4 * q + 1]));
+          v.y = pack2(f32_to_bits(a[4 * q + 2]), f32_to_bits(a[4 * q + 3]));
+          *reinterpret_cast<uint2*>(zs + off) = v;
+        }
+      }
+    };
+    if (wn == 0) { zwrite(R0, 0); zwrite(R1, 1); }
+    else if (wn == 1) { zwrite(R2, 0); zwrite(R3, 1); }
+    else if (wn == 2) { zwrite(W0, 0); zwrite(W0 + 8192, 1); }
+    else { zwrite(W1, 0); zwrite(W1 + 8192, 1); }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    // fragment offsets: z2' rows as in the ring (fn), block rows 64 wn + l32
+    uint32_t fq[2];
+    {
+      const int l32 = lane & 31, h = lane >> 5, sw = (l32 >> 2) & 3;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) fq[s2] = (uint32_t)((wn * 64 + l32) * 64 + (((2 * s2 + h) ^ sw) << 4));
+    }
+    auto rfrags = [&](const uint16_t* zs, const uint16_t* qs) {
+      typedef int pi32x4 __attribute__((ext_vector_type(4)));
+      const uint32_t zb = (uint32_t)reinterpret_cast<uintptr_t>(zs);
+      const uint32_t qb = (uint32_t)reinterpret_cast<uintptr_t>(qs);
+      const uint32_t a0 = zb + fn[0], a1 = zb + fn[1], b0 = qb + fq[0], b1 = qb + fq[1];
+      pi32x4 x[8], y[4];
+      asm volatile(
+          "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
+          "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %12 offset:6144\n\t"
+          "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:2048\n\t"
+          "ds_read_b128 %6, %13 offset:4096\n\tds_read_b128 %7, %13 offset:6144\n\t"
+          "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:2048\n\t"
+          "ds_read_b128 %10, %15\n\tds_read_b128 %11, %15 offset:2048\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+            "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
+          : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
+          : "memory");
+      BF[0][0] = __builtin_bit_cast(bf16x8, y[0]);
+      BF[0][1] = __builtin_bit_cast(bf16x8, y[1]);
+      BF[1][0] = __builtin_bit_cast(bf16x8, y[2]);
+      BF[1][1] = __builtin_bit_cast(bf16x8, y[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        AF[0][i] = __builtin_bit_cast(bf16x8, x[i]);
+        AF[1][i] = __builtin_bit_cast(bf16x8, x[4 + i]);
+      }
+    };
+    // chunk 0 in, chunk 1 in flight; the z2' tile written
+    PPBAR(2)
+    // step C: z2' stage ZS with Q stage QS; once every wave has read QS,
+    // refill it with chunk C + 2; then wait for chunk C + 1
+#define RSSTEP(C_, ZS, QS)                                                           \
+  {                                                                                  \
+    rfrags(ZS, QS);                                                                  \
+    if ((C_) + 2 < 8) {                                                              \
+      PPBAR(2)                                                                       \
+      qload((C_) + 2, QS);                                                           \
+      asm volatile("" ::: "memory");                                                 \
+    }                                                                                \
+    mma();                                                                           \
+    if ((C_) + 2 < 8) PPBAR(2) else PPBAR(0)                                         \
+  }
+    RSSTEP(0, R0, Q0) RSSTEP(1, R1, Q1) RSSTEP(2, R2, Q0) RSSTEP(3, R3, Q1)
+    RSSTEP(4, W0, Q0) RSSTEP(5, W0 + 8192, Q1) RSSTEP(6, W1, Q0) RSSTEP(7, W1 + 8192, Q1)
+#undef RSSTEP
+  }
 #undef PPSTEADY
 #undef PPSTEP
 #undef PPBAR
@@ -859,8 +979,8 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     // per training step for NT and NN together.  Short K keeps the 4-stage
     // ring (shorter prologue).
     const bool wide = g.batch == 1 && g.K % 64 == 0 && g.K >= 2048;
-    if (wide && nn) hipLaunchKernelGGL(gemm_wide_kernel<true>, dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
-    else if (wide) hipLaunchKernelGGL(gemm_wide_kernel<false>, dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    if (wide && nn) hipLaunchKernelGGL((gemm_wide_kernel<true, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+    else if (wide) hipLaunchKernelGGL((gemm_wide_kernel<false, false>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
     else if (nn) GEMM_LAUNCH(true, false)
     else if (g.batch > 1) GEMM_LAUNCH(false, true)
     else GEMM_LAUNCH(false, false)
@@ -870,6 +990,25 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
     if (nn) hipLaunchKernelGGL(gemm_bf16_generic_kernel<true>, grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL(gemm_bf16_generic_kernel<false>, grid, dim3(256), 0, s, g);
   }
+}
+
+bool gemm_nt_rside_applies(const void* A, const void* W, const void* Q, const void* C, int64_t M, int64_t N,
+                           int64_t K) {
+  return K % 64 == 0 && K >= 2048 && N % GBN == 0 && M > 0 && N > 0 && gemm_tiled_shape(N, K, K, K, 0, 0) &&
+         aligned8(A) && aligned8(W) && aligned8(Q) && aligned8(C);
+}
+
+void launch_gemm_nt_rside(const uint16_t* A, const uint16_t* W, const uint16_t* Q, uint16_t* C, int64_t M, int64_t N,
+                          int64_t K, hipStream_t s) {
+  GemmArgs g{};
+  g.A = A; g.B = W; g.C = C; g.Qr = Q;
+  g.M = (int)M; g.N = (int)N; g.K = (int)K;
+  g.lda = K; g.ldb = K; g.ldc = N;
+  g.batch = 1;
+  const int tn = (int)(N / GBN), tm = (g.M + GBM - 1) / GBM;
+  const int nt = tn * tm;
+  const int grid = ((nt + 7) / 8) * 8;
+  hipLaunchKernelGGL((gemm_wide_kernel<false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
 }
 
 bool launch_gemm_q8(bool nn, const uint16_t* A, const int8_t* codes, const float* scales, uint16_t* C, int64_t M,

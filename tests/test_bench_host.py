@@ -13,8 +13,9 @@ import bench
 
 def test_kernel_classes_of_the_product_kernels():
     cases = {
-        "void poetx::gemm_wide_kernel<false>(poetx::GemmArgs, int, int, int)": ("gemm_nt", 1),
-        "void poetx::gemm_wide_kernel<true>(poetx::GemmArgs, int, int, int)": ("gemm_nn", 1),
+        "void poetx::gemm_wide_kernel<false, false>(poetx::GemmArgs, int, int, int)": ("gemm_nt", 1),
+        "void poetx::gemm_wide_kernel<false, true>(poetx::GemmArgs, int, int, int)": ("gemm_nt_rside", 1),
+        "void poetx::gemm_wide_kernel<true, false>(poetx::GemmArgs, int, int, int)": ("gemm_nn", 1),
         "void poetx::gemm_bf16_kernel<false, false, false>(poetx::GemmArgs, int, int, int)": ("gemm_nt", 1),
         "void poetx::gemm_bf16_kernel<true, false, true>(poetx::GemmArgs, int, int, int)": ("gemm_nn", 1),
         "void poetx::gemm_bf16_kernel<false, true, false>(poetx::GemmArgs, int, int, int)": ("xform_blockmul", 1),
@@ -45,7 +46,7 @@ def _write_pmc(path, rows):
 def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda files: "feedbeef")
-    nt = "void poetx::gemm_wide_kernel<false>(poetx::GemmArgs, int, int, int)"
+    nt = "void poetx::gemm_wide_kernel<false, false>(poetx::GemmArgs, int, int, int)"
     red = "poetx::gram_reduce_kernel(float const*, int, long, float*)"
     gram = "poetx::gram_stream_kernel(unsigned short const*, ...)"
     neg = "void at::native::neg_kernel_cuda(...)"
@@ -80,7 +81,7 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
 
 def test_traffic_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    nt = "void poetx::gemm_wide_kernel<false>(poetx::GemmArgs, int, int, int)"
+    nt = "void poetx::gemm_wide_kernel<false, false>(poetx::GemmArgs, int, int, int)"
     _write_pmc(str(tmp_path / "f"), [(1, nt, "FETCH_SIZE", 10.0)])
     _write_pmc(str(tmp_path / "w"), [(1, nt, "WRITE_SIZE", 10.0)])
     with pytest.raises(SystemExit):
@@ -92,25 +93,25 @@ def test_trace_window_keeps_the_marked_pass(tmp_path):
     rows = [("sigmoid_kernel", 0, 10),            # earlier markers are ignored
             ("poetx::gram_stream_kernel", 20, 30),
             ("sigmoid_kernel", 100, 110),         # opens the window
-            ("void poetx::gemm_wide_kernel<false>", 120, 220),
-            ("void poetx::gemm_wide_kernel<false>", 230, 330),
+            ("void poetx::gemm_wide_kernel<false, false>", 120, 220),
+            ("void poetx::gemm_wide_kernel<false, false>", 230, 330),
             ("poetx::gram_reduce_kernel", 340, 350),
             ("sigmoid_kernel", 400, 410),         # closes it
-            ("void poetx::gemm_wide_kernel<false>", 500, 900)]
+            ("void poetx::gemm_wide_kernel<false, false>", 500, 900)]
     with open(path, "w", newline="") as fh:
         w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
         w.writeheader()
         for name, t0, t1 in rows:
             w.writerow(dict(Kernel_Name=name, Start_Timestamp=t0, End_Timestamp=t1))
     got = {r["Name"]: (int(r["Calls"]), float(r["TotalDurationNs"])) for r in bench._trace_window(path, None)}
-    assert got == {"void poetx::gemm_wide_kernel<false>": (2, 200.0), "poetx::gram_reduce_kernel": (1, 10.0)}
+    assert got == {"void poetx::gemm_wide_kernel<false, false>": (2, 200.0), "poetx::gram_reduce_kernel": (1, 10.0)}
 
 
 def test_mfma_summary_from_counters(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda files: "feedbeef")
     os.makedirs(tmp_path / "profiles")
-    nt = "void poetx::gemm_wide_kernel<false>(poetx::GemmArgs, int, int, int)"
+    nt = "void poetx::gemm_wide_kernel<false, false>(poetx::GemmArgs, int, int, int)"
     rows = []
     # two launches; MOPS and busy cycles arrive per SE and are summed, GUI_ACTIVE per XCD (max)
     for did, mops, busy in ((1, 1000.0, 2.0e5), (2, 3000.0, 6.0e5)):
@@ -133,7 +134,7 @@ def test_counter_summaries_keep_the_marked_pass(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda files: "feedbeef")
     os.makedirs(tmp_path / "profiles")
-    nn = "void poetx::gemm_wide_kernel<true>(poetx::GemmArgs, int, int, int)"
+    nn = "void poetx::gemm_wide_kernel<true, false>(poetx::GemmArgs, int, int, int)"
     mark = "void at::native::vectorized_elementwise_kernel<4, at::native::sigmoid_kernel_cuda...>"
     rows = []
     for did, name, mops in ((1, nn, 10.0), (2, mark, 0.0), (3, nn, 4000.0), (4, nn, 4000.0), (5, mark, 0.0),

@@ -214,6 +214,36 @@ def test_deferred_chain_matches_backward_blocks(shapes, b, N):
         assert torch.equal(aR, dR + dR) and torch.equal(aP, dP + dP)
 
 
+@pytest.mark.parametrize("m,n,N", [
+    (256, 2048, 300),     # one column tile (k and v of the layer set)
+    (768, 2112, 257),     # K = 33 * 64, a ragged token tile
+    (2048, 5632, 333),    # the down projection's K
+    (5632, 2048, 1000),   # 22 column tiles (gate and up)
+])
+def test_fused_rside_forward_matches_two_passes(m, n, N):
+    """At b = 256 (no identity tail, K >= 2048) the forward GEMM applies the
+    R-side blocks in its epilogue.  Its Y equals the two-pass path's (the
+    kept-z2' forward: GEMM, then the block product) bit for bit, and for the
+    smaller shapes the oracle's within the Y bound."""
+    torch = torch_mod()
+    from orthogonal_reparameterized_poetx_amd import build_layer_blocks
+    inp = WL.small_case(81, m, n, 256, N, dtype="bf16")
+    lay, d = make_layer(inp)
+    _log("fused R side m=%d n=%d N=%d" % (m, n, N))
+    build_layer_blocks([lay], "forward")
+    Y0 = lay.forward_blocks(d["X"])
+    Z2 = torch.empty((N, m), dtype=torch.bfloat16, device="cuda:0")
+    Y1, _ = lay.forward_blocks_z2(d["X"], Z2=Z2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0, Y1)
+    if m * n * N <= (1 << 29):
+        sigma, tau = oracle_perms(inp, 0)
+        W0, thR, thP, X, gY = inp["W0"][1], inp["thR"][1], inp["thP"][1], inp["X"][1], inp["gY"][1]
+        _, _, _, it = oracle.backward(W0, thR, thP, sigma, tau, X, gY, 256, contract=True, intermediates=True)
+        compare(from_dev(Y0), oracle.forward(W0, thR, thP, sigma, tau, X, 256, contract=True), "bf16", "Y",
+                floor=layer_floors(W0, it)["Y"])
+
+
 @pytest.mark.parametrize("m,n,b,N", [
     (600, 520, 256, 70),     # identity tails on both sides
     (2048, 2048, 256, 45),   # the 64-deep GEMM ring (K >= 2048)
