@@ -77,6 +77,10 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
 /* poetx_layer.flags */
 #define POETX_ACCUMULATE_GRAD 1u /* backward adds into dthR/dthP instead of overwriting */
 #define POETX_W0_INT8 2u         /* W0p in the INT8 weight format (bf16 layers), below */
+/* b = 256, bf16: the forward's R-side block product as a pass of its own
+ * instead of in the epilogue of the GEMM before it.  Results are
+ * bit-identical either way; for verification. */
+#define POETX_SEPARATE_BLOCK_PRODUCTS 4u
 
 /* op codes for poetx_workspace_bytes */
 #define POETX_OP_FORWARD 0
@@ -92,7 +96,8 @@ typedef struct {
   int64_t n;      /* columns of W0 = input features                       */
   int32_t b;      /* block size of R and P                                */
   int32_t dtype;  /* poetx_dtype of W0p, X, Y, dY, dX                     */
-  uint32_t flags; /* POETX_ACCUMULATE_GRAD, POETX_W0_INT8                 */
+  uint32_t flags; /* POETX_ACCUMULATE_GRAD, POETX_W0_INT8,
+                     POETX_SEPARATE_BLOCK_PRODUCTS                        */
   uint32_t reserved; /* must be 0                                         */
 } poetx_layer;
 

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     OP_MERGE_BLOCKS,
     POETX_ACCUMULATE_GRAD,
     POETX_W0_INT8,
+    POETX_SEPARATE_BLOCK_PRODUCTS,
     POETX_BF16,
     POETX_F32,
     Blocks,

@@ -16,6 +16,7 @@ POETX_F32 = 0
 POETX_BF16 = 1
 POETX_ACCUMULATE_GRAD = 1
 POETX_W0_INT8 = 2
+POETX_SEPARATE_BLOCK_PRODUCTS = 4
 OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS, OP_MERGE_BLOCKS, OP_BACKWARD_DQ = range(7)
 
 _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDTYPE",

@@ -90,7 +90,8 @@ int validate_layer(const poetx_layer* L) {
   if (L->m < 1 || L->m > kMaxDim || L->n < 1 || L->n > kMaxDim)
     return fail(POETX_ESHAPE, "m=%lld n=%lld out of range [1, %lld]", (long long)L->m, (long long)L->n,
                 (long long)kMaxDim);
-  if (L->flags & ~(POETX_ACCUMULATE_GRAD | POETX_W0_INT8)) return fail(POETX_EINVAL, "unknown flags 0x%x", L->flags);
+  if (L->flags & ~(POETX_ACCUMULATE_GRAD | POETX_W0_INT8 | POETX_SEPARATE_BLOCK_PRODUCTS))
+    return fail(POETX_EINVAL, "unknown flags 0x%x", L->flags);
   if ((L->flags & POETX_W0_INT8) && L->dtype != POETX_BF16)
     return fail(POETX_EDTYPE, "POETX_W0_INT8 applies to bf16 layers");
   return POETX_OK;
@@ -330,6 +331,7 @@ struct Shape {
   int b, kR, kP;
   bool f32;
   bool q8;    // W0p holds INT8 codes and per-row scales (POETX_W0_INT8)
+  bool sep;   // POETX_SEPARATE_BLOCK_PRODUCTS
   size_t es;  // element size of activations / weight
 };
 
@@ -340,6 +342,7 @@ Shape shape_of(const poetx_layer* L, int64_t N) {
   S.kP = (int)(L->n / L->b);
   S.f32 = L->dtype == POETX_F32;
   S.q8 = (L->flags & POETX_W0_INT8) != 0;
+  S.sep = (L->flags & POETX_SEPARATE_BLOCK_PRODUCTS) != 0;
   S.es = S.f32 ? 4 : 2;
   return S;
 }
@@ -629,7 +632,7 @@ int fwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
   // b = 256 without an identity tail, z2' not kept: the R-side block product
   // in the GEMM's epilogue, r = D_R z2' straight into sc (bit-identical to
   // the two passes below)
-  if (!z2out && !W0.q && S.b == 256 && (int64_t)S.kR * S.b == m &&
+  if (!z2out && !S.sep && !W0.q && S.b == 256 && (int64_t)S.kR * S.b == m &&
       gemm_nt_rside_applies(w.z1, W0.bf, q.qbR, w.sc, N, S.m, S.n)) {
     {
       Tm tm(s, "gemm_nt_rside", 2.0 * N * S.m * S.n + xf_flops(N, S.kR, S.b),

@@ -12,14 +12,19 @@ from . import _lib as L
 
 
 class PoetxLayer:
-    def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0, ws_pool=None, w0_int8=False):
+    def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0, ws_pool=None, w0_int8=False,
+                 separate_block_products=False):
         """w0_int8: keep W0p in the INT8 weight format (per-row codes and
         scales, POETX_W0_INT8; bf16 layers), turned into bf16 inside the
-        passes' GEMMs or dequantized by each pass (include/poetx.h says which)."""
+        passes' GEMMs or dequantized by each pass (include/poetx.h says which).
+        separate_block_products: at b = 256, run the forward's R-side block
+        product as a pass of its own rather than in the epilogue of the GEMM
+        before it (POETX_SEPARATE_BLOCK_PRODUCTS; bit-identical results)."""
         self.device = torch.device(device)
         self.dt = L.POETX_BF16 if dtype == "bf16" else L.POETX_F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.flags = L.POETX_W0_INT8 if w0_int8 else 0
+        self.flags = (L.POETX_W0_INT8 if w0_int8 else 0) | \
+            (L.POETX_SEPARATE_BLOCK_PRODUCTS if separate_block_products else 0)
         self.layer = L.Layer(m, n, b, self.dt, self.flags)
         self.m, self.n, self.b = m, n, b
         nt = b * (b - 1) // 2

@@ -164,13 +164,13 @@ def inputs_to_device(inp):
                 X=to_dev(inp["X"][0], dt), gY=to_dev(inp["gY"][0], dt))
 
 
-def make_layer(inp, device="cuda:0", w0_int8=False):
+def make_layer(inp, device="cuda:0", w0_int8=False, **kw):
     """PoetxLayer packed from the true-coordinate W0 (w0_int8: quantized to
-    the INT8 weight format), generators loaded."""
+    the INT8 weight format), generators loaded; kw go to PoetxLayer."""
     from orthogonal_reparameterized_poetx_amd import PoetxLayer
     d = inputs_to_device(inp)
     lay = PoetxLayer(inp["m"], inp["n"], inp["b"], inp["dtype"], device, perm_seed=inp["perm_seed"],
-                     w0_int8=w0_int8)
+                     w0_int8=w0_int8, **kw)
     lay.pack(d["W0"])
     lay.thR.copy_(d["thR"])
     lay.thP.copy_(d["thP"])

@@ -63,6 +63,11 @@ def test_argument_validation_on_host():
         assert rc == code, (rc, P.last_error())
         assert P.last_error()
         assert L.poetx_workspace_bytes(ctypes.byref(lay), 64, 0) == 0
+    # POETX_SEPARATE_BLOCK_PRODUCTS is a known flag and changes no workspace size
+    sep = P.Layer(2048, 2048, 256, P.POETX_BF16, P.POETX_SEPARATE_BLOCK_PRODUCTS)
+    plain = P.Layer(2048, 2048, 256, P.POETX_BF16)
+    for op in range(7):
+        assert L.poetx_workspace_bytes(ctypes.byref(sep), 64, op) == L.poetx_workspace_bytes(ctypes.byref(plain), 64, op) > 0
     bad = P.Layer(256, 256, 32)
     bad.reserved = 1
     assert L.poetx_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, 64, fake, fake, ws_need, None) == -1

@@ -220,28 +220,43 @@ def test_deferred_chain_matches_backward_blocks(shapes, b, N):
     (2048, 5632, 333),    # the down projection's K
     (5632, 2048, 1000),   # 22 column tiles (gate and up)
 ])
-def test_fused_rside_forward_matches_two_passes(m, n, N):
+def test_fused_block_products_match_separate_passes(m, n, N):
     """At b = 256 (no identity tail, K >= 2048) the forward GEMM applies the
-    R-side blocks in its epilogue.  Its Y equals the two-pass path's (the
-    kept-z2' forward: GEMM, then the block product) bit for bit, and for the
-    smaller shapes the oracle's within the Y bound."""
+    R-side blocks in its epilogue.  Y equals that of the same layer with
+    POETX_SEPARATE_BLOCK_PRODUCTS (GEMM, then the block product) bit for
+    bit, and so do the kept-z2' forward and both backward calls (which take
+    the two passes either way); for the smaller shapes Y, dX and dL/dQ meet
+    the oracle's bounds."""
     torch = torch_mod()
     from orthogonal_reparameterized_poetx_amd import build_layer_blocks
     inp = WL.small_case(81, m, n, 256, N, dtype="bf16")
     lay, d = make_layer(inp)
-    _log("fused R side m=%d n=%d N=%d" % (m, n, N))
-    build_layer_blocks([lay], "forward")
-    Y0 = lay.forward_blocks(d["X"])
-    Z2 = torch.empty((N, m), dtype=torch.bfloat16, device="cuda:0")
-    Y1, _ = lay.forward_blocks_z2(d["X"], Z2=Z2)
+    sep, _ = make_layer(inp, separate_block_products=True)
+    _log("fused block products m=%d n=%d N=%d" % (m, n, N))
+    build_layer_blocks([lay, sep], "forward")
+    build_layer_blocks([lay, sep], "backward")
+    outs = []
+    for L_ in (lay, sep):
+        lay_y = L_.forward_blocks(d["X"]).clone()
+        Z2 = torch.empty((N, m), dtype=torch.bfloat16, device="cuda:0")
+        Yz, _ = L_.forward_blocks_z2(d["X"], Z2=Z2)
+        dX, GR, GP = (t.clone() for t in L_.backward_blocks_dq(d["X"], d["gY"]))
+        dXz, GRz, GPz = (t.clone() for t in L_.backward_blocks_dq_z2(d["X"], d["gY"], Z2))
+        outs.append((lay_y, Yz.clone(), Z2, dX, GR, GP, dXz, GRz, GPz))
     torch.cuda.synchronize()
-    assert torch.equal(Y0, Y1)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    Y, dX, GR, GP = outs[0][0], outs[0][3], outs[0][4], outs[0][5]
     if m * n * N <= (1 << 29):
         sigma, tau = oracle_perms(inp, 0)
         W0, thR, thP, X, gY = inp["W0"][1], inp["thR"][1], inp["thP"][1], inp["X"][1], inp["gY"][1]
-        _, _, _, it = oracle.backward(W0, thR, thP, sigma, tau, X, gY, 256, contract=True, intermediates=True)
-        compare(from_dev(Y0), oracle.forward(W0, thR, thP, sigma, tau, X, 256, contract=True), "bf16", "Y",
-                floor=layer_floors(W0, it)["Y"])
+        dXr, _, _, it = oracle.backward(W0, thR, thP, sigma, tau, X, gY, 256, contract=True, intermediates=True)
+        fl = layer_floors(W0, it)
+        compare(from_dev(Y), oracle.forward(W0, thR, thP, sigma, tau, X, 256, contract=True), "bf16", "Y",
+                floor=fl["Y"])
+        compare(from_dev(dX), dXr, "bf16", "dX", floor=fl["dX"])
+        compare(from_dev(GR), np.array(it["GR"]), "sum", "dL/dQ_R", terms=N)
+        compare(from_dev(GP), np.array(it["GP"]), "sum", "dL/dQ_P", terms=N)
 
 
 @pytest.mark.parametrize("m,n,b,N", [
