@@ -77,8 +77,8 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
 /* poetx_layer.flags */
 #define POETX_ACCUMULATE_GRAD 1u /* backward adds into dthR/dthP instead of overwriting */
 #define POETX_W0_INT8 2u         /* W0p in the INT8 weight format (bf16 layers), below */
-/* b = 256, bf16: the forward's R-side block product as a pass of its own
- * instead of in the epilogue of the GEMM before it.  Results are
+/* bf16, b in {64, 128, 256}: the forward's R-side block product as a pass
+ * of its own instead of in the epilogue of the GEMM before it.  Results are
  * bit-identical either way; for verification. */
 #define POETX_SEPARATE_BLOCK_PRODUCTS 4u
 

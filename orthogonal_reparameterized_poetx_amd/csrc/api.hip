@@ -629,15 +629,16 @@ int fwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
   if ((rc = gather_blockmul(X, tau, q.qbP, w.sc, w.z1, nullptr, N, n, S.b, S.kP, S.es, s))) return rc;
   // z2' = z1' W0p^T
   void* const z2 = z2out ? z2out : w.z2;
-  // b = 256 without an identity tail, z2' not kept: the R-side block product
-  // in the GEMM's epilogue, r = D_R z2' straight into sc (bit-identical to
-  // the two passes below)
-  if (!z2out && !S.sep && !W0.q && S.b == 256 && (int64_t)S.kR * S.b == m &&
-      gemm_nt_rside_applies(w.z1, W0.bf, q.qbR, w.sc, N, S.m, S.n)) {
+  // b of 64 to 256 without an identity tail, z2' not kept: the R-side block
+  // product in the GEMM's epilogue, r = D_R z2' straight into sc
+  // (bit-identical to the two passes below)
+  if (!z2out && !S.sep && !W0.q && (int64_t)S.kR * S.b == m &&
+      gemm_nt_rside_applies(w.z1, W0.bf, q.qbR, w.sc, N, S.m, S.n, S.b)) {
     {
       Tm tm(s, "gemm_nt_rside", 2.0 * N * S.m * S.n + xf_flops(N, S.kR, S.b),
             (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-      launch_gemm_nt_rside((const uint16_t*)w.z1, (const uint16_t*)W0.bf, q.qbR, (uint16_t*)w.sc, N, S.m, S.n, s);
+      launch_gemm_nt_rside((const uint16_t*)w.z1, (const uint16_t*)W0.bf, q.qbR, (uint16_t*)w.sc, N, S.m, S.n, S.b,
+                           s);
     }
     if ((rc = check_launch("forward GEMM with the R-side blocks"))) return rc;
     return permute(false, w.sc, z2, Y, nullptr, sigma, N, m, S.kR * S.b, S.es, s);

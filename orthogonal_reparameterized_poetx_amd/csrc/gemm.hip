@@ -531,16 +531,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_generic_kernel(GemmArgs g) {
 // even step one 64-deep stage (stage t / 2 + 2).  k is summed in the same
 // order as in the kernel above, so the results are identical.
 //
-// RS (NT only): the forward's R-side block product at b = 256 in the
-// epilogue.  A 256-column output tile is exactly one R block, so the tile,
-// rounded to bf16 as z2' is, goes into the LDS as the A operand of a
-// K = 256 NT product with the block (B operand: rows = output features),
-// k in 32-deep chunks through two stages, and that product is what the
-// epilogue writes.  Summed over k in ascending 16-deep steps on the same
-// MFMA with the same operand roles as the block product kernel, so the
-// result is bit-identical to the two passes; it saves their z2' write and
-// read [P3 "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
-// Transformation", Methodologie item 3: the block-parallel transform].
+// RS (NT only): the forward's R-side block product in the epilogue, for b
+// in {64, 128, 256}.  A 256-column output tile holds 256 / b whole blocks,
+// and each wave's 64 columns lie inside one of them.  The tile, rounded to
+// bf16 as z2' is, goes into the LDS as the A operand of an NT product with
+// the tile's blocks (B operand: rows = output features; the blocks, one
+// after another, form a [256][b] matrix), k in b / 32 chunks of 32 through
+// two stages, each wave reading the z2' chunks of its own block; that
+// product is what the epilogue writes.  Summed over k in ascending 16-deep
+// steps on the same MFMA with the same operand roles as the block product
+// kernels, so the result is bit-identical to the two passes; it saves their
+// z2' write and read [P3 "POET-X: Memory-efficient LLM Training by Scaling
+// Orthogonal Transformation", Methodologie item 3: the block-parallel
+// transform].
 template <bool NN, bool RS = false>
 __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m, int tiles_n, int ntiles) {
   // R0..R3: the 32-deep ring (16 KiB stages); W0..W2: the 64-deep ring
@@ -801,17 +804,20 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m,
   if (!lag) __builtin_amdgcn_s_barrier();
   if constexpr (RS) {
     // r = bf16(z2') Q^T for this tile (the ring is drained: every step's
-    // loads were waited for).  Q chunks c (k in [32 c, 32 c + 32)) go to the
-    // two halves of W2 in the 32-deep layout; the z2' tile fills the other
-    // eight 16 KiB stages, stage c holding columns [32 c, 32 c + 32).
+    // loads were waited for).  Q chunks c (k in [32 c, 32 c + 32) of each
+    // block) go to the two halves of W2 in the 32-deep layout; the z2' tile
+    // fills the other eight 16 KiB stages, stage c holding columns
+    // [32 c, 32 c + 32).  This wave's block starts at stage zb.
+    const int qb = g.qb, nst = qb >> 5;
+    const int zb = ((wn * 64) / qb) * nst;
     __syncthreads();
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(g.Qr, gemm_range_q(bn));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(g.Qr, gemm_range_q(bn, qb));
     int vq[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = (wave * 2 + q) * 16 + (lane >> 2);
       const int cs = (lane & 3) ^ ((r >> 2) & 3);
-      vq[q] = (r * GBN + cs * 8) * 2;
+      vq[q] = (r * qb + cs * 8) * 2;
     }
     auto qload = [&](int c, uint16_t* st) {
 #pragma unroll
@@ -861,11 +867,14 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m,
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) fq[s2] = (uint32_t)((wn * 64 + l32) * 64 + (((2 * s2 + h) ^ sw) << 4));
     }
+    auto zstage = [&](int sg) -> const uint16_t* {
+      return sg == 0 ? R0 : sg == 1 ? R1 : sg == 2 ? R2 : sg == 3 ? R3 : (sg < 6 ? W0 : W1) + (sg & 1) * 8192;
+    };
     auto rfrags = [&](const uint16_t* zs, const uint16_t* qs) {
       typedef int pi32x4 __attribute__((ext_vector_type(4)));
-      const uint32_t zb = (uint32_t)reinterpret_cast<uintptr_t>(zs);
-      const uint32_t qb = (uint32_t)reinterpret_cast<uintptr_t>(qs);
-      const uint32_t a0 = zb + fn[0], a1 = zb + fn[1], b0 = qb + fq[0], b1 = qb + fq[1];
+      const uint32_t zb_ = (uint32_t)reinterpret_cast<uintptr_t>(zs);
+      const uint32_t qb_ = (uint32_t)reinterpret_cast<uintptr_t>(qs);
+      const uint32_t a0 = zb_ + fn[0], a1 = zb_ + fn[1], b0 = qb_ + fq[0], b1 = qb_ + fq[1];
       pi32x4 x[8], y[4];
       asm volatile(
           "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
@@ -891,21 +900,22 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m,
     };
     // chunk 0 in, chunk 1 in flight; the z2' tile written
     PPBAR(2)
-    // step C: z2' stage ZS with Q stage QS; once every wave has read QS,
-    // refill it with chunk C + 2; then wait for chunk C + 1
-#define RSSTEP(C_, ZS, QS)                                                           \
-  {                                                                                  \
-    rfrags(ZS, QS);                                                                  \
-    if ((C_) + 2 < 8) {                                                              \
+    // step C (C < nst, the same for every wave): z2' stage zb + C with Q
+    // stage QS; once every wave has read QS, refill it with chunk C + 2;
+    // then wait for chunk C + 1
+#define RSSTEP(C_, QS)                                                               \
+  if ((C_) < nst) {                                                                  \
+    rfrags(zstage(zb + (C_)), QS);                                                   \
+    if ((C_) + 2 < nst) {                                                            \
       PPBAR(2)                                                                       \
       qload((C_) + 2, QS);                                                           \
       asm volatile("" ::: "memory");                                                 \
     }                                                                                \
     mma();                                                                           \
-    if ((C_) + 2 < 8) PPBAR(2) else PPBAR(0)                                         \
+    if ((C_) + 2 < nst) PPBAR(2) else PPBAR(0)                                       \
   }
-    RSSTEP(0, R0, Q0) RSSTEP(1, R1, Q1) RSSTEP(2, R2, Q0) RSSTEP(3, R3, Q1)
-    RSSTEP(4, W0, Q0) RSSTEP(5, W0 + 8192, Q1) RSSTEP(6, W1, Q0) RSSTEP(7, W1 + 8192, Q1)
+    RSSTEP(0, Q0) RSSTEP(1, Q1) RSSTEP(2, Q0) RSSTEP(3, Q1)
+    RSSTEP(4, Q0) RSSTEP(5, Q1) RSSTEP(6, Q0) RSSTEP(7, Q1)
 #undef RSSTEP
   }
 #undef PPSTEADY
@@ -993,15 +1003,15 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
 }
 
 bool gemm_nt_rside_applies(const void* A, const void* W, const void* Q, const void* C, int64_t M, int64_t N,
-                           int64_t K) {
-  return K % 64 == 0 && K >= 2048 && N % GBN == 0 && M > 0 && N > 0 && gemm_tiled_shape(N, K, K, K, 0, 0) &&
-         aligned8(A) && aligned8(W) && aligned8(Q) && aligned8(C);
+                           int64_t K, int b) {
+  return (b == 64 || b == 128 || b == 256) && K % 64 == 0 && K >= 2048 && N % GBN == 0 && M > 0 && N > 0 &&
+         gemm_tiled_shape(N, K, K, K, 0, 0) && aligned8(A) && aligned8(W) && aligned8(Q) && aligned8(C);
 }
 
 void launch_gemm_nt_rside(const uint16_t* A, const uint16_t* W, const uint16_t* Q, uint16_t* C, int64_t M, int64_t N,
-                          int64_t K, hipStream_t s) {
+                          int64_t K, int b, hipStream_t s) {
   GemmArgs g{};
-  g.A = A; g.B = W; g.C = C; g.Qr = Q;
+  g.A = A; g.B = W; g.C = C; g.Qr = Q; g.qb = b;
   g.M = (int)M; g.N = (int)N; g.K = (int)K;
   g.lda = K; g.ldb = K; g.ldc = N;
   g.batch = 1;

@@ -151,19 +151,21 @@ struct GemmArgs {
   // scale per weight row
   const int8_t* Bq;
   const float* Bs;
-  // R-side blocks (launch_gemm_nt_rside): bf16 [N / 256][256][256]
+  // R-side blocks (launch_gemm_nt_rside): bf16 [N / qb][qb][qb]
   const uint16_t* Qr;
+  int qb;
 };
 void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s);
-// C = Z with every 256-column tile t of Z = A W^T multiplied by block t of
-// Q (C[:, T] = bf16(Z[:, T]) Q_t^T): the forward GEMM and the R-side block
-// product at b = 256 in one launch.  Bit-identical to launch_gemm_bf16
-// followed by the block product.  Takes K a multiple of 64 of at least 2048,
-// N a multiple of 256 and 16-byte aligned operands (gemm_nt_rside_applies).
+// C = Z with every b-column block l of Z = A W^T multiplied by block l of
+// Q (C[:, L] = bf16(Z[:, L]) Q_l^T): the forward GEMM and the R-side block
+// product in one launch.  Bit-identical to launch_gemm_bf16 followed by the
+// block product.  Takes b in {64, 128, 256}, K a multiple of 64 of at least
+// 2048, N a multiple of 256 and 16-byte aligned operands
+// (gemm_nt_rside_applies).
 bool gemm_nt_rside_applies(const void* A, const void* W, const void* Q, const void* C, int64_t M, int64_t N,
-                           int64_t K);
+                           int64_t K, int b);
 void launch_gemm_nt_rside(const uint16_t* A, const uint16_t* W, const uint16_t* Q, uint16_t* C, int64_t M, int64_t N,
-                          int64_t K, hipStream_t s);
+                          int64_t K, int b, hipStream_t s);
 // C = A op(W) with W = bf16(s_i q_ij) formed inside the GEMM from INT8 codes
 // q [rows][cols] and scales s [rows] (NT: W [N][K], rows = N; NN: W [K][N],
 // rows = K).  Returns false (nothing launched) where the tiled kernel does not

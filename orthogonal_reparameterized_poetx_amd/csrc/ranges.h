@@ -47,9 +47,10 @@ POETX_HD inline BufRange gemm_range_b_nn(int64_t n0, int64_t N, int64_t K, int64
   return tile_range(0, K, n0, N - n0, ldb, 2);
 }
 
-// the R-side block multiplying output column tile bn of the fused forward
-// GEMM: rows [256 bn, 256 bn + 256) of the blocks [N / 256 * 256][256]
-POETX_HD inline BufRange gemm_range_q(int64_t bn) { return tile_range(bn * GEMM_TILE, GEMM_TILE, 0, GEMM_TILE, GEMM_TILE, 2); }
+// the R-side blocks multiplying output column tile bn of the fused forward
+// GEMM: the 256 / b blocks of b x b from block 256 bn / b on, which form
+// rows [256 bn, 256 bn + 256) of the blocks viewed as a [N][b] matrix
+POETX_HD inline BufRange gemm_range_q(int64_t bn, int64_t b) { return tile_range(bn * GEMM_TILE, GEMM_TILE, 0, b, b, 2); }
 
 // the same tiles of an INT8 weight (one byte per code)
 POETX_HD inline BufRange gemm_range_bq_nt(int64_t n0, int64_t N, int64_t K, int64_t ldb) {

@@ -17,7 +17,7 @@ class PoetxLayer:
         """w0_int8: keep W0p in the INT8 weight format (per-row codes and
         scales, POETX_W0_INT8; bf16 layers), turned into bf16 inside the
         passes' GEMMs or dequantized by each pass (include/poetx.h says which).
-        separate_block_products: at b = 256, run the forward's R-side block
+        separate_block_products: at b in {64, 128, 256}, run the forward's R-side block
         product as a pass of its own rather than in the epilogue of the GEMM
         before it (POETX_SEPARATE_BLOCK_PRODUCTS; bit-identical results)."""
         self.device = torch.device(device)

@@ -51,11 +51,12 @@ int main() {
       for (long long n0 = 0; n0 < N; n0 += GEMM_TILE)
         if (!within(nn ? gemm_range_b_nn(n0, N, K, ldb) : gemm_range_b_nt(n0, N, K, ldb), extB, "gemm B", buf))
           return 1;
-      // the fused forward (NT, N a multiple of 256): block n0 / 256 of the
-      // R-side blocks [N / 256][256][256]
+      // the fused forward (NT, N a multiple of 256): the blocks of column
+      // tile n0 / 256 among the R-side blocks [N / b][b][b]
       if (!nn && N % GEMM_TILE == 0)
-        for (long long n0 = 0; n0 < N; n0 += GEMM_TILE)
-          if (!within(gemm_range_q(n0 / GEMM_TILE), N * GEMM_TILE, "gemm Q", buf)) return 1;
+        for (long long b = 64; b <= GEMM_TILE; b *= 2)
+          for (long long n0 = 0; n0 < N; n0 += GEMM_TILE)
+            if (!within(gemm_range_q(n0 / GEMM_TILE, b), N * b, "gemm Q", buf)) return 1;
     } else if (!std::strcmp(kind, "bdiag")) {
       if (std::sscanf(buf, "%*s %lld %lld %lld %lld %lld", &a[0], &a[1], &a[2], &a[3], &a[4]) != 5) return 2;
       const long long N = a[0], lda = a[1], ldc = a[2];

@@ -214,25 +214,28 @@ def test_deferred_chain_matches_backward_blocks(shapes, b, N):
         assert torch.equal(aR, dR + dR) and torch.equal(aP, dP + dP)
 
 
-@pytest.mark.parametrize("m,n,N", [
-    (256, 2048, 300),     # one column tile (k and v of the layer set)
-    (768, 2112, 257),     # K = 33 * 64, a ragged token tile
-    (2048, 5632, 333),    # the down projection's K
-    (5632, 2048, 1000),   # 22 column tiles (gate and up)
+@pytest.mark.parametrize("m,n,b,N", [
+    (256, 2048, 256, 300),     # one column tile (k and v of the layer set)
+    (768, 2112, 256, 257),     # K = 33 * 64, a ragged token tile
+    (2048, 5632, 256, 333),    # the down projection's K
+    (5632, 2048, 256, 1000),   # 22 column tiles (gate and up)
+    (1024, 2048, 64, 300),     # four blocks per column tile
+    (1536, 2112, 128, 257),    # two blocks per column tile
+    (2816, 4096, 128, 129),
 ])
-def test_fused_block_products_match_separate_passes(m, n, N):
-    """At b = 256 (no identity tail, K >= 2048) the forward GEMM applies the
-    R-side blocks in its epilogue.  Y equals that of the same layer with
+def test_fused_block_products_match_separate_passes(m, n, b, N):
+    """At b in {64, 128, 256} (no identity tail, K >= 2048) the forward GEMM
+    applies the R-side blocks in its epilogue.  Y equals that of the same layer with
     POETX_SEPARATE_BLOCK_PRODUCTS (GEMM, then the block product) bit for
     bit, and so do the kept-z2' forward and both backward calls (which take
     the two passes either way); for the smaller shapes Y, dX and dL/dQ meet
     the oracle's bounds."""
     torch = torch_mod()
     from orthogonal_reparameterized_poetx_amd import build_layer_blocks
-    inp = WL.small_case(81, m, n, 256, N, dtype="bf16")
+    inp = WL.small_case(81, m, n, b, N, dtype="bf16")
     lay, d = make_layer(inp)
     sep, _ = make_layer(inp, separate_block_products=True)
-    _log("fused block products m=%d n=%d N=%d" % (m, n, N))
+    _log("fused block products m=%d n=%d b=%d N=%d" % (m, n, b, N))
     build_layer_blocks([lay, sep], "forward")
     build_layer_blocks([lay, sep], "backward")
     outs = []
@@ -244,15 +247,15 @@ def test_fused_block_products_match_separate_passes(m, n, N):
         dXz, GRz, GPz = (t.clone() for t in L_.backward_blocks_dq_z2(d["X"], d["gY"], Z2))
         outs.append((lay_y, Yz.clone(), Z2, dX, GR, GP, dXz, GRz, GPz))
     torch.cuda.synchronize()
-    for a, b in zip(*outs):
-        assert torch.equal(a, b)
+    for got, sep_got in zip(*outs):
+        assert torch.equal(got, sep_got)
     Y, dX, GR, GP = outs[0][0], outs[0][3], outs[0][4], outs[0][5]
     if m * n * N <= (1 << 29):
         sigma, tau = oracle_perms(inp, 0)
         W0, thR, thP, X, gY = inp["W0"][1], inp["thR"][1], inp["thP"][1], inp["X"][1], inp["gY"][1]
-        dXr, _, _, it = oracle.backward(W0, thR, thP, sigma, tau, X, gY, 256, contract=True, intermediates=True)
+        dXr, _, _, it = oracle.backward(W0, thR, thP, sigma, tau, X, gY, b, contract=True, intermediates=True)
         fl = layer_floors(W0, it)
-        compare(from_dev(Y), oracle.forward(W0, thR, thP, sigma, tau, X, 256, contract=True), "bf16", "Y",
+        compare(from_dev(Y), oracle.forward(W0, thR, thP, sigma, tau, X, b, contract=True), "bf16", "Y",
                 floor=fl["Y"])
         compare(from_dev(dX), dXr, "bf16", "dX", floor=fl["dX"])
         compare(from_dev(GR), np.array(it["GR"]), "sum", "dL/dQ_R", terms=N)
