@@ -36,11 +36,12 @@ PEAK_HBM_GBS = 8000.0
 # fp32-accurate product from three bf16 products of split operands (hi hi +
 # hi lo + lo hi), so its fp32 flops peak at 2500/3; the Cayley builder's
 # trailing updates take six (three-way splits), so 2500/6
-MFMA_CLASSES = {"gemm_nt": 2500.0, "gemm_nt_rside": 2500.0, "gemm_nn": 2500.0, "cayley_build": 2500.0 / 6,
-                "chain_rule": 2500.0 / 3}
-# the weight products (gemm_nt_rside: the forward's, with the R-side block
-# product of b = 256 in its epilogue; its flops include that product's)
-GEMM_CLASSES = ("gemm_nt", "gemm_nt_rside", "gemm_nn")
+MFMA_CLASSES = {"gemm_nt": 2500.0, "gemm_nt_rside": 2500.0, "gemm_nn": 2500.0, "gemm_nn_rside": 2500.0,
+                "cayley_build": 2500.0 / 6, "chain_rule": 2500.0 / 3}
+# the weight products (gemm_nt_rside / gemm_nn_rside: the forward's, with the
+# R-side block product in its epilogue; their flops include that product's;
+# the NN form reads the transposed weight copy)
+GEMM_CLASSES = ("gemm_nt", "gemm_nt_rside", "gemm_nn", "gemm_nn_rside")
 CU_COUNT = 256
 SIMD_COUNT = 1024   # 256 compute units x 4 SIMDs
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")
@@ -62,6 +63,7 @@ KERNEL_CLASSES = [
     ("gemm_wide_kernel<false, false>", "gemm_nt", 1),
     ("gemm_wide_kernel<false, true>", "gemm_nt_rside", 1),
     ("gemm_wide_kernel<true, false>", "gemm_nn", 1),
+    ("gemm_wide_kernel<true, true>", "gemm_nn_rside", 1),
     ("gemm_bf16_kernel<true, false,", "gemm_nn", 1),
     ("chain_product_kernel", "chain_rule", 3),
     ("skew_project_kernel", "chain_rule", 3),
@@ -165,13 +167,19 @@ def parse():
     ap.add_argument("--w0-int8", action="store_true",
                     help="layer set: base weights stored as per-row INT8 codes and scales (POET-XQ), turned "
                          "into bf16 inside the GEMMs")
+    ap.add_argument("--plain-w0", action="store_true",
+                    help="bf16 base weights as W0p alone; by default W0p also holds its transpose "
+                         "(POETX_W0_TRANSPOSED, 2 more bytes per weight), which the forward products and their "
+                         "recompute read as NN GEMMs (bit-identical results)")
     ap.add_argument("--keep-z2", action="store_true",
                     help="layer set: the variant without activation recompute (the forward keeps z2' for the "
                          "backward, N*m*2 bytes per matrix); the default recomputes it (POET-Xmem)")
     ap.add_argument("--per-layer-builds", action="store_true",
                     help="let every forward / backward call build its own blocks (one builder launch per call) "
                          "instead of one batched build per pass")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.w0_transposed = not (args.plain_w0 or args.w0_int8)
+    return args
 
 
 def kernel_source_hash(files):
@@ -311,17 +319,17 @@ def mfma_from(d):
               % (cls, rec["mfma_flops_per_launch"], rec["mfma_busy_frac"], launches))
 
 
-def run_tag(workload, tokens, w0_int8=False, keep_z2=False):
+def run_tag(workload, tokens, w0_int8=False, keep_z2=False, w0_transposed=False):
     """Names the run a counter record was taken on: workload, tokens and variant."""
-    return "%s, %d tokens (%s weights, activations %s)" % (workload, tokens, "INT8" if w0_int8 else "bf16",
-                                                          "kept" if keep_z2 else "recomputed")
+    w = "INT8" if w0_int8 else "bf16 + transposed" if w0_transposed else "bf16"
+    return "%s, %d tokens (%s weights, activations %s)" % (workload, tokens, w, "kept" if keep_z2 else "recomputed")
 
 
 def profiled_run_tag():
     """The run the committed counter records come from: bench.py's default
-    (the layer set, bf16 weights, recompute)."""
+    (the layer set, bf16 weights with the transposed copy, recompute)."""
     import workloads as WL
-    return run_tag(WL.CONFIGS[3]["name"], WL.CONFIGS[3]["N"])
+    return run_tag(WL.CONFIGS[3]["name"], WL.CONFIGS[3]["N"], w0_transposed=True)
 
 
 def counter_record(kind, cls, tag):
@@ -396,7 +404,8 @@ class Stack:
     can check them; the rest draw the same distributions on the device from a
     torch generator seeded by (config, matrix, stream)."""
 
-    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=(), streams=3, w0_int8=False, merge="sets"):
+    def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=(), streams=3, w0_int8=False, merge="sets",
+                 w0_transposed=False):
         import math
         import numpy as np
         self.P, self.torch, self.N = P, torch, N
@@ -436,7 +445,8 @@ class Stack:
         for l, idx, m, n in mats:
             j = 7 * l + idx
             lay = P.PoetxLayer(m, n, b, "bf16", dev, perm_seed=WL.perm_seed(5, j),
-                               ws_pool=pools[self.where[len(mats_done)]], w0_int8=w0_int8)
+                               ws_pool=pools[self.where[len(mats_done)]], w0_int8=w0_int8,
+                               w0_transposed=w0_transposed)
             mats_done.append(j)
             kR, kP = m // b, n // b
             lay.thR = self.theta[off:off + kR * nt].view(kR, nt)
@@ -566,7 +576,8 @@ def bench_stack(args):
     dev = "cuda:0"
     torch.cuda.set_device(0)
     N = args.tokens or WL.CONFIGS[5]["N"]
-    st = Stack(P, WL, torch, dev, N, streams=args.streams, w0_int8=args.w0_int8, merge=args.merge)
+    st = Stack(P, WL, torch, dev, N, streams=args.streams, w0_int8=args.w0_int8, merge=args.merge,
+               w0_transposed=args.w0_transposed)
     torch.cuda.synchronize()
     resident = torch.cuda.memory_allocated()
     stream = torch.cuda.current_stream()
@@ -601,7 +612,8 @@ def bench_stack(args):
     P.timing_enable(False)
     st.workers, st.side = saved
     per_step = {c: dict(v) for c, v in kern.items()}
-    roof = dominant_roofline(per_step, run_tag(WL.CONFIGS[5]["name"], N, args.w0_int8))
+    roof = dominant_roofline(per_step, run_tag(WL.CONFIGS[5]["name"], N, args.w0_int8,
+                                               w0_transposed=args.w0_transposed))
     cpu = None
     if not args.no_cpu:
         # one layer's seven matrices on the oracle; a stack step runs 24 layers
@@ -614,7 +626,8 @@ def bench_stack(args):
         "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded Gaussian inputs with the stack's shapes)",
         "config": {"workload": WL.CONFIGS[5]["name"], "tokens": N, "matrices": len(st.layers), "b": WL.CONFIGS[5]["b"],
-                   "base_weights": "INT8 codes with per-row fp32 scales (POET-XQ)" if args.w0_int8 else "bf16",
+                   "base_weights": "INT8 codes with per-row fp32 scales (POET-XQ)" if args.w0_int8 else
+                   "bf16 with a transposed copy (POETX_W0_TRANSPOSED)" if args.w0_transposed else "bf16",
                    "merge": "one batched call per stream" if args.merge == "sets" else "one call per matrix"},
         "phases_ms": {"fwd_bwd": round(fb / k, 3), "adam": round(ad / k, 3), "merge": round(mg / k, 3)},
         "generators": st.theta.numel(),
@@ -686,7 +699,7 @@ def main():
     for j in mats:
         inp = WL.matrix_inputs(c, j, N=N, b=b_over)
         lay = P.PoetxLayer(inp["m"], inp["n"], inp["b"], "bf16", dev, perm_seed=inp["perm_seed"],
-                           w0_int8=args.w0_int8)
+                           w0_int8=args.w0_int8, w0_transposed=args.w0_transposed)
         lay.pack(up(inp["W0"], "bf16"))
         lay.thR.copy_(up(inp["thR"], "f32"))
         lay.thP.copy_(up(inp["thP"], "f32"))
@@ -809,7 +822,7 @@ def main():
                         flops=v["flops"] / args.profile_steps, bytes=v["bytes"] / args.profile_steps)
                 for k, v in kern.items()}
     tag = run_tag(cfg["name"] if b_over is None else "%s_b%d" % (cfg["name"], b_over), N, args.w0_int8,
-                  args.keep_z2)
+                  args.keep_z2, args.w0_transposed)
     roof = dominant_roofline(per_step, tag)
     # every class against its own roofline (kernel level: the bytes or flops
     # each launch must move or compute, over its event-timed duration)
@@ -904,7 +917,8 @@ def main():
                    "activations": "z2' kept from the forward pass (no recompute)" if args.keep_z2 else
                    "recomputed in the backward pass (POET-Xmem)",
                    "base_weights": "INT8 codes with per-row fp32 scales, dequantized inside the GEMMs "
-                   "(POET-XQ)" if args.w0_int8 else "bf16"},
+                   "(POET-XQ)" if args.w0_int8 else "bf16 with a transposed copy (POETX_W0_TRANSPOSED)"
+                   if args.w0_transposed else "bf16"},
         "roofline": roof,
         "roofline_classes": classes,
         "roofline_gemms": gemms,

@@ -81,6 +81,8 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
  * of its own instead of in the epilogue of the GEMM before it.  Results are
  * bit-identical either way; for verification. */
 #define POETX_SEPARATE_BLOCK_PRODUCTS 4u
+/* bf16 layers: W0p also holds its transpose (format below) */
+#define POETX_W0_TRANSPOSED 8u
 
 /* op codes for poetx_workspace_bytes */
 #define POETX_OP_FORWARD 0
@@ -97,7 +99,7 @@ typedef struct {
   int32_t b;      /* block size of R and P                                */
   int32_t dtype;  /* poetx_dtype of W0p, X, Y, dY, dX                     */
   uint32_t flags; /* POETX_ACCUMULATE_GRAD, POETX_W0_INT8,
-                     POETX_SEPARATE_BLOCK_PRODUCTS                        */
+                     POETX_SEPARATE_BLOCK_PRODUCTS, POETX_W0_TRANSPOSED   */
   uint32_t reserved; /* must be 0                                         */
 } poetx_layer;
 
@@ -129,7 +131,7 @@ size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op);
  *   s[i] = max_j |w[i][j]| / 127, q[i][j] = clamp(rne(w[i][j] / s[i]), -127, 127)
  * in fp32 (s[i] = 0, q[i] = 0 for a row of zeros).
  *
- * poetx_w0_bytes: bytes of the W0p buffer of this layer (either format);
+ * poetx_w0_bytes: bytes of the W0p buffer of this layer (any format);
  *   0 and the last error set if the layer is invalid.  Host only.
  * poetx_quantize_w0: W0q (INT8 format) from a bf16 [m][n] weight W0bf16 in
  *   the same layout, by the rule above.  Device pointers; no workspace.
@@ -139,6 +141,24 @@ size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op);
 size_t poetx_w0_bytes(const poetx_layer* layer);
 int poetx_quantize_w0(const poetx_layer* layer, const void* W0bf16, void* W0q, void* stream);
 int poetx_dequantize_w0(const poetx_layer* layer, const void* W0q, void* W0bf16, void* stream);
+
+/*
+ * Weight with its transpose (POETX_W0_TRANSPOSED, bf16 layers, not with
+ * POETX_W0_INT8): every W0p argument points to
+ *   bytes [0, 2mn)            bf16 W0p [m][n], working layout, as without the flag
+ *   bytes [off, off + 2mn)    bf16 W0p^T [n][m], off = 2mn rounded up to 256
+ * The forward product z2' = z1' W0p^T (and its recompute in the backward
+ * pass) then reads W0p^T, whose rows run along the output features: the
+ * GEMM's weight operand in the layout of the backward product, which the
+ * GEMM kernels stage faster.  Results are bit-identical to the layer
+ * without the flag [P3 "POET-X: Memory-efficient LLM Training by Scaling
+ * Orthogonal Transformation", Methodologie item 1: the weight-sized product
+ * the input-centric form keeps].  Every merge writes both halves.
+ *
+ * poetx_transpose_w0: writes the second half from the first (after the
+ *   caller has written W0p itself).  POETX_EINVAL without the flag.
+ */
+int poetx_transpose_w0(const poetx_layer* layer, void* W0p, void* stream);
 
 /*
  * One batch of Cayley blocks for poetx_build_block_sets: the generators of

@@ -17,6 +17,7 @@ POETX_BF16 = 1
 POETX_ACCUMULATE_GRAD = 1
 POETX_W0_INT8 = 2
 POETX_SEPARATE_BLOCK_PRODUCTS = 4
+POETX_W0_TRANSPOSED = 8
 OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS, OP_MERGE_BLOCKS, OP_BACKWARD_DQ = range(7)
 
 _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDTYPE",
@@ -29,7 +30,7 @@ EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build
             "poetx_backward_blocks_dq_z2", "poetx_chain_rule_sets",
             "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_merge_blocks_sets",
             "poetx_merge_sets_workspace_bytes", "poetx_make_permutation",
-            "poetx_adam_step", "poetx_w0_bytes", "poetx_quantize_w0", "poetx_dequantize_w0",
+            "poetx_adam_step", "poetx_w0_bytes", "poetx_quantize_w0", "poetx_dequantize_w0", "poetx_transpose_w0",
             "poetx_last_error", "poetx_timing_enable", "poetx_timing_summary")
 
 
@@ -135,6 +136,7 @@ def lib():
         "poetx_w0_bytes": (sz, [LP]),
         "poetx_quantize_w0": (ctypes.c_int, [LP, vp, vp, vp]),
         "poetx_dequantize_w0": (ctypes.c_int, [LP, vp, vp, vp]),
+        "poetx_transpose_w0": (ctypes.c_int, [LP, vp, vp]),
         "poetx_last_error": (ctypes.c_char_p, []),
         "poetx_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "poetx_timing_summary": (ctypes.c_int, [ctypes.c_char_p, sz]),
@@ -203,6 +205,10 @@ def poetx_quantize_w0(layer, W0bf16, W0q, stream=None):
 def poetx_dequantize_w0(layer, W0q, W0bf16, stream=None):
     _check("poetx_dequantize_w0", lib().poetx_dequantize_w0(ctypes.byref(layer), _ptr(W0q), _ptr(W0bf16),
                                                             _stream(stream)))
+
+
+def poetx_transpose_w0(layer, W0p, stream=None):
+    _check("poetx_transpose_w0", lib().poetx_transpose_w0(ctypes.byref(layer), _ptr(W0p), _stream(stream)))
 
 
 def make_workspace(nbytes, device):

@@ -90,10 +90,14 @@ int validate_layer(const poetx_layer* L) {
   if (L->m < 1 || L->m > kMaxDim || L->n < 1 || L->n > kMaxDim)
     return fail(POETX_ESHAPE, "m=%lld n=%lld out of range [1, %lld]", (long long)L->m, (long long)L->n,
                 (long long)kMaxDim);
-  if (L->flags & ~(POETX_ACCUMULATE_GRAD | POETX_W0_INT8 | POETX_SEPARATE_BLOCK_PRODUCTS))
+  if (L->flags & ~(POETX_ACCUMULATE_GRAD | POETX_W0_INT8 | POETX_SEPARATE_BLOCK_PRODUCTS | POETX_W0_TRANSPOSED))
     return fail(POETX_EINVAL, "unknown flags 0x%x", L->flags);
   if ((L->flags & POETX_W0_INT8) && L->dtype != POETX_BF16)
     return fail(POETX_EDTYPE, "POETX_W0_INT8 applies to bf16 layers");
+  if ((L->flags & POETX_W0_TRANSPOSED) && L->dtype != POETX_BF16)
+    return fail(POETX_EDTYPE, "POETX_W0_TRANSPOSED applies to bf16 layers");
+  if ((L->flags & POETX_W0_TRANSPOSED) && (L->flags & POETX_W0_INT8))
+    return fail(POETX_EINVAL, "POETX_W0_TRANSPOSED and POETX_W0_INT8 exclude each other");
   return POETX_OK;
 }
 
@@ -332,6 +336,7 @@ struct Shape {
   bool f32;
   bool q8;    // W0p holds INT8 codes and per-row scales (POETX_W0_INT8)
   bool sep;   // POETX_SEPARATE_BLOCK_PRODUCTS
+  bool tr;    // W0p followed by its transpose (POETX_W0_TRANSPOSED)
   size_t es;  // element size of activations / weight
 };
 
@@ -343,12 +348,15 @@ Shape shape_of(const poetx_layer* L, int64_t N) {
   S.f32 = L->dtype == POETX_F32;
   S.q8 = (L->flags & POETX_W0_INT8) != 0;
   S.sep = (L->flags & POETX_SEPARATE_BLOCK_PRODUCTS) != 0;
+  S.tr = (L->flags & POETX_W0_TRANSPOSED) != 0;
   S.es = S.f32 ? 4 : 2;
   return S;
 }
 
 // INT8 weight format: codes [m][n], then fp32 scales [m] at this byte offset
 size_t w0_scale_offset(int64_t m, int64_t n) { return ((size_t)m * n + kAlign - 1) / kAlign * kAlign; }
+// transposed weight format: bf16 [m][n], then bf16 [n][m] at this byte offset
+size_t w0t_offset(int64_t m, int64_t n) { return ((size_t)m * n * 2 + kAlign - 1) / kAlign * kAlign; }
 
 // INT8 layers whose shapes the fused GEMM takes: the weight products can read
 // the codes and scales directly (bf16(s q) formed inside the GEMM)
@@ -369,6 +377,7 @@ struct Wop {
   const void* bf;
   const int8_t* q;
   const float* sc;
+  const void* bt;   // bf16 [n][m], the transposed copy (POETX_W0_TRANSPOSED), or null
 };
 
 // the bf16 weight a pass reads: W0p itself, or (INT8 layers) its codes
@@ -385,6 +394,7 @@ const void* weight_for_pass(const Shape& S, const void* W0p, void* w0, hipStream
 // w0 == nullptr: no room for a dequantized copy (the layer then reads its
 // codes directly; callers check q8_direct first)
 Wop weight_operand(const Shape& S, const void* W0p, void* w0, hipStream_t s) {
+  if (S.tr) return Wop{W0p, nullptr, nullptr, static_cast<const char*>(W0p) + w0t_offset(S.m, S.n)};
   if (!(q8_fused(S) || (!w0 && q8_direct(S)))) return Wop{weight_for_pass(S, W0p, w0, s), nullptr, nullptr};
   const int8_t* q = static_cast<const int8_t*>(W0p);
   const float* sc = reinterpret_cast<const float*>(static_cast<const char*>(W0p) + w0_scale_offset(S.m, S.n));
@@ -629,23 +639,27 @@ int fwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
   if ((rc = gather_blockmul(X, tau, q.qbP, w.sc, w.z1, nullptr, N, n, S.b, S.kP, S.es, s))) return rc;
   // z2' = z1' W0p^T
   void* const z2 = z2out ? z2out : w.z2;
+  // with the transposed copy the product is NN, z2' = z1' (W0p^T) with the
+  // weight's output features along its contiguous rows; else NT on W0p.
   // b of 64 to 256 without an identity tail, z2' not kept: the R-side block
   // product in the GEMM's epilogue, r = D_R z2' straight into sc
   // (bit-identical to the two passes below)
+  const bool tn = W0.bt != nullptr;
+  const uint16_t* const Wf = static_cast<const uint16_t*>(tn ? W0.bt : W0.bf);
   if (!z2out && !S.sep && !W0.q && (int64_t)S.kR * S.b == m &&
-      gemm_nt_rside_applies(w.z1, W0.bf, q.qbR, w.sc, N, S.m, S.n, S.b)) {
+      gemm_rside_applies(tn, w.z1, Wf, q.qbR, w.sc, N, S.m, S.n, S.b)) {
     {
-      Tm tm(s, "gemm_nt_rside", 2.0 * N * S.m * S.n + xf_flops(N, S.kR, S.b),
+      Tm tm(s, tn ? "gemm_nn_rside" : "gemm_nt_rside", 2.0 * N * S.m * S.n + xf_flops(N, S.kR, S.b),
             (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-      launch_gemm_nt_rside((const uint16_t*)w.z1, (const uint16_t*)W0.bf, q.qbR, (uint16_t*)w.sc, N, S.m, S.n, S.b,
-                           s);
+      launch_gemm_rside(tn, (const uint16_t*)w.z1, Wf, q.qbR, (uint16_t*)w.sc, N, S.m, S.n, S.b, s);
     }
     if ((rc = check_launch("forward GEMM with the R-side blocks"))) return rc;
     return permute(false, w.sc, z2, Y, nullptr, sigma, N, m, S.kR * S.b, S.es, s);
   }
   {
-    Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-    if ((rc = weight_gemm(false, (const uint16_t*)w.z1, W0, (uint16_t*)z2, N, S.m, S.n, s))) return rc;
+    Tm tm(s, tn ? "gemm_nn" : "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+    if (tn) launch_gemm_bf16(true, (const uint16_t*)w.z1, Wf, (uint16_t*)z2, N, S.m, S.n, s);
+    else if ((rc = weight_gemm(false, (const uint16_t*)w.z1, W0, (uint16_t*)z2, N, S.m, S.n, s))) return rc;
   }
   if ((rc = check_launch("forward GEMM"))) return rc;
   // y = Pi_sigma^T r with r = D_R z2' (the tail of r is the tail of z2')
@@ -692,8 +706,12 @@ int bwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
       if ((rc = permute(true, X, nullptr, w.xg, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
     } else {
       if ((rc = gather_blockmul(X, tau, q.qbP, nullptr, w.z1, w.xg, N, n, S.b, S.kP, S.es, s))) return rc;
-      Tm tm(s, "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
-      if ((rc = weight_gemm(false, (const uint16_t*)w.z1, W0, (uint16_t*)w.z2, N, S.m, S.n, s))) return rc;
+      // NN on the transposed copy when there is one, as in the forward pass
+      Tm tm(s, W0.bt ? "gemm_nn" : "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
+      if (W0.bt)
+        launch_gemm_bf16(true, (const uint16_t*)w.z1, static_cast<const uint16_t*>(W0.bt), (uint16_t*)w.z2, N, S.m,
+                         S.n, s);
+      else if ((rc = weight_gemm(false, (const uint16_t*)w.z1, W0, (uint16_t*)w.z2, N, S.m, S.n, s))) return rc;
     }
     if ((rc = check_launch("recompute"))) return rc;
     // R side: gY' = Pi_sigma gY (kept), gz2' = D_R^T gY' (blocks Q_R^T)
@@ -862,9 +880,23 @@ int merge_core(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, 
 
 // merge of the layer's stored weight: INT8 layers merge their dequantized
 // weight in the workspace and store its new codes and scales
+// the transposed copy of a merged weight (POETX_W0_TRANSPOSED)
+int refresh_transpose(const Shape& S, void* W0p, hipStream_t s) {
+  if (!S.tr) return POETX_OK;
+  {
+    Tm tm(s, "transpose", 0.0, 4.0 * S.m * S.n);
+    launch_transpose_bf16(static_cast<const uint16_t*>(W0p),
+                          reinterpret_cast<uint16_t*>(static_cast<char*>(W0p) + w0t_offset(S.m, S.n)), S.m, S.n, s);
+  }
+  return check_launch("weight transpose");
+}
+
 int merge_w0(const Shape& S, void* W0p, const Blk& q, float* thR, float* thP, int32_t* sigma, int32_t* tau,
              uint64_t seed, uint64_t merge_index, const MrgWs& w, hipStream_t s) {
-  if (!S.q8) return merge_core(S, W0p, q, thR, thP, sigma, tau, seed, merge_index, w, s);
+  if (!S.q8) {
+    const int rc = merge_core(S, W0p, q, thR, thP, sigma, tau, seed, merge_index, w, s);
+    return rc ? rc : refresh_transpose(S, W0p, s);
+  }
   weight_for_pass(S, W0p, w.w0, s);
   int rc = merge_core(S, w.w0, q, thR, thP, sigma, tau, seed, merge_index, w, s);
   if (rc) return rc;
@@ -1450,6 +1482,8 @@ int poetx_merge_blocks_sets(const poetx_merge_set* sets, int32_t count, void* ws
     }
     launch_zero_generators_batch(b, s);
     if ((rc = check_launch("batched merge"))) return rc;
+    for (int i = 0; i < b.count; ++i)
+      if ((rc = refresh_transpose(S[batched[c0 + i]], sets[batched[c0 + i]].W0p, s))) return rc;
   }
   return POETX_OK;
 }
@@ -1458,7 +1492,17 @@ size_t poetx_w0_bytes(const poetx_layer* layer) {
   if (validate_layer(layer) != POETX_OK) return 0;
   const Shape S = shape_of(layer, 0);
   if (S.q8) return w0_scale_offset(S.m, S.n) + (size_t)S.m * sizeof(float);
+  if (S.tr) return w0t_offset(S.m, S.n) + (size_t)S.m * S.n * 2;
   return (size_t)S.m * S.n * S.es;
+}
+
+int poetx_transpose_w0(const poetx_layer* layer, void* W0p, void* stream) {
+  int rc = validate_layer(layer);
+  if (rc) return rc;
+  const Shape S = shape_of(layer, 0);
+  if (!S.tr) return fail(POETX_EINVAL, "layer.flags lacks POETX_W0_TRANSPOSED");
+  if (!W0p) return fail(POETX_EINVAL, "NULL tensor argument");
+  return refresh_transpose(S, W0p, static_cast<hipStream_t>(stream));
 }
 
 int poetx_quantize_w0(const poetx_layer* layer, const void* W0bf16, void* W0q, void* stream) {

@@ -531,8 +531,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_generic_kernel(GemmArgs g) {
 // even step one 64-deep stage (stage t / 2 + 2).  k is summed in the same
 // order as in the kernel above, so the results are identical.
 //
-// RS (NT only): the forward's R-side block product in the epilogue, for b
-// in {64, 128, 256}.  A 256-column output tile holds 256 / b whole blocks,
+// RS: the forward's R-side block product in the epilogue, for b in
+// {64, 128, 256}; NT reads W0p [m][n], NN its transposed copy [n][m].  A 256-column output tile holds 256 / b whole blocks,
 // and each wave's 64 columns lie inside one of them.  The tile, rounded to
 // bf16 as z2' is, goes into the LDS as the A operand of an NT product with
 // the tile's blocks (B operand: rows = output features; the blocks, one
@@ -860,12 +860,16 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m,
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    // fragment offsets: z2' rows as in the ring (fn), block rows 64 wn + l32
-    uint32_t fq[2];
+    // fragment offsets in the 32-deep layout: z2' rows 128 wm + l32 (fz),
+    // block rows 64 wn + l32 (fq)
+    uint32_t fz[2], fq[2];
     {
       const int l32 = lane & 31, h = lane >> 5, sw = (l32 >> 2) & 3;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) fq[s2] = (uint32_t)((wn * 64 + l32) * 64 + (((2 * s2 + h) ^ sw) << 4));
+      for (int s2 = 0; s2 < 2; ++s2) {
+        fz[s2] = (uint32_t)((wm * 128 + l32) * 64 + (((2 * s2 + h) ^ sw) << 4));
+        fq[s2] = (uint32_t)((wn * 64 + l32) * 64 + (((2 * s2 + h) ^ sw) << 4));
+      }
     }
     auto zstage = [&](int sg) -> const uint16_t* {
       return sg == 0 ? R0 : sg == 1 ? R1 : sg == 2 ? R2 : sg == 3 ? R3 : (sg < 6 ? W0 : W1) + (sg & 1) * 8192;
@@ -874,7 +878,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g, int tiles_m,
       typedef int pi32x4 __attribute__((ext_vector_type(4)));
       const uint32_t zb_ = (uint32_t)reinterpret_cast<uintptr_t>(zs);
       const uint32_t qb_ = (uint32_t)reinterpret_cast<uintptr_t>(qs);
-      const uint32_t a0 = zb_ + fn[0], a1 = zb_ + fn[1], b0 = qb_ + fq[0], b1 = qb_ + fq[1];
+      const uint32_t a0 = zb_ + fz[0], a1 = zb_ + fz[1], b0 = qb_ + fq[0], b1 = qb_ + fq[1];
       pi32x4 x[8], y[4];
       asm volatile(
           "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
@@ -1002,23 +1006,24 @@ void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s) {
   }
 }
 
-bool gemm_nt_rside_applies(const void* A, const void* W, const void* Q, const void* C, int64_t M, int64_t N,
-                           int64_t K, int b) {
+bool gemm_rside_applies(bool nn, const void* A, const void* W, const void* Q, const void* C, int64_t M, int64_t N,
+                        int64_t K, int b) {
   return (b == 64 || b == 128 || b == 256) && K % 64 == 0 && K >= 2048 && N % GBN == 0 && M > 0 && N > 0 &&
-         gemm_tiled_shape(N, K, K, K, 0, 0) && aligned8(A) && aligned8(W) && aligned8(Q) && aligned8(C);
+         gemm_tiled_shape(N, K, K, nn ? N : K, 0, 0) && aligned8(A) && aligned8(W) && aligned8(Q) && aligned8(C);
 }
 
-void launch_gemm_nt_rside(const uint16_t* A, const uint16_t* W, const uint16_t* Q, uint16_t* C, int64_t M, int64_t N,
-                          int64_t K, int b, hipStream_t s) {
+void launch_gemm_rside(bool nn, const uint16_t* A, const uint16_t* W, const uint16_t* Q, uint16_t* C, int64_t M,
+                       int64_t N, int64_t K, int b, hipStream_t s) {
   GemmArgs g{};
   g.A = A; g.B = W; g.C = C; g.Qr = Q; g.qb = b;
   g.M = (int)M; g.N = (int)N; g.K = (int)K;
-  g.lda = K; g.ldb = K; g.ldc = N;
+  g.lda = K; g.ldb = nn ? N : K; g.ldc = N;
   g.batch = 1;
   const int tn = (int)(N / GBN), tm = (g.M + GBM - 1) / GBM;
   const int nt = tn * tm;
   const int grid = ((nt + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_wide_kernel<false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+  if (nn) hipLaunchKernelGGL((gemm_wide_kernel<true, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
+  else hipLaunchKernelGGL((gemm_wide_kernel<false, true>), dim3(grid), dim3(512), 0, s, g, tm, tn, nt);
 }
 
 bool launch_gemm_q8(bool nn, const uint16_t* A, const int8_t* codes, const float* scales, uint16_t* C, int64_t M,

@@ -156,16 +156,18 @@ struct GemmArgs {
   int qb;
 };
 void launch_gemm_bf16(bool nn, const GemmArgs& g, hipStream_t s);
-// C = Z with every b-column block l of Z = A W^T multiplied by block l of
-// Q (C[:, L] = bf16(Z[:, L]) Q_l^T): the forward GEMM and the R-side block
-// product in one launch.  Bit-identical to launch_gemm_bf16 followed by the
-// block product.  Takes b in {64, 128, 256}, K a multiple of 64 of at least
-// 2048, N a multiple of 256 and 16-byte aligned operands
-// (gemm_nt_rside_applies).
-bool gemm_nt_rside_applies(const void* A, const void* W, const void* Q, const void* C, int64_t M, int64_t N,
-                           int64_t K, int b);
-void launch_gemm_nt_rside(const uint16_t* A, const uint16_t* W, const uint16_t* Q, uint16_t* C, int64_t M, int64_t N,
-                          int64_t K, int b, hipStream_t s);
+// C = Z with every b-column block l of Z = A op(W) (W^T for NT, W for NN)
+// multiplied by block l of Q (C[:, L] = bf16(Z[:, L]) Q_l^T): the forward
+// GEMM and the R-side block product in one launch.  Bit-identical to
+// launch_gemm_bf16 followed by the block product.  Takes b in {64, 128,
+// 256}, K a multiple of 64 of at least 2048, N a multiple of 256 and 16-byte
+// aligned operands (gemm_rside_applies).
+bool gemm_rside_applies(bool nn, const void* A, const void* W, const void* Q, const void* C, int64_t M, int64_t N,
+                        int64_t K, int b);
+void launch_gemm_rside(bool nn, const uint16_t* A, const uint16_t* W, const uint16_t* Q, uint16_t* C, int64_t M,
+                       int64_t N, int64_t K, int b, hipStream_t s);
+// out [n][m] = in [m][n]^T, bf16 (the transposed weight copy)
+void launch_transpose_bf16(const uint16_t* in, uint16_t* out, int64_t m, int64_t n, hipStream_t s);
 // C = A op(W) with W = bf16(s_i q_ij) formed inside the GEMM from INT8 codes
 // q [rows][cols] and scales s [rows] (NT: W [N][K], rows = N; NN: W [K][N],
 // rows = K).  Returns false (nothing launched) where the tiled kernel does not

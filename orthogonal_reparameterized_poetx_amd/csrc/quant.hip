@@ -1,3 +1,7 @@
+// Weight storage formats.  The transposed copy: bf16 W0p [m][n] written as
+// [n][m] beside it, so that the forward products can read the weight with
+// its output features along the rows' contiguous direction.
+//
 // POET-XQ weight storage: the frozen base weight kept as INT8 codes with one
 // fp32 scale per row and dequantized to bf16 for each pass that reads it
 // [P3 "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
@@ -75,6 +79,65 @@ void launch_dequant_rows(const int8_t* q, const float* sc, uint16_t* w, int64_t 
 void launch_quantize_rows(const uint16_t* w, int8_t* q, float* sc, int64_t m, int64_t n, hipStream_t s) {
   if (m <= 0 || n <= 0) return;
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)m), dim3(256), 0, s, w, q, sc, n);
+}
+
+// out[c][r] = in[r][c] for a 64 x 64 tile through LDS (pitch 66 elements):
+// 16-byte loads of input rows and 16-byte stores of output rows where the
+// rows are 8-element aligned and the chunk lies inside (vin / vout), element
+// by element at ragged edges
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                             int64_t m, int64_t n, int vin, int vout) {
+  __shared__ uint16_t t[64][66];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int id = tid + 256 * h, row = id >> 3, ch = id & 7;
+    const int64_t gr = r0 + row, gc = c0 + ch * 8;
+    uint16_t v[8];
+    if (vin && gr < m && gc + 8 <= n) {
+      const uint4 x = *reinterpret_cast<const uint4*>(in + gr * n + gc);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (gr < m && gc + e < n) ? in[gr * n + gc + e] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[row][ch * 8 + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int id = tid + 256 * h, col = id >> 3, ch = id & 7;
+    const int64_t oc = c0 + col, orr = r0 + ch * 8;   // output row oc, columns orr ..
+    if (oc >= n) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = t[ch * 8 + e][col];
+    uint16_t* dst = out + oc * m + orr;
+    if (vout && orr + 8 <= m) {
+      uint4 x;
+      x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+      x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+      x.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+      x.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+      *reinterpret_cast<uint4*>(dst) = x;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (orr + e < m) dst[e] = v[e];
+    }
+  }
+}
+
+void launch_transpose_bf16(const uint16_t* in, uint16_t* out, int64_t m, int64_t n, hipStream_t s) {
+  if (m <= 0 || n <= 0) return;
+  const int vin = n % 8 == 0 && (reinterpret_cast<uintptr_t>(in) & 15) == 0;
+  const int vout = m % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, in, out, m, n, vin, vout);
 }
 
 }  // namespace poetx

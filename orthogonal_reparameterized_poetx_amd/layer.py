@@ -13,23 +13,29 @@ from . import _lib as L
 
 class PoetxLayer:
     def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0, ws_pool=None, w0_int8=False,
-                 separate_block_products=False):
+                 separate_block_products=False, w0_transposed=False):
         """w0_int8: keep W0p in the INT8 weight format (per-row codes and
         scales, POETX_W0_INT8; bf16 layers), turned into bf16 inside the
         passes' GEMMs or dequantized by each pass (include/poetx.h says which).
         separate_block_products: at b in {64, 128, 256}, run the forward's R-side block
         product as a pass of its own rather than in the epilogue of the GEMM
-        before it (POETX_SEPARATE_BLOCK_PRODUCTS; bit-identical results)."""
+        before it (POETX_SEPARATE_BLOCK_PRODUCTS; bit-identical results).
+        w0_transposed: W0p also holds its transpose, which the forward
+        products read (POETX_W0_TRANSPOSED; bf16 layers; 2 more bytes per
+        weight; bit-identical results)."""
         self.device = torch.device(device)
         self.dt = L.POETX_BF16 if dtype == "bf16" else L.POETX_F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.flags = (L.POETX_W0_INT8 if w0_int8 else 0) | \
-            (L.POETX_SEPARATE_BLOCK_PRODUCTS if separate_block_products else 0)
+            (L.POETX_SEPARATE_BLOCK_PRODUCTS if separate_block_products else 0) | \
+            (L.POETX_W0_TRANSPOSED if w0_transposed else 0)
         self.layer = L.Layer(m, n, b, self.dt, self.flags)
         self.m, self.n, self.b = m, n, b
         nt = b * (b - 1) // 2
         if w0_int8:
             self.W0p = torch.zeros(L.w0_bytes(self.layer), dtype=torch.uint8, device=self.device)
+        elif w0_transposed:
+            self.W0p = torch.zeros(L.w0_bytes(self.layer) // 2, dtype=self.tdtype, device=self.device)
         else:
             self.W0p = torch.zeros(m, n, dtype=self.tdtype, device=self.device)
         self.thR = torch.zeros(m // b, nt, dtype=torch.float32, device=self.device)
@@ -63,7 +69,8 @@ class PoetxLayer:
         if self.flags & L.POETX_W0_INT8:
             L.poetx_quantize_w0(self.layer, W0.to(self.tdtype).contiguous(), self.W0p)
         else:
-            self.W0p.copy_(W0.to(self.tdtype))
+            # (the merge below also writes the transposed copy)
+            self.weight().copy_(W0.to(self.tdtype))
         self.thR.zero_()
         self.thP.zero_()
         self.sigma.copy_(torch.arange(self.m, dtype=torch.int32, device=self.device))
@@ -203,11 +210,18 @@ class PoetxLayer:
 
     def weight(self):
         """The bf16 working-layout weight the passes use ([m][n])."""
+        if self.flags & L.POETX_W0_TRANSPOSED:
+            return self.W0p[:self.m * self.n].view(self.m, self.n)
         if not self.flags & L.POETX_W0_INT8:
             return self.W0p
         W = torch.empty(self.m, self.n, dtype=torch.bfloat16, device=self.device)
         L.poetx_dequantize_w0(self.layer, self.W0p, W)
         return W
+
+    def weight_t(self):
+        """The transposed copy [n][m] of a POETX_W0_TRANSPOSED layer."""
+        off = L.w0_bytes(self.layer) // 2 - self.m * self.n
+        return self.W0p[off:off + self.m * self.n].view(self.n, self.m)
 
     def merge_blocks(self, stream=None, ws=None):
         """Merge with blocks from build_layer_blocks(..., "merge"); ws: a merge

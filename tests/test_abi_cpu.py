@@ -58,11 +58,24 @@ def test_argument_validation_on_host():
     assert ws_need > 0
     # bad block size, dtype, shape, flags, reserved
     for lay, code in [(P.Layer(256, 256, 48), -1), (P.Layer(256, 256, 32, 7), -3), (P.Layer(0, 256, 32), -2),
-                      (P.Layer(256, 40000, 32), -2), (P.Layer(256, 256, 32, P.POETX_BF16, 8), -1)]:
+                      (P.Layer(256, 40000, 32), -2), (P.Layer(256, 256, 32, P.POETX_BF16, 16), -1),
+                      (P.Layer(256, 256, 32, P.POETX_F32, P.POETX_W0_TRANSPOSED), -3),
+                      (P.Layer(256, 256, 32, P.POETX_BF16, P.POETX_W0_TRANSPOSED | P.POETX_W0_INT8), -1)]:
         rc = L.poetx_forward(ctypes.byref(lay), fake, fake, fake, fake, fake, fake, 64, fake, fake, ws_need, None)
         assert rc == code, (rc, P.last_error())
         assert P.last_error()
         assert L.poetx_workspace_bytes(ctypes.byref(lay), 64, 0) == 0
+    # the transposed weight format: W0p, then its transpose 256-byte aligned;
+    # the transpose call wants the flag and a weight
+    tl = P.Layer(600, 520, 64, P.POETX_BF16, P.POETX_W0_TRANSPOSED)
+    assert P.w0_bytes(tl) == -(-600 * 520 * 2 // 256) * 256 + 600 * 520 * 2
+    assert P.w0_bytes(P.Layer(600, 520, 64, P.POETX_BF16)) == 600 * 520 * 2
+    assert L.poetx_transpose_w0(ctypes.byref(P.Layer(600, 520, 64, P.POETX_BF16)), fake, None) == -1
+    assert "POETX_W0_TRANSPOSED" in P.last_error()
+    assert L.poetx_transpose_w0(ctypes.byref(tl), None, None) == -1
+    for op in range(7):
+        assert L.poetx_workspace_bytes(ctypes.byref(tl), 64, op) == L.poetx_workspace_bytes(
+            ctypes.byref(P.Layer(600, 520, 64, P.POETX_BF16)), 64, op) > 0
     # POETX_SEPARATE_BLOCK_PRODUCTS is a known flag and changes no workspace size
     sep = P.Layer(2048, 2048, 256, P.POETX_BF16, P.POETX_SEPARATE_BLOCK_PRODUCTS)
     plain = P.Layer(2048, 2048, 256, P.POETX_BF16)

@@ -77,6 +77,7 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert bench.counter_record("traffic", "gemm_nt", bench.run_tag("llama1b_layerset_bf16_b256", 4096)) is None
     assert bench.counter_record("traffic", "gemm_nt", bench.run_tag("llama1b_layerset_bf16_b256", 8192,
                                                                       w0_int8=True)) is None
+    assert bench.counter_record("traffic", "gemm_nt", bench.run_tag("llama1b_layerset_bf16_b256", 8192)) is None
 
 
 def test_traffic_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
