@@ -378,6 +378,11 @@ struct Wop {
   const int8_t* q;
   const float* sc;
   const void* bt;   // bf16 [n][m], the transposed copy (POETX_W0_TRANSPOSED), or null
+  // INT8 layers dequantized per pass with bt the dequantized copy, transposed,
+  // in buf: the codes (W0p) and buf, for the [m][n] copy the backward product
+  // takes afterwards in the same buffer
+  const void* q8src;
+  void* q8buf;
 };
 
 // the bf16 weight a pass reads: W0p itself, or (INT8 layers) its codes
@@ -392,9 +397,21 @@ const void* weight_for_pass(const Shape& S, const void* W0p, void* w0, hipStream
 }
 
 // w0 == nullptr: no room for a dequantized copy (the layer then reads its
-// codes directly; callers check q8_direct first)
-Wop weight_operand(const Shape& S, const void* W0p, void* w0, hipStream_t s) {
+// codes directly; callers check q8_direct first).  fwd_product: the pass runs
+// the forward product z1' W0p^T, which an INT8 layer dequantized per pass
+// then reads from a transposed copy as an NN GEMM, as a layer with
+// POETX_W0_TRANSPOSED does (bit-identical either way)
+Wop weight_operand(const Shape& S, const void* W0p, void* w0, hipStream_t s, bool fwd_product = true) {
   if (S.tr) return Wop{W0p, nullptr, nullptr, static_cast<const char*>(W0p) + w0t_offset(S.m, S.n)};
+  if (S.q8 && w0 && fwd_product && !q8_fused(S)) {
+    const int8_t* q = static_cast<const int8_t*>(W0p);
+    const float* sc = reinterpret_cast<const float*>(static_cast<const char*>(W0p) + w0_scale_offset(S.m, S.n));
+    {
+      Tm tm(s, "dequant", 0.0, (double)S.m * S.n * 3);
+      launch_dequant_transpose(q, sc, static_cast<uint16_t*>(w0), S.m, S.n, s);
+    }
+    return Wop{nullptr, nullptr, nullptr, w0, W0p, w0};
+  }
   if (!(q8_fused(S) || (!w0 && q8_direct(S)))) return Wop{weight_for_pass(S, W0p, w0, s), nullptr, nullptr};
   const int8_t* q = static_cast<const int8_t*>(W0p);
   const float* sc = reinterpret_cast<const float*>(static_cast<const char*>(W0p) + w0_scale_offset(S.m, S.n));
@@ -727,9 +744,16 @@ int bwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
   // gz1' = gz2' W0p (into the z1' buffer)
   void* gz1 = w.z1;
   {
+    // an INT8 layer whose buffer held the transposed copy for the recompute
+    // takes its [m][n] dequantized copy there now
+    Wop Wn = W0;
+    if (W0.q8src) {
+      Wn.bf = weight_for_pass(S, W0.q8src, W0.q8buf, s);
+      Wn.bt = nullptr;
+    }
     Tm tm(s, S.f32 ? "gemm_fp32" : "gemm_nn", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
     if (S.f32) launch_gemm_f32(true, (const float*)w.gz2, (const float*)W0.bf, (float*)gz1, N, S.n, S.m, s);
-    else if ((rc = weight_gemm(true, (const uint16_t*)w.gz2, W0, (uint16_t*)gz1, N, S.n, S.m, s))) return rc;
+    else if ((rc = weight_gemm(true, (const uint16_t*)w.gz2, Wn, (uint16_t*)gz1, N, S.n, S.m, s))) return rc;
   }
   // G_P = gz1'^T x' per block
   {
@@ -952,8 +976,8 @@ int backward_dq_impl(const poetx_layer* layer, const void* W0p, const poetx_bloc
   plan_bwd(S, false, nullptr, &need, true);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const BwdWs w = plan_bwd(S, false, ws, &need, true);
-  return bwd_core(S, weight_operand(S, W0p, w.w0, s), blk_of(blocks), sigma, tau, X, dY, dX, nullptr, nullptr,
-                  false, w, s, GR, GP, Z2);
+  return bwd_core(S, weight_operand(S, W0p, w.w0, s, Z2 == nullptr), blk_of(blocks), sigma, tau, X, dY, dX, nullptr,
+                  nullptr, false, w, s, GR, GP, Z2);
 }
 
 // ---- allocation-free forward: intermediates in a file-scope device array

@@ -168,6 +168,8 @@ void launch_gemm_rside(bool nn, const uint16_t* A, const uint16_t* W, const uint
                        int64_t N, int64_t K, int b, hipStream_t s);
 // out [n][m] = in [m][n]^T, bf16 (the transposed weight copy)
 void launch_transpose_bf16(const uint16_t* in, uint16_t* out, int64_t m, int64_t n, hipStream_t s);
+// out [n][m] = the dequantized INT8 weight [m][n], transposed
+void launch_dequant_transpose(const int8_t* q, const float* sc, uint16_t* out, int64_t m, int64_t n, hipStream_t s);
 // C = A op(W) with W = bf16(s_i q_ij) formed inside the GEMM from INT8 codes
 // q [rows][cols] and scales s [rows] (NT: W [N][K], rows = N; NN: W [K][N],
 // rows = K).  Returns false (nothing launched) where the tiled kernel does not

@@ -81,10 +81,39 @@ void launch_quantize_rows(const uint16_t* w, int8_t* q, float* sc, int64_t m, in
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)m), dim3(256), 0, s, w, q, sc, n);
 }
 
+// writes the 64 x 64 tile t (rows r0.., columns c0.. of an [m][n] matrix)
+// transposed into out [n][m]: 16-byte stores of output rows where they are
+// 8-element aligned and inside (vout), element by element at ragged edges
+__device__ __forceinline__ void store_tile_transposed(const uint16_t (*t)[66], uint16_t* __restrict__ out, int64_t r0,
+                                                      int64_t c0, int64_t m, int64_t n, int vout) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int id = tid + 256 * h, col = id >> 3, ch = id & 7;
+    const int64_t oc = c0 + col, orr = r0 + ch * 8;   // output row oc, columns orr ..
+    if (oc >= n) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = t[ch * 8 + e][col];
+    uint16_t* dst = out + oc * m + orr;
+    if (vout && orr + 8 <= m) {
+      uint4 x;
+      x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+      x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+      x.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+      x.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+      *reinterpret_cast<uint4*>(dst) = x;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (orr + e < m) dst[e] = v[e];
+    }
+  }
+}
+
 // out[c][r] = in[r][c] for a 64 x 64 tile through LDS (pitch 66 elements):
-// 16-byte loads of input rows and 16-byte stores of output rows where the
-// rows are 8-element aligned and the chunk lies inside (vin / vout), element
-// by element at ragged edges
+// 16-byte loads of input rows where they are 8-element aligned and the chunk
+// lies inside (vin), element by element at ragged edges
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
                                                              int64_t m, int64_t n, int vin, int vout) {
   __shared__ uint16_t t[64][66];
@@ -108,28 +137,56 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
     for (int e = 0; e < 8; ++e) t[row][ch * 8 + e] = v[e];
   }
   __syncthreads();
+  store_tile_transposed(t, out, r0, c0, m, n, vout);
+}
+
+// out [n][m] = bf16(s_i q[i][j]) transposed: the dequantized weight of an INT8
+// layer in the layout of the transposed copy (same rounding as
+// dequant_rows_kernel); 16 codes per thread where rows are 16-byte aligned
+// (vin), one per thread otherwise
+__global__ __launch_bounds__(256) void dequant_transpose_kernel(const int8_t* __restrict__ q,
+                                                                const float* __restrict__ sc,
+                                                                uint16_t* __restrict__ out, int64_t m, int64_t n,
+                                                                int vin, int vout) {
+  __shared__ uint16_t t[64][66];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  if (vin) {
+    const int row = tid >> 2, cc = (tid & 3) * 16;
+    const int64_t gr = r0 + row, gc = c0 + cc;
+    uint16_t v[16];
+    if (gr < m && gc + 16 <= n) {
+      const float s = sc[gr];
+      const uint4 x = *reinterpret_cast<const uint4*>(q + gr * n + gc);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int id = tid + 256 * h, col = id >> 3, ch = id & 7;
-    const int64_t oc = c0 + col, orr = r0 + ch * 8;   // output row oc, columns orr ..
-    if (oc >= n) continue;
-    uint16_t v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = t[ch * 8 + e][col];
-    uint16_t* dst = out + oc * m + orr;
-    if (vout && orr + 8 <= m) {
-      uint4 x;
-      x.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-      x.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-      x.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
-      x.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
-      *reinterpret_cast<uint4*>(dst) = x;
+      for (int e = 0; e < 16; ++e) v[e] = f32_to_bits((float)(int8_t)(w[e >> 2] >> (8 * (e & 3))) * s);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (orr + e < m) dst[e] = v[e];
+      for (int e = 0; e < 16; ++e)
+        v[e] = (gr < m && gc + e < n) ? f32_to_bits((float)q[gr * n + gc + e] * sc[gr]) : (uint16_t)0;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[row][cc + e] = v[e];
+  } else {
+    const int col = tid & 63;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int row = (tid >> 6) + 4 * k;
+      const int64_t gr = r0 + row, gc = c0 + col;
+      t[row][col] = (gr < m && gc < n) ? f32_to_bits((float)q[gr * n + gc] * sc[gr]) : (uint16_t)0;
     }
   }
+  __syncthreads();
+  store_tile_transposed(t, out, r0, c0, m, n, vout);
+}
+
+void launch_dequant_transpose(const int8_t* q, const float* sc, uint16_t* out, int64_t m, int64_t n, hipStream_t s) {
+  if (m <= 0 || n <= 0) return;
+  const int vin = n % 16 == 0 && (reinterpret_cast<uintptr_t>(q) & 15) == 0;
+  const int vout = m % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
+  hipLaunchKernelGGL(dequant_transpose_kernel, grid, dim3(256), 0, s, q, sc, out, m, n, vin, vout);
 }
 
 void launch_transpose_bf16(const uint16_t* in, uint16_t* out, int64_t m, int64_t n, hipStream_t s) {
