@@ -125,7 +125,9 @@ size_t poetx_workspace_bytes(const poetx_layer* layer, int64_t N, int op);
  * n or m is a multiple of 64 of at least 2048 (there a dequantized copy in
  * the workspace feeding the wide bf16 GEMM is faster); those layers, and
  * other shapes, dequantize w into the pass's workspace first (the workspace
- * sizes include that buffer).  poetx_forward_blocks_noalloc always reads the
+ * sizes include that buffer), transposed for the forward product and its
+ * recompute (read as NN GEMMs, as with POETX_W0_TRANSPOSED below) and
+ * [m][n] for the backward product.  poetx_forward_blocks_noalloc always reads the
  * codes directly.  A
  * merge merges the dequantized weight and stores it again as codes:
  *   s[i] = max_j |w[i][j]| / 127, q[i][j] = clamp(rne(w[i][j] / s[i]), -127, 127)
