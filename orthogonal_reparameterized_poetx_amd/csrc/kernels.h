@@ -151,7 +151,7 @@ struct GemmArgs {
   // scale per weight row
   const int8_t* Bq;
   const float* Bs;
-  // R-side blocks (launch_gemm_nt_rside): bf16 [N / qb][qb][qb]
+  // R-side blocks (launch_gemm_rside): bf16 [N / qb][qb][qb]
   const uint16_t* Qr;
   int qb;
 };
