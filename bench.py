@@ -171,6 +171,11 @@ def parse():
                     help="bf16 base weights as W0p alone; by default W0p also holds its transpose "
                          "(POETX_W0_TRANSPOSED, 2 more bytes per weight), which the forward products and their "
                          "recompute read as NN GEMMs (bit-identical results)")
+    ap.add_argument("--x-permuted", action="store_true",
+                    help="layer set: each matrix's input gathered into the working layout once per step "
+                         "(poetx_permute_input, on a stream of its own while the forward blocks are built) and "
+                         "kept for the backward pass instead of X (POETX_X_PERMUTED; bit-identical results; "
+                         "one N*n*2-byte buffer per matrix)")
     ap.add_argument("--keep-z2", action="store_true",
                     help="layer set: the variant without activation recompute (the forward keeps z2' for the "
                          "backward, N*m*2 bytes per matrix); the default recomputes it (POET-Xmem)")
@@ -319,10 +324,11 @@ def mfma_from(d):
               % (cls, rec["mfma_flops_per_launch"], rec["mfma_busy_frac"], launches))
 
 
-def run_tag(workload, tokens, w0_int8=False, keep_z2=False, w0_transposed=False):
+def run_tag(workload, tokens, w0_int8=False, keep_z2=False, w0_transposed=False, x_permuted=False):
     """Names the run a counter record was taken on: workload, tokens and variant."""
     w = "INT8" if w0_int8 else "bf16 + transposed" if w0_transposed else "bf16"
-    return "%s, %d tokens (%s weights, activations %s)" % (workload, tokens, w, "kept" if keep_z2 else "recomputed")
+    return "%s, %d tokens (%s weights, activations %s%s)" % (workload, tokens, w, "kept" if keep_z2 else "recomputed",
+                                                            ", inputs gathered once" if x_permuted else "")
 
 
 def profiled_run_tag():
@@ -643,6 +649,9 @@ def bench_stack(args):
 def main():
     args = parse()
     if args.workload == "stack24":
+        if args.x_permuted:
+            print("--x-permuted applies to the single-step workloads (layerset, square, mlp7b)", file=sys.stderr)
+            sys.exit(2)
         if args.gpus != 1:
             print("bench.py measures one GPU. Run with --gpus 1.", file=sys.stderr)
             sys.exit(2)
@@ -670,8 +679,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(2)
-    if args.keep_z2 and args.per_layer_builds:
-        print("--keep-z2 uses the prebuilt-block calls; drop --per-layer-builds", file=sys.stderr)
+    if (args.keep_z2 or args.x_permuted) and args.per_layer_builds:
+        print("--keep-z2 and --x-permuted use the prebuilt-block calls; drop --per-layer-builds", file=sys.stderr)
         sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -699,7 +708,8 @@ def main():
     for j in mats:
         inp = WL.matrix_inputs(c, j, N=N, b=b_over)
         lay = P.PoetxLayer(inp["m"], inp["n"], inp["b"], "bf16", dev, perm_seed=inp["perm_seed"],
-                           w0_int8=args.w0_int8, w0_transposed=args.w0_transposed)
+                           w0_int8=args.w0_int8, w0_transposed=args.w0_transposed,
+                           x_permuted=args.x_permuted)
         lay.pack(up(inp["W0"], "bf16"))
         lay.thR.copy_(up(inp["thR"], "f32"))
         lay.thP.copy_(up(inp["thP"], "f32"))
@@ -707,6 +717,8 @@ def main():
         if owner not in Xs:
             Xs[owner] = up(inp["X"], "bf16")
         lay.x_key = owner
+        # the matrix's input in its working layout (--x-permuted)
+        lay.xp = torch.empty(N, inp["n"], dtype=torch.bfloat16, device=dev) if args.x_permuted else None
         gYs.append(up(inp["gY"], "bf16"))
         outs.append(dict(Y=torch.empty(N, inp["m"], dtype=torch.bfloat16, device=dev),
                          dX=torch.empty(N, inp["n"], dtype=torch.bfloat16, device=dev),
@@ -739,7 +751,9 @@ def main():
     # matrix's kernel tails and small launches overlap another's work
     workers = [stream] + [torch.cuda.Stream() for _ in range(max(args.streams, 1) - 1)]
 
-    active = {"workers": workers, "side": side}
+    gather = torch.cuda.Stream()        # default priority
+    inputs_ready, step_start = torch.cuda.Event(), torch.cuda.Event()
+    active = {"workers": workers, "side": side, "gather": gather}
 
     where = {len(workers): balance_streams([(lay.m, lay.n) for lay in layers], N, len(workers)), 1: [0] * len(layers)}
 
@@ -761,25 +775,41 @@ def main():
         # after their dL/dQ (--chain batched) or per matrix on its stream
         # right after its dL/dQ (--chain per-matrix)
         bs = active["side"]
+        gs = active["gather"]
+        if args.x_permuted and gs is not stream:
+            step_start.record(stream)
         # the backward build waits for the forward build, so the two do not
         # split the CUs while nothing else can run; it then overlaps the
         # forward pass
         P.build_layer_blocks(layers, "forward")
+        if args.x_permuted:
+            # the inputs' gathers need no blocks: they run beside the forward
+            # build, on the CUs it leaves idle (enqueued after it, so that the
+            # build's workgroups take their CUs first)
+            if gs is not stream:
+                gs.wait_event(step_start)
+            with torch.cuda.stream(gs):
+                for lay in layers:
+                    lay.permute_input(Xs[lay.x_key], Xp=lay.xp)
+                inputs_ready.record(gs)
         bs.wait_stream(stream)
         with torch.cuda.stream(bs):
             P.build_layer_blocks(layers, "backward")
             bwd_blocks_ready.record(bs)
+        if args.x_permuted:
+            stream.wait_event(inputs_ready)
+        xin = (lambda lay: lay.xp) if args.x_permuted else (lambda lay: Xs[lay.x_key])
         if args.keep_z2:
             fan_out(list(zip(layers, outs)),
-                    lambda lay, o: lay.forward_blocks_z2(Xs[lay.x_key], Y=o["Y"], Z2=o["Z2"]))
+                    lambda lay, o: lay.forward_blocks_z2(xin(lay), Y=o["Y"], Z2=o["Z2"]))
         else:
-            fan_out(list(zip(layers, outs)), lambda lay, o: lay.forward_blocks(Xs[lay.x_key], Y=o["Y"]))
+            fan_out(list(zip(layers, outs)), lambda lay, o: lay.forward_blocks(xin(lay), Y=o["Y"]))
         stream.wait_event(bwd_blocks_ready)
         def bwd(lay, g, o):
             if args.keep_z2:
-                lay.backward_blocks_dq_z2(Xs[lay.x_key], g, o["Z2"], dX=o["dX"])
+                lay.backward_blocks_dq_z2(xin(lay), g, o["Z2"], dX=o["dX"])
             else:
-                lay.backward_blocks_dq(Xs[lay.x_key], g, dX=o["dX"])
+                lay.backward_blocks_dq(xin(lay), g, dX=o["dX"])
             if args.chain == "per-matrix":
                 P.chain_rule_layers([lay], [(o["dR"], o["dP"])])
         fan_out(list(zip(reversed(layers), reversed(gYs), reversed(outs))), bwd)
@@ -808,21 +838,21 @@ def main():
     torch.cuda.synchronize()
     torch.sigmoid_(marker)
     torch.cuda.synchronize()
-    active["workers"], active["side"] = [stream], stream
+    active["workers"], active["side"], active["gather"] = [stream], stream, stream
     P.timing_enable(True)
     for _ in range(args.profile_steps):
         step()
     torch.cuda.synchronize()
     kern = P.timing_summary()
     P.timing_enable(False)
-    active["workers"], active["side"] = workers, side
+    active["workers"], active["side"], active["gather"] = workers, side, gather
     torch.sigmoid_(marker)
     torch.cuda.synchronize()
     per_step = {k: dict(v, ms=v["ms"] / args.profile_steps, launches=v["launches"] / args.profile_steps,
                         flops=v["flops"] / args.profile_steps, bytes=v["bytes"] / args.profile_steps)
                 for k, v in kern.items()}
     tag = run_tag(cfg["name"] if b_over is None else "%s_b%d" % (cfg["name"], b_over), N, args.w0_int8,
-                  args.keep_z2, args.w0_transposed)
+                  args.keep_z2, args.w0_transposed, args.x_permuted)
     roof = dominant_roofline(per_step, tag)
     # every class against its own roofline (kernel level: the bytes or flops
     # each launch must move or compute, over its event-timed duration)
@@ -916,6 +946,9 @@ def main():
                    "streams": 1 if args.per_layer_builds else max(args.streams, 1),
                    "activations": "z2' kept from the forward pass (no recompute)" if args.keep_z2 else
                    "recomputed in the backward pass (POET-Xmem)",
+                   "inputs": "gathered into the working layout once per step beside the forward build and kept "
+                   "for the backward pass (POETX_X_PERMUTED)" if args.x_permuted else
+                   "gathered by every forward and backward call",
                    "base_weights": "INT8 codes with per-row fp32 scales, dequantized inside the GEMMs "
                    "(POET-XQ)" if args.w0_int8 else "bf16 with a transposed copy (POETX_W0_TRANSPOSED)"
                    if args.w0_transposed else "bf16"},

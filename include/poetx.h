@@ -83,6 +83,10 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
 #define POETX_SEPARATE_BLOCK_PRODUCTS 4u
 /* bf16 layers: W0p also holds its transpose (format below) */
 #define POETX_W0_TRANSPOSED 8u
+/* bf16 layers: the X argument of the forward and backward calls holds
+ * x' = Pi_tau x, the input already gathered into the working layout
+ * (poetx_permute_input below), instead of x */
+#define POETX_X_PERMUTED 16u
 
 /* op codes for poetx_workspace_bytes */
 #define POETX_OP_FORWARD 0
@@ -99,7 +103,8 @@ typedef struct {
   int32_t b;      /* block size of R and P                                */
   int32_t dtype;  /* poetx_dtype of W0p, X, Y, dY, dX                     */
   uint32_t flags; /* POETX_ACCUMULATE_GRAD, POETX_W0_INT8,
-                     POETX_SEPARATE_BLOCK_PRODUCTS, POETX_W0_TRANSPOSED   */
+                     POETX_SEPARATE_BLOCK_PRODUCTS, POETX_W0_TRANSPOSED,
+                     POETX_X_PERMUTED                                     */
   uint32_t reserved; /* must be 0                                         */
 } poetx_layer;
 
@@ -161,6 +166,27 @@ int poetx_dequantize_w0(const poetx_layer* layer, const void* W0q, void* W0bf16,
  *   caller has written W0p itself).  POETX_EINVAL without the flag.
  */
 int poetx_transpose_w0(const poetx_layer* layer, void* W0p, void* stream);
+
+/*
+ * The input in the working layout [P3 "POET-X: Memory-efficient LLM Training
+ * by Scaling Orthogonal Transformation", Methodologie items 2-3: the
+ * permutation of P regroups the input coordinates into the blocks that act
+ * on them]:
+ *   Xp[t][j] = X[t][tau[j]]   (t < N, j < n, the identity tail included)
+ * For layers with POETX_X_PERMUTED (bf16 only), every forward and backward
+ * call takes Xp where it takes X, and skips its own gather of X: the pass
+ * then starts with the P-side block product.  A caller can so gather the
+ * input while the blocks are being built (the gather does not need them),
+ * and keep Xp instead of X for the backward pass (same bytes; its recompute
+ * then gathers nothing).  Results are bit-identical to the layer without the
+ * flag on X.
+ *   tau  [n] int32 (a permutation; not checked); X, Xp [N][n] bf16, device,
+ *   not overlapping.  The layer's flags need not include POETX_X_PERMUTED.
+ * Errors: POETX_EINVAL (NULL argument), POETX_EDTYPE (fp32 layer),
+ * POETX_ESHAPE (N out of range), POETX_EHIP (launch failed).
+ */
+int poetx_permute_input(const poetx_layer* layer, const int32_t* tau, const void* X, int64_t N, void* Xp,
+                        void* stream);
 
 /*
  * One batch of Cayley blocks for poetx_build_block_sets: the generators of

@@ -18,6 +18,7 @@ POETX_ACCUMULATE_GRAD = 1
 POETX_W0_INT8 = 2
 POETX_SEPARATE_BLOCK_PRODUCTS = 4
 POETX_W0_TRANSPOSED = 8
+POETX_X_PERMUTED = 16
 OP_FORWARD, OP_BACKWARD, OP_MERGE, OP_FORWARD_BLOCKS, OP_BACKWARD_BLOCKS, OP_MERGE_BLOCKS, OP_BACKWARD_DQ = range(7)
 
 _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDTYPE",
@@ -25,7 +26,8 @@ _STATUS = {0: "POETX_OK", -1: "POETX_EINVAL", -2: "POETX_ESHAPE", -3: "POETX_EDT
 
 EXPORTED = ("poetx_workspace_bytes", "poetx_build_workspace_bytes", "poetx_build_blocks",
             "poetx_build_block_sets", "poetx_build_cnp_workspace_bytes", "poetx_build_block_sets_cnp",
-            "poetx_forward", "poetx_forward_blocks", "poetx_forward_blocks_noalloc", "poetx_backward",
+            "poetx_forward", "poetx_forward_blocks", "poetx_forward_blocks_noalloc", "poetx_permute_input",
+            "poetx_backward",
             "poetx_backward_blocks", "poetx_backward_blocks_dq", "poetx_forward_blocks_z2",
             "poetx_backward_blocks_dq_z2", "poetx_chain_rule_sets",
             "poetx_chain_workspace_bytes", "poetx_merge", "poetx_merge_blocks", "poetx_merge_blocks_sets",
@@ -118,6 +120,7 @@ def lib():
         "poetx_forward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "poetx_forward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, i64, vp, vp, sz, vp]),
         "poetx_forward_blocks_noalloc": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, i64, vp, vp]),
+        "poetx_permute_input": (ctypes.c_int, [LP, vp, vp, i64, vp, vp]),
         "poetx_backward": (ctypes.c_int, [LP, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_backward_blocks": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "poetx_backward_blocks_dq": (ctypes.c_int, [LP, vp, BP, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
@@ -259,6 +262,11 @@ def poetx_forward_blocks_noalloc(layer, W0p, blocks, sigma, tau, X, N, Y, stream
     _check("poetx_forward_blocks_noalloc", lib().poetx_forward_blocks_noalloc(
         ctypes.byref(layer), _ptr(W0p), None if blocks is None else ctypes.byref(blocks), _ptr(sigma), _ptr(tau),
         _ptr(X), int(N), _ptr(Y), _stream(stream)))
+
+
+def poetx_permute_input(layer, tau, X, N, Xp, stream=None):
+    _check("poetx_permute_input", lib().poetx_permute_input(ctypes.byref(layer), _ptr(tau), _ptr(X), int(N), _ptr(Xp),
+                                                            _stream(stream)))
 
 
 def poetx_backward_blocks(layer, W0p, blocks, sigma, tau, X, dY, N, dX, dthR, dthP, ws, stream=None):

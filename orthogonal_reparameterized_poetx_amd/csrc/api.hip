@@ -90,8 +90,11 @@ int validate_layer(const poetx_layer* L) {
   if (L->m < 1 || L->m > kMaxDim || L->n < 1 || L->n > kMaxDim)
     return fail(POETX_ESHAPE, "m=%lld n=%lld out of range [1, %lld]", (long long)L->m, (long long)L->n,
                 (long long)kMaxDim);
-  if (L->flags & ~(POETX_ACCUMULATE_GRAD | POETX_W0_INT8 | POETX_SEPARATE_BLOCK_PRODUCTS | POETX_W0_TRANSPOSED))
+  if (L->flags & ~(POETX_ACCUMULATE_GRAD | POETX_W0_INT8 | POETX_SEPARATE_BLOCK_PRODUCTS | POETX_W0_TRANSPOSED |
+                   POETX_X_PERMUTED))
     return fail(POETX_EINVAL, "unknown flags 0x%x", L->flags);
+  if ((L->flags & POETX_X_PERMUTED) && L->dtype != POETX_BF16)
+    return fail(POETX_EDTYPE, "POETX_X_PERMUTED applies to bf16 layers");
   if ((L->flags & POETX_W0_INT8) && L->dtype != POETX_BF16)
     return fail(POETX_EDTYPE, "POETX_W0_INT8 applies to bf16 layers");
   if ((L->flags & POETX_W0_TRANSPOSED) && L->dtype != POETX_BF16)
@@ -337,6 +340,7 @@ struct Shape {
   bool q8;    // W0p holds INT8 codes and per-row scales (POETX_W0_INT8)
   bool sep;   // POETX_SEPARATE_BLOCK_PRODUCTS
   bool tr;    // W0p followed by its transpose (POETX_W0_TRANSPOSED)
+  bool xp;    // X given as x' = Pi_tau x (POETX_X_PERMUTED)
   size_t es;  // element size of activations / weight
 };
 
@@ -349,6 +353,7 @@ Shape shape_of(const poetx_layer* L, int64_t N) {
   S.q8 = (L->flags & POETX_W0_INT8) != 0;
   S.sep = (L->flags & POETX_SEPARATE_BLOCK_PRODUCTS) != 0;
   S.tr = (L->flags & POETX_W0_TRANSPOSED) != 0;
+  S.xp = (L->flags & POETX_X_PERMUTED) != 0;
   S.es = S.f32 ? 4 : 2;
   return S;
 }
@@ -624,6 +629,22 @@ int gather_blockmul(const void* in, const int32_t* perm, const uint16_t* q, void
   return blockmul(xg, q, out, N, W, b, k, s);
 }
 
+// z = D x' for an x' the caller gathered (POETX_X_PERMUTED): the block
+// product over the k b block columns, and the identity tail (columns from
+// k b on) copied from x'
+int blockmul_permuted(const void* xp, const uint16_t* q, void* out, int64_t N, int W, int b, int k, size_t es,
+                      hipStream_t s) {
+  int rc;
+  if ((rc = blockmul(xp, q, out, N, W, b, k, s))) return rc;
+  const int t0 = k * b;
+  if (t0 >= W || N <= 0) return POETX_OK;
+  const size_t pitch = (size_t)W * es;
+  if (hipMemcpy2DAsync(static_cast<char*>(out) + t0 * es, pitch, static_cast<const char*>(xp) + t0 * es, pitch,
+                       (size_t)(W - t0) * es, (size_t)N, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return fail(POETX_EHIP, "identity-tail copy failed");
+  return POETX_OK;
+}
+
 // forward after the blocks exist: a3, a4, a5
 // z2out non-null (bf16): z2' goes there instead of the workspace (kept for
 // the backward pass)
@@ -652,8 +673,11 @@ int fwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
     }
     return check_launch("fp32 forward");
   }
-  // z1' = D_P x' with x' = Pi_tau x (the identity tail of x' goes straight to z1')
-  if ((rc = gather_blockmul(X, tau, q.qbP, w.sc, w.z1, nullptr, N, n, S.b, S.kP, S.es, s))) return rc;
+  // z1' = D_P x' with x' = Pi_tau x (the identity tail of x' goes straight to
+  // z1'); with POETX_X_PERMUTED, X is x' already
+  if (S.xp) rc = blockmul_permuted(X, q.qbP, w.z1, N, n, S.b, S.kP, S.es, s);
+  else rc = gather_blockmul(X, tau, q.qbP, w.sc, w.z1, nullptr, N, n, S.b, S.kP, S.es, s);
+  if (rc) return rc;
   // z2' = z1' W0p^T
   void* const z2 = z2out ? z2out : w.z2;
   // with the transposed copy the product is NN, z2' = z1' (W0p^T) with the
@@ -718,11 +742,14 @@ int bwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
       launch_gather_in_f32(r, s);
     }
   } else {
-    // recompute x' = Pi_tau x (kept for dL/dQ_P), z1' = D_P x', z2' = z1' W0p^T
+    // recompute x' = Pi_tau x (kept for dL/dQ_P), z1' = D_P x', z2' = z1' W0p^T;
+    // with POETX_X_PERMUTED, X is x' already
     if (z2in) {
-      if ((rc = permute(true, X, nullptr, w.xg, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
+      if (!S.xp && (rc = permute(true, X, nullptr, w.xg, w.z1, tau, N, n, S.kP * S.b, S.es, s))) return rc;
     } else {
-      if ((rc = gather_blockmul(X, tau, q.qbP, nullptr, w.z1, w.xg, N, n, S.b, S.kP, S.es, s))) return rc;
+      if (S.xp) rc = blockmul_permuted(X, q.qbP, w.z1, N, n, S.b, S.kP, S.es, s);
+      else rc = gather_blockmul(X, tau, q.qbP, nullptr, w.z1, w.xg, N, n, S.b, S.kP, S.es, s);
+      if (rc) return rc;
       // NN on the transposed copy when there is one, as in the forward pass
       Tm tm(s, W0.bt ? "gemm_nn" : "gemm_nt", 2.0 * N * S.m * S.n, (double)(N * S.n + S.m * S.n + N * S.m) * S.es);
       if (W0.bt)
@@ -758,7 +785,7 @@ int bwd_core(const Shape& S, const Wop& W0, const Blk& q, const int32_t* sigma, 
   // G_P = gz1'^T x' per block
   {
     Tm tm(s, "gram", xf_flops(N, S.kP, S.b), 2.0 * N * S.n * S.es);
-    launch_gram(S.f32, gz1, w.xg, N, n, S.b, S.kP, GP, w.part, s);
+    launch_gram(S.f32, gz1, S.xp ? X : w.xg, N, n, S.b, S.kP, GP, w.part, s);
   }
   if ((rc = check_launch("P-side gradient"))) return rc;
   // dX = Pi_tau^T D_P^T gz1'
@@ -1213,6 +1240,18 @@ int poetx_forward_blocks_z2(const poetx_layer* layer, const void* W0p, const poe
   if (layer && layer->dtype == POETX_F32) return fail(POETX_EDTYPE, "poetx_forward_blocks_z2 takes bf16 layers");
   if (N > 0 && !Z2) return fail(POETX_EINVAL, "Z2 is NULL");
   return forward_blocks_impl(layer, W0p, blocks, sigma, tau, X, N, Y, Z2, ws, ws_bytes, stream);
+}
+
+int poetx_permute_input(const poetx_layer* layer, const int32_t* tau, const void* X, int64_t N, void* Xp,
+                        void* stream) {
+  int rc = validate_layer(layer);
+  if (rc) return rc;
+  if ((rc = validate_N(N))) return rc;
+  const Shape S = shape_of(layer, N);
+  if (S.f32) return fail(POETX_EDTYPE, "poetx_permute_input takes bf16 layers");
+  if (N > 0 && (!tau || !X || !Xp)) return fail(POETX_EINVAL, "NULL tensor argument");
+  if (N == 0) return POETX_OK;
+  return permute(true, X, nullptr, Xp, Xp, tau, N, (int)S.n, S.kP * S.b, S.es, static_cast<hipStream_t>(stream));
 }
 
 int poetx_forward_blocks_noalloc(const poetx_layer* layer, const void* W0p, const poetx_blocks* blocks,

@@ -13,7 +13,7 @@ from . import _lib as L
 
 class PoetxLayer:
     def __init__(self, m, n, b, dtype="bf16", device="cuda:0", perm_seed=0, ws_pool=None, w0_int8=False,
-                 separate_block_products=False, w0_transposed=False):
+                 separate_block_products=False, w0_transposed=False, x_permuted=False):
         """w0_int8: keep W0p in the INT8 weight format (per-row codes and
         scales, POETX_W0_INT8; bf16 layers), turned into bf16 inside the
         passes' GEMMs or dequantized by each pass (include/poetx.h says which).
@@ -22,13 +22,18 @@ class PoetxLayer:
         before it (POETX_SEPARATE_BLOCK_PRODUCTS; bit-identical results).
         w0_transposed: W0p also holds its transpose, which the forward
         products read (POETX_W0_TRANSPOSED; bf16 layers; 2 more bytes per
-        weight; bit-identical results)."""
+        weight; bit-identical results).
+        x_permuted: the forward and backward calls take x' = X[:, tau]
+        (permute_input) instead of X (POETX_X_PERMUTED; bf16 layers;
+        bit-identical results).  x' follows tau, so it must be gathered
+        again after a merge."""
         self.device = torch.device(device)
         self.dt = L.POETX_BF16 if dtype == "bf16" else L.POETX_F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.flags = (L.POETX_W0_INT8 if w0_int8 else 0) | \
             (L.POETX_SEPARATE_BLOCK_PRODUCTS if separate_block_products else 0) | \
-            (L.POETX_W0_TRANSPOSED if w0_transposed else 0)
+            (L.POETX_W0_TRANSPOSED if w0_transposed else 0) | \
+            (L.POETX_X_PERMUTED if x_permuted else 0)
         self.layer = L.Layer(m, n, b, self.dt, self.flags)
         self.m, self.n, self.b = m, n, b
         nt = b * (b - 1) // 2
@@ -132,6 +137,14 @@ class PoetxLayer:
         kR, kP = self.m // self.b, self.n // self.b
         return [(self.thR, kR, q.get("Q32R"), q.get("QR"), q.get("QTR")),
                 (self.thP, kP, q.get("Q32P"), q.get("QP"), q.get("QTP"))]
+
+    def permute_input(self, X, Xp=None, stream=None):
+        """x' = X[:, tau], the input in the working layout (poetx_permute_input)."""
+        N = X.shape[0]
+        if Xp is None:
+            Xp = torch.empty(N, self.n, dtype=self.tdtype, device=self.device)
+        L.poetx_permute_input(self.layer, self.tau, X, N, Xp, stream)
+        return Xp
 
     def forward_blocks(self, X, Y=None, stream=None):
         N = X.shape[0]

@@ -58,7 +58,7 @@ def test_argument_validation_on_host():
     assert ws_need > 0
     # bad block size, dtype, shape, flags, reserved
     for lay, code in [(P.Layer(256, 256, 48), -1), (P.Layer(256, 256, 32, 7), -3), (P.Layer(0, 256, 32), -2),
-                      (P.Layer(256, 40000, 32), -2), (P.Layer(256, 256, 32, P.POETX_BF16, 16), -1),
+                      (P.Layer(256, 40000, 32), -2), (P.Layer(256, 256, 32, P.POETX_BF16, 32), -1),
                       (P.Layer(256, 256, 32, P.POETX_F32, P.POETX_W0_TRANSPOSED), -3),
                       (P.Layer(256, 256, 32, P.POETX_BF16, P.POETX_W0_TRANSPOSED | P.POETX_W0_INT8), -1)]:
         rc = L.poetx_forward(ctypes.byref(lay), fake, fake, fake, fake, fake, fake, 64, fake, fake, ws_need, None)
@@ -365,3 +365,26 @@ def test_stream_handle_normalization():
     assert _lib.stream_handle(FakeStream()) == 0x1234
     assert _lib.stream_handle(0x5678) == 0x5678
     assert _lib._stream(FakeStream()).value == 0x1234
+
+
+def test_permuted_input_validates_on_host():
+    P = _P()
+    L = P.lib()
+    fake = ctypes.c_void_p(0x1000)
+    lay = P.Layer(512, 256, 64, P.POETX_BF16)
+    l32 = P.Layer(512, 256, 64, P.POETX_F32)
+    # the gather: NULL arguments, fp32 layers, N out of range; N = 0 enqueues nothing
+    assert L.poetx_permute_input(ctypes.byref(lay), None, fake, 64, fake, None) == -1
+    assert L.poetx_permute_input(ctypes.byref(lay), fake, None, 64, fake, None) == -1
+    assert L.poetx_permute_input(ctypes.byref(lay), fake, fake, 64, None, None) == -1
+    assert L.poetx_permute_input(ctypes.byref(l32), fake, fake, 64, fake, None) == -3
+    assert L.poetx_permute_input(ctypes.byref(lay), fake, fake, -1, fake, None) == -2
+    assert L.poetx_permute_input(ctypes.byref(lay), None, None, 0, None, None) == 0
+    # the flag: bf16 layers only; workspaces as without it
+    x32 = P.Layer(512, 256, 64, P.POETX_F32, P.POETX_X_PERMUTED)
+    assert L.poetx_workspace_bytes(ctypes.byref(x32), 64, P.OP_FORWARD) == 0
+    assert "POETX_X_PERMUTED" in P.last_error()
+    xp = P.Layer(512, 256, 64, P.POETX_BF16, P.POETX_X_PERMUTED)
+    for op in (P.OP_FORWARD, P.OP_BACKWARD, P.OP_FORWARD_BLOCKS, P.OP_BACKWARD_DQ):
+        assert P.workspace_bytes(xp, 64, op) == P.workspace_bytes(lay, 64, op)
+    assert P.POETX_X_PERMUTED == 16
