@@ -176,6 +176,10 @@ def parse():
                          "(poetx_permute_input, on a stream of its own while the forward blocks are built) and "
                          "kept for the backward pass instead of X (POETX_X_PERMUTED; bit-identical results; "
                          "one N*n*2-byte buffer per matrix)")
+    ap.add_argument("--bwd-build", choices=["after-fwd", "beside-fwd"], default="beside-fwd",
+                    help="when the backward pass's Cayley build starts on its own stream: once the forward "
+                         "build is done (after-fwd), or at once, enqueued after the forward build so that it "
+                         "takes the CUs the forward build leaves idle (beside-fwd)")
     ap.add_argument("--keep-z2", action="store_true",
                     help="layer set: the variant without activation recompute (the forward keeps z2' for the "
                          "backward, N*m*2 bytes per matrix); the default recomputes it (POET-Xmem)")
@@ -776,11 +780,14 @@ def main():
         # right after its dL/dQ (--chain per-matrix)
         bs = active["side"]
         gs = active["gather"]
-        if args.x_permuted and gs is not stream:
+        if (args.x_permuted and gs is not stream) or (args.bwd_build == "beside-fwd" and bs is not stream):
             step_start.record(stream)
-        # the backward build waits for the forward build, so the two do not
-        # split the CUs while nothing else can run; it then overlaps the
-        # forward pass
+        # the backward build starts at once (--bwd-build beside-fwd),
+        # enqueued after the forward build so that the forward build's
+        # workgroups take their CUs first and the backward build's fill the
+        # CUs it leaves idle (it has one workgroup per block, 154 for the
+        # layer set), its last ones running beside the forward pass's first
+        # kernels; or once the forward build is done (after-fwd)
         P.build_layer_blocks(layers, "forward")
         if args.x_permuted:
             # the inputs' gathers need no blocks: they run beside the forward
@@ -792,7 +799,10 @@ def main():
                 for lay in layers:
                     lay.permute_input(Xs[lay.x_key], Xp=lay.xp)
                 inputs_ready.record(gs)
-        bs.wait_stream(stream)
+        if args.bwd_build == "beside-fwd" and bs is not stream:
+            bs.wait_event(step_start)
+        else:
+            bs.wait_stream(stream)
         with torch.cuda.stream(bs):
             P.build_layer_blocks(layers, "backward")
             bwd_blocks_ready.record(bs)
