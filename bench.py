@@ -180,6 +180,10 @@ def parse():
                     help="when the backward pass's Cayley build starts on its own stream: once the forward "
                          "build is done (after-fwd), or at once, enqueued after the forward build so that it "
                          "takes the CUs the forward build leaves idle (beside-fwd)")
+    ap.add_argument("--stack-fwd-builds", choices=["per-layer", "whole"], default="per-layer",
+                    help="stack24: the forward blocks built one decoder layer at a time on a side stream, "
+                         "each layer's matrices waiting for their own build (per-layer), or all 168 matrices' "
+                         "in one build before the forward pass (whole)")
     ap.add_argument("--keep-z2", action="store_true",
                     help="layer set: the variant without activation recompute (the forward keeps z2' for the "
                          "backward, N*m*2 bytes per matrix); the default recomputes it (POET-Xmem)")
@@ -415,7 +419,7 @@ class Stack:
     torch generator seeded by (config, matrix, stream)."""
 
     def __init__(self, P, WL, torch, dev, N, nlayers=24, exact=(), streams=3, w0_int8=False, merge="sets",
-                 w0_transposed=False):
+                 w0_transposed=False, fwd_builds="per-layer"):
         import math
         import numpy as np
         self.P, self.torch, self.N = P, torch, N
@@ -511,6 +515,7 @@ class Stack:
             need = [max(P.merge_sets_workspace_need(g), 1) for g in self.mgroups]
         self.merge_ws = [P.make_workspace(x, dev) for x in need]
         self.adam_steps = 0
+        self.fwd_builds = fwd_builds
 
     def _fan_out(self, main, idx_items, fn):
         for w in self.workers[1:]:
@@ -531,18 +536,38 @@ class Stack:
         P, torch = self.P, self.torch
         main = torch.cuda.current_stream()
         self._streams(main)
-        # the backward blocks depend only on the generators: build them on a
-        # second stream while the forward pass runs.  That build starts once
-        # the forward build is done, so the two do not split the CUs while
-        # nothing else can run
-        P.build_layer_blocks(self.layers, "forward")
-        self.side.wait_stream(main)
+        n = len(self.layers)
+        if self.fwd_builds == "per-layer":
+            # the forward blocks of the first decoder layer now, those of each
+            # later one (seven matrices, 154 blocks) on the side stream while
+            # the layers before it run their forward pass: a matrix waits
+            # only for its own layer's build
+            groups = {}
+            for lay in self.layers:
+                groups.setdefault(lay.j // 7, []).append(lay)
+            order = sorted(groups)
+            if not hasattr(self, "fwd_ready"):
+                self.fwd_ready = {l: torch.cuda.Event() for l in order}
+            P.build_layer_blocks(groups[order[0]], "forward")
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                for l in order[1:]:
+                    P.build_layer_blocks(groups[l], "forward")
+                    self.fwd_ready[l].record(self.side)
+        else:
+            P.build_layer_blocks(self.layers, "forward")
+            self.side.wait_stream(main)
+        # the backward blocks depend only on the generators: build them on the
+        # side stream while the forward pass runs
         with torch.cuda.stream(self.side):
             P.build_layer_blocks(self.layers, "backward")
             self.bwd_ready.record(self.side)
-        n = len(self.layers)
-        self._fan_out(main, [(i, (self.layers[i], self.out[i])) for i in range(n)],
-                      lambda lay, o: lay.forward_blocks(self.X[lay.x_key], Y=o["Y"]))
+
+        def fwd(lay, o):
+            if self.fwd_builds == "per-layer" and lay.j // 7 != order[0]:
+                torch.cuda.current_stream().wait_event(self.fwd_ready[lay.j // 7])
+            lay.forward_blocks(self.X[lay.x_key], Y=o["Y"])
+        self._fan_out(main, [(i, (self.layers[i], self.out[i])) for i in range(n)], fwd)
         main.wait_event(self.bwd_ready)
         self._fan_out(main, [(i, (self.layers[i], self.gY[i], self.out[i])) for i in reversed(range(n))],
                       lambda lay, g, o: lay.backward_blocks_dq(self.X[lay.x_key], g, dX=o["dX"]))
@@ -587,7 +612,7 @@ def bench_stack(args):
     torch.cuda.set_device(0)
     N = args.tokens or WL.CONFIGS[5]["N"]
     st = Stack(P, WL, torch, dev, N, streams=args.streams, w0_int8=args.w0_int8, merge=args.merge,
-               w0_transposed=args.w0_transposed)
+               w0_transposed=args.w0_transposed, fwd_builds=args.stack_fwd_builds)
     torch.cuda.synchronize()
     resident = torch.cuda.memory_allocated()
     stream = torch.cuda.current_stream()
@@ -638,7 +663,9 @@ def bench_stack(args):
         "config": {"workload": WL.CONFIGS[5]["name"], "tokens": N, "matrices": len(st.layers), "b": WL.CONFIGS[5]["b"],
                    "base_weights": "INT8 codes with per-row fp32 scales (POET-XQ)" if args.w0_int8 else
                    "bf16 with a transposed copy (POETX_W0_TRANSPOSED)" if args.w0_transposed else "bf16",
-                   "merge": "one batched call per stream" if args.merge == "sets" else "one call per matrix"},
+                   "merge": "one batched call per stream" if args.merge == "sets" else "one call per matrix",
+                   "forward_builds": "one per decoder layer, beside the forward pass of the layers before it"
+                   if args.stack_fwd_builds == "per-layer" else "one for all matrices before the forward pass"},
         "phases_ms": {"fwd_bwd": round(fb / k, 3), "adam": round(ad / k, 3), "merge": round(mg / k, 3)},
         "generators": st.theta.numel(),
         "resident_gb": round(resident / 1e9, 3),
