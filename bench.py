@@ -151,6 +151,9 @@ def parse():
     ap.add_argument("--kernel-stats", metavar="CSV",
                     help="no GPU: summarize by kernel class a rocprofv3 kernel_stats.csv (whole run) or a "
                          "kernel_trace.csv (only the marked, serialized per-kernel timing pass)")
+    ap.add_argument("--concurrency-from", metavar="CSV",
+                    help="no GPU: from a rocprofv3 kernel_trace.csv of a run with --steps K, the last K timed "
+                         "steps before the marked pass: how much of the step has 0, 1, 2, ... weight GEMMs running")
     ap.add_argument("--workload", choices=("layerset", "square", "mlp7b", "stack24"), default="layerset",
                     help="layerset: fwd+bwd of the LLaMA-1B layer set (default); square: the 2048x2048 layer, b=256, "
                          "4096 tokens; mlp7b: the LLaMA-7B MLP projection 11008x4096, 8192 tokens, block size --b; "
@@ -677,6 +680,38 @@ def bench_stack(args):
     }), flush=True)
 
 
+def concurrency_from(csv_path, steps):
+    """Weight-GEMM concurrency over the timed steps of a kernel trace: the
+    launches from the start of the steps-th last step (each step opens with
+    its two Cayley builds) up to the first marker kernel."""
+    import csv
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in rows]
+    marks = [i for i, nm in enumerate(names) if "sigmoid" in nm.lower()]
+    if not marks:
+        raise SystemExit("no marker kernels in %s" % csv_path)
+    builds = [i for i in range(marks[0]) if "gj_kernel" in names[i]]
+    if len(builds) < 2 * steps:
+        raise SystemExit("fewer than %d steps before the marked pass" % steps)
+    timed = rows[builds[-2 * steps]:marks[0]]
+    t0 = int(timed[0]["Start_Timestamp"])
+    t1 = max(int(r["End_Timestamp"]) for r in timed)
+    ev = []
+    for r in timed:
+        if "gemm_wide_kernel" in r["Kernel_Name"] or "gemm_bf16_kernel<true, false" in r["Kernel_Name"]:
+            ev += [(int(r["Start_Timestamp"]), 1), (int(r["End_Timestamp"]), -1)]
+    ev.sort()
+    hist, cur, last = {}, 0, t0
+    for t, d in ev:
+        hist[cur] = hist.get(cur, 0) + t - last
+        cur, last = cur + d, t
+    hist[cur] = hist.get(cur, 0) + t1 - last
+    span = t1 - t0
+    print("%d timed steps, %.1f us per step, %d launches" % (steps, span / 1e3 / steps, len(timed)))
+    for k in sorted(hist):
+        print("weight GEMMs running: %d  %5.1f %% of the time" % (k, 100.0 * hist[k] / span))
+
+
 def main():
     args = parse()
     if args.workload == "stack24":
@@ -693,6 +728,9 @@ def main():
         return
     if args.kernel_stats:
         kernel_stats(args.kernel_stats)
+        return
+    if args.concurrency_from:
+        concurrency_from(args.concurrency_from, args.steps)
         return
     if args.mfma_from:
         mfma_from(args.mfma_from)

@@ -164,3 +164,25 @@ def test_balance_streams_places_every_matrix_once():
     cost = [6.0 * 8192 * m * n / 1.1e15 + (28.0 * n + 20.0 * m) * 8192 / 3.5e12 for m, n in stack]
     load = [sum(c for c, w in zip(cost, w24) if w == s) for s in range(3)]
     assert max(load) - min(load) <= max(cost)
+
+
+def test_concurrency_summary_counts_overlapping_gemms(tmp_path, capsys):
+    # two steps (each opening with its two builds), then the marker: step 2
+    # spans t = 100..200 with GEMMs over 110..150 and 130..170 (two at once
+    # over 130..150) and a transform to 200; the marker is not counted
+    rows = [("gj_kernel<256, 6>", 0, 10), ("gj_kernel<256, 6>", 0, 10), ("void poetx::gemm_wide_kernel<true, true>", 20, 60),
+            ("gj_kernel<256, 6>", 100, 105), ("gj_kernel<256, 6>", 101, 108),
+            ("void poetx::gemm_wide_kernel<true, false>", 110, 150), ("void poetx::gemm_wide_kernel<true, true>", 130, 170),
+            ("poetx::blockdiag_pp_kernel", 170, 200), ("void at::sigmoid_kernel", 300, 301)]
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for r in rows:
+            w.writerow(r)
+    bench.concurrency_from(str(path), 1)
+    out = capsys.readouterr().out
+    assert "1 timed steps, 0.1 us per step, 5 launches" in out
+    # 100 ns in all: none running over 100..110 and 170..200, one over
+    # 110..130 and 150..170, two over 130..150
+    assert "running: 0   40.0 %" in out and "running: 1   40.0 %" in out and "running: 2   20.0 %" in out
